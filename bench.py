@@ -1,0 +1,254 @@
+"""Throughput of the 4-bit Shampoo preconditioner step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic gradients
+already resident in HBM: update_stats (dequantize, Bjorck, statistics, warm-started
+QR refresh, Rayleigh eigenvalues, requantize), refresh_root when t % T == 0, and
+precondition, for every block of the workload.  ``value`` is block-steps per second.
+
+Prints one JSON line with the metric, the dominant kernel's roofline figures
+(measured with HIP events around every launch of a second, instrumented pass on the
+library's stream) and the CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "preconditioned block-steps/sec + GEMM TFLOP/s (% MFMA peak), quant GB/s (% HBM)"
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+DEFAULT_CONFIG = "single_1024"
+
+
+def log(msg: str):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_gradients(wl, steps: int, device):
+    """Per-step gradient lists on the device.  Small workloads come from the NumPy
+    generators the tests use; large ones are drawn on the device with the same
+    distributions (torch generator, seed 0) to keep host time bounded."""
+    import numpy as np
+    import torch
+    total_bytes = sum(m * n * 4 for m, n in wl.shapes)
+    distinct = steps if total_bytes * steps <= (2 << 30) else max(1, min(steps, (8 << 30) // total_bytes))
+    if total_bytes * distinct <= (512 << 20):
+        out = []
+        for t in range(1, distinct + 1):
+            out.append([torch.from_numpy(G).to(device) for G in wl.gradients(t)])
+        return out, distinct, "numpy generators (tests' recipe)"
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed)
+    out = []
+    for t in range(distinct):
+        grads = []
+        for (s, r0, c0, m, n) in wl.blocks:
+            if wl.kind == "student_bf16":
+                # Student-t(3) = N / sqrt(chi2_3 / 3), rounded to bf16 and widened
+                z = torch.randn((m, n), device=device, generator=g)
+                chi = torch.randn((3, m, n), device=device, generator=g).pow(2).sum(0) / 3.0
+                G = (z / chi.sqrt()).to(torch.bfloat16).to(torch.float32)
+            elif wl.kind == "lowrank":
+                A = torch.randn((m, 32), device=device, generator=g)
+                B = torch.randn((n, 32), device=device, generator=g)
+                Z = torch.randn((32, 32), device=device, generator=g)
+                G = (A @ Z @ B.T) / 32.0 + 0.01 * torch.randn((m, n), device=device, generator=g)
+            elif wl.kind == "conv":
+                c = torch.exp(torch.randn((1, n), device=device, generator=g))
+                G = torch.randn((m, n), device=device, generator=g) * c
+            else:
+                a = torch.rand((m, 1), device=device, generator=g) * 2 - 1
+                b = torch.rand((1, n), device=device, generator=g) * 2 - 1
+                G = torch.randn((m, n), device=device, generator=g) * (10.0 ** a) * (10.0 ** b)
+            grads.append(G.contiguous())
+        out.append(grads)
+    del np
+    return out, distinct, "device generator with the workload's distributions"
+
+
+def cpu_baseline(wl, budget_s: float = 15.0):
+    """The CPU oracle, as it stands, on the first steps of the same workload."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import shampoo4 as o
+    blocks = list(range(len(wl.blocks)))
+    # bound the sample: the first blocks of the workload, one step at a time
+    max_blocks = len(blocks)
+    est = sum(m ** 3 + n ** 3 for m, n in wl.shapes)
+    if est > 4 * 1024 ** 3:
+        cum, max_blocks = 0, 0
+        for (m, n) in wl.shapes:
+            cum += m ** 3 + n ** 3
+            max_blocks += 1
+            if cum >= 2 * 1024 ** 3:
+                break
+    sel = blocks[:max_blocks]
+    shapes = [wl.shapes[i] for i in sel]
+    orc = o.Shampoo4Oracle(shapes, beta=wl.beta, eps=wl.eps, qblock=wl.qblock,
+                           bjorck_iters=wl.bjorck_iters, power_iters=wl.power_iters)
+    steps = 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    while elapsed < budget_s and steps < wl.steps:
+        steps += 1
+        Gs = [wl.block_gradient(i, steps) for i in sel]
+        t1 = time.perf_counter()
+        orc.step(Gs, steps, wl.root_interval)
+        elapsed += time.perf_counter() - t1
+    del t0
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    return {
+        "value": len(sel) * steps / elapsed,
+        "unit": "block-steps/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{steps} step(s) x {len(sel)} of {len(wl.blocks)} blocks of {wl.name} "
+                  f"(float64 NumPy, {elapsed:.1f} s, {os.cpu_count()} host cpus visible)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--no-root-cache", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the step is a per-GPU kernel path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bit_quantized_shampoo_amd import Shampoo4Blocks, Shampoo4Config
+    from workloads import cost, get_workload
+
+    wl = get_workload(args.config)
+    steps = args.steps if args.steps is not None else (100 if len(wl.blocks) <= 4 else 5)
+    warmup = args.warmup if args.warmup is not None else (10 if len(wl.blocks) <= 4 else 2)
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    cfg = Shampoo4Config(beta=wl.beta, eps=wl.eps, qblock=wl.qblock, bjorck_iters=wl.bjorck_iters,
+                         power_iters=wl.power_iters, root_cache=not args.no_root_cache)
+    log(f"[bench] workload {wl.name}: {len(wl.blocks)} blocks, steps {steps}, warmup {warmup}")
+    grads, distinct, gen = make_gradients(wl, steps + warmup, dev)
+    blocks = Shampoo4Blocks(wl.shapes, cfg, device=dev)
+    outs = [torch.empty((m, n), dtype=torch.float32, device=dev) for m, n in wl.shapes]
+    stream = torch.cuda.current_stream()
+
+    def run(t):
+        blocks.step(grads[(t - 1) % distinct], t, wl.root_interval, outs=outs)
+
+    t = 0
+    for _ in range(warmup):
+        t += 1
+        run(t)
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t_start = t
+    e0.record(stream)
+    for _ in range(steps):
+        t += 1
+        run(t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / steps
+    value = len(wl.blocks) * steps / (ms / 1e3)
+    log(f"[bench] timed {steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} block-steps/s")
+
+    # second pass, every launch bracketed by HIP events on the library's stream
+    blocks.timing(True)
+    t = t_start
+    for _ in range(steps):
+        t += 1
+        run(t)
+    rep = blocks.timing_report()
+    blocks.timing(False)
+    torch.cuda.synchronize()
+    for name, r in rep.items():
+        if r["launches"]:
+            log(f"[bench] {name:12s} launches {r['launches']:6d}  {r['ms'] / steps:9.3f} ms/step  "
+                f"{r['flops'] / max(r['ms'], 1e-9) / 1e9:8.2f} TFLOP/s  "
+                f"{r['bytes'] / max(r['ms'], 1e-9) / 1e6:8.1f} GB/s")
+    g = rep["gemm"]
+    gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12 if g["ms"] > 0 else 0.0
+    q = rep["quant"]
+    quant_gbps = q["bytes"] / (q["ms"] * 1e-3) / 1e9 if q["ms"] > 0 else 0.0
+    dq = rep["dequant"]
+    dequant_gbps = dq["bytes"] / (dq["ms"] * 1e-3) / 1e9 if dq["ms"] > 0 else 0.0
+    step_flops = sum(cost.block_step_flops(m, n, wl.bjorck_iters, wl.root_interval, wl.power_iters,
+                                           cached_root=cfg.root_cache) for m, n in wl.shapes)
+    roofline = {
+        "bound": "mfma",
+        "kernel": "gemm_kernel (fp32 v_mfma_f32_32x32x2_f32, all matrix products of the step)",
+        "achieved": round(gemm_tflops, 3),
+        "peak": PEAK_FP32_MFMA_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(gemm_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+        "traffic": None,
+        "launches_per_step": g["launches"] / steps,
+        "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 3),
+    }
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "block-steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": f"synthetic ({gen}, {distinct} distinct gradient batches)",
+        "config": {
+            "workload": wl.name,
+            "description": wl.description,
+            "blocks": len(wl.blocks),
+            "beta": wl.beta, "eps": wl.eps, "qblock": wl.qblock,
+            "bjorck_iters": wl.bjorck_iters, "power_iters": wl.power_iters,
+            "root_interval": wl.root_interval, "root_cache": cfg.root_cache,
+        },
+        "gemm_tflops": round(gemm_tflops, 3),
+        "gemm_frac_mfma_peak": round(gemm_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+        "quant_gbps": round(quant_gbps, 1),
+        "quant_frac_hbm_peak": round(quant_gbps / PEAK_HBM_GBPS, 4),
+        "dequant_gbps": round(dequant_gbps, 1),
+        "algorithmic_tflops_per_step": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "roofline": roofline,
+        "kernel_ms_per_step": {k: round(v["ms"] / steps, 4) for k, v in rep.items() if v["launches"]},
+        "cpu_baseline": None,
+    }
+    blocks.close()
+    del grads
+    if not args.no_cpu:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

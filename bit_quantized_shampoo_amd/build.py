@@ -1,0 +1,63 @@
+"""Build libshampoo4.so (HIP kernels + C ABI runtime) in-tree for gfx950.
+
+Usage: ``python -m bit_quantized_shampoo_amd.build`` or ``build_library()``.
+Every source is compiled with hipcc for gfx950 only, in parallel, then linked
+into ``bit_quantized_shampoo_amd/libshampoo4.so``.
+"""
+
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libshampoo4.so")
+BUILD_DIR = os.path.join(PKG, "_build")
+
+SOURCES = ["gemm.hip", "codec.hip", "qr.hip", "elementwise.hip", "runtime.cpp"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    # no packed fp32 instructions in the generated code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep fp32 subnormals (the codec is bit-exact on them) and IEEE divide / sqrt
+    "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-I", os.path.join(ROOT, "include"),
+    "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
+]
+
+
+def _compile(src: str) -> str:
+    out = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, "-c", *FLAGS, os.path.join(CSRC, src), "-o", out]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{proc.stderr}")
+    return out
+
+
+def build_library(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    workers = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8"))))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    if proc.returncode != 0:
+        raise RuntimeError(f"link failed:\n{proc.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build_library(verbose=True)
+    sys.exit(0)

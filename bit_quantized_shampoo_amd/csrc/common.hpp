@@ -1,0 +1,100 @@
+// Shared device-side types for the 4-bit Shampoo kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s4 {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Per-block user pointers of one call, uploaded once per call; descriptors refer
+// to an entry by index so that the static descriptor tables never change.
+struct IoEntry {
+    const float* G;
+    int64_t ldg;
+    float* P;
+    int64_t ldp;
+};
+
+// One matrix product D = alpha * op(A) op(B) [* rscale rows][* cscale cols] + beta * C.
+// op(B)'s row k is multiplied by kscale[k] when kscale is set.  A pointer given by an
+// io index (>= 0) is taken from the call's io table instead of the field.
+struct GemmDesc {
+    const float* A;
+    const float* B;
+    const float* C;
+    float* D;
+    const float* kscale;
+    const float* rscale;
+    const float* cscale;
+    int64_t lda, ldb, ldc, ldd;
+    int32_t M, N, K;
+    int32_t tiles_m;          // tiles along M for the launch's tile shape
+    float alpha, beta;
+    int32_t a_io, b_io, d_io; // -1 or index into the io table (A/B = G, D = P)
+    int32_t pad;
+};
+static_assert(sizeof(GemmDesc) == 128, "GemmDesc layout");
+
+// Codec work item: one flattened matrix of n fp32 elements.
+struct CodecDesc {
+    const uint8_t* codes_in;  // dequant source
+    const float* scales_in;
+    uint8_t* codes_out;       // quant destination
+    float* scales_out;
+    const float* x_in;        // quant source
+    float* x_out;             // dequant destination
+    int64_t n;
+    int64_t pad;
+};
+static_assert(sizeof(CodecDesc) == 64, "CodecDesc layout");
+
+// One Householder panel of one matrix: rows c0.., columns c0..c0+nb-1 of A.
+struct PanelDesc {
+    float* A;                 // matrix base (p x p)
+    float* V;                 // out: [h, 32] explicit unit-lower reflector vectors
+    float* Y;                 // out: [h, 32] V T (compact WY)
+    float* rdiag;             // out: R diagonal, entries c0..c0+nb-1
+    int64_t ld;
+    int32_t c0, h, nb, pad;
+};
+static_assert(sizeof(PanelDesc) == 56, "PanelDesc layout");
+
+// Column / vector work item for the small elementwise kernels.
+struct VecDesc {
+    const float* a;           // e.g. Q
+    const float* b;           // e.g. L~ Q
+    float* out;               // e.g. eigenvalues / root scaling / W
+    const float* aux;         // e.g. R diagonal
+    uint8_t* codes;           // identity init
+    float* scales;
+    int64_t ld;
+    int32_t p, pad;
+};
+static_assert(sizeof(VecDesc) == 64, "VecDesc layout");
+
+// Initial state of one side: U = I (codes and scales), lam = 0, root = (I, d = 1).
+struct InitDesc {
+    uint8_t* codes;
+    float* scales;
+    float* lam;
+    uint8_t* rcodes;
+    float* rscales;
+    float* d;
+    int32_t p, pad;
+};
+static_assert(sizeof(InitDesc) == 56, "InitDesc layout");
+
+// Find the work item owning `tile` from an inclusive-exclusive prefix of tile counts.
+__device__ __forceinline__ int find_item(const int* __restrict__ prefix, int n, int tile) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace s4

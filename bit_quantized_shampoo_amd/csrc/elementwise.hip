@@ -1,0 +1,134 @@
+// Small bandwidth-bound kernels of the step.
+//  * rayleigh:      lam_j = max(sum_r Q[r][j] (L~ Q)[r][j], 0), one workgroup per 64
+//                   columns (lanes own columns, 4 row slots, fixed-order reduction);
+//  * root scaling:  d_i = (lam_i + eps)^(-1/4) ("Shampoo -- Second-Order Optimizer",
+//                   "Computing the inverse fourth root": damping before rooting);
+//  * sign diagonal: W = diag(sign R_jj) (0 -> +1), the start of the explicit-Q
+//                   accumulation, so that Q comes out with diag(R) >= 0;
+//  * identity state: U = I coded exactly (code 15 on the diagonal, 7 elsewhere,
+//                   scale 1 for blocks holding a diagonal element, else 0), lam = 0,
+//                   root = (I, d = 1).
+#include "kernels.hpp"
+
+namespace s4 {
+
+namespace {
+
+__global__ __launch_bounds__(256) void rayleigh_kernel(const VecDesc* __restrict__ descs,
+                                                       const int* __restrict__ prefix, int ndesc,
+                                                       uint32_t* __restrict__ flag) {
+    __shared__ float red[4][RAYLEIGH_COLS];
+    const int item = find_item(prefix, ndesc, blockIdx.x);
+    const VecDesc& d = descs[item];
+    const int chunk = blockIdx.x - prefix[item];
+    const int c = threadIdx.x & 63;
+    const int slot = threadIdx.x >> 6;
+    const int col = chunk * RAYLEIGH_COLS + c;
+    const int p = d.p;
+    const int64_t ld = d.ld;
+    float s = 0.f;
+    if (col < p)
+        for (int r = slot; r < p; r += 4) s += d.a[(int64_t)r * ld + col] * d.b[(int64_t)r * ld + col];
+    red[slot][c] = s;
+    __syncthreads();
+    if (threadIdx.x < 64 && col < p) {
+        const float t = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+        if (!__builtin_isfinite(t)) flag[0] = 1u;
+        d.out[col] = t > 0.f ? t : 0.f;
+    }
+}
+
+__global__ __launch_bounds__(256) void root_scaling_kernel(const VecDesc* __restrict__ descs,
+                                                           const int* __restrict__ prefix, int ndesc,
+                                                           float eps, uint32_t* __restrict__ flag) {
+    const int item = find_item(prefix, ndesc, blockIdx.x);
+    const VecDesc& d = descs[item];
+    const int i = (blockIdx.x - prefix[item]) * 256 + threadIdx.x;
+    if (i >= d.p) return;
+    const float x = d.a[i] + eps;
+    if (!__builtin_isfinite(x)) flag[0] = 1u;
+    d.out[i] = 1.0f / sqrtf(sqrtf(x));
+}
+
+__global__ __launch_bounds__(256) void sign_diag_kernel(const VecDesc* __restrict__ descs,
+                                                        const int* __restrict__ prefix, int ndesc) {
+    const int item = find_item(prefix, ndesc, blockIdx.x);
+    const VecDesc& d = descs[item];
+    const int64_t p = d.p;
+    const int64_t base = (int64_t)(blockIdx.x - prefix[item]) * FILL_TILE;
+    for (int64_t e = base + threadIdx.x; e < base + FILL_TILE && e < p * p; e += 256) {
+        const int64_t i = e / p, j = e - i * p;
+        float v = 0.f;
+        if (i == j) v = (d.aux[j] < 0.f) ? -1.f : 1.f;
+        d.out[i * d.ld + j] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void identity_state_kernel(const InitDesc* __restrict__ descs,
+                                                             const int* __restrict__ prefix, int ndesc) {
+    const int item = find_item(prefix, ndesc, blockIdx.x);
+    const InitDesc& d = descs[item];
+    const int64_t p = d.p;
+    const int64_t n = p * p;
+    const int64_t nqb = (n + 63) / 64;
+    const int64_t i = (int64_t)(blockIdx.x - prefix[item]) * 256 + threadIdx.x;
+    if (i < nqb) {
+        bool any = false;
+        uint32_t words[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t idx = i * 64 + w * 8 + e;
+                const bool diag = idx < n && (idx % (p + 1)) == 0;
+                any = any || diag;
+                word |= (diag ? 15u : 7u) << (4 * e);
+            }
+            words[w] = word;
+        }
+        uint32_t* c = reinterpret_cast<uint32_t*>(d.codes) + i * 8;
+        uint32_t* rc = reinterpret_cast<uint32_t*>(d.rcodes) + i * 8;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) { c[w] = words[w]; rc[w] = words[w]; }
+        d.scales[i] = any ? 1.f : 0.f;
+        d.rscales[i] = any ? 1.f : 0.f;
+    }
+    if (i < p) {
+        d.lam[i] = 0.f;
+        d.d[i] = 1.f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rayleigh(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                           uint32_t* flag, hipStream_t stream) {
+    if (ntiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(rayleigh_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_root_scaling(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                               float eps, uint32_t* flag, hipStream_t stream) {
+    if (ntiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(root_scaling_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc,
+                       eps, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_sign_diag(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                            hipStream_t stream) {
+    if (ntiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(sign_diag_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    return hipGetLastError();
+}
+
+hipError_t launch_identity_state(const InitDesc* descs, const int* prefix, int ndesc, int ntiles,
+                                 hipStream_t stream) {
+    if (ntiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(identity_state_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    return hipGetLastError();
+}
+
+}  // namespace s4

@@ -1,0 +1,49 @@
+// Host-side launchers of the gfx950 kernels.  Every launcher enqueues one kernel on
+// `stream` and returns the launch status; work items are described by device
+// descriptor arrays plus an exclusive prefix of per-item tile counts.
+#pragma once
+
+#include "common.hpp"
+
+namespace s4 {
+
+// Tile shapes of the fp32 MFMA GEMM (workgroup of 4 waves).
+enum GemmCfg { GEMM_128x128 = 0, GEMM_64x64 = 1, GEMM_32x128 = 2, GEMM_NCFG = 3 };
+void gemm_tile_dims(int cfg, int* bm, int* bn);
+hipError_t launch_gemm(int cfg, bool ta, bool tb, const GemmDesc* descs, const int* prefix,
+                       int ndesc, int ntiles, const IoEntry* io, hipStream_t stream);
+
+// Codec: elements per workgroup tile.
+constexpr int DEQ_TILE = 2048;     // 256 threads x 8 elements
+constexpr int QUANT_TILE = 1024;   // 256 threads x 4 elements
+constexpr int COPY_TILE = 8192;    // bytes of codes per workgroup
+hipError_t launch_dequant(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                          hipStream_t stream);
+hipError_t launch_quant(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                        uint32_t* flag, hipStream_t stream);
+hipError_t launch_dequant_single(const CodecDesc& d, hipStream_t stream);
+hipError_t launch_quant_single(const CodecDesc& d, hipStream_t stream);
+hipError_t launch_codec_copy(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                             hipStream_t stream);
+void host_codebook(float levels[16], float midpoints[15]);
+
+// Householder panel factorization, one workgroup per panel.
+constexpr int PANEL_THREADS = 512;
+constexpr int PANEL_LDS_MAX_ROWS = 1024;     // panels up to this height are staged in LDS
+size_t panel_lds_bytes(bool in_lds, int max_h);
+hipError_t launch_panel(bool in_lds, const PanelDesc* descs, int ndesc, int max_h,
+                        hipStream_t stream);
+
+// Small per-column / per-element kernels.
+constexpr int RAYLEIGH_COLS = 64;            // columns per workgroup
+constexpr int FILL_TILE = 4096;              // elements per workgroup
+hipError_t launch_rayleigh(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                           uint32_t* flag, hipStream_t stream);
+hipError_t launch_root_scaling(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                               float eps, uint32_t* flag, hipStream_t stream);
+hipError_t launch_sign_diag(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                            hipStream_t stream);
+hipError_t launch_identity_state(const InitDesc* descs, const int* prefix, int ndesc, int ntiles,
+                                 hipStream_t stream);
+
+}  // namespace s4

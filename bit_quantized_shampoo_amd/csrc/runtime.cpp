@@ -1,0 +1,931 @@
+// Host runtime and C ABI of the 4-bit Shampoo step (see include/shampoo4.h).
+//
+// A context is a static plan: at init every kernel launch of every entry point is
+// described once by device descriptor tables (written into the tail of the
+// caller's workspace) whose pointers address the caller's state and workspace
+// buffers.  G and P change per call, so descriptors refer to them by block index
+// into a small io table that is the only thing uploaded per call.  Each entry
+// point then just enqueues its fixed sequence of grouped launches on the stream:
+// one launch covers every block and both sides of a stage.
+#include "../../include/shampoo4.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <memory>
+#include <vector>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace s4;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kRing = 8;            // pinned io staging slots
+constexpr int kPanel = 32;          // Householder panel width
+constexpr int kMaxDim = 8192;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+enum Family { FAM_GEMM = 0, FAM_DEQUANT, FAM_QUANT, FAM_PANEL, FAM_RAYLEIGH, FAM_ELEMENTWISE, FAM_N };
+const char* kFamilyNames[FAM_N] = {"gemm", "dequant", "quant", "qr_panel", "rayleigh", "elementwise"};
+
+enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_SIGN, K_INIT };
+
+struct Launch {
+    Kind kind = K_GEMM;
+    int cfg = 0;
+    bool ta = false, tb = false, lds = false;
+    size_t desc_off = 0, prefix_off = 0;   // offsets inside the descriptor region
+    int ndesc = 0, ntiles = 0, max_h = 0;
+    double flops = 0, bytes = 0;
+};
+using Seq = std::vector<Launch>;
+
+struct Side {
+    int p = 0, q = 0;
+    int64_t nqb = 0;
+    // state offsets
+    size_t codes = 0, scales = 0, lam = 0, rcodes = 0, rscales = 0, d = 0;
+    // workspace offsets
+    size_t Vs = 0, Vr = 0, Tmp = 0, Wg = 0, Lt = 0, Pm = 0, Qm = 0, Vb = 0, Yb = 0, Z = 0, rdiag = 0;
+    std::vector<size_t> panel_rows;   // row offset of panel s inside Vb / Yb
+};
+
+struct TimingRec {
+    int family;
+    hipEvent_t e0, e1;
+    double flops, bytes;
+};
+
+}  // namespace
+
+struct shampoo4_ctx_s {
+    shampoo4_config cfg{};
+    int nb = 0;
+    std::vector<shampoo4_shape> shapes;
+    uint8_t* st = nullptr;
+    uint8_t* ws = nullptr;
+    size_t st_bytes = 0, ws_bytes = 0;
+    std::vector<Side> sides;             // 2 per block: L then R
+    std::vector<size_t> X1, X2;          // per block precondition temporaries
+    size_t io_off = 0, flag_off = 0, desc_base = 0;
+    std::vector<uint8_t> blob;           // descriptor region contents
+    int lds_rows = 0;
+    int max_panels = 0;
+
+    Seq deq_stats, deq_root, init_seq;
+    std::vector<Seq> bj_stats, bj_root;
+    Seq stats_x[2], stats_g, power_first[2], power_next;
+    std::vector<Seq> panel, trail, form;
+    Seq sign, ray_gemm, rayleigh, quant, root_d, root_copy;
+    Seq pre[4];
+
+    bool root_v_valid = false;        // workspace Vr holds Bjorck(dequant(root codes))
+    bool root_v_is_stats = false;     // ... and the root codes equal the current codes
+
+    // io staging
+    uint8_t* pinned = nullptr;
+    hipEvent_t ring_ev[kRing] = {};
+    bool ring_used[kRing] = {};
+    int ring_next = 0;
+
+    // timing
+    bool timing = false;
+    std::vector<TimingRec> recs;
+    std::vector<hipEvent_t> ev_pool;
+    size_t ev_used = 0;
+
+    ~shampoo4_ctx_s() {
+        for (auto& e : ring_ev)
+            if (e) (void)hipEventDestroy(e);
+        for (auto& e : ev_pool) (void)hipEventDestroy(e);
+        if (pinned) (void)hipHostFree(pinned);
+    }
+
+    template <class T>
+    T* wsp(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+    template <class T>
+    T* stp(size_t off) const { return reinterpret_cast<T*>(st + off); }
+    float* wsf(size_t off) const { return wsp<float>(off); }
+    float* stf(size_t off) const { return stp<float>(off); }
+
+    // ---- descriptor region ---------------------------------------------------
+    size_t blob_put(const void* data, size_t bytes) {
+        const size_t off = align_up(blob.size());
+        blob.resize(off + align_up(bytes ? bytes : 1), 0);
+        if (bytes) std::memcpy(blob.data() + off, data, bytes);
+        return off;
+    }
+
+    struct GemmItem {
+        GemmDesc d;
+        bool ta, tb;
+    };
+
+    Seq make_gemm(std::vector<GemmItem> items) {
+        Seq out;
+        for (int mode = 0; mode < 4; ++mode) {
+            const bool ta = mode & 1, tb = mode & 2;
+            std::vector<GemmDesc> ds;
+            for (auto& it : items)
+                if (it.ta == ta && it.tb == tb && it.d.M > 0 && it.d.N > 0) ds.push_back(it.d);
+            if (ds.empty()) continue;
+            int maxM = 0;
+            long tiles128 = 0;
+            for (auto& d : ds) {
+                maxM = std::max(maxM, d.M);
+                tiles128 += (long)((d.M + 127) / 128) * ((d.N + 127) / 128);
+            }
+            int cfgsel = maxM <= 32 ? GEMM_32x128 : (tiles128 >= 512 ? GEMM_128x128 : GEMM_64x64);
+            int bm, bn;
+            gemm_tile_dims(cfgsel, &bm, &bn);
+            std::vector<int> prefix;
+            int total = 0;
+            Launch L;
+            for (auto& d : ds) {
+                d.tiles_m = (d.M + bm - 1) / bm;
+                prefix.push_back(total);
+                total += d.tiles_m * ((d.N + bn - 1) / bn);
+                L.flops += 2.0 * d.M * d.N * d.K;
+                L.bytes += 4.0 * ((double)d.M * d.K + (double)d.K * d.N + (double)d.M * d.N *
+                                                                           (d.beta != 0.f ? 2 : 1));
+            }
+            prefix.push_back(total);
+            L.kind = K_GEMM;
+            L.cfg = cfgsel;
+            L.ta = ta;
+            L.tb = tb;
+            L.ndesc = (int)ds.size();
+            L.ntiles = total;
+            L.desc_off = blob_put(ds.data(), ds.size() * sizeof(GemmDesc));
+            L.prefix_off = blob_put(prefix.data(), prefix.size() * sizeof(int));
+            out.push_back(L);
+        }
+        return out;
+    }
+
+    template <class D>
+    Launch make_items(Kind kind, const std::vector<D>& ds, const std::vector<int>& tiles) {
+        Launch L;
+        L.kind = kind;
+        std::vector<int> prefix;
+        int total = 0;
+        for (int t : tiles) {
+            prefix.push_back(total);
+            total += t;
+        }
+        prefix.push_back(total);
+        L.ndesc = (int)ds.size();
+        L.ntiles = total;
+        L.desc_off = blob_put(ds.data(), ds.size() * sizeof(D));
+        L.prefix_off = blob_put(prefix.data(), prefix.size() * sizeof(int));
+        return L;
+    }
+
+    // ---- plan ---------------------------------------------------------------------
+    void layout() {
+        sides.assign(2 * nb, Side{});
+        size_t so = 0, wo = 0;
+        auto st_take = [&](size_t b) { size_t o = so; so += align_up(b ? b : 1); return o; };
+        auto ws_take = [&](size_t b) { size_t o = wo; wo += align_up(b ? b : 1); return o; };
+        io_off = ws_take((size_t)nb * sizeof(IoEntry));
+        flag_off = ws_take(sizeof(uint32_t) * 4);
+        X1.resize(nb);
+        X2.resize(nb);
+        for (int b = 0; b < nb; ++b) {
+            for (int s = 0; s < 2; ++s) {
+                Side& S = sides[2 * b + s];
+                S.p = s == 0 ? shapes[b].m : shapes[b].n;
+                S.q = s == 0 ? shapes[b].n : shapes[b].m;
+                const int64_t p = S.p;
+                S.nqb = (p * p + 63) / 64;
+                S.codes = st_take(S.nqb * 32);
+                S.scales = st_take(S.nqb * 4);
+                S.lam = st_take(p * 4);
+                S.rcodes = st_take(S.nqb * 32);
+                S.rscales = st_take(S.nqb * 4);
+                S.d = st_take(p * 4);
+                const size_t mat = (size_t)p * p * 4;
+                S.Vs = ws_take(mat);
+                S.Vr = ws_take(mat);
+                S.Tmp = ws_take(mat);
+                S.Wg = ws_take(mat);
+                S.Lt = ws_take(mat);
+                S.Pm = ws_take(mat);
+                S.Qm = ws_take(mat);
+                S.panel_rows.clear();
+                size_t rows = 0;
+                for (int c0 = 0; c0 < p; c0 += kPanel) {
+                    S.panel_rows.push_back(rows);
+                    rows += p - c0;
+                }
+                S.Vb = ws_take(rows * kPanel * 4);
+                S.Yb = ws_take(rows * kPanel * 4);
+                S.Z = ws_take((size_t)kPanel * p * 4);
+                S.rdiag = ws_take(p * 4);
+            }
+            X1[b] = ws_take((size_t)shapes[b].m * shapes[b].n * 4);
+            X2[b] = ws_take((size_t)shapes[b].m * shapes[b].n * 4);
+        }
+        st_bytes = so;
+        desc_base = wo;
+        max_panels = 0;
+        for (auto& S : sides) max_panels = std::max(max_panels, (int)S.panel_rows.size());
+    }
+
+    GemmDesc gd(const float* A, int64_t lda, const float* B, int64_t ldb, float* D, int64_t ldd,
+                int M, int N, int K, float alpha = 1.f, float beta = 0.f, const float* C = nullptr,
+                int64_t ldc = 0) const {
+        GemmDesc d;
+        std::memset(&d, 0, sizeof(d));
+        d.A = A; d.B = B; d.C = C; d.D = D;
+        d.lda = lda; d.ldb = ldb; d.ldc = ldc ? ldc : ldd; d.ldd = ldd;
+        d.M = M; d.N = N; d.K = K;
+        d.alpha = alpha; d.beta = beta;
+        d.a_io = d.b_io = d.d_io = -1;
+        return d;
+    }
+
+    // Bjorck chain for one family of buffers; the result lands in `fin`.
+    void build_bjorck(bool root, Seq& deq, std::vector<Seq>& iters) {
+        const int k = cfg.bjorck_iters;
+        std::vector<CodecDesc> cds;
+        std::vector<int> tiles;
+        for (auto& S : sides) {
+            const size_t fin = root ? S.Vr : S.Vs;
+            const size_t start = (k % 2 == 1) ? S.Tmp : fin;
+            CodecDesc c;
+            std::memset(&c, 0, sizeof(c));
+            c.codes_in = stp<uint8_t>(root ? S.rcodes : S.codes);
+            c.scales_in = stf(root ? S.rscales : S.scales);
+            c.x_out = wsf(start);
+            c.n = (int64_t)S.p * S.p;
+            cds.push_back(c);
+            tiles.push_back((int)((S.nqb * 8 + 255) / 256));
+        }
+        Launch L = make_items(K_DEQUANT, cds, tiles);
+        for (auto& S : sides) L.bytes += (double)S.p * S.p * (4.0 + 0.5 + 4.0 / 64);
+        deq = {L};
+        iters.clear();
+        for (int i = 0; i < k; ++i) {
+            std::vector<GemmItem> gram, upd;
+            for (auto& S : sides) {
+                const size_t fin = root ? S.Vr : S.Vs;
+                const size_t start = (k % 2 == 1) ? S.Tmp : fin;
+                const size_t other = (start == S.Tmp) ? fin : S.Tmp;
+                const size_t in = (i % 2 == 0) ? start : other;
+                const size_t out = (i % 2 == 0) ? other : start;
+                const int p = S.p;
+                gram.push_back({gd(wsf(in), p, wsf(in), p, wsf(S.Wg), p, p, p, p), true, false});
+                upd.push_back({gd(wsf(in), p, wsf(S.Wg), p, wsf(out), p, p, p, p, -0.5f, 1.5f, wsf(in), p),
+                               false, false});
+            }
+            Seq s = make_gemm(gram);
+            Seq u = make_gemm(upd);
+            s.insert(s.end(), u.begin(), u.end());
+            iters.push_back(s);
+        }
+    }
+
+    void build() {
+        blob.clear();
+        const float beta = cfg.beta;
+        build_bjorck(false, deq_stats, bj_stats);
+        build_bjorck(true, deq_root, bj_root);
+
+        // statistics: Lt = beta V diag(lam) V^T, then Lt += (1 - beta) G G^T (side R: G^T G)
+        for (int var = 0; var < 2; ++var) {
+            std::vector<GemmItem> xs, pw;
+            for (auto& S : sides) {
+                const int p = S.p;
+                const float* V = wsf(var == 0 ? S.Vs : S.Vr);
+                GemmDesc d = gd(V, p, V, p, wsf(S.Lt), p, p, p, p, beta);
+                d.kscale = stf(S.lam);
+                xs.push_back({d, false, true});
+                pw.push_back({gd(wsf(S.Lt), p, V, p, wsf(S.Pm), p, p, p, p), false, false});
+            }
+            stats_x[var] = make_gemm(xs);
+            power_first[var] = make_gemm(pw);
+        }
+        {
+            std::vector<GemmItem> gs, pn;
+            for (int b = 0; b < nb; ++b) {
+                for (int s = 0; s < 2; ++s) {
+                    Side& S = sides[2 * b + s];
+                    const int p = S.p, q = S.q;
+                    GemmDesc d = gd(nullptr, 0, nullptr, 0, wsf(S.Lt), p, p, p, q, 1.f - beta, 1.f,
+                                    wsf(S.Lt), p);
+                    d.a_io = d.b_io = b;
+                    gs.push_back({d, s == 1, s == 0});
+                    pn.push_back({gd(wsf(S.Lt), p, wsf(S.Qm), p, wsf(S.Pm), p, p, p, p), false, false});
+                }
+            }
+            stats_g = make_gemm(gs);
+            power_next = make_gemm(pn);
+        }
+
+        // Householder QR of P, panel by panel, then explicit Q by backward accumulation
+        panel.assign(max_panels, Seq{});
+        trail.assign(max_panels, Seq{});
+        form.assign(max_panels, Seq{});
+        for (int sidx = 0; sidx < max_panels; ++sidx) {
+            std::vector<PanelDesc> pl_lds, pl_glb;
+            std::vector<int> t_lds, t_glb;
+            int mh_lds = 0, mh_glb = 0;
+            std::vector<GemmItem> t1, t2, f1, f2;
+            for (auto& S : sides) {
+                const int p = S.p;
+                const int c0 = sidx * kPanel;
+                if (c0 >= p) continue;
+                const int nbw = std::min(kPanel, p - c0);
+                const int h = p - c0;
+                PanelDesc pd;
+                std::memset(&pd, 0, sizeof(pd));
+                pd.A = wsf(S.Pm);
+                pd.V = wsf(S.Vb) + S.panel_rows[sidx] * kPanel;
+                pd.Y = wsf(S.Yb) + S.panel_rows[sidx] * kPanel;
+                pd.rdiag = wsf(S.rdiag);
+                pd.ld = p;
+                pd.c0 = c0;
+                pd.h = h;
+                pd.nb = nbw;
+                if (h <= lds_rows) {
+                    pl_lds.push_back(pd); t_lds.push_back(1); mh_lds = std::max(mh_lds, h);
+                } else {
+                    pl_glb.push_back(pd); t_glb.push_back(1); mh_glb = std::max(mh_glb, h);
+                }
+                float* Vp = pd.V;
+                float* Yp = pd.Y;
+                float* Z = wsf(S.Z);
+                const int ntr = p - c0 - nbw;
+                if (ntr > 0) {
+                    float* At = wsf(S.Pm) + (int64_t)c0 * p + c0 + nbw;
+                    t1.push_back({gd(Yp, kPanel, At, p, Z, p, nbw, ntr, h), true, false});
+                    t2.push_back({gd(Vp, kPanel, Z, p, At, p, h, ntr, nbw, -1.f, 1.f, At, p), false, false});
+                }
+                float* Qs = wsf(S.Qm) + (int64_t)c0 * p + c0;
+                f1.push_back({gd(Vp, kPanel, Qs, p, Z, p, nbw, p - c0, h), true, false});
+                f2.push_back({gd(Yp, kPanel, Z, p, Qs, p, h, p - c0, nbw, -1.f, 1.f, Qs, p), false, false});
+            }
+            if (!pl_lds.empty()) {
+                Launch L = make_items(K_PANEL, pl_lds, t_lds);
+                L.lds = true; L.max_h = mh_lds; L.ntiles = (int)pl_lds.size();
+                panel[sidx].push_back(L);
+            }
+            if (!pl_glb.empty()) {
+                Launch L = make_items(K_PANEL, pl_glb, t_glb);
+                L.lds = false; L.max_h = mh_glb; L.ntiles = (int)pl_glb.size();
+                panel[sidx].push_back(L);
+            }
+            Seq a = make_gemm(t1), b = make_gemm(t2);
+            trail[sidx] = a;
+            trail[sidx].insert(trail[sidx].end(), b.begin(), b.end());
+            Seq c = make_gemm(f1), e = make_gemm(f2);
+            form[sidx] = c;
+            form[sidx].insert(form[sidx].end(), e.begin(), e.end());
+        }
+        {
+            std::vector<VecDesc> sg, ry, rt;
+            std::vector<int> tsg, try_, trt;
+            std::vector<GemmItem> yg;
+            std::vector<CodecDesc> qd, cp;
+            std::vector<int> tq, tcp;
+            std::vector<InitDesc> in;
+            std::vector<int> tin;
+            double qbytes = 0;
+            for (auto& S : sides) {
+                const int p = S.p;
+                VecDesc v;
+                std::memset(&v, 0, sizeof(v));
+                v.out = wsf(S.Qm); v.aux = wsf(S.rdiag); v.ld = p; v.p = p;
+                sg.push_back(v);
+                tsg.push_back((int)(((int64_t)p * p + FILL_TILE - 1) / FILL_TILE));
+                yg.push_back({gd(wsf(S.Lt), p, wsf(S.Qm), p, wsf(S.Wg), p, p, p, p), false, false});
+                std::memset(&v, 0, sizeof(v));
+                v.a = wsf(S.Qm); v.b = wsf(S.Wg); v.out = stf(S.lam); v.ld = p; v.p = p;
+                ry.push_back(v);
+                try_.push_back((p + RAYLEIGH_COLS - 1) / RAYLEIGH_COLS);
+                std::memset(&v, 0, sizeof(v));
+                v.a = stf(S.lam); v.out = stf(S.d); v.p = p;
+                rt.push_back(v);
+                trt.push_back((p + 255) / 256);
+                CodecDesc c;
+                std::memset(&c, 0, sizeof(c));
+                c.x_in = wsf(S.Qm); c.codes_out = stp<uint8_t>(S.codes); c.scales_out = stf(S.scales);
+                c.n = (int64_t)p * p;
+                qd.push_back(c);
+                tq.push_back((int)((S.nqb * 16 + 255) / 256));
+                qbytes += (double)p * p * (4.0 + 0.5 + 4.0 / 64);
+                std::memset(&c, 0, sizeof(c));
+                c.codes_in = stp<uint8_t>(S.codes); c.scales_in = stf(S.scales);
+                c.codes_out = stp<uint8_t>(S.rcodes); c.scales_out = stf(S.rscales);
+                c.n = (int64_t)p * p;
+                cp.push_back(c);
+                tcp.push_back((int)((S.nqb * 32 + COPY_TILE - 1) / COPY_TILE));
+                InitDesc id;
+                std::memset(&id, 0, sizeof(id));
+                id.codes = stp<uint8_t>(S.codes); id.scales = stf(S.scales); id.lam = stf(S.lam);
+                id.rcodes = stp<uint8_t>(S.rcodes); id.rscales = stf(S.rscales); id.d = stf(S.d);
+                id.p = p;
+                in.push_back(id);
+                tin.push_back((int)((std::max<int64_t>(S.nqb, p) + 255) / 256));
+            }
+            sign = {make_items(K_SIGN, sg, tsg)};
+            ray_gemm = make_gemm(yg);
+            rayleigh = {make_items(K_RAYLEIGH, ry, try_)};
+            root_d = {make_items(K_ROOT, rt, trt)};
+            Launch Lq = make_items(K_QUANT, qd, tq);
+            Lq.bytes = qbytes;
+            quant = {Lq};
+            root_copy = {make_items(K_COPY, cp, tcp)};
+            init_seq = {make_items(K_INIT, in, tin)};
+        }
+        // precondition: X1 = diag(d_L) V_L^T G; X2 = X1 V_R diag(d_R); X1 = V_L X2; P = X1 V_R^T
+        {
+            std::vector<GemmItem> p1, p2, p3, p4;
+            for (int b = 0; b < nb; ++b) {
+                const Side& L = sides[2 * b];
+                const Side& R = sides[2 * b + 1];
+                const int m = shapes[b].m, n = shapes[b].n;
+                GemmDesc d1 = gd(wsf(L.Vr), m, nullptr, 0, wsf(X1[b]), n, m, n, m);
+                d1.b_io = b;
+                d1.rscale = stf(L.d);
+                p1.push_back({d1, true, false});
+                GemmDesc d2 = gd(wsf(X1[b]), n, wsf(R.Vr), n, wsf(X2[b]), n, m, n, n);
+                d2.cscale = stf(R.d);
+                p2.push_back({d2, false, false});
+                p3.push_back({gd(wsf(L.Vr), m, wsf(X2[b]), n, wsf(X1[b]), n, m, n, m), false, false});
+                GemmDesc d4 = gd(wsf(X1[b]), n, wsf(R.Vr), n, nullptr, 0, m, n, n);
+                d4.d_io = b;
+                p4.push_back({d4, false, true});
+            }
+            pre[0] = make_gemm(p1);
+            pre[1] = make_gemm(p2);
+            pre[2] = make_gemm(p3);
+            pre[3] = make_gemm(p4);
+        }
+    }
+
+    // ---- execution ------------------------------------------------------------
+    hipError_t run(const Launch& L, hipStream_t s) {
+        const uint8_t* base = ws + desc_base;
+        const int* prefix = reinterpret_cast<const int*>(base + L.prefix_off);
+        const IoEntry* io = wsp<IoEntry>(io_off);
+        uint32_t* flag = wsp<uint32_t>(flag_off);
+        TimingRec rec{};
+        if (timing) {
+            rec.e0 = next_event();
+            rec.e1 = next_event();
+            (void)hipEventRecord(rec.e0, s);
+        }
+        hipError_t e = hipSuccess;
+        int fam = FAM_ELEMENTWISE;
+        switch (L.kind) {
+            case K_GEMM:
+                fam = FAM_GEMM;
+                e = launch_gemm(L.cfg, L.ta, L.tb, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
+                                prefix, L.ndesc, L.ntiles, io, s);
+                break;
+            case K_DEQUANT:
+                fam = FAM_DEQUANT;
+                e = launch_dequant(reinterpret_cast<const CodecDesc*>(base + L.desc_off), prefix, L.ndesc,
+                                   L.ntiles, s);
+                break;
+            case K_QUANT:
+                fam = FAM_QUANT;
+                e = launch_quant(reinterpret_cast<const CodecDesc*>(base + L.desc_off), prefix, L.ndesc,
+                                 L.ntiles, flag, s);
+                break;
+            case K_COPY:
+                e = launch_codec_copy(reinterpret_cast<const CodecDesc*>(base + L.desc_off), prefix,
+                                      L.ndesc, L.ntiles, s);
+                break;
+            case K_PANEL:
+                fam = FAM_PANEL;
+                e = launch_panel(L.lds, reinterpret_cast<const PanelDesc*>(base + L.desc_off), L.ndesc,
+                                 L.max_h, s);
+                break;
+            case K_RAYLEIGH:
+                fam = FAM_RAYLEIGH;
+                e = launch_rayleigh(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix, L.ndesc,
+                                    L.ntiles, flag, s);
+                break;
+            case K_ROOT:
+                e = launch_root_scaling(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix,
+                                        L.ndesc, L.ntiles, cfg.eps, flag, s);
+                break;
+            case K_SIGN:
+                e = launch_sign_diag(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix, L.ndesc,
+                                     L.ntiles, s);
+                break;
+            case K_INIT:
+                e = launch_identity_state(reinterpret_cast<const InitDesc*>(base + L.desc_off), prefix,
+                                          L.ndesc, L.ntiles, s);
+                break;
+        }
+        if (timing) {
+            (void)hipEventRecord(rec.e1, s);
+            rec.family = fam;
+            rec.flops = L.flops;
+            rec.bytes = L.bytes;
+            recs.push_back(rec);
+        }
+        return e;
+    }
+
+    hipError_t run(const Seq& seq, hipStream_t s) {
+        for (const auto& L : seq) {
+            hipError_t e = run(L, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+
+    hipEvent_t next_event() {
+        if (ev_used == ev_pool.size()) {
+            hipEvent_t e;
+            (void)hipEventCreate(&e);
+            ev_pool.push_back(e);
+        }
+        return ev_pool[ev_used++];
+    }
+
+    hipError_t upload_io(const shampoo4_io* io, hipStream_t s) {
+        const size_t bytes = (size_t)nb * sizeof(IoEntry);
+        const int slot = ring_next;
+        ring_next = (ring_next + 1) % kRing;
+        if (ring_used[slot]) {
+            hipError_t e = hipEventSynchronize(ring_ev[slot]);
+            if (e != hipSuccess) return e;
+        }
+        uint8_t* dst = pinned + (size_t)slot * align_up(bytes);
+        std::memcpy(dst, io, bytes);
+        hipError_t e = hipMemcpyAsync(ws + io_off, dst, bytes, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return e;
+        ring_used[slot] = true;
+        return hipEventRecord(ring_ev[slot], s);
+    }
+
+    hipError_t root_eigenvectors(hipStream_t s) {
+        hipError_t e = run(deq_root, s);
+        for (auto& it : bj_root)
+            if (e == hipSuccess) e = run(it, s);
+        return e;
+    }
+};
+
+namespace {
+
+shampoo4_status validate_cfg(const shampoo4_config* cfg) {
+    if (!cfg) return SHAMPOO4_EINVAL;
+    if (!(cfg->beta >= 0.f && cfg->beta <= 1.f)) return SHAMPOO4_EINVAL;
+    if (!(cfg->eps >= 0.f) || !std::isfinite(cfg->eps)) return SHAMPOO4_EINVAL;
+    if (cfg->qblock != 64) return SHAMPOO4_EINVAL;
+    if (cfg->bjorck_iters < 0 || cfg->bjorck_iters > 16) return SHAMPOO4_EINVAL;
+    if (cfg->power_iters < 1 || cfg->power_iters > 8) return SHAMPOO4_EINVAL;
+    if (cfg->flags & ~(SHAMPOO4_FLAG_ROOT_CACHE | SHAMPOO4_FLAG_KEEP_STATE)) return SHAMPOO4_EINVAL;
+    return SHAMPOO4_OK;
+}
+
+shampoo4_status validate_shapes(int32_t nblocks, const shampoo4_shape* shapes) {
+    if (nblocks < 1 || nblocks > (1 << 20) || !shapes) return SHAMPOO4_EINVAL;
+    for (int b = 0; b < nblocks; ++b)
+        if (shapes[b].m < 1 || shapes[b].n < 1 || shapes[b].m > kMaxDim || shapes[b].n > kMaxDim)
+            return SHAMPOO4_ESHAPE;
+    return SHAMPOO4_OK;
+}
+
+shampoo4_status validate_io(const shampoo4_ctx_s* c, const shampoo4_io* io, bool need_p) {
+    if (!io) return SHAMPOO4_EINVAL;
+    for (int b = 0; b < c->nb; ++b) {
+        if (!io[b].G) return SHAMPOO4_EINVAL;
+        if (io[b].ldg < c->shapes[b].n) return SHAMPOO4_ESHAPE;
+        if (need_p) {
+            if (!io[b].P) return SHAMPOO4_EINVAL;
+            if (io[b].ldp < c->shapes[b].n) return SHAMPOO4_ESHAPE;
+        }
+    }
+    return SHAMPOO4_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+std::unique_ptr<shampoo4_ctx_s> make_plan(const shampoo4_config* cfg, int32_t nblocks,
+                                          const shampoo4_shape* shapes) {
+    auto c = std::make_unique<shampoo4_ctx_s>();
+    c->cfg = *cfg;
+    c->nb = nblocks;
+    c->shapes.assign(shapes, shapes + nblocks);
+    c->lds_rows = PANEL_LDS_MAX_ROWS;
+    c->layout();
+    return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t shampoo4_abi_version(void) { return SHAMPOO4_ABI_VERSION; }
+
+const char* shampoo4_strerror(shampoo4_status s) {
+    switch (s) {
+        case SHAMPOO4_OK: return "ok";
+        case SHAMPOO4_EINVAL: return "invalid argument";
+        case SHAMPOO4_ESHAPE: return "invalid shape or leading dimension";
+        case SHAMPOO4_EALIGN: return "buffer not 256-byte aligned";
+        case SHAMPOO4_ESMALLBUF: return "buffer smaller than planned";
+        case SHAMPOO4_EHIP: return "HIP runtime error";
+        case SHAMPOO4_ENONFINITE: return "non-finite value seen on device";
+    }
+    return "unknown status";
+}
+
+shampoo4_status shampoo4_plan(const shampoo4_config* cfg, int32_t nblocks, const shampoo4_shape* shapes,
+                              size_t* state_bytes, size_t* workspace_bytes) {
+    shampoo4_status st = validate_cfg(cfg);
+    if (st != SHAMPOO4_OK) return st;
+    if ((st = validate_shapes(nblocks, shapes)) != SHAMPOO4_OK) return st;
+    if (!state_bytes || !workspace_bytes) return SHAMPOO4_EINVAL;
+    auto c = make_plan(cfg, nblocks, shapes);
+    c->build();   // null bases: only the sizes matter
+    *state_bytes = c->st_bytes;
+    *workspace_bytes = c->desc_base + align_up(c->blob.size());
+    return SHAMPOO4_OK;
+}
+
+shampoo4_status shampoo4_init(const shampoo4_config* cfg, int32_t nblocks, const shampoo4_shape* shapes,
+                              void* state, size_t state_bytes, void* workspace, size_t workspace_bytes,
+                              void* stream, shampoo4_ctx* out) {
+    shampoo4_status st = validate_cfg(cfg);
+    if (st != SHAMPOO4_OK) return st;
+    if ((st = validate_shapes(nblocks, shapes)) != SHAMPOO4_OK) return st;
+    if (!state || !workspace || !out) return SHAMPOO4_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(state) % kAlign) || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
+        return SHAMPOO4_EALIGN;
+    auto c = make_plan(cfg, nblocks, shapes);
+    {   // panels staged in LDS up to what one workgroup may allocate
+        int dev = 0, lds = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return SHAMPOO4_EHIP;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return SHAMPOO4_EHIP;
+        const int rows = (int)(((size_t)lds - panel_lds_bytes(false, 0)) / (33 * sizeof(float)));
+        c->lds_rows = std::max(0, std::min(PANEL_LDS_MAX_ROWS, rows));
+    }
+    c->st = static_cast<uint8_t*>(state);
+    c->ws = static_cast<uint8_t*>(workspace);
+    c->build();
+    const size_t need_ws = c->desc_base + align_up(c->blob.size());
+    if (state_bytes < c->st_bytes || workspace_bytes < need_ws) return SHAMPOO4_ESMALLBUF;
+    c->ws_bytes = need_ws;
+    hipStream_t s = as_stream(stream);
+    if (hipHostMalloc(reinterpret_cast<void**>(&c->pinned), kRing * align_up((size_t)nblocks * sizeof(IoEntry)),
+                      hipHostMallocDefault) != hipSuccess)
+        return SHAMPOO4_EHIP;
+    for (auto& e : c->ring_ev)
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return SHAMPOO4_EHIP;
+    if (hipMemcpyAsync(c->ws + c->desc_base, c->blob.data(), c->blob.size(), hipMemcpyHostToDevice, s) !=
+        hipSuccess)
+        return SHAMPOO4_EHIP;
+    const uint32_t zero[4] = {0, 0, 0, 0};
+    if (hipMemcpyAsync(c->ws + c->flag_off, zero, sizeof(zero), hipMemcpyHostToDevice, s) != hipSuccess)
+        return SHAMPOO4_EHIP;
+    if (!(cfg->flags & SHAMPOO4_FLAG_KEEP_STATE)) {
+        if (c->run(c->init_seq, s) != hipSuccess) return SHAMPOO4_EHIP;
+    }
+    if (cfg->flags & SHAMPOO4_FLAG_ROOT_CACHE) {
+        if (c->root_eigenvectors(s) != hipSuccess) return SHAMPOO4_EHIP;
+        c->root_v_valid = true;
+        c->root_v_is_stats = !(cfg->flags & SHAMPOO4_FLAG_KEEP_STATE);
+    }
+    if (hipStreamSynchronize(s) != hipSuccess) return SHAMPOO4_EHIP;
+    *out = c.release();
+    return SHAMPOO4_OK;
+}
+
+shampoo4_status shampoo4_update_stats(shampoo4_ctx c, const shampoo4_io* io, void* stream) {
+    if (!c) return SHAMPOO4_EINVAL;
+    shampoo4_status st = validate_io(c, io, false);
+    if (st != SHAMPOO4_OK) return st;
+    hipStream_t s = as_stream(stream);
+    if (c->upload_io(io, s) != hipSuccess) return SHAMPOO4_EHIP;
+    const bool reuse = (c->cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) && c->root_v_valid && c->root_v_is_stats;
+    const int var = reuse ? 1 : 0;
+    hipError_t e = hipSuccess;
+    if (!reuse) {
+        e = c->run(c->deq_stats, s);
+        for (auto& it : c->bj_stats)
+            if (e == hipSuccess) e = c->run(it, s);
+    }
+    if (e == hipSuccess) e = c->run(c->stats_x[var], s);
+    if (e == hipSuccess) e = c->run(c->stats_g, s);
+    for (int it = 0; it < c->cfg.power_iters && e == hipSuccess; ++it) {
+        e = c->run(it == 0 ? c->power_first[var] : c->power_next, s);
+        for (int p = 0; p < c->max_panels && e == hipSuccess; ++p) {
+            e = c->run(c->panel[p], s);
+            if (e == hipSuccess) e = c->run(c->trail[p], s);
+        }
+        if (e == hipSuccess) e = c->run(c->sign, s);
+        for (int p = c->max_panels - 1; p >= 0 && e == hipSuccess; --p) e = c->run(c->form[p], s);
+    }
+    if (e == hipSuccess) e = c->run(c->ray_gemm, s);
+    if (e == hipSuccess) e = c->run(c->rayleigh, s);
+    if (e == hipSuccess) e = c->run(c->quant, s);
+    c->root_v_is_stats = false;
+    return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+}
+
+shampoo4_status shampoo4_refresh_root(shampoo4_ctx c, void* stream) {
+    if (!c) return SHAMPOO4_EINVAL;
+    hipStream_t s = as_stream(stream);
+    hipError_t e = c->run(c->root_d, s);
+    if (e == hipSuccess) e = c->run(c->root_copy, s);
+    if (e == hipSuccess && (c->cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE)) {
+        e = c->root_eigenvectors(s);
+        c->root_v_valid = (e == hipSuccess);
+        c->root_v_is_stats = (e == hipSuccess);
+    } else {
+        c->root_v_valid = false;
+    }
+    return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+}
+
+shampoo4_status shampoo4_precondition(shampoo4_ctx c, const shampoo4_io* io, void* stream) {
+    if (!c) return SHAMPOO4_EINVAL;
+    shampoo4_status st = validate_io(c, io, true);
+    if (st != SHAMPOO4_OK) return st;
+    hipStream_t s = as_stream(stream);
+    if (c->upload_io(io, s) != hipSuccess) return SHAMPOO4_EHIP;
+    hipError_t e = hipSuccess;
+    if (!((c->cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) && c->root_v_valid)) {
+        e = c->root_eigenvectors(s);
+        c->root_v_is_stats = false;
+    }
+    for (int i = 0; i < 4 && e == hipSuccess; ++i) e = c->run(c->pre[i], s);
+    return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+}
+
+shampoo4_status shampoo4_check(shampoo4_ctx c, void* stream, uint32_t* device_flags) {
+    if (!c) return SHAMPOO4_EINVAL;
+    hipStream_t s = as_stream(stream);
+    uint32_t f = 0;
+    if (hipStreamSynchronize(s) != hipSuccess) return SHAMPOO4_EHIP;
+    if (hipMemcpy(&f, c->ws + c->flag_off, sizeof(f), hipMemcpyDeviceToHost) != hipSuccess)
+        return SHAMPOO4_EHIP;
+    if (device_flags) *device_flags = f;
+    if (f) {
+        const uint32_t zero = 0;
+        if (hipMemcpy(c->ws + c->flag_off, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess)
+            return SHAMPOO4_EHIP;
+        return SHAMPOO4_ENONFINITE;
+    }
+    return SHAMPOO4_OK;
+}
+
+shampoo4_status shampoo4_destroy(shampoo4_ctx c) {
+    if (!c) return SHAMPOO4_EINVAL;
+    for (int i = 0; i < kRing; ++i)
+        if (c->ring_used[i]) (void)hipEventSynchronize(c->ring_ev[i]);
+    delete c;
+    return SHAMPOO4_OK;
+}
+
+shampoo4_status shampoo4_layout(shampoo4_ctx c, int32_t block, int32_t side, shampoo4_buffer which,
+                                size_t* offset, size_t* bytes) {
+    if (!c || !offset || !bytes) return SHAMPOO4_EINVAL;
+    if (block < 0 || block >= c->nb || side < 0 || side > 1) return SHAMPOO4_EINVAL;
+    const Side& S = c->sides[2 * block + side];
+    const size_t p = S.p;
+    const size_t mat = p * p * 4;
+    switch (which) {
+        case SHAMPOO4_BUF_CODES: *offset = S.codes; *bytes = S.nqb * 32; break;
+        case SHAMPOO4_BUF_SCALES: *offset = S.scales; *bytes = S.nqb * 4; break;
+        case SHAMPOO4_BUF_EIG: *offset = S.lam; *bytes = p * 4; break;
+        case SHAMPOO4_BUF_ROOT_CODES: *offset = S.rcodes; *bytes = S.nqb * 32; break;
+        case SHAMPOO4_BUF_ROOT_SCALES: *offset = S.rscales; *bytes = S.nqb * 4; break;
+        case SHAMPOO4_BUF_ROOT_D: *offset = S.d; *bytes = p * 4; break;
+        case SHAMPOO4_BUF_V: *offset = S.Vs; *bytes = mat; break;
+        case SHAMPOO4_BUF_STAT: *offset = S.Lt; *bytes = mat; break;
+        case SHAMPOO4_BUF_Q: *offset = S.Qm; *bytes = mat; break;
+        case SHAMPOO4_BUF_ROOT_V: *offset = S.Vr; *bytes = mat; break;
+        default: return SHAMPOO4_EINVAL;
+    }
+    return SHAMPOO4_OK;
+}
+
+shampoo4_status shampoo4_codebook(float levels[16], float midpoints[15]) {
+    if (!levels || !midpoints) return SHAMPOO4_EINVAL;
+    host_codebook(levels, midpoints);
+    return SHAMPOO4_OK;
+}
+
+shampoo4_status shampoo4_quantize(const float* x, int64_t n, int32_t qblock, uint8_t* codes, float* scales,
+                                  void* stream) {
+    if (qblock != 64 || n < 0) return SHAMPOO4_EINVAL;
+    if (n == 0) return SHAMPOO4_OK;
+    if (!x || !codes || !scales) return SHAMPOO4_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(codes) & 1) || (reinterpret_cast<uintptr_t>(scales) & 3) ||
+        (reinterpret_cast<uintptr_t>(x) & 3))
+        return SHAMPOO4_EALIGN;
+    CodecDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.x_in = x; d.codes_out = codes; d.scales_out = scales; d.n = n;
+    return launch_quant_single(d, as_stream(stream)) == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+}
+
+shampoo4_status shampoo4_dequantize(const uint8_t* codes, const float* scales, int64_t n, int32_t qblock,
+                                    float* x, void* stream) {
+    if (qblock != 64 || n < 0) return SHAMPOO4_EINVAL;
+    if (n == 0) return SHAMPOO4_OK;
+    if (!x || !codes || !scales) return SHAMPOO4_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(codes) & 3) || (reinterpret_cast<uintptr_t>(scales) & 3) ||
+        (reinterpret_cast<uintptr_t>(x) & 3))
+        return SHAMPOO4_EALIGN;
+    CodecDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.codes_in = codes; d.scales_in = scales; d.x_out = x; d.n = n;
+    return launch_dequant_single(d, as_stream(stream)) == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+}
+
+size_t shampoo4_gemm_workspace_bytes(int32_t count) {
+    return align_up((size_t)std::max(count, 0) * sizeof(GemmDesc)) + align_up(((size_t)std::max(count, 0) + 1) * 4);
+}
+
+shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t transB, const int32_t* M,
+                                      const int32_t* N, const int32_t* K, float alpha, const float* const* A,
+                                      const int64_t* lda, const float* const* B, const int64_t* ldb, float beta,
+                                      const float* const* C, const int64_t* ldc, float* const* D,
+                                      const int64_t* ldd, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+    if (count < 0) return SHAMPOO4_EINVAL;
+    if (count == 0) return SHAMPOO4_OK;
+    if (!M || !N || !K || !A || !lda || !B || !ldb || !D || !ldd || !workspace) return SHAMPOO4_EINVAL;
+    if (beta != 0.f && (!C || !ldc)) return SHAMPOO4_EINVAL;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return SHAMPOO4_EALIGN;
+    if (workspace_bytes < shampoo4_gemm_workspace_bytes(count)) return SHAMPOO4_ESMALLBUF;
+    shampoo4_ctx_s tmp;
+    tmp.ws = static_cast<uint8_t*>(workspace);
+    std::vector<shampoo4_ctx_s::GemmItem> items;
+    for (int i = 0; i < count; ++i) {
+        if (M[i] < 0 || N[i] < 0 || K[i] < 0) return SHAMPOO4_ESHAPE;
+        const int64_t acols = transA ? M[i] : K[i];
+        const int64_t bcols = transB ? K[i] : N[i];
+        if (!A[i] || !B[i] || !D[i]) return SHAMPOO4_EINVAL;
+        if (lda[i] < std::max<int64_t>(acols, 1) || ldb[i] < std::max<int64_t>(bcols, 1) ||
+            ldd[i] < std::max<int32_t>(N[i], 1))
+            return SHAMPOO4_ESHAPE;
+        if (beta != 0.f && (!C[i] || ldc[i] < std::max<int32_t>(N[i], 1))) return SHAMPOO4_ESHAPE;
+        GemmDesc d = tmp.gd(A[i], lda[i], B[i], ldb[i], D[i], ldd[i], M[i], N[i], K[i], alpha, beta,
+                            beta != 0.f ? C[i] : nullptr, beta != 0.f ? ldc[i] : 0);
+        items.push_back({d, transA != 0, transB != 0});
+    }
+    Seq seq = tmp.make_gemm(items);
+    if (seq.empty()) return SHAMPOO4_OK;
+    const Launch& L = seq[0];
+    hipStream_t s = as_stream(stream);
+    // the descriptors and prefix sit at offsets 0 and align_up(count * 128) of the blob
+    if (tmp.blob.size() > workspace_bytes) return SHAMPOO4_ESMALLBUF;
+    if (hipMemcpyAsync(workspace, tmp.blob.data(), tmp.blob.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+        return SHAMPOO4_EHIP;
+    const uint8_t* base = static_cast<const uint8_t*>(workspace);
+    hipError_t e = launch_gemm(L.cfg, L.ta, L.tb, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
+                               reinterpret_cast<const int*>(base + L.prefix_off), L.ndesc, L.ntiles, nullptr, s);
+    return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+}
+
+shampoo4_status shampoo4_timing(shampoo4_ctx c, int32_t enable) {
+    if (!c) return SHAMPOO4_EINVAL;
+    c->timing = enable != 0;
+    c->recs.clear();
+    c->ev_used = 0;
+    return SHAMPOO4_OK;
+}
+
+shampoo4_status shampoo4_timing_report(shampoo4_ctx c, int32_t* count, const char** names, int64_t* launches,
+                                       double* total_ms, double* flops, double* bytes) {
+    if (!c || !count) return SHAMPOO4_EINVAL;
+    if (*count < FAM_N || !names || !launches || !total_ms || !flops || !bytes) {
+        *count = FAM_N;
+        return SHAMPOO4_EINVAL;
+    }
+    for (int f = 0; f < FAM_N; ++f) {
+        names[f] = kFamilyNames[f];
+        launches[f] = 0;
+        total_ms[f] = flops[f] = bytes[f] = 0;
+    }
+    for (auto& r : c->recs) {
+        if (hipEventSynchronize(r.e1) != hipSuccess) return SHAMPOO4_EHIP;
+        float ms = 0;
+        if (hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) return SHAMPOO4_EHIP;
+        launches[r.family] += 1;
+        total_ms[r.family] += ms;
+        flops[r.family] += r.flops;
+        bytes[r.family] += r.bytes;
+    }
+    *count = FAM_N;
+    return SHAMPOO4_OK;
+}
+
+}  // extern "C"

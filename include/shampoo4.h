@@ -1,0 +1,213 @@
+/*
+ * shampoo4.h -- C ABI of the 4-bit Shampoo preconditioner step for MI355X (gfx950).
+ *
+ * The method ("4-bit Shampoo for Memory-Efficient Network Training", abstract;
+ * "Shampoo -- Second-Order Optimizer", sections "Kronecker factorization",
+ * "Where the fourth root comes from", "Rotation, not just rescaling",
+ * "Computing the inverse fourth root", "The cost dial", "Pitfalls"):
+ * for every weight block G:[m,n] two Kronecker factors L:[m,m] and R:[n,n] are
+ * kept, each as a 4-bit eigenvector matrix U (block-wise linear-square codes,
+ * one fp32 absmax scale per 64 consecutive elements of U flattened row-major,
+ * eigenvectors in the columns) plus fp32 eigenvalues.  A step
+ *
+ *   update_stats(G):  V = Bjorck^k(dequant(U))  (V <- 1.5 V - 0.5 V V^T V)
+ *                     L~ = beta V diag(lam) V^T + (1 - beta) G G^T
+ *                     Q R = L~ V (Householder, diag R >= 0)
+ *                     lam_i = max(q_i^T L~ q_i, 0),  U <- quant(Q)
+ *                     (side R: G^T in place of G)
+ *   refresh_root():   d_i = (lam_i + eps)^(-1/4), root codes <- codes
+ *   precondition(G):  V^r = Bjorck^k(dequant(root codes)) per side,
+ *                     P = V^r_L diag(d_L) V^r_L^T G V^r_R diag(d_R) V^r_R^T
+ *
+ * Conventions shared by every entry point:
+ *  - All matrices are fp32, row-major, with an explicit leading dimension
+ *    (elements, >= number of columns).  G and P of a block may be strided
+ *    views into a larger weight matrix.
+ *  - Pointers named "device" are HIP device pointers; everything else is
+ *    host memory.  The caller owns all device memory (state and workspace
+ *    buffers, G, P): the library never allocates or frees device memory.
+ *    The only memory the library allocates is host memory inside the context
+ *    (descriptor tables and a small pinned staging ring), freed by
+ *    shampoo4_destroy.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously on it; unless stated otherwise a call
+ *    returns without waiting for the device.  Calls on one context must be
+ *    ordered on one stream (or externally synchronized): they share the
+ *    context's workspace.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    failed validation returns an error and enqueues nothing.
+ *  - A context is not thread-safe; separate contexts are independent.
+ */
+#ifndef SHAMPOO4_H
+#define SHAMPOO4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SHAMPOO4_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SHAMPOO4_API __attribute__((visibility("default")))
+#else
+#define SHAMPOO4_API
+#endif
+
+typedef struct shampoo4_ctx_s* shampoo4_ctx;
+
+typedef enum {
+    SHAMPOO4_OK = 0,
+    SHAMPOO4_EINVAL = 1,      /* null pointer, bad config value, bad index */
+    SHAMPOO4_ESHAPE = 2,      /* a block dimension outside [1, 8192], or ld < cols */
+    SHAMPOO4_EALIGN = 3,      /* a state/workspace buffer not 256-byte aligned */
+    SHAMPOO4_ESMALLBUF = 4,   /* buffer smaller than shampoo4_plan reported */
+    SHAMPOO4_EHIP = 5,        /* a HIP runtime call or kernel launch failed */
+    SHAMPOO4_ENONFINITE = 6   /* device saw NaN/Inf (reported by shampoo4_check) */
+} shampoo4_status;
+
+/* Config flags. */
+#define SHAMPOO4_FLAG_ROOT_CACHE 1u   /* keep the rectified fp32 root eigenvectors in the
+                                         workspace between calls: refresh_root computes them
+                                         once, precondition reuses them, and an update_stats
+                                         that directly follows a refresh_root reuses them as
+                                         its own rectified eigenvectors (identical values).
+                                         Without the flag precondition recomputes them. */
+#define SHAMPOO4_FLAG_KEEP_STATE 2u   /* shampoo4_init: do not write the initial state;
+                                         the state buffer already holds a saved state. */
+
+typedef struct {
+    int32_t m, n;             /* block shape: G is [m, n]; side L has order m, side R order n */
+} shampoo4_shape;
+
+typedef struct {
+    float beta;               /* EMA factor of the statistics, in [0, 1] */
+    float eps;                /* damping added to the eigenvalues before the -1/4 power, >= 0 */
+    int32_t qblock;           /* elements per quantization block; only 64 is supported */
+    int32_t bjorck_iters;     /* Bjorck iterations k, 0..16 */
+    int32_t power_iters;      /* subspace-iteration steps per update, 1..8 */
+    uint32_t flags;           /* SHAMPOO4_FLAG_* */
+} shampoo4_config;
+
+typedef struct {
+    const float* G;           /* device, [m, n] gradient of the block, row-major */
+    int64_t ldg;              /* leading dimension of G (elements), >= n */
+    float* P;                 /* device, [m, n] output (precondition only; may be NULL for
+                                 update_stats), row-major; must not overlap G */
+    int64_t ldp;              /* leading dimension of P (elements), >= n */
+} shampoo4_io;
+
+/* Which buffer shampoo4_layout describes. */
+typedef enum {
+    SHAMPOO4_BUF_CODES = 0,       /* state: uint8 [nqb*32] packed codes of U */
+    SHAMPOO4_BUF_SCALES = 1,      /* state: fp32 [nqb] block scales of U */
+    SHAMPOO4_BUF_EIG = 2,         /* state: fp32 [p] eigenvalues lam */
+    SHAMPOO4_BUF_ROOT_CODES = 3,  /* state: uint8 [nqb*32] root codes */
+    SHAMPOO4_BUF_ROOT_SCALES = 4, /* state: fp32 [nqb] root scales */
+    SHAMPOO4_BUF_ROOT_D = 5,      /* state: fp32 [p] root scaling d */
+    SHAMPOO4_BUF_V = 16,          /* workspace: fp32 [p,p] rectified eigenvectors of the
+                                     last update_stats */
+    SHAMPOO4_BUF_STAT = 17,       /* workspace: fp32 [p,p] statistic L~ of the last update */
+    SHAMPOO4_BUF_Q = 18,          /* workspace: fp32 [p,p] refreshed eigenvectors Q */
+    SHAMPOO4_BUF_ROOT_V = 19      /* workspace: fp32 [p,p] rectified root eigenvectors of
+                                     the last refresh_root (ROOT_CACHE) or precondition */
+} shampoo4_buffer;
+
+/* ABI version of the loaded library (SHAMPOO4_ABI_VERSION). */
+SHAMPOO4_API int32_t shampoo4_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+SHAMPOO4_API const char* shampoo4_strerror(shampoo4_status status);
+
+/* Sizes of the caller-owned buffers for `nblocks` blocks of `shapes` (host array).
+ * state_bytes: the optimizer state (codes, scales, eigenvalues, root; serializable).
+ * workspace_bytes: descriptor tables, the optional root cache and temporaries.
+ * Host only; no HIP call. */
+SHAMPOO4_API shampoo4_status shampoo4_plan(const shampoo4_config* cfg, int32_t nblocks,
+                              const shampoo4_shape* shapes,
+                              size_t* state_bytes, size_t* workspace_bytes);
+
+/* Create a context over caller-owned device buffers (both 256-byte aligned and at
+ * least as large as shampoo4_plan reports) and, unless SHAMPOO4_FLAG_KEEP_STATE is
+ * set, enqueue the initial state: U = I, lam = 0, root = (I, d = 1).  Enqueues the
+ * descriptor tables into the workspace and waits for that copy (the only call that
+ * synchronizes with the stream).  The buffers must outlive the context. */
+SHAMPOO4_API shampoo4_status shampoo4_init(const shampoo4_config* cfg, int32_t nblocks,
+                              const shampoo4_shape* shapes,
+                              void* state, size_t state_bytes,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream, shampoo4_ctx* out);
+
+/* One statistics update of every block: io is a host array of nblocks entries
+ * (only G/ldg are read). */
+SHAMPOO4_API shampoo4_status shampoo4_update_stats(shampoo4_ctx ctx, const shampoo4_io* io, void* stream);
+
+/* Root refresh of every block: d = (lam + eps)^(-1/4), root codes <- codes. */
+SHAMPOO4_API shampoo4_status shampoo4_refresh_root(shampoo4_ctx ctx, void* stream);
+
+/* Preconditioned direction of every block into io[b].P. */
+SHAMPOO4_API shampoo4_status shampoo4_precondition(shampoo4_ctx ctx, const shampoo4_io* io, void* stream);
+
+/* Wait for `stream`, then report and clear the device non-finite flag
+ * (raised when a quantized block or an eigenvalue is NaN/Inf).  *device_flags
+ * (may be NULL) receives the raw flag word.  Returns SHAMPOO4_ENONFINITE if set. */
+SHAMPOO4_API shampoo4_status shampoo4_check(shampoo4_ctx ctx, void* stream, uint32_t* device_flags);
+
+/* Destroy a context (host memory only; device buffers stay the caller's). */
+SHAMPOO4_API shampoo4_status shampoo4_destroy(shampoo4_ctx ctx);
+
+/* Byte offset and size of one per-side buffer inside the state (state buffers,
+ * values < 16) or the workspace (values >= 16).  side: 0 = L, 1 = R.  Host only. */
+SHAMPOO4_API shampoo4_status shampoo4_layout(shampoo4_ctx ctx, int32_t block, int32_t side,
+                                shampoo4_buffer which, size_t* offset, size_t* bytes);
+
+/* Codec in isolation ("4-bit Shampoo ..." abstract: block-wise linear-square 4-bit
+ * quantization).  x: device fp32 [n]; codes: device uint8 [ceil(n/64)*32];
+ * scales: device fp32 [ceil(n/64)].  Blocks are 64 consecutive elements, the last
+ * one zero-padded; element 2i goes to the low nibble of byte i.  qblock must be 64.
+ * Non-finite input raises the device flag of no context; the codes are then undefined. */
+SHAMPOO4_API shampoo4_status shampoo4_quantize(const float* x, int64_t n, int32_t qblock,
+                                  uint8_t* codes, float* scales, void* stream);
+SHAMPOO4_API shampoo4_status shampoo4_dequantize(const uint8_t* codes, const float* scales, int64_t n,
+                                    int32_t qblock, float* x, void* stream);
+
+/* The float32 codebook the kernels use (host copy): 16 levels (ascending) and the
+ * 15 decision midpoints.  Host only. */
+SHAMPOO4_API shampoo4_status shampoo4_codebook(float levels[16], float midpoints[15]);
+
+/* Device workspace bytes shampoo4_gemm_batched needs for `count` products. */
+SHAMPOO4_API size_t shampoo4_gemm_workspace_bytes(int32_t count);
+
+/* Batched fp32 MFMA GEMM in isolation: for each i < count,
+ *   D_i = alpha * op(A_i) op(B_i) + beta * C_i     (op = transpose when trans* != 0)
+ * with op(A_i) [M,K], op(B_i) [K,N], C_i and D_i [M,N] row-major.  All pointer arrays
+ * are host arrays of device pointers; C may be NULL when beta == 0.  Used to test and
+ * time the matrix-product kernel every stage of the step runs on.  `workspace` is a
+ * 256-byte aligned device buffer of at least shampoo4_gemm_workspace_bytes(count)
+ * bytes that receives the descriptors (one host-to-device copy from pageable memory
+ * is enqueued before the kernel); it must stay untouched until the kernel ran. */
+SHAMPOO4_API shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t transB,
+                                      const int32_t* M, const int32_t* N, const int32_t* K,
+                                      float alpha, const float* const* A, const int64_t* lda,
+                                      const float* const* B, const int64_t* ldb,
+                                      float beta, const float* const* C, const int64_t* ldc,
+                                      float* const* D, const int64_t* ldd,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kernel timing (HIP events around every launch of the next calls on a context).
+ * enable != 0 starts recording (clears previous records); the report waits for the
+ * device and returns, per kernel family, the number of launches, total milliseconds,
+ * and algorithmic flops and bytes.  names: "gemm", "dequant", "quant", "qr_panel",
+ * "rayleigh", "elementwise".  Host arrays of length *count (in: capacity, out: used). */
+SHAMPOO4_API shampoo4_status shampoo4_timing(shampoo4_ctx ctx, int32_t enable);
+SHAMPOO4_API shampoo4_status shampoo4_timing_report(shampoo4_ctx ctx, int32_t* count, const char** names,
+                                       int64_t* launches, double* total_ms,
+                                       double* flops, double* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHAMPOO4_H */

@@ -1,0 +1,80 @@
+"""Codec kernels in isolation: packed codes and scales bit-exact against the oracle
+on identical float32 inputs; dequantization bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codec
+from tests.gpu_util import announce, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _adversarial(rng, n):
+    x = rng.standard_normal(n).astype(np.float32)
+    x *= (10.0 ** rng.uniform(-3, 3, n)).astype(np.float32)
+    return x
+
+
+def _cases():
+    rng = np.random.default_rng(100)
+    cases = {}
+    for n in (1, 3, 63, 64, 65, 127, 1000, 4096, 64 * 64, 1024 * 1024 + 7):
+        cases[f"normal_{n}"] = rng.standard_normal(n).astype(np.float32)
+    cases["wide_range"] = _adversarial(rng, 50_000)
+    # values exactly on the decision midpoints and their neighbours, absmax 1 per block
+    mids = np.concatenate([codec.MIDPOINTS, np.nextafter(codec.MIDPOINTS, np.float32(2)),
+                           np.nextafter(codec.MIDPOINTS, np.float32(-2))]).astype(np.float32)
+    blocks = np.zeros((len(mids) // 63 + 1, 64), np.float32)
+    blocks[:, 0] = 1.0
+    flat = blocks[:, 1:].reshape(-1)
+    flat[: len(mids)] = mids
+    blocks[:, 1:] = flat.reshape(blocks.shape[0], 63)
+    cases["midpoints"] = blocks.ravel()
+    # codebook values times scales
+    codes = rng.integers(0, 16, (200, 64))
+    codes[:, 0] = 15
+    s = (10.0 ** rng.uniform(-5, 5, 200)).astype(np.float32)
+    cases["codebook"] = (codec.LEVELS[codes] * s[:, None]).astype(np.float32).ravel()
+    z = np.zeros(64 * 5, np.float32)
+    z[64:128] = -0.0
+    z[130] = 1e-42
+    z[131] = -3e-41
+    z[200] = 7.0
+    cases["zeros_subnormals"] = z
+    cases["identity_1024"] = np.eye(1024, dtype=np.float32).ravel()
+    return cases
+
+
+@pytest.mark.parametrize("name", list(_cases().keys()))
+def test_quantize_bit_exact(name):
+    require_gpu()
+    from bit_quantized_shampoo_amd import dequantize, quantize
+    x = _cases()[name]
+    announce(f"codec quantize {name} n={x.size}")
+    c_gpu, s_gpu = quantize(to_dev(x))
+    torch.cuda.synchronize()
+    c_ref, s_ref = codec.quantize(x)
+    assert np.array_equal(s_gpu.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(c_gpu.cpu().numpy(), c_ref)
+    announce(f"codec dequantize {name}")
+    y_gpu = dequantize(c_gpu, s_gpu, x.size)
+    torch.cuda.synchronize()
+    y_ref = codec.dequantize(c_ref, s_ref, x.size)
+    assert np.array_equal(y_gpu.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
+def test_dequantize_random_codes_bit_exact():
+    require_gpu()
+    from bit_quantized_shampoo_amd import dequantize
+    rng = np.random.default_rng(101)
+    n = 64 * 777 + 13
+    nqb = (n + 63) // 64
+    codes = rng.integers(0, 256, nqb * 32).astype(np.uint8)
+    scales = (10.0 ** rng.uniform(-30, 30, nqb)).astype(np.float32)
+    announce(f"codec dequantize random codes n={n}")
+    y = dequantize(to_dev(codes), to_dev(scales), n)
+    torch.cuda.synchronize()
+    ref = codec.dequantize(codes, scales, n)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), ref.view(np.uint32))

@@ -1,0 +1,81 @@
+"""The fp32 MFMA GEMM kernel in isolation against float64 NumPy products:
+every transpose mode, every tile shape (chosen by batch size), ragged edges,
+strided operands, alpha/beta."""
+
+import numpy as np
+import pytest
+import torch
+
+from tests.gpu_util import announce, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(As, Bs, Ds, ta, tb, alpha, beta, Cs):
+    for i, (A, B, D) in enumerate(zip(As, Bs, Ds)):
+        a = A.cpu().numpy().astype(np.float64)
+        b = B.cpu().numpy().astype(np.float64)
+        a = a.T if ta else a
+        b = b.T if tb else b
+        ref = alpha * (a @ b)
+        if beta != 0.0:
+            ref = ref + beta * Cs[i].cpu().numpy().astype(np.float64)
+        got = D.cpu().numpy().astype(np.float64)
+        # fp32 accumulation: bound by K * eps * |A||B| elementwise
+        bound = 4 * np.float32(np.finfo(np.float32).eps) * (np.abs(a) @ np.abs(b)) * max(1.0, abs(alpha)) \
+            * np.sqrt(a.shape[1] + 1) + 1e-30
+        if beta != 0.0:
+            bound = bound + 4 * np.finfo(np.float32).eps * np.abs(beta * Cs[i].cpu().numpy())
+        err = np.abs(got - ref)
+        assert np.all(err <= bound), (i, float(np.max(err / bound)))
+
+
+@pytest.mark.parametrize("ta", [False, True])
+@pytest.mark.parametrize("tb", [False, True])
+@pytest.mark.parametrize("shapes", [
+    [(1, 1, 1)],
+    [(5, 7, 3)],
+    [(33, 65, 17)],
+    [(64, 64, 64)],
+    [(130, 70, 129), (31, 200, 5)],
+    [(256, 256, 256)] * 3,
+    [(1024, 1024, 1024)],                 # single large product
+    [(32, 1000, 700)] * 2,                # skinny M
+])
+def test_gemm_modes(ta, tb, shapes):
+    require_gpu()
+    from bit_quantized_shampoo_amd import gemm_batched
+    rng = np.random.default_rng(hash((ta, tb, len(shapes), shapes[0])) % (2 ** 32))
+    As, Bs = [], []
+    for (M, N, K) in shapes:
+        A = rng.standard_normal((K, M) if ta else (M, K)).astype(np.float32)
+        B = rng.standard_normal((N, K) if tb else (K, N)).astype(np.float32)
+        As.append(to_dev(A))
+        Bs.append(to_dev(B))
+    announce(f"gemm ta={ta} tb={tb} shapes={shapes}")
+    Ds, _ = gemm_batched(As, Bs, transA=ta, transB=tb)
+    torch.cuda.synchronize()
+    _check(As, Bs, Ds, ta, tb, 1.0, 0.0, None)
+
+
+def test_gemm_alpha_beta_and_strides():
+    require_gpu()
+    from bit_quantized_shampoo_amd import gemm_batched
+    rng = np.random.default_rng(7)
+    big = to_dev(rng.standard_normal((300, 301)).astype(np.float32))
+    A = big[5:105, 3:83]          # strided view [100, 80], ld 301 (unaligned rows)
+    B = to_dev(rng.standard_normal((80, 90)).astype(np.float32))
+    C = to_dev(rng.standard_normal((100, 90)).astype(np.float32))
+    D = torch.empty((100, 90), dtype=torch.float32, device="cuda")
+    announce("gemm alpha/beta strided")
+    gemm_batched([A], [B], [D], alpha=-0.5, beta=1.5, Cs=[C])
+    torch.cuda.synchronize()
+    _check([A], [B], [D], False, False, -0.5, 1.5, [C])
+    # K = 0 gives beta * C
+    A0 = big[5:105, 3:3]          # [100, 0] view with a valid base pointer
+    B0 = B[:0, :]                 # [0, 90]
+    D0 = torch.empty((100, 90), dtype=torch.float32, device="cuda")
+    announce("gemm K=0")
+    gemm_batched([A0], [B0], [D0], alpha=1.0, beta=2.0, Cs=[C])
+    torch.cuda.synchronize()
+    assert torch.equal(D0, 2.0 * C)

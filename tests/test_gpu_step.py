@@ -1,0 +1,211 @@
+"""Teacher-forced parity of the whole step against the CPU oracle.
+
+Each entry point is checked from the state the GPU itself produced:
+  update_stats   the oracle recomputes the rectified eigenvectors from the GPU's
+                 codes, the statistic from them and the GPU's eigenvalues, and the
+                 refresh from the GPU's statistic; compared are the statistic, the
+                 basis-invariant product Q diag(lam) Q^T and the eigenvalues
+                 (rel-Frobenius <= 1e-3), and the new codes, which must equal the
+                 oracle codec applied to the GPU's own fp32 Q bit for bit;
+  refresh_root   d and the root codes;
+  precondition   the oracle's preconditioned gradient from the GPU's root state
+                 (rel-Frobenius <= 1e-3).
+Where several results are correct (the basis of an eigenspace of a repeated or
+zero eigenvalue), only basis-invariant products are compared.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codec
+from oracle import shampoo4 as o
+from tests.gpu_util import announce, rel_fro, require_gpu, to_dev
+from workloads import get_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power_iters=1,
+                        root_interval=1, root_cache=False, label=""):
+    from bit_quantized_shampoo_amd import Shampoo4Blocks, Shampoo4Config
+    cfg = Shampoo4Config(beta=beta, eps=eps, bjorck_iters=k, power_iters=power_iters,
+                         root_cache=root_cache)
+    announce(f"step parity {label}: init {shapes}")
+    blocks = Shampoo4Blocks(shapes, cfg)
+    torch.cuda.synchronize()
+    # initial state equals the oracle's
+    for b, (m, n) in enumerate(shapes):
+        for s, p in ((0, m), (1, n)):
+            ref = o.initial_side(p)
+            got = blocks.side_state(b, s)
+            assert np.array_equal(got["codes"], ref.codes)
+            assert np.array_equal(got["scales"], ref.scales)
+            assert np.array_equal(got["root_codes"], ref.root_codes)
+            assert np.all(got["lam"] == 0) and np.all(got["d"] == 1)
+    worst = {"stat": 0.0, "recon": 0.0, "lam": 0.0, "P": 0.0}
+    for t in range(1, steps + 1):
+        Gs = grads_fn(t)
+        Gd = [to_dev(G) for G in Gs]
+        before = [[blocks.side_state(b, s) for s in (0, 1)] for b in range(len(shapes))]
+        announce(f"step parity {label}: t={t} update_stats")
+        blocks.update_stats(Gd)
+        torch.cuda.synchronize()
+        for b, (m, n) in enumerate(shapes):
+            for s, p in ((0, m), (1, n)):
+                st = before[b][s]
+                Gs_side = o.side_gradient(Gs[b], s)
+                V = o.rectified_eigenvectors(st["codes"], st["scales"], p, k)
+                Lt_ref = o.statistics(V, st["lam"], Gs_side, beta)
+                Lt_gpu = blocks.view(b, s, 17).cpu().numpy().astype(np.float64)
+                e_stat = rel_fro(Lt_gpu, Lt_ref)
+                assert e_stat <= TOL, (label, t, b, s, "statistic", e_stat)
+                Q_ref, lam_ref = o.eigen_refresh(Lt_gpu, V, power_iters)
+                Q_gpu32 = blocks.view(b, s, 18).cpu().numpy()
+                after = blocks.side_state(b, s)
+                lam_gpu = after["lam"].astype(np.float64)
+                Q_gpu = Q_gpu32.astype(np.float64)
+                e_rec = rel_fro((Q_gpu * lam_gpu) @ Q_gpu.T, (Q_ref * lam_ref) @ Q_ref.T)
+                e_lam = rel_fro(lam_gpu, lam_ref)
+                assert e_rec <= TOL, (label, t, b, s, "Q diag(lam) Q^T", e_rec)
+                assert e_lam <= TOL, (label, t, b, s, "eigenvalues", e_lam)
+                assert np.allclose(Q_gpu.T @ Q_gpu, np.eye(p), atol=1e-4), (label, t, b, s, "orthonormal Q")
+                c_ref, s_ref = codec.quantize_matrix(Q_gpu32)
+                assert np.array_equal(after["codes"], c_ref), (label, t, b, s, "codes")
+                assert np.array_equal(after["scales"].view(np.uint32), s_ref.view(np.uint32))
+                worst["stat"] = max(worst["stat"], e_stat)
+                worst["recon"] = max(worst["recon"], e_rec)
+                worst["lam"] = max(worst["lam"], e_lam)
+        if t % root_interval == 0:
+            announce(f"step parity {label}: t={t} refresh_root")
+            blocks.refresh_root()
+            torch.cuda.synchronize()
+            for b, (m, n) in enumerate(shapes):
+                for s in (0, 1):
+                    st = blocks.side_state(b, s)
+                    assert np.array_equal(st["root_codes"], st["codes"])
+                    assert np.array_equal(st["root_scales"], st["scales"])
+                    d_ref = o.root_scaling(st["lam"], eps)
+                    assert np.allclose(st["d"], d_ref, rtol=2e-6, atol=0), (label, t, b, s, "d")
+        announce(f"step parity {label}: t={t} precondition")
+        outs = blocks.precondition(Gd)
+        torch.cuda.synchronize()
+        for b, (m, n) in enumerate(shapes):
+            sl, sr = blocks.side_state(b, 0), blocks.side_state(b, 1)
+            VL = o.rectified_eigenvectors(sl["root_codes"], sl["root_scales"], m, k)
+            VR = o.rectified_eigenvectors(sr["root_codes"], sr["root_scales"], n, k)
+            P_ref = o.precondition_block(VL, sl["d"], VR, sr["d"], Gs[b])
+            e_p = rel_fro(outs[b].cpu().numpy(), P_ref)
+            assert e_p <= TOL, (label, t, b, "P", e_p)
+            worst["P"] = max(worst["P"], e_p)
+    announce(f"step parity {label}: worst {worst}")
+    blocks.close()
+    return worst
+
+
+def test_single_64x32_all_steps():
+    require_gpu()
+    wl = get_workload("single_64x32")
+    _run_teacher_forced(wl.shapes, wl.gradients, wl.steps, beta=wl.beta, eps=wl.eps,
+                        k=wl.bjorck_iters, root_interval=wl.root_interval, label="single_64x32")
+
+
+def test_single_64x32_root_cache():
+    require_gpu()
+    wl = get_workload("single_64x32")
+    _run_teacher_forced(wl.shapes, wl.gradients, 6, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
+                        root_interval=1, root_cache=True, label="single_64x32_cache")
+
+
+@pytest.mark.parametrize("shapes,k,power_iters,T,cache", [
+    ([(1, 1), (2, 3), (5, 1)], 1, 1, 1, False),           # degenerate tiny blocks
+    ([(40, 72), (33, 33), (100, 7)], 2, 1, 2, True),      # ragged, across panels
+    ([(96, 160), (130, 65)], 0, 2, 1, False),             # no Bjorck, two power steps
+    ([(64, 64)], 5, 1, 1, True),
+])
+def test_ragged_batches(shapes, k, power_iters, T, cache):
+    require_gpu()
+    rng = np.random.default_rng(sum(m * 31 + n for m, n in shapes))
+    scales = [(10.0 ** rng.uniform(-1, 1, (m, 1))) * (10.0 ** rng.uniform(-1, 1, (1, n))) for m, n in shapes]
+
+    def grads(t):
+        r = np.random.default_rng([t, len(shapes)])
+        return [(r.standard_normal((m, n)) * sc).astype(np.float32) for (m, n), sc in zip(shapes, scales)]
+
+    _run_teacher_forced(shapes, grads, 4, k=k, power_iters=power_iters, root_interval=T,
+                        root_cache=cache, label=f"ragged {shapes}")
+
+
+def test_single_1024_steps():
+    """The 1024 x 1024 workload for its first root-refresh period (stats every step,
+    root every 10 steps), so precondition runs with the identity root and then with
+    a refreshed one."""
+    require_gpu()
+    wl = get_workload("single_1024")
+    _run_teacher_forced(wl.shapes, wl.gradients, 11, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
+                        root_interval=wl.root_interval, label="single_1024")
+
+
+def test_cnn_batch_two_steps():
+    require_gpu()
+    wl = get_workload("cnn_batch")
+    sel = [0, 1, 2, 3, 4, 5, 6, 7]
+    # a handful of the batch's blocks, every distinct shape represented
+    shapes_all = wl.shapes
+    seen, idx = set(), []
+    for i, s in enumerate(shapes_all):
+        if s not in seen:
+            seen.add(s)
+            idx.append(i)
+    shapes = [shapes_all[i] for i in idx]
+
+    def grads(t):
+        return [wl.block_gradient(i, t) for i in idx]
+
+    del sel
+    _run_teacher_forced(shapes, grads, 2, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters, label="cnn_batch")
+
+
+def test_update_is_deterministic_and_resumable():
+    """Two contexts fed the same gradients stay bit-identical; a context restarted from
+    a saved state continues bit-identically."""
+    require_gpu()
+    from bit_quantized_shampoo_amd import Shampoo4Blocks, Shampoo4Config
+    shapes = [(96, 64), (64, 130)]
+    rng = np.random.default_rng(5)
+    Gs = [[to_dev(rng.standard_normal(s).astype(np.float32)) for s in shapes] for _ in range(4)]
+    cfg = Shampoo4Config(root_cache=True)
+    announce("determinism/resume")
+    a = Shampoo4Blocks(shapes, cfg)
+    b = Shampoo4Blocks(shapes, cfg)
+    for t in range(2):
+        Pa = a.step(Gs[t], t + 1)
+        Pb = b.step(Gs[t], t + 1)
+        torch.cuda.synchronize()
+        for x, y in zip(Pa, Pb):
+            assert torch.equal(x, y)
+    saved = a.state.clone()
+    c = Shampoo4Blocks(shapes, cfg, state=saved)
+    for t in range(2, 4):
+        Pa = a.step(Gs[t], t + 1)
+        Pc = c.step(Gs[t], t + 1)
+        torch.cuda.synchronize()
+        for x, y in zip(Pa, Pc):
+            assert torch.equal(x, y)
+    assert torch.equal(a.state, c.state)
+
+
+def test_nonfinite_flag():
+    require_gpu()
+    from bit_quantized_shampoo_amd import Shampoo4Blocks
+    announce("nonfinite flag")
+    blk = Shampoo4Blocks([(16, 8)])
+    G = torch.zeros((16, 8), dtype=torch.float32, device="cuda")
+    blk.update_stats([G])
+    assert blk.check() == 0
+    G[3, 2] = float("nan")
+    blk.update_stats([G])
+    assert blk.check() != 0
+    assert blk.check() == 0      # cleared by the previous check

@@ -1,0 +1,106 @@
+"""Host-only checks of libshampoo4.so: it loads, exports every symbol the header
+declares, its codebook equals the oracle's bit for bit, and host-side planning /
+validation behave as documented.  No device call is made."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_quantized_shampoo_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "shampoo4.h")
+
+
+def _lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("library not built (run __graft_entry__.build())")
+    return L.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SHAMPOO4_API[^;(]*?\b(shampoo4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_surface():
+    assert declared_symbols() == sorted(L.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    assert lib.shampoo4_abi_version() == 1
+
+
+def test_codebook_matches_oracle_bitwise():
+    _lib()
+    from bit_quantized_shampoo_amd.shampoo4 import codebook
+    from oracle import codec
+    lv, mp = codebook()
+    assert np.array_equal(np.array(lv, np.float32).view(np.uint32), codec.LEVELS.view(np.uint32))
+    assert np.array_equal(np.array(mp, np.float32).view(np.uint32), codec.MIDPOINTS.view(np.uint32))
+
+
+def _plan(shapes, **kw):
+    lib = _lib()
+    cfg = L.Config(kw.get("beta", 0.95), kw.get("eps", 1e-6), kw.get("qblock", 64),
+                   kw.get("k", 1), kw.get("pi", 1), kw.get("flags", 0))
+    arr = (L.Shape * len(shapes))(*[L.Shape(m, n) for m, n in shapes])
+    sb, wb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    st = lib.shampoo4_plan(ctypes.byref(cfg), len(shapes), arr, ctypes.byref(sb), ctypes.byref(wb))
+    return st, sb.value, wb.value
+
+
+def test_plan_sizes():
+    st, sb, wb = _plan([(64, 32)])
+    assert st == L.OK
+    # state: per side codes + scales + lam + root codes + root scales + d, 256-byte aligned pieces
+    def side(p):
+        nqb = (p * p + 63) // 64
+        al = lambda b: (b + 255) // 256 * 256
+        return 2 * al(nqb * 32) + 2 * al(nqb * 4) + 2 * al(p * 4)
+    assert sb == side(64) + side(32)
+    assert wb > 7 * (64 * 64 + 32 * 32) * 4
+    st2, sb2, wb2 = _plan([(64, 32), (1024, 1024)])
+    assert st2 == L.OK and sb2 > sb and wb2 > wb
+
+
+@pytest.mark.parametrize("shapes,kw,status", [
+    ([(0, 4)], {}, L.ESHAPE),
+    ([(8193, 4)], {}, L.ESHAPE),
+    ([(4, 4)], {"qblock": 32}, L.EINVAL),
+    ([(4, 4)], {"beta": 1.5}, L.EINVAL),
+    ([(4, 4)], {"eps": -1.0}, L.EINVAL),
+    ([(4, 4)], {"k": -1}, L.EINVAL),
+    ([(4, 4)], {"k": 17}, L.EINVAL),
+    ([(4, 4)], {"pi": 0}, L.EINVAL),
+    ([(4, 4)], {"flags": 8}, L.EINVAL),
+    ([(1, 1)], {}, L.OK),
+    ([(8192, 1)], {}, L.OK),
+])
+def test_plan_validation(shapes, kw, status):
+    st, _, _ = _plan(shapes, **kw)
+    assert st == status
+
+
+def test_strerror_and_gemm_workspace():
+    lib = _lib()
+    for s in range(7):
+        assert isinstance(lib.shampoo4_strerror(s), bytes)
+    assert lib.shampoo4_gemm_workspace_bytes(3) >= 3 * 128 + 16
+
+
+def test_null_arguments_rejected_on_host():
+    lib = _lib()
+    assert lib.shampoo4_update_stats(None, None, None) == L.EINVAL
+    assert lib.shampoo4_refresh_root(None, None) == L.EINVAL
+    assert lib.shampoo4_precondition(None, None, None) == L.EINVAL
+    assert lib.shampoo4_destroy(None) == L.EINVAL
+    assert lib.shampoo4_quantize(None, 5, 64, None, None, None) == L.EINVAL
+    assert lib.shampoo4_quantize(None, 5, 32, None, None, None) == L.EINVAL
+    assert lib.shampoo4_dequantize(None, None, 0, 64, None, None) == L.OK
