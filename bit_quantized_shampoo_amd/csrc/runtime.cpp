@@ -872,7 +872,8 @@ shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t tra
         if (M[i] < 0 || N[i] < 0 || K[i] < 0) return SHAMPOO4_ESHAPE;
         const int64_t acols = transA ? M[i] : K[i];
         const int64_t bcols = transB ? K[i] : N[i];
-        if (!A[i] || !B[i] || !D[i]) return SHAMPOO4_EINVAL;
+        const bool empty_out = M[i] == 0 || N[i] == 0;
+        if ((!empty_out && !D[i]) || (!empty_out && K[i] > 0 && (!A[i] || !B[i]))) return SHAMPOO4_EINVAL;
         if (lda[i] < std::max<int64_t>(acols, 1) || ldb[i] < std::max<int64_t>(bcols, 1) ||
             ldd[i] < std::max<int32_t>(N[i], 1))
             return SHAMPOO4_ESHAPE;
