@@ -34,7 +34,13 @@ struct GemmDesc {
     int32_t tiles_m;          // tiles along M for the launch's tile shape
     float alpha, beta;
     int32_t a_io, b_io, d_io; // -1 or index into the io table (A/B = G, D = P)
-    int32_t pad;
+    int32_t flags;            // GEMM_F_* below
+};
+enum : int32_t {
+    GEMM_F_TA = 1,            // op(A) = A^T
+    GEMM_F_TB = 2,            // op(B) = B^T
+    GEMM_F_COLDOT = 4,        // epilogue: D[tile_m][col] = sum over the tile's rows of
+                              //   alpha * (op(A) op(B))[row][col] * C[row][col]; ldd = row stride
 };
 static_assert(sizeof(GemmDesc) == 128, "GemmDesc layout");
 
@@ -71,7 +77,7 @@ struct VecDesc {
     uint8_t* codes;           // identity init
     float* scales;
     int64_t ld;
-    int32_t p, pad;
+    int32_t p, rows;          // rows: number of partial rows (Rayleigh reduction)
 };
 static_assert(sizeof(VecDesc) == 64, "VecDesc layout");
 

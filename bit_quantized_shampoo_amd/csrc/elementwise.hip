@@ -1,10 +1,11 @@
 // Small bandwidth-bound kernels of the step.
-//  * rayleigh:      lam_j = max(sum_r Q[r][j] (L~ Q)[r][j], 0), one workgroup per 64
-//                   columns (lanes own columns, 4 row slots, fixed-order reduction);
 //  * root scaling:  d_i = (lam_i + eps)^(-1/4) ("Shampoo -- Second-Order Optimizer",
 //                   "Computing the inverse fourth root": damping before rooting);
-//  * sign diagonal: W = diag(sign R_jj) (0 -> +1), the start of the explicit-Q
-//                   accumulation, so that Q comes out with diag(R) >= 0;
+//  * rayleigh reduce: lam_j = max(sum_r Q[r][j] (L~ Q)[r][j], 0) from the per-tile
+//                   partial sums the column-dot GEMM epilogue leaves (fixed order);
+//  * identity fill / sign flip: Q starts as I for the forward accumulation of
+//                   the reflectors and its column j is finally multiplied by
+//                   sign(R_jj) (0 -> +), so that diag(R) >= 0;
 //  * identity state: U = I coded exactly (code 15 on the diagonal, 7 elsewhere,
 //                   scale 1 for blocks holding a diagonal element, else 0), lam = 0,
 //                   root = (I, d = 1).
@@ -13,30 +14,6 @@
 namespace s4 {
 
 namespace {
-
-__global__ __launch_bounds__(256) void rayleigh_kernel(const VecDesc* __restrict__ descs,
-                                                       const int* __restrict__ prefix, int ndesc,
-                                                       uint32_t* __restrict__ flag) {
-    __shared__ float red[4][RAYLEIGH_COLS];
-    const int item = find_item(prefix, ndesc, blockIdx.x);
-    const VecDesc& d = descs[item];
-    const int chunk = blockIdx.x - prefix[item];
-    const int c = threadIdx.x & 63;
-    const int slot = threadIdx.x >> 6;
-    const int col = chunk * RAYLEIGH_COLS + c;
-    const int p = d.p;
-    const int64_t ld = d.ld;
-    float s = 0.f;
-    if (col < p)
-        for (int r = slot; r < p; r += 4) s += d.a[(int64_t)r * ld + col] * d.b[(int64_t)r * ld + col];
-    red[slot][c] = s;
-    __syncthreads();
-    if (threadIdx.x < 64 && col < p) {
-        const float t = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
-        if (!__builtin_isfinite(t)) flag[0] = 1u;
-        d.out[col] = t > 0.f ? t : 0.f;
-    }
-}
 
 __global__ __launch_bounds__(256) void root_scaling_kernel(const VecDesc* __restrict__ descs,
                                                            const int* __restrict__ prefix, int ndesc,
@@ -50,7 +27,34 @@ __global__ __launch_bounds__(256) void root_scaling_kernel(const VecDesc* __rest
     d.out[i] = 1.0f / sqrtf(sqrtf(x));
 }
 
-__global__ __launch_bounds__(256) void sign_diag_kernel(const VecDesc* __restrict__ descs,
+__global__ __launch_bounds__(256) void rayleigh_reduce_kernel(const VecDesc* __restrict__ descs,
+                                                              const int* __restrict__ prefix, int ndesc,
+                                                              uint32_t* __restrict__ flag) {
+    const int item = find_item(prefix, ndesc, blockIdx.x);
+    const VecDesc& d = descs[item];
+    const int j = (blockIdx.x - prefix[item]) * 256 + threadIdx.x;
+    if (j >= d.p) return;
+    float t = 0.f;
+    for (int r = 0; r < d.rows; ++r) t += d.a[(int64_t)r * d.ld + j];
+    if (!__builtin_isfinite(t)) flag[0] = 1u;
+    d.out[j] = t > 0.f ? t : 0.f;
+}
+
+// out = I (p x p, leading dimension ld)
+__global__ __launch_bounds__(256) void identity_fill_kernel(const VecDesc* __restrict__ descs,
+                                                            const int* __restrict__ prefix, int ndesc) {
+    const int item = find_item(prefix, ndesc, blockIdx.x);
+    const VecDesc& d = descs[item];
+    const int64_t p = d.p;
+    const int64_t base = (int64_t)(blockIdx.x - prefix[item]) * FILL_TILE;
+    for (int64_t e = base + threadIdx.x; e < base + FILL_TILE && e < p * p; e += 256) {
+        const int64_t i = e / p, j = e - i * p;
+        d.out[i * d.ld + j] = (i == j) ? 1.f : 0.f;
+    }
+}
+
+// column j of out times sign(aux[j]) (0 counts as +)
+__global__ __launch_bounds__(256) void sign_flip_kernel(const VecDesc* __restrict__ descs,
                                                         const int* __restrict__ prefix, int ndesc) {
     const int item = find_item(prefix, ndesc, blockIdx.x);
     const VecDesc& d = descs[item];
@@ -58,9 +62,7 @@ __global__ __launch_bounds__(256) void sign_diag_kernel(const VecDesc* __restric
     const int64_t base = (int64_t)(blockIdx.x - prefix[item]) * FILL_TILE;
     for (int64_t e = base + threadIdx.x; e < base + FILL_TILE && e < p * p; e += 256) {
         const int64_t i = e / p, j = e - i * p;
-        float v = 0.f;
-        if (i == j) v = (d.aux[j] < 0.f) ? -1.f : 1.f;
-        d.out[i * d.ld + j] = v;
+        if (d.aux[j] < 0.f) d.out[i * d.ld + j] = -d.out[i * d.ld + j];
     }
 }
 
@@ -102,13 +104,6 @@ __global__ __launch_bounds__(256) void identity_state_kernel(const InitDesc* __r
 
 }  // namespace
 
-hipError_t launch_rayleigh(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
-                           uint32_t* flag, hipStream_t stream) {
-    if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(rayleigh_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc, flag);
-    return hipGetLastError();
-}
-
 hipError_t launch_root_scaling(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
                                float eps, uint32_t* flag, hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
@@ -117,10 +112,24 @@ hipError_t launch_root_scaling(const VecDesc* descs, const int* prefix, int ndes
     return hipGetLastError();
 }
 
-hipError_t launch_sign_diag(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+hipError_t launch_rayleigh_reduce(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                                  uint32_t* flag, hipStream_t stream) {
+    if (ntiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(rayleigh_reduce_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_identity_fill(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                                hipStream_t stream) {
+    if (ntiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(identity_fill_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    return hipGetLastError();
+}
+
+hipError_t launch_sign_flip(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
                             hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(sign_diag_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    hipLaunchKernelGGL(sign_flip_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
     return hipGetLastError();
 }
 

@@ -2,31 +2,48 @@
 //
 // Every product of the step (Bjorck V^T V and V (V^T V), the statistics
 // V diag(lam) V^T and G G^T, the power step L~ V, the Householder trailing
-// updates and explicit-Q accumulation, the Rayleigh product L~ Q and the
-// four-product preconditioner sandwich) goes through this one kernel, batched
-// over all blocks and both sides in a single launch per transpose mode.
+// updates and Q accumulation, the Rayleigh product L~ Q and the four-product
+// preconditioner sandwich) goes through this kernel, batched over all blocks and
+// both sides in a single launch.
 //
 // Design:
 //  * workgroup = 4 waves (256 threads); a wave owns TM x TN blocks of 32x32
-//    accumulators (16 fp32 each, in AGPR/VGPR);
+//    accumulators (16 fp32 each);
 //  * the K loop stages BK = 16 slices of op(A) and op(B) in LDS, double
-//    buffered with a register prefetch of the next slice, so there is one
-//    barrier per slice;
+//    buffered with a register prefetch of the next slice, one barrier per slice;
 //  * LDS layout follows the global layout so that every global load is a
-//    16-byte vector load and every LDS store is a 16-byte store:
-//    K-contiguous operands (A row-major, B transposed) are kept as [row][k]
-//    with a pitch of BK+4 floats and read back with one ds_read_b128 per
-//    four k values; M/N-contiguous operands (A transposed, B row-major) are
-//    kept as [k][row] with a pitch of BM+8 floats and read with ds_read_b32;
+//    16-byte vector load and every LDS store a 16-byte store: K-contiguous
+//    operands (A row-major, B transposed) are kept as [row][k] with a pitch of
+//    BK+4 floats and read back with one ds_read_b128 per four k values;
+//    M/N-contiguous operands (A transposed, B row-major) are kept as [k][row]
+//    with a pitch of BM+8 floats and read with ds_read_b32;
 //  * within an 8-wide k chunk, lane half h feeds k = 4h + s to MFMA step s,
 //    a permutation of the summation order only;
-//  * the epilogue applies alpha, optional row / column scales and beta * C,
-//    writing each half-wave's 32 consecutive columns at once.
+//  * the epilogue applies alpha, optional row / column scales and beta * C, or
+//    (COLDOT) reduces alpha * acc * C over the tile's rows into one partial row
+//    per tile (used for the Rayleigh quotients q_j^T L~ q_j without writing L~ Q).
+//  * a launch either has one transpose mode (specialized kernel) or mixes them
+//    (one kernel, branch uniform per workgroup).
 #include "kernels.hpp"
 
 namespace s4 {
 
 namespace {
+
+template <int WM, int WN, int TM, int TN>
+struct Tile {
+    static constexpr int BM = WM * TM * 32;
+    static constexpr int BN = WN * TN * 32;
+    static constexpr int BK = 16;
+    static constexpr int KCP = BK + 4;
+    static constexpr int AMCP = BM + 8;
+    static constexpr int BMCP = BN + 8;
+    static constexpr int A_KC = BM * KCP, A_MC = BK * AMCP;
+    static constexpr int B_KC = BN * KCP, B_MC = BK * BMCP;
+    static constexpr int A_MAX = A_KC > A_MC ? A_KC : A_MC;
+    static constexpr int B_MAX = B_KC > B_MC ? B_KC : B_MC;
+    static constexpr int RED = WM * BN;        // COLDOT cross-wave partials
+};
 
 __device__ __forceinline__ floatx4 load_quad(const float* __restrict__ base, int64_t ld,
                                              int row, int col, int rows, int cols, bool vec_ok) {
@@ -45,31 +62,20 @@ __device__ __forceinline__ floatx4 load_quad(const float* __restrict__ base, int
 }
 
 template <int WM, int WN, int TM, int TN, bool TA, bool TB>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ descs,
-                                                   const int* __restrict__ prefix, int ndesc,
-                                                   const IoEntry* __restrict__ io) {
-    constexpr int BM = WM * TM * 32;
-    constexpr int BN = WN * TN * 32;
-    constexpr int BK = 16;
-    constexpr int KCP = BK + 4;          // pitch of K-contiguous tiles
-    constexpr int AMCP = BM + 8;         // pitch of M-contiguous A tiles
-    constexpr int BMCP = BN + 8;         // pitch of N-contiguous B tiles
-    constexpr int A_SZ = TA ? BK * AMCP : BM * KCP;
-    constexpr int B_SZ = TB ? BN * KCP : BK * BMCP;
-    constexpr int NQA = BM * BK / 4;     // float4 quads per A slice
+__device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEntry* __restrict__ io,
+                                          float* __restrict__ As, float* __restrict__ Bs) {
+    using T = Tile<WM, WN, TM, TN>;
+    constexpr int BM = T::BM, BN = T::BN, BK = T::BK, KCP = T::KCP, AMCP = T::AMCP, BMCP = T::BMCP;
+    constexpr int A_SZ = TA ? T::A_MC : T::A_KC;
+    constexpr int B_SZ = TB ? T::B_KC : T::B_MC;
+    constexpr int NQA = BM * BK / 4;
     constexpr int NQB = BN * BK / 4;
     constexpr int RA = (NQA + 255) / 256;
     constexpr int RB = (NQB + 255) / 256;
-    static_assert(WM * WN == 4, "4 waves");
 
-    __shared__ __attribute__((aligned(16))) float As[2][A_SZ];
-    __shared__ __attribute__((aligned(16))) float Bs[2][B_SZ];
-
-    const int item = find_item(prefix, ndesc, blockIdx.x);
-    const GemmDesc& dsc = descs[item];
-    const int t = blockIdx.x - prefix[item];
     const int tiles_m = dsc.tiles_m;
-    const int row0 = (t % tiles_m) * BM;
+    const int tile_m = t % tiles_m;
+    const int row0 = tile_m * BM;
     const int col0 = (t / tiles_m) * BN;
     const int M = dsc.M, N = dsc.N, K = dsc.K;
 
@@ -146,16 +152,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ 
     };
 
     auto store_slice = [&](int buf) {
+        float* as = As + buf * A_SZ;
+        float* bs = Bs + buf * B_SZ;
 #pragma unroll
         for (int r = 0; r < RA; ++r) {
             const int q = tid + r * 256;
             if (q < NQA) {
                 if constexpr (!TA) {
                     const int i = q / (BK / 4), kq = (q % (BK / 4)) * 4;
-                    *reinterpret_cast<floatx4*>(&As[buf][i * KCP + kq]) = ra[r];
+                    *reinterpret_cast<floatx4*>(&as[i * KCP + kq]) = ra[r];
                 } else {
                     const int k = q / (BM / 4), iq = (q % (BM / 4)) * 4;
-                    *reinterpret_cast<floatx4*>(&As[buf][k * AMCP + iq]) = ra[r];
+                    *reinterpret_cast<floatx4*>(&as[k * AMCP + iq]) = ra[r];
                 }
             }
         }
@@ -165,10 +173,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ 
             if (q < NQB) {
                 if constexpr (TB) {
                     const int j = q / (BK / 4), kq = (q % (BK / 4)) * 4;
-                    *reinterpret_cast<floatx4*>(&Bs[buf][j * KCP + kq]) = rb[r];
+                    *reinterpret_cast<floatx4*>(&bs[j * KCP + kq]) = rb[r];
                 } else {
                     const int k = q / (BN / 4), jq = (q % (BN / 4)) * 4;
-                    *reinterpret_cast<floatx4*>(&Bs[buf][k * BMCP + jq]) = rb[r];
+                    *reinterpret_cast<floatx4*>(&bs[k * BMCP + jq]) = rb[r];
                 }
             }
         }
@@ -185,6 +193,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ 
         const int cur = kt & 1;
         const bool more = kt + 1 < nk;
         if (more) load_slice((kt + 1) * BK);
+        const float* as = As + cur * A_SZ;
+        const float* bs = Bs + cur * B_SZ;
 
 #pragma unroll
         for (int kc = 0; kc < BK / 8; ++kc) {
@@ -194,20 +204,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ 
             for (int m = 0; m < TM; ++m) {
                 const int row = wave_m * TM * 32 + m * 32 + l32;
                 if constexpr (!TA) {
-                    a[m] = *reinterpret_cast<const floatx4*>(&As[cur][row * KCP + kb]);
+                    a[m] = *reinterpret_cast<const floatx4*>(&as[row * KCP + kb]);
                 } else {
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) a[m][s] = As[cur][(kb + s) * AMCP + row];
+                    for (int s = 0; s < 4; ++s) a[m][s] = as[(kb + s) * AMCP + row];
                 }
             }
 #pragma unroll
             for (int n = 0; n < TN; ++n) {
                 const int col = wave_n * TN * 32 + n * 32 + l32;
                 if constexpr (TB) {
-                    b[n] = *reinterpret_cast<const floatx4*>(&Bs[cur][col * KCP + kb]);
+                    b[n] = *reinterpret_cast<const floatx4*>(&bs[col * KCP + kb]);
                 } else {
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) b[n][s] = Bs[cur][(kb + s) * BMCP + col];
+                    for (int s = 0; s < 4; ++s) b[n][s] = bs[(kb + s) * BMCP + col];
                 }
             }
 #pragma unroll
@@ -229,6 +239,42 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ 
     const float alpha = dsc.alpha, beta = dsc.beta;
     const float* __restrict__ C = dsc.C;
     const int64_t ldc = dsc.ldc;
+
+    if (dsc.flags & GEMM_F_COLDOT) {
+        // LDS is free after the final barrier of the K loop: reuse As for partials
+        float* red = As;
+#pragma unroll
+        for (int n = 0; n < TN; ++n) {
+            const int lcol = wave_n * TN * 32 + n * 32 + l32;
+            const int col = col0 + lcol;
+            float s = 0.f;
+            if (col < N) {
+#pragma unroll
+                for (int m = 0; m < TM; ++m)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                        if (row < M) s += acc[m][n][r] * C[(int64_t)row * ldc + col];
+                    }
+            }
+            s += __shfl_xor(s, 32);
+            if (h == 0) red[wave_m * BN + lcol] = s;
+        }
+        __syncthreads();
+        if (wave_m == 0 && h == 0) {
+#pragma unroll
+            for (int n = 0; n < TN; ++n) {
+                const int lcol = wave_n * TN * 32 + n * 32 + l32;
+                const int col = col0 + lcol;
+                float s = 0.f;
+#pragma unroll
+                for (int w = 0; w < WM; ++w) s += red[w * BN + lcol];
+                if (col < N) D[(int64_t)tile_m * ldd + col] = alpha * s;
+            }
+        }
+        return;
+    }
+
     const float* __restrict__ rs = dsc.rscale;
     const float* __restrict__ cs = dsc.cscale;
 #pragma unroll
@@ -253,22 +299,65 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ 
     }
 }
 
+template <int WM, int WN, int TM, int TN, bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ descs,
+                                                   const int* __restrict__ prefix, int ndesc,
+                                                   const IoEntry* __restrict__ io) {
+    using T = Tile<WM, WN, TM, TN>;
+    constexpr int A_SZ = TA ? T::A_MC : T::A_KC;
+    constexpr int B_SZ = TB ? T::B_KC : T::B_MC;
+    constexpr int A_ALL = (2 * A_SZ > T::RED) ? 2 * A_SZ : T::RED;
+    __shared__ __attribute__((aligned(16))) float As[A_ALL];
+    __shared__ __attribute__((aligned(16))) float Bs[2 * B_SZ];
+    const int item = find_item(prefix, ndesc, blockIdx.x);
+    gemm_body<WM, WN, TM, TN, TA, TB>(descs[item], blockIdx.x - prefix[item], io, As, Bs);
+}
+
 template <int WM, int WN, int TM, int TN>
-hipError_t launch_cfg(bool ta, bool tb, const GemmDesc* descs, const int* prefix, int ndesc,
-                      int ntiles, const IoEntry* io, hipStream_t stream) {
+__global__ __launch_bounds__(256) void gemm_kernel_mixed(const GemmDesc* __restrict__ descs,
+                                                         const int* __restrict__ prefix, int ndesc,
+                                                         const IoEntry* __restrict__ io) {
+    using T = Tile<WM, WN, TM, TN>;
+    constexpr int A_ALL = (2 * T::A_MAX > T::RED) ? 2 * T::A_MAX : T::RED;
+    __shared__ __attribute__((aligned(16))) float As[A_ALL];
+    __shared__ __attribute__((aligned(16))) float Bs[2 * T::B_MAX];
+    const int item = find_item(prefix, ndesc, blockIdx.x);
+    const GemmDesc& d = descs[item];
+    const int t = blockIdx.x - prefix[item];
+    switch (d.flags & (GEMM_F_TA | GEMM_F_TB)) {
+        case 0: gemm_body<WM, WN, TM, TN, false, false>(d, t, io, As, Bs); break;
+        case GEMM_F_TB: gemm_body<WM, WN, TM, TN, false, true>(d, t, io, As, Bs); break;
+        case GEMM_F_TA: gemm_body<WM, WN, TM, TN, true, false>(d, t, io, As, Bs); break;
+        default: gemm_body<WM, WN, TM, TN, true, true>(d, t, io, As, Bs); break;
+    }
+}
+
+template <int WM, int WN, int TM, int TN>
+hipError_t launch_cfg(int mode, const GemmDesc* descs, const int* prefix, int ndesc, int ntiles,
+                      const IoEntry* io, hipStream_t stream) {
     dim3 grid(ntiles), block(256);
-    if (!ta && !tb)
-        hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, false, false>), grid, block, 0, stream,
-                           descs, prefix, ndesc, io);
-    else if (!ta && tb)
-        hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, false, true>), grid, block, 0, stream,
-                           descs, prefix, ndesc, io);
-    else if (ta && !tb)
-        hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, true, false>), grid, block, 0, stream,
-                           descs, prefix, ndesc, io);
-    else
-        hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, true, true>), grid, block, 0, stream,
-                           descs, prefix, ndesc, io);
+    switch (mode) {
+        case 0:
+            hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, false, false>), grid, block, 0, stream,
+                               descs, prefix, ndesc, io);
+            break;
+        case GEMM_F_TB:
+            hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, false, true>), grid, block, 0, stream,
+                               descs, prefix, ndesc, io);
+            break;
+        case GEMM_F_TA:
+            hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, true, false>), grid, block, 0, stream,
+                               descs, prefix, ndesc, io);
+            break;
+        case GEMM_F_TA | GEMM_F_TB:
+            hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, true, true>), grid, block, 0, stream,
+                               descs, prefix, ndesc, io);
+            break;
+        default:
+            hipLaunchKernelGGL((gemm_kernel_mixed<WM, WN, TM, TN>), grid, block, 0, stream, descs,
+                               prefix, ndesc, io);
+            break;
+    }
     return hipGetLastError();
 }
 
@@ -282,13 +371,13 @@ void gemm_tile_dims(int cfg, int* bm, int* bn) {
     }
 }
 
-hipError_t launch_gemm(int cfg, bool ta, bool tb, const GemmDesc* descs, const int* prefix,
-                       int ndesc, int ntiles, const IoEntry* io, hipStream_t stream) {
+hipError_t launch_gemm(int cfg, int mode, const GemmDesc* descs, const int* prefix, int ndesc, int ntiles,
+                       const IoEntry* io, hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
     switch (cfg) {
-        case GEMM_128x128: return launch_cfg<2, 2, 2, 2>(ta, tb, descs, prefix, ndesc, ntiles, io, stream);
-        case GEMM_64x64: return launch_cfg<2, 2, 1, 1>(ta, tb, descs, prefix, ndesc, ntiles, io, stream);
-        default: return launch_cfg<1, 4, 1, 1>(ta, tb, descs, prefix, ndesc, ntiles, io, stream);
+        case GEMM_128x128: return launch_cfg<2, 2, 2, 2>(mode, descs, prefix, ndesc, ntiles, io, stream);
+        case GEMM_64x64: return launch_cfg<2, 2, 1, 1>(mode, descs, prefix, ndesc, ntiles, io, stream);
+        default: return launch_cfg<1, 4, 1, 1>(mode, descs, prefix, ndesc, ntiles, io, stream);
     }
 }
 

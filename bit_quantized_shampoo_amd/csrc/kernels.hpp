@@ -9,8 +9,10 @@ namespace s4 {
 
 // Tile shapes of the fp32 MFMA GEMM (workgroup of 4 waves).
 enum GemmCfg { GEMM_128x128 = 0, GEMM_64x64 = 1, GEMM_32x128 = 2, GEMM_NCFG = 3 };
+constexpr int GEMM_MODE_MIXED = -1;   // descriptors of one launch carry different transposes
 void gemm_tile_dims(int cfg, int* bm, int* bn);
-hipError_t launch_gemm(int cfg, bool ta, bool tb, const GemmDesc* descs, const int* prefix,
+// mode: GEMM_F_TA | GEMM_F_TB shared by all descriptors, or GEMM_MODE_MIXED
+hipError_t launch_gemm(int cfg, int mode, const GemmDesc* descs, const int* prefix,
                        int ndesc, int ntiles, const IoEntry* io, hipStream_t stream);
 
 // Codec: elements per workgroup tile.
@@ -27,22 +29,28 @@ hipError_t launch_codec_copy(const CodecDesc* descs, const int* prefix, int ndes
                              hipStream_t stream);
 void host_codebook(float levels[16], float midpoints[15]);
 
-// Householder panel factorization, one workgroup per panel.
+// Householder panel factorization, one workgroup per panel.  Panels of height
+// h <= 16 * rows_class (rows_class in {2,4,...,64}) keep the panel in registers;
+// rows_class 0 works on taller panels in place in global memory.
 constexpr int PANEL_THREADS = 512;
-constexpr int PANEL_LDS_MAX_ROWS = 1024;     // panels up to this height are staged in LDS
-size_t panel_lds_bytes(bool in_lds, int max_h);
-hipError_t launch_panel(bool in_lds, const PanelDesc* descs, int ndesc, int max_h,
+constexpr int PANEL_LDS_MAX_ROWS = 1024;
+int panel_rows_class(int h);
+size_t panel_lds_bytes(bool in_regs, int max_h);
+hipError_t launch_panel(int rows_class, const PanelDesc* descs, int ndesc, int max_h,
                         hipStream_t stream);
 
 // Small per-column / per-element kernels.
-constexpr int RAYLEIGH_COLS = 64;            // columns per workgroup
 constexpr int FILL_TILE = 4096;              // elements per workgroup
-hipError_t launch_rayleigh(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
-                           uint32_t* flag, hipStream_t stream);
+// lam_j = max(sum_t partial[t][j], 0) over the per-tile partial rows of the fused
+// column-dot GEMM epilogue
+hipError_t launch_rayleigh_reduce(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                                  uint32_t* flag, hipStream_t stream);
+hipError_t launch_identity_fill(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                                hipStream_t stream);
+hipError_t launch_sign_flip(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+                            hipStream_t stream);
 hipError_t launch_root_scaling(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
                                float eps, uint32_t* flag, hipStream_t stream);
-hipError_t launch_sign_diag(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
-                            hipStream_t stream);
 hipError_t launch_identity_state(const InitDesc* descs, const int* prefix, int ndesc, int ntiles,
                                  hipStream_t stream);
 

@@ -32,12 +32,12 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 enum Family { FAM_GEMM = 0, FAM_DEQUANT, FAM_QUANT, FAM_PANEL, FAM_RAYLEIGH, FAM_ELEMENTWISE, FAM_N };
 const char* kFamilyNames[FAM_N] = {"gemm", "dequant", "quant", "qr_panel", "rayleigh", "elementwise"};
 
-enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_SIGN, K_INIT };
+enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT };
 
 struct Launch {
     Kind kind = K_GEMM;
     int cfg = 0;
-    bool ta = false, tb = false, lds = false;
+    int mode = 0;        // GEMM: shared transpose flags or GEMM_MODE_MIXED; panel: rows class
     size_t desc_off = 0, prefix_off = 0;   // offsets inside the descriptor region
     int ndesc = 0, ntiles = 0, max_h = 0;
     double flops = 0, bytes = 0;
@@ -50,7 +50,7 @@ struct Side {
     // state offsets
     size_t codes = 0, scales = 0, lam = 0, rcodes = 0, rscales = 0, d = 0;
     // workspace offsets
-    size_t Vs = 0, Vr = 0, Tmp = 0, Wg = 0, Lt = 0, Pm = 0, Qm = 0, Vb = 0, Yb = 0, Z = 0, rdiag = 0;
+    size_t Vs = 0, Vr = 0, Tmp = 0, Wg = 0, Lt = 0, Pm = 0, Qm = 0, Vb = 0, Yb = 0, Z = 0, W = 0, rdiag = 0;
     std::vector<size_t> panel_rows;   // row offset of panel s inside Vb / Yb
 };
 
@@ -73,14 +73,14 @@ struct shampoo4_ctx_s {
     std::vector<size_t> X1, X2;          // per block precondition temporaries
     size_t io_off = 0, flag_off = 0, desc_base = 0;
     std::vector<uint8_t> blob;           // descriptor region contents
-    int lds_rows = 0;
+    size_t lds_limit = 0;                // bytes of LDS one workgroup may use
     int max_panels = 0;
 
     Seq deq_stats, deq_root, init_seq;
     std::vector<Seq> bj_stats, bj_root;
     Seq stats_x[2], stats_g, power_first[2], power_next;
-    std::vector<Seq> panel, trail, form;
-    Seq sign, ray_gemm, rayleigh, quant, root_d, root_copy;
+    std::vector<Seq> panel, trail, upd;
+    Seq qinit, sign, ray_gemm, rayleigh, quant, root_d, root_copy;
     Seq pre[4];
 
     bool root_v_valid = false;        // workspace Vr holds Bjorck(dequant(root codes))
@@ -125,46 +125,50 @@ struct shampoo4_ctx_s {
         bool ta, tb;
     };
 
+    // One launch for a batch of products (mixed transposes allowed).
     Seq make_gemm(std::vector<GemmItem> items) {
-        Seq out;
-        for (int mode = 0; mode < 4; ++mode) {
-            const bool ta = mode & 1, tb = mode & 2;
-            std::vector<GemmDesc> ds;
-            for (auto& it : items)
-                if (it.ta == ta && it.tb == tb && it.d.M > 0 && it.d.N > 0) ds.push_back(it.d);
-            if (ds.empty()) continue;
-            int maxM = 0;
-            long tiles128 = 0;
-            for (auto& d : ds) {
-                maxM = std::max(maxM, d.M);
-                tiles128 += (long)((d.M + 127) / 128) * ((d.N + 127) / 128);
-            }
-            int cfgsel = maxM <= 32 ? GEMM_32x128 : (tiles128 >= 512 ? GEMM_128x128 : GEMM_64x64);
-            int bm, bn;
-            gemm_tile_dims(cfgsel, &bm, &bn);
-            std::vector<int> prefix;
-            int total = 0;
-            Launch L;
-            for (auto& d : ds) {
-                d.tiles_m = (d.M + bm - 1) / bm;
-                prefix.push_back(total);
-                total += d.tiles_m * ((d.N + bn - 1) / bn);
-                L.flops += 2.0 * d.M * d.N * d.K;
-                L.bytes += 4.0 * ((double)d.M * d.K + (double)d.K * d.N + (double)d.M * d.N *
-                                                                           (d.beta != 0.f ? 2 : 1));
-            }
-            prefix.push_back(total);
-            L.kind = K_GEMM;
-            L.cfg = cfgsel;
-            L.ta = ta;
-            L.tb = tb;
-            L.ndesc = (int)ds.size();
-            L.ntiles = total;
-            L.desc_off = blob_put(ds.data(), ds.size() * sizeof(GemmDesc));
-            L.prefix_off = blob_put(prefix.data(), prefix.size() * sizeof(int));
-            out.push_back(L);
+        std::vector<GemmDesc> ds;
+        int modes = 0, first_mode = -2;
+        for (auto& it : items) {
+            if (it.d.M <= 0 || it.d.N <= 0) continue;
+            GemmDesc d = it.d;
+            d.flags = (d.flags & ~(GEMM_F_TA | GEMM_F_TB)) | (it.ta ? GEMM_F_TA : 0) | (it.tb ? GEMM_F_TB : 0);
+            const int m = d.flags & (GEMM_F_TA | GEMM_F_TB);
+            if (first_mode == -2) first_mode = m;
+            if (m != first_mode) modes = 1;
+            ds.push_back(d);
         }
-        return out;
+        if (ds.empty()) return {};
+        int maxM = 0;
+        long tiles128 = 0;
+        for (auto& d : ds) {
+            maxM = std::max(maxM, d.M);
+            tiles128 += (long)((d.M + 127) / 128) * ((d.N + 127) / 128);
+        }
+        const int cfgsel = maxM <= 32 ? GEMM_32x128 : (tiles128 >= 512 ? GEMM_128x128 : GEMM_64x64);
+        int bm, bn;
+        gemm_tile_dims(cfgsel, &bm, &bn);
+        std::vector<int> prefix;
+        int total = 0;
+        Launch L;
+        for (auto& d : ds) {
+            d.tiles_m = (d.M + bm - 1) / bm;
+            prefix.push_back(total);
+            total += d.tiles_m * ((d.N + bn - 1) / bn);
+            L.flops += 2.0 * d.M * d.N * d.K;
+            const bool coldot = d.flags & GEMM_F_COLDOT;
+            L.bytes += 4.0 * ((double)d.M * d.K + (double)d.K * d.N +
+                              (double)d.M * d.N * ((d.beta != 0.f || coldot) ? 2 : 1));
+        }
+        prefix.push_back(total);
+        L.kind = K_GEMM;
+        L.cfg = cfgsel;
+        L.mode = modes ? GEMM_MODE_MIXED : first_mode;
+        L.ndesc = (int)ds.size();
+        L.ntiles = total;
+        L.desc_off = blob_put(ds.data(), ds.size() * sizeof(GemmDesc));
+        L.prefix_off = blob_put(prefix.data(), prefix.size() * sizeof(int));
+        return {L};
     }
 
     template <class D>
@@ -225,6 +229,7 @@ struct shampoo4_ctx_s {
                 S.Vb = ws_take(rows * kPanel * 4);
                 S.Yb = ws_take(rows * kPanel * 4);
                 S.Z = ws_take((size_t)kPanel * p * 4);
+                S.W = ws_take((size_t)kPanel * p * 4);
                 S.rdiag = ws_take(p * 4);
             }
             X1[b] = ws_take((size_t)shapes[b].m * shapes[b].n * 4);
@@ -327,15 +332,17 @@ struct shampoo4_ctx_s {
             power_next = make_gemm(pn);
         }
 
-        // Householder QR of P, panel by panel, then explicit Q by backward accumulation
+        // Householder QR of P, panel by panel.  Q is accumulated forward
+        // (Q <- Q H_k = Q - (Q Y) V^T) in the same launches as the trailing update
+        // (A <- H_k^T A = A - V (Y^T A)); the columns are flipped to diag(R) >= 0 at the end.
         panel.assign(max_panels, Seq{});
         trail.assign(max_panels, Seq{});
-        form.assign(max_panels, Seq{});
+        upd.assign(max_panels, Seq{});
         for (int sidx = 0; sidx < max_panels; ++sidx) {
-            std::vector<PanelDesc> pl_lds, pl_glb;
-            std::vector<int> t_lds, t_glb;
-            int mh_lds = 0, mh_glb = 0;
-            std::vector<GemmItem> t1, t2, f1, f2;
+            // panels bucketed by register class (0 = in place in global memory)
+            std::vector<std::vector<PanelDesc>> byc(8);
+            std::vector<int> maxh(8, 0);
+            std::vector<GemmItem> t1, t2;
             for (auto& S : sides) {
                 const int p = S.p;
                 const int c0 = sidx * kPanel;
@@ -352,44 +359,42 @@ struct shampoo4_ctx_s {
                 pd.c0 = c0;
                 pd.h = h;
                 pd.nb = nbw;
-                if (h <= lds_rows) {
-                    pl_lds.push_back(pd); t_lds.push_back(1); mh_lds = std::max(mh_lds, h);
-                } else {
-                    pl_glb.push_back(pd); t_glb.push_back(1); mh_glb = std::max(mh_glb, h);
-                }
+                int cls = panel_rows_class(h);
+                if (cls > 0 && panel_lds_bytes(true, h) > lds_limit) cls = 0;
+                int bucket = 0;
+                while (cls > 0 && (2 << bucket) < cls) ++bucket;
+                bucket = cls > 0 ? bucket + 1 : 0;
+                byc[bucket].push_back(pd);
+                maxh[bucket] = std::max(maxh[bucket], h);
                 float* Vp = pd.V;
                 float* Yp = pd.Y;
                 float* Z = wsf(S.Z);
+                float* Wb = wsf(S.W);
+                float* Qs = wsf(S.Qm) + c0;                       // Q[:, c0:]
                 const int ntr = p - c0 - nbw;
                 if (ntr > 0) {
                     float* At = wsf(S.Pm) + (int64_t)c0 * p + c0 + nbw;
                     t1.push_back({gd(Yp, kPanel, At, p, Z, p, nbw, ntr, h), true, false});
                     t2.push_back({gd(Vp, kPanel, Z, p, At, p, h, ntr, nbw, -1.f, 1.f, At, p), false, false});
                 }
-                float* Qs = wsf(S.Qm) + (int64_t)c0 * p + c0;
-                f1.push_back({gd(Vp, kPanel, Qs, p, Z, p, nbw, p - c0, h), true, false});
-                f2.push_back({gd(Yp, kPanel, Z, p, Qs, p, h, p - c0, nbw, -1.f, 1.f, Qs, p), false, false});
+                t1.push_back({gd(Qs, p, Yp, kPanel, Wb, kPanel, p, nbw, h), false, false});
+                t2.push_back({gd(Wb, kPanel, Vp, kPanel, Qs, p, p, h, nbw, -1.f, 1.f, Qs, p), false, true});
             }
-            if (!pl_lds.empty()) {
-                Launch L = make_items(K_PANEL, pl_lds, t_lds);
-                L.lds = true; L.max_h = mh_lds; L.ntiles = (int)pl_lds.size();
+            for (int b = 0; b < 8; ++b) {
+                if (byc[b].empty()) continue;
+                std::vector<int> ones(byc[b].size(), 1);
+                Launch L = make_items(K_PANEL, byc[b], ones);
+                L.mode = b == 0 ? 0 : (1 << b);
+                L.max_h = maxh[b];
+                L.ntiles = (int)byc[b].size();
                 panel[sidx].push_back(L);
             }
-            if (!pl_glb.empty()) {
-                Launch L = make_items(K_PANEL, pl_glb, t_glb);
-                L.lds = false; L.max_h = mh_glb; L.ntiles = (int)pl_glb.size();
-                panel[sidx].push_back(L);
-            }
-            Seq a = make_gemm(t1), b = make_gemm(t2);
-            trail[sidx] = a;
-            trail[sidx].insert(trail[sidx].end(), b.begin(), b.end());
-            Seq c = make_gemm(f1), e = make_gemm(f2);
-            form[sidx] = c;
-            form[sidx].insert(form[sidx].end(), e.begin(), e.end());
+            trail[sidx] = make_gemm(t1);
+            upd[sidx] = make_gemm(t2);
         }
         {
-            std::vector<VecDesc> sg, ry, rt;
-            std::vector<int> tsg, try_, trt;
+            std::vector<VecDesc> qi, rr, rt;
+            std::vector<int> tqi, trr, trt;
             std::vector<GemmItem> yg;
             std::vector<CodecDesc> qd, cp;
             std::vector<int> tq, tcp;
@@ -401,13 +406,12 @@ struct shampoo4_ctx_s {
                 VecDesc v;
                 std::memset(&v, 0, sizeof(v));
                 v.out = wsf(S.Qm); v.aux = wsf(S.rdiag); v.ld = p; v.p = p;
-                sg.push_back(v);
-                tsg.push_back((int)(((int64_t)p * p + FILL_TILE - 1) / FILL_TILE));
-                yg.push_back({gd(wsf(S.Lt), p, wsf(S.Qm), p, wsf(S.Wg), p, p, p, p), false, false});
-                std::memset(&v, 0, sizeof(v));
-                v.a = wsf(S.Qm); v.b = wsf(S.Wg); v.out = stf(S.lam); v.ld = p; v.p = p;
-                ry.push_back(v);
-                try_.push_back((p + RAYLEIGH_COLS - 1) / RAYLEIGH_COLS);
+                qi.push_back(v);
+                tqi.push_back((int)(((int64_t)p * p + FILL_TILE - 1) / FILL_TILE));
+                // Rayleigh: partial column sums of Q .* (L~ Q) per row tile into Wg
+                GemmDesc d = gd(wsf(S.Lt), p, wsf(S.Qm), p, wsf(S.Wg), p, p, p, p, 1.f, 0.f, wsf(S.Qm), p);
+                d.flags = GEMM_F_COLDOT;
+                yg.push_back({d, false, false});
                 std::memset(&v, 0, sizeof(v));
                 v.a = stf(S.lam); v.out = stf(S.d); v.p = p;
                 rt.push_back(v);
@@ -433,9 +437,19 @@ struct shampoo4_ctx_s {
                 in.push_back(id);
                 tin.push_back((int)((std::max<int64_t>(S.nqb, p) + 255) / 256));
             }
-            sign = {make_items(K_SIGN, sg, tsg)};
+            qinit = {make_items(K_IDENTITY, qi, tqi)};
+            sign = {make_items(K_SIGN, qi, tqi)};
             ray_gemm = make_gemm(yg);
-            rayleigh = {make_items(K_RAYLEIGH, ry, try_)};
+            int bm = 32, bn = 128;
+            gemm_tile_dims(ray_gemm.empty() ? GEMM_32x128 : ray_gemm[0].cfg, &bm, &bn);
+            for (auto& S : sides) {
+                VecDesc v;
+                std::memset(&v, 0, sizeof(v));
+                v.a = wsf(S.Wg); v.out = stf(S.lam); v.ld = S.p; v.p = S.p; v.rows = (S.p + bm - 1) / bm;
+                rr.push_back(v);
+                trr.push_back((S.p + 255) / 256);
+            }
+            rayleigh = {make_items(K_RAYLEIGH, rr, trr)};
             root_d = {make_items(K_ROOT, rt, trt)};
             Launch Lq = make_items(K_QUANT, qd, tq);
             Lq.bytes = qbytes;
@@ -486,7 +500,7 @@ struct shampoo4_ctx_s {
         switch (L.kind) {
             case K_GEMM:
                 fam = FAM_GEMM;
-                e = launch_gemm(L.cfg, L.ta, L.tb, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
+                e = launch_gemm(L.cfg, L.mode, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
                                 prefix, L.ndesc, L.ntiles, io, s);
                 break;
             case K_DEQUANT:
@@ -505,20 +519,24 @@ struct shampoo4_ctx_s {
                 break;
             case K_PANEL:
                 fam = FAM_PANEL;
-                e = launch_panel(L.lds, reinterpret_cast<const PanelDesc*>(base + L.desc_off), L.ndesc,
+                e = launch_panel(L.mode, reinterpret_cast<const PanelDesc*>(base + L.desc_off), L.ndesc,
                                  L.max_h, s);
                 break;
             case K_RAYLEIGH:
                 fam = FAM_RAYLEIGH;
-                e = launch_rayleigh(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix, L.ndesc,
-                                    L.ntiles, flag, s);
+                e = launch_rayleigh_reduce(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix,
+                                           L.ndesc, L.ntiles, flag, s);
                 break;
             case K_ROOT:
                 e = launch_root_scaling(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix,
                                         L.ndesc, L.ntiles, cfg.eps, flag, s);
                 break;
+            case K_IDENTITY:
+                e = launch_identity_fill(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix,
+                                         L.ndesc, L.ntiles, s);
+                break;
             case K_SIGN:
-                e = launch_sign_diag(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix, L.ndesc,
+                e = launch_sign_flip(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix, L.ndesc,
                                      L.ntiles, s);
                 break;
             case K_INIT:
@@ -619,7 +637,7 @@ std::unique_ptr<shampoo4_ctx_s> make_plan(const shampoo4_config* cfg, int32_t nb
     c->cfg = *cfg;
     c->nb = nblocks;
     c->shapes.assign(shapes, shapes + nblocks);
-    c->lds_rows = PANEL_LDS_MAX_ROWS;
+    c->lds_limit = 160 * 1024;
     c->layout();
     return c;
 }
@@ -652,7 +670,8 @@ shampoo4_status shampoo4_plan(const shampoo4_config* cfg, int32_t nblocks, const
     auto c = make_plan(cfg, nblocks, shapes);
     c->build();   // null bases: only the sizes matter
     *state_bytes = c->st_bytes;
-    *workspace_bytes = c->desc_base + align_up(c->blob.size());
+    // slack: the panel launches are regrouped at init by the device's LDS limit
+    *workspace_bytes = c->desc_base + align_up(c->blob.size()) + (size_t)c->max_panels * 8 * kAlign;
     return SHAMPOO4_OK;
 }
 
@@ -666,13 +685,12 @@ shampoo4_status shampoo4_init(const shampoo4_config* cfg, int32_t nblocks, const
     if ((reinterpret_cast<uintptr_t>(state) % kAlign) || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
         return SHAMPOO4_EALIGN;
     auto c = make_plan(cfg, nblocks, shapes);
-    {   // panels staged in LDS up to what one workgroup may allocate
+    {   // panel register classes are limited by what one workgroup may allocate in LDS
         int dev = 0, lds = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SHAMPOO4_EHIP;
         if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
             return SHAMPOO4_EHIP;
-        const int rows = (int)(((size_t)lds - panel_lds_bytes(false, 0)) / (33 * sizeof(float)));
-        c->lds_rows = std::max(0, std::min(PANEL_LDS_MAX_ROWS, rows));
+        c->lds_limit = (size_t)lds;
     }
     c->st = static_cast<uint8_t*>(state);
     c->ws = static_cast<uint8_t*>(workspace);
@@ -723,12 +741,13 @@ shampoo4_status shampoo4_update_stats(shampoo4_ctx c, const shampoo4_io* io, voi
     if (e == hipSuccess) e = c->run(c->stats_g, s);
     for (int it = 0; it < c->cfg.power_iters && e == hipSuccess; ++it) {
         e = c->run(it == 0 ? c->power_first[var] : c->power_next, s);
+        if (e == hipSuccess) e = c->run(c->qinit, s);
         for (int p = 0; p < c->max_panels && e == hipSuccess; ++p) {
             e = c->run(c->panel[p], s);
             if (e == hipSuccess) e = c->run(c->trail[p], s);
+            if (e == hipSuccess) e = c->run(c->upd[p], s);
         }
         if (e == hipSuccess) e = c->run(c->sign, s);
-        for (int p = c->max_panels - 1; p >= 0 && e == hipSuccess; --p) e = c->run(c->form[p], s);
     }
     if (e == hipSuccess) e = c->run(c->ray_gemm, s);
     if (e == hipSuccess) e = c->run(c->rayleigh, s);
@@ -891,7 +910,7 @@ shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t tra
     if (hipMemcpyAsync(workspace, tmp.blob.data(), tmp.blob.size(), hipMemcpyHostToDevice, s) != hipSuccess)
         return SHAMPOO4_EHIP;
     const uint8_t* base = static_cast<const uint8_t*>(workspace);
-    hipError_t e = launch_gemm(L.cfg, L.ta, L.tb, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
+    hipError_t e = launch_gemm(L.cfg, L.mode, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
                                reinterpret_cast<const int*>(base + L.prefix_off), L.ndesc, L.ntiles, nullptr, s);
     return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }

@@ -124,6 +124,7 @@ def test_single_64x32_root_cache():
     ([(40, 72), (33, 33), (100, 7)], 2, 1, 2, True),      # ragged, across panels
     ([(96, 160), (130, 65)], 0, 2, 1, False),             # no Bjorck, two power steps
     ([(64, 64)], 5, 1, 1, True),
+    ([(1100, 40)], 1, 1, 1, True),                        # panels taller than the register path
 ])
 def test_ragged_batches(shapes, k, power_iters, T, cache):
     require_gpu()
