@@ -192,7 +192,11 @@ def main():
             log(f"[bench] {name:12s} launches {r['launches']:6d}  {r['ms'] / steps:9.3f} ms/step  "
                 f"{r['flops'] / max(r['ms'], 1e-9) / 1e9:8.2f} TFLOP/s  "
                 f"{r['bytes'] / max(r['ms'], 1e-9) / 1e6:8.1f} GB/s")
-    g = rep["gemm"]
+    g = {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0}
+    for name, r in rep.items():
+        if name.startswith("gemm"):
+            for k in g:
+                g[k] += r[k]
     gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12 if g["ms"] > 0 else 0.0
     q = rep["quant"]
     quant_gbps = q["bytes"] / (q["ms"] * 1e-3) / 1e9 if q["ms"] > 0 else 0.0

@@ -29,8 +29,14 @@ constexpr int kMaxDim = 8192;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
-enum Family { FAM_GEMM = 0, FAM_DEQUANT, FAM_QUANT, FAM_PANEL, FAM_RAYLEIGH, FAM_ELEMENTWISE, FAM_N };
-const char* kFamilyNames[FAM_N] = {"gemm", "dequant", "quant", "qr_panel", "rayleigh", "elementwise"};
+// Timing families: the matrix products are split by the stage they serve.
+enum Family {
+    FAM_GEMM_BJORCK = 0, FAM_GEMM_STATS, FAM_GEMM_POWER, FAM_GEMM_QR, FAM_GEMM_RAYLEIGH,
+    FAM_GEMM_PRECOND, FAM_DEQUANT, FAM_QUANT, FAM_PANEL, FAM_RAYLEIGH, FAM_ELEMENTWISE, FAM_N
+};
+const char* kFamilyNames[FAM_N] = {"gemm_bjorck", "gemm_stats", "gemm_power", "gemm_qr", "gemm_rayleigh",
+                                   "gemm_precond", "dequant", "quant", "qr_panel", "rayleigh",
+                                   "elementwise"};
 
 enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT };
 
@@ -38,6 +44,7 @@ struct Launch {
     Kind kind = K_GEMM;
     int cfg = 0;
     int mode = 0;        // GEMM: shared transpose flags or GEMM_MODE_MIXED; panel: rows class
+    int fam = FAM_ELEMENTWISE;
     size_t desc_off = 0, prefix_off = 0;   // offsets inside the descriptor region
     int ndesc = 0, ntiles = 0, max_h = 0;
     double flops = 0, bytes = 0;
@@ -126,7 +133,7 @@ struct shampoo4_ctx_s {
     };
 
     // One launch for a batch of products (mixed transposes allowed).
-    Seq make_gemm(std::vector<GemmItem> items) {
+    Seq make_gemm(std::vector<GemmItem> items, int fam) {
         std::vector<GemmDesc> ds;
         int modes = 0, first_mode = -2;
         for (auto& it : items) {
@@ -162,6 +169,7 @@ struct shampoo4_ctx_s {
         }
         prefix.push_back(total);
         L.kind = K_GEMM;
+        L.fam = fam;
         L.cfg = cfgsel;
         L.mode = modes ? GEMM_MODE_MIXED : first_mode;
         L.ndesc = (int)ds.size();
@@ -175,6 +183,8 @@ struct shampoo4_ctx_s {
     Launch make_items(Kind kind, const std::vector<D>& ds, const std::vector<int>& tiles) {
         Launch L;
         L.kind = kind;
+        L.fam = kind == K_DEQUANT ? FAM_DEQUANT : kind == K_QUANT ? FAM_QUANT : kind == K_PANEL ? FAM_PANEL
+              : kind == K_RAYLEIGH ? FAM_RAYLEIGH : FAM_ELEMENTWISE;
         std::vector<int> prefix;
         int total = 0;
         for (int t : tiles) {
@@ -288,8 +298,8 @@ struct shampoo4_ctx_s {
                 upd.push_back({gd(wsf(in), p, wsf(S.Wg), p, wsf(out), p, p, p, p, -0.5f, 1.5f, wsf(in), p),
                                false, false});
             }
-            Seq s = make_gemm(gram);
-            Seq u = make_gemm(upd);
+            Seq s = make_gemm(gram, FAM_GEMM_BJORCK);
+            Seq u = make_gemm(upd, FAM_GEMM_BJORCK);
             s.insert(s.end(), u.begin(), u.end());
             iters.push_back(s);
         }
@@ -312,8 +322,8 @@ struct shampoo4_ctx_s {
                 xs.push_back({d, false, true});
                 pw.push_back({gd(wsf(S.Lt), p, V, p, wsf(S.Pm), p, p, p, p), false, false});
             }
-            stats_x[var] = make_gemm(xs);
-            power_first[var] = make_gemm(pw);
+            stats_x[var] = make_gemm(xs, FAM_GEMM_STATS);
+            power_first[var] = make_gemm(pw, FAM_GEMM_POWER);
         }
         {
             std::vector<GemmItem> gs, pn;
@@ -328,8 +338,8 @@ struct shampoo4_ctx_s {
                     pn.push_back({gd(wsf(S.Lt), p, wsf(S.Qm), p, wsf(S.Pm), p, p, p, p), false, false});
                 }
             }
-            stats_g = make_gemm(gs);
-            power_next = make_gemm(pn);
+            stats_g = make_gemm(gs, FAM_GEMM_STATS);
+            power_next = make_gemm(pn, FAM_GEMM_POWER);
         }
 
         // Householder QR of P, panel by panel.  Q is accumulated forward
@@ -389,8 +399,8 @@ struct shampoo4_ctx_s {
                 L.ntiles = (int)byc[b].size();
                 panel[sidx].push_back(L);
             }
-            trail[sidx] = make_gemm(t1);
-            upd[sidx] = make_gemm(t2);
+            trail[sidx] = make_gemm(t1, FAM_GEMM_QR);
+            upd[sidx] = make_gemm(t2, FAM_GEMM_QR);
         }
         {
             std::vector<VecDesc> qi, rr, rt;
@@ -439,7 +449,7 @@ struct shampoo4_ctx_s {
             }
             qinit = {make_items(K_IDENTITY, qi, tqi)};
             sign = {make_items(K_SIGN, qi, tqi)};
-            ray_gemm = make_gemm(yg);
+            ray_gemm = make_gemm(yg, FAM_GEMM_RAYLEIGH);
             int bm = 32, bn = 128;
             gemm_tile_dims(ray_gemm.empty() ? GEMM_32x128 : ray_gemm[0].cfg, &bm, &bn);
             for (auto& S : sides) {
@@ -476,10 +486,10 @@ struct shampoo4_ctx_s {
                 d4.d_io = b;
                 p4.push_back({d4, false, true});
             }
-            pre[0] = make_gemm(p1);
-            pre[1] = make_gemm(p2);
-            pre[2] = make_gemm(p3);
-            pre[3] = make_gemm(p4);
+            pre[0] = make_gemm(p1, FAM_GEMM_PRECOND);
+            pre[1] = make_gemm(p2, FAM_GEMM_PRECOND);
+            pre[2] = make_gemm(p3, FAM_GEMM_PRECOND);
+            pre[3] = make_gemm(p4, FAM_GEMM_PRECOND);
         }
     }
 
@@ -496,20 +506,17 @@ struct shampoo4_ctx_s {
             (void)hipEventRecord(rec.e0, s);
         }
         hipError_t e = hipSuccess;
-        int fam = FAM_ELEMENTWISE;
+        const int fam = L.fam;
         switch (L.kind) {
             case K_GEMM:
-                fam = FAM_GEMM;
                 e = launch_gemm(L.cfg, L.mode, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
                                 prefix, L.ndesc, L.ntiles, io, s);
                 break;
             case K_DEQUANT:
-                fam = FAM_DEQUANT;
                 e = launch_dequant(reinterpret_cast<const CodecDesc*>(base + L.desc_off), prefix, L.ndesc,
                                    L.ntiles, s);
                 break;
             case K_QUANT:
-                fam = FAM_QUANT;
                 e = launch_quant(reinterpret_cast<const CodecDesc*>(base + L.desc_off), prefix, L.ndesc,
                                  L.ntiles, flag, s);
                 break;
@@ -518,12 +525,10 @@ struct shampoo4_ctx_s {
                                       L.ndesc, L.ntiles, s);
                 break;
             case K_PANEL:
-                fam = FAM_PANEL;
                 e = launch_panel(L.mode, reinterpret_cast<const PanelDesc*>(base + L.desc_off), L.ndesc,
                                  L.max_h, s);
                 break;
             case K_RAYLEIGH:
-                fam = FAM_RAYLEIGH;
                 e = launch_rayleigh_reduce(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix,
                                            L.ndesc, L.ntiles, flag, s);
                 break;
@@ -901,7 +906,7 @@ shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t tra
                             beta != 0.f ? C[i] : nullptr, beta != 0.f ? ldc[i] : 0);
         items.push_back({d, transA != 0, transB != 0});
     }
-    Seq seq = tmp.make_gemm(items);
+    Seq seq = tmp.make_gemm(items, FAM_GEMM_PRECOND);
     if (seq.empty()) return SHAMPOO4_OK;
     const Launch& L = seq[0];
     hipStream_t s = as_stream(stream);

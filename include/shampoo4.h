@@ -199,8 +199,10 @@ SHAMPOO4_API shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA
 /* Kernel timing (HIP events around every launch of the next calls on a context).
  * enable != 0 starts recording (clears previous records); the report waits for the
  * device and returns, per kernel family, the number of launches, total milliseconds,
- * and algorithmic flops and bytes.  names: "gemm", "dequant", "quant", "qr_panel",
- * "rayleigh", "elementwise".  Host arrays of length *count (in: capacity, out: used). */
+ * and algorithmic flops and bytes.  names: "gemm_bjorck", "gemm_stats", "gemm_power",
+ * "gemm_qr", "gemm_rayleigh", "gemm_precond" (the matrix products by the stage they
+ * serve), "dequant", "quant", "qr_panel", "rayleigh", "elementwise".  Host arrays of
+ * length *count (in: capacity, out: used). */
 SHAMPOO4_API shampoo4_status shampoo4_timing(shampoo4_ctx ctx, int32_t enable);
 SHAMPOO4_API shampoo4_status shampoo4_timing_report(shampoo4_ctx ctx, int32_t* count, const char** names,
                                        int64_t* launches, double* total_ms,
