@@ -21,6 +21,9 @@ struct IoEntry {
 // One matrix product D = alpha * op(A) op(B) [* rscale rows][* cscale cols] + beta * C.
 // op(B)'s row k is multiplied by kscale[k] when kscale is set.  A pointer given by an
 // io index (>= 0) is taken from the call's io table instead of the field.
+// Split K: with ksplit > 1 the K range is cut into chunks of kchunk and chunk s writes
+// its partial product (beta must be 0) to D + s * dslab.  A consumer reads such
+// partials back summed: op(A) = sum_{s < anslab} A[s * aslab ...] (same for B).
 struct GemmDesc {
     const float* A;
     const float* B;
@@ -30,19 +33,22 @@ struct GemmDesc {
     const float* rscale;
     const float* cscale;
     int64_t lda, ldb, ldc, ldd;
+    int64_t aslab, bslab, dslab;
     int32_t M, N, K;
     int32_t tiles_m;          // tiles along M for the launch's tile shape
     float alpha, beta;
     int32_t a_io, b_io, d_io; // -1 or index into the io table (A/B = G, D = P)
     int32_t flags;            // GEMM_F_* below
+    int32_t ksplit, kchunk, anslab, bnslab;
+    int32_t pad0, pad1;
 };
+static_assert(sizeof(GemmDesc) == 176, "GemmDesc layout");
 enum : int32_t {
     GEMM_F_TA = 1,            // op(A) = A^T
     GEMM_F_TB = 2,            // op(B) = B^T
     GEMM_F_COLDOT = 4,        // epilogue: D[tile_m][col] = sum over the tile's rows of
                               //   alpha * (op(A) op(B))[row][col] * C[row][col]; ldd = row stride
 };
-static_assert(sizeof(GemmDesc) == 128, "GemmDesc layout");
 
 // Codec work item: one flattened matrix of n fp32 elements.
 struct CodecDesc {

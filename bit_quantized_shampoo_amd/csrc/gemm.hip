@@ -23,7 +23,10 @@
 //    (COLDOT) reduces alpha * acc * C over the tile's rows into one partial row
 //    per tile (used for the Rayleigh quotients q_j^T L~ q_j without writing L~ Q).
 //  * a launch either has one transpose mode (specialized kernel) or mixes them
-//    (one kernel, branch uniform per workgroup).
+//    (one kernel, branch uniform per workgroup);
+//  * split K for long-K, few-tile products: chunk s of the K range writes its own
+//    partial slab and the consuming product sums the slabs while loading its
+//    operand tiles (a fixed order, so results are deterministic).
 #include "kernels.hpp"
 
 namespace s4 {
@@ -44,6 +47,21 @@ struct Tile {
     static constexpr int B_MAX = B_KC > B_MC ? B_KC : B_MC;
     static constexpr int RED = WM * BN;        // COLDOT cross-wave partials
 };
+
+__device__ __forceinline__ floatx4 load_quad(const float* __restrict__ base, int64_t ld,
+                                             int row, int col, int rows, int cols, bool vec_ok);
+
+// Sum of `nslab` split-K partials (slab stride `slab` elements); one slab is a plain load.
+__device__ __forceinline__ floatx4 load_quad_sum(const float* __restrict__ base, int64_t slab, int nslab,
+                                                 int64_t ld, int row, int col, int rows, int cols,
+                                                 bool vec_ok) {
+    floatx4 v = load_quad(base, ld, row, col, rows, cols, vec_ok);
+    for (int s = 1; s < nslab; ++s) {
+        const floatx4 w = load_quad(base + s * slab, ld, row, col, rows, cols, vec_ok);
+        v[0] += w[0]; v[1] += w[1]; v[2] += w[2]; v[3] += w[3];
+    }
+    return v;
+}
 
 __device__ __forceinline__ floatx4 load_quad(const float* __restrict__ base, int64_t ld,
                                              int row, int col, int rows, int cols, bool vec_ok) {
@@ -74,10 +92,15 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
     constexpr int RB = (NQB + 255) / 256;
 
     const int tiles_m = dsc.tiles_m;
-    const int tile_m = t % tiles_m;
+    const int tiles_mn = tiles_m * ((dsc.N + BN - 1) / BN);
+    const int ks = t / tiles_mn;                 // split-K chunk (0 without split)
+    const int tmn = t - ks * tiles_mn;
+    const int tile_m = tmn % tiles_m;
     const int row0 = tile_m * BM;
-    const int col0 = (t / tiles_m) * BN;
-    const int M = dsc.M, N = dsc.N, K = dsc.K;
+    const int col0 = (tmn / tiles_m) * BN;
+    const int M = dsc.M, N = dsc.N;
+    const int kbeg = ks * dsc.kchunk;
+    const int K = (dsc.ksplit > 1) ? min(dsc.K, kbeg + dsc.kchunk) : dsc.K;   // loads stop at K
 
     const float* A = dsc.A;
     int64_t lda = dsc.lda;
@@ -85,9 +108,11 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
     const float* B = dsc.B;
     int64_t ldb = dsc.ldb;
     if (dsc.b_io >= 0) { B = io[dsc.b_io].G; ldb = io[dsc.b_io].ldg; }
-    float* D = dsc.D;
+    float* D = dsc.D + ks * dsc.dslab;
     int64_t ldd = dsc.ldd;
     if (dsc.d_io >= 0) { D = io[dsc.d_io].P; ldd = io[dsc.d_io].ldp; }
+    const int anslab = dsc.anslab, bnslab = dsc.bnslab;
+    const int64_t aslab = dsc.aslab, bslab = dsc.bslab;
     const float* __restrict__ kscale = dsc.kscale;
 
     const bool avec = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && ((lda & 3) == 0);
@@ -118,10 +143,10 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
             if (q < NQA) {
                 if constexpr (!TA) {
                     const int i = q / (BK / 4), kq = (q % (BK / 4)) * 4;
-                    ra[r] = load_quad(A, lda, row0 + i, k0 + kq, M, K, avec);
+                    ra[r] = load_quad_sum(A, aslab, anslab, lda, row0 + i, k0 + kq, M, K, avec);
                 } else {
                     const int k = q / (BM / 4), iq = (q % (BM / 4)) * 4;
-                    ra[r] = load_quad(A, lda, k0 + k, row0 + iq, K, M, avec);
+                    ra[r] = load_quad_sum(A, aslab, anslab, lda, k0 + k, row0 + iq, K, M, avec);
                 }
             }
         }
@@ -131,7 +156,7 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
             if (q < NQB) {
                 if constexpr (TB) {
                     const int j = q / (BK / 4), kq = (q % (BK / 4)) * 4;
-                    floatx4 v = load_quad(B, ldb, col0 + j, k0 + kq, N, K, bvec);
+                    floatx4 v = load_quad_sum(B, bslab, bnslab, ldb, col0 + j, k0 + kq, N, K, bvec);
                     if (kscale) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
@@ -140,7 +165,7 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
                     rb[r] = v;
                 } else {
                     const int k = q / (BN / 4), jq = (q % (BN / 4)) * 4;
-                    floatx4 v = load_quad(B, ldb, k0 + k, col0 + jq, K, N, bvec);
+                    floatx4 v = load_quad_sum(B, bslab, bnslab, ldb, k0 + k, col0 + jq, K, N, bvec);
                     if (kscale && k0 + k < K) {
                         const float s = kscale[k0 + k];
                         v[0] *= s; v[1] *= s; v[2] *= s; v[3] *= s;
@@ -182,9 +207,9 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
         }
     };
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (K - kbeg + BK - 1) / BK;
     if (nk > 0) {
-        load_slice(0);
+        load_slice(kbeg);
         store_slice(0);
     }
     __syncthreads();
@@ -192,7 +217,7 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         const bool more = kt + 1 < nk;
-        if (more) load_slice((kt + 1) * BK);
+        if (more) load_slice(kbeg + (kt + 1) * BK);
         const float* as = As + cur * A_SZ;
         const float* bs = Bs + cur * B_SZ;
 

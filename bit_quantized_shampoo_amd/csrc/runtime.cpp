@@ -25,6 +25,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kRing = 8;            // pinned io staging slots
 constexpr int kPanel = 32;          // Householder panel width
+constexpr int kMaxSplit = 8;        // split-K chunks of the skinny QR products
 constexpr int kMaxDim = 8192;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
@@ -161,7 +162,7 @@ struct shampoo4_ctx_s {
         for (auto& d : ds) {
             d.tiles_m = (d.M + bm - 1) / bm;
             prefix.push_back(total);
-            total += d.tiles_m * ((d.N + bn - 1) / bn);
+            total += d.tiles_m * ((d.N + bn - 1) / bn) * std::max(1, d.ksplit);
             L.flops += 2.0 * d.M * d.N * d.K;
             const bool coldot = d.flags & GEMM_F_COLDOT;
             L.bytes += 4.0 * ((double)d.M * d.K + (double)d.K * d.N +
@@ -238,8 +239,8 @@ struct shampoo4_ctx_s {
                 }
                 S.Vb = ws_take(rows * kPanel * 4);
                 S.Yb = ws_take(rows * kPanel * 4);
-                S.Z = ws_take((size_t)kPanel * p * 4);
-                S.W = ws_take((size_t)kPanel * p * 4);
+                S.Z = ws_take((size_t)kMaxSplit * kPanel * p * 4);   // split-K slabs of Y^T A
+                S.W = ws_take((size_t)kMaxSplit * kPanel * p * 4);   // split-K slabs of Q Y
                 S.rdiag = ws_take(p * 4);
             }
             X1[b] = ws_take((size_t)shapes[b].m * shapes[b].n * 4);
@@ -353,6 +354,21 @@ struct shampoo4_ctx_s {
             std::vector<std::vector<PanelDesc>> byc(8);
             std::vector<int> maxh(8, 0);
             std::vector<GemmItem> t1, t2;
+            // Split the long-K (K = h) products when the batch alone cannot fill the GPU.
+            long base_tiles = 0;
+            int min_h = 1 << 30;
+            for (auto& S : sides) {
+                const int c0 = sidx * kPanel;
+                if (c0 >= S.p) continue;
+                const int ntr = S.p - c0 - std::min(kPanel, S.p - c0);
+                base_tiles += (ntr + 63) / 64 + (S.p + 63) / 64;
+                min_h = std::min(min_h, S.p - c0);
+            }
+            int ksplit = 1;
+            if (base_tiles > 0 && base_tiles < 512) {
+                ksplit = (int)std::min<long>(kMaxSplit, (512 + base_tiles - 1) / base_tiles);
+                ksplit = std::max(1, std::min(ksplit, min_h / 64));
+            }
             for (auto& S : sides) {
                 const int p = S.p;
                 const int c0 = sidx * kPanel;
@@ -382,13 +398,24 @@ struct shampoo4_ctx_s {
                 float* Wb = wsf(S.W);
                 float* Qs = wsf(S.Qm) + c0;                       // Q[:, c0:]
                 const int ntr = p - c0 - nbw;
+                const int kchunk = ((h + ksplit - 1) / ksplit + 15) / 16 * 16;
+                const int nsplit = (h + kchunk - 1) / kchunk;
+                const int64_t zslab = (int64_t)kPanel * p, wslab = (int64_t)p * kPanel;
                 if (ntr > 0) {
                     float* At = wsf(S.Pm) + (int64_t)c0 * p + c0 + nbw;
-                    t1.push_back({gd(Yp, kPanel, At, p, Z, p, nbw, ntr, h), true, false});
-                    t2.push_back({gd(Vp, kPanel, Z, p, At, p, h, ntr, nbw, -1.f, 1.f, At, p), false, false});
+                    GemmDesc z = gd(Yp, kPanel, At, p, Z, p, nbw, ntr, h);
+                    z.ksplit = nsplit; z.kchunk = kchunk; z.dslab = zslab;
+                    t1.push_back({z, true, false});
+                    GemmDesc u = gd(Vp, kPanel, Z, p, At, p, h, ntr, nbw, -1.f, 1.f, At, p);
+                    u.bnslab = nsplit; u.bslab = zslab;
+                    t2.push_back({u, false, false});
                 }
-                t1.push_back({gd(Qs, p, Yp, kPanel, Wb, kPanel, p, nbw, h), false, false});
-                t2.push_back({gd(Wb, kPanel, Vp, kPanel, Qs, p, p, h, nbw, -1.f, 1.f, Qs, p), false, true});
+                GemmDesc w = gd(Qs, p, Yp, kPanel, Wb, kPanel, p, nbw, h);
+                w.ksplit = nsplit; w.kchunk = kchunk; w.dslab = wslab;
+                t1.push_back({w, false, false});
+                GemmDesc q = gd(Wb, kPanel, Vp, kPanel, Qs, p, p, h, nbw, -1.f, 1.f, Qs, p);
+                q.anslab = nsplit; q.aslab = wslab;
+                t2.push_back({q, false, true});
             }
             for (int b = 0; b < 8; ++b) {
                 if (byc[b].empty()) continue;
