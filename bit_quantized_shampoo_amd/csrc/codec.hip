@@ -16,9 +16,11 @@
 //  * quant: one lane per 4 consecutive elements (a 16-byte load), 16 lanes per
 //    block; the block absmax is a 4-step xor-shuffle reduction inside the
 //    16-lane group; each lane writes its 4 codes as one 16-bit store, lane 0 of
-//    the group writes the scale.
+//    the group writes the scale.  The code comes from one LDS table lookup keyed
+//    by the bits of x_hat instead of a scan over the 15 midpoints.
 //  * dequant: one lane per 8 elements (one 32-bit code word, two 16-byte
-//    stores), levels looked up in a 16-entry LDS table (conflict-free).
+//    stores), several words per lane in flight, levels looked up in a 16-entry
+//    LDS table.
 #include "kernels.hpp"
 
 namespace s4 {
@@ -43,37 +45,116 @@ constexpr float kLevelsHost[16] = {
     S4_LV(-225), S4_LV(-169), S4_LV(-121), S4_LV(-81), S4_LV(-49), S4_LV(-25), S4_LV(-9), 0.0f,
     S4_LV(1),    S4_LV(9),    S4_LV(25),   S4_LV(49),  S4_LV(81),  S4_LV(121), S4_LV(169), S4_LV(225)};
 
-__device__ __forceinline__ uint32_t code_of(float xh) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < 15; ++j) c += (xh > kMid[j]) ? 1u : 0u;
-    return c;
+// Code lookup without a midpoint scan.  The magnitude's float32 bit pattern, shifted
+// right by 21, is the exponent with the top two mantissa bits: a bucket of width at
+// most 1.25x.  Adjacent midpoints of one sign differ by at least 1.36x, so every
+// bucket over [2^-9, 2) holds at most one midpoint (checked at compile time below)
+// and magnitudes under 2^-9 lie below every midpoint.  Each (sign, bucket) entry
+// stores the code of a magnitude at or below the bucket's midpoint, the code above
+// it, and the midpoint's bit pattern as an unsigned threshold; the result equals the
+// count of midpoints strictly below x_hat for every float32 x_hat, signed zeros and
+// subnormals included.
+constexpr uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+constexpr int QB_E0 = 118 * 4;   // bucket 0 starts at 2^-9 (biased exponent 118)
+constexpr int QB_N = 40;         // buckets per sign, [2^-9, 2)
+
+constexpr int bucket_of(uint32_t mag) {
+    const int b = (int)(mag >> 21) - QB_E0;
+    return b < 0 ? 0 : (b >= QB_N ? QB_N - 1 : b);
 }
+
+struct QTab {
+    uint32_t thr[2 * QB_N];    // the in-bucket midpoint (as magnitude bits), or all ones
+    uint32_t code[2 * QB_N];   // low nibble: code at or below thr; next nibble: code above
+    int max_per_bucket;
+};
+
+constexpr QTab make_qtab() {
+    QTab t{};
+    t.max_per_bucket = 0;
+    for (int s = 0; s < 2; ++s) {
+        for (int b = 0; b < QB_N; ++b) {
+            const uint32_t lo_u = b > 0 ? (uint32_t)(b + QB_E0) << 21 : 0u;
+            int below = 0, inb = 0;
+            uint32_t thr = 0xffffffffu;
+            for (int j = 0; j < 15; ++j) {
+                const bool neg = kMid[j] < 0.0f;
+                if (neg != (s == 1)) continue;
+                const uint32_t mag = f32_bits(kMid[j]) & 0x7fffffffu;
+                if (mag < lo_u) ++below;
+                if (bucket_of(mag) == b) {
+                    ++inb;
+                    // positive: code rises once x_hat > m; negative: the count of
+                    // midpoints below x_hat drops once |x_hat| >= |m|
+                    thr = s == 0 ? mag : mag - 1u;
+                }
+            }
+            const int lo = s == 0 ? 7 + below : 7 - below;
+            const int hi = inb ? (s == 0 ? lo + 1 : lo - 1) : lo;
+            t.thr[s * QB_N + b] = thr;
+            t.code[s * QB_N + b] = (uint32_t)lo | ((uint32_t)hi << 4);
+            if (inb > t.max_per_bucket) t.max_per_bucket = inb;
+        }
+    }
+    return t;
+}
+
+constexpr QTab kQTab = make_qtab();
+static_assert(kQTab.max_per_bucket == 1, "a code bucket holds more than one midpoint");
+static_assert(f32_bits(kMid[7]) >> 21 >= QB_E0 && (f32_bits(-kMid[6]) >> 21) >= QB_E0,
+              "a midpoint lies below the first bucket");
+
+__constant__ QTab c_qtab = kQTab;
+
+__device__ __forceinline__ uint32_t code_of(float xh, const uint2* __restrict__ tab) {
+    const uint32_t u = __float_as_uint(xh);
+    const uint32_t mag = u & 0x7fffffffu;
+    const int b = min(max((int)(mag >> 21) - QB_E0, 0), QB_N - 1) + (int)(u >> 31) * QB_N;
+    const uint2 e = tab[b];
+    return mag > e.x ? (e.y >> 4) : (e.y & 15u);
+}
+
+// Dequantization: each lane expands DEQ_WORDS 32-bit code words (8 elements each)
+// spaced 256 words apart, so a wave keeps DEQ_WORDS coalesced code loads in flight.
+constexpr int DEQ_WORDS = DEQ_TILE / (256 * 8);
 
 __device__ __forceinline__ void dequant_item(const CodecDesc& d, int tile) {
     __shared__ float lv[16];
     if (threadIdx.x < 16) lv[threadIdx.x] = c_levels[threadIdx.x];
     __syncthreads();
-    const int64_t w = (int64_t)tile * 256 + threadIdx.x;
     const int64_t n = d.n;
     const int64_t nwords = ((n + 63) / 64) * 8;
-    if (w >= nwords) return;
-    const uint32_t cw = reinterpret_cast<const uint32_t*>(d.codes_in)[w];
-    const float s = d.scales_in[w >> 3];
-    float v[8];
+    const int64_t w0 = (int64_t)tile * (DEQ_TILE / 8) + threadIdx.x;
+    const uint32_t* __restrict__ cw_in = reinterpret_cast<const uint32_t*>(d.codes_in);
+    uint32_t cw[DEQ_WORDS];
+    float sc[DEQ_WORDS];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = lv[(cw >> (4 * e)) & 15u] * s;
-    const int64_t e0 = w * 8;
+    for (int k = 0; k < DEQ_WORDS; ++k) {
+        const int64_t w = w0 + k * 256;
+        const bool ok = w < nwords;
+        cw[k] = ok ? cw_in[w] : 0u;
+        sc[k] = ok ? d.scales_in[w >> 3] : 0.f;
+    }
     float* __restrict__ x = d.x_out;
-    if (e0 + 8 <= n && ((reinterpret_cast<uintptr_t>(x) & 15) == 0)) {
-        floatx4 a = {v[0], v[1], v[2], v[3]};
-        floatx4 b = {v[4], v[5], v[6], v[7]};
-        *reinterpret_cast<floatx4*>(x + e0) = a;
-        *reinterpret_cast<floatx4*>(x + e0 + 4) = b;
-    } else {
+    const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (e0 + e < n) x[e0 + e] = v[e];
+    for (int k = 0; k < DEQ_WORDS; ++k) {
+        const int64_t w = w0 + k * 256;
+        if (w >= nwords) break;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = lv[(cw[k] >> (4 * e)) & 15u] * sc[k];
+        const int64_t e0 = w * 8;
+        if (e0 + 8 <= n && aligned) {
+            floatx4 a = {v[0], v[1], v[2], v[3]};
+            floatx4 b = {v[4], v[5], v[6], v[7]};
+            *reinterpret_cast<floatx4*>(x + e0) = a;
+            *reinterpret_cast<floatx4*>(x + e0 + 4) = b;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e0 + e < n) x[e0 + e] = v[e];
+        }
     }
 }
 
@@ -87,46 +168,58 @@ __global__ __launch_bounds__(256) void dequant_single_kernel(CodecDesc d) {
     dequant_item(d, blockIdx.x);
 }
 
+// Quantization: a lane codes 4 consecutive elements (one 16-byte load), 16 lanes
+// cover a quantization block and reduce its absmax with xor shuffles; each lane
+// handles QUANT_QUADS such quads spaced 256 quads apart.
+constexpr int QUANT_QUADS = QUANT_TILE / (256 * 4);
+
 __device__ __forceinline__ void quant_item(const CodecDesc& d, int tile, uint32_t* __restrict__ flag) {
-    const int64_t qd = (int64_t)tile * 256 + threadIdx.x;
+    __shared__ uint2 tab[2 * QB_N];
+    if (threadIdx.x < 2 * QB_N) tab[threadIdx.x] = make_uint2(c_qtab.thr[threadIdx.x], c_qtab.code[threadIdx.x]);
     const int64_t n = d.n;
     const int64_t nquads = ((n + 63) / 64) * 16;
-    const bool active = qd < nquads;
+    const int64_t q0 = (int64_t)tile * (QUANT_TILE / 4) + threadIdx.x;
     const float* __restrict__ x = d.x_in;
-    const int64_t e0 = qd * 4;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (active) {
-        if (e0 + 4 <= n && ((reinterpret_cast<uintptr_t>(x) & 15) == 0)) {
+    const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    float v[QUANT_QUADS][4];
+#pragma unroll
+    for (int k = 0; k < QUANT_QUADS; ++k) {
+        const int64_t e0 = (q0 + k * 256) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[k][e] = 0.f;
+        if (e0 + 4 <= n && aligned) {
             const floatx4 q = *reinterpret_cast<const floatx4*>(x + e0);
-            v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+            v[k][0] = q[0]; v[k][1] = q[1]; v[k][2] = q[2]; v[k][3] = q[3];
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                if (e0 + e < n) v[e] = x[e0 + e];
+                if (e0 + e < n) v[k][e] = x[e0 + e];
         }
     }
+    __syncthreads();
     bool finite = true;
-    float amax = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        finite = finite && __builtin_isfinite(v[e]);
-        amax = fmaxf(amax, fabsf(v[e]));
+    for (int k = 0; k < QUANT_QUADS; ++k) {
+        const int64_t qd = q0 + k * 256;
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            finite = finite && __builtin_isfinite(v[k][e]);
+            amax = fmaxf(amax, fabsf(v[k][e]));
+        }
+        // absmax over the 16 lanes of this quantization block (lane groups are aligned)
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+        if (qd < nquads) {
+            uint32_t packed = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) packed |= code_of(__fdiv_rn(v[k][e], amax), tab) << (4 * e);
+            if (amax == 0.f) packed = 0x7777u;
+            reinterpret_cast<uint16_t*>(d.codes_out)[qd] = (uint16_t)packed;
+            if ((qd & 15) == 0) d.scales_out[qd >> 4] = amax;
+        }
     }
-    // absmax over the 16 lanes of this quantization block (lane groups are aligned)
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-    if (!active) return;
     if (!finite && flag) flag[0] = 1u;
-    uint32_t packed;
-    if (amax == 0.f) {
-        packed = 0x7777u;
-    } else {
-        packed = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) packed |= code_of(__fdiv_rn(v[e], amax)) << (4 * e);
-    }
-    reinterpret_cast<uint16_t*>(d.codes_out)[qd] = (uint16_t)packed;
-    if ((qd & 15) == 0) d.scales_out[qd >> 4] = amax;
 }
 
 __global__ __launch_bounds__(256) void quant_kernel(const CodecDesc* __restrict__ descs,
@@ -166,35 +259,35 @@ void host_codebook(float levels[16], float midpoints[15]) {
 hipError_t launch_dequant(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
                           hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(dequant_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    S4_LAUNCH(dequant_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
     return hipGetLastError();
 }
 
 hipError_t launch_quant(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
                         uint32_t* flag, hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc, flag);
+    S4_LAUNCH(quant_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc, flag);
     return hipGetLastError();
 }
 
 hipError_t launch_dequant_single(const CodecDesc& d, hipStream_t stream) {
-    const int64_t tiles = ((d.n + 63) / 64 * 8 + 255) / 256;
+    const int64_t tiles = dequant_tiles(d.n);
     if (tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(dequant_single_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, d);
+    S4_LAUNCH(dequant_single_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, d);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_single(const CodecDesc& d, hipStream_t stream) {
-    const int64_t tiles = ((d.n + 63) / 64 * 16 + 255) / 256;
+    const int64_t tiles = quant_tiles(d.n);
     if (tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_single_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, d);
+    S4_LAUNCH(quant_single_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, d);
     return hipGetLastError();
 }
 
 hipError_t launch_codec_copy(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
                              hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(codec_copy_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    S4_LAUNCH(codec_copy_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
     return hipGetLastError();
 }
 

@@ -1,10 +1,28 @@
 // Shared device-side types for the 4-bit Shampoo kernels (gfx950, wave64).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace s4 {
+
+// Optional start/stop events for the next kernel launch.  Launches go through
+// hipExtLaunchKernelGGL, which records the events in the dispatch itself, so a
+// timed launch measures the kernel alone (no separate event packets).
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+inline LaunchTiming& launch_timing() {
+    static thread_local LaunchTiming t;
+    return t;
+}
+#define S4_LAUNCH(kernel, grid, block, shmem, stream, ...)                                         \
+    do {                                                                                          \
+        ::s4::LaunchTiming& lt_ = ::s4::launch_timing();                                          \
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, lt_.start, lt_.stop, 0, __VA_ARGS__); \
+        lt_.start = lt_.stop = nullptr;                                                           \
+    } while (0)
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));

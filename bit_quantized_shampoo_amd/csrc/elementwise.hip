@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void identity_state_kernel(const InitDesc* __r
 hipError_t launch_root_scaling(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
                                float eps, uint32_t* flag, hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(root_scaling_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc,
+    S4_LAUNCH(root_scaling_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc,
                        eps, flag);
     return hipGetLastError();
 }
@@ -115,28 +115,28 @@ hipError_t launch_root_scaling(const VecDesc* descs, const int* prefix, int ndes
 hipError_t launch_rayleigh_reduce(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
                                   uint32_t* flag, hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(rayleigh_reduce_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc, flag);
+    S4_LAUNCH(rayleigh_reduce_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc, flag);
     return hipGetLastError();
 }
 
 hipError_t launch_identity_fill(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
                                 hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(identity_fill_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    S4_LAUNCH(identity_fill_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
     return hipGetLastError();
 }
 
 hipError_t launch_sign_flip(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
                             hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(sign_flip_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    S4_LAUNCH(sign_flip_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
     return hipGetLastError();
 }
 
 hipError_t launch_identity_state(const InitDesc* descs, const int* prefix, int ndesc, int ntiles,
                                  hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(identity_state_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    S4_LAUNCH(identity_state_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
     return hipGetLastError();
 }
 

@@ -363,23 +363,23 @@ hipError_t launch_cfg(int mode, const GemmDesc* descs, const int* prefix, int nd
     dim3 grid(ntiles), block(256);
     switch (mode) {
         case 0:
-            hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, false, false>), grid, block, 0, stream,
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, false>), grid, block, 0, stream,
                                descs, prefix, ndesc, io);
             break;
         case GEMM_F_TB:
-            hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, false, true>), grid, block, 0, stream,
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, true>), grid, block, 0, stream,
                                descs, prefix, ndesc, io);
             break;
         case GEMM_F_TA:
-            hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, true, false>), grid, block, 0, stream,
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, false>), grid, block, 0, stream,
                                descs, prefix, ndesc, io);
             break;
         case GEMM_F_TA | GEMM_F_TB:
-            hipLaunchKernelGGL((gemm_kernel<WM, WN, TM, TN, true, true>), grid, block, 0, stream,
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, true>), grid, block, 0, stream,
                                descs, prefix, ndesc, io);
             break;
         default:
-            hipLaunchKernelGGL((gemm_kernel_mixed<WM, WN, TM, TN>), grid, block, 0, stream, descs,
+            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN>), grid, block, 0, stream, descs,
                                prefix, ndesc, io);
             break;
     }

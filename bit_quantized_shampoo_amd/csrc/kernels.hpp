@@ -16,9 +16,12 @@ hipError_t launch_gemm(int cfg, int mode, const GemmDesc* descs, const int* pref
                        int ndesc, int ntiles, const IoEntry* io, hipStream_t stream);
 
 // Codec: elements per workgroup tile.
-constexpr int DEQ_TILE = 2048;     // 256 threads x 8 elements
-constexpr int QUANT_TILE = 1024;   // 256 threads x 4 elements
+constexpr int DEQ_TILE = 8192;     // 256 threads x 4 code words x 8 elements
+constexpr int QUANT_TILE = 2048;   // 256 threads x 2 quads x 4 elements
 constexpr int COPY_TILE = 8192;    // bytes of codes per workgroup
+// workgroups for n elements (quantization blocks of 64 padded)
+inline int64_t dequant_tiles(int64_t n) { return ((n + 63) / 64 * 64 + DEQ_TILE - 1) / DEQ_TILE; }
+inline int64_t quant_tiles(int64_t n) { return ((n + 63) / 64 * 64 + QUANT_TILE - 1) / QUANT_TILE; }
 hipError_t launch_dequant(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
                           hipStream_t stream);
 hipError_t launch_quant(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,

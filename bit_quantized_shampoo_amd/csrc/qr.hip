@@ -416,7 +416,7 @@ hipError_t launch_reg(const PanelDesc* descs, int ndesc, int max_h, hipStream_t 
         (int)panel_lds_bytes(true, NSLOT * NR < PANEL_LDS_MAX_ROWS ? NSLOT * NR : PANEL_LDS_MAX_ROWS));
     if (attr != hipSuccess) return attr;
     const size_t lds = panel_lds_bytes(true, max_h);
-    hipLaunchKernelGGL(panel_reg_kernel<NR>, dim3(ndesc), dim3(PANEL_THREADS), lds, stream, descs);
+    S4_LAUNCH(panel_reg_kernel<NR>, dim3(ndesc), dim3(PANEL_THREADS), lds, stream, descs);
     return hipGetLastError();
 }
 
@@ -448,7 +448,7 @@ hipError_t launch_panel(int rows_class, const PanelDesc* descs, int ndesc, int m
         default: break;
     }
     const size_t lds = panel_lds_bytes(false, max_h);
-    hipLaunchKernelGGL(panel_global_kernel, dim3(ndesc), dim3(PANEL_THREADS), lds, stream, descs);
+    S4_LAUNCH(panel_global_kernel, dim3(ndesc), dim3(PANEL_THREADS), lds, stream, descs);
     return hipGetLastError();
 }
 

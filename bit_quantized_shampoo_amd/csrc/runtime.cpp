@@ -280,7 +280,7 @@ struct shampoo4_ctx_s {
             c.x_out = wsf(start);
             c.n = (int64_t)S.p * S.p;
             cds.push_back(c);
-            tiles.push_back((int)((S.nqb * 8 + 255) / 256));
+            tiles.push_back((int)dequant_tiles(c.n));
         }
         Launch L = make_items(K_DEQUANT, cds, tiles);
         for (auto& S : sides) L.bytes += (double)S.p * S.p * (4.0 + 0.5 + 4.0 / 64);
@@ -458,7 +458,7 @@ struct shampoo4_ctx_s {
                 c.x_in = wsf(S.Qm); c.codes_out = stp<uint8_t>(S.codes); c.scales_out = stf(S.scales);
                 c.n = (int64_t)p * p;
                 qd.push_back(c);
-                tq.push_back((int)((S.nqb * 16 + 255) / 256));
+                tq.push_back((int)quant_tiles(c.n));
                 qbytes += (double)p * p * (4.0 + 0.5 + 4.0 / 64);
                 std::memset(&c, 0, sizeof(c));
                 c.codes_in = stp<uint8_t>(S.codes); c.scales_in = stf(S.scales);
@@ -530,7 +530,8 @@ struct shampoo4_ctx_s {
         if (timing) {
             rec.e0 = next_event();
             rec.e1 = next_event();
-            (void)hipEventRecord(rec.e0, s);
+            launch_timing().start = rec.e0;
+            launch_timing().stop = rec.e1;
         }
         hipError_t e = hipSuccess;
         const int fam = L.fam;
@@ -577,11 +578,15 @@ struct shampoo4_ctx_s {
                 break;
         }
         if (timing) {
-            (void)hipEventRecord(rec.e1, s);
-            rec.family = fam;
-            rec.flops = L.flops;
-            rec.bytes = L.bytes;
-            recs.push_back(rec);
+            // the launcher consumed the events only if it launched a kernel
+            const bool launched = launch_timing().start == nullptr;
+            launch_timing().start = launch_timing().stop = nullptr;
+            if (launched) {
+                rec.family = fam;
+                rec.flops = L.flops;
+                rec.bytes = L.bytes;
+                recs.push_back(rec);
+            }
         }
         return e;
     }

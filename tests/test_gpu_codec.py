@@ -32,6 +32,20 @@ def _cases():
     flat[: len(mids)] = mids
     blocks[:, 1:] = flat.reshape(blocks.shape[0], 63)
     cases["midpoints"] = blocks.ravel()
+    # every power-of-two quarter step from 2^-14 to 2 (the edges of the exponent /
+    # top-mantissa-bit buckets a fast code lookup may key on), their neighbours, both
+    # signs, in blocks of absmax 1
+    edges = np.array([2.0 ** e * (1 + k / 4) for e in range(-14, 1) for k in range(4)], np.float32)
+    edges = np.concatenate([edges, np.nextafter(edges, np.float32(0)), np.nextafter(edges, np.float32(4))])
+    edges = edges[np.abs(edges) <= 1]
+    edges = np.concatenate([edges, -edges]).astype(np.float32)
+    eb = np.zeros((len(edges) // 63 + 1, 64), np.float32)
+    eb[:, 0] = 1.0
+    ef = eb[:, 1:].reshape(-1)
+    ef[: len(edges)] = edges
+    eb[:, 1:] = ef.reshape(eb.shape[0], 63)
+    cases["bucket_edges"] = eb.ravel()
+    cases["dense_sweep"] = np.linspace(-1, 1, 1 << 20, dtype=np.float32)
     # codebook values times scales
     codes = rng.integers(0, 16, (200, 64))
     codes[:, 0] = 15
