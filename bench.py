@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-root-cache", action="store_true")
+    ap.add_argument("--qr", default="auto", choices=["auto", "blocked", "lookahead"],
+                    help="Householder QR schedule (default: chosen by the library from the batch size)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
@@ -148,7 +150,7 @@ def main():
         raise RuntimeError("bench.py needs a GPU")
     dev = torch.device("cuda:0")
     cfg = Shampoo4Config(beta=wl.beta, eps=wl.eps, qblock=wl.qblock, bjorck_iters=wl.bjorck_iters,
-                         power_iters=wl.power_iters, root_cache=not args.no_root_cache)
+                         power_iters=wl.power_iters, root_cache=not args.no_root_cache, qr_schedule=args.qr)
     log(f"[bench] workload {wl.name}: {len(wl.blocks)} blocks, steps {steps}, warmup {warmup}")
     grads, distinct, gen = make_gradients(wl, steps + warmup, dev)
     blocks = Shampoo4Blocks(wl.shapes, cfg, device=dev)
@@ -234,7 +236,7 @@ def main():
             "blocks": len(wl.blocks),
             "beta": wl.beta, "eps": wl.eps, "qblock": wl.qblock,
             "bjorck_iters": wl.bjorck_iters, "power_iters": wl.power_iters,
-            "root_interval": wl.root_interval, "root_cache": cfg.root_cache,
+            "root_interval": wl.root_interval, "root_cache": cfg.root_cache, "qr_schedule": args.qr,
         },
         "gemm_tflops": round(gemm_tflops, 3),
         "gemm_frac_mfma_peak": round(gemm_tflops / PEAK_FP32_MFMA_TFLOPS, 4),

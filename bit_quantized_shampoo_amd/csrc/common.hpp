@@ -84,13 +84,16 @@ static_assert(sizeof(CodecDesc) == 64, "CodecDesc layout");
 // One Householder panel of one matrix: rows c0.., columns c0..c0+nb-1 of A.
 struct PanelDesc {
     float* A;                 // matrix base (p x p)
-    float* V;                 // out: [h, 32] explicit unit-lower reflector vectors
-    float* Y;                 // out: [h, 32] V T (compact WY)
+    float* V;                 // out: explicit unit-lower reflector vectors, 32 columns
+    float* Y;                 // out: V T (compact WY), same shape and pitch as V
     float* rdiag;             // out: R diagonal, entries c0..c0+nb-1
-    int64_t ld;
-    int32_t c0, h, nb, pad;
+    int64_t ld;               // of A
+    int64_t vld;              // row pitch of V and Y
+    int32_t c0, h, nb;
+    int32_t zrows;            // V and Y start zrows rows above the panel's top row; those
+                              // rows are written as zeros
 };
-static_assert(sizeof(PanelDesc) == 56, "PanelDesc layout");
+static_assert(sizeof(PanelDesc) == 64, "PanelDesc layout");
 
 // Column / vector work item for the small elementwise kernels.
 struct VecDesc {

@@ -40,29 +40,36 @@ __global__ __launch_bounds__(256) void rayleigh_reduce_kernel(const VecDesc* __r
     d.out[j] = t > 0.f ? t : 0.f;
 }
 
-// out = I (p x p, leading dimension ld)
+// out = I (p x p, leading dimension ld); a workgroup covers fill_rows(p) whole rows
 __global__ __launch_bounds__(256) void identity_fill_kernel(const VecDesc* __restrict__ descs,
                                                             const int* __restrict__ prefix, int ndesc) {
     const int item = find_item(prefix, ndesc, blockIdx.x);
     const VecDesc& d = descs[item];
-    const int64_t p = d.p;
-    const int64_t base = (int64_t)(blockIdx.x - prefix[item]) * FILL_TILE;
-    for (int64_t e = base + threadIdx.x; e < base + FILL_TILE && e < p * p; e += 256) {
-        const int64_t i = e / p, j = e - i * p;
-        d.out[i * d.ld + j] = (i == j) ? 1.f : 0.f;
+    const int p = d.p;
+    const int rows = fill_rows(p);
+    const int r0 = (blockIdx.x - prefix[item]) * rows;
+    const int r1 = min(r0 + rows, p);
+    for (int i = r0; i < r1; ++i) {
+        float* __restrict__ row = d.out + (int64_t)i * d.ld;
+        for (int j = threadIdx.x; j < p; j += 256) row[j] = (i == j) ? 1.f : 0.f;
     }
 }
 
-// column j of out times sign(aux[j]) (0 counts as +)
+// column j of out times sign(aux[j]) (0 counts as +), same row tiling
 __global__ __launch_bounds__(256) void sign_flip_kernel(const VecDesc* __restrict__ descs,
                                                         const int* __restrict__ prefix, int ndesc) {
     const int item = find_item(prefix, ndesc, blockIdx.x);
     const VecDesc& d = descs[item];
-    const int64_t p = d.p;
-    const int64_t base = (int64_t)(blockIdx.x - prefix[item]) * FILL_TILE;
-    for (int64_t e = base + threadIdx.x; e < base + FILL_TILE && e < p * p; e += 256) {
-        const int64_t i = e / p, j = e - i * p;
-        if (d.aux[j] < 0.f) d.out[i * d.ld + j] = -d.out[i * d.ld + j];
+    const int p = d.p;
+    const int rows = fill_rows(p);
+    const int r0 = (blockIdx.x - prefix[item]) * rows;
+    const int r1 = min(r0 + rows, p);
+    for (int j = threadIdx.x; j < p; j += 256) {
+        if (!(d.aux[j] < 0.f)) continue;
+        for (int i = r0; i < r1; ++i) {
+            float* __restrict__ e = d.out + (int64_t)i * d.ld + j;
+            *e = -*e;
+        }
     }
 }
 

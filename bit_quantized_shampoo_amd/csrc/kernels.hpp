@@ -43,7 +43,9 @@ hipError_t launch_panel(int rows_class, const PanelDesc* descs, int ndesc, int m
                         hipStream_t stream);
 
 // Small per-column / per-element kernels.
-constexpr int FILL_TILE = 4096;              // elements per workgroup
+constexpr int FILL_TILE = 4096;              // elements per workgroup (at least one row)
+constexpr int fill_rows(int p) { return p >= FILL_TILE ? 1 : FILL_TILE / p; }
+constexpr int fill_tiles(int p) { return (p + fill_rows(p) - 1) / fill_rows(p); }
 // lam_j = max(sum_t partial[t][j], 0) over the per-tile partial rows of the fused
 // column-dot GEMM epilogue
 hipError_t launch_rayleigh_reduce(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,

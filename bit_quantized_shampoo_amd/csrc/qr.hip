@@ -55,7 +55,8 @@ constexpr int OFF_SALL = OFF_ROWJ + 64;          // [32][32] s vector of step j
 constexpr int OFF_TAU = OFF_SALL + PW * PW;      // [32]
 constexpr int OFF_T = OFF_TAU + PW;              // [32][33]
 constexpr int OFF_RED = OFF_T + PW * 33;         // [NWAVE]
-constexpr int OFF_COL = ((OFF_RED + NWAVE + 3) / 4) * 4;  // [NSLOT][64] column j+1 of each half-wave's rows
+constexpr int OFF_RD = OFF_RED + NWAVE;          // [32] R diagonal (written out after the loop)
+constexpr int OFF_COL = ((OFF_RD + PW + 3) / 4) * 4;  // [NSLOT][64] column j+1 of each half-wave's rows
 constexpr int OFF_VS = OFF_COL + NSLOT * 64;     // [hpad][33] V staging (register variant)
 static_assert(NWAVE == 8, "partials are read as two 16-byte vectors");
 
@@ -139,9 +140,10 @@ __device__ __forceinline__ void build_T(float* smem, int nb, int tid) {
     }
 }
 
-// Y = V T for rows [0, h): V rows come from `vsrc` (pitch vpitch floats), T from LDS.
+// Y = V T for rows [0, h): V rows come from `vsrc` (pitch vpitch floats), T from LDS,
+// Y rows have pitch ypitch.
 __device__ __forceinline__ void form_Y(const float* vsrc, int64_t vpitch, const float* smem, float* Y,
-                                       int h, int tid) {
+                                       int64_t ypitch, int h, int tid) {
     const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, hh = lane >> 5;
     const int nchunk = (h + 31) / 32;
     for (int q = wv; q < nchunk; q += PANEL_THREADS / 64) {
@@ -159,8 +161,18 @@ __device__ __forceinline__ void form_Y(const float* vsrc, int64_t vpitch, const 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int orow = q * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-            if (orow < h) Y[(int64_t)orow * PW + l32] = acc[r];
+            if (orow < h) Y[(int64_t)orow * ypitch + l32] = acc[r];
         }
+    }
+}
+
+// The zrows rows of V and Y above the panel (inside a wider block of reflectors whose
+// earlier panels start higher) are zero.
+__device__ __forceinline__ void zero_above(const PanelDesc& d, int tid) {
+    for (int e = tid; e < d.zrows * PW; e += PANEL_THREADS) {
+        const int64_t off = (int64_t)(e / PW) * d.vld + (e % PW);
+        d.V[off] = 0.f;
+        d.Y[off] = 0.f;
     }
 }
 
@@ -233,7 +245,7 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_reg_kernel(const PanelDes
             smem[OFF_SALL + j * PW + c] = sv;
             if (c == 0) {
                 smem[OFF_TAU + j] = R.tau;
-                d.rdiag[d.c0 + j] = R.beta;
+                smem[OFF_RD + j] = R.beta;   // no global store inside the loop
             }
         }
         const float f = R.tau * sv;                      // 0 for columns c < j
@@ -303,8 +315,11 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_reg_kernel(const PanelDes
         __syncthreads();
     }
 
+    if (tid < nb) d.rdiag[d.c0 + tid] = smem[OFF_RD + tid];
     // explicit V to global and to LDS (rows padded to 32 with zeros)
     float* Vs = smem + OFF_VS;
+    float* Vt = d.V + (int64_t)d.zrows * d.vld;
+    float* Yt = d.Y + (int64_t)d.zrows * d.vld;
     const int hpad = (h + 31) & ~31;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -313,12 +328,13 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_reg_kernel(const PanelDes
             float v = 0.f;
             if (r < h && c < nb) v = (r > c) ? x[i] : (r == c ? 1.f : 0.f);
             Vs[r * 33 + c] = v;
-            if (r < h) d.V[(int64_t)r * PW + c] = v;
+            if (r < h) Vt[(int64_t)r * d.vld + c] = v;
         }
     }
     build_T(smem, nb, tid);
+    zero_above(d, tid);
     __syncthreads();
-    form_Y(Vs, 33, smem, d.Y, h, tid);
+    form_Y(Vs, 33, smem, Yt, d.vld, h, tid);
 }
 
 __global__ __launch_bounds__(PANEL_THREADS) void panel_global_kernel(const PanelDesc* __restrict__ descs) {
@@ -371,7 +387,7 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_global_kernel(const Panel
             smem[OFF_SALL + j * PW + c] = sv;
             if (c == 0) {
                 smem[OFF_TAU + j] = R.tau;
-                d.rdiag[d.c0 + j] = R.beta;
+                smem[OFF_RD + j] = R.beta;   // no global store inside the loop
             }
         }
         const float f = R.tau * sv;
@@ -398,14 +414,18 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_global_kernel(const Panel
         __syncthreads();
     }
 
+    if (tid < nb) d.rdiag[d.c0 + tid] = smem[OFF_RD + tid];
+    float* Vt = d.V + (int64_t)d.zrows * d.vld;
+    float* Yt = d.Y + (int64_t)d.zrows * d.vld;
     for (int r = slot; r < h; r += NSLOT) {
         float v = 0.f;
         if (c < nb) v = (r > c) ? Ap[r * ld + c] : (r == c ? 1.f : 0.f);
-        d.V[(int64_t)r * PW + c] = v;
+        Vt[(int64_t)r * d.vld + c] = v;
     }
     build_T(smem, nb, tid);
+    zero_above(d, tid);
     __syncthreads();
-    form_Y(d.V, PW, smem, d.Y, h, tid);
+    form_Y(Vt, d.vld, smem, Yt, d.vld, h, tid);
 }
 
 template <int NR>

@@ -25,6 +25,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kRing = 8;            // pinned io staging slots
 constexpr int kPanel = 32;          // Householder panel width
+constexpr int kOuter = 128;         // columns whose reflectors update the trailing matrix together
 constexpr int kMaxSplit = 8;        // split-K chunks of the skinny QR products
 constexpr int kMaxDim = 8192;
 
@@ -39,7 +40,8 @@ const char* kFamilyNames[FAM_N] = {"gemm_bjorck", "gemm_stats", "gemm_power", "g
                                    "gemm_precond", "dequant", "quant", "qr_panel", "rayleigh",
                                    "elementwise"};
 
-enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT };
+enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT,
+            K_RECORD, K_WAIT };
 
 struct Launch {
     Kind kind = K_GEMM;
@@ -48,6 +50,8 @@ struct Launch {
     int fam = FAM_ELEMENTWISE;
     size_t desc_off = 0, prefix_off = 0;   // offsets inside the descriptor region
     int ndesc = 0, ntiles = 0, max_h = 0;
+    int strm = 0;        // 0: the caller's stream, 1: the context's second stream
+    int ev = -1;         // K_RECORD / K_WAIT: index of the context's synchronization event
     double flops = 0, bytes = 0;
 };
 using Seq = std::vector<Launch>;
@@ -58,8 +62,9 @@ struct Side {
     // state offsets
     size_t codes = 0, scales = 0, lam = 0, rcodes = 0, rscales = 0, d = 0;
     // workspace offsets
-    size_t Vs = 0, Vr = 0, Tmp = 0, Wg = 0, Lt = 0, Pm = 0, Qm = 0, Vb = 0, Yb = 0, Z = 0, W = 0, rdiag = 0;
-    std::vector<size_t> panel_rows;   // row offset of panel s inside Vb / Yb
+    size_t Vs = 0, Vr = 0, Tmp = 0, Wg = 0, Lt = 0, Pm = 0, Qm = 0, Vb = 0, Yb = 0, Z = 0, W = 0, Mb = 0,
+           Z2 = 0, rdiag = 0;
+    std::vector<size_t> outer_rows;   // row offset of outer block o inside Vb / Yb (pitch = outer width)
 };
 
 struct TimingRec {
@@ -87,7 +92,13 @@ struct shampoo4_ctx_s {
     Seq deq_stats, deq_root, init_seq;
     std::vector<Seq> bj_stats, bj_root;
     Seq stats_x[2], stats_g, power_first[2], power_next;
-    std::vector<Seq> panel, trail, upd;
+    std::vector<Seq> qr_steps;            // per panel index: panel, block and trailing products
+    Seq qr_join;                          // second stream's work joined back (look-ahead plans)
+    int outer = kOuter;                   // columns whose reflectors update the trailing matrix together
+    bool lookahead = false;               // small batches: trailing and Q updates on a second stream
+    int n_sync = 0;                       // synchronization events the plan uses
+    hipStream_t aux = nullptr;
+    std::vector<hipEvent_t> sync_ev;
     Seq qinit, sign, ray_gemm, rayleigh, quant, root_d, root_copy;
     Seq pre[4];
 
@@ -110,6 +121,9 @@ struct shampoo4_ctx_s {
         for (auto& e : ring_ev)
             if (e) (void)hipEventDestroy(e);
         for (auto& e : ev_pool) (void)hipEventDestroy(e);
+        for (auto& e : sync_ev)
+            if (e) (void)hipEventDestroy(e);
+        if (aux) (void)hipStreamDestroy(aux);
         if (pinned) (void)hipHostFree(pinned);
     }
 
@@ -202,6 +216,16 @@ struct shampoo4_ctx_s {
 
     // ---- plan ---------------------------------------------------------------------
     void layout() {
+        // Large batches are throughput-bound: reflectors go to the trailing matrix 128
+        // columns at a time.  Small ones are bound by the chain of panels and by launch
+        // latency: panel-wide updates on the caller's stream (or, on request, with the
+        // trailing and Q updates overlapped on a second stream).
+        double work = 0;
+        for (auto& sh : shapes) work += (double)sh.m * sh.m * sh.m + (double)sh.n * sh.n * sh.n;
+        lookahead = (cfg.flags & SHAMPOO4_FLAG_QR_LOOKAHEAD) != 0;
+        const bool blocked = (cfg.flags & SHAMPOO4_FLAG_QR_BLOCKED) ||
+                             (!lookahead && work >= 16.0 * 1073741824.0);
+        outer = blocked ? kOuter : kPanel;
         sides.assign(2 * nb, Side{});
         size_t so = 0, wo = 0;
         auto st_take = [&](size_t b) { size_t o = so; so += align_up(b ? b : 1); return o; };
@@ -231,16 +255,18 @@ struct shampoo4_ctx_s {
                 S.Lt = ws_take(mat);
                 S.Pm = ws_take(mat);
                 S.Qm = ws_take(mat);
-                S.panel_rows.clear();
+                S.outer_rows.clear();
                 size_t rows = 0;
-                for (int c0 = 0; c0 < p; c0 += kPanel) {
-                    S.panel_rows.push_back(rows);
+                for (int c0 = 0; c0 < p; c0 += outer) {
+                    S.outer_rows.push_back(rows);
                     rows += p - c0;
                 }
-                S.Vb = ws_take(rows * kPanel * 4);
-                S.Yb = ws_take(rows * kPanel * 4);
-                S.Z = ws_take((size_t)kMaxSplit * kPanel * p * 4);   // split-K slabs of Y^T A
-                S.W = ws_take((size_t)kMaxSplit * kPanel * p * 4);   // split-K slabs of Q Y
+                S.Vb = ws_take(rows * outer * 4);
+                S.Yb = ws_take(rows * outer * 4);
+                S.Z = ws_take((size_t)kMaxSplit * outer * p * 4);        // split-K slabs of Y^T A
+                S.W = ws_take((size_t)kMaxSplit * outer * p * 4);        // split-K slabs of Q Y
+                S.Mb = ws_take((size_t)kMaxSplit * outer * kPanel * 4);  // split-K slabs of V^T Y
+                S.Z2 = ws_take((size_t)kMaxSplit * kPanel * kPanel * 4); // look-ahead Y^T A
                 S.rdiag = ws_take(p * 4);
             }
             X1[b] = ws_take((size_t)shapes[b].m * shapes[b].n * 4);
@@ -249,7 +275,7 @@ struct shampoo4_ctx_s {
         st_bytes = so;
         desc_base = wo;
         max_panels = 0;
-        for (auto& S : sides) max_panels = std::max(max_panels, (int)S.panel_rows.size());
+        for (auto& S : sides) max_panels = std::max(max_panels, (S.p + kPanel - 1) / kPanel);
     }
 
     GemmDesc gd(const float* A, int64_t lda, const float* B, int64_t ldb, float* D, int64_t ldd,
@@ -306,6 +332,274 @@ struct shampoo4_ctx_s {
         }
     }
 
+    // ---- Householder QR ---------------------------------------------------------
+    static long tiles64(long M, long N) { return ((M + 63) / 64) * ((N + 63) / 64); }
+    // split-K factor for a launch whose products have `tiles` 64 x 64 output tiles and
+    // depth at least min_k: a batch too small to fill the GPU still spreads its long-K
+    // (K = panel height) products
+    static int split_for(long tiles, int min_k) {
+        if (tiles <= 0 || tiles >= 512) return 1;
+        const int ks = (int)std::min<long>(kMaxSplit, (512 + tiles - 1) / tiles);
+        return std::max(1, std::min(ks, min_k / 64));
+    }
+    static int set_split(GemmDesc& d, int ks) {
+        const int kchunk = ((d.K + ks - 1) / ks + 15) / 16 * 16;
+        d.kchunk = kchunk;
+        d.ksplit = (d.K + kchunk - 1) / kchunk;
+        return d.ksplit;
+    }
+    // panels bucketed by register class (0 = in place in global memory)
+    void add_panel(std::vector<std::vector<PanelDesc>>& byc, std::vector<int>& maxh, const PanelDesc& pd) const {
+        int cls = panel_rows_class(pd.h);
+        if (cls > 0 && panel_lds_bytes(true, pd.h) > lds_limit) cls = 0;
+        int bucket = 0;
+        while (cls > 0 && (2 << bucket) < cls) ++bucket;
+        bucket = cls > 0 ? bucket + 1 : 0;
+        byc[bucket].push_back(pd);
+        maxh[bucket] = std::max(maxh[bucket], pd.h);
+    }
+    void panel_launches(Seq& st, std::vector<std::vector<PanelDesc>>& byc, const std::vector<int>& maxh) {
+        for (int b = 0; b < 8; ++b) {
+            if (byc[b].empty()) continue;
+            std::vector<int> ones(byc[b].size(), 1);
+            Launch L = make_items(K_PANEL, byc[b], ones);
+            L.mode = b == 0 ? 0 : (1 << b);
+            L.max_h = maxh[b];
+            L.ntiles = (int)byc[b].size();
+            st.push_back(L);
+        }
+    }
+    static Launch sync_op(Kind k, int strm, int ev) {
+        Launch L;
+        L.kind = k;
+        L.strm = strm;
+        L.ev = ev;
+        return L;
+    }
+    static void on_stream(Seq& seq, int strm) {
+        for (auto& L : seq) L.strm = strm;
+    }
+
+    void build_qr_blocked() {
+        // Householder QR of P, blocked twice (or once, when the outer width is 32).
+        // Panels of 32 columns are factored one workgroup each; the panel's reflectors
+        // are applied at once (compact WY) only to the rest of its outer block, and each panel's Y = V T is folded into
+        // the outer block's Y (Y_b <- Y_b - Y_a (V_a^T Y_b), which is V T of the product
+        // of all the block's reflectors).  After an outer block's last panel its
+        // reflectors update the trailing columns (A <- A - V (Y^T A)) and the forward
+        // accumulation of Q (Q <- Q - (Q Y) V^T) as products of depth `outer`.  The columns
+        // of Q are flipped to diag(R) >= 0 at the end.
+        qr_steps.assign(max_panels, Seq{});
+        qr_join.clear();
+        for (int sidx = 0; sidx < max_panels; ++sidx) {
+            // panels bucketed by register class (0 = in place in global memory)
+            std::vector<std::vector<PanelDesc>> byc(8);
+            std::vector<int> maxh(8, 0);
+            std::vector<GemmItem> in1, in2, out1, out2;
+            // split-K factors: chosen per launch so that a batch too small to fill the
+            // GPU still spreads its long-K (K = panel height) products
+            long tin = 0, tout = 0;
+            int kin = 1 << 30, kout = 1 << 30;
+            for (auto& S : sides) {
+                const int p = S.p, c0 = sidx * kPanel;
+                if (c0 >= p) continue;
+                const int C0 = c0 / outer * outer, wb = std::min(outer, p - C0);
+                const int nbw = std::min(kPanel, p - c0), i = (c0 - C0) / kPanel;
+                const int ninner = C0 + wb - c0 - nbw;
+                tin += tiles64(nbw, ninner) + tiles64((long)i * kPanel, nbw);
+                kin = std::min(kin, p - c0);
+                if (ninner == 0) {
+                    tout += tiles64(wb, p - C0 - wb) + tiles64(p, wb);
+                    kout = std::min(kout, p - C0);
+                }
+            }
+            const int ks_in = split_for(tin, kin), ks_out = split_for(tout, kout);
+            for (auto& S : sides) {
+                const int p = S.p;
+                const int c0 = sidx * kPanel;
+                if (c0 >= p) continue;
+                const int C0 = c0 / outer * outer;
+                const int wb = std::min(outer, p - C0);
+                const int ho = p - C0;                       // rows of the outer block
+                const int nbw = std::min(kPanel, p - c0);
+                const int h = p - c0;
+                const int i = (c0 - C0) / kPanel;            // panel index inside the block
+                const int ninner = C0 + wb - c0 - nbw;       // block columns right of the panel
+                const int ntr = p - C0 - wb;                 // columns right of the block
+                float* Vo = wsf(S.Vb) + S.outer_rows[C0 / outer] * outer;
+                float* Yo = wsf(S.Yb) + S.outer_rows[C0 / outer] * outer;
+                float* Pm = wsf(S.Pm);
+                float* Z = wsf(S.Z);
+                float* Wb = wsf(S.W);
+                float* Mb = wsf(S.Mb);
+                const int64_t zslab = (int64_t)outer * p, wslab = (int64_t)p * outer,
+                              mslab = (int64_t)outer * kPanel;
+                PanelDesc pd;
+                std::memset(&pd, 0, sizeof(pd));
+                pd.A = Pm;
+                pd.V = Vo + i * kPanel;
+                pd.Y = Yo + i * kPanel;
+                pd.rdiag = wsf(S.rdiag);
+                pd.ld = p;
+                pd.vld = outer;
+                pd.c0 = c0;
+                pd.h = h;
+                pd.nb = nbw;
+                pd.zrows = c0 - C0;
+                add_panel(byc, maxh, pd);
+                float* Vp = Vo + (int64_t)(c0 - C0) * outer + i * kPanel;   // panel's V, top row c0
+                float* Yp = Yo + (int64_t)(c0 - C0) * outer + i * kPanel;
+                if (ninner > 0) {   // the panel's reflectors on the rest of its outer block
+                    float* Ab = Pm + (int64_t)c0 * p + c0 + nbw;
+                    GemmDesc z = gd(Yp, outer, Ab, p, Z, p, nbw, ninner, h);
+                    const int ns = set_split(z, ks_in);
+                    z.dslab = zslab;
+                    in1.push_back({z, true, false});
+                    GemmDesc u = gd(Vp, outer, Z, p, Ab, p, h, ninner, nbw, -1.f, 1.f, Ab, p);
+                    u.bnslab = ns; u.bslab = zslab;
+                    in2.push_back({u, false, false});
+                }
+                if (i > 0) {        // fold this panel's Y into the block's
+                    GemmDesc m = gd(Vo + (int64_t)(c0 - C0) * outer, outer, Yp, outer, Mb, kPanel,
+                                    i * kPanel, nbw, h);
+                    const int ns = set_split(m, ks_in);
+                    m.dslab = mslab;
+                    in1.push_back({m, true, false});
+                    GemmDesc y = gd(Yo, outer, Mb, kPanel, Yo + i * kPanel, outer, ho, nbw, i * kPanel,
+                                    -1.f, 1.f, Yo + i * kPanel, outer);
+                    y.bnslab = ns; y.bslab = mslab;
+                    in2.push_back({y, false, false});
+                }
+                if (ninner == 0) {  // last panel of the block: trailing columns and Q
+                    if (ntr > 0) {
+                        float* At = Pm + (int64_t)C0 * p + C0 + wb;
+                        GemmDesc z = gd(Yo, outer, At, p, Z, p, wb, ntr, ho);
+                        const int ns = set_split(z, ks_out);
+                        z.dslab = zslab;
+                        out1.push_back({z, true, false});
+                        GemmDesc u = gd(Vo, outer, Z, p, At, p, ho, ntr, wb, -1.f, 1.f, At, p);
+                        u.bnslab = ns; u.bslab = zslab;
+                        out2.push_back({u, false, false});
+                    }
+                    float* Qs = wsf(S.Qm) + C0;                  // Q[:, C0:]
+                    GemmDesc w = gd(Qs, p, Yo, outer, Wb, outer, p, wb, ho);
+                    const int ns = set_split(w, ks_out);
+                    w.dslab = wslab;
+                    out1.push_back({w, false, false});
+                    GemmDesc q = gd(Wb, outer, Vo, outer, Qs, p, p, ho, wb, -1.f, 1.f, Qs, p);
+                    q.anslab = ns; q.aslab = wslab;
+                    out2.push_back({q, false, true});
+                }
+            }
+            Seq& st = qr_steps[sidx];
+            panel_launches(st, byc, maxh);
+            for (auto* items : {&in1, &in2, &out1, &out2}) {
+                Seq g = make_gemm(*items, FAM_GEMM_QR);
+                st.insert(st.end(), g.begin(), g.end());
+            }
+        }
+    }
+
+    // Panel-wide reflector blocks with look-ahead.  The caller's stream runs the chain
+    // of panels: panel k, then H_k applied to panel k+1's columns only.  The second
+    // stream applies H_k to the columns beyond and accumulates Q; panel k+1's own
+    // look-ahead update waits for that trailing update of k.  Event k of each kind is
+    // recorded once per pass, before any wait on it is enqueued.
+    void build_qr_lookahead() {
+        qr_steps.assign(max_panels, Seq{});
+        qr_join.clear();
+        const int evA = 0, evR = max_panels, evEnd = 2 * max_panels;
+        n_sync = 2 * max_panels + 1;
+        for (int sidx = 0; sidx < max_panels; ++sidx) {
+            std::vector<std::vector<PanelDesc>> byc(8);
+            std::vector<int> maxh(8, 0);
+            std::vector<GemmItem> la1, la2, r1, r2, q1, q2;
+            long tla = 0, trest = 0;
+            int kmin = 1 << 30;
+            for (auto& S : sides) {
+                const int p = S.p, c0 = sidx * kPanel;
+                if (c0 >= p) continue;
+                const int nbw = std::min(kPanel, p - c0);
+                const int nxt = std::min(kPanel, p - c0 - nbw);
+                tla += tiles64(nbw, nxt);
+                trest += tiles64(nbw, p - c0 - nbw - nxt) + tiles64(p, nbw);
+                kmin = std::min(kmin, p - c0);
+            }
+            const int ks_la = split_for(tla, kmin), ks_rest = split_for(trest, kmin);
+            for (auto& S : sides) {
+                const int p = S.p;
+                const int c0 = sidx * kPanel;
+                if (c0 >= p) continue;
+                const int nbw = std::min(kPanel, p - c0);
+                const int h = p - c0;
+                const int nxt = std::min(kPanel, p - c0 - nbw);     // look-ahead columns
+                const int nrest = p - c0 - nbw - nxt;
+                float* Vp = wsf(S.Vb) + S.outer_rows[sidx] * kPanel;
+                float* Yp = wsf(S.Yb) + S.outer_rows[sidx] * kPanel;
+                float* Pm = wsf(S.Pm);
+                PanelDesc pd;
+                std::memset(&pd, 0, sizeof(pd));
+                pd.A = Pm; pd.V = Vp; pd.Y = Yp; pd.rdiag = wsf(S.rdiag);
+                pd.ld = p; pd.vld = kPanel;
+                pd.c0 = c0; pd.h = h; pd.nb = nbw; pd.zrows = 0;
+                add_panel(byc, maxh, pd);
+                if (nxt > 0) {
+                    float* An = Pm + (int64_t)c0 * p + c0 + nbw;
+                    float* Z2 = wsf(S.Z2);
+                    GemmDesc z = gd(Yp, kPanel, An, p, Z2, kPanel, nbw, nxt, h);
+                    const int ns = set_split(z, ks_la);
+                    z.dslab = (int64_t)kPanel * kPanel;
+                    la1.push_back({z, true, false});
+                    GemmDesc u = gd(Vp, kPanel, Z2, kPanel, An, p, h, nxt, nbw, -1.f, 1.f, An, p);
+                    u.bnslab = ns; u.bslab = (int64_t)kPanel * kPanel;
+                    la2.push_back({u, false, false});
+                }
+                if (nrest > 0) {
+                    float* At = Pm + (int64_t)c0 * p + c0 + nbw + nxt;
+                    float* Z = wsf(S.Z);
+                    GemmDesc z = gd(Yp, kPanel, At, p, Z, p, nbw, nrest, h);
+                    const int ns = set_split(z, ks_rest);
+                    z.dslab = (int64_t)kPanel * p;
+                    r1.push_back({z, true, false});
+                    GemmDesc u = gd(Vp, kPanel, Z, p, At, p, h, nrest, nbw, -1.f, 1.f, At, p);
+                    u.bnslab = ns; u.bslab = (int64_t)kPanel * p;
+                    r2.push_back({u, false, false});
+                }
+                float* Qs = wsf(S.Qm) + c0;
+                float* Wb = wsf(S.W);
+                GemmDesc w = gd(Qs, p, Yp, kPanel, Wb, kPanel, p, nbw, h);
+                const int ns = set_split(w, ks_rest);
+                w.dslab = (int64_t)p * kPanel;
+                q1.push_back({w, false, false});
+                GemmDesc q = gd(Wb, kPanel, Vp, kPanel, Qs, p, p, h, nbw, -1.f, 1.f, Qs, p);
+                q.anslab = ns; q.aslab = (int64_t)p * kPanel;
+                q2.push_back({q, false, true});
+            }
+            Seq& st = qr_steps[sidx];
+            panel_launches(st, byc, maxh);
+            if (sidx > 0) st.push_back(sync_op(K_WAIT, 0, evR + sidx - 1));
+            for (auto* items : {&la1, &la2}) {
+                Seq g = make_gemm(*items, FAM_GEMM_QR);
+                st.insert(st.end(), g.begin(), g.end());
+            }
+            st.push_back(sync_op(K_RECORD, 0, evA + sidx));
+            st.push_back(sync_op(K_WAIT, 1, evA + sidx));
+            for (auto* items : {&r1, &r2}) {
+                Seq g = make_gemm(*items, FAM_GEMM_QR);
+                on_stream(g, 1);
+                st.insert(st.end(), g.begin(), g.end());
+            }
+            st.push_back(sync_op(K_RECORD, 1, evR + sidx));
+            for (auto* items : {&q1, &q2}) {
+                Seq g = make_gemm(*items, FAM_GEMM_QR);
+                on_stream(g, 1);
+                st.insert(st.end(), g.begin(), g.end());
+            }
+        }
+        qr_join.push_back(sync_op(K_RECORD, 1, evEnd));
+        qr_join.push_back(sync_op(K_WAIT, 0, evEnd));
+    }
+
     void build() {
         blob.clear();
         const float beta = cfg.beta;
@@ -343,92 +637,7 @@ struct shampoo4_ctx_s {
             power_next = make_gemm(pn, FAM_GEMM_POWER);
         }
 
-        // Householder QR of P, panel by panel.  Q is accumulated forward
-        // (Q <- Q H_k = Q - (Q Y) V^T) in the same launches as the trailing update
-        // (A <- H_k^T A = A - V (Y^T A)); the columns are flipped to diag(R) >= 0 at the end.
-        panel.assign(max_panels, Seq{});
-        trail.assign(max_panels, Seq{});
-        upd.assign(max_panels, Seq{});
-        for (int sidx = 0; sidx < max_panels; ++sidx) {
-            // panels bucketed by register class (0 = in place in global memory)
-            std::vector<std::vector<PanelDesc>> byc(8);
-            std::vector<int> maxh(8, 0);
-            std::vector<GemmItem> t1, t2;
-            // Split the long-K (K = h) products when the batch alone cannot fill the GPU.
-            long base_tiles = 0;
-            int min_h = 1 << 30;
-            for (auto& S : sides) {
-                const int c0 = sidx * kPanel;
-                if (c0 >= S.p) continue;
-                const int ntr = S.p - c0 - std::min(kPanel, S.p - c0);
-                base_tiles += (ntr + 63) / 64 + (S.p + 63) / 64;
-                min_h = std::min(min_h, S.p - c0);
-            }
-            int ksplit = 1;
-            if (base_tiles > 0 && base_tiles < 512) {
-                ksplit = (int)std::min<long>(kMaxSplit, (512 + base_tiles - 1) / base_tiles);
-                ksplit = std::max(1, std::min(ksplit, min_h / 64));
-            }
-            for (auto& S : sides) {
-                const int p = S.p;
-                const int c0 = sidx * kPanel;
-                if (c0 >= p) continue;
-                const int nbw = std::min(kPanel, p - c0);
-                const int h = p - c0;
-                PanelDesc pd;
-                std::memset(&pd, 0, sizeof(pd));
-                pd.A = wsf(S.Pm);
-                pd.V = wsf(S.Vb) + S.panel_rows[sidx] * kPanel;
-                pd.Y = wsf(S.Yb) + S.panel_rows[sidx] * kPanel;
-                pd.rdiag = wsf(S.rdiag);
-                pd.ld = p;
-                pd.c0 = c0;
-                pd.h = h;
-                pd.nb = nbw;
-                int cls = panel_rows_class(h);
-                if (cls > 0 && panel_lds_bytes(true, h) > lds_limit) cls = 0;
-                int bucket = 0;
-                while (cls > 0 && (2 << bucket) < cls) ++bucket;
-                bucket = cls > 0 ? bucket + 1 : 0;
-                byc[bucket].push_back(pd);
-                maxh[bucket] = std::max(maxh[bucket], h);
-                float* Vp = pd.V;
-                float* Yp = pd.Y;
-                float* Z = wsf(S.Z);
-                float* Wb = wsf(S.W);
-                float* Qs = wsf(S.Qm) + c0;                       // Q[:, c0:]
-                const int ntr = p - c0 - nbw;
-                const int kchunk = ((h + ksplit - 1) / ksplit + 15) / 16 * 16;
-                const int nsplit = (h + kchunk - 1) / kchunk;
-                const int64_t zslab = (int64_t)kPanel * p, wslab = (int64_t)p * kPanel;
-                if (ntr > 0) {
-                    float* At = wsf(S.Pm) + (int64_t)c0 * p + c0 + nbw;
-                    GemmDesc z = gd(Yp, kPanel, At, p, Z, p, nbw, ntr, h);
-                    z.ksplit = nsplit; z.kchunk = kchunk; z.dslab = zslab;
-                    t1.push_back({z, true, false});
-                    GemmDesc u = gd(Vp, kPanel, Z, p, At, p, h, ntr, nbw, -1.f, 1.f, At, p);
-                    u.bnslab = nsplit; u.bslab = zslab;
-                    t2.push_back({u, false, false});
-                }
-                GemmDesc w = gd(Qs, p, Yp, kPanel, Wb, kPanel, p, nbw, h);
-                w.ksplit = nsplit; w.kchunk = kchunk; w.dslab = wslab;
-                t1.push_back({w, false, false});
-                GemmDesc q = gd(Wb, kPanel, Vp, kPanel, Qs, p, p, h, nbw, -1.f, 1.f, Qs, p);
-                q.anslab = nsplit; q.aslab = wslab;
-                t2.push_back({q, false, true});
-            }
-            for (int b = 0; b < 8; ++b) {
-                if (byc[b].empty()) continue;
-                std::vector<int> ones(byc[b].size(), 1);
-                Launch L = make_items(K_PANEL, byc[b], ones);
-                L.mode = b == 0 ? 0 : (1 << b);
-                L.max_h = maxh[b];
-                L.ntiles = (int)byc[b].size();
-                panel[sidx].push_back(L);
-            }
-            trail[sidx] = make_gemm(t1, FAM_GEMM_QR);
-            upd[sidx] = make_gemm(t2, FAM_GEMM_QR);
-        }
+        if (lookahead) build_qr_lookahead(); else build_qr_blocked();
         {
             std::vector<VecDesc> qi, rr, rt;
             std::vector<int> tqi, trr, trt;
@@ -444,7 +653,7 @@ struct shampoo4_ctx_s {
                 std::memset(&v, 0, sizeof(v));
                 v.out = wsf(S.Qm); v.aux = wsf(S.rdiag); v.ld = p; v.p = p;
                 qi.push_back(v);
-                tqi.push_back((int)(((int64_t)p * p + FILL_TILE - 1) / FILL_TILE));
+                tqi.push_back(fill_tiles(p));
                 // Rayleigh: partial column sums of Q .* (L~ Q) per row tile into Wg
                 GemmDesc d = gd(wsf(S.Lt), p, wsf(S.Qm), p, wsf(S.Wg), p, p, p, p, 1.f, 0.f, wsf(S.Qm), p);
                 d.flags = GEMM_F_COLDOT;
@@ -521,7 +730,10 @@ struct shampoo4_ctx_s {
     }
 
     // ---- execution ------------------------------------------------------------
-    hipError_t run(const Launch& L, hipStream_t s) {
+    hipError_t run(const Launch& L, hipStream_t caller) {
+        const hipStream_t s = L.strm ? aux : caller;
+        if (L.kind == K_RECORD) return hipEventRecord(sync_ev[L.ev], s);
+        if (L.kind == K_WAIT) return hipStreamWaitEvent(s, sync_ev[L.ev], 0);
         const uint8_t* base = ws + desc_base;
         const int* prefix = reinterpret_cast<const int*>(base + L.prefix_off);
         const IoEntry* io = wsp<IoEntry>(io_off);
@@ -575,6 +787,9 @@ struct shampoo4_ctx_s {
             case K_INIT:
                 e = launch_identity_state(reinterpret_cast<const InitDesc*>(base + L.desc_off), prefix,
                                           L.ndesc, L.ntiles, s);
+                break;
+            case K_RECORD:
+            case K_WAIT:
                 break;
         }
         if (timing) {
@@ -641,7 +856,11 @@ shampoo4_status validate_cfg(const shampoo4_config* cfg) {
     if (cfg->qblock != 64) return SHAMPOO4_EINVAL;
     if (cfg->bjorck_iters < 0 || cfg->bjorck_iters > 16) return SHAMPOO4_EINVAL;
     if (cfg->power_iters < 1 || cfg->power_iters > 8) return SHAMPOO4_EINVAL;
-    if (cfg->flags & ~(SHAMPOO4_FLAG_ROOT_CACHE | SHAMPOO4_FLAG_KEEP_STATE)) return SHAMPOO4_EINVAL;
+    if (cfg->flags & ~(SHAMPOO4_FLAG_ROOT_CACHE | SHAMPOO4_FLAG_KEEP_STATE | SHAMPOO4_FLAG_QR_BLOCKED |
+                       SHAMPOO4_FLAG_QR_LOOKAHEAD))
+        return SHAMPOO4_EINVAL;
+    if ((cfg->flags & SHAMPOO4_FLAG_QR_BLOCKED) && (cfg->flags & SHAMPOO4_FLAG_QR_LOOKAHEAD))
+        return SHAMPOO4_EINVAL;
     return SHAMPOO4_OK;
 }
 
@@ -732,6 +951,12 @@ shampoo4_status shampoo4_init(const shampoo4_config* cfg, int32_t nblocks, const
     c->st = static_cast<uint8_t*>(state);
     c->ws = static_cast<uint8_t*>(workspace);
     c->build();
+    if (c->n_sync > 0) {   // second stream (default priority) and its synchronization events
+        if (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess) return SHAMPOO4_EHIP;
+        c->sync_ev.assign(c->n_sync, nullptr);
+        for (auto& ev : c->sync_ev)
+            if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return SHAMPOO4_EHIP;
+    }
     const size_t need_ws = c->desc_base + align_up(c->blob.size());
     if (state_bytes < c->st_bytes || workspace_bytes < need_ws) return SHAMPOO4_ESMALLBUF;
     c->ws_bytes = need_ws;
@@ -780,10 +1005,9 @@ shampoo4_status shampoo4_update_stats(shampoo4_ctx c, const shampoo4_io* io, voi
         e = c->run(it == 0 ? c->power_first[var] : c->power_next, s);
         if (e == hipSuccess) e = c->run(c->qinit, s);
         for (int p = 0; p < c->max_panels && e == hipSuccess; ++p) {
-            e = c->run(c->panel[p], s);
-            if (e == hipSuccess) e = c->run(c->trail[p], s);
-            if (e == hipSuccess) e = c->run(c->upd[p], s);
+            e = c->run(c->qr_steps[p], s);
         }
+        if (e == hipSuccess) e = c->run(c->qr_join, s);
         if (e == hipSuccess) e = c->run(c->sign, s);
     }
     if (e == hipSuccess) e = c->run(c->ray_gemm, s);

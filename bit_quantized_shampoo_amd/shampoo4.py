@@ -55,9 +55,13 @@ class Shampoo4Config:
     bjorck_iters: int = 1
     power_iters: int = 1
     root_cache: bool = False
+    qr_schedule: str = "auto"       # "auto", "blocked" or "lookahead"
 
     def c(self, keep_state: bool = False) -> L.Config:
         flags = (L.FLAG_ROOT_CACHE if self.root_cache else 0) | (L.FLAG_KEEP_STATE if keep_state else 0)
+        if self.qr_schedule not in ("auto", "blocked", "lookahead"):
+            raise ValueError(f"qr_schedule must be auto, blocked or lookahead, not {self.qr_schedule!r}")
+        flags |= {"auto": 0, "blocked": L.FLAG_QR_BLOCKED, "lookahead": L.FLAG_QR_LOOKAHEAD}[self.qr_schedule]
         return L.Config(self.beta, self.eps, self.qblock, self.bjorck_iters, self.power_iters, flags)
 
 

@@ -77,6 +77,17 @@ typedef enum {
                                          Without the flag precondition recomputes them. */
 #define SHAMPOO4_FLAG_KEEP_STATE 2u   /* shampoo4_init: do not write the initial state;
                                          the state buffer already holds a saved state. */
+/* Schedule of the Householder QR (same results either way up to rounding order).  By
+   default the plan picks from the total work W = sum over sides of p^3: reflectors reach
+   the trailing matrix and Q in blocks of 128 columns when W >= 16 * 2^30 (throughput:
+   large batches), else panel by panel (32 columns), all on the caller's stream.
+   QR_BLOCKED   always 128-column blocks;
+   QR_LOOKAHEAD 32-column panels; the caller's stream carries only the chain of panels
+                and each panel's update of the next panel, a second stream of the context
+                (default priority) the trailing and Q updates.
+   Setting both is EINVAL. */
+#define SHAMPOO4_FLAG_QR_BLOCKED 4u
+#define SHAMPOO4_FLAG_QR_LOOKAHEAD 8u
 
 typedef struct {
     int32_t m, n;             /* block shape: G is [m, n]; side L has order m, side R order n */

@@ -29,10 +29,10 @@ TOL = 1e-3
 
 
 def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power_iters=1,
-                        root_interval=1, root_cache=False, label=""):
+                        root_interval=1, root_cache=False, label="", qr="auto"):
     from bit_quantized_shampoo_amd import Shampoo4Blocks, Shampoo4Config
     cfg = Shampoo4Config(beta=beta, eps=eps, bjorck_iters=k, power_iters=power_iters,
-                         root_cache=root_cache)
+                         root_cache=root_cache, qr_schedule=qr)
     announce(f"step parity {label}: init {shapes}")
     blocks = Shampoo4Blocks(shapes, cfg)
     torch.cuda.synchronize()
@@ -125,8 +125,10 @@ def test_single_64x32_root_cache():
     ([(96, 160), (130, 65)], 0, 2, 1, False),             # no Bjorck, two power steps
     ([(64, 64)], 5, 1, 1, True),
     ([(1100, 40)], 1, 1, 1, True),                        # panels taller than the register path
+    ([(300, 257), (129, 128)], 1, 1, 1, False),           # ragged 128-column reflector blocks
 ])
-def test_ragged_batches(shapes, k, power_iters, T, cache):
+@pytest.mark.parametrize("qr", ["auto", "blocked", "lookahead"])
+def test_ragged_batches(shapes, k, power_iters, T, cache, qr):
     require_gpu()
     rng = np.random.default_rng(sum(m * 31 + n for m, n in shapes))
     scales = [(10.0 ** rng.uniform(-1, 1, (m, 1))) * (10.0 ** rng.uniform(-1, 1, (1, n))) for m, n in shapes]
@@ -136,7 +138,7 @@ def test_ragged_batches(shapes, k, power_iters, T, cache):
         return [(r.standard_normal((m, n)) * sc).astype(np.float32) for (m, n), sc in zip(shapes, scales)]
 
     _run_teacher_forced(shapes, grads, 4, k=k, power_iters=power_iters, root_interval=T,
-                        root_cache=cache, label=f"ragged {shapes}")
+                        root_cache=cache, label=f"ragged {shapes} qr={qr}", qr=qr)
 
 
 def test_single_1024_steps():
@@ -166,7 +168,8 @@ def test_cnn_batch_two_steps():
         return [wl.block_gradient(i, t) for i in idx]
 
     del sel
-    _run_teacher_forced(shapes, grads, 2, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters, label="cnn_batch")
+    _run_teacher_forced(shapes, grads, 2, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters, label="cnn_batch",
+                        qr="blocked")
 
 
 def test_update_is_deterministic_and_resumable():

@@ -79,7 +79,10 @@ def test_plan_sizes():
     ([(4, 4)], {"k": -1}, L.EINVAL),
     ([(4, 4)], {"k": 17}, L.EINVAL),
     ([(4, 4)], {"pi": 0}, L.EINVAL),
-    ([(4, 4)], {"flags": 8}, L.EINVAL),
+    ([(4, 4)], {"flags": 16}, L.EINVAL),
+    ([(4, 4)], {"flags": L.FLAG_QR_BLOCKED | L.FLAG_QR_LOOKAHEAD}, L.EINVAL),
+    ([(4, 4)], {"flags": L.FLAG_QR_BLOCKED}, L.OK),
+    ([(4, 4)], {"flags": L.FLAG_QR_LOOKAHEAD}, L.OK),
     ([(1, 1)], {}, L.OK),
     ([(8192, 1)], {}, L.OK),
 ])
