@@ -27,6 +27,21 @@ inline LaunchTiming& launch_timing() {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+// Loads and stores through the global address space.  Pointers taken from descriptor
+// tables are generic (flat) to the compiler; flat accesses also count against the LDS
+// wait counter, so every LDS wait of a kernel would also wait for its in-flight global
+// prefetches.  Casting to address space 1 emits global_load / global_store instead.
+template <class T>
+__device__ __forceinline__ T ldg(const T* p) {
+    using G = __attribute__((address_space(1))) const T;
+    return *(G*)p;
+}
+template <class T>
+__device__ __forceinline__ void stg(T* p, T v) {
+    using G = __attribute__((address_space(1))) T;
+    *(G*)p = v;
+}
+
 // Per-block user pointers of one call, uploaded once per call; descriptors refer
 // to an entry by index so that the static descriptor tables never change.
 struct IoEntry {
@@ -42,6 +57,9 @@ struct IoEntry {
 // Split K: with ksplit > 1 the K range is cut into chunks of kchunk and chunk s writes
 // its partial product (beta must be 0) to D + s * dslab.  A consumer reads such
 // partials back summed: op(A) = sum_{s < anslab} A[s * aslab ...] (same for B).
+// Most split-K partial slabs a GEMM operand may sum while loading.
+constexpr int GEMM_MAX_SLABS = 8;
+
 struct GemmDesc {
     const float* A;
     const float* B;

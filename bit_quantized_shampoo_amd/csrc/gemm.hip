@@ -48,38 +48,67 @@ struct Tile {
     static constexpr int RED = WM * BN;        // COLDOT cross-wave partials
 };
 
-__device__ __forceinline__ floatx4 load_quad(const float* __restrict__ base, int64_t ld,
-                                             int row, int col, int rows, int cols, bool vec_ok);
-
-// Sum of `nslab` split-K partials (slab stride `slab` elements); one slab is a plain load.
-__device__ __forceinline__ floatx4 load_quad_sum(const float* __restrict__ base, int64_t slab, int nslab,
-                                                 int64_t ld, int row, int col, int rows, int cols,
-                                                 bool vec_ok) {
-    floatx4 v = load_quad(base, ld, row, col, rows, cols, vec_ok);
-    for (int s = 1; s < nslab; ++s) {
-        const floatx4 w = load_quad(base + s * slab, ld, row, col, rows, cols, vec_ok);
-        v[0] += w[0]; v[1] += w[1]; v[2] += w[2]; v[3] += w[3];
-    }
-    return v;
+// Operand loads are branch-free: every address is clamped into the operand and
+// out-of-range elements are zeroed with an AND on the loaded bits.  (A select on a
+// loaded value is turned into a branch around the load with a wait for it inside,
+// which serializes the loads of a tile.)
+__device__ __forceinline__ float keep_if(float v, bool keep) {
+    return __uint_as_float(__float_as_uint(v) & (keep ? 0xffffffffu : 0u));
 }
 
-__device__ __forceinline__ floatx4 load_quad(const float* __restrict__ base, int64_t ld,
-                                             int row, int col, int rows, int cols, bool vec_ok) {
-    floatx4 v = {0.f, 0.f, 0.f, 0.f};
-    if (row >= rows) return v;
-    const float* p = base + (int64_t)row * ld + col;
-    if (vec_ok && col + 3 < cols) {
-        v = *reinterpret_cast<const floatx4*>(p);
+// Elements (row, col..col+3) of a rows x cols operand (rows, cols >= 1) are loaded in
+// two phases so that a slice's loads stay in flight across the matrix-core work of the
+// previous slice: raw_quad issues the loads (addresses clamped into the operand, no
+// use of the values), finish_quad later zeroes the out-of-range elements.  VEC (chosen
+// per launch: 16-byte aligned base, ld and cols multiples of 4) makes a quad lie
+// entirely inside or entirely outside the operand: one 16-byte load.
+template <bool VEC>
+__device__ __forceinline__ floatx4 raw_quad(const float* __restrict__ base, int64_t ld, int row, int col,
+                                            int rows, int cols) {
+    const float* p = base + (int64_t)min(row, rows - 1) * ld;
+    floatx4 v;
+    if constexpr (VEC) {
+        v = ldg(reinterpret_cast<const floatx4*>(p + min(col, cols - 4)));
     } else {
-        if (col + 0 < cols) v[0] = p[0];
-        if (col + 1 < cols) v[1] = p[1];
-        if (col + 2 < cols) v[2] = p[2];
-        if (col + 3 < cols) v[3] = p[3];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = ldg(p + min(col + e, cols - 1));
     }
     return v;
 }
 
-template <int WM, int WN, int TM, int TN, bool TA, bool TB>
+template <bool VEC>
+__device__ __forceinline__ floatx4 finish_quad(floatx4 v, int row, int col, int rows, int cols) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = keep_if(v[e], row < rows && (VEC ? col : col + e) < cols);
+    return v;
+}
+
+// Split-K partial slabs a consuming operand sums while loading (slab order, fixed).
+template <bool SLAB>
+constexpr int kSlabs = SLAB ? GEMM_MAX_SLABS : 1;
+
+// Raw loads of one quad from every slab (slab index clamped to nslab - 1).
+template <bool VEC, bool SLAB>
+__device__ __forceinline__ void raw_quads(floatx4 (&w)[kSlabs<SLAB>], const float* __restrict__ base,
+                                          int64_t slab, int nslab, int64_t ld, int row, int col, int rows,
+                                          int cols) {
+#pragma unroll
+    for (int s = 0; s < kSlabs<SLAB>; ++s)
+        w[s] = raw_quad<VEC>(base + (int64_t)min(s, nslab - 1) * slab, ld, row, col, rows, cols);
+}
+
+template <bool VEC, bool SLAB>
+__device__ __forceinline__ floatx4 finish_quads(const floatx4 (&w)[kSlabs<SLAB>], int nslab, int row, int col,
+                                                int rows, int cols) {
+    floatx4 v = w[0];
+#pragma unroll
+    for (int s = 1; s < kSlabs<SLAB>; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += keep_if(w[s][e], s < nslab);
+    return finish_quad<VEC>(v, row, col, rows, cols);
+}
+
+template <int WM, int WN, int TM, int TN, bool TA, bool TB, bool VEC, bool SLAB>
 __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEntry* __restrict__ io,
                                           float* __restrict__ As, float* __restrict__ Bs) {
     using T = Tile<WM, WN, TM, TN>;
@@ -115,9 +144,6 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
     const int64_t aslab = dsc.aslab, bslab = dsc.bslab;
     const float* __restrict__ kscale = dsc.kscale;
 
-    const bool avec = ((reinterpret_cast<uintptr_t>(A) & 15) == 0) && ((lda & 3) == 0);
-    const bool bvec = ((reinterpret_cast<uintptr_t>(B) & 15) == 0) && ((ldb & 3) == 0);
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
@@ -134,74 +160,90 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
 
-    floatx4 ra[RA], rb[RB];
+    // raw operand loads of the slice in flight, and the raw K-scale values of B's rows
+    floatx4 ra[RA][kSlabs<SLAB>], rb[RB][kSlabs<SLAB>];
+    float kraw[RB][TB ? 4 : 1];
 
+    // The K scale (statistics: V diag(lam) V^T) is applied branch-free: without one, the
+    // scale is read from B itself and replaced by 1 with a bit mask.
+    const float* __restrict__ ksp = kscale ? kscale : B;
+    const uint32_t ksm = kscale ? 0xffffffffu : 0u;
+    auto kfac = [&](float raw) { return __uint_as_float((__float_as_uint(raw) & ksm) | (0x3f800000u & ~ksm)); };
+
+    // quad q of a slice: (row, col) coordinates inside the operand as stored
+    auto a_coord = [&](int q, int k0, int& row, int& col) {
+        if constexpr (!TA) { row = row0 + q / (BK / 4); col = k0 + (q % (BK / 4)) * 4; }
+        else { row = k0 + q / (BM / 4); col = row0 + (q % (BM / 4)) * 4; }
+    };
+    auto b_coord = [&](int q, int k0, int& row, int& col) {
+        if constexpr (TB) { row = col0 + q / (BK / 4); col = k0 + (q % (BK / 4)) * 4; }
+        else { row = k0 + q / (BN / 4); col = col0 + (q % (BN / 4)) * 4; }
+    };
+
+    // Every thread issues all its loads of a slice unconditionally (threads past the
+    // slice's last quad reload it and do not store it), so no load sits behind a branch.
     auto load_slice = [&](int k0) {
 #pragma unroll
         for (int r = 0; r < RA; ++r) {
-            const int q = tid + r * 256;
-            if (q < NQA) {
-                if constexpr (!TA) {
-                    const int i = q / (BK / 4), kq = (q % (BK / 4)) * 4;
-                    ra[r] = load_quad_sum(A, aslab, anslab, lda, row0 + i, k0 + kq, M, K, avec);
-                } else {
-                    const int k = q / (BM / 4), iq = (q % (BM / 4)) * 4;
-                    ra[r] = load_quad_sum(A, aslab, anslab, lda, k0 + k, row0 + iq, K, M, avec);
-                }
-            }
+            int row, col;
+            a_coord(min(tid + r * 256, NQA - 1), k0, row, col);
+            raw_quads<VEC, SLAB>(ra[r], A, aslab, anslab, lda, row, col, TA ? K : M, TA ? M : K);
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const int q = tid + r * 256;
-            if (q < NQB) {
-                if constexpr (TB) {
-                    const int j = q / (BK / 4), kq = (q % (BK / 4)) * 4;
-                    floatx4 v = load_quad_sum(B, bslab, bnslab, ldb, col0 + j, k0 + kq, N, K, bvec);
-                    if (kscale) {
+            int row, col;
+            b_coord(min(tid + r * 256, NQB - 1), k0, row, col);
+            raw_quads<VEC, SLAB>(rb[r], B, bslab, bnslab, ldb, row, col, TB ? N : K, TB ? K : N);
+            if constexpr (TB) {
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (k0 + kq + e < K) v[e] *= kscale[k0 + kq + e];
-                    }
-                    rb[r] = v;
-                } else {
-                    const int k = q / (BN / 4), jq = (q % (BN / 4)) * 4;
-                    floatx4 v = load_quad_sum(B, bslab, bnslab, ldb, k0 + k, col0 + jq, K, N, bvec);
-                    if (kscale && k0 + k < K) {
-                        const float s = kscale[k0 + k];
-                        v[0] *= s; v[1] *= s; v[2] *= s; v[3] *= s;
-                    }
-                    rb[r] = v;
-                }
+                for (int e = 0; e < 4; ++e) kraw[r][e] = ldg(ksp + min(col + e, K - 1));
+            } else {
+                kraw[r][0] = ldg(ksp + min(row, K - 1));
             }
         }
     };
 
-    auto store_slice = [&](int buf) {
+    // masks, slab sums and the K scale are applied here, after the previous slice's
+    // matrix-core work, then the slice goes to LDS
+    auto store_slice = [&](int buf, int k0) {
         float* as = As + buf * A_SZ;
         float* bs = Bs + buf * B_SZ;
 #pragma unroll
         for (int r = 0; r < RA; ++r) {
             const int q = tid + r * 256;
-            if (q < NQA) {
+            int row, col;
+            a_coord(min(q, NQA - 1), k0, row, col);
+            const floatx4 v = finish_quads<VEC, SLAB>(ra[r], anslab, row, col, TA ? K : M, TA ? M : K);
+            if (NQA % 256 == 0 || q < NQA) {
                 if constexpr (!TA) {
                     const int i = q / (BK / 4), kq = (q % (BK / 4)) * 4;
-                    *reinterpret_cast<floatx4*>(&as[i * KCP + kq]) = ra[r];
+                    *reinterpret_cast<floatx4*>(&as[i * KCP + kq]) = v;
                 } else {
                     const int k = q / (BM / 4), iq = (q % (BM / 4)) * 4;
-                    *reinterpret_cast<floatx4*>(&as[k * AMCP + iq]) = ra[r];
+                    *reinterpret_cast<floatx4*>(&as[k * AMCP + iq]) = v;
                 }
             }
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             const int q = tid + r * 256;
-            if (q < NQB) {
+            int row, col;
+            b_coord(min(q, NQB - 1), k0, row, col);
+            floatx4 v = finish_quads<VEC, SLAB>(rb[r], bnslab, row, col, TB ? N : K, TB ? K : N);
+            if constexpr (TB) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= kfac(kraw[r][e]);   // past K: already zero
+            } else {
+                const float f = kfac(kraw[r][0]);
+                v[0] *= f; v[1] *= f; v[2] *= f; v[3] *= f;
+            }
+            if (NQB % 256 == 0 || q < NQB) {
                 if constexpr (TB) {
                     const int j = q / (BK / 4), kq = (q % (BK / 4)) * 4;
-                    *reinterpret_cast<floatx4*>(&bs[j * KCP + kq]) = rb[r];
+                    *reinterpret_cast<floatx4*>(&bs[j * KCP + kq]) = v;
                 } else {
                     const int k = q / (BN / 4), jq = (q % (BN / 4)) * 4;
-                    *reinterpret_cast<floatx4*>(&bs[k * BMCP + jq]) = rb[r];
+                    *reinterpret_cast<floatx4*>(&bs[k * BMCP + jq]) = v;
                 }
             }
         }
@@ -210,7 +252,7 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
     const int nk = (K - kbeg + BK - 1) / BK;
     if (nk > 0) {
         load_slice(kbeg);
-        store_slice(0);
+        store_slice(0, kbeg);
     }
     __syncthreads();
 
@@ -255,7 +297,7 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
                                                                          acc[m][n], 0, 0, 0);
         }
 
-        if (more) store_slice(cur ^ 1);
+        if (more) store_slice(cur ^ 1, kbeg + (kt + 1) * BK);
         __syncthreads();
     }
 
@@ -273,14 +315,20 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
             const int lcol = wave_n * TN * 32 + n * 32 + l32;
             const int col = col0 + lcol;
             float s = 0.f;
-            if (col < N) {
+            const int colc = min(col, N - 1);
 #pragma unroll
-                for (int m = 0; m < TM; ++m)
+            for (int m = 0; m < TM; ++m) {
+                float cv[16];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                        if (row < M) s += acc[m][n][r] * C[(int64_t)row * ldc + col];
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                    cv[r] = ldg(C + (int64_t)min(row, M - 1) * ldc + colc);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                    s += acc[m][n][r] * keep_if(cv[r], row < M && col < N);
+                }
             }
             s += __shfl_xor(s, 32);
             if (h == 0) red[wave_m * BN + lcol] = s;
@@ -294,7 +342,7 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
                 float s = 0.f;
 #pragma unroll
                 for (int w = 0; w < WM; ++w) s += red[w * BN + lcol];
-                if (col < N) D[(int64_t)tile_m * ldd + col] = alpha * s;
+                if (col < N) stg(D + (int64_t)tile_m * ldd + col, alpha * s);
             }
         }
         return;
@@ -302,28 +350,41 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
 
     const float* __restrict__ rs = dsc.rscale;
     const float* __restrict__ cs = dsc.cscale;
+    // the C, row-scale and column-scale values of a 32 x 32 block are loaded (clamped
+    // addresses) before any is used, absent ones from D in their place and replaced by
+    // bit masks; stores are predicated on the bounds
+    const float* __restrict__ cp = (beta != 0.f) ? C : D;
+    const int64_t ldcp = (beta != 0.f) ? ldc : ldd;
+    const float* __restrict__ rsp = rs ? rs : D;
+    const uint32_t rsm = rs ? 0xffffffffu : 0u;
+    const float* __restrict__ csp = cs ? cs : D;
+    const uint32_t csm = cs ? 0xffffffffu : 0u;
 #pragma unroll
     for (int n = 0; n < TN; ++n) {
         const int col = col0 + wave_n * TN * 32 + n * 32 + l32;
-        if (col >= N) continue;
-        const float csv = cs ? cs[col] : 1.f;
+        const int colc = min(col, N - 1);
+        const float csv = __uint_as_float((__float_as_uint(ldg(csp + colc)) & csm) | (0x3f800000u & ~csm));
 #pragma unroll
         for (int m = 0; m < TM; ++m) {
+            float cv[16], rv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                if (row < M) {
-                    float v = alpha * acc[m][n][r];
-                    if (rs) v *= rs[row];
-                    v *= csv;
-                    if (beta != 0.f) v += beta * C[(int64_t)row * ldc + col];
-                    D[(int64_t)row * ldd + col] = v;
-                }
+                const int rowc = min(row, M - 1);
+                cv[r] = keep_if(ldg(cp + (int64_t)rowc * ldcp + colc), beta != 0.f);
+                rv[r] = __uint_as_float((__float_as_uint(ldg(rsp + rowc)) & rsm) | (0x3f800000u & ~rsm));
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+                const float v = fmaf(beta, cv[r], alpha * acc[m][n][r] * rv[r] * csv);
+                if (row < M && col < N) stg(D + (int64_t)row * ldd + col, v);
             }
         }
     }
 }
 
+// One transpose mode for the whole launch, 16-byte loads, no split-K slabs.
 template <int WM, int WN, int TM, int TN, bool TA, bool TB>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ descs,
                                                    const int* __restrict__ prefix, int ndesc,
@@ -335,10 +396,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ 
     __shared__ __attribute__((aligned(16))) float As[A_ALL];
     __shared__ __attribute__((aligned(16))) float Bs[2 * B_SZ];
     const int item = find_item(prefix, ndesc, blockIdx.x);
-    gemm_body<WM, WN, TM, TN, TA, TB>(descs[item], blockIdx.x - prefix[item], io, As, Bs);
+    gemm_body<WM, WN, TM, TN, TA, TB, true, false>(descs[item], blockIdx.x - prefix[item], io, As, Bs);
 }
 
-template <int WM, int WN, int TM, int TN>
+// Transpose mode per descriptor (uniform per workgroup); VEC and SLAB per launch.
+template <int WM, int WN, int TM, int TN, bool VEC, bool SLAB>
 __global__ __launch_bounds__(256) void gemm_kernel_mixed(const GemmDesc* __restrict__ descs,
                                                          const int* __restrict__ prefix, int ndesc,
                                                          const IoEntry* __restrict__ io) {
@@ -350,43 +412,58 @@ __global__ __launch_bounds__(256) void gemm_kernel_mixed(const GemmDesc* __restr
     const GemmDesc& d = descs[item];
     const int t = blockIdx.x - prefix[item];
     switch (d.flags & (GEMM_F_TA | GEMM_F_TB)) {
-        case 0: gemm_body<WM, WN, TM, TN, false, false>(d, t, io, As, Bs); break;
-        case GEMM_F_TB: gemm_body<WM, WN, TM, TN, false, true>(d, t, io, As, Bs); break;
-        case GEMM_F_TA: gemm_body<WM, WN, TM, TN, true, false>(d, t, io, As, Bs); break;
-        default: gemm_body<WM, WN, TM, TN, true, true>(d, t, io, As, Bs); break;
+        case 0: gemm_body<WM, WN, TM, TN, false, false, VEC, SLAB>(d, t, io, As, Bs); break;
+        case GEMM_F_TB: gemm_body<WM, WN, TM, TN, false, true, VEC, SLAB>(d, t, io, As, Bs); break;
+        case GEMM_F_TA: gemm_body<WM, WN, TM, TN, true, false, VEC, SLAB>(d, t, io, As, Bs); break;
+        default: gemm_body<WM, WN, TM, TN, true, true, VEC, SLAB>(d, t, io, As, Bs); break;
     }
 }
 
 template <int WM, int WN, int TM, int TN>
-hipError_t launch_cfg(int mode, const GemmDesc* descs, const int* prefix, int ndesc, int ntiles,
-                      const IoEntry* io, hipStream_t stream) {
+hipError_t launch_cfg(int mode, bool vec, bool slab, const GemmDesc* descs, const int* prefix, int ndesc,
+                      int ntiles, const IoEntry* io, hipStream_t stream) {
     dim3 grid(ntiles), block(256);
+    if (!vec || slab || mode == GEMM_MODE_MIXED) {
+        if (vec && slab)
+            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, true, true>), grid, block, 0, stream, descs, prefix, ndesc, io);
+        else if (vec)
+            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, true, false>), grid, block, 0, stream, descs, prefix, ndesc, io);
+        else if (slab)
+            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, false, true>), grid, block, 0, stream, descs, prefix, ndesc, io);
+        else
+            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, false, false>), grid, block, 0, stream, descs, prefix, ndesc, io);
+        return hipGetLastError();
+    }
     switch (mode) {
         case 0:
-            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, false>), grid, block, 0, stream,
-                               descs, prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, false>), grid, block, 0, stream, descs, prefix, ndesc, io);
             break;
         case GEMM_F_TB:
-            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, true>), grid, block, 0, stream,
-                               descs, prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, true>), grid, block, 0, stream, descs, prefix, ndesc, io);
             break;
         case GEMM_F_TA:
-            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, false>), grid, block, 0, stream,
-                               descs, prefix, ndesc, io);
-            break;
-        case GEMM_F_TA | GEMM_F_TB:
-            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, true>), grid, block, 0, stream,
-                               descs, prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, false>), grid, block, 0, stream, descs, prefix, ndesc, io);
             break;
         default:
-            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN>), grid, block, 0, stream, descs,
-                               prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, true>), grid, block, 0, stream, descs, prefix, ndesc, io);
             break;
     }
     return hipGetLastError();
 }
 
 }  // namespace
+
+bool gemm_vec_ok(const GemmDesc& d) {
+    const bool ta = d.flags & GEMM_F_TA, tb = d.flags & GEMM_F_TB;
+    auto ok = [](const void* p, int64_t ld, int64_t extent, int nslab, int64_t slab) {
+        return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && (ld & 3) == 0 && (extent & 3) == 0 &&
+               (nslab <= 1 || (slab & 3) == 0);
+    };
+    const int64_t ea = ta ? d.M : d.K, eb = tb ? d.K : d.N;
+    const bool a = d.a_io >= 0 ? (ea & 3) == 0 : ok(d.A, d.lda, ea, d.anslab, d.aslab);
+    const bool b = d.b_io >= 0 ? (eb & 3) == 0 : ok(d.B, d.ldb, eb, d.bnslab, d.bslab);
+    return a && b;
+}
 
 void gemm_tile_dims(int cfg, int* bm, int* bn) {
     switch (cfg) {
@@ -396,13 +473,13 @@ void gemm_tile_dims(int cfg, int* bm, int* bn) {
     }
 }
 
-hipError_t launch_gemm(int cfg, int mode, const GemmDesc* descs, const int* prefix, int ndesc, int ntiles,
-                       const IoEntry* io, hipStream_t stream) {
+hipError_t launch_gemm(int cfg, int mode, bool vec, bool slab, const GemmDesc* descs, const int* prefix,
+                       int ndesc, int ntiles, const IoEntry* io, hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
     switch (cfg) {
-        case GEMM_128x128: return launch_cfg<2, 2, 2, 2>(mode, descs, prefix, ndesc, ntiles, io, stream);
-        case GEMM_64x64: return launch_cfg<2, 2, 1, 1>(mode, descs, prefix, ndesc, ntiles, io, stream);
-        default: return launch_cfg<1, 4, 1, 1>(mode, descs, prefix, ndesc, ntiles, io, stream);
+        case GEMM_128x128: return launch_cfg<2, 2, 2, 2>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
+        case GEMM_64x64: return launch_cfg<2, 2, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
+        default: return launch_cfg<1, 4, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
     }
 }
 

@@ -11,9 +11,16 @@ namespace s4 {
 enum GemmCfg { GEMM_128x128 = 0, GEMM_64x64 = 1, GEMM_32x128 = 2, GEMM_NCFG = 3 };
 constexpr int GEMM_MODE_MIXED = -1;   // descriptors of one launch carry different transposes
 void gemm_tile_dims(int cfg, int* bm, int* bn);
-// mode: GEMM_F_TA | GEMM_F_TB shared by all descriptors, or GEMM_MODE_MIXED
-hipError_t launch_gemm(int cfg, int mode, const GemmDesc* descs, const int* prefix,
+// mode: GEMM_F_TA | GEMM_F_TB shared by all descriptors, or GEMM_MODE_MIXED.
+// vec: every operand of every descriptor has a 16-byte aligned base (after io
+// indirection), a pitch and a contiguous extent that are multiples of 4, and slab
+// strides that are multiples of 4 (gemm_vec_ok on the host).
+// slab: some descriptor sums split-K slabs while loading (anslab or bnslab > 1).
+hipError_t launch_gemm(int cfg, int mode, bool vec, bool slab, const GemmDesc* descs, const int* prefix,
                        int ndesc, int ntiles, const IoEntry* io, hipStream_t stream);
+// Host check of the 16-byte-load conditions of one descriptor, operands given through
+// the io table excepted (their pointers and pitches are checked per call).
+bool gemm_vec_ok(const GemmDesc& d);
 
 // Codec: elements per workgroup tile.
 constexpr int DEQ_TILE = 8192;     // 256 threads x 4 code words x 8 elements

@@ -154,7 +154,9 @@ __device__ __forceinline__ void form_Y(const float* vsrc, int64_t vpitch, const 
 #pragma unroll
         for (int ks = 0; ks < PW / 2; ++ks) {
             const int k = 2 * ks + hh;
-            const float a = (row < h) ? vsrc[(int64_t)row * vpitch + k] : 0.f;
+            const int rc = row < h ? row : h - 1;
+            const uint32_t m = row < h ? 0xffffffffu : 0u;
+            const float a = __uint_as_float(__float_as_uint(vsrc[(int64_t)rc * vpitch + k]) & m);
             const float b = smem[OFF_T + k * 33 + l32];
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
         }
@@ -197,14 +199,24 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_reg_kernel(const PanelDes
     // Rows beyond h and columns beyond nb are zero: they stay zero under every update
     // and add nothing to any dot, so only the first row groups (r <= 32, where r may
     // equal j or j+1 or lie above the diagonal) need row tests.
+    // All NR loads are issued before any is used: the address is clamped into the panel
+    // and the value masked with an AND (a select on the loaded value would become a
+    // branch around each load, with a wait for it inside).
     float x[NR], xc[NR];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        const int r = slot + NSLOT * i;
-        const int rr = r < h ? r : h - 1;
+    {
         const int cc = c < nb ? c : nb - 1;
-        const float v = Ap[(int64_t)rr * d.ld + cc];
-        x[i] = (r < h && c < nb) ? v : 0.f;
+        const uint32_t cmask = c < nb ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int r = slot + NSLOT * i;
+            const int rr = r < h ? r : h - 1;
+            x[i] = Ap[(int64_t)rr * d.ld + cc];
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const uint32_t m = (slot + NSLOT * i < h) ? cmask : 0u;
+            x[i] = __uint_as_float(__float_as_uint(x[i]) & m);
+        }
     }
     {
         float mx = 0.f;

@@ -26,7 +26,7 @@ constexpr size_t kAlign = 256;
 constexpr int kRing = 8;            // pinned io staging slots
 constexpr int kPanel = 32;          // Householder panel width
 constexpr int kOuter = 128;         // columns whose reflectors update the trailing matrix together
-constexpr int kMaxSplit = 8;        // split-K chunks of the skinny QR products
+constexpr int kMaxSplit = GEMM_MAX_SLABS;   // split-K chunks of the skinny QR products
 constexpr int kMaxDim = 8192;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
@@ -51,6 +51,9 @@ struct Launch {
     size_t desc_off = 0, prefix_off = 0;   // offsets inside the descriptor region
     int ndesc = 0, ntiles = 0, max_h = 0;
     int strm = 0;        // 0: the caller's stream, 1: the context's second stream
+    bool vec = false;    // GEMM: 16-byte operand loads (io operands: also checked per call)
+    bool slab = false;   // GEMM: some operand sums split-K slabs
+    bool uses_io = false;
     int ev = -1;         // K_RECORD / K_WAIT: index of the context's synchronization event
     double flops = 0, bytes = 0;
 };
@@ -107,6 +110,7 @@ struct shampoo4_ctx_s {
 
     // io staging
     uint8_t* pinned = nullptr;
+    bool io_vec = false;              // every G of the current call allows 16-byte loads
     hipEvent_t ring_ev[kRing] = {};
     bool ring_used[kRing] = {};
     int ring_next = 0;
@@ -183,6 +187,12 @@ struct shampoo4_ctx_s {
                               (double)d.M * d.N * ((d.beta != 0.f || coldot) ? 2 : 1));
         }
         prefix.push_back(total);
+        L.vec = true;
+        for (auto& d : ds) {
+            L.vec = L.vec && gemm_vec_ok(d);
+            L.slab = L.slab || d.anslab > 1 || d.bnslab > 1;
+            L.uses_io = L.uses_io || d.a_io >= 0 || d.b_io >= 0;
+        }
         L.kind = K_GEMM;
         L.fam = fam;
         L.cfg = cfgsel;
@@ -749,8 +759,9 @@ struct shampoo4_ctx_s {
         const int fam = L.fam;
         switch (L.kind) {
             case K_GEMM:
-                e = launch_gemm(L.cfg, L.mode, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
-                                prefix, L.ndesc, L.ntiles, io, s);
+                e = launch_gemm(L.cfg, L.mode, L.vec && (!L.uses_io || io_vec), L.slab,
+                                reinterpret_cast<const GemmDesc*>(base + L.desc_off), prefix, L.ndesc, L.ntiles,
+                                io, s);
                 break;
             case K_DEQUANT:
                 e = launch_dequant(reinterpret_cast<const CodecDesc*>(base + L.desc_off), prefix, L.ndesc,
@@ -833,6 +844,9 @@ struct shampoo4_ctx_s {
         }
         uint8_t* dst = pinned + (size_t)slot * align_up(bytes);
         std::memcpy(dst, io, bytes);
+        io_vec = true;
+        for (int b = 0; b < nb; ++b)
+            io_vec = io_vec && (reinterpret_cast<uintptr_t>(io[b].G) & 15) == 0 && (io[b].ldg & 3) == 0;
         hipError_t e = hipMemcpyAsync(ws + io_off, dst, bytes, hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return e;
         ring_used[slot] = true;
@@ -1166,12 +1180,12 @@ shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t tra
     if (seq.empty()) return SHAMPOO4_OK;
     const Launch& L = seq[0];
     hipStream_t s = as_stream(stream);
-    // the descriptors and prefix sit at offsets 0 and align_up(count * 128) of the blob
+    // the descriptors and their tile prefix sit at the start of the caller's workspace
     if (tmp.blob.size() > workspace_bytes) return SHAMPOO4_ESMALLBUF;
     if (hipMemcpyAsync(workspace, tmp.blob.data(), tmp.blob.size(), hipMemcpyHostToDevice, s) != hipSuccess)
         return SHAMPOO4_EHIP;
     const uint8_t* base = static_cast<const uint8_t*>(workspace);
-    hipError_t e = launch_gemm(L.cfg, L.mode, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
+    hipError_t e = launch_gemm(L.cfg, L.mode, L.vec, L.slab, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
                                reinterpret_cast<const int*>(base + L.prefix_off), L.ndesc, L.ntiles, nullptr, s);
     return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
