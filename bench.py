@@ -27,11 +27,109 @@ if ROOT not in sys.path:
 METRIC = "preconditioned block-steps/sec + GEMM TFLOP/s (% MFMA peak), quant GB/s (% HBM)"
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP32_VALU_TFLOPS = 157.3   # 256 CUs x 2.4 GHz x 256 fp32 flops per CU per clock
 DEFAULT_CONFIG = "single_1024"
 
 
 def log(msg: str):
     print(msg, file=sys.stderr, flush=True)
+
+
+# kernel families of the roofline: timing-report families -> (kernel-name test, source file)
+FAMILIES = {
+    "gemm": (lambda n: "gemm_kernel" in n, "gemm.hip"),
+    "qr_panel": (lambda n: "panel_" in n and "_kernel" in n, "qr.hip"),
+    "quant": (lambda n: "quant_kernel" in n and "dequant" not in n, "codec.hip"),
+    "dequant": (lambda n: "dequant_kernel" in n, "codec.hip"),
+}
+CSRC = os.path.join(ROOT, "bit_quantized_shampoo_amd", "csrc")
+
+
+def source_hash(fname: str) -> str:
+    import hashlib
+    with open(os.path.join(CSRC, fname), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+
+
+def summarize_traffic(workload: str, outdir: str):
+    """Per-launch HBM traffic of each kernel family from two rocprofv3 --pmc runs of the
+    bench (FETCH_SIZE, WRITE_SIZE) scaled by the same counters on a plain 1 GiB copy;
+    writes the summary read back by the bench's roofline."""
+    import csv
+    from collections import defaultdict
+
+    def rows(kind, counter):
+        path = os.path.join(outdir, f"pmc_{kind}_{counter}", "run_counter_collection.csv")
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    factor = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp = [float(r["Counter_Value"]) for r in rows("copy", counter) if "copyBuffer" in r["Kernel_Name"]]
+        factor[counter] = (1 << 30) / 1024.0 / (sum(cp) / len(cp))   # KiB per launch of a 1 GiB copy
+    per = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        acc = defaultdict(lambda: [0, 0.0])
+        for r in rows("bench", counter):
+            for fam, (test, _) in FAMILIES.items():
+                if test(r["Kernel_Name"]):
+                    acc[fam][0] += 1
+                    acc[fam][1] += float(r["Counter_Value"])
+        for fam, (n, v) in acc.items():
+            per.setdefault(fam, {})[counter] = (n, v / n)
+    lines = [f"# HBM traffic per launch — `{workload}` bench", "",
+             "Commands (from the repository root, on one MI355X; each counter in its own run):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp"]
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        lines.append(f"rocprofv3 --pmc {counter} --output-format csv -d <repo>/gpurun_out/pmc_copy_{counter} "
+                     f"-o run -- python3 <repo>/bench.py --copy-calibration")
+        lines.append(f"rocprofv3 --pmc {counter} --output-format csv -d <repo>/gpurun_out/pmc_bench_{counter} "
+                     f"-o run -- python3 <repo>/bench.py --config {workload} --steps 3 --warmup 1 --no-cpu")
+    lines += [f"python3 <repo>/bench.py --summarize-traffic <repo>/gpurun_out --config {workload}", "```", "",
+              "Calibration on the plain 1 GiB device copy (`__amd_rocclr_copyBuffer`): FETCH_SIZE reads "
+              f"{1024 * 1024 / factor['FETCH_SIZE']:.0f} KiB and WRITE_SIZE "
+              f"{1024 * 1024 / factor['WRITE_SIZE']:.0f} KiB per launch for 1048576 KiB moved each way, "
+              f"so the scale factors are {factor['FETCH_SIZE']:.4f} (fetch) and {factor['WRITE_SIZE']:.4f} (write).",
+              "", "| Family | Dispatches | FETCH_SIZE KiB (raw avg) | WRITE_SIZE KiB (raw avg) | "
+              "HBM bytes per launch (scaled) |", "|---|---|---|---|---|"]
+    machine = []
+    for fam in FAMILIES:
+        if fam not in per or len(per[fam]) < 2:
+            continue
+        nf, f = per[fam]["FETCH_SIZE"]
+        _, w = per[fam]["WRITE_SIZE"]
+        total = 1024.0 * (f * factor["FETCH_SIZE"] + w * factor["WRITE_SIZE"])
+        lines.append(f"| `{fam}` | {nf} | {f:.1f} | {w:.1f} | {total:.0f} |")
+        machine.append(f"{fam} bytes={total:.0f} source={FAMILIES[fam][1]}:{source_hash(FAMILIES[fam][1])}")
+    lines += ["", "The bench reads the lines below; a line counts only while the kernel source it names still "
+              "has the recorded hash.", "", "```traffic"] + machine + ["```", ""]
+    os.makedirs(os.path.dirname(traffic_path(workload)), exist_ok=True)
+    with open(traffic_path(workload), "w") as f:
+        f.write("\n".join(lines))
+    print(traffic_path(workload))
+
+
+def recorded_traffic(workload: str) -> dict:
+    """family -> scaled HBM bytes per launch, for kernels unchanged since the counters."""
+    out = {}
+    try:
+        with open(traffic_path(workload)) as f:
+            text = f.read()
+    except OSError:
+        return out
+    if "```traffic" not in text:
+        return out
+    block = text.split("```traffic", 1)[1].split("```", 1)[0]
+    for line in block.strip().splitlines():
+        parts = dict(p.split("=", 1) for p in line.split()[1:])
+        fname, h = parts["source"].split(":")
+        if source_hash(fname) == h:
+            out[line.split()[0]] = float(parts["bytes"])
+    return out
 
 
 def make_gradients(wl, steps: int, device):
@@ -131,6 +229,11 @@ def main():
                     help="Householder QR schedule (default: chosen by the library from the batch size)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--summarize-traffic", metavar="OUTDIR", default=None,
+                    help="write profiles/traffic_<config>.md from the rocprofv3 --pmc runs under OUTDIR")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -138,7 +241,22 @@ def main():
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
+    if args.summarize_traffic:
+        summarize_traffic(args.config, args.summarize_traffic)
+        return
+
     import torch
+
+    if args.copy_calibration:
+        n = (1 << 30) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                          "launches": 5}), flush=True)
+        return
 
     from bit_quantized_shampoo_amd import Shampoo4Blocks, Shampoo4Config
     from workloads import cost, get_workload
@@ -194,11 +312,14 @@ def main():
             log(f"[bench] {name:12s} launches {r['launches']:6d}  {r['ms'] / steps:9.3f} ms/step  "
                 f"{r['flops'] / max(r['ms'], 1e-9) / 1e9:8.2f} TFLOP/s  "
                 f"{r['bytes'] / max(r['ms'], 1e-9) / 1e6:8.1f} GB/s")
-    g = {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0}
+    fam = {"gemm": {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0}}
     for name, r in rep.items():
         if name.startswith("gemm"):
-            for k in g:
-                g[k] += r[k]
+            for k in fam["gemm"]:
+                fam["gemm"][k] += r[k]
+        elif name in ("qr_panel", "quant", "dequant"):
+            fam[name] = dict(r)
+    g = fam["gemm"]
     gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12 if g["ms"] > 0 else 0.0
     q = rep["quant"]
     quant_gbps = q["bytes"] / (q["ms"] * 1e-3) / 1e9 if q["ms"] > 0 else 0.0
@@ -206,17 +327,36 @@ def main():
     dequant_gbps = dq["bytes"] / (dq["ms"] * 1e-3) / 1e9 if dq["ms"] > 0 else 0.0
     step_flops = sum(cost.block_step_flops(m, n, wl.bjorck_iters, wl.root_interval, wl.power_iters,
                                            cached_root=cfg.root_cache) for m, n in wl.shapes)
-    roofline = {
-        "bound": "mfma",
-        "kernel": "gemm_kernel (fp32 v_mfma_f32_32x32x2_f32, all matrix products of the step)",
-        "achieved": round(gemm_tflops, 3),
-        "peak": PEAK_FP32_MFMA_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(gemm_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
-        "traffic": None,
-        "launches_per_step": g["launches"] / steps,
-        "avg_launch_us": round(g["ms"] * 1e3 / max(g["launches"], 1), 3),
+    traffic = recorded_traffic(wl.name)
+    kernels = {
+        "gemm": ("mfma", "gemm_kernel (fp32 v_mfma_f32_32x32x2_f32): every matrix product of the step; "
+                 "algorithmic flops = 2 M N K of the products each launch is given"),
+        "qr_panel": ("alu", "panel_*_kernel: Householder factorization of one 32-column panel per workgroup "
+                     "(one workgroup per side: a dependent chain of reflector steps, latency-bound)"),
+        "quant": ("hbm", "quant_kernel: 4.5625 B per element (fp32 in, nibble + 1/16 scale out)"),
+        "dequant": ("hbm", "dequant_kernel: 4.5625 B per element (nibble + scale in, fp32 out)"),
     }
+    rooflines = {}
+    for name, (bound, desc) in kernels.items():
+        r = fam.get(name)
+        if not r or not r["launches"] or r["ms"] <= 0:
+            continue
+        per_launch_s = r["ms"] * 1e-3 / r["launches"]
+        if bound == "hbm":
+            achieved, peak, unit = r["bytes"] / r["launches"] / per_launch_s / 1e9, PEAK_HBM_GBPS, "GB/s"
+        else:
+            achieved = r["flops"] / r["launches"] / per_launch_s / 1e12
+            peak, unit = (PEAK_FP32_MFMA_TFLOPS if bound == "mfma" else PEAK_FP32_VALU_TFLOPS), "TFLOP/s"
+        rooflines[name] = {
+            "bound": bound, "kernel": desc, "achieved": round(achieved, 4), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 6),
+            "traffic": round(traffic[name]) if name in traffic else None,
+            "algorithmic_bytes_per_launch": round(r["bytes"] / r["launches"]),
+            "launches_per_step": r["launches"] / steps, "avg_launch_us": round(per_launch_s * 1e6, 3),
+            "ms_per_step": round(r["ms"] / steps, 4),
+        }
+    dominant = max(rooflines, key=lambda k: rooflines[k]["ms_per_step"])
+    roofline = dict(rooflines[dominant], family=dominant)
     result = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -245,6 +385,7 @@ def main():
         "dequant_gbps": round(dequant_gbps, 1),
         "algorithmic_tflops_per_step": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
         "roofline": roofline,
+        "rooflines": rooflines,
         "kernel_ms_per_step": {k: round(v["ms"] / steps, 4) for k, v in rep.items() if v["launches"]},
         "cpu_baseline": None,
     }

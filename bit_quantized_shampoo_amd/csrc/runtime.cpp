@@ -376,8 +376,20 @@ struct shampoo4_ctx_s {
             L.mode = b == 0 ? 0 : (1 << b);
             L.max_h = maxh[b];
             L.ntiles = (int)byc[b].size();
+            for (const auto& pd : byc[b]) {
+                L.flops += panel_flops(pd.h, pd.nb);
+                L.bytes += 4.0 * (double)pd.h * pd.nb * 3;   // read the panel, write V and Y
+            }
             st.push_back(L);
         }
+    }
+    // Algorithmic flops of one h x nb panel: for reflector j the column dots over rows
+    // j.. of columns j.. (2 (h-j)(nb-j)) and the update of columns j+1.. (2 (h-j)(nb-j-1)),
+    // the triangular factor T (nb^3 / 3) and Y = V T with triangular T (h nb^2).
+    static double panel_flops(int h, int nb) {
+        double f = (double)nb * nb * nb / 3.0 + (double)h * nb * nb;
+        for (int j = 0; j < nb; ++j) f += 2.0 * (h - j) * (2.0 * (nb - j) - 1.0);
+        return f;
     }
     static Launch sync_op(Kind k, int strm, int ev) {
         Launch L;
