@@ -41,6 +41,7 @@ FAMILIES = {
     "qr_panel": (lambda n: "panel_" in n and "_kernel" in n, "qr.hip"),
     "quant": (lambda n: "quant_kernel" in n and "dequant" not in n, "codec.hip"),
     "dequant": (lambda n: "dequant_kernel" in n, "codec.hip"),
+    "graft": (lambda n: "graft_" in n and "_kernel" in n, "graft.hip"),
 }
 CSRC = os.path.join(ROOT, "bit_quantized_shampoo_amd", "csrc")
 
@@ -225,6 +226,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-root-cache", action="store_true")
+    ap.add_argument("--graft", default="none", choices=["none", "sgd", "adam"],
+                    help="add the grafted weight update after the preconditioner to every step")
     ap.add_argument("--qr", default="auto", choices=["auto", "blocked", "lookahead"],
                     help="Householder QR schedule (default: chosen by the library from the batch size)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -275,8 +278,18 @@ def main():
     outs = [torch.empty((m, n), dtype=torch.float32, device=dev) for m, n in wl.shapes]
     stream = torch.cuda.current_stream()
 
+    if args.graft != "none":
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1)
+        weights = [torch.randn((m, n), device=dev, generator=gen) for m, n in wl.shapes]
+        moments = ([(torch.zeros((m, n), device=dev), torch.zeros((m, n), device=dev)) for m, n in wl.shapes]
+                   if args.graft == "adam" else None)
+
     def run(t):
-        blocks.step(grads[(t - 1) % distinct], t, wl.root_interval, outs=outs)
+        G = grads[(t - 1) % distinct]
+        blocks.step(G, t, wl.root_interval, outs=outs)
+        if args.graft != "none":
+            blocks.graft(G, outs, weights, moments, mode=args.graft, lr=1e-3, step=t)
 
     t = 0
     for _ in range(warmup):
@@ -317,7 +330,7 @@ def main():
         if name.startswith("gemm"):
             for k in fam["gemm"]:
                 fam["gemm"][k] += r[k]
-        elif name in ("qr_panel", "quant", "dequant"):
+        elif name in ("qr_panel", "quant", "dequant", "graft"):
             fam[name] = dict(r)
     g = fam["gemm"]
     gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12 if g["ms"] > 0 else 0.0
@@ -335,6 +348,8 @@ def main():
                      "(one workgroup per side: a dependent chain of reflector steps, latency-bound)"),
         "quant": ("hbm", "quant_kernel: 4.5625 B per element (fp32 in, nibble + 1/16 scale out)"),
         "dequant": ("hbm", "dequant_kernel: 4.5625 B per element (nibble + scale in, fp32 out)"),
+        "graft": ("hbm", "graft_norms_kernel + graft_apply_kernel: per element G and P read (Adam: moments "
+                  "read and written) for the block norms, then P and W read and W written"),
     }
     rooflines = {}
     for name, (bound, desc) in kernels.items():
@@ -377,6 +392,7 @@ def main():
             "beta": wl.beta, "eps": wl.eps, "qblock": wl.qblock,
             "bjorck_iters": wl.bjorck_iters, "power_iters": wl.power_iters,
             "root_interval": wl.root_interval, "root_cache": cfg.root_cache, "qr_schedule": args.qr,
+            "graft": args.graft,
         },
         "gemm_tflops": round(gemm_tflops, 3),
         "gemm_frac_mfma_peak": round(gemm_tflops / PEAK_FP32_MFMA_TFLOPS, 4),

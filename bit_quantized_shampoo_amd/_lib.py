@@ -25,8 +25,10 @@ EXPORTED = [
     "shampoo4_update_stats", "shampoo4_refresh_root", "shampoo4_precondition",
     "shampoo4_check", "shampoo4_destroy", "shampoo4_layout", "shampoo4_quantize",
     "shampoo4_dequantize", "shampoo4_codebook", "shampoo4_gemm_workspace_bytes",
-    "shampoo4_gemm_batched", "shampoo4_timing", "shampoo4_timing_report",
+    "shampoo4_gemm_batched", "shampoo4_timing", "shampoo4_timing_report", "shampoo4_graft",
 ]
+
+GRAFT_SGD, GRAFT_ADAM = 0, 1
 
 
 class Config(ctypes.Structure):
@@ -42,6 +44,17 @@ class Shape(ctypes.Structure):
 class Io(ctypes.Structure):
     _fields_ = [("G", ctypes.c_void_p), ("ldg", ctypes.c_int64),
                 ("P", ctypes.c_void_p), ("ldp", ctypes.c_int64)]
+
+
+class GraftConfig(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("step", ctypes.c_int32), ("lr", ctypes.c_float),
+                ("eps_graft", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps_adam", ctypes.c_float)]
+
+
+class GraftIo(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("ldw", ctypes.c_int64), ("M", ctypes.c_void_p),
+                ("V", ctypes.c_void_p)]
 
 
 class Shampoo4Error(RuntimeError):
@@ -86,6 +99,7 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(i64), ctypes.POINTER(vp), ctypes.POINTER(i64),
                                        vp, sz, vp]),
         "shampoo4_timing": (st, [vp, i32]),
+        "shampoo4_graft": (st, [vp, ctypes.POINTER(Io), ctypes.POINTER(GraftIo), ctypes.POINTER(GraftConfig), vp]),
         "shampoo4_timing_report": (st, [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_char_p),
                                         ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),

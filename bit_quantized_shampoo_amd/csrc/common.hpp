@@ -113,6 +113,24 @@ struct PanelDesc {
 };
 static_assert(sizeof(PanelDesc) == 64, "PanelDesc layout");
 
+// One block of the grafting epilogue: rows of G, P (io table entry `blk`) and of W, M, V
+// (graft io table entry `blk`) in tiles of `rows` rows; `parts` receives two partial
+// sums per tile (||d_graft||^2 and ||P||^2 over the tile).
+struct GraftDesc {
+    float* parts;
+    int32_t m, n, rows, blk;
+    int32_t ntiles, pad0;
+};
+static_assert(sizeof(GraftDesc) == 32, "GraftDesc layout");
+
+// Per-call entry of the graft io table (same layout as shampoo4_graft_io).
+struct GraftIo {
+    float* W;
+    int64_t ldw;
+    float* M;
+    float* V;
+};
+
 // Column / vector work item for the small elementwise kernels.
 struct VecDesc {
     const float* a;           // e.g. Q

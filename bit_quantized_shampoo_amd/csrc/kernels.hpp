@@ -66,4 +66,18 @@ hipError_t launch_root_scaling(const VecDesc* descs, const int* prefix, int ndes
 hipError_t launch_identity_state(const InitDesc* descs, const int* prefix, int ndesc, int ntiles,
                                  hipStream_t stream);
 
+// Grafting epilogue: two launches over the same row tiles of every block.
+constexpr int GRAFT_TILE = 4096;             // elements per workgroup (at least one row)
+constexpr int graft_rows(int n) { return n >= GRAFT_TILE ? 1 : GRAFT_TILE / n; }
+struct GraftParams {
+    int mode;                                // 0 SGD, 1 Adam
+    float lr, eps_graft, beta1, beta2, eps_adam;
+    float c1, c2;                            // Adam bias corrections 1 - beta^t
+};
+hipError_t launch_graft_norms(const GraftDesc* descs, const int* prefix, int ndesc, int ntiles,
+                              const IoEntry* io, const GraftIo* gio, GraftParams prm, uint32_t* flag,
+                              hipStream_t stream);
+hipError_t launch_graft_apply(const GraftDesc* descs, const int* prefix, int ndesc, int ntiles,
+                              const IoEntry* io, const GraftIo* gio, GraftParams prm, hipStream_t stream);
+
 }  // namespace s4

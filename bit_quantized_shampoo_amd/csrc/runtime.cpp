@@ -24,6 +24,9 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kRing = 8;            // pinned io staging slots
+static_assert(sizeof(IoEntry) == sizeof(shampoo4_io) && sizeof(GraftIo) == sizeof(shampoo4_graft_io) &&
+                  sizeof(GraftIo) == sizeof(IoEntry),
+              "per-call tables share the staging slots");
 constexpr int kPanel = 32;          // Householder panel width
 constexpr int kOuter = 128;         // columns whose reflectors update the trailing matrix together
 constexpr int kMaxSplit = GEMM_MAX_SLABS;   // split-K chunks of the skinny QR products
@@ -34,14 +37,14 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 // Timing families: the matrix products are split by the stage they serve.
 enum Family {
     FAM_GEMM_BJORCK = 0, FAM_GEMM_STATS, FAM_GEMM_POWER, FAM_GEMM_QR, FAM_GEMM_RAYLEIGH,
-    FAM_GEMM_PRECOND, FAM_DEQUANT, FAM_QUANT, FAM_PANEL, FAM_RAYLEIGH, FAM_ELEMENTWISE, FAM_N
+    FAM_GEMM_PRECOND, FAM_DEQUANT, FAM_QUANT, FAM_PANEL, FAM_RAYLEIGH, FAM_ELEMENTWISE, FAM_GRAFT, FAM_N
 };
 const char* kFamilyNames[FAM_N] = {"gemm_bjorck", "gemm_stats", "gemm_power", "gemm_qr", "gemm_rayleigh",
                                    "gemm_precond", "dequant", "quant", "qr_panel", "rayleigh",
-                                   "elementwise"};
+                                   "elementwise", "graft"};
 
 enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT,
-            K_RECORD, K_WAIT };
+            K_RECORD, K_WAIT, K_GRAFT_NORMS, K_GRAFT_APPLY };
 
 struct Launch {
     Kind kind = K_GEMM;
@@ -87,7 +90,7 @@ struct shampoo4_ctx_s {
     size_t st_bytes = 0, ws_bytes = 0;
     std::vector<Side> sides;             // 2 per block: L then R
     std::vector<size_t> X1, X2;          // per block precondition temporaries
-    size_t io_off = 0, flag_off = 0, desc_base = 0;
+    size_t io_off = 0, gio_off = 0, flag_off = 0, parts_off = 0, desc_base = 0;
     std::vector<uint8_t> blob;           // descriptor region contents
     size_t lds_limit = 0;                // bytes of LDS one workgroup may use
     int max_panels = 0;
@@ -104,6 +107,8 @@ struct shampoo4_ctx_s {
     std::vector<hipEvent_t> sync_ev;
     Seq qinit, sign, ray_gemm, rayleigh, quant, root_d, root_copy;
     Seq pre[4];
+    Seq graft_seq[2];                    // per graft mode (bytes differ): norms, apply
+    GraftParams graft_prm{};
 
     bool root_v_valid = false;        // workspace Vr holds Bjorck(dequant(root codes))
     bool root_v_is_stats = false;     // ... and the root codes equal the current codes
@@ -209,7 +214,8 @@ struct shampoo4_ctx_s {
         Launch L;
         L.kind = kind;
         L.fam = kind == K_DEQUANT ? FAM_DEQUANT : kind == K_QUANT ? FAM_QUANT : kind == K_PANEL ? FAM_PANEL
-              : kind == K_RAYLEIGH ? FAM_RAYLEIGH : FAM_ELEMENTWISE;
+              : kind == K_RAYLEIGH ? FAM_RAYLEIGH
+              : (kind == K_GRAFT_NORMS || kind == K_GRAFT_APPLY) ? FAM_GRAFT : FAM_ELEMENTWISE;
         std::vector<int> prefix;
         int total = 0;
         for (int t : tiles) {
@@ -241,7 +247,13 @@ struct shampoo4_ctx_s {
         auto st_take = [&](size_t b) { size_t o = so; so += align_up(b ? b : 1); return o; };
         auto ws_take = [&](size_t b) { size_t o = wo; wo += align_up(b ? b : 1); return o; };
         io_off = ws_take((size_t)nb * sizeof(IoEntry));
+        gio_off = ws_take((size_t)nb * sizeof(GraftIo));
         flag_off = ws_take(sizeof(uint32_t) * 4);
+        {   // grafting partials: two floats per row tile of every block
+            size_t tiles = 0;
+            for (auto& sh : shapes) tiles += (sh.m + graft_rows(sh.n) - 1) / graft_rows(sh.n);
+            parts_off = ws_take(tiles * 2 * sizeof(float));
+        }
         X1.resize(nb);
         X2.resize(nb);
         for (int b = 0; b < nb; ++b) {
@@ -751,6 +763,37 @@ struct shampoo4_ctx_s {
         }
     }
 
+    // grafting epilogue: the same row tiles for both passes; bytes per element depend on
+    // the mode (SGD: G, P read; Adam: also both moments read and written)
+    void build_graft() {
+        std::vector<GraftDesc> ds;
+        std::vector<int> tiles;
+        size_t t0 = 0;
+        for (int b = 0; b < nb; ++b) {
+            GraftDesc d;
+            std::memset(&d, 0, sizeof(d));
+            d.m = shapes[b].m;
+            d.n = shapes[b].n;
+            d.rows = graft_rows(d.n);
+            d.blk = b;
+            d.ntiles = (d.m + d.rows - 1) / d.rows;
+            d.parts = wsf(parts_off) + 2 * t0;
+            t0 += d.ntiles;
+            ds.push_back(d);
+            tiles.push_back(d.ntiles);
+        }
+        for (int mode = 0; mode < 2; ++mode) {
+            Launch a = make_items(K_GRAFT_NORMS, ds, tiles);
+            Launch u = make_items(K_GRAFT_APPLY, ds, tiles);
+            for (auto& sh : shapes) {
+                const double e = (double)sh.m * sh.n;
+                a.bytes += e * (mode ? 24.0 : 8.0);
+                u.bytes += e * 12.0;
+            }
+            graft_seq[mode] = {a, u};
+        }
+    }
+
     // ---- execution ------------------------------------------------------------
     hipError_t run(const Launch& L, hipStream_t caller) {
         const hipStream_t s = L.strm ? aux : caller;
@@ -811,6 +854,14 @@ struct shampoo4_ctx_s {
                 e = launch_identity_state(reinterpret_cast<const InitDesc*>(base + L.desc_off), prefix,
                                           L.ndesc, L.ntiles, s);
                 break;
+            case K_GRAFT_NORMS:
+                e = launch_graft_norms(reinterpret_cast<const GraftDesc*>(base + L.desc_off), prefix, L.ndesc,
+                                       L.ntiles, io, wsp<GraftIo>(gio_off), graft_prm, flag, s);
+                break;
+            case K_GRAFT_APPLY:
+                e = launch_graft_apply(reinterpret_cast<const GraftDesc*>(base + L.desc_off), prefix, L.ndesc,
+                                       L.ntiles, io, wsp<GraftIo>(gio_off), graft_prm, s);
+                break;
             case K_RECORD:
             case K_WAIT:
                 break;
@@ -847,6 +898,14 @@ struct shampoo4_ctx_s {
     }
 
     hipError_t upload_io(const shampoo4_io* io, hipStream_t s) {
+        io_vec = true;
+        for (int b = 0; b < nb; ++b)
+            io_vec = io_vec && (reinterpret_cast<uintptr_t>(io[b].G) & 15) == 0 && (io[b].ldg & 3) == 0;
+        return upload_table(io, io_off, s);
+    }
+
+    // One per-call table (nb entries of 32 bytes) through a pinned staging slot.
+    hipError_t upload_table(const void* table, size_t dev_off, hipStream_t s) {
         const size_t bytes = (size_t)nb * sizeof(IoEntry);
         const int slot = ring_next;
         ring_next = (ring_next + 1) % kRing;
@@ -855,11 +914,8 @@ struct shampoo4_ctx_s {
             if (e != hipSuccess) return e;
         }
         uint8_t* dst = pinned + (size_t)slot * align_up(bytes);
-        std::memcpy(dst, io, bytes);
-        io_vec = true;
-        for (int b = 0; b < nb; ++b)
-            io_vec = io_vec && (reinterpret_cast<uintptr_t>(io[b].G) & 15) == 0 && (io[b].ldg & 3) == 0;
-        hipError_t e = hipMemcpyAsync(ws + io_off, dst, bytes, hipMemcpyHostToDevice, s);
+        std::memcpy(dst, table, bytes);
+        hipError_t e = hipMemcpyAsync(ws + dev_off, dst, bytes, hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return e;
         ring_used[slot] = true;
         return hipEventRecord(ring_ev[slot], s);
@@ -951,6 +1007,7 @@ shampoo4_status shampoo4_plan(const shampoo4_config* cfg, int32_t nblocks, const
     if (!state_bytes || !workspace_bytes) return SHAMPOO4_EINVAL;
     auto c = make_plan(cfg, nblocks, shapes);
     c->build();   // null bases: only the sizes matter
+    c->build_graft();
     *state_bytes = c->st_bytes;
     // slack: the panel launches are regrouped at init by the device's LDS limit
     *workspace_bytes = c->desc_base + align_up(c->blob.size()) + (size_t)c->max_panels * 8 * kAlign;
@@ -977,6 +1034,7 @@ shampoo4_status shampoo4_init(const shampoo4_config* cfg, int32_t nblocks, const
     c->st = static_cast<uint8_t*>(state);
     c->ws = static_cast<uint8_t*>(workspace);
     c->build();
+    c->build_graft();
     if (c->n_sync > 0) {   // second stream (default priority) and its synchronization events
         if (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess) return SHAMPOO4_EHIP;
         c->sync_ev.assign(c->n_sync, nullptr);
@@ -1070,6 +1128,41 @@ shampoo4_status shampoo4_precondition(shampoo4_ctx c, const shampoo4_io* io, voi
         c->root_v_is_stats = false;
     }
     for (int i = 0; i < 4 && e == hipSuccess; ++i) e = c->run(c->pre[i], s);
+    return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+}
+
+shampoo4_status shampoo4_graft(shampoo4_ctx c, const shampoo4_io* io, const shampoo4_graft_io* gio,
+                               const shampoo4_graft_config* cfg, void* stream) {
+    if (!c || !gio || !cfg) return SHAMPOO4_EINVAL;
+    shampoo4_status st = validate_io(c, io, true);
+    if (st != SHAMPOO4_OK) return st;
+    if (cfg->mode != SHAMPOO4_GRAFT_SGD && cfg->mode != SHAMPOO4_GRAFT_ADAM) return SHAMPOO4_EINVAL;
+    if (!std::isfinite(cfg->lr) || !(cfg->eps_graft >= 0.f) || !std::isfinite(cfg->eps_graft))
+        return SHAMPOO4_EINVAL;
+    const bool adam = cfg->mode == SHAMPOO4_GRAFT_ADAM;
+    if (adam && (cfg->step < 1 || !(cfg->beta1 >= 0.f && cfg->beta1 < 1.f) ||
+                 !(cfg->beta2 >= 0.f && cfg->beta2 < 1.f) || !(cfg->eps_adam >= 0.f) ||
+                 !std::isfinite(cfg->eps_adam)))
+        return SHAMPOO4_EINVAL;
+    for (int b = 0; b < c->nb; ++b) {
+        if (!gio[b].W || (adam && (!gio[b].M || !gio[b].V))) return SHAMPOO4_EINVAL;
+        if (gio[b].ldw < c->shapes[b].n) return SHAMPOO4_ESHAPE;
+    }
+    GraftParams prm{};
+    prm.mode = adam ? 1 : 0;
+    prm.lr = cfg->lr;
+    prm.eps_graft = cfg->eps_graft;
+    prm.beta1 = cfg->beta1;
+    prm.beta2 = cfg->beta2;
+    prm.eps_adam = cfg->eps_adam;
+    prm.c1 = adam ? (float)(1.0 - std::pow((double)cfg->beta1, (double)cfg->step)) : 1.f;
+    prm.c2 = adam ? (float)(1.0 - std::pow((double)cfg->beta2, (double)cfg->step)) : 1.f;
+    if (adam && !(prm.c1 > 0.f && prm.c2 > 0.f)) return SHAMPOO4_EINVAL;
+    c->graft_prm = prm;
+    hipStream_t s = as_stream(stream);
+    if (c->upload_io(io, s) != hipSuccess) return SHAMPOO4_EHIP;
+    if (c->upload_table(gio, c->gio_off, s) != hipSuccess) return SHAMPOO4_EHIP;
+    const hipError_t e = c->run(c->graft_seq[prm.mode], s);
     return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
 

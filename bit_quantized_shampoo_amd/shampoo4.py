@@ -141,6 +141,40 @@ class Shampoo4Blocks:
             self.refresh_root(stream)
         return self.precondition(grads, outs, stream)
 
+    def graft(self, grads, directions, weights, moments=None, *, mode: str = "sgd", lr: float = 1.0,
+              eps_graft: float = 1e-8, step: int = 1, beta1: float = 0.9, beta2: float = 0.999,
+              eps_adam: float = 1e-8, stream=None):
+        """Grafted weight update W <- W - lr ||d_graft|| / (||P|| + eps_graft) P per block, in
+        place on `weights`; `directions` are the preconditioned P.  mode "adam" needs
+        `moments` = [(M, V), ...] (contiguous fp32, updated in place)."""
+        if mode not in ("sgd", "adam"):
+            raise ValueError(f"mode must be sgd or adam, not {mode!r}")
+        adam = mode == "adam"
+        if adam and moments is None:
+            raise ValueError("mode adam needs moments=[(M, V), ...]")
+        io = self._io(grads, directions)
+        gio = (L.GraftIo * len(self.shapes))()
+        for b, (m, n) in enumerate(self.shapes):
+            W = weights[b]
+            _require_gpu_tensor(W, torch.float32, "W")
+            if tuple(W.shape) != (m, n) or (W.stride(1) != 1 and n > 1):
+                raise ValueError(f"W must be a row-major {(m, n)} tensor")
+            gio[b].W = _ptr(W)
+            gio[b].ldw = max(W.stride(0), n) if m > 1 else n
+            if adam:
+                Mt, Vt = moments[b]
+                for t_, nm in ((Mt, "M"), (Vt, "V")):
+                    _require_gpu_tensor(t_, torch.float32, nm)
+                    if tuple(t_.shape) != (m, n) or not t_.is_contiguous():
+                        raise ValueError(f"{nm} must be a contiguous {(m, n)} tensor")
+                gio[b].M = _ptr(Mt)
+                gio[b].V = _ptr(Vt)
+        cfg = L.GraftConfig(L.GRAFT_ADAM if adam else L.GRAFT_SGD, int(step), float(lr), float(eps_graft),
+                            float(beta1), float(beta2), float(eps_adam))
+        L.check(L.lib().shampoo4_graft(self._ctx, io, gio, ctypes.byref(cfg), _stream_ptr(stream)),
+                "shampoo4_graft")
+        return weights
+
     def check(self, stream=None) -> int:
         flags = ctypes.c_uint32(0)
         st = L.lib().shampoo4_check(self._ctx, _stream_ptr(stream), ctypes.byref(flags))

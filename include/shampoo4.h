@@ -161,6 +161,42 @@ SHAMPOO4_API shampoo4_status shampoo4_refresh_root(shampoo4_ctx ctx, void* strea
 /* Preconditioned direction of every block into io[b].P. */
 SHAMPOO4_API shampoo4_status shampoo4_precondition(shampoo4_ctx ctx, const shampoo4_io* io, void* stream);
 
+/* Grafting and the weight update ("Shampoo -- Second-Order Optimizer", section
+ * "Grafting: borrow a step size that already works"): per block,
+ *     W <- W - lr * ||d_graft||_F / (||P||_F + eps_graft) * P
+ * with P = io[b].P the preconditioned direction (as written by shampoo4_precondition)
+ * and d_graft the step of the grafted method on G = io[b].G:
+ *   SHAMPOO4_GRAFT_SGD   d_graft = G;
+ *   SHAMPOO4_GRAFT_ADAM  m <- beta1 m + (1 - beta1) G, v <- beta2 v + (1 - beta2) G^2
+ *                        (elementwise, moments updated in place),
+ *                        d_graft = (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps_adam).
+ * Norms are block Frobenius norms, reduced in a fixed order (deterministic). */
+#define SHAMPOO4_GRAFT_SGD 0
+#define SHAMPOO4_GRAFT_ADAM 1
+
+typedef struct {
+    int32_t mode;             /* SHAMPOO4_GRAFT_* */
+    int32_t step;             /* Adam's step t >= 1 for the bias correction (SGD: ignored) */
+    float lr;                 /* eta, finite */
+    float eps_graft;          /* >= 0 */
+    float beta1, beta2;       /* Adam moment factors in [0, 1) */
+    float eps_adam;           /* >= 0 */
+} shampoo4_graft_config;
+
+typedef struct {
+    float* W;                 /* device, [m, n] weights of the block, row-major, updated in place */
+    int64_t ldw;              /* >= n */
+    float* M;                 /* device, [m, n] Adam first moment, contiguous (ld n); SGD: unused */
+    float* V;                 /* device, [m, n] Adam second moment, contiguous; SGD: unused */
+} shampoo4_graft_io;
+
+/* io: G/ldg and P/ldp of every block (read only); gio: nblocks entries.  Two kernels on
+ * `stream` (block norms with the Adam moment update, then the scaled update of W).
+ * EINVAL: null arguments, a bad mode, a non-finite lr or eps out of range; ESHAPE:
+ * ldw < n. */
+SHAMPOO4_API shampoo4_status shampoo4_graft(shampoo4_ctx ctx, const shampoo4_io* io, const shampoo4_graft_io* gio,
+                                            const shampoo4_graft_config* cfg, void* stream);
+
 /* Wait for `stream`, then report and clear the device non-finite flag
  * (raised when a quantized block or an eigenvalue is NaN/Inf).  *device_flags
  * (may be NULL) receives the raw flag word.  Returns SHAMPOO4_ENONFINITE if set. */
@@ -212,7 +248,7 @@ SHAMPOO4_API shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA
  * device and returns, per kernel family, the number of launches, total milliseconds,
  * and algorithmic flops and bytes.  names: "gemm_bjorck", "gemm_stats", "gemm_power",
  * "gemm_qr", "gemm_rayleigh", "gemm_precond" (the matrix products by the stage they
- * serve), "dequant", "quant", "qr_panel", "rayleigh", "elementwise".  Host arrays of
+ * serve), "dequant", "quant", "qr_panel", "rayleigh", "elementwise", "graft".  Host arrays of
  * length *count (in: capacity, out: used). */
 SHAMPOO4_API shampoo4_status shampoo4_timing(shampoo4_ctx ctx, int32_t enable);
 SHAMPOO4_API shampoo4_status shampoo4_timing_report(shampoo4_ctx ctx, int32_t* count, const char** names,
