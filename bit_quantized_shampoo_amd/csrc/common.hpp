@@ -152,7 +152,8 @@ struct InitDesc {
     uint8_t* rcodes;
     float* rscales;
     float* d;
-    int32_t p, pad;
+    int32_t p;
+    int32_t fp32;             // U kept in float32: codes/rcodes hold p x p floats, no scales
 };
 static_assert(sizeof(InitDesc) == 56, "InitDesc layout");
 

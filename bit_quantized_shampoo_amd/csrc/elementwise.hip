@@ -81,7 +81,18 @@ __global__ __launch_bounds__(256) void identity_state_kernel(const InitDesc* __r
     const int64_t n = p * p;
     const int64_t nqb = (n + 63) / 64;
     const int64_t i = (int64_t)(blockIdx.x - prefix[item]) * 256 + threadIdx.x;
-    if (i < nqb) {
+    if (i < nqb && d.fp32) {   // float32 U = I: 64 elements per thread
+        float* u = reinterpret_cast<float*>(d.codes);
+        float* ru = reinterpret_cast<float*>(d.rcodes);
+        for (int e = 0; e < 64; ++e) {
+            const int64_t idx = i * 64 + e;
+            if (idx < n) {
+                const float v = (idx % (p + 1)) == 0 ? 1.f : 0.f;
+                u[idx] = v;
+                ru[idx] = v;
+            }
+        }
+    } else if (i < nqb) {
         bool any = false;
         uint32_t words[8];
 #pragma unroll
@@ -109,7 +120,50 @@ __global__ __launch_bounds__(256) void identity_state_kernel(const InitDesc* __r
     }
 }
 
+// out = a for n = ld floats (16-byte vectors, scalar tail); with a flag, non-finite
+// values raise it (the 32-bit state's stand-in for the quantizer's check)
+__global__ __launch_bounds__(256) void copyf_kernel(const VecDesc* __restrict__ descs,
+                                                    const int* __restrict__ prefix, int ndesc,
+                                                    uint32_t* __restrict__ flag) {
+    const int item = find_item(prefix, ndesc, blockIdx.x);
+    const VecDesc& d = descs[item];
+    const int64_t n = d.ld;
+    const int64_t base = (int64_t)(blockIdx.x - prefix[item]) * COPYF_TILE;
+    const bool vec = ((reinterpret_cast<uintptr_t>(d.a) | reinterpret_cast<uintptr_t>(d.out)) & 15) == 0;
+    bool finite = true;
+    if (vec) {
+        for (int64_t e = base + 4 * threadIdx.x; e < base + COPYF_TILE && e < n; e += 4 * 256) {
+            if (e + 4 <= n) {
+                const floatx4 v = ldg(reinterpret_cast<const floatx4*>(d.a + e));
+                stg(reinterpret_cast<floatx4*>(d.out + e), v);
+                finite = finite && __builtin_isfinite(v[0]) && __builtin_isfinite(v[1]) &&
+                         __builtin_isfinite(v[2]) && __builtin_isfinite(v[3]);
+            } else {
+                for (int64_t k = e; k < n; ++k) {
+                    const float v = ldg(d.a + k);
+                    stg(d.out + k, v);
+                    finite = finite && __builtin_isfinite(v);
+                }
+            }
+        }
+    } else {
+        for (int64_t e = base + threadIdx.x; e < base + COPYF_TILE && e < n; e += 256) {
+            const float v = ldg(d.a + e);
+            stg(d.out + e, v);
+            finite = finite && __builtin_isfinite(v);
+        }
+    }
+    if (!finite && flag) stg(flag, 1u);
+}
+
 }  // namespace
+
+hipError_t launch_copyf(const VecDesc* descs, const int* prefix, int ndesc, int ntiles, uint32_t* flag,
+                        hipStream_t stream) {
+    if (ntiles <= 0) return hipSuccess;
+    S4_LAUNCH(copyf_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc, flag);
+    return hipGetLastError();
+}
 
 hipError_t launch_root_scaling(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
                                float eps, uint32_t* flag, hipStream_t stream) {

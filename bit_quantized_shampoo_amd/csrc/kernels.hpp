@@ -65,6 +65,10 @@ hipError_t launch_root_scaling(const VecDesc* descs, const int* prefix, int ndes
                                float eps, uint32_t* flag, hipStream_t stream);
 hipError_t launch_identity_state(const InitDesc* descs, const int* prefix, int ndesc, int ntiles,
                                  hipStream_t stream);
+// out[0..n) = a[0..n) (n = desc.ld), 16-byte vectors; with a flag, non-finite values raise it
+constexpr int COPYF_TILE = 4096;             // elements per workgroup
+hipError_t launch_copyf(const VecDesc* descs, const int* prefix, int ndesc, int ntiles, uint32_t* flag,
+                        hipStream_t stream);
 
 // Grafting epilogue: two launches over the same row tiles of every block.
 constexpr int GRAFT_TILE = 4096;             // elements per workgroup (at least one row)

@@ -44,7 +44,7 @@ const char* kFamilyNames[FAM_N] = {"gemm_bjorck", "gemm_stats", "gemm_power", "g
                                    "elementwise", "graft"};
 
 enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT,
-            K_RECORD, K_WAIT, K_GRAFT_NORMS, K_GRAFT_APPLY };
+            K_RECORD, K_WAIT, K_GRAFT_NORMS, K_GRAFT_APPLY, K_COPYF };
 
 struct Launch {
     Kind kind = K_GEMM;
@@ -102,6 +102,7 @@ struct shampoo4_ctx_s {
     Seq qr_join;                          // second stream's work joined back (look-ahead plans)
     int outer = kOuter;                   // columns whose reflectors update the trailing matrix together
     bool lookahead = false;               // small batches: trailing and Q updates on a second stream
+    bool fp32_state = false;              // U kept in float32 (the 32-bit baseline), no codec
     int n_sync = 0;                       // synchronization events the plan uses
     hipStream_t aux = nullptr;
     std::vector<hipEvent_t> sync_ev;
@@ -232,6 +233,7 @@ struct shampoo4_ctx_s {
 
     // ---- plan ---------------------------------------------------------------------
     void layout() {
+        fp32_state = (cfg.flags & SHAMPOO4_FLAG_FP32_STATE) != 0;
         // Large batches are throughput-bound: reflectors go to the trailing matrix 128
         // columns at a time.  Small ones are bound by the chain of panels and by launch
         // latency: panel-wide updates on the caller's stream (or, on request, with the
@@ -263,11 +265,13 @@ struct shampoo4_ctx_s {
                 S.q = s == 0 ? shapes[b].n : shapes[b].m;
                 const int64_t p = S.p;
                 S.nqb = (p * p + 63) / 64;
-                S.codes = st_take(S.nqb * 32);
-                S.scales = st_take(S.nqb * 4);
+                const size_t ubytes = fp32_state ? (size_t)p * p * 4 : (size_t)S.nqb * 32;
+                const size_t sbytes = fp32_state ? 0 : (size_t)S.nqb * 4;
+                S.codes = st_take(ubytes);
+                S.scales = st_take(sbytes);
                 S.lam = st_take(p * 4);
-                S.rcodes = st_take(S.nqb * 32);
-                S.rscales = st_take(S.nqb * 4);
+                S.rcodes = st_take(ubytes);
+                S.rscales = st_take(sbytes);
                 S.d = st_take(p * 4);
                 const size_t mat = (size_t)p * p * 4;
                 S.Vs = ws_take(mat);
@@ -314,6 +318,16 @@ struct shampoo4_ctx_s {
     }
 
     // Bjorck chain for one family of buffers; the result lands in `fin`.
+    static VecDesc copyf_desc(const float* src, float* dst, int64_t n) {
+        VecDesc v;
+        std::memset(&v, 0, sizeof(v));
+        v.a = src;
+        v.out = dst;
+        v.ld = n;   // element count
+        return v;
+    }
+    static int copyf_tiles(int64_t n) { return (int)((n + COPYF_TILE - 1) / COPYF_TILE); }
+
     void build_bjorck(bool root, Seq& deq, std::vector<Seq>& iters) {
         const int k = cfg.bjorck_iters;
         std::vector<CodecDesc> cds;
@@ -330,9 +344,24 @@ struct shampoo4_ctx_s {
             cds.push_back(c);
             tiles.push_back((int)dequant_tiles(c.n));
         }
-        Launch L = make_items(K_DEQUANT, cds, tiles);
-        for (auto& S : sides) L.bytes += (double)S.p * S.p * (4.0 + 0.5 + 4.0 / 64);
-        deq = {L};
+        if (fp32_state) {   // 32-bit state: U is copied into the Bjorck chain's first buffer
+            std::vector<VecDesc> vd;
+            std::vector<int> vt;
+            for (auto& S : sides) {
+                const size_t fin = root ? S.Vr : S.Vs;
+                vd.push_back(copyf_desc(stf(root ? S.rcodes : S.codes), wsf((k % 2 == 1) ? S.Tmp : fin),
+                                        (int64_t)S.p * S.p));
+                vt.push_back(copyf_tiles(vd.back().ld));
+            }
+            Launch L = make_items(K_COPYF, vd, vt);
+            L.fam = FAM_DEQUANT;
+            for (auto& S : sides) L.bytes += (double)S.p * S.p * 8.0;
+            deq = {L};
+        } else {
+            Launch L = make_items(K_DEQUANT, cds, tiles);
+            for (auto& S : sides) L.bytes += (double)S.p * S.p * (4.0 + 0.5 + 4.0 / 64);
+            deq = {L};
+        }
         iters.clear();
         for (int i = 0; i < k; ++i) {
             std::vector<GemmItem> gram, upd;
@@ -731,10 +760,28 @@ struct shampoo4_ctx_s {
             }
             rayleigh = {make_items(K_RAYLEIGH, rr, trr)};
             root_d = {make_items(K_ROOT, rt, trt)};
-            Launch Lq = make_items(K_QUANT, qd, tq);
-            Lq.bytes = qbytes;
-            quant = {Lq};
-            root_copy = {make_items(K_COPY, cp, tcp)};
+            if (fp32_state) {
+                std::vector<VecDesc> qv, rv;
+                std::vector<int> qt;
+                for (auto& S : sides) {
+                    const int64_t n = (int64_t)S.p * S.p;
+                    qv.push_back(copyf_desc(wsf(S.Qm), stf(S.codes), n));
+                    rv.push_back(copyf_desc(stf(S.codes), stf(S.rcodes), n));
+                    qt.push_back(copyf_tiles(n));
+                }
+                Launch Lq = make_items(K_COPYF, qv, qt);
+                Lq.fam = FAM_QUANT;
+                Lq.mode = 1;   // check finiteness
+                for (auto& S : sides) Lq.bytes += (double)S.p * S.p * 8.0;
+                quant = {Lq};
+                root_copy = {make_items(K_COPYF, rv, qt)};
+                for (auto& d : in) d.fp32 = 1;
+            } else {
+                Launch Lq = make_items(K_QUANT, qd, tq);
+                Lq.bytes = qbytes;
+                quant = {Lq};
+                root_copy = {make_items(K_COPY, cp, tcp)};
+            }
             init_seq = {make_items(K_INIT, in, tin)};
         }
         // precondition: X1 = diag(d_L) V_L^T G; X2 = X1 V_R diag(d_R); X1 = V_L X2; P = X1 V_R^T
@@ -854,6 +901,10 @@ struct shampoo4_ctx_s {
                 e = launch_identity_state(reinterpret_cast<const InitDesc*>(base + L.desc_off), prefix,
                                           L.ndesc, L.ntiles, s);
                 break;
+            case K_COPYF:
+                e = launch_copyf(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix, L.ndesc, L.ntiles,
+                                 L.mode ? flag : nullptr, s);
+                break;
             case K_GRAFT_NORMS:
                 e = launch_graft_norms(reinterpret_cast<const GraftDesc*>(base + L.desc_off), prefix, L.ndesc,
                                        L.ntiles, io, wsp<GraftIo>(gio_off), graft_prm, flag, s);
@@ -939,7 +990,7 @@ shampoo4_status validate_cfg(const shampoo4_config* cfg) {
     if (cfg->bjorck_iters < 0 || cfg->bjorck_iters > 16) return SHAMPOO4_EINVAL;
     if (cfg->power_iters < 1 || cfg->power_iters > 8) return SHAMPOO4_EINVAL;
     if (cfg->flags & ~(SHAMPOO4_FLAG_ROOT_CACHE | SHAMPOO4_FLAG_KEEP_STATE | SHAMPOO4_FLAG_QR_BLOCKED |
-                       SHAMPOO4_FLAG_QR_LOOKAHEAD))
+                       SHAMPOO4_FLAG_QR_LOOKAHEAD | SHAMPOO4_FLAG_FP32_STATE))
         return SHAMPOO4_EINVAL;
     if ((cfg->flags & SHAMPOO4_FLAG_QR_BLOCKED) && (cfg->flags & SHAMPOO4_FLAG_QR_LOOKAHEAD))
         return SHAMPOO4_EINVAL;
@@ -1199,11 +1250,11 @@ shampoo4_status shampoo4_layout(shampoo4_ctx c, int32_t block, int32_t side, sha
     const size_t p = S.p;
     const size_t mat = p * p * 4;
     switch (which) {
-        case SHAMPOO4_BUF_CODES: *offset = S.codes; *bytes = S.nqb * 32; break;
-        case SHAMPOO4_BUF_SCALES: *offset = S.scales; *bytes = S.nqb * 4; break;
+        case SHAMPOO4_BUF_CODES: *offset = S.codes; *bytes = c->fp32_state ? (size_t)p * p * 4 : S.nqb * 32; break;
+        case SHAMPOO4_BUF_SCALES: *offset = S.scales; *bytes = c->fp32_state ? 0 : S.nqb * 4; break;
         case SHAMPOO4_BUF_EIG: *offset = S.lam; *bytes = p * 4; break;
-        case SHAMPOO4_BUF_ROOT_CODES: *offset = S.rcodes; *bytes = S.nqb * 32; break;
-        case SHAMPOO4_BUF_ROOT_SCALES: *offset = S.rscales; *bytes = S.nqb * 4; break;
+        case SHAMPOO4_BUF_ROOT_CODES: *offset = S.rcodes; *bytes = c->fp32_state ? (size_t)p * p * 4 : S.nqb * 32; break;
+        case SHAMPOO4_BUF_ROOT_SCALES: *offset = S.rscales; *bytes = c->fp32_state ? 0 : S.nqb * 4; break;
         case SHAMPOO4_BUF_ROOT_D: *offset = S.d; *bytes = p * 4; break;
         case SHAMPOO4_BUF_V: *offset = S.Vs; *bytes = mat; break;
         case SHAMPOO4_BUF_STAT: *offset = S.Lt; *bytes = mat; break;

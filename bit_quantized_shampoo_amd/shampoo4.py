@@ -56,12 +56,15 @@ class Shampoo4Config:
     power_iters: int = 1
     root_cache: bool = False
     qr_schedule: str = "auto"       # "auto", "blocked" or "lookahead"
+    fp32_state: bool = False        # keep U in float32 (the 32-bit baseline) instead of 4-bit codes
 
     def c(self, keep_state: bool = False) -> L.Config:
         flags = (L.FLAG_ROOT_CACHE if self.root_cache else 0) | (L.FLAG_KEEP_STATE if keep_state else 0)
         if self.qr_schedule not in ("auto", "blocked", "lookahead"):
             raise ValueError(f"qr_schedule must be auto, blocked or lookahead, not {self.qr_schedule!r}")
         flags |= {"auto": 0, "blocked": L.FLAG_QR_BLOCKED, "lookahead": L.FLAG_QR_LOOKAHEAD}[self.qr_schedule]
+        if self.fp32_state:
+            flags |= L.FLAG_FP32_STATE
         return L.Config(self.beta, self.eps, self.qblock, self.bjorck_iters, self.power_iters, flags)
 
 
@@ -200,6 +203,14 @@ class Shampoo4Blocks:
             p = self.shapes[block][side]
             return t.view(p, p)
         return t
+
+    def eigenvectors(self, block: int, side: int, root: bool = False) -> torch.Tensor:
+        """The float32 U of a side (only with fp32_state), p x p, a view into the state."""
+        if not self.config.fp32_state:
+            raise ValueError("eigenvectors() needs fp32_state; 4-bit states hold codes")
+        p = self.shapes[block][side]
+        raw = self.view(block, side, L.BUF_ROOT_CODES if root else L.BUF_CODES)
+        return raw.view(torch.float32).view(p, p)
 
     def side_state(self, block: int, side: int) -> dict:
         """Host copies of one side's state (codes, scales, lam, root codes/scales, d)."""

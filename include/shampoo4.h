@@ -88,6 +88,11 @@ typedef enum {
    Setting both is EINVAL. */
 #define SHAMPOO4_FLAG_QR_BLOCKED 4u
 #define SHAMPOO4_FLAG_QR_LOOKAHEAD 8u
+/* The 32-bit baseline the 4-bit method is measured against ("4-bit Shampoo ..." abstract:
+   performance comparable to the 32-bit counterpart): the eigenvector matrices U are kept
+   in float32 (state buffers CODES / ROOT_CODES hold p x p floats, SCALES / ROOT_SCALES are
+   empty) and every stage runs the same kernels with the codec replaced by copies. */
+#define SHAMPOO4_FLAG_FP32_STATE 16u
 
 typedef struct {
     int32_t m, n;             /* block shape: G is [m, n]; side L has order m, side R order n */

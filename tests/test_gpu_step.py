@@ -213,3 +213,79 @@ def test_nonfinite_flag():
     blk.update_stats([G])
     assert blk.check() != 0
     assert blk.check() == 0      # cleared by the previous check
+
+
+def _run_teacher_forced_fp32(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, root_interval=1,
+                             label="", qr="auto"):
+    """The 32-bit baseline (U kept in float32): same checks as the 4-bit path with the
+    codec replaced by the identity on float32 values, so the new U must equal the GPU's
+    own float32 Q bit for bit."""
+    from bit_quantized_shampoo_amd import Shampoo4Blocks, Shampoo4Config
+    cfg = Shampoo4Config(beta=beta, eps=eps, bjorck_iters=k, fp32_state=True, qr_schedule=qr)
+    announce(f"fp32 state {label}: init {shapes}")
+    blocks = Shampoo4Blocks(shapes, cfg)
+    torch.cuda.synchronize()
+    for b, (m, n) in enumerate(shapes):
+        for s, p in ((0, m), (1, n)):
+            assert np.array_equal(blocks.eigenvectors(b, s).cpu().numpy(), np.eye(p, dtype=np.float32))
+            assert np.array_equal(blocks.eigenvectors(b, s, root=True).cpu().numpy(), np.eye(p, dtype=np.float32))
+    for t in range(1, steps + 1):
+        Gs = grads_fn(t)
+        Gd = [to_dev(G) for G in Gs]
+        before = [[(blocks.eigenvectors(b, s).cpu().numpy(), blocks.side_state(b, s)["lam"]) for s in (0, 1)]
+                  for b in range(len(shapes))]
+        announce(f"fp32 state {label}: t={t} update_stats")
+        blocks.update_stats(Gd)
+        torch.cuda.synchronize()
+        for b, (m, n) in enumerate(shapes):
+            for s, p in ((0, m), (1, n)):
+                U0, lam0 = before[b][s]
+                V = o.bjorck(U0.astype(np.float64), k)
+                Lt_ref = o.statistics(V, lam0, o.side_gradient(Gs[b], s), beta)
+                Lt_gpu = blocks.view(b, s, 17).cpu().numpy().astype(np.float64)
+                assert rel_fro(Lt_gpu, Lt_ref) <= TOL, (label, t, b, s, "statistic")
+                Q_ref, lam_ref = o.eigen_refresh(Lt_gpu, V, 1)
+                Q32 = blocks.view(b, s, 18).cpu().numpy()
+                lam_gpu = blocks.side_state(b, s)["lam"].astype(np.float64)
+                Qg = Q32.astype(np.float64)
+                assert rel_fro((Qg * lam_gpu) @ Qg.T, (Q_ref * lam_ref) @ Q_ref.T) <= TOL, (label, t, b, s)
+                assert rel_fro(lam_gpu, lam_ref) <= TOL, (label, t, b, s, "eigenvalues")
+                assert np.array_equal(blocks.eigenvectors(b, s).cpu().numpy().view(np.uint32), Q32.view(np.uint32))
+        if t % root_interval == 0:
+            blocks.refresh_root()
+            torch.cuda.synchronize()
+            for b in range(len(shapes)):
+                for s in (0, 1):
+                    assert torch.equal(blocks.eigenvectors(b, s, root=True), blocks.eigenvectors(b, s))
+        announce(f"fp32 state {label}: t={t} precondition")
+        outs = blocks.precondition(Gd)
+        torch.cuda.synchronize()
+        for b, (m, n) in enumerate(shapes):
+            sl, sr = blocks.side_state(b, 0), blocks.side_state(b, 1)
+            VL = o.bjorck(blocks.eigenvectors(b, 0, root=True).cpu().numpy().astype(np.float64), k)
+            VR = o.bjorck(blocks.eigenvectors(b, 1, root=True).cpu().numpy().astype(np.float64), k)
+            P_ref = o.precondition_block(VL, sl["d"], VR, sr["d"], Gs[b])
+            assert rel_fro(outs[b].cpu().numpy(), P_ref) <= TOL, (label, t, b, "P")
+    assert blocks.check() == 0
+    blocks.close()
+
+
+@pytest.mark.parametrize("qr", ["auto", "blocked"])
+def test_fp32_state_ragged(qr):
+    require_gpu()
+    shapes = [(40, 72), (130, 65), (1, 3)]
+    rng = np.random.default_rng(21)
+    scales = [(10.0 ** rng.uniform(-1, 1, (m, 1))) * (10.0 ** rng.uniform(-1, 1, (1, n))) for m, n in shapes]
+
+    def grads(t):
+        r = np.random.default_rng([t, 99])
+        return [(r.standard_normal((m, n)) * sc).astype(np.float32) for (m, n), sc in zip(shapes, scales)]
+
+    _run_teacher_forced_fp32(shapes, grads, 3, root_interval=2, label=f"ragged qr={qr}", qr=qr)
+
+
+def test_fp32_state_single_1024():
+    require_gpu()
+    wl = get_workload("single_1024")
+    _run_teacher_forced_fp32(wl.shapes, wl.gradients, 3, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
+                             root_interval=1, label="single_1024")
