@@ -226,6 +226,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-root-cache", action="store_true")
+    ap.add_argument("--state", default="4bit", choices=["4bit", "fp32"],
+                    help="eigenvector storage: 4-bit codes (the method) or float32 (its 32-bit baseline)")
     ap.add_argument("--graft", default="none", choices=["none", "sgd", "adam"],
                     help="add the grafted weight update after the preconditioner to every step")
     ap.add_argument("--qr", default="auto", choices=["auto", "blocked", "lookahead"],
@@ -271,7 +273,8 @@ def main():
         raise RuntimeError("bench.py needs a GPU")
     dev = torch.device("cuda:0")
     cfg = Shampoo4Config(beta=wl.beta, eps=wl.eps, qblock=wl.qblock, bjorck_iters=wl.bjorck_iters,
-                         power_iters=wl.power_iters, root_cache=not args.no_root_cache, qr_schedule=args.qr)
+                         power_iters=wl.power_iters, root_cache=not args.no_root_cache, qr_schedule=args.qr,
+                         fp32_state=args.state == "fp32")
     log(f"[bench] workload {wl.name}: {len(wl.blocks)} blocks, steps {steps}, warmup {warmup}")
     grads, distinct, gen = make_gradients(wl, steps + warmup, dev)
     blocks = Shampoo4Blocks(wl.shapes, cfg, device=dev)
@@ -392,7 +395,7 @@ def main():
             "beta": wl.beta, "eps": wl.eps, "qblock": wl.qblock,
             "bjorck_iters": wl.bjorck_iters, "power_iters": wl.power_iters,
             "root_interval": wl.root_interval, "root_cache": cfg.root_cache, "qr_schedule": args.qr,
-            "graft": args.graft,
+            "graft": args.graft, "state": args.state,
         },
         "gemm_tflops": round(gemm_tflops, 3),
         "gemm_frac_mfma_peak": round(gemm_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
