@@ -228,6 +228,9 @@ def main():
     ap.add_argument("--no-root-cache", action="store_true")
     ap.add_argument("--state", default="4bit", choices=["4bit", "fp32"],
                     help="eigenvector storage: 4-bit codes (the method) or float32 (its 32-bit baseline)")
+    ap.add_argument("--newton", type=int, default=0, metavar="ITERS",
+                    help="also time the coupled Newton inverse 4th root (GEMM only) of every side's "
+                         "statistic with ITERS iterations (the unquantized baseline's root)")
     ap.add_argument("--graft", default="none", choices=["none", "sgd", "adam"],
                     help="add the grafted weight update after the preconditioner to every step")
     ap.add_argument("--qr", default="auto", choices=["auto", "blocked", "lookahead"],
@@ -408,6 +411,31 @@ def main():
         "kernel_ms_per_step": {k: round(v["ms"] / steps, 4) for k, v in rep.items() if v["launches"]},
         "cpu_baseline": None,
     }
+    if args.newton > 0:
+        from bit_quantized_shampoo_amd import inverse_root
+        stats = [blocks.view(b, s_, 17).clone() for b in range(len(wl.shapes)) for s_ in (0, 1)]
+        Xs, ws = inverse_root(stats, eps=wl.eps, iters=args.newton)
+        torch.cuda.synchronize()
+        reps = 3
+        n0 = torch.cuda.Event(enable_timing=True)
+        n1 = torch.cuda.Event(enable_timing=True)
+        n0.record(stream)
+        for _ in range(reps):
+            inverse_root(stats, eps=wl.eps, iters=args.newton, Xs=Xs, workspace=ws)
+        n1.record(stream)
+        torch.cuda.synchronize()
+        nms = n0.elapsed_time(n1) / reps
+        nflops = sum(4 * 2.0 * t.shape[0] ** 3 * args.newton for t in stats)
+        ach = nflops / (nms * 1e-3) / 1e12
+        rooflines["newton_root"] = {
+            "bound": "mfma", "kernel": "coupled Newton inverse 4th root: 4 products of order p per iteration on "
+            "gemm_kernel plus elementwise steps, all sides batched; timed as whole calls",
+            "achieved": round(ach, 4), "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 6), "traffic": None, "iters": args.newton,
+            "ms_per_call": round(nms, 4),
+        }
+        log(f"[bench] newton root ({args.newton} iters, {len(stats)} matrices): {nms:.3f} ms/call, {ach:.2f} TFLOP/s")
+        del stats, Xs, ws
     blocks.close()
     del grads
     if not args.no_cpu:

@@ -7,4 +7,4 @@ binding.  Build with ``python -m bit_quantized_shampoo_amd.build``.
 
 from ._lib import LIB_PATH, Shampoo4Error  # noqa: F401
 from .shampoo4 import (Shampoo4Blocks, Shampoo4Config, codebook, dequantize,  # noqa: F401
-                       gemm_batched, plan, quantize)
+                       gemm_batched, inverse_root, plan, quantize)

@@ -27,6 +27,7 @@ EXPORTED = [
     "shampoo4_check", "shampoo4_destroy", "shampoo4_layout", "shampoo4_quantize",
     "shampoo4_dequantize", "shampoo4_codebook", "shampoo4_gemm_workspace_bytes",
     "shampoo4_gemm_batched", "shampoo4_timing", "shampoo4_timing_report", "shampoo4_graft",
+    "shampoo4_inverse_root_workspace_bytes", "shampoo4_inverse_root",
 ]
 
 GRAFT_SGD, GRAFT_ADAM = 0, 1
@@ -100,6 +101,9 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(i64), ctypes.POINTER(vp), ctypes.POINTER(i64),
                                        vp, sz, vp]),
         "shampoo4_timing": (st, [vp, i32]),
+        "shampoo4_inverse_root_workspace_bytes": (sz, [i32, ctypes.POINTER(i32)]),
+        "shampoo4_inverse_root": (st, [i32, ctypes.POINTER(i32), ctypes.POINTER(vp), ctypes.POINTER(i64), f32, i32,
+                                       ctypes.POINTER(vp), ctypes.POINTER(i64), vp, sz, vp]),
         "shampoo4_graft": (st, [vp, ctypes.POINTER(Io), ctypes.POINTER(GraftIo), ctypes.POINTER(GraftConfig), vp]),
         "shampoo4_timing_report": (st, [vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_char_p),
                                         ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_double),

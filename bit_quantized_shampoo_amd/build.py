@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libshampoo4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["gemm.hip", "codec.hip", "qr.hip", "elementwise.hip", "graft.hip", "runtime.cpp"]
+SOURCES = ["gemm.hip", "codec.hip", "qr.hip", "elementwise.hip", "graft.hip", "newton.hip", "runtime.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

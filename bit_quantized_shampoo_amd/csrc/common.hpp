@@ -123,6 +123,23 @@ struct GraftDesc {
 };
 static_assert(sizeof(GraftDesc) == 32, "GraftDesc layout");
 
+// One matrix of the coupled Newton inverse root: the caller's input and output (with
+// their leading dimensions), the contiguous p x p source and destination of an
+// elementwise step, the identity target of the initial step, the per-row-tile partial
+// sums of the Frobenius norm and the matrix's scale slot.
+struct NewtonDesc {
+    const float* A;
+    float* out;
+    const float* src;
+    float* dst;
+    float* ident;
+    float* parts;
+    float* scale;
+    int64_t lda, ldo;
+    int32_t p, pad;
+};
+static_assert(sizeof(NewtonDesc) == 80, "NewtonDesc layout");
+
 // Per-call entry of the graft io table (same layout as shampoo4_graft_io).
 struct GraftIo {
     float* W;

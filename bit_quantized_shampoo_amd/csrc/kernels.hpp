@@ -70,6 +70,14 @@ constexpr int COPYF_TILE = 4096;             // elements per workgroup
 hipError_t launch_copyf(const VecDesc* descs, const int* prefix, int ndesc, int ntiles, uint32_t* flag,
                         hipStream_t stream);
 
+// Coupled Newton inverse 4th root: elementwise steps (row tiles of fill_rows(p) rows).
+hipError_t launch_newton_norm(const NewtonDesc* descs, const int* prefix, int ndesc, int ntiles, float eps,
+                              hipStream_t stream);
+hipError_t launch_newton_scale(const NewtonDesc* descs, int ndesc, hipStream_t stream);
+// mode 0: scaled damped input and identity; 1: F = 1.25 I - 0.25 M; 2: scaled result out
+hipError_t launch_newton_elem(const NewtonDesc* descs, const int* prefix, int ndesc, int ntiles, int mode,
+                              float eps, hipStream_t stream);
+
 // Grafting epilogue: two launches over the same row tiles of every block.
 constexpr int GRAFT_TILE = 4096;             // elements per workgroup (at least one row)
 constexpr int graft_rows(int n) { return n >= GRAFT_TILE ? 1 : GRAFT_TILE / n; }

@@ -44,7 +44,8 @@ const char* kFamilyNames[FAM_N] = {"gemm_bjorck", "gemm_stats", "gemm_power", "g
                                    "elementwise", "graft"};
 
 enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT,
-            K_RECORD, K_WAIT, K_GRAFT_NORMS, K_GRAFT_APPLY, K_COPYF };
+            K_RECORD, K_WAIT, K_GRAFT_NORMS, K_GRAFT_APPLY, K_COPYF, K_NEWTON_NORM, K_NEWTON_SCALE,
+            K_NEWTON_ELEM };
 
 struct Launch {
     Kind kind = K_GEMM;
@@ -110,6 +111,7 @@ struct shampoo4_ctx_s {
     Seq pre[4];
     Seq graft_seq[2];                    // per graft mode (bytes differ): norms, apply
     GraftParams graft_prm{};
+    float newton_eps = 0.f;              // damping of the coupled Newton inverse root (standalone call)
 
     bool root_v_valid = false;        // workspace Vr holds Bjorck(dequant(root codes))
     bool root_v_is_stats = false;     // ... and the root codes equal the current codes
@@ -901,6 +903,17 @@ struct shampoo4_ctx_s {
                 e = launch_identity_state(reinterpret_cast<const InitDesc*>(base + L.desc_off), prefix,
                                           L.ndesc, L.ntiles, s);
                 break;
+            case K_NEWTON_NORM:
+                e = launch_newton_norm(reinterpret_cast<const NewtonDesc*>(base + L.desc_off), prefix, L.ndesc,
+                                       L.ntiles, newton_eps, s);
+                break;
+            case K_NEWTON_SCALE:
+                e = launch_newton_scale(reinterpret_cast<const NewtonDesc*>(base + L.desc_off), L.ndesc, s);
+                break;
+            case K_NEWTON_ELEM:
+                e = launch_newton_elem(reinterpret_cast<const NewtonDesc*>(base + L.desc_off), prefix, L.ndesc,
+                                       L.ntiles, L.mode, newton_eps, s);
+                break;
             case K_COPYF:
                 e = launch_copyf(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix, L.ndesc, L.ntiles,
                                  L.mode ? flag : nullptr, s);
@@ -1344,6 +1357,118 @@ shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t tra
     hipError_t e = launch_gemm(L.cfg, L.mode, L.vec, L.slab, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
                                reinterpret_cast<const int*>(base + L.prefix_off), L.ndesc, L.ntiles, nullptr, s);
     return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+}
+
+namespace {
+
+// Plan of one coupled Newton call over caller-given matrices: work buffers first, then
+// the descriptor tables; `ctx.ws` must already point at the workspace (or null for sizing).
+struct NewtonPlan {
+    shampoo4_ctx_s ctx;
+    size_t buffers = 0;
+    Seq seq;
+};
+
+void plan_newton(NewtonPlan& np, int32_t count, const int32_t* p, const float* const* A, const int64_t* lda,
+                 int32_t iters, float* const* X, const int64_t* ldx) {
+    shampoo4_ctx_s& c = np.ctx;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes ? bytes : 1); return o; };
+    struct Bufs { size_t M[2], X[2], F, F2, F4, parts, scale; };
+    std::vector<Bufs> bufs(count);
+    for (int i = 0; i < count; ++i) {
+        const size_t mat = (size_t)p[i] * p[i] * 4;
+        Bufs& b = bufs[i];
+        b.M[0] = take(mat); b.M[1] = take(mat); b.X[0] = take(mat); b.X[1] = take(mat);
+        b.F = take(mat); b.F2 = take(mat); b.F4 = take(mat);
+        b.parts = take((size_t)fill_tiles(p[i]) * 4);
+        b.scale = take(4);
+    }
+    np.buffers = off;
+    c.desc_base = off;
+    c.blob.clear();
+    auto wf = [&](size_t o) { return c.wsf(o); };
+    std::vector<NewtonDesc> base(count);
+    std::vector<int> tiles(count);
+    for (int i = 0; i < count; ++i) {
+        NewtonDesc d;
+        std::memset(&d, 0, sizeof(d));
+        d.A = A ? A[i] : nullptr; d.lda = lda ? lda[i] : 0;
+        d.out = X ? X[i] : nullptr; d.ldo = ldx ? ldx[i] : 0;
+        d.parts = wf(bufs[i].parts); d.scale = wf(bufs[i].scale);
+        d.p = p[i];
+        base[i] = d;
+        tiles[i] = fill_tiles(p[i]);
+    }
+    auto elem = [&](int mode, auto fill) {
+        std::vector<NewtonDesc> ds = base;
+        for (int i = 0; i < count; ++i) fill(ds[i], bufs[i]);
+        Launch L = c.make_items(K_NEWTON_ELEM, ds, tiles);
+        L.mode = mode;
+        return L;
+    };
+    np.seq.clear();
+    np.seq.push_back(c.make_items(K_NEWTON_NORM, base, tiles));
+    {
+        std::vector<int> ones(count, 1);
+        np.seq.push_back(c.make_items(K_NEWTON_SCALE, base, ones));
+    }
+    np.seq.push_back(elem(0, [&](NewtonDesc& d, const Bufs& b) { d.dst = wf(b.M[0]); d.ident = wf(b.X[0]); }));
+    Seq per[2];
+    for (int q = 0; q < 2; ++q) {
+        per[q].push_back(elem(1, [&](NewtonDesc& d, const Bufs& b) { d.src = wf(b.M[q]); d.dst = wf(b.F); }));
+        std::vector<shampoo4_ctx_s::GemmItem> g1, g2, g3;
+        for (int i = 0; i < count; ++i) {
+            const int n = p[i];
+            const Bufs& b = bufs[i];
+            g1.push_back({c.gd(wf(b.X[q]), n, wf(b.F), n, wf(b.X[1 - q]), n, n, n, n), false, false});
+            g1.push_back({c.gd(wf(b.F), n, wf(b.F), n, wf(b.F2), n, n, n, n), false, false});
+            g2.push_back({c.gd(wf(b.F2), n, wf(b.F2), n, wf(b.F4), n, n, n, n), false, false});
+            g3.push_back({c.gd(wf(b.F4), n, wf(b.M[q]), n, wf(b.M[1 - q]), n, n, n, n), false, false});
+        }
+        for (auto* items : {&g1, &g2, &g3}) {
+            Seq g = c.make_gemm(*items, FAM_GEMM_PRECOND);
+            per[q].insert(per[q].end(), g.begin(), g.end());
+        }
+    }
+    for (int it = 0; it < iters; ++it) np.seq.insert(np.seq.end(), per[it & 1].begin(), per[it & 1].end());
+    np.seq.push_back(elem(2, [&](NewtonDesc& d, const Bufs& b) { d.src = wf(b.X[iters & 1]); }));
+}
+
+}  // namespace
+
+size_t shampoo4_inverse_root_workspace_bytes(int32_t count, const int32_t* p) {
+    if (count <= 0 || !p) return 0;
+    for (int i = 0; i < count; ++i)
+        if (p[i] < 1 || p[i] > kMaxDim) return 0;
+    NewtonPlan np;
+    plan_newton(np, count, p, nullptr, nullptr, 2, nullptr, nullptr);
+    return np.buffers + align_up(np.ctx.blob.size());
+}
+
+shampoo4_status shampoo4_inverse_root(int32_t count, const int32_t* p, const float* const* A, const int64_t* lda,
+                                      float eps, int32_t iters, float* const* X, const int64_t* ldx,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (count < 0) return SHAMPOO4_EINVAL;
+    if (count == 0) return SHAMPOO4_OK;
+    if (!p || !A || !lda || !X || !ldx || !workspace) return SHAMPOO4_EINVAL;
+    if (!(eps >= 0.f) || !std::isfinite(eps) || iters < 0 || iters > 100) return SHAMPOO4_EINVAL;
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return SHAMPOO4_EALIGN;
+    for (int i = 0; i < count; ++i) {
+        if (p[i] < 1 || p[i] > kMaxDim) return SHAMPOO4_ESHAPE;
+        if (!A[i] || !X[i]) return SHAMPOO4_EINVAL;
+        if (lda[i] < p[i] || ldx[i] < p[i]) return SHAMPOO4_ESHAPE;
+    }
+    if (workspace_bytes < shampoo4_inverse_root_workspace_bytes(count, p)) return SHAMPOO4_ESMALLBUF;
+    NewtonPlan np;
+    np.ctx.ws = static_cast<uint8_t*>(workspace);
+    np.ctx.newton_eps = eps;
+    plan_newton(np, count, p, A, lda, iters, X, ldx);
+    hipStream_t s = as_stream(stream);
+    if (hipMemcpyAsync(np.ctx.ws + np.ctx.desc_base, np.ctx.blob.data(), np.ctx.blob.size(),
+                       hipMemcpyHostToDevice, s) != hipSuccess)
+        return SHAMPOO4_EHIP;
+    return np.ctx.run(np.seq, s) == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
 
 shampoo4_status shampoo4_timing(shampoo4_ctx c, int32_t enable) {

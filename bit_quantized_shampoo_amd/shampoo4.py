@@ -306,3 +306,29 @@ def gemm_batched(As, Bs, Ds=None, transA=False, transB=False, alpha=1.0, beta=0.
         vp(*[_ptr(d) for d in Ds]), i64(*[d.stride(0) for d in Ds]),
         _ptr(workspace), workspace.numel(), _stream_ptr(stream)), "shampoo4_gemm_batched")
     return Ds, workspace
+
+
+def inverse_root(As, eps: float = 1e-6, iters: int = 20, Xs=None, workspace: torch.Tensor | None = None,
+                 stream=None):
+    """(A_i + eps I)^(-1/4) by the coupled Newton iteration on the MFMA GEMM (square,
+    row-major fp32 device tensors).  Returns (Xs, workspace)."""
+    count = len(As)
+    for A in As:
+        _require_gpu_tensor(A, torch.float32, "A")
+        if A.dim() != 2 or A.shape[0] != A.shape[1] or (A.stride(1) != 1 and A.shape[1] > 1):
+            raise ValueError("square row-major matrices required")
+    ps = [int(A.shape[0]) for A in As]
+    if Xs is None:
+        Xs = [torch.empty((n, n), dtype=torch.float32, device=As[0].device) for n in ps]
+    i32 = ctypes.c_int32 * count
+    i64 = ctypes.c_int64 * count
+    vp = ctypes.c_void_p * count
+    parr = i32(*ps)
+    need = L.lib().shampoo4_inverse_root_workspace_bytes(count, parr)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=As[0].device)
+    L.check(L.lib().shampoo4_inverse_root(
+        count, parr, vp(*[_ptr(a) for a in As]), i64(*[max(a.stride(0), a.shape[1]) for a in As]),
+        float(eps), int(iters), vp(*[_ptr(x) for x in Xs]), i64(*[max(x.stride(0), x.shape[1]) for x in Xs]),
+        _ptr(workspace), workspace.numel(), _stream_ptr(stream)), "shampoo4_inverse_root")
+    return Xs, workspace

@@ -248,6 +248,26 @@ SHAMPOO4_API shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA
                                       float* const* D, const int64_t* ldd,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Inverse 4th root by the coupled Newton iteration, matrix products only ("Shampoo --
+ * Second-Order Optimizer", section "Computing the inverse fourth root", second route),
+ * for the unquantized baseline: for each i < count,
+ *     X_i = (A_i + eps I)^(-1/4)
+ * with A_i symmetric positive semi-definite [p_i, p_i] (leading dimension lda_i), after
+ * scaling by c = ||A_i + eps I||_F: X = I, M = (A_i + eps I) / c, then `iters` times
+ * F = (5 I - M) / 4, X <- X F, M <- F^4 M (three grouped MFMA GEMM launches per
+ * iteration over all matrices), and X_i = c^(-1/4) X.  M tends to I quadratically once
+ * close; a factor with condition number k needs about log(k) / log(2.44) + 5 iterations.
+ * Host arrays of device pointers; `workspace` is 256-byte aligned device memory of at
+ * least shampoo4_inverse_root_workspace_bytes(count, p) bytes (seven p x p float matrices
+ * per input plus descriptor tables, copied from pageable host memory at the call).
+ * ESHAPE: p outside 1..8192 or ld < p; EINVAL: null pointers, eps < 0, iters outside
+ * 0..100; ESMALLBUF: workspace too small. */
+SHAMPOO4_API size_t shampoo4_inverse_root_workspace_bytes(int32_t count, const int32_t* p);
+SHAMPOO4_API shampoo4_status shampoo4_inverse_root(int32_t count, const int32_t* p, const float* const* A,
+                                                   const int64_t* lda, float eps, int32_t iters,
+                                                   float* const* X, const int64_t* ldx,
+                                                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Kernel timing (HIP events around every launch of the next calls on a context).
  * enable != 0 starts recording (clears previous records); the report waits for the
  * device and returns, per kernel family, the number of launches, total milliseconds,

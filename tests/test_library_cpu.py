@@ -108,3 +108,14 @@ def test_null_arguments_rejected_on_host():
     assert lib.shampoo4_quantize(None, 5, 64, None, None, None) == L.EINVAL
     assert lib.shampoo4_quantize(None, 5, 32, None, None, None) == L.EINVAL
     assert lib.shampoo4_dequantize(None, None, 0, 64, None, None) == L.OK
+
+
+def test_inverse_root_workspace_sizes():
+    lib = _lib()
+    i32 = ctypes.c_int32
+    p = (i32 * 3)(1024, 77, 1)
+    need = lib.shampoo4_inverse_root_workspace_bytes(3, p)
+    assert need >= 7 * 4 * (1024 * 1024 + 77 * 77 + 1)
+    bad = (i32 * 1)(0)
+    assert lib.shampoo4_inverse_root_workspace_bytes(1, bad) == 0
+    assert lib.shampoo4_inverse_root(1, bad, None, None, 0.0, 1, None, None, None, 0, None) == L.EINVAL
