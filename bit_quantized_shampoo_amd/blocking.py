@@ -1,0 +1,94 @@
+"""Host-side parameter blocking with diagonal fallbacks.
+
+Follows "Shampoo -- Second-Order Optimizer", section "Blocked and distributed variants":
+every matrix parameter is cut into tiles of at most ``block`` x ``block`` that are
+preconditioned independently (capping both the factor memory and the cubic cost), and
+the page's two fallbacks route parameters without a usable matrix structure to a
+diagonal method:
+
+* 1-D (and 0-D) parameters such as biases and normalization gains;
+* parameters with a dimension above ``max_dim`` when blocking is off (``block=None``):
+  the page drops that side's factor and keeps a diagonal method along it; this library
+  preconditions both sides of every block, so such a parameter goes to the diagonal
+  method as a whole.
+
+Matrix parameters of higher rank (convolution kernels [out, in, kh, kw]) are viewed as
+[out, in * kh * kw].  Tiles are row-major with a remainder tile at the end of each row
+and column of tiles.  Everything here is host bookkeeping: the blocks are strided views
+of the caller's tensors (no copies), which the library reads with their leading
+dimensions.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+
+@dataclass
+class ParamPlan:
+    index: int                      # position in the caller's parameter list
+    shape: tuple                    # the parameter's own shape
+    kind: str                       # "blocks" or "diagonal"
+    matrix: tuple | None = None     # (m, n) 2-D view for "blocks"
+    tiles: list = field(default_factory=list)   # (r0, c0, rows, cols)
+
+
+def matrix_view_shape(shape) -> tuple | None:
+    """[out, prod(rest)] for parameters of rank >= 2, None otherwise."""
+    if len(shape) < 2:
+        return None
+    n = 1
+    for d in shape[1:]:
+        n *= int(d)
+    return (int(shape[0]), n)
+
+
+def tile(m: int, n: int, block: int) -> list:
+    return [(r0, c0, min(block, m - r0), min(block, n - c0))
+            for r0 in range(0, m, block) for c0 in range(0, n, block)]
+
+
+def plan_blocks(shapes, block: int | None = 1024, max_dim: int = 8192) -> list:
+    """One ParamPlan per parameter shape."""
+    if block is not None and block < 1:
+        raise ValueError("block must be positive")
+    out = []
+    for i, shape in enumerate(shapes):
+        shape = tuple(int(d) for d in shape)
+        mv = matrix_view_shape(shape)
+        if mv is None or 0 in mv:
+            out.append(ParamPlan(i, shape, "diagonal"))
+            continue
+        m, n = mv
+        if block is None:
+            if m > max_dim or n > max_dim:
+                out.append(ParamPlan(i, shape, "diagonal"))
+            else:
+                out.append(ParamPlan(i, shape, "blocks", mv, [(0, 0, m, n)]))
+            continue
+        out.append(ParamPlan(i, shape, "blocks", mv, tile(m, n, block)))
+    return out
+
+
+def block_shapes(plans) -> list:
+    """(rows, cols) of every tile, in plan order (the shapes a context is built for)."""
+    return [(t[2], t[3]) for p in plans if p.kind == "blocks" for t in p.tiles]
+
+
+def block_views(tensors, plans) -> list:
+    """Strided 2-D views of the tiles of `tensors` (same order as block_shapes)."""
+    views = []
+    for p in plans:
+        if p.kind != "blocks":
+            continue
+        t = tensors[p.index]
+        if not t.is_contiguous():
+            raise ValueError(f"parameter {p.index} must be contiguous to be viewed as a matrix")
+        mat = t.reshape(p.matrix)
+        for (r0, c0, rows, cols) in p.tiles:
+            views.append(mat[r0:r0 + rows, c0:c0 + cols])
+    return views
+
+
+def diagonal_indices(plans) -> list:
+    return [p.index for p in plans if p.kind == "diagonal"]

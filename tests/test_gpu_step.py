@@ -289,3 +289,30 @@ def test_fp32_state_single_1024():
     wl = get_workload("single_1024")
     _run_teacher_forced_fp32(wl.shapes, wl.gradients, 3, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
                              root_interval=1, label="single_1024")
+
+
+def test_blocked_parameter_views():
+    """Blocks of real parameters as strided views (no copies): the step reads them with
+    their leading dimensions and writes the directions into views of a full-size buffer;
+    the result equals the same step on contiguous copies, bit for bit."""
+    require_gpu()
+    from bit_quantized_shampoo_amd import Shampoo4Blocks, blocking
+    announce("blocked parameter views")
+    rng = np.random.default_rng(4)
+    params = [torch.from_numpy(rng.standard_normal((1100, 70)).astype(np.float32)).cuda(),
+              torch.from_numpy(rng.standard_normal((16, 8, 3, 3)).astype(np.float32)).cuda()]
+    plans = blocking.plan_blocks([p.shape for p in params])
+    shapes = blocking.block_shapes(plans)
+    assert shapes == [(1024, 70), (76, 70), (16, 72)]
+    views = blocking.block_views(params, plans)
+    dirs = [torch.empty_like(p) for p in params]
+    out_views = blocking.block_views(dirs, plans)
+    a = Shampoo4Blocks(shapes)
+    a.step(views, 1, outs=out_views)
+    b = Shampoo4Blocks(shapes)
+    ref = b.step([v.contiguous() for v in views], 1)
+    torch.cuda.synchronize()
+    for o, r in zip(out_views, ref):
+        assert torch.equal(o, r)
+    a.close()
+    b.close()
