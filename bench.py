@@ -233,6 +233,7 @@ def main():
                          "statistic with ITERS iterations (the unquantized baseline's root)")
     ap.add_argument("--graft", default="none", choices=["none", "sgd", "adam"],
                     help="add the grafted weight update after the preconditioner to every step")
+    ap.add_argument("--graphs", action="store_true", help="replay update_stats from a captured HIP graph")
     ap.add_argument("--qr", default="auto", choices=["auto", "blocked", "lookahead"],
                     help="Householder QR schedule (default: chosen by the library from the batch size)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -277,7 +278,7 @@ def main():
     dev = torch.device("cuda:0")
     cfg = Shampoo4Config(beta=wl.beta, eps=wl.eps, qblock=wl.qblock, bjorck_iters=wl.bjorck_iters,
                          power_iters=wl.power_iters, root_cache=not args.no_root_cache, qr_schedule=args.qr,
-                         fp32_state=args.state == "fp32")
+                         fp32_state=args.state == "fp32", graphs=args.graphs)
     log(f"[bench] workload {wl.name}: {len(wl.blocks)} blocks, steps {steps}, warmup {warmup}")
     grads, distinct, gen = make_gradients(wl, steps + warmup, dev)
     blocks = Shampoo4Blocks(wl.shapes, cfg, device=dev)
@@ -398,7 +399,7 @@ def main():
             "beta": wl.beta, "eps": wl.eps, "qblock": wl.qblock,
             "bjorck_iters": wl.bjorck_iters, "power_iters": wl.power_iters,
             "root_interval": wl.root_interval, "root_cache": cfg.root_cache, "qr_schedule": args.qr,
-            "graft": args.graft, "state": args.state,
+            "graft": args.graft, "state": args.state, "graphs": args.graphs,
         },
         "gemm_tflops": round(gemm_tflops, 3),
         "gemm_frac_mfma_peak": round(gemm_tflops / PEAK_FP32_MFMA_TFLOPS, 4),

@@ -17,6 +17,7 @@ FLAG_KEEP_STATE = 2
 FLAG_QR_BLOCKED = 4
 FLAG_QR_LOOKAHEAD = 8
 FLAG_FP32_STATE = 16
+FLAG_GRAPHS = 32
 
 BUF_CODES, BUF_SCALES, BUF_EIG, BUF_ROOT_CODES, BUF_ROOT_SCALES, BUF_ROOT_D = range(6)
 BUF_V, BUF_STAT, BUF_Q, BUF_ROOT_V = 16, 17, 18, 19

@@ -7,9 +7,10 @@
 
 namespace s4 {
 
-// Optional start/stop events for the next kernel launch.  Launches go through
-// hipExtLaunchKernelGGL, which records the events in the dispatch itself, so a
-// timed launch measures the kernel alone (no separate event packets).
+// Optional start/stop events for the next kernel launch.  A timed launch goes through
+// hipExtLaunchKernelGGL, which records the events in the dispatch itself, so it measures
+// the kernel alone (no separate event packets); untimed launches (and launches under
+// graph capture) are plain hipLaunchKernelGGL.
 struct LaunchTiming {
     hipEvent_t start = nullptr, stop = nullptr;
 };
@@ -20,7 +21,10 @@ inline LaunchTiming& launch_timing() {
 #define S4_LAUNCH(kernel, grid, block, shmem, stream, ...)                                         \
     do {                                                                                          \
         ::s4::LaunchTiming& lt_ = ::s4::launch_timing();                                          \
-        hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, lt_.start, lt_.stop, 0, __VA_ARGS__); \
+        if (lt_.start)                                                                            \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, lt_.start, lt_.stop, 0, __VA_ARGS__); \
+        else                                                                                      \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                  \
         lt_.start = lt_.stop = nullptr;                                                           \
     } while (0)
 

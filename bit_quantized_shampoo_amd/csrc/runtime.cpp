@@ -107,6 +107,12 @@ struct shampoo4_ctx_s {
     int n_sync = 0;                       // synchronization events the plan uses
     hipStream_t aux = nullptr;
     std::vector<hipEvent_t> sync_ev;
+    // update_stats replayed from a HIP graph (captured on `cap` at the first call of each
+    // variant: with or without the cached rectified eigenvectors)
+    bool use_graphs = false;
+    bool graph_ok = true;
+    hipStream_t cap = nullptr;
+    hipGraphExec_t stats_graph[2] = {};
     Seq qinit, sign, ray_gemm, rayleigh, quant, root_d, root_copy;
     Seq pre[4];
     Seq graft_seq[2];                    // per graft mode (bytes differ): norms, apply
@@ -135,7 +141,10 @@ struct shampoo4_ctx_s {
         for (auto& e : ev_pool) (void)hipEventDestroy(e);
         for (auto& e : sync_ev)
             if (e) (void)hipEventDestroy(e);
+        for (auto& g : stats_graph)
+            if (g) (void)hipGraphExecDestroy(g);
         if (aux) (void)hipStreamDestroy(aux);
+        if (cap) (void)hipStreamDestroy(cap);
         if (pinned) (void)hipHostFree(pinned);
     }
 
@@ -236,6 +245,7 @@ struct shampoo4_ctx_s {
     // ---- plan ---------------------------------------------------------------------
     void layout() {
         fp32_state = (cfg.flags & SHAMPOO4_FLAG_FP32_STATE) != 0;
+        use_graphs = (cfg.flags & SHAMPOO4_FLAG_GRAPHS) != 0;
         // Large batches are throughput-bound: reflectors go to the trailing matrix 128
         // columns at a time.  Small ones are bound by the chain of panels and by launch
         // latency: panel-wide updates on the caller's stream (or, on request, with the
@@ -985,6 +995,54 @@ struct shampoo4_ctx_s {
         return hipEventRecord(ring_ev[slot], s);
     }
 
+    // The kernels of one statistics update (everything after the io upload).
+    hipError_t stats_body(bool reuse, hipStream_t s) {
+        const int var = reuse ? 1 : 0;
+        hipError_t e = hipSuccess;
+        if (!reuse) {
+            e = run(deq_stats, s);
+            for (auto& it : bj_stats)
+                if (e == hipSuccess) e = run(it, s);
+        }
+        if (e == hipSuccess) e = run(stats_x[var], s);
+        if (e == hipSuccess) e = run(stats_g, s);
+        for (int it = 0; it < cfg.power_iters && e == hipSuccess; ++it) {
+            e = run(it == 0 ? power_first[var] : power_next, s);
+            if (e == hipSuccess) e = run(qinit, s);
+            for (int p = 0; p < max_panels && e == hipSuccess; ++p) e = run(qr_steps[p], s);
+            if (e == hipSuccess) e = run(qr_join, s);
+            if (e == hipSuccess) e = run(sign, s);
+        }
+        if (e == hipSuccess) e = run(ray_gemm, s);
+        if (e == hipSuccess) e = run(rayleigh, s);
+        if (e == hipSuccess) e = run(quant, s);
+        return e;
+    }
+
+    // Capture the statistics update once per variant on the private stream; a failed
+    // capture turns graphs off for the context (the calls then launch eagerly).
+    void capture_stats(bool reuse) {
+        const int var = reuse ? 1 : 0;
+        if (!cap && hipStreamCreateWithFlags(&cap, hipStreamNonBlocking) != hipSuccess) {
+            graph_ok = false;
+            return;
+        }
+        if (hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+            graph_ok = false;
+            return;
+        }
+        const hipError_t e = stats_body(reuse, cap);
+        hipGraph_t g = nullptr;
+        const hipError_t e2 = hipStreamEndCapture(cap, &g);
+        if (e != hipSuccess || e2 != hipSuccess || !g ||
+            hipGraphInstantiate(&stats_graph[var], g, nullptr, nullptr, 0) != hipSuccess) {
+            stats_graph[var] = nullptr;
+            graph_ok = false;
+        }
+        if (g) (void)hipGraphDestroy(g);
+        (void)hipGetLastError();
+    }
+
     hipError_t root_eigenvectors(hipStream_t s) {
         hipError_t e = run(deq_root, s);
         for (auto& it : bj_root)
@@ -1003,7 +1061,7 @@ shampoo4_status validate_cfg(const shampoo4_config* cfg) {
     if (cfg->bjorck_iters < 0 || cfg->bjorck_iters > 16) return SHAMPOO4_EINVAL;
     if (cfg->power_iters < 1 || cfg->power_iters > 8) return SHAMPOO4_EINVAL;
     if (cfg->flags & ~(SHAMPOO4_FLAG_ROOT_CACHE | SHAMPOO4_FLAG_KEEP_STATE | SHAMPOO4_FLAG_QR_BLOCKED |
-                       SHAMPOO4_FLAG_QR_LOOKAHEAD | SHAMPOO4_FLAG_FP32_STATE))
+                       SHAMPOO4_FLAG_QR_LOOKAHEAD | SHAMPOO4_FLAG_FP32_STATE | SHAMPOO4_FLAG_GRAPHS))
         return SHAMPOO4_EINVAL;
     if ((cfg->flags & SHAMPOO4_FLAG_QR_BLOCKED) && (cfg->flags & SHAMPOO4_FLAG_QR_LOOKAHEAD))
         return SHAMPOO4_EINVAL;
@@ -1140,27 +1198,13 @@ shampoo4_status shampoo4_update_stats(shampoo4_ctx c, const shampoo4_io* io, voi
     hipStream_t s = as_stream(stream);
     if (c->upload_io(io, s) != hipSuccess) return SHAMPOO4_EHIP;
     const bool reuse = (c->cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) && c->root_v_valid && c->root_v_is_stats;
-    const int var = reuse ? 1 : 0;
     hipError_t e = hipSuccess;
-    if (!reuse) {
-        e = c->run(c->deq_stats, s);
-        for (auto& it : c->bj_stats)
-            if (e == hipSuccess) e = c->run(it, s);
+    if (c->use_graphs && c->graph_ok && !c->timing) {
+        if (!c->stats_graph[reuse ? 1 : 0]) c->capture_stats(reuse);
+        e = c->stats_graph[reuse ? 1 : 0] ? hipGraphLaunch(c->stats_graph[reuse ? 1 : 0], s) : c->stats_body(reuse, s);
+    } else {
+        e = c->stats_body(reuse, s);
     }
-    if (e == hipSuccess) e = c->run(c->stats_x[var], s);
-    if (e == hipSuccess) e = c->run(c->stats_g, s);
-    for (int it = 0; it < c->cfg.power_iters && e == hipSuccess; ++it) {
-        e = c->run(it == 0 ? c->power_first[var] : c->power_next, s);
-        if (e == hipSuccess) e = c->run(c->qinit, s);
-        for (int p = 0; p < c->max_panels && e == hipSuccess; ++p) {
-            e = c->run(c->qr_steps[p], s);
-        }
-        if (e == hipSuccess) e = c->run(c->qr_join, s);
-        if (e == hipSuccess) e = c->run(c->sign, s);
-    }
-    if (e == hipSuccess) e = c->run(c->ray_gemm, s);
-    if (e == hipSuccess) e = c->run(c->rayleigh, s);
-    if (e == hipSuccess) e = c->run(c->quant, s);
     c->root_v_is_stats = false;
     return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }

@@ -57,6 +57,7 @@ class Shampoo4Config:
     root_cache: bool = False
     qr_schedule: str = "auto"       # "auto", "blocked" or "lookahead"
     fp32_state: bool = False        # keep U in float32 (the 32-bit baseline) instead of 4-bit codes
+    graphs: bool = False            # replay update_stats from a captured HIP graph
 
     def c(self, keep_state: bool = False) -> L.Config:
         flags = (L.FLAG_ROOT_CACHE if self.root_cache else 0) | (L.FLAG_KEEP_STATE if keep_state else 0)
@@ -65,6 +66,8 @@ class Shampoo4Config:
         flags |= {"auto": 0, "blocked": L.FLAG_QR_BLOCKED, "lookahead": L.FLAG_QR_LOOKAHEAD}[self.qr_schedule]
         if self.fp32_state:
             flags |= L.FLAG_FP32_STATE
+        if self.graphs:
+            flags |= L.FLAG_GRAPHS
         return L.Config(self.beta, self.eps, self.qblock, self.bjorck_iters, self.power_iters, flags)
 
 

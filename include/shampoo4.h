@@ -93,6 +93,12 @@ typedef enum {
    in float32 (state buffers CODES / ROOT_CODES hold p x p floats, SCALES / ROOT_SCALES are
    empty) and every stage runs the same kernels with the codec replaced by copies. */
 #define SHAMPOO4_FLAG_FP32_STATE 16u
+/* Replay shampoo4_update_stats from a HIP graph captured at the first call (one graph
+   per variant: with or without the cached rectified eigenvectors): the kernels, and the
+   second stream of QR_LOOKAHEAD with its event dependencies, are submitted as one graph
+   launch instead of one host call each.  The io upload stays a separate copy before the
+   launch.  While kernel timing is on, and if a capture fails, calls launch eagerly. */
+#define SHAMPOO4_FLAG_GRAPHS 32u
 
 typedef struct {
     int32_t m, n;             /* block shape: G is [m, n]; side L has order m, side R order n */

@@ -79,7 +79,8 @@ def test_plan_sizes():
     ([(4, 4)], {"k": -1}, L.EINVAL),
     ([(4, 4)], {"k": 17}, L.EINVAL),
     ([(4, 4)], {"pi": 0}, L.EINVAL),
-    ([(4, 4)], {"flags": 32}, L.EINVAL),
+    ([(4, 4)], {"flags": 64}, L.EINVAL),
+    ([(4, 4)], {"flags": L.FLAG_GRAPHS}, L.OK),
     ([(4, 4)], {"flags": L.FLAG_FP32_STATE}, L.OK),
     ([(4, 4)], {"flags": L.FLAG_QR_BLOCKED | L.FLAG_QR_LOOKAHEAD}, L.EINVAL),
     ([(4, 4)], {"flags": L.FLAG_QR_BLOCKED}, L.OK),
