@@ -8,7 +8,9 @@
 //
 // Design:
 //  * workgroup = 4 waves (256 threads); a wave owns TM x TN blocks of 32x32
-//    accumulators (16 fp32 each);
+//    accumulators (16 fp32 each); the register budget is capped for two workgroups
+//    per CU (two waves per SIMD hide each other's barrier and LDS waits: +20% on the
+//    1024^3 products against one wave per SIMD with a few registers spilled);
 //  * the K loop stages BK = 16 slices of op(A) and op(B) in LDS, double
 //    buffered with a register prefetch of the next slice, one barrier per slice;
 //  * LDS layout follows the global layout so that every global load is a
@@ -329,6 +331,7 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
                     const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
                     s += acc[m][n][r] * keep_if(cv[r], row < M && col < N);
                 }
+                __builtin_amdgcn_sched_barrier(0);   // one 32 x 32 block's C values live at a time
             }
             s += __shfl_xor(s, 32);
             if (h == 0) red[wave_m * BN + lcol] = s;
@@ -380,13 +383,16 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
                 const float v = fmaf(beta, cv[r], alpha * acc[m][n][r] * rv[r] * csv);
                 if (row < M && col < N) stg(D + (int64_t)row * ldd + col, v);
             }
+            // one 32 x 32 block at a time: keeps the next block's loads from being
+            // hoisted here (their registers would cap the kernel's occupancy)
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
 // One transpose mode for the whole launch, 16-byte loads, no split-K slabs.
 template <int WM, int WN, int TM, int TN, bool TA, bool TB>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ descs,
+__global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmDesc* __restrict__ descs,
                                                    const int* __restrict__ prefix, int ndesc,
                                                    const IoEntry* __restrict__ io) {
     using T = Tile<WM, WN, TM, TN>;
@@ -401,7 +407,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmDesc* __restrict__ 
 
 // Transpose mode per descriptor (uniform per workgroup); VEC and SLAB per launch.
 template <int WM, int WN, int TM, int TN, bool VEC, bool SLAB>
-__global__ __launch_bounds__(256) void gemm_kernel_mixed(const GemmDesc* __restrict__ descs,
+__global__ __launch_bounds__(256, 2) void gemm_kernel_mixed(const GemmDesc* __restrict__ descs,
                                                          const int* __restrict__ prefix, int ndesc,
                                                          const IoEntry* __restrict__ io) {
     using T = Tile<WM, WN, TM, TN>;
