@@ -169,7 +169,22 @@ struct shampoo4_ctx_s {
     };
 
     // One launch for a batch of products (mixed transposes allowed).
-    Seq make_gemm(std::vector<GemmItem> items, int fam) {
+    // With split_modes, products of different transpose modes go to separate launches
+    // of the specialized kernels (fewer registers than the mixed kernel, which spills a
+    // little at the 128 x 128 tile); otherwise one launch covers them all.
+    Seq make_gemm(std::vector<GemmItem> items, int fam, bool split_modes = false) {
+        if (split_modes) {
+            Seq out;
+            for (int mode = 0; mode < 4; ++mode) {
+                std::vector<GemmItem> part;
+                for (auto& it : items)
+                    if (((it.ta ? GEMM_F_TA : 0) | (it.tb ? GEMM_F_TB : 0)) == mode) part.push_back(it);
+                if (part.empty()) continue;
+                Seq g = make_gemm(part, fam, false);
+                out.insert(out.end(), g.begin(), g.end());
+            }
+            return out;
+        }
         std::vector<GemmDesc> ds;
         int modes = 0, first_mode = -2;
         for (auto& it : items) {
@@ -569,7 +584,7 @@ struct shampoo4_ctx_s {
             Seq& st = qr_steps[sidx];
             panel_launches(st, byc, maxh);
             for (auto* items : {&in1, &in2, &out1, &out2}) {
-                Seq g = make_gemm(*items, FAM_GEMM_QR);
+                Seq g = make_gemm(*items, FAM_GEMM_QR, outer == kOuter);
                 st.insert(st.end(), g.begin(), g.end());
             }
         }
