@@ -18,9 +18,9 @@
 //    16-lane group; each lane writes its 4 codes as one 16-bit store, lane 0 of
 //    the group writes the scale.  The code comes from one LDS table lookup keyed
 //    by the bits of x_hat instead of a scan over the 15 midpoints.
-//  * dequant: one lane per 8 elements (one 32-bit code word, two 16-byte
-//    stores), several words per lane in flight, levels looked up in a 16-entry
-//    LDS table.
+//  * dequant: a lane expands 4 elements at a time (one 16-bit code word, one
+//    16-byte store), several quads per lane in flight, spaced so that every store
+//    instruction of a wave writes 1 KB contiguous; levels from a 16-entry LDS table.
 #include "kernels.hpp"
 
 namespace s4 {
@@ -114,45 +114,43 @@ __device__ __forceinline__ uint32_t code_of(float xh, const uint2* __restrict__ 
     return mag > e.x ? (e.y >> 4) : (e.y & 15u);
 }
 
-// Dequantization: each lane expands DEQ_WORDS 32-bit code words (8 elements each)
-// spaced 256 words apart, so a wave keeps DEQ_WORDS coalesced code loads in flight.
-constexpr int DEQ_WORDS = DEQ_TILE / (256 * 8);
+// Dequantization: each lane expands DEQ_QUADS groups of 4 elements (one 16-bit code
+// word, one 16-byte store) spaced 256 quads apart, so every store instruction of a wave
+// writes 1 KB contiguous.
+constexpr int DEQ_QUADS = DEQ_TILE / (256 * 4);
 
 __device__ __forceinline__ void dequant_item(const CodecDesc& d, int tile) {
     __shared__ float lv[16];
     if (threadIdx.x < 16) lv[threadIdx.x] = c_levels[threadIdx.x];
     __syncthreads();
     const int64_t n = d.n;
-    const int64_t nwords = ((n + 63) / 64) * 8;
-    const int64_t w0 = (int64_t)tile * (DEQ_TILE / 8) + threadIdx.x;
-    const uint32_t* __restrict__ cw_in = reinterpret_cast<const uint32_t*>(d.codes_in);
-    uint32_t cw[DEQ_WORDS];
-    float sc[DEQ_WORDS];
+    const int64_t nquads = ((n + 63) / 64) * 16;
+    const int64_t q0 = (int64_t)tile * (DEQ_TILE / 4) + threadIdx.x;
+    const uint16_t* __restrict__ cq = reinterpret_cast<const uint16_t*>(d.codes_in);
+    uint32_t cw[DEQ_QUADS];
+    float sc[DEQ_QUADS];
 #pragma unroll
-    for (int k = 0; k < DEQ_WORDS; ++k) {
-        const int64_t w = w0 + k * 256;
-        const bool ok = w < nwords;
-        cw[k] = ok ? cw_in[w] : 0u;
-        sc[k] = ok ? d.scales_in[w >> 3] : 0.f;
+    for (int k = 0; k < DEQ_QUADS; ++k) {
+        const int64_t q = min(q0 + k * 256, nquads - 1);
+        cw[k] = ldg(cq + q);
+        sc[k] = ldg(d.scales_in + (q >> 4));
     }
     float* __restrict__ x = d.x_out;
     const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
 #pragma unroll
-    for (int k = 0; k < DEQ_WORDS; ++k) {
-        const int64_t w = w0 + k * 256;
-        if (w >= nwords) break;
-        float v[8];
+    for (int k = 0; k < DEQ_QUADS; ++k) {
+        const int64_t q = q0 + k * 256;
+        if (q >= nquads) break;
+        float v[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = lv[(cw[k] >> (4 * e)) & 15u] * sc[k];
-        const int64_t e0 = w * 8;
-        if (e0 + 8 <= n && aligned) {
-            floatx4 a = {v[0], v[1], v[2], v[3]};
-            floatx4 b = {v[4], v[5], v[6], v[7]};
-            *reinterpret_cast<floatx4*>(x + e0) = a;
-            *reinterpret_cast<floatx4*>(x + e0 + 4) = b;
+        for (int e = 0; e < 4; ++e) v[e] = lv[(cw[k] >> (4 * e)) & 15u] * sc[k];
+        const int64_t e0 = q * 4;
+        if (e0 + 4 <= n && aligned) {
+            const floatx4 a = {v[0], v[1], v[2], v[3]};
+            stg(reinterpret_cast<floatx4*>(x + e0), a);
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
+            for (int e = 0; e < 4; ++e)
                 if (e0 + e < n) x[e0 + e] = v[e];
         }
     }

@@ -23,8 +23,8 @@ hipError_t launch_gemm(int cfg, int mode, bool vec, bool slab, const GemmDesc* d
 bool gemm_vec_ok(const GemmDesc& d);
 
 // Codec: elements per workgroup tile.
-constexpr int DEQ_TILE = 8192;     // 256 threads x 4 code words x 8 elements
-constexpr int QUANT_TILE = 2048;   // 256 threads x 2 quads x 4 elements
+constexpr int DEQ_TILE = 8192;     // 256 threads x 8 quads x 4 elements
+constexpr int QUANT_TILE = 4096;   // 256 threads x 4 quads x 4 elements
 constexpr int COPY_TILE = 8192;    // bytes of codes per workgroup
 // workgroups for n elements (quantization blocks of 64 padded)
 inline int64_t dequant_tiles(int64_t n) { return ((n + 63) / 64 * 64 + DEQ_TILE - 1) / DEQ_TILE; }
