@@ -11,7 +11,8 @@ float64 inverse root of the blog's "Computing the inverse fourth root" section
 (damping before rooting: (L + eps I)^(-1/4) = U diag((lam + eps)^(-1/4)) U^T):
 
 * ``root_fp32``      U and lam rounded to float32 (the 32-bit state);
-* ``root_eigvec4``   U quantized to 4 bits (block-wise linear-square codec), then
+* ``root_eigvec4``   U quantized to 4 bits (block-wise linear-square codec, or the
+                     dynamic tree codebook the abstract compares it with), then
                      k Bjorck iterations, with the float32 eigenvalues;
 * ``root_precond4``  L itself quantized to 4 bits with the same codec (row-major
                      blocks of 64), then the float64 inverse root of the dequantized
@@ -55,11 +56,13 @@ def root_fp32(L, eps: float):
     return root_from(U.astype(np.float32), lam.astype(np.float32), eps)
 
 
-def root_eigvec4(L, eps: float, bjorck_iters: int = 1, qblock: int = 64):
+def root_eigvec4(L, eps: float, bjorck_iters: int = 1, qblock: int = 64,
+                 codebook: str = codec.LINEAR_SQUARE):
     lam, U = eigh_desc(L)
     p = U.shape[0]
-    codes, scales = codec.quantize_matrix(U.astype(np.float32), qblock)
-    V = bjorck(codec.dequantize_matrix(codes, scales, p, qblock).astype(np.float64), bjorck_iters)
+    codes, scales = codec.quantize_matrix(U.astype(np.float32), qblock, codebook)
+    V = bjorck(codec.dequantize_matrix(codes, scales, p, qblock, codebook).astype(np.float64),
+               bjorck_iters)
     return root_from(V, lam.astype(np.float32), eps)
 
 
@@ -81,6 +84,7 @@ def ablation(L, eps: float, bjorck_iters: int = 1):
         "fp32": rel_err(root_fp32(L, eps), truth),
         "eigvec4_no_rectify": rel_err(root_eigvec4(L, eps, 0), truth),
         "eigvec4": rel_err(root_eigvec4(L, eps, bjorck_iters), truth),
+        "eigvec4_dt": rel_err(root_eigvec4(L, eps, bjorck_iters, codebook=codec.DYNAMIC_TREE), truth),
         "precond4": rel_err(root_precond4(L, eps), truth),
     }
 

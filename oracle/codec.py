@@ -1,4 +1,5 @@
-"""Linear-square 4-bit block codec, bit-exact float32 emulation (oracle side).
+"""4-bit block codecs (linear-square and dynamic tree), bit-exact float32
+emulation (oracle side).
 
 TEST INFRASTRUCTURE ONLY -- see the package docstring.
 
@@ -31,6 +32,29 @@ design notes):
 Parity status: pinned by tests (round trip on codebook values, identity
 exactness, brute-force nearest-level search with exact rational distances,
 hand-worked golden block).
+
+Dynamic tree codebook (``codebook="dt"``).  The same abstract names dynamic tree
+quantization as the alternative that linear-square slightly outperforms, and the
+pages cite its source (the 8-bit optimizers paper) by title only; its definition is
+taken from that published method and written out here (readings marked):
+
+* A 4-bit pattern is a sign bit and three magnitude bits.  In the magnitude, the
+  number E of leading zero bits is a base-10 exponent, the first one bit is an
+  indicator, and the b = 2 - E bits after it are a linear fraction f: the value is
+  sign * 10^-E * (1/10 + (9/10) * (2f + 1) / 2^(b+1)), i.e. the midpoints of 2^b
+  equal bins of [1/10, 1], scaled into the decade [10^-(E+1), 10^-E].
+* The all-zero magnitude is zero.  Reading: the pattern with the sign bit set and
+  an all-zero magnitude (a second zero) stands for +1, so that the block maximum,
+  which normalizes to exactly 1, is represented exactly -- as the linear-square
+  codebook's top level does.
+* Levels times 2000: -1775 -1325 -875 -425 -155 -65 -11 0 11 65 155 425 875 1325
+  1775 2000.  Codes are indices into the ascending level list (the zero level is
+  code 7 as in the linear-square codebook); rounding, midpoints, blocks,
+  normalization, packing and dequantization are exactly as above.
+
+Parity status of the dynamic tree levels: unpinned by the pages (the definition
+is not on them); the tests pin the table to the bit-level decoding rule and the
+nearest-level mechanics as for linear-square.
 """
 
 from __future__ import annotations
@@ -86,12 +110,58 @@ def exact_midpoints() -> list[Fraction]:
 LEVELS = np.array([rn32(q) for q in exact_levels()], dtype=np.float32)
 MIDPOINTS = np.array([rn32(m) for m in exact_midpoints()], dtype=np.float32)
 
+LINEAR_SQUARE = "ls"
+DYNAMIC_TREE = "dt"
+
+
+def dynamic_tree_value(pattern: int) -> Fraction:
+    """Exact value of a 4-bit dynamic tree pattern (bit 3: sign, bits 2..0: magnitude)."""
+    if not 0 <= pattern < 16:
+        raise ValueError("a 4-bit pattern")
+    negative = bool(pattern & 8)
+    mag = pattern & 7
+    if mag == 0:
+        return Fraction(1) if negative else Fraction(0)
+    e = 3 - mag.bit_length()          # leading zeros of the 3-bit magnitude
+    b = 2 - e                         # fraction bits after the indicator bit
+    f = mag & ((1 << b) - 1)
+    value = Fraction(1, 10 ** e) * (Fraction(1, 10) + Fraction(9, 10) * Fraction(2 * f + 1, 2 ** (b + 1)))
+    return -value if negative else value
+
+
+def exact_levels_of(codebook: str) -> list[Fraction]:
+    if codebook == LINEAR_SQUARE:
+        return exact_levels()
+    if codebook == DYNAMIC_TREE:
+        return sorted(dynamic_tree_value(t) for t in range(16))
+    raise ValueError(f"unknown codebook {codebook!r}")
+
+
+def _tables(codebook: str):
+    lv = exact_levels_of(codebook)
+    mids = [(lv[j] + lv[j + 1]) / 2 for j in range(15)]
+    return (np.array([rn32(q) for q in lv], dtype=np.float32),
+            np.array([rn32(m) for m in mids], dtype=np.float32))
+
+
+_TABLES = {LINEAR_SQUARE: (LEVELS, MIDPOINTS), DYNAMIC_TREE: _tables(DYNAMIC_TREE)}
+
+
+def levels(codebook: str = LINEAR_SQUARE) -> np.ndarray:
+    """float32 levels (ascending) of a codebook."""
+    return _TABLES[codebook][0]
+
+
+def midpoints(codebook: str = LINEAR_SQUARE) -> np.ndarray:
+    """float32 decision midpoints of a codebook."""
+    return _TABLES[codebook][1]
+
 
 def num_qblocks(n: int, qblock: int = 64) -> int:
     return (n + qblock - 1) // qblock
 
 
-def quantize(x, qblock: int = 64):
+def quantize(x, qblock: int = 64, codebook: str = LINEAR_SQUARE):
     """Quantize a float32 array (flattened row-major) into packed 4-bit codes.
 
     Returns ``(codes, scales)``: ``codes`` is uint8 of length
@@ -110,7 +180,7 @@ def quantize(x, qblock: int = 64):
     if np.any(nz):
         with np.errstate(invalid="ignore", divide="ignore", over="ignore"):
             xhat = (blocks[nz] / scales[nz, None]).astype(np.float32)
-        codes[nz] = np.searchsorted(MIDPOINTS, xhat, side="left").astype(np.uint8)
+        codes[nz] = np.searchsorted(midpoints(codebook), xhat, side="left").astype(np.uint8)
     return pack_nibbles(codes.ravel()), scales
 
 
@@ -131,20 +201,20 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequantize(codes, scales, n: int, qblock: int = 64) -> np.ndarray:
+def dequantize(codes, scales, n: int, qblock: int = 64, codebook: str = LINEAR_SQUARE) -> np.ndarray:
     """Inverse of :func:`quantize`: float32 array of length ``n``."""
     scales = np.asarray(scales, dtype=np.float32).ravel()
     c = unpack_nibbles(codes)
     nqb = scales.size
     c = c[: nqb * qblock].reshape(nqb, qblock)
-    x = (LEVELS[c] * scales[:, None]).astype(np.float32)
+    x = (levels(codebook)[c] * scales[:, None]).astype(np.float32)
     return x.ravel()[:n]
 
 
-def quantize_matrix(U, qblock: int = 64):
+def quantize_matrix(U, qblock: int = 64, codebook: str = LINEAR_SQUARE):
     U = np.asarray(U, dtype=np.float32)
-    return quantize(U.ravel(), qblock)
+    return quantize(U.ravel(), qblock, codebook)
 
 
-def dequantize_matrix(codes, scales, p: int, qblock: int = 64) -> np.ndarray:
-    return dequantize(codes, scales, p * p, qblock).reshape(p, p)
+def dequantize_matrix(codes, scales, p: int, qblock: int = 64, codebook: str = LINEAR_SQUARE) -> np.ndarray:
+    return dequantize(codes, scales, p * p, qblock, codebook).reshape(p, p)

@@ -81,9 +81,10 @@ def bjorck(V, iters: int) -> np.ndarray:
     return V
 
 
-def rectified_eigenvectors(codes, scales, p: int, iters: int, qblock: int = 64) -> np.ndarray:
+def rectified_eigenvectors(codes, scales, p: int, iters: int, qblock: int = 64,
+                           codebook: str = codec.LINEAR_SQUARE) -> np.ndarray:
     """Steps 1-2: dequantize a side's eigenvector codes and rectify them."""
-    Vt = codec.dequantize_matrix(codes, scales, p, qblock).astype(np.float64)
+    Vt = codec.dequantize_matrix(codes, scales, p, qblock, codebook).astype(np.float64)
     return bjorck(Vt, iters)
 
 
@@ -169,8 +170,8 @@ class SideState:
                          self.root_codes.copy(), self.root_scales.copy(), self.d.copy())
 
 
-def initial_side(p: int, qblock: int = 64) -> SideState:
-    codes, scales = codec.quantize_matrix(np.eye(p, dtype=np.float32), qblock)
+def initial_side(p: int, qblock: int = 64, codebook: str = codec.LINEAR_SQUARE) -> SideState:
+    codes, scales = codec.quantize_matrix(np.eye(p, dtype=np.float32), qblock, codebook)
     return SideState(p=p, codes=codes, scales=scales,
                      lam=np.zeros(p, np.float32),
                      root_codes=codes.copy(), root_scales=scales.copy(),
@@ -178,12 +179,13 @@ def initial_side(p: int, qblock: int = 64) -> SideState:
 
 
 def update_side(st: SideState, Gs, beta: float, bjorck_iters: int,
-                power_iters: int = 1, qblock: int = 64) -> SideState:
+                power_iters: int = 1, qblock: int = 64,
+                codebook: str = codec.LINEAR_SQUARE) -> SideState:
     """Steps 1-5 for one side.  Returns the new state (root unchanged)."""
-    V = rectified_eigenvectors(st.codes, st.scales, st.p, bjorck_iters, qblock)
+    V = rectified_eigenvectors(st.codes, st.scales, st.p, bjorck_iters, qblock, codebook)
     Lt = statistics(V, st.lam, Gs, beta)
     Q, lam = eigen_refresh(Lt, V, power_iters)
-    codes, scales = codec.quantize_matrix(Q.astype(np.float32), qblock)
+    codes, scales = codec.quantize_matrix(Q.astype(np.float32), qblock, codebook)
     out = SideState(p=st.p, codes=codes, scales=scales, lam=lam.astype(np.float32),
                     root_codes=st.root_codes.copy(), root_scales=st.root_scales.copy(),
                     d=st.d.copy())
@@ -201,29 +203,32 @@ def refresh_side(st: SideState, eps: float) -> SideState:
     return out
 
 
-def root_eigenvectors(st: SideState, bjorck_iters: int, qblock: int = 64) -> np.ndarray:
-    return rectified_eigenvectors(st.root_codes, st.root_scales, st.p, bjorck_iters, qblock)
+def root_eigenvectors(st: SideState, bjorck_iters: int, qblock: int = 64,
+                      codebook: str = codec.LINEAR_SQUARE) -> np.ndarray:
+    return rectified_eigenvectors(st.root_codes, st.root_scales, st.p, bjorck_iters, qblock, codebook)
 
 
 class Shampoo4Oracle:
     """The whole schedule over a list of blocks (one SideState per block and side)."""
 
     def __init__(self, shapes, beta: float = 0.95, eps: float = 1e-6, qblock: int = 64,
-                 bjorck_iters: int = 1, power_iters: int = 1):
+                 bjorck_iters: int = 1, power_iters: int = 1, codebook: str = codec.LINEAR_SQUARE):
         self.shapes = [tuple(int(v) for v in s) for s in shapes]
         self.beta = beta
         self.eps = eps
         self.qblock = qblock
         self.bjorck_iters = bjorck_iters
         self.power_iters = power_iters
-        self.sides = [[initial_side(m, qblock), initial_side(n, qblock)] for (m, n) in self.shapes]
+        self.codebook = codebook
+        self.sides = [[initial_side(m, qblock, codebook), initial_side(n, qblock, codebook)]
+                      for (m, n) in self.shapes]
 
     def update_stats(self, Gs):
         for b, G in enumerate(Gs):
             for side in (SIDE_L, SIDE_R):
                 self.sides[b][side] = update_side(self.sides[b][side], side_gradient(G, side),
                                                   self.beta, self.bjorck_iters,
-                                                  self.power_iters, self.qblock)
+                                                  self.power_iters, self.qblock, self.codebook)
 
     def refresh_root(self):
         for b in range(len(self.shapes)):
@@ -234,8 +239,8 @@ class Shampoo4Oracle:
         out = []
         for b, G in enumerate(Gs):
             sl, sr = self.sides[b]
-            VL = root_eigenvectors(sl, self.bjorck_iters, self.qblock)
-            VR = root_eigenvectors(sr, self.bjorck_iters, self.qblock)
+            VL = root_eigenvectors(sl, self.bjorck_iters, self.qblock, self.codebook)
+            VR = root_eigenvectors(sr, self.bjorck_iters, self.qblock, self.codebook)
             out.append(precondition_block(VL, sl.d, VR, sr.d, G).astype(np.float32))
         return out
 
