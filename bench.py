@@ -175,7 +175,7 @@ def make_gradients(wl, steps: int, device):
     return out, distinct, "device generator with the workload's distributions"
 
 
-def cpu_baseline(wl, budget_s: float = 15.0):
+def cpu_baseline(wl, budget_s: float = 15.0, codebook: str = "ls"):
     """The CPU oracle, as it stands, on the first steps of the same workload."""
     from threadpoolctl import threadpool_info
 
@@ -194,7 +194,7 @@ def cpu_baseline(wl, budget_s: float = 15.0):
     sel = blocks[:max_blocks]
     shapes = [wl.shapes[i] for i in sel]
     orc = o.Shampoo4Oracle(shapes, beta=wl.beta, eps=wl.eps, qblock=wl.qblock,
-                           bjorck_iters=wl.bjorck_iters, power_iters=wl.power_iters)
+                           bjorck_iters=wl.bjorck_iters, power_iters=wl.power_iters, codebook=codebook)
     steps = 0
     t0 = time.perf_counter()
     elapsed = 0.0
@@ -228,6 +228,8 @@ def main():
     ap.add_argument("--no-root-cache", action="store_true")
     ap.add_argument("--state", default="4bit", choices=["4bit", "fp32"],
                     help="eigenvector storage: 4-bit codes (the method) or float32 (its 32-bit baseline)")
+    ap.add_argument("--codebook", default="ls", choices=["ls", "dt"],
+                    help="4-bit codebook: linear-square (the method) or dynamic tree (its compared alternative)")
     ap.add_argument("--newton", type=int, default=0, metavar="ITERS",
                     help="also time the coupled Newton inverse 4th root (GEMM only) of every side's "
                          "statistic with ITERS iterations (the unquantized baseline's root)")
@@ -278,7 +280,7 @@ def main():
     dev = torch.device("cuda:0")
     cfg = Shampoo4Config(beta=wl.beta, eps=wl.eps, qblock=wl.qblock, bjorck_iters=wl.bjorck_iters,
                          power_iters=wl.power_iters, root_cache=not args.no_root_cache, qr_schedule=args.qr,
-                         fp32_state=args.state == "fp32", graphs=args.graphs)
+                         fp32_state=args.state == "fp32", graphs=args.graphs, codebook=args.codebook)
     log(f"[bench] workload {wl.name}: {len(wl.blocks)} blocks, steps {steps}, warmup {warmup}")
     grads, distinct, gen = make_gradients(wl, steps + warmup, dev)
     blocks = Shampoo4Blocks(wl.shapes, cfg, device=dev)
@@ -399,7 +401,7 @@ def main():
             "beta": wl.beta, "eps": wl.eps, "qblock": wl.qblock,
             "bjorck_iters": wl.bjorck_iters, "power_iters": wl.power_iters,
             "root_interval": wl.root_interval, "root_cache": cfg.root_cache, "qr_schedule": args.qr,
-            "graft": args.graft, "state": args.state, "graphs": args.graphs,
+            "graft": args.graft, "state": args.state, "codebook": args.codebook, "graphs": args.graphs,
         },
         "gemm_tflops": round(gemm_tflops, 3),
         "gemm_frac_mfma_peak": round(gemm_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
@@ -441,7 +443,7 @@ def main():
     del grads
     if not args.no_cpu:
         log("[bench] timing the CPU oracle on a bounded sample")
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, args.codebook)
     print(json.dumps(result), flush=True)
 
 

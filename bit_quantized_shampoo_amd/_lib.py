@@ -18,6 +18,9 @@ FLAG_QR_BLOCKED = 4
 FLAG_QR_LOOKAHEAD = 8
 FLAG_FP32_STATE = 16
 FLAG_GRAPHS = 32
+FLAG_DT_CODEBOOK = 64
+CODEBOOK_LINEAR_SQUARE = 0
+CODEBOOK_DYNAMIC_TREE = 1
 
 BUF_CODES, BUF_SCALES, BUF_EIG, BUF_ROOT_CODES, BUF_ROOT_SCALES, BUF_ROOT_D = range(6)
 BUF_V, BUF_STAT, BUF_Q, BUF_ROOT_V = 16, 17, 18, 19
@@ -26,7 +29,8 @@ EXPORTED = [
     "shampoo4_abi_version", "shampoo4_strerror", "shampoo4_plan", "shampoo4_init",
     "shampoo4_update_stats", "shampoo4_refresh_root", "shampoo4_precondition",
     "shampoo4_check", "shampoo4_destroy", "shampoo4_layout", "shampoo4_quantize",
-    "shampoo4_dequantize", "shampoo4_codebook", "shampoo4_gemm_workspace_bytes",
+    "shampoo4_dequantize", "shampoo4_codebook", "shampoo4_quantize_ex", "shampoo4_dequantize_ex",
+    "shampoo4_codebook_ex", "shampoo4_gemm_workspace_bytes",
     "shampoo4_gemm_batched", "shampoo4_timing", "shampoo4_timing_report", "shampoo4_graft",
     "shampoo4_inverse_root_workspace_bytes", "shampoo4_inverse_root",
 ]
@@ -95,6 +99,9 @@ def lib() -> ctypes.CDLL:
         "shampoo4_quantize": (st, [vp, i64, i32, vp, vp, vp]),
         "shampoo4_dequantize": (st, [vp, vp, i64, i32, vp, vp]),
         "shampoo4_codebook": (st, [ctypes.POINTER(f32), ctypes.POINTER(f32)]),
+        "shampoo4_quantize_ex": (st, [vp, i64, i32, i32, vp, vp, vp]),
+        "shampoo4_dequantize_ex": (st, [vp, vp, i64, i32, i32, vp, vp]),
+        "shampoo4_codebook_ex": (st, [i32, ctypes.POINTER(f32), ctypes.POINTER(f32)]),
         "shampoo4_gemm_workspace_bytes": (sz, [i32]),
         "shampoo4_gemm_batched": (st, [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                        ctypes.POINTER(i32), f32, ctypes.POINTER(vp), ctypes.POINTER(i64),

@@ -1,15 +1,22 @@
-// Block-wise 4-bit linear-square codec ("4-bit Shampoo for Memory-Efficient Network
-// Training", abstract: the eigenvector matrix is stored in 4 bits with linear-square
-// quantization, block-wise).
+// Block-wise 4-bit codecs ("4-bit Shampoo for Memory-Efficient Network Training",
+// abstract: the eigenvector matrix is stored in 4 bits, block-wise, with linear-square
+// quantization, which the abstract compares with dynamic tree quantization).
 //
-// Codebook: 16 levels sign(t) t^2 on the grid t = -1 + 2j/15 (j = 0..15) with the
-// j = 7 level set to an exact zero; times 225 the levels are
+// Linear-square codebook: 16 levels sign(t) t^2 on the grid t = -1 + 2j/15 (j = 0..15)
+// with the j = 7 level set to an exact zero; times 225 the levels are
 //   -225 -169 -121 -81 -49 -25 -9 0 1 9 25 49 81 121 169 225.
-// A value x of a 64-element block with absmax s > 0 is normalized as
-// x_hat = x / s (IEEE correctly rounded) and coded as the number of float32
-// decision midpoints strictly below x_hat (a value equal to a midpoint takes the
-// lower code); s = 0 codes the whole block as the zero level.  Two codes per byte,
-// even element in the low nibble.  Dequantization is one fp32 multiply q[code] * s.
+// Dynamic tree codebook (defined in the 8-bit optimizers paper the pages cite): a sign
+// bit and three magnitude bits whose leading zeros E are a base-10 exponent, then an
+// indicator bit and 2 - E linear fraction bits (midpoints of equal bins of [0.1, 1],
+// times 10^-E); zero, and +1 in place of the negative zero so that a block's maximum is
+// exact.  Ascending, times 2000:
+//   -1775 -1325 -875 -425 -155 -65 -11 0 11 65 155 425 875 1325 1775 2000.
+// Codes index the ascending levels (the zero level is code 7 in both).  A value x of a
+// 64-element block with absmax s > 0 is normalized as x_hat = x / s (IEEE correctly
+// rounded) and coded as the number of float32 decision midpoints strictly below x_hat
+// (a value equal to a midpoint takes the lower code); s = 0 codes the whole block as
+// the zero level.  Two codes per byte, even element in the low nibble.
+// Dequantization is one fp32 multiply q[code] * s.
 //
 // Both kernels are HBM-bound streams: the quantizer reads 4 B and writes
 // 0.5 B + 4/64 B per element, the dequantizer the reverse.
@@ -27,62 +34,94 @@ namespace s4 {
 
 namespace {
 
-// Level numerators over 225 and midpoint numerators over 450, rounded once to fp32
-// from double (a host test checks them bit-for-bit against exactly rounded values).
-#define S4_LV(a) ((float)((double)(a) / 225.0))
-#define S4_MP(a, b) ((float)((double)((a) + (b)) / 450.0))
-
-__constant__ float c_levels[16] = {
-    S4_LV(-225), S4_LV(-169), S4_LV(-121), S4_LV(-81), S4_LV(-49), S4_LV(-25), S4_LV(-9), 0.0f,
-    S4_LV(1),    S4_LV(9),    S4_LV(25),   S4_LV(49),  S4_LV(81),  S4_LV(121), S4_LV(169), S4_LV(225)};
-
-constexpr float kMid[15] = {
-    S4_MP(-225, -169), S4_MP(-169, -121), S4_MP(-121, -81), S4_MP(-81, -49), S4_MP(-49, -25),
-    S4_MP(-25, -9),    S4_MP(-9, 0),      S4_MP(0, 1),      S4_MP(1, 9),     S4_MP(9, 25),
-    S4_MP(25, 49),     S4_MP(49, 81),     S4_MP(81, 121),   S4_MP(121, 169), S4_MP(169, 225)};
-
-constexpr float kLevelsHost[16] = {
-    S4_LV(-225), S4_LV(-169), S4_LV(-121), S4_LV(-81), S4_LV(-49), S4_LV(-25), S4_LV(-9), 0.0f,
-    S4_LV(1),    S4_LV(9),    S4_LV(25),   S4_LV(49),  S4_LV(81),  S4_LV(121), S4_LV(169), S4_LV(225)};
-
-// Code lookup without a midpoint scan.  The magnitude's float32 bit pattern, shifted
-// right by 21, is the exponent with the top two mantissa bits: a bucket of width at
-// most 1.25x.  Adjacent midpoints of one sign differ by at least 1.36x, so every
-// bucket over [2^-9, 2) holds at most one midpoint (checked at compile time below)
-// and magnitudes under 2^-9 lie below every midpoint.  Each (sign, bucket) entry
-// stores the code of a magnitude at or below the bucket's midpoint, the code above
-// it, and the midpoint's bit pattern as an unsigned threshold; the result equals the
-// count of midpoints strictly below x_hat for every float32 x_hat, signed zeros and
-// subnormals included.
-constexpr uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
-constexpr int QB_E0 = 118 * 4;   // bucket 0 starts at 2^-9 (biased exponent 118)
-constexpr int QB_N = 40;         // buckets per sign, [2^-9, 2)
-
-constexpr int bucket_of(uint32_t mag) {
-    const int b = (int)(mag >> 21) - QB_E0;
-    return b < 0 ? 0 : (b >= QB_N ? QB_N - 1 : b);
-}
-
-struct QTab {
-    uint32_t thr[2 * QB_N];    // the in-bucket midpoint (as magnitude bits), or all ones
-    uint32_t code[2 * QB_N];   // low nibble: code at or below thr; next nibble: code above
-    int max_per_bucket;
+// Level numerators over DEN, ascending.  Levels and midpoints are rounded once to
+// fp32 from double (a host test checks them bit-for-bit against exactly rounded
+// values).  MB: mantissa bits of the quantizer's bucket key (below).
+struct LinearSquare {
+    static constexpr int ID = SHAMPOO4_CODEBOOK_LINEAR_SQUARE;
+    static constexpr double DEN = 225.0;
+    static constexpr int NUM[16] = {-225, -169, -121, -81, -49, -25, -9, 0, 1, 9, 25, 49, 81, 121, 169, 225};
+    static constexpr int MB = 2;
+};
+struct DynamicTree {
+    static constexpr int ID = SHAMPOO4_CODEBOOK_DYNAMIC_TREE;
+    static constexpr double DEN = 2000.0;
+    static constexpr int NUM[16] = {-1775, -1325, -875, -425, -155, -65, -11, 0,
+                                    11,    65,    155,  425,  875,  1325, 1775, 2000};
+    static constexpr int MB = 3;
 };
 
-constexpr QTab make_qtab() {
-    QTab t{};
+template <class CB> constexpr float level_of(int j) { return (float)((double)CB::NUM[j] / CB::DEN); }
+template <class CB> constexpr float mid_of(int j) {
+    return (float)((double)(CB::NUM[j] + CB::NUM[j + 1]) / (2.0 * CB::DEN));
+}
+
+__constant__ float c_levels[2][16] = {
+    {level_of<LinearSquare>(0), level_of<LinearSquare>(1), level_of<LinearSquare>(2), level_of<LinearSquare>(3),
+     level_of<LinearSquare>(4), level_of<LinearSquare>(5), level_of<LinearSquare>(6), level_of<LinearSquare>(7),
+     level_of<LinearSquare>(8), level_of<LinearSquare>(9), level_of<LinearSquare>(10), level_of<LinearSquare>(11),
+     level_of<LinearSquare>(12), level_of<LinearSquare>(13), level_of<LinearSquare>(14), level_of<LinearSquare>(15)},
+    {level_of<DynamicTree>(0), level_of<DynamicTree>(1), level_of<DynamicTree>(2), level_of<DynamicTree>(3),
+     level_of<DynamicTree>(4), level_of<DynamicTree>(5), level_of<DynamicTree>(6), level_of<DynamicTree>(7),
+     level_of<DynamicTree>(8), level_of<DynamicTree>(9), level_of<DynamicTree>(10), level_of<DynamicTree>(11),
+     level_of<DynamicTree>(12), level_of<DynamicTree>(13), level_of<DynamicTree>(14), level_of<DynamicTree>(15)}};
+
+// Code lookup without a midpoint scan.  The magnitude's float32 bit pattern, shifted
+// right by 23 - MB, is the exponent with the top MB mantissa bits: a bucket of width at
+// most (1 + 2^-MB)x.  Adjacent midpoints of one sign differ by at least 1.36x
+// (linear-square, MB = 2: buckets of 1.25x) or 1.21x (dynamic tree, MB = 3: 1.125x), so
+// every bucket over [2^-9, 2) holds at most one midpoint (checked at compile time
+// below) and magnitudes under 2^-9 lie below every midpoint.  Each (sign, bucket) entry
+// stores the code of a magnitude at or below the bucket's midpoint, the code above it,
+// and the midpoint's bit pattern as an unsigned threshold; the result equals the count
+// of midpoints strictly below x_hat for every float32 x_hat, signed zeros and
+// subnormals included.
+constexpr uint32_t f32_bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+template <class CB>
+struct Buckets {
+    static constexpr int SHIFT = 23 - CB::MB;
+    static constexpr int E0 = 118 << CB::MB;   // bucket 0 starts at 2^-9 (biased exponent 118)
+    static constexpr int N = 10 << CB::MB;     // buckets per sign, [2^-9, 2)
+    static constexpr int bucket_of(uint32_t mag) {
+        const int b = (int)(mag >> SHIFT) - E0;
+        return b < 0 ? 0 : (b >= N ? N - 1 : b);
+    }
+};
+
+template <class CB>
+struct QTab {
+    uint32_t thr[2 * Buckets<CB>::N];    // the in-bucket midpoint (as magnitude bits), or all ones
+    uint32_t code[2 * Buckets<CB>::N];   // low nibble: code at or below thr; next nibble: code above
+    int max_per_bucket;
+    bool mids_in_range;                  // every midpoint magnitude lies in [2^-9, 2)
+};
+
+template <class CB>
+constexpr QTab<CB> make_qtab() {
+    using B = Buckets<CB>;
+    QTab<CB> t{};
     t.max_per_bucket = 0;
+    t.mids_in_range = true;
+    int negatives = 0;
+    for (int j = 0; j < 15; ++j) {
+        const uint32_t mag = f32_bits(mid_of<CB>(j)) & 0x7fffffffu;
+        const int raw = (int)(mag >> B::SHIFT) - B::E0;
+        if (raw < 0 || raw >= B::N) t.mids_in_range = false;
+        if (mid_of<CB>(j) < 0.0f) ++negatives;
+    }
+    if (negatives != 7) t.mids_in_range = false;   // the zero level must be code 7
     for (int s = 0; s < 2; ++s) {
-        for (int b = 0; b < QB_N; ++b) {
-            const uint32_t lo_u = b > 0 ? (uint32_t)(b + QB_E0) << 21 : 0u;
+        for (int b = 0; b < B::N; ++b) {
+            const uint32_t lo_u = b > 0 ? (uint32_t)(b + B::E0) << B::SHIFT : 0u;
             int below = 0, inb = 0;
             uint32_t thr = 0xffffffffu;
             for (int j = 0; j < 15; ++j) {
-                const bool neg = kMid[j] < 0.0f;
+                const bool neg = mid_of<CB>(j) < 0.0f;
                 if (neg != (s == 1)) continue;
-                const uint32_t mag = f32_bits(kMid[j]) & 0x7fffffffu;
+                const uint32_t mag = f32_bits(mid_of<CB>(j)) & 0x7fffffffu;
                 if (mag < lo_u) ++below;
-                if (bucket_of(mag) == b) {
+                if (B::bucket_of(mag) == b) {
                     ++inb;
                     // positive: code rises once x_hat > m; negative: the count of
                     // midpoints below x_hat drops once |x_hat| >= |m|
@@ -91,25 +130,34 @@ constexpr QTab make_qtab() {
             }
             const int lo = s == 0 ? 7 + below : 7 - below;
             const int hi = inb ? (s == 0 ? lo + 1 : lo - 1) : lo;
-            t.thr[s * QB_N + b] = thr;
-            t.code[s * QB_N + b] = (uint32_t)lo | ((uint32_t)hi << 4);
+            t.thr[s * B::N + b] = thr;
+            t.code[s * B::N + b] = (uint32_t)lo | ((uint32_t)hi << 4);
             if (inb > t.max_per_bucket) t.max_per_bucket = inb;
         }
     }
     return t;
 }
 
-constexpr QTab kQTab = make_qtab();
-static_assert(kQTab.max_per_bucket == 1, "a code bucket holds more than one midpoint");
-static_assert(f32_bits(kMid[7]) >> 21 >= QB_E0 && (f32_bits(-kMid[6]) >> 21) >= QB_E0,
-              "a midpoint lies below the first bucket");
+constexpr QTab<LinearSquare> kQTabLS = make_qtab<LinearSquare>();
+constexpr QTab<DynamicTree> kQTabDT = make_qtab<DynamicTree>();
+static_assert(kQTabLS.max_per_bucket == 1 && kQTabDT.max_per_bucket == 1,
+              "a code bucket holds more than one midpoint");
+static_assert(kQTabLS.mids_in_range && kQTabDT.mids_in_range,
+              "a midpoint lies outside the buckets (or the zero level is not code 7)");
 
-__constant__ QTab c_qtab = kQTab;
+__constant__ QTab<LinearSquare> c_qtab_ls = kQTabLS;
+__constant__ QTab<DynamicTree> c_qtab_dt = kQTabDT;
 
+template <class CB> __device__ __forceinline__ const QTab<CB>& qtab();
+template <> __device__ __forceinline__ const QTab<LinearSquare>& qtab<LinearSquare>() { return c_qtab_ls; }
+template <> __device__ __forceinline__ const QTab<DynamicTree>& qtab<DynamicTree>() { return c_qtab_dt; }
+
+template <class CB>
 __device__ __forceinline__ uint32_t code_of(float xh, const uint2* __restrict__ tab) {
+    using B = Buckets<CB>;
     const uint32_t u = __float_as_uint(xh);
     const uint32_t mag = u & 0x7fffffffu;
-    const int b = min(max((int)(mag >> 21) - QB_E0, 0), QB_N - 1) + (int)(u >> 31) * QB_N;
+    const int b = min(max((int)(mag >> B::SHIFT) - B::E0, 0), B::N - 1) + (int)(u >> 31) * B::N;
     const uint2 e = tab[b];
     return mag > e.x ? (e.y >> 4) : (e.y & 15u);
 }
@@ -119,9 +167,10 @@ __device__ __forceinline__ uint32_t code_of(float xh, const uint2* __restrict__ 
 // writes 1 KB contiguous.
 constexpr int DEQ_QUADS = DEQ_TILE / (256 * 4);
 
+template <class CB>
 __device__ __forceinline__ void dequant_item(const CodecDesc& d, int tile) {
     __shared__ float lv[16];
-    if (threadIdx.x < 16) lv[threadIdx.x] = c_levels[threadIdx.x];
+    if (threadIdx.x < 16) lv[threadIdx.x] = c_levels[CB::ID][threadIdx.x];
     __syncthreads();
     const int64_t n = d.n;
     const int64_t nquads = ((n + 63) / 64) * 16;
@@ -156,14 +205,16 @@ __device__ __forceinline__ void dequant_item(const CodecDesc& d, int tile) {
     }
 }
 
+template <class CB>
 __global__ __launch_bounds__(256) void dequant_kernel(const CodecDesc* __restrict__ descs,
                                                       const int* __restrict__ prefix, int ndesc) {
     const int item = find_item(prefix, ndesc, blockIdx.x);
-    dequant_item(descs[item], blockIdx.x - prefix[item]);
+    dequant_item<CB>(descs[item], blockIdx.x - prefix[item]);
 }
 
+template <class CB>
 __global__ __launch_bounds__(256) void dequant_single_kernel(CodecDesc d) {
-    dequant_item(d, blockIdx.x);
+    dequant_item<CB>(d, blockIdx.x);
 }
 
 // Quantization: a lane codes 4 consecutive elements (one 16-byte load), 16 lanes
@@ -171,9 +222,12 @@ __global__ __launch_bounds__(256) void dequant_single_kernel(CodecDesc d) {
 // handles QUANT_QUADS such quads spaced 256 quads apart.
 constexpr int QUANT_QUADS = QUANT_TILE / (256 * 4);
 
+template <class CB>
 __device__ __forceinline__ void quant_item(const CodecDesc& d, int tile, uint32_t* __restrict__ flag) {
-    __shared__ uint2 tab[2 * QB_N];
-    if (threadIdx.x < 2 * QB_N) tab[threadIdx.x] = make_uint2(c_qtab.thr[threadIdx.x], c_qtab.code[threadIdx.x]);
+    constexpr int NT = 2 * Buckets<CB>::N;
+    static_assert(NT <= 256, "one table entry per thread");
+    __shared__ uint2 tab[NT];
+    if (threadIdx.x < NT) tab[threadIdx.x] = make_uint2(qtab<CB>().thr[threadIdx.x], qtab<CB>().code[threadIdx.x]);
     const int64_t n = d.n;
     const int64_t nquads = ((n + 63) / 64) * 16;
     const int64_t q0 = (int64_t)tile * (QUANT_TILE / 4) + threadIdx.x;
@@ -211,7 +265,7 @@ __device__ __forceinline__ void quant_item(const CodecDesc& d, int tile, uint32_
         if (qd < nquads) {
             uint32_t packed = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) packed |= code_of(__fdiv_rn(v[k][e], amax), tab) << (4 * e);
+            for (int e = 0; e < 4; ++e) packed |= code_of<CB>(__fdiv_rn(v[k][e], amax), tab) << (4 * e);
             if (amax == 0.f) packed = 0x7777u;
             reinterpret_cast<uint16_t*>(d.codes_out)[qd] = (uint16_t)packed;
             if ((qd & 15) == 0) d.scales_out[qd >> 4] = amax;
@@ -220,15 +274,17 @@ __device__ __forceinline__ void quant_item(const CodecDesc& d, int tile, uint32_
     if (!finite && flag) flag[0] = 1u;
 }
 
+template <class CB>
 __global__ __launch_bounds__(256) void quant_kernel(const CodecDesc* __restrict__ descs,
                                                     const int* __restrict__ prefix, int ndesc,
                                                     uint32_t* __restrict__ flag) {
     const int item = find_item(prefix, ndesc, blockIdx.x);
-    quant_item(descs[item], blockIdx.x - prefix[item], flag);
+    quant_item<CB>(descs[item], blockIdx.x - prefix[item], flag);
 }
 
+template <class CB>
 __global__ __launch_bounds__(256) void quant_single_kernel(CodecDesc d) {
-    quant_item(d, blockIdx.x, nullptr);
+    quant_item<CB>(d, blockIdx.x, nullptr);
 }
 
 // Copy of codes and scales (root snapshot).
@@ -249,36 +305,56 @@ __global__ __launch_bounds__(256) void codec_copy_kernel(const CodecDesc* __rest
 
 }  // namespace
 
-void host_codebook(float levels[16], float midpoints[15]) {
-    for (int i = 0; i < 16; ++i) levels[i] = kLevelsHost[i];
-    for (int i = 0; i < 15; ++i) midpoints[i] = kMid[i];
+template <class CB>
+void fill_codebook(float levels[16], float midpoints[15]) {
+    for (int i = 0; i < 16; ++i) levels[i] = level_of<CB>(i);
+    for (int i = 0; i < 15; ++i) midpoints[i] = mid_of<CB>(i);
 }
 
-hipError_t launch_dequant(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
+bool host_codebook(int codebook, float levels[16], float midpoints[15]) {
+    if (codebook == LinearSquare::ID) fill_codebook<LinearSquare>(levels, midpoints);
+    else if (codebook == DynamicTree::ID) fill_codebook<DynamicTree>(levels, midpoints);
+    else return false;
+    return true;
+}
+
+hipError_t launch_dequant(int codebook, const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
                           hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    S4_LAUNCH(dequant_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    if (codebook == DynamicTree::ID)
+        S4_LAUNCH(dequant_kernel<DynamicTree>, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    else
+        S4_LAUNCH(dequant_kernel<LinearSquare>, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
     return hipGetLastError();
 }
 
-hipError_t launch_quant(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
+hipError_t launch_quant(int codebook, const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
                         uint32_t* flag, hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    S4_LAUNCH(quant_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc, flag);
+    if (codebook == DynamicTree::ID)
+        S4_LAUNCH(quant_kernel<DynamicTree>, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc, flag);
+    else
+        S4_LAUNCH(quant_kernel<LinearSquare>, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc, flag);
     return hipGetLastError();
 }
 
-hipError_t launch_dequant_single(const CodecDesc& d, hipStream_t stream) {
+hipError_t launch_dequant_single(int codebook, const CodecDesc& d, hipStream_t stream) {
     const int64_t tiles = dequant_tiles(d.n);
     if (tiles <= 0) return hipSuccess;
-    S4_LAUNCH(dequant_single_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, d);
+    if (codebook == DynamicTree::ID)
+        S4_LAUNCH(dequant_single_kernel<DynamicTree>, dim3((unsigned)tiles), dim3(256), 0, stream, d);
+    else
+        S4_LAUNCH(dequant_single_kernel<LinearSquare>, dim3((unsigned)tiles), dim3(256), 0, stream, d);
     return hipGetLastError();
 }
 
-hipError_t launch_quant_single(const CodecDesc& d, hipStream_t stream) {
+hipError_t launch_quant_single(int codebook, const CodecDesc& d, hipStream_t stream) {
     const int64_t tiles = quant_tiles(d.n);
     if (tiles <= 0) return hipSuccess;
-    S4_LAUNCH(quant_single_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, d);
+    if (codebook == DynamicTree::ID)
+        S4_LAUNCH(quant_single_kernel<DynamicTree>, dim3((unsigned)tiles), dim3(256), 0, stream, d);
+    else
+        S4_LAUNCH(quant_single_kernel<LinearSquare>, dim3((unsigned)tiles), dim3(256), 0, stream, d);
     return hipGetLastError();
 }
 

@@ -4,6 +4,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "shampoo4.h"
 
 namespace s4 {
 
@@ -29,15 +30,16 @@ constexpr int COPY_TILE = 8192;    // bytes of codes per workgroup
 // workgroups for n elements (quantization blocks of 64 padded)
 inline int64_t dequant_tiles(int64_t n) { return ((n + 63) / 64 * 64 + DEQ_TILE - 1) / DEQ_TILE; }
 inline int64_t quant_tiles(int64_t n) { return ((n + 63) / 64 * 64 + QUANT_TILE - 1) / QUANT_TILE; }
-hipError_t launch_dequant(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
+// codebook: SHAMPOO4_CODEBOOK_LINEAR_SQUARE or SHAMPOO4_CODEBOOK_DYNAMIC_TREE
+hipError_t launch_dequant(int codebook, const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
                           hipStream_t stream);
-hipError_t launch_quant(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
+hipError_t launch_quant(int codebook, const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
                         uint32_t* flag, hipStream_t stream);
-hipError_t launch_dequant_single(const CodecDesc& d, hipStream_t stream);
-hipError_t launch_quant_single(const CodecDesc& d, hipStream_t stream);
+hipError_t launch_dequant_single(int codebook, const CodecDesc& d, hipStream_t stream);
+hipError_t launch_quant_single(int codebook, const CodecDesc& d, hipStream_t stream);
 hipError_t launch_codec_copy(const CodecDesc* descs, const int* prefix, int ndesc, int ntiles,
                              hipStream_t stream);
-void host_codebook(float levels[16], float midpoints[15]);
+bool host_codebook(int codebook, float levels[16], float midpoints[15]);
 
 // Householder panel factorization, one workgroup per panel.  Panels of height
 // h <= 16 * rows_class (rows_class in {2,4,...,64}) keep the panel in registers;

@@ -104,6 +104,7 @@ struct shampoo4_ctx_s {
     int outer = kOuter;                   // columns whose reflectors update the trailing matrix together
     bool lookahead = false;               // small batches: trailing and Q updates on a second stream
     bool fp32_state = false;              // U kept in float32 (the 32-bit baseline), no codec
+    int codebook = SHAMPOO4_CODEBOOK_LINEAR_SQUARE;   // 4-bit codebook of U and the root
     int n_sync = 0;                       // synchronization events the plan uses
     hipStream_t aux = nullptr;
     std::vector<hipEvent_t> sync_ev;
@@ -260,6 +261,8 @@ struct shampoo4_ctx_s {
     // ---- plan ---------------------------------------------------------------------
     void layout() {
         fp32_state = (cfg.flags & SHAMPOO4_FLAG_FP32_STATE) != 0;
+        codebook = (cfg.flags & SHAMPOO4_FLAG_DT_CODEBOOK) ? SHAMPOO4_CODEBOOK_DYNAMIC_TREE
+                                                           : SHAMPOO4_CODEBOOK_LINEAR_SQUARE;
         use_graphs = (cfg.flags & SHAMPOO4_FLAG_GRAPHS) != 0;
         // Large batches are throughput-bound: reflectors go to the trailing matrix 128
         // columns at a time.  Small ones are bound by the chain of panels and by launch
@@ -893,12 +896,12 @@ struct shampoo4_ctx_s {
                                 io, s);
                 break;
             case K_DEQUANT:
-                e = launch_dequant(reinterpret_cast<const CodecDesc*>(base + L.desc_off), prefix, L.ndesc,
-                                   L.ntiles, s);
+                e = launch_dequant(codebook, reinterpret_cast<const CodecDesc*>(base + L.desc_off), prefix,
+                                   L.ndesc, L.ntiles, s);
                 break;
             case K_QUANT:
-                e = launch_quant(reinterpret_cast<const CodecDesc*>(base + L.desc_off), prefix, L.ndesc,
-                                 L.ntiles, flag, s);
+                e = launch_quant(codebook, reinterpret_cast<const CodecDesc*>(base + L.desc_off), prefix,
+                                 L.ndesc, L.ntiles, flag, s);
                 break;
             case K_COPY:
                 e = launch_codec_copy(reinterpret_cast<const CodecDesc*>(base + L.desc_off), prefix,
@@ -1076,7 +1079,10 @@ shampoo4_status validate_cfg(const shampoo4_config* cfg) {
     if (cfg->bjorck_iters < 0 || cfg->bjorck_iters > 16) return SHAMPOO4_EINVAL;
     if (cfg->power_iters < 1 || cfg->power_iters > 8) return SHAMPOO4_EINVAL;
     if (cfg->flags & ~(SHAMPOO4_FLAG_ROOT_CACHE | SHAMPOO4_FLAG_KEEP_STATE | SHAMPOO4_FLAG_QR_BLOCKED |
-                       SHAMPOO4_FLAG_QR_LOOKAHEAD | SHAMPOO4_FLAG_FP32_STATE | SHAMPOO4_FLAG_GRAPHS))
+                       SHAMPOO4_FLAG_QR_LOOKAHEAD | SHAMPOO4_FLAG_FP32_STATE | SHAMPOO4_FLAG_GRAPHS |
+                       SHAMPOO4_FLAG_DT_CODEBOOK))
+        return SHAMPOO4_EINVAL;
+    if ((cfg->flags & SHAMPOO4_FLAG_DT_CODEBOOK) && (cfg->flags & SHAMPOO4_FLAG_FP32_STATE))
         return SHAMPOO4_EINVAL;
     if ((cfg->flags & SHAMPOO4_FLAG_QR_BLOCKED) && (cfg->flags & SHAMPOO4_FLAG_QR_LOOKAHEAD))
         return SHAMPOO4_EINVAL;
@@ -1337,15 +1343,32 @@ shampoo4_status shampoo4_layout(shampoo4_ctx c, int32_t block, int32_t side, sha
     return SHAMPOO4_OK;
 }
 
-shampoo4_status shampoo4_codebook(float levels[16], float midpoints[15]) {
+shampoo4_status shampoo4_codebook_ex(int32_t codebook, float levels[16], float midpoints[15]) {
     if (!levels || !midpoints) return SHAMPOO4_EINVAL;
-    host_codebook(levels, midpoints);
-    return SHAMPOO4_OK;
+    return host_codebook(codebook, levels, midpoints) ? SHAMPOO4_OK : SHAMPOO4_EINVAL;
+}
+
+shampoo4_status shampoo4_codebook(float levels[16], float midpoints[15]) {
+    return shampoo4_codebook_ex(SHAMPOO4_CODEBOOK_LINEAR_SQUARE, levels, midpoints);
+}
+
+static bool valid_codebook(int32_t codebook) {
+    return codebook == SHAMPOO4_CODEBOOK_LINEAR_SQUARE || codebook == SHAMPOO4_CODEBOOK_DYNAMIC_TREE;
 }
 
 shampoo4_status shampoo4_quantize(const float* x, int64_t n, int32_t qblock, uint8_t* codes, float* scales,
                                   void* stream) {
-    if (qblock != 64 || n < 0) return SHAMPOO4_EINVAL;
+    return shampoo4_quantize_ex(x, n, qblock, SHAMPOO4_CODEBOOK_LINEAR_SQUARE, codes, scales, stream);
+}
+
+shampoo4_status shampoo4_dequantize(const uint8_t* codes, const float* scales, int64_t n, int32_t qblock,
+                                    float* x, void* stream) {
+    return shampoo4_dequantize_ex(codes, scales, n, qblock, SHAMPOO4_CODEBOOK_LINEAR_SQUARE, x, stream);
+}
+
+shampoo4_status shampoo4_quantize_ex(const float* x, int64_t n, int32_t qblock, int32_t codebook, uint8_t* codes,
+                                     float* scales, void* stream) {
+    if (qblock != 64 || n < 0 || !valid_codebook(codebook)) return SHAMPOO4_EINVAL;
     if (n == 0) return SHAMPOO4_OK;
     if (!x || !codes || !scales) return SHAMPOO4_EINVAL;
     if ((reinterpret_cast<uintptr_t>(codes) & 1) || (reinterpret_cast<uintptr_t>(scales) & 3) ||
@@ -1354,12 +1377,12 @@ shampoo4_status shampoo4_quantize(const float* x, int64_t n, int32_t qblock, uin
     CodecDesc d;
     std::memset(&d, 0, sizeof(d));
     d.x_in = x; d.codes_out = codes; d.scales_out = scales; d.n = n;
-    return launch_quant_single(d, as_stream(stream)) == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+    return launch_quant_single(codebook, d, as_stream(stream)) == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
 
-shampoo4_status shampoo4_dequantize(const uint8_t* codes, const float* scales, int64_t n, int32_t qblock,
-                                    float* x, void* stream) {
-    if (qblock != 64 || n < 0) return SHAMPOO4_EINVAL;
+shampoo4_status shampoo4_dequantize_ex(const uint8_t* codes, const float* scales, int64_t n, int32_t qblock,
+                                       int32_t codebook, float* x, void* stream) {
+    if (qblock != 64 || n < 0 || !valid_codebook(codebook)) return SHAMPOO4_EINVAL;
     if (n == 0) return SHAMPOO4_OK;
     if (!x || !codes || !scales) return SHAMPOO4_EINVAL;
     if ((reinterpret_cast<uintptr_t>(codes) & 3) || (reinterpret_cast<uintptr_t>(scales) & 3) ||
@@ -1368,7 +1391,7 @@ shampoo4_status shampoo4_dequantize(const uint8_t* codes, const float* scales, i
     CodecDesc d;
     std::memset(&d, 0, sizeof(d));
     d.codes_in = codes; d.scales_in = scales; d.x_out = x; d.n = n;
-    return launch_dequant_single(d, as_stream(stream)) == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+    return launch_dequant_single(codebook, d, as_stream(stream)) == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
 
 size_t shampoo4_gemm_workspace_bytes(int32_t count) {

@@ -58,6 +58,7 @@ class Shampoo4Config:
     qr_schedule: str = "auto"       # "auto", "blocked" or "lookahead"
     fp32_state: bool = False        # keep U in float32 (the 32-bit baseline) instead of 4-bit codes
     graphs: bool = False            # replay update_stats from a captured HIP graph
+    codebook: str = "ls"            # 4-bit codebook of U: "ls" linear-square, "dt" dynamic tree
 
     def c(self, keep_state: bool = False) -> L.Config:
         flags = (L.FLAG_ROOT_CACHE if self.root_cache else 0) | (L.FLAG_KEEP_STATE if keep_state else 0)
@@ -68,6 +69,7 @@ class Shampoo4Config:
             flags |= L.FLAG_FP32_STATE
         if self.graphs:
             flags |= L.FLAG_GRAPHS
+        flags |= {"ls": 0, "dt": L.FLAG_DT_CODEBOOK}[self.codebook]
         return L.Config(self.beta, self.eps, self.qblock, self.bjorck_iters, self.power_iters, flags)
 
 
@@ -248,31 +250,37 @@ class Shampoo4Blocks:
 
 # -- codec and GEMM in isolation -------------------------------------------------------
 
-def quantize(x: torch.Tensor, qblock: int = 64, stream=None):
+def _codebook_id(codebook: str) -> int:
+    return {"ls": L.CODEBOOK_LINEAR_SQUARE, "dt": L.CODEBOOK_DYNAMIC_TREE}[codebook]
+
+
+def quantize(x: torch.Tensor, qblock: int = 64, stream=None, codebook: str = "ls"):
     _require_gpu_tensor(x, torch.float32, "x")
     x = x.contiguous().view(-1)
     n = x.numel()
     nqb = (n + qblock - 1) // qblock
     codes = torch.empty(nqb * qblock // 2, dtype=torch.uint8, device=x.device)
     scales = torch.empty(nqb, dtype=torch.float32, device=x.device)
-    L.check(L.lib().shampoo4_quantize(_ptr(x), n, qblock, _ptr(codes), _ptr(scales), _stream_ptr(stream)),
-            "shampoo4_quantize")
+    L.check(L.lib().shampoo4_quantize_ex(_ptr(x), n, qblock, _codebook_id(codebook), _ptr(codes), _ptr(scales),
+                                         _stream_ptr(stream)), "shampoo4_quantize_ex")
     return codes, scales
 
 
-def dequantize(codes: torch.Tensor, scales: torch.Tensor, n: int, qblock: int = 64, stream=None):
+def dequantize(codes: torch.Tensor, scales: torch.Tensor, n: int, qblock: int = 64, stream=None,
+               codebook: str = "ls"):
     _require_gpu_tensor(codes, torch.uint8, "codes")
     _require_gpu_tensor(scales, torch.float32, "scales")
     x = torch.empty(n, dtype=torch.float32, device=codes.device)
-    L.check(L.lib().shampoo4_dequantize(_ptr(codes.contiguous()), _ptr(scales.contiguous()), n, qblock,
-                                        _ptr(x), _stream_ptr(stream)), "shampoo4_dequantize")
+    L.check(L.lib().shampoo4_dequantize_ex(_ptr(codes.contiguous()), _ptr(scales.contiguous()), n, qblock,
+                                           _codebook_id(codebook), _ptr(x), _stream_ptr(stream)),
+            "shampoo4_dequantize_ex")
     return x
 
 
-def codebook():
+def codebook(name: str = "ls"):
     lv = (ctypes.c_float * 16)()
     mp = (ctypes.c_float * 15)()
-    L.check(L.lib().shampoo4_codebook(lv, mp), "shampoo4_codebook")
+    L.check(L.lib().shampoo4_codebook_ex(_codebook_id(name), lv, mp), "shampoo4_codebook_ex")
     return list(lv), list(mp)
 
 

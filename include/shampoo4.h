@@ -99,6 +99,23 @@ typedef enum {
    launch instead of one host call each.  The io upload stays a separate copy before the
    launch.  While kernel timing is on, and if a capture fails, calls launch eagerly. */
 #define SHAMPOO4_FLAG_GRAPHS 32u
+/* Code the eigenvector matrices (U and the root snapshot) with the 4-bit dynamic tree
+   codebook instead of linear-square: the alternative the abstract of "4-bit Shampoo ..."
+   compares linear-square with (it reports linear-square slightly ahead).  Every stage is
+   unchanged but the codec's level table.  EINVAL together with FP32_STATE. */
+#define SHAMPOO4_FLAG_DT_CODEBOOK 64u
+
+/* 4-bit codebooks (16 levels, ascending, code = index; the zero level is code 7).
+   LINEAR_SQUARE: sign(t) t^2 on t = -1 + 2j/15 with the j = 7 level exactly 0; times 225:
+     -225 -169 -121 -81 -49 -25 -9 0 1 9 25 49 81 121 169 225.
+   DYNAMIC_TREE (defined by the 8-bit optimizers paper the pages cite; not on the pages):
+     a sign bit and three magnitude bits whose leading zeros E are a base-10 exponent,
+     then an indicator bit and 2 - E linear fraction bits, the midpoints of equal bins of
+     [0.1, 1] times 10^-E; zero; and +1 in place of the negative zero, so that a block's
+     maximum is exact.  Times 2000:
+     -1775 -1325 -875 -425 -155 -65 -11 0 11 65 155 425 875 1325 1775 2000. */
+#define SHAMPOO4_CODEBOOK_LINEAR_SQUARE 0
+#define SHAMPOO4_CODEBOOK_DYNAMIC_TREE 1
 
 typedef struct {
     int32_t m, n;             /* block shape: G is [m, n]; side L has order m, side R order n */
@@ -234,6 +251,15 @@ SHAMPOO4_API shampoo4_status shampoo4_dequantize(const uint8_t* codes, const flo
 /* The float32 codebook the kernels use (host copy): 16 levels (ascending) and the
  * 15 decision midpoints.  Host only. */
 SHAMPOO4_API shampoo4_status shampoo4_codebook(float levels[16], float midpoints[15]);
+
+/* The same three calls for a named codebook (SHAMPOO4_CODEBOOK_*; EINVAL otherwise).
+ * shampoo4_quantize / shampoo4_dequantize / shampoo4_codebook are these with
+ * SHAMPOO4_CODEBOOK_LINEAR_SQUARE. */
+SHAMPOO4_API shampoo4_status shampoo4_quantize_ex(const float* x, int64_t n, int32_t qblock, int32_t codebook,
+                                                  uint8_t* codes, float* scales, void* stream);
+SHAMPOO4_API shampoo4_status shampoo4_dequantize_ex(const uint8_t* codes, const float* scales, int64_t n,
+                                                    int32_t qblock, int32_t codebook, float* x, void* stream);
+SHAMPOO4_API shampoo4_status shampoo4_codebook_ex(int32_t codebook, float levels[16], float midpoints[15]);
 
 /* Device workspace bytes shampoo4_gemm_batched needs for `count` products. */
 SHAMPOO4_API size_t shampoo4_gemm_workspace_bytes(int32_t count);

@@ -1,7 +1,8 @@
 """The abstract's ablation on the GPU kernels ("4-bit Shampoo for Memory-Efficient Network
-Training": 4-bit eigenvector matrix versus 4-bit preconditioner, and the effect of
-rectifying orthogonality).  The eigenvector matrix and the factor are quantized and
-dequantized by the library's codec, and the Bjorck rectification runs on its MFMA GEMM;
+Training": 4-bit eigenvector matrix versus 4-bit preconditioner, the effect of rectifying
+orthogonality, and linear-square versus dynamic tree codes).  The eigenvector matrix and
+the factor are quantized and dequantized by the library's codec, and the Bjorck
+rectification runs on its MFMA GEMM;
 only the float64 eigendecompositions (truth, and the inverse root of the dequantized
 factor) run on the host.  The errors must agree with the oracle's (relative 1e-3: the
 GEMM rectifies in float32) and reproduce the claim."""
@@ -49,9 +50,15 @@ def test_ablation_on_gpu_kernels(workload):
     L4 = dequantize(c, s, p * p).view(p, p)
     torch.cuda.synchronize()
     errs["precond4"] = ab.rel_err(ab.inverse_root(L4.cpu().numpy().astype(np.float64), eps), truth)
+    # the same 4-bit eigenvectors with the dynamic tree codebook
+    c, s = quantize(to_dev(U.astype(np.float32)), codebook="dt")
+    V = _gpu_bjorck(dequantize(c, s, p * p, codebook="dt").view(p, p), 1)
+    torch.cuda.synchronize()
+    errs["eigvec4_dt"] = ab.rel_err(ab.root_from(V.cpu().numpy(), lam.astype(np.float32), eps), truth)
     ref = ab.ablation(L, eps, 1)
     announce(f"ablation {workload}: gpu {errs} oracle {ref}")
     for k, v in errs.items():
         assert abs(v - ref[k]) <= 1e-3 * ref[k], (workload, k, v, ref[k])
     assert errs["eigvec4"] < errs["precond4"]
     assert errs["eigvec4"] < errs["eigvec4_no_rectify"]
+    assert errs["eigvec4"] < errs["eigvec4_dt"]       # linear-square ahead of dynamic tree

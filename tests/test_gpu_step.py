@@ -29,17 +29,17 @@ TOL = 1e-3
 
 
 def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power_iters=1,
-                        root_interval=1, root_cache=False, label="", qr="auto"):
+                        root_interval=1, root_cache=False, label="", qr="auto", codebook="ls"):
     from bit_quantized_shampoo_amd import Shampoo4Blocks, Shampoo4Config
     cfg = Shampoo4Config(beta=beta, eps=eps, bjorck_iters=k, power_iters=power_iters,
-                         root_cache=root_cache, qr_schedule=qr)
+                         root_cache=root_cache, qr_schedule=qr, codebook=codebook)
     announce(f"step parity {label}: init {shapes}")
     blocks = Shampoo4Blocks(shapes, cfg)
     torch.cuda.synchronize()
     # initial state equals the oracle's
     for b, (m, n) in enumerate(shapes):
         for s, p in ((0, m), (1, n)):
-            ref = o.initial_side(p)
+            ref = o.initial_side(p, 64, codebook)
             got = blocks.side_state(b, s)
             assert np.array_equal(got["codes"], ref.codes)
             assert np.array_equal(got["scales"], ref.scales)
@@ -57,7 +57,7 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
             for s, p in ((0, m), (1, n)):
                 st = before[b][s]
                 Gs_side = o.side_gradient(Gs[b], s)
-                V = o.rectified_eigenvectors(st["codes"], st["scales"], p, k)
+                V = o.rectified_eigenvectors(st["codes"], st["scales"], p, k, 64, codebook)
                 Lt_ref = o.statistics(V, st["lam"], Gs_side, beta)
                 Lt_gpu = blocks.view(b, s, 17).cpu().numpy().astype(np.float64)
                 e_stat = rel_fro(Lt_gpu, Lt_ref)
@@ -72,7 +72,7 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
                 assert e_rec <= TOL, (label, t, b, s, "Q diag(lam) Q^T", e_rec)
                 assert e_lam <= TOL, (label, t, b, s, "eigenvalues", e_lam)
                 assert np.allclose(Q_gpu.T @ Q_gpu, np.eye(p), atol=1e-4), (label, t, b, s, "orthonormal Q")
-                c_ref, s_ref = codec.quantize_matrix(Q_gpu32)
+                c_ref, s_ref = codec.quantize_matrix(Q_gpu32, 64, codebook)
                 assert np.array_equal(after["codes"], c_ref), (label, t, b, s, "codes")
                 assert np.array_equal(after["scales"].view(np.uint32), s_ref.view(np.uint32))
                 worst["stat"] = max(worst["stat"], e_stat)
@@ -94,8 +94,8 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
         torch.cuda.synchronize()
         for b, (m, n) in enumerate(shapes):
             sl, sr = blocks.side_state(b, 0), blocks.side_state(b, 1)
-            VL = o.rectified_eigenvectors(sl["root_codes"], sl["root_scales"], m, k)
-            VR = o.rectified_eigenvectors(sr["root_codes"], sr["root_scales"], n, k)
+            VL = o.rectified_eigenvectors(sl["root_codes"], sl["root_scales"], m, k, 64, codebook)
+            VR = o.rectified_eigenvectors(sr["root_codes"], sr["root_scales"], n, k, 64, codebook)
             P_ref = o.precondition_block(VL, sl["d"], VR, sr["d"], Gs[b])
             e_p = rel_fro(outs[b].cpu().numpy(), P_ref)
             assert e_p <= TOL, (label, t, b, "P", e_p)
@@ -170,6 +170,37 @@ def test_cnn_batch_two_steps():
     del sel
     _run_teacher_forced(shapes, grads, 2, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters, label="cnn_batch",
                         qr="blocked")
+
+
+def test_dynamic_tree_single_64x32():
+    """The dynamic tree codebook: every stage as with linear-square, codes bit-exact
+    through the dynamic tree codec."""
+    require_gpu()
+    wl = get_workload("single_64x32")
+    _run_teacher_forced(wl.shapes, wl.gradients, 8, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
+                        root_interval=2, root_cache=True, label="single_64x32 dt", codebook="dt")
+
+
+@pytest.mark.parametrize("qr", ["auto", "blocked"])
+def test_dynamic_tree_ragged(qr):
+    require_gpu()
+    shapes = [(40, 72), (1, 1), (130, 65), (257, 300)]
+    rng = np.random.default_rng(77)
+    scales = [(10.0 ** rng.uniform(-1, 1, (m, 1))) for m, n in shapes]
+
+    def grads(t):
+        r = np.random.default_rng([t, 77])
+        return [(r.standard_normal((m, n)) * sc).astype(np.float32) for (m, n), sc in zip(shapes, scales)]
+
+    _run_teacher_forced(shapes, grads, 3, k=1, root_interval=1, label=f"ragged dt qr={qr}", qr=qr,
+                        codebook="dt")
+
+
+def test_dynamic_tree_single_1024():
+    require_gpu()
+    wl = get_workload("single_1024")
+    _run_teacher_forced(wl.shapes, wl.gradients, 3, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
+                        root_interval=2, label="single_1024 dt", codebook="dt")
 
 
 def test_update_is_deterministic_and_resumable():

@@ -37,13 +37,24 @@ def test_library_exports_every_declared_symbol():
     assert lib.shampoo4_abi_version() == 1
 
 
-def test_codebook_matches_oracle_bitwise():
+@pytest.mark.parametrize("name", ["ls", "dt"])
+def test_codebook_matches_oracle_bitwise(name):
     _lib()
     from bit_quantized_shampoo_amd.shampoo4 import codebook
     from oracle import codec
-    lv, mp = codebook()
-    assert np.array_equal(np.array(lv, np.float32).view(np.uint32), codec.LEVELS.view(np.uint32))
-    assert np.array_equal(np.array(mp, np.float32).view(np.uint32), codec.MIDPOINTS.view(np.uint32))
+    lv, mp = codebook(name)
+    assert np.array_equal(np.array(lv, np.float32).view(np.uint32), codec.levels(name).view(np.uint32))
+    assert np.array_equal(np.array(mp, np.float32).view(np.uint32), codec.midpoints(name).view(np.uint32))
+
+
+def test_unknown_codebook_rejected():
+    lib = _lib()
+    lv = (ctypes.c_float * 16)()
+    mp = (ctypes.c_float * 15)()
+    assert lib.shampoo4_codebook_ex(2, lv, mp) == L.EINVAL
+    assert lib.shampoo4_quantize_ex(None, 5, 64, 7, None, None, None) == L.EINVAL
+    assert lib.shampoo4_dequantize_ex(None, None, 5, 64, -1, None, None) == L.EINVAL
+    assert lib.shampoo4_dequantize_ex(None, None, 0, 64, L.CODEBOOK_DYNAMIC_TREE, None, None) == L.OK
 
 
 def _plan(shapes, **kw):
@@ -79,7 +90,9 @@ def test_plan_sizes():
     ([(4, 4)], {"k": -1}, L.EINVAL),
     ([(4, 4)], {"k": 17}, L.EINVAL),
     ([(4, 4)], {"pi": 0}, L.EINVAL),
-    ([(4, 4)], {"flags": 64}, L.EINVAL),
+    ([(4, 4)], {"flags": 128}, L.EINVAL),
+    ([(4, 4)], {"flags": L.FLAG_DT_CODEBOOK}, L.OK),
+    ([(4, 4)], {"flags": L.FLAG_DT_CODEBOOK | L.FLAG_FP32_STATE}, L.EINVAL),
     ([(4, 4)], {"flags": L.FLAG_GRAPHS}, L.OK),
     ([(4, 4)], {"flags": L.FLAG_FP32_STATE}, L.OK),
     ([(4, 4)], {"flags": L.FLAG_QR_BLOCKED | L.FLAG_QR_LOOKAHEAD}, L.EINVAL),
