@@ -38,7 +38,7 @@ def log(msg: str):
 # kernel families of the roofline: timing-report families -> (kernel-name test, source file)
 FAMILIES = {
     "gemm": (lambda n: "gemm_kernel" in n, "gemm.hip"),
-    "qr_panel": (lambda n: "panel_" in n and "_kernel" in n, "qr.hip"),
+    "qr_panel": (lambda n: ("panel_" in n and "_kernel" in n) or "qr_step_kernel" in n, "qr.hip"),
     "quant": (lambda n: "quant_kernel" in n and "dequant" not in n, "codec.hip"),
     "dequant": (lambda n: "dequant_kernel" in n, "codec.hip"),
     "graft": (lambda n: "graft_" in n and "_kernel" in n, "graft.hip"),
@@ -353,8 +353,10 @@ def main():
     kernels = {
         "gemm": ("mfma", "gemm_kernel (fp32 v_mfma_f32_32x32x2_f32): every matrix product of the step; "
                  "algorithmic flops = 2 M N K of the products each launch is given"),
-        "qr_panel": ("alu", "panel_*_kernel: Householder factorization of one 32-column panel per workgroup "
-                     "(one workgroup per side: a dependent chain of reflector steps, latency-bound)"),
+        "qr_panel": ("alu", "panel_*_kernel / qr_step_kernel: Householder factorization of one 32-column "
+                     "panel per workgroup (one workgroup per side: a dependent chain of reflector steps, "
+                     "latency-bound); in the fused QR step of small batches the same launch carries the "
+                     "previous panel's compact-WY products on other workgroups (their flops included)"),
         "quant": ("hbm", "quant_kernel: 4.5625 B per element (fp32 in, nibble + 1/16 scale out)"),
         "dequant": ("hbm", "dequant_kernel: 4.5625 B per element (nibble + scale in, fp32 out)"),
         "graft": ("hbm", "graft_norms_kernel + graft_apply_kernel: per element G and P read (Adam: moments "

@@ -117,6 +117,35 @@ struct PanelDesc {
 };
 static_assert(sizeof(PanelDesc) == 64, "PanelDesc layout");
 
+// One panel of a fused QR step: the panel, and the reflector block of the panel before it,
+// which the workgroup first applies to this panel's columns (nbp == 0: none).  The panel
+// writes V (pd.V) and its 32 x 32 T (row-major) instead of Y.
+struct StepPanelDesc {
+    PanelDesc pd;
+    const float* Vp;          // previous panel's V, top row pd.c0 - nbp, pitch pd.vld
+    const float* Tp;          // previous panel's T
+    float* T;                 // this panel's T
+    int32_t hp, nbp;          // rows of Vp (pd.h + nbp) and its reflector count
+};
+static_assert(sizeof(StepPanelDesc) == 96, "StepPanelDesc layout");
+
+// One slab of a fused QR step: a reflector block (V: h rows, 32 columns of which the first
+// nb are reflectors, pitch vld; T: 32 x 32) applied as M <- M - V (T^T (V^T M)) to
+// `count` <= 32 columns of P (role 0; M points at row r0 of the first column, h rows) or as
+// M <- M - ((M V) T) V^T to `count` <= 32 rows of Q (role 1; M points at column r0 of the
+// first row, h columns).
+struct SlabDesc {
+    float* M;
+    const float* V;
+    const float* T;
+    int64_t ld;               // of M
+    int64_t vld;
+    int32_t role, h;
+    int32_t count, pad0;
+    int64_t pad1;
+};
+static_assert(sizeof(SlabDesc) == 64, "SlabDesc layout");
+
 // One block of the grafting epilogue: rows of G, P (io table entry `blk`) and of W, M, V
 // (graft io table entry `blk`) in tiles of `rows` rows; `parts` receives two partial
 // sums per tile (||d_graft||^2 and ||P||^2 over the tile).

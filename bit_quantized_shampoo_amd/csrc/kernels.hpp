@@ -48,6 +48,13 @@ constexpr int PANEL_THREADS = 512;
 constexpr int PANEL_LDS_MAX_ROWS = 1024;
 int panel_rows_class(int h);
 size_t panel_lds_bytes(bool in_regs, int max_h);
+// Fused QR step: npanel panel workgroups (each first applying the previous panel's
+// reflectors to its own columns, then factoring them) and nslab slab workgroups (the
+// previous panel's reflectors on trailing columns of P and on rows of Q) in one launch.
+// rows_class: register class of the tallest panel (2 when npanel == 0).
+size_t qr_step_lds_bytes(int max_h);
+hipError_t launch_qr_step(int rows_class, const StepPanelDesc* panels, int npanel, const SlabDesc* slabs,
+                          int nslab, int max_h, hipStream_t stream);
 hipError_t launch_panel(int rows_class, const PanelDesc* descs, int ndesc, int max_h,
                         hipStream_t stream);
 

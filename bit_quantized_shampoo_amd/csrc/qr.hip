@@ -51,13 +51,14 @@ constexpr int PART = PW * NWAVE;             // one partials buffer: [32 columns
 // LDS layout (floats)
 constexpr int OFF_PART = 0;                      // [2][32][NWAVE]
 constexpr int OFF_ROWJ = OFF_PART + 2 * PART;    // [2][32]
-constexpr int OFF_SALL = OFF_ROWJ + 64;          // [32][32] s vector of step j
-constexpr int OFF_TAU = OFF_SALL + PW * PW;      // [32]
+constexpr int OFF_SALL = OFF_ROWJ + 64;          // [32 columns][33] s_j[c] of step j at c * 33 + j
+constexpr int OFF_TAU = OFF_SALL + PW * 33;      // [32]
 constexpr int OFF_T = OFF_TAU + PW;              // [32][33]
 constexpr int OFF_RED = OFF_T + PW * 33;         // [NWAVE]
 constexpr int OFF_RD = OFF_RED + NWAVE;          // [32] R diagonal (written out after the loop)
 constexpr int OFF_COL = ((OFF_RD + PW + 3) / 4) * 4;  // [NSLOT][64] column j+1 of each half-wave's rows
 constexpr int OFF_VS = OFF_COL + NSLOT * 64;     // [hpad][33] V staging (register variant)
+constexpr int OFF_VS_T12 = OFF_COL;              // [16][16] scratch of build_T (after the loop)
 static_assert(NWAVE == 8, "partials are read as two 16-byte vectors");
 
 struct Refl {
@@ -115,29 +116,69 @@ __device__ __forceinline__ float panel_max(float mx, float* smem, int lane, int 
     return m;
 }
 
-// T (upper triangular, nb x nb) from the kept s vectors and taus: one lane per row.
-// Row c has zeros left of the diagonal, so T[c][j] = -tau_j sum_{l < j} T[c][l] s_l
-// for c < j needs no lower bound on l, and the same sum is 0 for c > j.
-__device__ __forceinline__ void build_T(float* smem, int nb, int tid) {
-    if (tid < PW) {
-        const int c = tid;
-        float trow[PW];
+// T (upper triangular, nb x nb) from the kept s vectors and taus, into LDS at OFF_T (pitch
+// 33), by the whole workgroup (two barriers inside).  T[c][j] = -tau_j sum_{c <= l < j} T[c][l]
+// s_j[l], T[j][j] = tau_j, with s_j[l] = v_j^T v_l at smem[OFF_SALL + l * 33 + j].  Blocked in
+// halves: the two diagonal 16 x 16 blocks run in parallel (one lane per row, right-looking:
+// once T[c][l] is known it is added into the running sums of every later column, so each step's
+// dependent work is one multiply and one fused multiply-add), then T12 = -T11 (V1^T V2) T22.
+// Entries of s for steps >= nb were never written: in the recurrence they only reach running
+// sums of columns >= nb, whose T entries are selected to zero, and in the off-diagonal product
+// they are masked.
+__device__ __forceinline__ void build_T_diag(float* smem, int nb, int tid) {
+    const int lane = tid & 63;
+    if (tid < 64 && (lane & 31) < 16) {
+        const int blk = lane >> 5, c = lane & 15;
+        const int b0 = 16 * blk, row = b0 + c;
+        float acc[16], trow[16];
 #pragma unroll
-        for (int l = 0; l < PW; ++l) trow[l] = 0.f;
+        for (int j = 0; j < 16; ++j) acc[j] = 0.f;
 #pragma unroll
-        for (int j = 0; j < PW; ++j) {
-            if (j < nb) {
-                const float tj = smem[OFF_TAU + j];
-                const float* sj = smem + OFF_SALL + j * PW;
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int ll = 0; ll < 16; ++ll) {
+            const int l = b0 + ll;
+            const float tl = smem[OFF_TAU + l];
+            float t = (c == ll) ? tl : ((c < ll) ? -tl * acc[ll] : 0.f);
+            t = (l < nb) ? t : 0.f;
+            trow[ll] = t;
+            const float* sl = smem + OFF_SALL + l * 33 + b0;
 #pragma unroll
-                for (int l = 0; l < j; ++l) acc[l & 3] = fmaf(trow[l], sj[l], acc[l & 3]);
-                trow[j] = (c == j) ? tj : -tj * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
-            }
+            for (int j = ll + 1; j < 16; ++j) acc[j] = fmaf(t, sl[j], acc[j]);
         }
 #pragma unroll
-        for (int l = 0; l < PW; ++l) smem[OFF_T + c * 33 + l] = trow[l];
+        for (int ll = 0; ll < 16; ++ll) {
+            smem[OFF_T + row * 33 + b0 + ll] = trow[ll];
+            if (blk == 1) smem[OFF_T + row * 33 + ll] = 0.f;        // below the diagonal blocks
+        }
     }
+}
+
+// The off-diagonal block, after build_T_diag and a barrier (one more barrier inside).
+__device__ __forceinline__ void build_T_offdiag(float* smem, int nb, int tid) {
+    // X = S12 T22 (16 x 16, kept in the T12 slot's registers): S12[l][m] = s_{16+m}[l]
+    float x = 0.f;
+    const int xr = (tid >> 4) & 15, xc = tid & 15;
+    if (tid < 256) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const uint32_t ok = 16 + m < nb ? 0xffffffffu : 0u;
+            const float s12 = __uint_as_float(__float_as_uint(smem[OFF_SALL + xr * 33 + 16 + m]) & ok);
+            x = fmaf(s12, smem[OFF_T + (16 + m) * 33 + 16 + xc], x);
+        }
+        smem[OFF_VS_T12 + xr * 16 + xc] = x;
+    }
+    __syncthreads();
+    if (tid < 256) {   // T12 = -T11 X
+        float t12 = 0.f;
+#pragma unroll
+        for (int l = 0; l < 16; ++l) t12 = fmaf(smem[OFF_T + xr * 33 + l], smem[OFF_VS_T12 + l * 16 + xc], t12);
+        smem[OFF_T + xr * 33 + 16 + xc] = -t12;
+    }
+}
+
+__device__ __forceinline__ void build_T(float* smem, int nb, int tid) {
+    build_T_diag(smem, nb, tid);
+    __syncthreads();
+    build_T_offdiag(smem, nb, tid);
 }
 
 // Y = V T for rows [0, h): V rows come from `vsrc` (pitch vpitch floats), T from LDS,
@@ -183,10 +224,246 @@ __device__ __forceinline__ float half_bcast(float v, int byte_addr) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(byte_addr, __float_as_int(v)));
 }
 
-template <int NR>
-__global__ __launch_bounds__(PANEL_THREADS) void panel_reg_kernel(const PanelDesc* __restrict__ descs) {
-    extern __shared__ float smem[];
-    const PanelDesc d = descs[blockIdx.x];
+// ---- Compact-WY application of a reflector block on the matrix cores -------------------
+// A block of nb <= 32 reflectors (explicit V: h rows, 32 columns of which those beyond nb
+// are zero, pitch vld; T: 32 x 32 upper triangular) multiplies to I - V T V^T.  The fused QR
+// step applies it from the left to columns of P (M <- M - V (T^T (V^T M)): the trailing
+// update) and from the right to rows of Q (M <- M - ((M V) T) V^T: the forward accumulation
+// of Q).  The long products are 32 x 32 x K contractions on v_mfma_f32_32x32x2_f32: the 8
+// waves split K and add their 32 x 32 partial results in LDS in a fixed order; T is applied
+// to the 32 x 32 result on the vector units; then each wave updates its share of 32-row (or
+// 32-column) blocks.  Inside a 32-deep contraction, lane half hh takes k = ks + 16 hh, so a
+// lane reads 16 consecutive floats of a V row.
+
+constexpr int WY_PART = 8 * 32 * 36;   // floats of per-wave partial products (or V tiles) in LDS
+
+__device__ __forceinline__ int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+
+__device__ __forceinline__ float masked(float v, uint32_t m) { return __uint_as_float(__float_as_uint(v) & m); }
+
+// Operands of one 32-deep block of a contraction, held while the next block's loads fly.
+struct WyBuf {
+    float a[16], b[16];
+};
+
+// Items first, first + 8, ... < n of one wave, two deep: the loads of item i + 8 are issued
+// before the matrix-core work of item i.
+template <class Load, class Use>
+__device__ __forceinline__ void wy_pipeline(int first, int n, Load load, Use use) {
+    WyBuf b0, b1;
+    int it = first;
+    if (it < n) load(it, b0);
+    for (; it < n; it += 16) {
+        const bool more = it + 8 < n;
+        if (more) load(it + 8, b1);
+        use(it, b0);
+        if (more) {
+            if (it + 16 < n) load(it + 16, b0);
+            use(it + 8, b1);
+        }
+    }
+}
+
+// out[m * 32 + n] = sum over the 8 waves of their accumulators (fixed order).
+__device__ __forceinline__ void wy_reduce(const floatx16& acc, float* part, float* out, int tid) {
+    const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[wv * 1024 + acc_row(r, hh) * 32 + l32] = acc[r];
+    __syncthreads();
+    for (int e = tid; e < 1024; e += PANEL_THREADS) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) s += part[w * 1024 + e];
+        out[e] = s;
+    }
+    __syncthreads();
+}
+
+// Sixteen consecutive floats of a V row (16-byte aligned: V rows have pitch 32).
+__device__ __forceinline__ void load_vrow16(const float* p, float (&v)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const floatx4 t = ldg(reinterpret_cast<const floatx4*>(p) + q);
+        v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
+    }
+}
+
+// W[i][c] = sum_{r < h} Y[r][i] M[r][c] for c < ncols (W row-major 32 x 32 in LDS); Y is a
+// 32-column block (V in the fused step).
+// Wave w takes the 32-row blocks w, w + 8, ...; in a block, lane half hh reads rows
+// ks + 16 hh (one coalesced row per half-wave and step).
+__device__ __forceinline__ void wy_left_product(const float* __restrict__ Y, int64_t vld, const float* __restrict__ M,
+                                int64_t ld, int h, int ncols, float* part, float* W, int tid) {
+    const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+    const int cc = l32 < ncols ? l32 : ncols - 1;
+    const uint32_t cm = l32 < ncols ? 0xffffffffu : 0u;
+    floatx16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    auto load = [&](int bk, WyBuf& B) {
+        const int rb = 32 * bk + 16 * hh;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const int rr = rb + ks < h ? rb + ks : h - 1;
+            B.a[ks] = ldg(Y + (int64_t)rr * vld + l32);
+            B.b[ks] = ldg(M + (int64_t)rr * ld + cc);
+        }
+    };
+    auto use = [&](int bk, const WyBuf& B) {
+        const int rb = 32 * bk + 16 * hh;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const uint32_t rm = rb + ks < h ? 0xffffffffu : 0u;
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(masked(B.a[ks], rm), masked(B.b[ks], rm & cm), acc, 0, 0, 0);
+        }
+    };
+    wy_pipeline(wv, (h + 31) / 32, load, use);
+    wy_reduce(acc, part, W, tid);
+}
+
+// M[r][c] -= sum_i V[r][i] W[i][c] for rows r < h and columns c < ncols.
+__device__ __forceinline__ void wy_update_rows(const float* __restrict__ V, int64_t vld, float* M, int64_t ld,
+                                               int h, int ncols, const float* W, int tid) {
+    const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+    const int cc = l32 < ncols ? l32 : ncols - 1;
+    float wb[16];                                     // B operand: W[ks + 16 hh][l32]
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) wb[ks] = W[(16 * hh + ks) * 32 + l32];
+    auto load = [&](int bk, WyBuf& B) {              // a: the block of M (C operand), b: V row
+        const int rb = 32 * bk;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = rb + acc_row(r, hh);
+            B.a[r] = ldg(M + (int64_t)(row < h ? row : h - 1) * ld + cc);
+        }
+        const int vr = rb + l32 < h ? rb + l32 : h - 1;
+        load_vrow16(V + (int64_t)vr * vld + 16 * hh, B.b);   // A operand: V[rb + l32][ks + 16 hh]
+    };
+    auto use = [&](int bk, const WyBuf& B) {
+        const int rb = 32 * bk;
+        floatx16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = B.a[r];
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(-B.b[ks], wb[ks], acc, 0, 0, 0);
+        if (l32 < ncols) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = rb + acc_row(r, hh);
+                if (row < h) stg(M + (int64_t)row * ld + l32, acc[r]);
+            }
+        }
+    };
+    wy_pipeline(wv, (h + 31) / 32, load, use);
+}
+
+// Z[m][i] = sum_{k < h} M[m][k] Y[k][i] for rows m < nrows of M (Z row-major 32 x 32 in LDS);
+// Y is a 32-column block (V in the fused step).
+// Wave w takes the 32-column chunks w, w + 8, ...
+__device__ __forceinline__ void wy_right_product(const float* __restrict__ M, int64_t ld, int nrows, const float* __restrict__ Y,
+                                 int64_t vld, int h, float* part, float* Z, int tid) {
+    const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+    const int mr = l32 < nrows ? l32 : nrows - 1;
+    const uint32_t rmask = l32 < nrows ? 0xffffffffu : 0u;
+    floatx16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    auto load = [&](int t, WyBuf& B) {
+        const int kb = 32 * t + 16 * hh;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const int k = kb + ks < h ? kb + ks : h - 1;
+            B.a[ks] = ldg(M + (int64_t)mr * ld + k);    // A operand: M[l32][k]
+            B.b[ks] = ldg(Y + (int64_t)k * vld + l32);  // B operand: Y[k][l32]
+        }
+    };
+    auto use = [&](int t, const WyBuf& B) {
+        const int kb = 32 * t + 16 * hh;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+            const uint32_t km = kb + ks < h ? 0xffffffffu : 0u;
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(masked(B.a[ks], km & rmask), masked(B.b[ks], km), acc, 0, 0, 0);
+        }
+    };
+    wy_pipeline(wv, (h + 31) / 32, load, use);
+    wy_reduce(acc, part, Z, tid);
+}
+
+// M[m][c] -= sum_i Z[m][i] V[c][i] for rows m < nrows and columns c < h.
+__device__ __forceinline__ void wy_update_cols(float* M, int64_t ld, int nrows, const float* __restrict__ V, int64_t vld, int h,
+                               const float* Z, int tid) {
+    const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+    float za[16];                                     // A operand: -Z[l32][ks + 16 hh]
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) za[ks] = -Z[l32 * 32 + 16 * hh + ks];
+    auto load = [&](int t, WyBuf& B) {               // a: the block of M (C operand), b: V row
+        const int col = 32 * t + l32 < h ? 32 * t + l32 : h - 1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = acc_row(r, hh);
+            B.a[r] = ldg(M + (int64_t)(row < nrows ? row : nrows - 1) * ld + col);
+        }
+        load_vrow16(V + (int64_t)col * vld + 16 * hh, B.b);  // B operand: V[32 t + l32][ks + 16 hh]
+    };
+    auto use = [&](int t, const WyBuf& B) {
+        const int cb = 32 * t;
+        floatx16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = B.a[r];
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(za[ks], B.b[ks], acc, 0, 0, 0);
+        if (cb + l32 < h) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = acc_row(r, hh);
+                if (row < nrows) stg(M + (int64_t)row * ld + cb + l32, acc[r]);
+            }
+        }
+    };
+    wy_pipeline(wv, (h + 31) / 32, load, use);
+}
+
+// T (32 x 32, row-major in global memory) into LDS at Tl with pitch 33.
+__device__ __forceinline__ void load_T(const float* __restrict__ T, float* Tl, int tid) {
+    for (int e = tid; e < PW * PW; e += PANEL_THREADS) Tl[(e >> 5) * 33 + (e & 31)] = ldg(T + e);
+}
+
+// X (32 x 32, row-major in LDS) <- T^T X (LEFT) or X T, T in LDS with pitch 33; fixed order.
+template <bool LEFT>
+__device__ __forceinline__ void wy_apply_t(const float* Tl, float* X, int tid) {
+    float o[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int e = tid + u * PANEL_THREADS;
+        const int row = e >> 5, col = e & 31;
+        float acc = 0.f;
+#pragma unroll
+        for (int l = 0; l < PW; ++l)
+            acc = LEFT ? fmaf(Tl[l * 33 + row], X[l * 32 + col], acc) : fmaf(X[row * 32 + l], Tl[l * 33 + col], acc);
+        o[u] = acc;
+    }
+    __syncthreads();
+    X[tid] = o[0];
+    X[tid + PANEL_THREADS] = o[1];
+    __syncthreads();
+}
+
+// Extra arguments of the panel in a fused QR step: the previous panel's block (Vp, Tp, nbp
+// reflectors, nbp = 0: none) and where this panel's T goes.
+struct PanelExtra {
+    const float* Vp;
+    const float* Tp;
+    float* T;
+    int nbp;
+};
+
+// The register-resident panel factorization of one workgroup.
+// MODE 0: a panel of the blocked / look-ahead QR: writes V and Y = V T.
+// MODE 1: a panel of a fused QR step: writes V and T (the consumers apply T themselves).
+// MODE 2: as 1, after first applying the previous panel's block I - Vp Tp Vp^T (transposed,
+//         from the left) to the panel's columns, in registers.
+template <int NR, int MODE>
+__device__ __forceinline__ void panel_body(const PanelDesc& d, const PanelExtra& ex, float* smem) {
     const int h = d.h, nb = d.nb;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -203,6 +480,7 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_reg_kernel(const PanelDes
     // and the value masked with an AND (a select on the loaded value would become a
     // branch around each load, with a wait for it inside).
     float x[NR], xc[NR];
+    float pa[MODE == 2 ? NR : 1], pa_top[2], pb_top[2];   // MODE 2: operands of the previous block
     {
         const int cc = c < nb ? c : nb - 1;
         const uint32_t cmask = c < nb ? 0xffffffffu : 0u;
@@ -210,12 +488,97 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_reg_kernel(const PanelDes
         for (int i = 0; i < NR; ++i) {
             const int r = slot + NSLOT * i;
             const int rr = r < h ? r : h - 1;
-            x[i] = Ap[(int64_t)rr * d.ld + cc];
+            x[i] = ldg(Ap + (int64_t)rr * d.ld + cc);
+        }
+        if constexpr (MODE == 2) {
+            // the previous block's operands, issued together with the panel's own loads
+            const int nbp = ex.nbp;
+            const float* Atop = d.A + (int64_t)(d.c0 - nbp) * d.ld + d.c0;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int tr = slot + NSLOT * t;
+                const int trc = tr < nbp ? tr : nbp - 1;
+                pa_top[t] = ldg(ex.Vp + (int64_t)trc * d.vld + c);
+                pb_top[t] = ldg(Atop + (int64_t)trc * d.ld + cc);
+            }
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int r = slot + NSLOT * i;
+                const int rr = r < h ? r : h - 1;
+                pa[i] = ldg(ex.Vp + (int64_t)(nbp + rr) * d.vld + c);
+            }
         }
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const uint32_t m = (slot + NSLOT * i < h) ? cmask : 0u;
             x[i] = __uint_as_float(__float_as_uint(x[i]) & m);
+        }
+    }
+    if constexpr (MODE == 2) {
+        // Previous block on this panel's columns: x <- x - Vp (Tp^T (Vp^T A)), where the
+        // contraction Vp^T A runs over the block's rows: its nbp rows above the panel and
+        // the panel's own rows, which this lane holds in x.  MFMA i of a wave takes the
+        // rows of x[i] of its two half-waves, so x[i] itself is the B operand; the update
+        // takes x[16 vb .. 16 vb + 15] as its accumulator, the A operand being the V rows
+        // that the accumulator layout assigns to each lane.
+        const int hh = lane >> 5;
+        const int nbp = ex.nbp;
+        load_T(ex.Tp, smem + OFF_T, tid);
+        const uint32_t cmask = c < nb ? 0xffffffffu : 0u;
+        floatx16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t m = slot + NSLOT * t < nbp ? 0xffffffffu : 0u;
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(masked(pa_top[t], m), masked(pb_top[t], m & cmask), acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const uint32_t m = slot + NSLOT * i < h ? 0xffffffffu : 0u;
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(masked(pa[i], m), x[i], acc, 0, 0, 0);
+        }
+        constexpr int NVB = NR >= 16 ? NR / 16 : 1;
+        // accumulator row m of this lane's A operand: m = c = 8 q + 4 hq + e
+        const int q = c >> 3, hq = (c >> 2) & 1, e4 = c & 3;
+        wy_reduce(acc, smem + OFF_VS, smem + OFF_SALL, tid);
+        wy_apply_t<true>(smem + OFF_T, smem + OFF_SALL, tid);
+        float wb[16];                                 // B operand: W[ks + 16 hh][c]
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) wb[ks] = smem[OFF_SALL + (16 * hh + ks) * 32 + c];
+        // The update's A operand is the V rows this wave already holds in pa (lane c, half
+        // hh: row of x[i], column c); a per-wave LDS tile (32 rows of pitch 36) turns them
+        // into the rows of 16 consecutive V columns each lane needs.
+        float* tile = smem + OFF_VS + wv * 32 * 36;
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+            const int ra = 2 * wv + hq + NSLOT * (16 * vb + 4 * q + e4);
+            const uint32_t am = ra < h ? 0xffffffffu : 0u;
+#pragma unroll
+            for (int il = 0; il < 16; ++il)
+                if (16 * vb + il < NR) tile[(2 * il + hh) * 36 + c] = pa[(16 * vb + il) % NR];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float va[16];
+            const float* trow_p = tile + (2 * (4 * q + e4) + hq) * 36 + 16 * hh;
+#pragma unroll
+            for (int t4 = 0; t4 < 4; ++t4) {
+                const floatx4 v4 = *reinterpret_cast<const floatx4*>(trow_p + 4 * t4);
+                va[4 * t4] = v4[0]; va[4 * t4 + 1] = v4[1]; va[4 * t4 + 2] = v4[2]; va[4 * t4 + 3] = v4[3];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            floatx16 o;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[r] = (16 * vb + r < NR) ? x[(16 * vb + r) % NR] : 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks)
+                o = __builtin_amdgcn_mfma_f32_32x32x2f32(masked(-va[ks], am), wb[ks], o, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (16 * vb + r < NR) x[16 * vb + r] = o[r];
         }
     }
     {
@@ -254,7 +617,7 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_reg_kernel(const PanelDes
         const Refl R = reflector(alpha, dj);
         const float sv = (c < nb && c != j) ? R.sc * (dc - R.beta * ajc) : 0.f;
         if (slot == 0) {
-            smem[OFF_SALL + j * PW + c] = sv;
+            smem[OFF_SALL + c * 33 + j] = sv;
             if (c == 0) {
                 smem[OFF_TAU + j] = R.tau;
                 smem[OFF_RD + j] = R.beta;   // no global store inside the loop
@@ -328,25 +691,87 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_reg_kernel(const PanelDes
     }
 
     if (tid < nb) d.rdiag[d.c0 + tid] = smem[OFF_RD + tid];
-    // explicit V to global and to LDS (rows padded to 32 with zeros)
-    float* Vs = smem + OFF_VS;
     float* Vt = d.V + (int64_t)d.zrows * d.vld;
-    float* Yt = d.Y + (int64_t)d.zrows * d.vld;
-    const int hpad = (h + 31) & ~31;
+    if constexpr (MODE == 0) {
+        // explicit V to global and to LDS (rows padded to 32 with zeros), then Y = V T
+        float* Vs = smem + OFF_VS;
+        float* Yt = d.Y + (int64_t)d.zrows * d.vld;
+        const int hpad = (h + 31) & ~31;
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        const int r = slot + NSLOT * i;
-        if (r < hpad) {
-            float v = 0.f;
-            if (r < h && c < nb) v = (r > c) ? x[i] : (r == c ? 1.f : 0.f);
-            Vs[r * 33 + c] = v;
-            if (r < h) Vt[(int64_t)r * d.vld + c] = v;
+        for (int i = 0; i < NR; ++i) {
+            const int r = slot + NSLOT * i;
+            if (r < hpad) {
+                float v = 0.f;
+                if (r < h && c < nb) v = (r > c) ? x[i] : (r == c ? 1.f : 0.f);
+                Vs[r * 33 + c] = v;
+                if (r < h) Vt[(int64_t)r * d.vld + c] = v;
+            }
         }
+        build_T(smem, nb, tid);
+        zero_above(d, tid);
+        __syncthreads();
+        form_Y(Vs, 33, smem, Yt, d.vld, h, tid);
+    } else {
+        // explicit V and T to global; the other waves write their V rows while wave 0
+        // builds the diagonal blocks of T
+        auto write_v = [&]() {
+#pragma unroll
+            for (int i = 0; i < NR; ++i) {
+                const int r = slot + NSLOT * i;
+                if (r < h) {
+                    float v = 0.f;
+                    if (c < nb) v = (r > c) ? x[i] : (r == c ? 1.f : 0.f);
+                    stg(Vt + (int64_t)r * d.vld + c, v);
+                }
+            }
+        };
+        if (wv != 0) write_v();
+        build_T_diag(smem, nb, tid);
+        if (wv == 0) write_v();
+        __syncthreads();
+        build_T_offdiag(smem, nb, tid);
+        __syncthreads();
+        for (int e = tid; e < PW * PW; e += PANEL_THREADS) stg(ex.T + e, smem[OFF_T + (e >> 5) * 33 + (e & 31)]);
     }
-    build_T(smem, nb, tid);
-    zero_above(d, tid);
-    __syncthreads();
-    form_Y(Vs, 33, smem, Yt, d.vld, h, tid);
+}
+
+template <int NR>
+__global__ __launch_bounds__(PANEL_THREADS) void panel_reg_kernel(const PanelDesc* __restrict__ descs) {
+    extern __shared__ float smem[];
+    const PanelDesc d = descs[blockIdx.x];
+    const PanelExtra ex{nullptr, nullptr, nullptr, 0};
+    panel_body<NR, 0>(d, ex, smem);
+}
+
+// One launch of the fused QR step.  Blocks [0, npanel) factor panels (after applying the
+// previous panel's reflectors to their columns in registers); the rest apply the previous
+// panel's reflectors to 32 trailing columns of P or 32 rows of Q.  The two kinds touch
+// disjoint data: a panel's own columns are excluded from the trailing slabs.
+template <int NR>
+__global__ __launch_bounds__(PANEL_THREADS) void qr_step_kernel(const StepPanelDesc* __restrict__ panels, int npanel,
+                                                                const SlabDesc* __restrict__ slabs) {
+    extern __shared__ float smem[];
+    const int tid = threadIdx.x;
+    if ((int)blockIdx.x < npanel) {
+        const StepPanelDesc sp = panels[blockIdx.x];
+        const PanelExtra ex{sp.Vp, sp.Tp, sp.T, sp.nbp};
+        if (sp.nbp > 0)
+            panel_body<NR, 2>(sp.pd, ex, smem);
+        else
+            panel_body<NR, 1>(sp.pd, ex, smem);
+        return;
+    }
+    const SlabDesc s = slabs[blockIdx.x - npanel];
+    load_T(s.T, smem + OFF_T, tid);
+    if (s.role == 0) {
+        wy_left_product(s.V, s.vld, s.M, s.ld, s.h, s.count, smem + OFF_VS, smem + OFF_SALL, tid);
+        wy_apply_t<true>(smem + OFF_T, smem + OFF_SALL, tid);
+        wy_update_rows(s.V, s.vld, s.M, s.ld, s.h, s.count, smem + OFF_SALL, tid);
+    } else {
+        wy_right_product(s.M, s.ld, s.count, s.V, s.vld, s.h, smem + OFF_VS, smem + OFF_SALL, tid);
+        wy_apply_t<false>(smem + OFF_T, smem + OFF_SALL, tid);
+        wy_update_cols(s.M, s.ld, s.count, s.V, s.vld, s.h, smem + OFF_SALL, tid);
+    }
 }
 
 __global__ __launch_bounds__(PANEL_THREADS) void panel_global_kernel(const PanelDesc* __restrict__ descs) {
@@ -396,7 +821,7 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_global_kernel(const Panel
         const Refl R = reflector(alpha, dj);
         const float sv = (c < nb && c != j) ? R.sc * (dc - R.beta * ajc) : 0.f;
         if (slot == 0) {
-            smem[OFF_SALL + j * PW + c] = sv;
+            smem[OFF_SALL + c * 33 + j] = sv;
             if (c == 0) {
                 smem[OFF_TAU + j] = R.tau;
                 smem[OFF_RD + j] = R.beta;   // no global store inside the loop
@@ -452,7 +877,39 @@ hipError_t launch_reg(const PanelDesc* descs, int ndesc, int max_h, hipStream_t 
     return hipGetLastError();
 }
 
+template <int NR>
+hipError_t launch_step(const StepPanelDesc* panels, int npanel, const SlabDesc* slabs, int nslab, int max_h,
+                       hipStream_t stream) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&qr_step_kernel<NR>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)qr_step_lds_bytes(NSLOT * NR < PANEL_LDS_MAX_ROWS ? NSLOT * NR : PANEL_LDS_MAX_ROWS));
+    if (attr != hipSuccess) return attr;
+    S4_LAUNCH(qr_step_kernel<NR>, dim3(npanel + nslab), dim3(PANEL_THREADS), qr_step_lds_bytes(max_h), stream,
+              panels, npanel, slabs);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+size_t qr_step_lds_bytes(int) {
+    // the fused panel keeps V in registers and writes it to global directly; LDS holds the
+    // fixed panel area and the partial products of the block applications
+    return (size_t)(OFF_VS + WY_PART) * sizeof(float);
+}
+
+hipError_t launch_qr_step(int rows_class, const StepPanelDesc* panels, int npanel, const SlabDesc* slabs,
+                          int nslab, int max_h, hipStream_t stream) {
+    if (npanel + nslab <= 0) return hipSuccess;
+    switch (rows_class) {
+        case 2: return launch_step<2>(panels, npanel, slabs, nslab, max_h, stream);
+        case 4: return launch_step<4>(panels, npanel, slabs, nslab, max_h, stream);
+        case 8: return launch_step<8>(panels, npanel, slabs, nslab, max_h, stream);
+        case 16: return launch_step<16>(panels, npanel, slabs, nslab, max_h, stream);
+        case 32: return launch_step<32>(panels, npanel, slabs, nslab, max_h, stream);
+        case 64: return launch_step<64>(panels, npanel, slabs, nslab, max_h, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 int panel_rows_class(int h) {
     if (h > PANEL_LDS_MAX_ROWS) return 0;

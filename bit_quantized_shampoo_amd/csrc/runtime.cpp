@@ -45,14 +45,15 @@ const char* kFamilyNames[FAM_N] = {"gemm_bjorck", "gemm_stats", "gemm_power", "g
 
 enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT,
             K_RECORD, K_WAIT, K_GRAFT_NORMS, K_GRAFT_APPLY, K_COPYF, K_NEWTON_NORM, K_NEWTON_SCALE,
-            K_NEWTON_ELEM };
+            K_NEWTON_ELEM, K_QRSTEP };
 
 struct Launch {
     Kind kind = K_GEMM;
     int cfg = 0;
-    int mode = 0;        // GEMM: shared transpose flags or GEMM_MODE_MIXED; panel: rows class
+    int mode = 0;        // GEMM: shared transpose flags or GEMM_MODE_MIXED; panel, QR step: rows class
     int fam = FAM_ELEMENTWISE;
-    size_t desc_off = 0, prefix_off = 0;   // offsets inside the descriptor region
+    size_t desc_off = 0, prefix_off = 0;   // offsets inside the descriptor region (QR step: the
+                                           // panel table and the slab table)
     int ndesc = 0, ntiles = 0, max_h = 0;
     int strm = 0;        // 0: the caller's stream, 1: the context's second stream
     bool vec = false;    // GEMM: 16-byte operand loads (io operands: also checked per call)
@@ -70,7 +71,7 @@ struct Side {
     size_t codes = 0, scales = 0, lam = 0, rcodes = 0, rscales = 0, d = 0;
     // workspace offsets
     size_t Vs = 0, Vr = 0, Tmp = 0, Wg = 0, Lt = 0, Pm = 0, Qm = 0, Vb = 0, Yb = 0, Z = 0, W = 0, Mb = 0,
-           Z2 = 0, rdiag = 0;
+           Z2 = 0, rdiag = 0, Tb = 0;
     std::vector<size_t> outer_rows;   // row offset of outer block o inside Vb / Yb (pitch = outer width)
 };
 
@@ -103,6 +104,7 @@ struct shampoo4_ctx_s {
     Seq qr_join;                          // second stream's work joined back (look-ahead plans)
     int outer = kOuter;                   // columns whose reflectors update the trailing matrix together
     bool lookahead = false;               // small batches: trailing and Q updates on a second stream
+    bool fused = false;                   // small batches: one launch per panel (QR step kernel)
     bool fp32_state = false;              // U kept in float32 (the 32-bit baseline), no codec
     int codebook = SHAMPOO4_CODEBOOK_LINEAR_SQUARE;   // 4-bit codebook of U and the root
     int n_sync = 0;                       // synchronization events the plan uses
@@ -324,6 +326,7 @@ struct shampoo4_ctx_s {
                 S.Mb = ws_take((size_t)kMaxSplit * outer * kPanel * 4);  // split-K slabs of V^T Y
                 S.Z2 = ws_take((size_t)kMaxSplit * kPanel * kPanel * 4); // look-ahead Y^T A
                 S.rdiag = ws_take(p * 4);
+                S.Tb = ws_take((size_t)((p + kPanel - 1) / kPanel) * kPanel * kPanel * 4);   // fused QR: T per panel
             }
             X1[b] = ws_take((size_t)shapes[b].m * shapes[b].n * 4);
             X2[b] = ws_take((size_t)shapes[b].m * shapes[b].n * 4);
@@ -593,6 +596,98 @@ struct shampoo4_ctx_s {
         }
     }
 
+    // Fused QR steps (panel-wide blocks, one launch per panel index k): the workgroup of
+    // panel k first applies panel k-1's reflectors to its own 32 columns and then factors
+    // them, while in the same launch other workgroups apply panel k-1's reflectors to the
+    // trailing columns beyond panel k (32 at a time) and to Q (32 rows at a time).  A last
+    // launch applies each side's final panel to Q.  The chain of launches is the chain of
+    // panels; the matrix products ride along instead of following each panel.
+    void build_qr_fused() {
+        qr_steps.assign(max_panels + 1, Seq{});
+        qr_join.clear();
+        for (int k = 0; k <= max_panels; ++k) {
+            std::vector<StepPanelDesc> pds;
+            std::vector<SlabDesc> sds;
+            int max_h = 0;
+            double flops = 0, bytes = 0;
+            for (auto& S : sides) {
+                const int p = S.p;
+                float* Pm = wsf(S.Pm);
+                float* Qm = wsf(S.Qm);
+                auto vblock = [&](int panel) { return wsf(S.Vb) + S.outer_rows[panel] * kPanel; };
+                auto tblock = [&](int panel) { return wsf(S.Tb) + (size_t)panel * kPanel * kPanel; };
+                const int c0 = k * kPanel;
+                if (c0 < p) {                                   // panel k
+                    StepPanelDesc sp;
+                    std::memset(&sp, 0, sizeof(sp));
+                    PanelDesc& pd = sp.pd;
+                    pd.A = Pm;
+                    pd.V = vblock(k);
+                    pd.Y = nullptr;
+                    sp.T = tblock(k);
+                    pd.rdiag = wsf(S.rdiag);
+                    pd.ld = p;
+                    pd.vld = kPanel;
+                    pd.c0 = c0;
+                    pd.h = p - c0;
+                    pd.nb = std::min(kPanel, p - c0);
+                    pd.zrows = 0;
+                    if (k > 0) {
+                        sp.Vp = vblock(k - 1);
+                        sp.Tp = tblock(k - 1);
+                        sp.nbp = kPanel;
+                        sp.hp = pd.h + kPanel;
+                        flops += 4.0 * sp.hp * kPanel * pd.nb + 4.0 * kPanel * kPanel * pd.nb;
+                        bytes += 4.0 * (2.0 * sp.hp * kPanel + (double)kPanel * pd.nb + kPanel * kPanel);
+                    }
+                    pds.push_back(sp);
+                    max_h = std::max(max_h, pd.h);
+                    flops += panel_flops(pd.h, pd.nb);
+                    bytes += 4.0 * (double)pd.h * pd.nb * 3;
+                }
+                const int r0 = (k - 1) * kPanel;
+                if (k > 0 && r0 < p) {                          // panel k-1 on P and on Q
+                    const int h = p - r0, nbk = std::min(kPanel, h);
+                    const float* V = vblock(k - 1);
+                    const float* T = tblock(k - 1);
+                    for (int cs = c0 + kPanel; cs < p; cs += kPanel) {
+                        SlabDesc sd;
+                        std::memset(&sd, 0, sizeof(sd));
+                        sd.M = Pm + (int64_t)r0 * p + cs;
+                        sd.V = V; sd.T = T; sd.ld = p; sd.vld = kPanel;
+                        sd.role = 0; sd.h = h; sd.count = std::min(kPanel, p - cs);
+                        sds.push_back(sd);
+                        flops += 4.0 * h * nbk * sd.count;
+                        bytes += 4.0 * h * (2.0 * kPanel + 2.0 * sd.count);
+                    }
+                    for (int q0 = 0; q0 < p; q0 += kPanel) {
+                        SlabDesc sd;
+                        std::memset(&sd, 0, sizeof(sd));
+                        sd.M = Qm + (int64_t)q0 * p + r0;
+                        sd.V = V; sd.T = T; sd.ld = p; sd.vld = kPanel;
+                        sd.role = 1; sd.h = h; sd.count = std::min(kPanel, p - q0);
+                        sds.push_back(sd);
+                        flops += 4.0 * h * nbk * sd.count;
+                        bytes += 4.0 * h * (2.0 * kPanel + 2.0 * sd.count);
+                    }
+                }
+            }
+            if (pds.empty() && sds.empty()) continue;
+            Launch L;
+            L.kind = K_QRSTEP;
+            L.fam = FAM_PANEL;
+            L.mode = pds.empty() ? 2 : panel_rows_class(max_h);
+            L.max_h = max_h;
+            L.ndesc = (int)pds.size();
+            L.ntiles = (int)(pds.size() + sds.size());
+            L.desc_off = blob_put(pds.data(), pds.size() * sizeof(StepPanelDesc));
+            L.prefix_off = blob_put(sds.data(), sds.size() * sizeof(SlabDesc));
+            L.flops = flops;
+            L.bytes = bytes;
+            qr_steps[k].push_back(L);
+        }
+    }
+
     // Panel-wide reflector blocks with look-ahead.  The caller's stream runs the chain
     // of panels: panel k, then H_k applied to panel k+1's columns only.  The second
     // stream applies H_k to the columns beyond and accumulates Q; panel k+1's own
@@ -730,7 +825,16 @@ struct shampoo4_ctx_s {
             power_next = make_gemm(pn, FAM_GEMM_POWER);
         }
 
-        if (lookahead) build_qr_lookahead(); else build_qr_blocked();
+        {   // panel-wide blocks on one stream run as fused QR steps when every panel fits
+            // the register-resident kernel (and the device's LDS)
+            int pmax = 0;
+            for (auto& sh : shapes) pmax = std::max(pmax, std::max(sh.m, sh.n));
+            fused = outer == kPanel && !lookahead && pmax <= PANEL_LDS_MAX_ROWS &&
+                    qr_step_lds_bytes(pmax) <= lds_limit;
+        }
+        if (lookahead) build_qr_lookahead();
+        else if (fused) build_qr_fused();
+        else build_qr_blocked();
         {
             std::vector<VecDesc> qi, rr, rt;
             std::vector<int> tqi, trr, trt;
@@ -911,6 +1015,11 @@ struct shampoo4_ctx_s {
                 e = launch_panel(L.mode, reinterpret_cast<const PanelDesc*>(base + L.desc_off), L.ndesc,
                                  L.max_h, s);
                 break;
+            case K_QRSTEP:
+                e = launch_qr_step(L.mode, reinterpret_cast<const StepPanelDesc*>(base + L.desc_off), L.ndesc,
+                                   reinterpret_cast<const SlabDesc*>(base + L.prefix_off), L.ntiles - L.ndesc,
+                                   L.max_h, s);
+                break;
             case K_RAYLEIGH:
                 e = launch_rayleigh_reduce(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix,
                                            L.ndesc, L.ntiles, flag, s);
@@ -1027,7 +1136,7 @@ struct shampoo4_ctx_s {
         for (int it = 0; it < cfg.power_iters && e == hipSuccess; ++it) {
             e = run(it == 0 ? power_first[var] : power_next, s);
             if (e == hipSuccess) e = run(qinit, s);
-            for (int p = 0; p < max_panels && e == hipSuccess; ++p) e = run(qr_steps[p], s);
+            for (size_t p = 0; p < qr_steps.size() && e == hipSuccess; ++p) e = run(qr_steps[p], s);
             if (e == hipSuccess) e = run(qr_join, s);
             if (e == hipSuccess) e = run(sign, s);
         }
