@@ -42,10 +42,13 @@ hipError_t launch_codec_copy(const CodecDesc* descs, const int* prefix, int ndes
 bool host_codebook(int codebook, float levels[16], float midpoints[15]);
 
 // Householder panel factorization, one workgroup per panel.  Panels of height
-// h <= 16 * rows_class (rows_class in {2,4,...,64}) keep the panel in registers;
-// rows_class 0 works on taller panels in place in global memory.
+// h <= 16 * rows_class (rows_class from PANEL_CLASSES: rows per lane) keep the panel in
+// registers; rows_class 0 works on taller panels in place in global memory.
 constexpr int PANEL_THREADS = 512;
 constexpr int PANEL_LDS_MAX_ROWS = 1024;
+constexpr int PANEL_NCLASS = 12;
+constexpr int PANEL_CLASSES[PANEL_NCLASS] = {2, 4, 8, 12, 16, 20, 24, 32, 40, 48, 56, 64};
+#define S4_PANEL_CLASSES(X) X(2) X(4) X(8) X(12) X(16) X(20) X(24) X(32) X(40) X(48) X(56) X(64)
 int panel_rows_class(int h);
 size_t panel_lds_bytes(bool in_regs, int max_h);
 // Fused QR step: npanel panel workgroups (each first applying the previous panel's

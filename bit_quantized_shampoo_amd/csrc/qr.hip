@@ -538,7 +538,7 @@ __device__ __forceinline__ void panel_body(const PanelDesc& d, const PanelExtra&
             const uint32_t m = slot + NSLOT * i < h ? 0xffffffffu : 0u;
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(masked(pa[i], m), x[i], acc, 0, 0, 0);
         }
-        constexpr int NVB = NR >= 16 ? NR / 16 : 1;
+        constexpr int NVB = (NR + 15) / 16;
         // accumulator row m of this lane's A operand: m = c = 8 q + 4 hq + e
         const int q = c >> 3, hq = (c >> 2) & 1, e4 = c & 3;
         wy_reduce(acc, smem + OFF_VS, smem + OFF_SALL, tid);
@@ -901,21 +901,18 @@ hipError_t launch_qr_step(int rows_class, const StepPanelDesc* panels, int npane
                           int nslab, int max_h, hipStream_t stream) {
     if (npanel + nslab <= 0) return hipSuccess;
     switch (rows_class) {
-        case 2: return launch_step<2>(panels, npanel, slabs, nslab, max_h, stream);
-        case 4: return launch_step<4>(panels, npanel, slabs, nslab, max_h, stream);
-        case 8: return launch_step<8>(panels, npanel, slabs, nslab, max_h, stream);
-        case 16: return launch_step<16>(panels, npanel, slabs, nslab, max_h, stream);
-        case 32: return launch_step<32>(panels, npanel, slabs, nslab, max_h, stream);
-        case 64: return launch_step<64>(panels, npanel, slabs, nslab, max_h, stream);
+#define S4_CASE(N) case N: return launch_step<N>(panels, npanel, slabs, nslab, max_h, stream);
+        S4_PANEL_CLASSES(S4_CASE)
+#undef S4_CASE
         default: return hipErrorInvalidValue;
     }
 }
 
 int panel_rows_class(int h) {
     if (h > PANEL_LDS_MAX_ROWS) return 0;
-    int nr = 2;
-    while (NSLOT * nr < h) nr *= 2;
-    return nr;
+    for (int i = 0; i < PANEL_NCLASS; ++i)
+        if (NSLOT * PANEL_CLASSES[i] >= h) return PANEL_CLASSES[i];
+    return 0;
 }
 
 size_t panel_lds_bytes(bool in_regs, int max_h) {
@@ -928,12 +925,9 @@ hipError_t launch_panel(int rows_class, const PanelDesc* descs, int ndesc, int m
                         hipStream_t stream) {
     if (ndesc <= 0) return hipSuccess;
     switch (rows_class) {
-        case 2: return launch_reg<2>(descs, ndesc, max_h, stream);
-        case 4: return launch_reg<4>(descs, ndesc, max_h, stream);
-        case 8: return launch_reg<8>(descs, ndesc, max_h, stream);
-        case 16: return launch_reg<16>(descs, ndesc, max_h, stream);
-        case 32: return launch_reg<32>(descs, ndesc, max_h, stream);
-        case 64: return launch_reg<64>(descs, ndesc, max_h, stream);
+#define S4_CASE(N) case N: return launch_reg<N>(descs, ndesc, max_h, stream);
+        S4_PANEL_CLASSES(S4_CASE)
+#undef S4_CASE
         default: break;
     }
     const size_t lds = panel_lds_bytes(false, max_h);

@@ -437,17 +437,17 @@ struct shampoo4_ctx_s {
         int cls = panel_rows_class(pd.h);
         if (cls > 0 && panel_lds_bytes(true, pd.h) > lds_limit) cls = 0;
         int bucket = 0;
-        while (cls > 0 && (2 << bucket) < cls) ++bucket;
-        bucket = cls > 0 ? bucket + 1 : 0;
+        for (int i = 0; cls > 0 && i < PANEL_NCLASS; ++i)
+            if (PANEL_CLASSES[i] == cls) bucket = i + 1;
         byc[bucket].push_back(pd);
         maxh[bucket] = std::max(maxh[bucket], pd.h);
     }
     void panel_launches(Seq& st, std::vector<std::vector<PanelDesc>>& byc, const std::vector<int>& maxh) {
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b <= PANEL_NCLASS; ++b) {
             if (byc[b].empty()) continue;
             std::vector<int> ones(byc[b].size(), 1);
             Launch L = make_items(K_PANEL, byc[b], ones);
-            L.mode = b == 0 ? 0 : (1 << b);
+            L.mode = b == 0 ? 0 : PANEL_CLASSES[b - 1];
             L.max_h = maxh[b];
             L.ntiles = (int)byc[b].size();
             for (const auto& pd : byc[b]) {
@@ -489,8 +489,8 @@ struct shampoo4_ctx_s {
         qr_join.clear();
         for (int sidx = 0; sidx < max_panels; ++sidx) {
             // panels bucketed by register class (0 = in place in global memory)
-            std::vector<std::vector<PanelDesc>> byc(8);
-            std::vector<int> maxh(8, 0);
+            std::vector<std::vector<PanelDesc>> byc(PANEL_NCLASS + 1);
+            std::vector<int> maxh(PANEL_NCLASS + 1, 0);
             std::vector<GemmItem> in1, in2, out1, out2;
             // split-K factors: chosen per launch so that a batch too small to fill the
             // GPU still spreads its long-K (K = panel height) products
@@ -699,8 +699,8 @@ struct shampoo4_ctx_s {
         const int evA = 0, evR = max_panels, evEnd = 2 * max_panels;
         n_sync = 2 * max_panels + 1;
         for (int sidx = 0; sidx < max_panels; ++sidx) {
-            std::vector<std::vector<PanelDesc>> byc(8);
-            std::vector<int> maxh(8, 0);
+            std::vector<std::vector<PanelDesc>> byc(PANEL_NCLASS + 1);
+            std::vector<int> maxh(PANEL_NCLASS + 1, 0);
             std::vector<GemmItem> la1, la2, r1, r2, q1, q2;
             long tla = 0, trest = 0;
             int kmin = 1 << 30;
