@@ -71,7 +71,7 @@ struct Side {
     size_t codes = 0, scales = 0, lam = 0, rcodes = 0, rscales = 0, d = 0;
     // workspace offsets
     size_t Vs = 0, Vr = 0, Tmp = 0, Wg = 0, Lt = 0, Pm = 0, Qm = 0, Vb = 0, Yb = 0, Z = 0, W = 0, Mb = 0,
-           Z2 = 0, rdiag = 0, Tb = 0;
+           Z2 = 0, rdiag = 0, Tb = 0, Rt = 0;
     std::vector<size_t> outer_rows;   // row offset of outer block o inside Vb / Yb (pitch = outer width)
 };
 
@@ -118,6 +118,7 @@ struct shampoo4_ctx_s {
     hipGraphExec_t stats_graph[2] = {};
     Seq qinit, sign, ray_gemm, rayleigh, quant, root_d, root_copy;
     Seq pre[4];
+    Seq root_mat, pre_cached[2];        // ROOT_CACHE: root matrices, then two products per block
     Seq graft_seq[2];                    // per graft mode (bytes differ): norms, apply
     GraftParams graft_prm{};
     float newton_eps = 0.f;              // damping of the coupled Newton inverse root (standalone call)
@@ -308,6 +309,7 @@ struct shampoo4_ctx_s {
                 const size_t mat = (size_t)p * p * 4;
                 S.Vs = ws_take(mat);
                 S.Vr = ws_take(mat);
+                S.Rt = ws_take(mat);   // root matrix V^r diag(d) V^r^T (ROOT_CACHE)
                 S.Tmp = ws_take(mat);
                 S.Wg = ws_take(mat);
                 S.Lt = ws_take(mat);
@@ -942,6 +944,30 @@ struct shampoo4_ctx_s {
             pre[2] = make_gemm(p3, FAM_GEMM_PRECOND);
             pre[3] = make_gemm(p4, FAM_GEMM_PRECOND);
         }
+        // with ROOT_CACHE the root matrices V^r diag(d) V^r^T are formed once per root refresh
+        // and precondition is X1 = Rt_L G, P = X1 Rt_R (same product, other association)
+        {
+            std::vector<GemmItem> rm, q1, q2;
+            for (auto& S : sides) {
+                GemmDesc d = gd(wsf(S.Vr), S.p, wsf(S.Vr), S.p, wsf(S.Rt), S.p, S.p, S.p, S.p);
+                d.kscale = stf(S.d);
+                rm.push_back({d, false, true});
+            }
+            for (int b = 0; b < nb; ++b) {
+                const Side& L = sides[2 * b];
+                const Side& R = sides[2 * b + 1];
+                const int m = shapes[b].m, n = shapes[b].n;
+                GemmDesc d1 = gd(wsf(L.Rt), m, nullptr, 0, wsf(X1[b]), n, m, n, m);
+                d1.b_io = b;
+                q1.push_back({d1, false, false});
+                GemmDesc d2 = gd(wsf(X1[b]), n, wsf(R.Rt), n, nullptr, 0, m, n, n);
+                d2.d_io = b;
+                q2.push_back({d2, false, false});
+            }
+            root_mat = make_gemm(rm, FAM_GEMM_PRECOND);
+            pre_cached[0] = make_gemm(q1, FAM_GEMM_PRECOND);
+            pre_cached[1] = make_gemm(q2, FAM_GEMM_PRECOND);
+        }
     }
 
     // grafting epilogue: the same row tiles for both passes; bytes per element depend on
@@ -1170,10 +1196,12 @@ struct shampoo4_ctx_s {
         (void)hipGetLastError();
     }
 
+    // Rectified root eigenvectors into Vr; with ROOT_CACHE also the root matrices.
     hipError_t root_eigenvectors(hipStream_t s) {
         hipError_t e = run(deq_root, s);
         for (auto& it : bj_root)
             if (e == hipSuccess) e = run(it, s);
+        if (e == hipSuccess && (cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE)) e = run(root_mat, s);
         return e;
     }
 };
@@ -1365,7 +1393,11 @@ shampoo4_status shampoo4_precondition(shampoo4_ctx c, const shampoo4_io* io, voi
         e = c->root_eigenvectors(s);
         c->root_v_is_stats = false;
     }
-    for (int i = 0; i < 4 && e == hipSuccess; ++i) e = c->run(c->pre[i], s);
+    if (c->cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) {
+        for (int i = 0; i < 2 && e == hipSuccess; ++i) e = c->run(c->pre_cached[i], s);
+    } else {
+        for (int i = 0; i < 4 && e == hipSuccess; ++i) e = c->run(c->pre[i], s);
+    }
     return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
 

@@ -71,10 +71,13 @@ typedef enum {
 /* Config flags. */
 #define SHAMPOO4_FLAG_ROOT_CACHE 1u   /* keep the rectified fp32 root eigenvectors in the
                                          workspace between calls: refresh_root computes them
-                                         once, precondition reuses them, and an update_stats
-                                         that directly follows a refresh_root reuses them as
-                                         its own rectified eigenvectors (identical values).
-                                         Without the flag precondition recomputes them. */
+                                         once, together with the root matrices
+                                         V^r diag(d) V^r^T of both sides, precondition
+                                         multiplies by those (two products per block instead
+                                         of four), and an update_stats that directly follows
+                                         a refresh_root reuses the eigenvectors as its own
+                                         rectified eigenvectors (identical values).  Without
+                                         the flag precondition recomputes them. */
 #define SHAMPOO4_FLAG_KEEP_STATE 2u   /* shampoo4_init: do not write the initial state;
                                          the state buffer already holds a saved state. */
 /* Schedule of the Householder QR (same results either way up to rounding order).  By

@@ -40,6 +40,8 @@ def _check(As, Bs, Ds, ta, tb, alpha, beta, Cs):
     [(130, 70, 129), (31, 200, 5)],
     [(256, 256, 256)] * 3,
     [(1024, 1024, 1024)],                 # single large product
+    [(1024, 1024, 1024)] * 2,             # two large products
+    [(1000, 600, 77)] * 6,                # ragged edges on both sides
     [(32, 1000, 700)] * 2,                # skinny M
 ])
 def test_gemm_modes(ta, tb, shapes):
