@@ -88,6 +88,9 @@ enum : int32_t {
     GEMM_F_TB = 2,            // op(B) = B^T
     GEMM_F_COLDOT = 4,        // epilogue: D[tile_m][col] = sum over the tile's rows of
                               //   alpha * (op(A) op(B))[row][col] * C[row][col]; ldd = row stride
+    GEMM_F_SYM = 8,           // the result is symmetric (M == N, square tiles, no row or column
+                              //   scale, C symmetric): only tiles on or above the diagonal are
+                              //   computed; an off-diagonal tile is also stored transposed
 };
 
 // Codec work item: one flattened matrix of n fp32 elements.

@@ -123,12 +123,24 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
     constexpr int RB = (NQB + 255) / 256;
 
     const int tiles_m = dsc.tiles_m;
-    const int tiles_mn = tiles_m * ((dsc.N + BN - 1) / BN);
+    const bool sym = (dsc.flags & GEMM_F_SYM) != 0;
+    const int tiles_mn = sym ? tiles_m * (tiles_m + 1) / 2 : tiles_m * ((dsc.N + BN - 1) / BN);
     const int ks = t / tiles_mn;                 // split-K chunk (0 without split)
     const int tmn = t - ks * tiles_mn;
-    const int tile_m = tmn % tiles_m;
+    int tile_m, tile_n;
+    if (sym) {   // upper triangle, column by column: tmn = tn (tn + 1) / 2 + tm with tm <= tn
+        int tn = (int)((sqrtf(8.f * (float)tmn + 1.f) - 1.f) * 0.5f);
+        while ((tn + 1) * (tn + 2) / 2 <= tmn) ++tn;
+        while (tn * (tn + 1) / 2 > tmn) --tn;
+        tile_n = tn;
+        tile_m = tmn - tn * (tn + 1) / 2;
+    } else {
+        tile_m = tmn % tiles_m;
+        tile_n = tmn / tiles_m;
+    }
+    const bool mirror = (BM == BN) && sym && tile_m != tile_n;   // square tiles only
     const int row0 = tile_m * BM;
-    const int col0 = (tmn / tiles_m) * BN;
+    const int col0 = tile_n * BN;
     const int M = dsc.M, N = dsc.N;
     const int kbeg = ks * dsc.kchunk;
     const int K = (dsc.ksplit > 1) ? min(dsc.K, kbeg + dsc.kchunk) : dsc.K;   // loads stop at K
@@ -377,11 +389,33 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
                 cv[r] = keep_if(ldg(cp + (int64_t)rowc * ldcp + colc), beta != 0.f);
                 rv[r] = __uint_as_float((__float_as_uint(ldg(rsp + rowc)) & rsm) | (0x3f800000u & ~rsm));
             }
+            float v[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                const float v = fmaf(beta, cv[r], alpha * acc[m][n][r] * rv[r] * csv);
-                if (row < M && col < N) stg(D + (int64_t)row * ldd + col, v);
+                v[r] = fmaf(beta, cv[r], alpha * acc[m][n][r] * rv[r] * csv);
+                if (row < M && col < N) stg(D + (int64_t)row * ldd + col, v[r]);
+            }
+            if (mirror) {
+                // the transposed block through a per-wave LDS tile (both operand buffers are
+                // free after the K loop's last barrier), stored with one row per half-wave
+                float* tl = (wv < 2 ? As : Bs) + (wv & 1) * (32 * 33);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tl[((r >> 2) * 8 + h * 4 + (r & 3)) * 33 + l32] = v[r];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const int r0b = row0 + wave_m * TM * 32 + m * 32;
+                const int c0b = col0 + wave_n * TN * 32 + n * 32;
+#pragma unroll
+                for (int s = 0; s < 16; ++s) {
+                    const int g = 2 * s + h;                    // column of the block -> row of D
+                    const float tv = tl[l32 * 33 + g];
+                    if (c0b + g < M && r0b + l32 < N) stg(D + (int64_t)(c0b + g) * ldd + r0b + l32, tv);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
             // one 32 x 32 block at a time: keeps the next block's loads from being
             // hoisted here (their registers would cap the kernel's occupancy)
@@ -389,6 +423,12 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
         }
     }
 }
+
+// The mirrored-store tiles of GEMM_F_SYM: two 32 x 33 tiles in each operand buffer.
+static_assert(2 * Tile<2, 2, 1, 1>::A_MC >= 2 * 32 * 33 && 2 * Tile<2, 2, 1, 1>::B_MC >= 2 * 32 * 33,
+              "LDS of the 64 x 64 tile too small for the mirrored stores");
+static_assert(2 * Tile<2, 2, 2, 2>::A_MC >= 2 * 32 * 33 && 2 * Tile<2, 2, 2, 2>::B_MC >= 2 * 32 * 33,
+              "LDS of the 128 x 128 tile too small for the mirrored stores");
 
 // One transpose mode for the whole launch, 16-byte loads, no split-K slabs.
 template <int WM, int WN, int TM, int TN, bool TA, bool TB>

@@ -205,19 +205,38 @@ struct shampoo4_ctx_s {
         long tiles128 = 0;
         for (auto& d : ds) {
             maxM = std::max(maxM, d.M);
-            tiles128 += (long)((d.M + 127) / 128) * ((d.N + 127) / 128);
+            const long t = (d.M + 127) / 128;
+            const bool sym = (d.flags & GEMM_F_SYM) && d.M == d.N;
+            tiles128 += sym ? t * (t + 1) / 2 : t * ((d.N + 127) / 128);
         }
         const int cfgsel = maxM <= 32 ? GEMM_32x128 : (tiles128 >= 512 ? GEMM_128x128 : GEMM_64x64);
         int bm, bn;
         gemm_tile_dims(cfgsel, &bm, &bn);
+        // a symmetric product computes the tiles on and above the diagonal (square tiles,
+        // no row / column scales)
+        for (auto& d : ds)
+            if (bm != bn || d.M != d.N || d.rscale || d.cscale || (d.flags & GEMM_F_COLDOT))
+                d.flags &= ~GEMM_F_SYM;
         std::vector<int> prefix;
         int total = 0;
         Launch L;
         for (auto& d : ds) {
             d.tiles_m = (d.M + bm - 1) / bm;
             prefix.push_back(total);
-            total += d.tiles_m * ((d.N + bn - 1) / bn) * std::max(1, d.ksplit);
-            L.flops += 2.0 * d.M * d.N * d.K;
+            if (d.flags & GEMM_F_SYM) {
+                const int t = d.tiles_m;
+                total += t * (t + 1) / 2 * std::max(1, d.ksplit);
+                // algorithmic work of the tiles computed: rows x columns of each tile on or
+                // above the diagonal
+                double elems = 0;
+                for (int tn = 0; tn < t; ++tn)
+                    for (int tm = 0; tm <= tn; ++tm)
+                        elems += (double)std::min(bm, d.M - tm * bm) * std::min(bn, d.N - tn * bn);
+                L.flops += 2.0 * elems * d.K;
+            } else {
+                total += d.tiles_m * ((d.N + bn - 1) / bn) * std::max(1, d.ksplit);
+                L.flops += 2.0 * d.M * d.N * d.K;
+            }
             const bool coldot = d.flags & GEMM_F_COLDOT;
             L.bytes += 4.0 * ((double)d.M * d.K + (double)d.K * d.N +
                               (double)d.M * d.N * ((d.beta != 0.f || coldot) ? 2 : 1));
@@ -407,7 +426,9 @@ struct shampoo4_ctx_s {
                 const size_t in = (i % 2 == 0) ? start : other;
                 const size_t out = (i % 2 == 0) ? other : start;
                 const int p = S.p;
-                gram.push_back({gd(wsf(in), p, wsf(in), p, wsf(S.Wg), p, p, p, p), true, false});
+                GemmDesc gw = gd(wsf(in), p, wsf(in), p, wsf(S.Wg), p, p, p, p);
+                gw.flags |= GEMM_F_SYM;                  // V^T V
+                gram.push_back({gw, true, false});
                 upd.push_back({gd(wsf(in), p, wsf(S.Wg), p, wsf(out), p, p, p, p, -0.5f, 1.5f, wsf(in), p),
                                false, false});
             }
@@ -804,6 +825,7 @@ struct shampoo4_ctx_s {
                 const float* V = wsf(var == 0 ? S.Vs : S.Vr);
                 GemmDesc d = gd(V, p, V, p, wsf(S.Lt), p, p, p, p, beta);
                 d.kscale = stf(S.lam);
+                d.flags |= GEMM_F_SYM;                   // V diag(lam) V^T
                 xs.push_back({d, false, true});
                 pw.push_back({gd(wsf(S.Lt), p, V, p, wsf(S.Pm), p, p, p, p), false, false});
             }
@@ -819,6 +841,7 @@ struct shampoo4_ctx_s {
                     GemmDesc d = gd(nullptr, 0, nullptr, 0, wsf(S.Lt), p, p, p, q, 1.f - beta, 1.f,
                                     wsf(S.Lt), p);
                     d.a_io = d.b_io = b;
+                    d.flags |= GEMM_F_SYM;               // G G^T (G^T G), added to a symmetric Lt
                     gs.push_back({d, s == 1, s == 0});
                     pn.push_back({gd(wsf(S.Lt), p, wsf(S.Qm), p, wsf(S.Pm), p, p, p, p), false, false});
                 }
@@ -951,6 +974,7 @@ struct shampoo4_ctx_s {
             for (auto& S : sides) {
                 GemmDesc d = gd(wsf(S.Vr), S.p, wsf(S.Vr), S.p, wsf(S.Rt), S.p, S.p, S.p, S.p);
                 d.kscale = stf(S.d);
+                d.flags |= GEMM_F_SYM;                   // V diag(d) V^T
                 rm.push_back({d, false, true});
             }
             for (int b = 0; b < nb; ++b) {

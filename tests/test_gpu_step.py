@@ -60,6 +60,9 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
                 V = o.rectified_eigenvectors(st["codes"], st["scales"], p, k, 64, codebook)
                 Lt_ref = o.statistics(V, st["lam"], Gs_side, beta)
                 Lt_gpu = blocks.view(b, s, 17).cpu().numpy().astype(np.float64)
+                # symmetric up to the float32 rounding of the K-scaled products (off-diagonal
+                # tiles are stored mirrored)
+                assert rel_fro(Lt_gpu, Lt_gpu.T) <= 1e-6, (label, t, b, s, "statistic not symmetric")
                 e_stat = rel_fro(Lt_gpu, Lt_ref)
                 assert e_stat <= TOL, (label, t, b, s, "statistic", e_stat)
                 Q_ref, lam_ref = o.eigen_refresh(Lt_gpu, V, power_iters)
