@@ -505,9 +505,11 @@ struct shampoo4_ctx_s {
         // are applied at once (compact WY) only to the rest of its outer block, and each panel's Y = V T is folded into
         // the outer block's Y (Y_b <- Y_b - Y_a (V_a^T Y_b), which is V T of the product
         // of all the block's reflectors).  After an outer block's last panel its
-        // reflectors update the trailing columns (A <- A - V (Y^T A)) and the forward
-        // accumulation of Q (Q <- Q - (Q Y) V^T) as products of depth `outer`.  The columns
-        // of Q are flipped to diag(R) >= 0 at the end.
+        // reflectors update the trailing columns (A <- A - V (Y^T A)) as products of depth
+        // `outer`.  Q = H_0 H_1 ... is accumulated backward once every block is factored:
+        // starting from I, block b updates only Q[C0:, C0:] (Q_s <- Q_s - Y (V^T Q_s)), which
+        // costs 4 w h^2 flops per block instead of the 4 w h p of forward accumulation.
+        // The columns of Q are flipped to diag(R) >= 0 at the end.
         qr_steps.assign(max_panels, Seq{});
         qr_join.clear();
         for (int sidx = 0; sidx < max_panels; ++sidx) {
@@ -528,7 +530,7 @@ struct shampoo4_ctx_s {
                 tin += tiles64(nbw, ninner) + tiles64((long)i * kPanel, nbw);
                 kin = std::min(kin, p - c0);
                 if (ninner == 0) {
-                    tout += tiles64(wb, p - C0 - wb) + tiles64(p, wb);
+                    tout += tiles64(wb, p - C0 - wb);
                     kout = std::min(kout, p - C0);
                 }
             }
@@ -549,10 +551,8 @@ struct shampoo4_ctx_s {
                 float* Yo = wsf(S.Yb) + S.outer_rows[C0 / outer] * outer;
                 float* Pm = wsf(S.Pm);
                 float* Z = wsf(S.Z);
-                float* Wb = wsf(S.W);
                 float* Mb = wsf(S.Mb);
-                const int64_t zslab = (int64_t)outer * p, wslab = (int64_t)p * outer,
-                              mslab = (int64_t)outer * kPanel;
+                const int64_t zslab = (int64_t)outer * p, mslab = (int64_t)outer * kPanel;
                 PanelDesc pd;
                 std::memset(&pd, 0, sizeof(pd));
                 pd.A = Pm;
@@ -589,25 +589,15 @@ struct shampoo4_ctx_s {
                     y.bnslab = ns; y.bslab = mslab;
                     in2.push_back({y, false, false});
                 }
-                if (ninner == 0) {  // last panel of the block: trailing columns and Q
-                    if (ntr > 0) {
-                        float* At = Pm + (int64_t)C0 * p + C0 + wb;
-                        GemmDesc z = gd(Yo, outer, At, p, Z, p, wb, ntr, ho);
-                        const int ns = set_split(z, ks_out);
-                        z.dslab = zslab;
-                        out1.push_back({z, true, false});
-                        GemmDesc u = gd(Vo, outer, Z, p, At, p, ho, ntr, wb, -1.f, 1.f, At, p);
-                        u.bnslab = ns; u.bslab = zslab;
-                        out2.push_back({u, false, false});
-                    }
-                    float* Qs = wsf(S.Qm) + C0;                  // Q[:, C0:]
-                    GemmDesc w = gd(Qs, p, Yo, outer, Wb, outer, p, wb, ho);
-                    const int ns = set_split(w, ks_out);
-                    w.dslab = wslab;
-                    out1.push_back({w, false, false});
-                    GemmDesc q = gd(Wb, outer, Vo, outer, Qs, p, p, ho, wb, -1.f, 1.f, Qs, p);
-                    q.anslab = ns; q.aslab = wslab;
-                    out2.push_back({q, false, true});
+                if (ninner == 0 && ntr > 0) {  // last panel of the block: trailing columns
+                    float* At = Pm + (int64_t)C0 * p + C0 + wb;
+                    GemmDesc z = gd(Yo, outer, At, p, Z, p, wb, ntr, ho);
+                    const int ns = set_split(z, ks_out);
+                    z.dslab = zslab;
+                    out1.push_back({z, true, false});
+                    GemmDesc u = gd(Vo, outer, Z, p, At, p, ho, ntr, wb, -1.f, 1.f, At, p);
+                    u.bnslab = ns; u.bslab = zslab;
+                    out2.push_back({u, false, false});
                 }
             }
             Seq& st = qr_steps[sidx];
@@ -615,6 +605,42 @@ struct shampoo4_ctx_s {
             for (auto* items : {&in1, &in2, &out1, &out2}) {
                 Seq g = make_gemm(*items, FAM_GEMM_QR, outer == kOuter);
                 st.insert(st.end(), g.begin(), g.end());
+            }
+        }
+        // backward accumulation of Q (Q holds I): block b, last to first
+        int max_outer = 0;
+        for (auto& S : sides) max_outer = std::max(max_outer, (S.p + outer - 1) / outer);
+        for (int ob = max_outer - 1; ob >= 0; --ob) {
+            std::vector<GemmItem> w1, w2;
+            long tw = 0;
+            int kw = 1 << 30;
+            for (auto& S : sides) {
+                const int C0 = ob * outer;
+                if (C0 >= S.p) continue;
+                tw += tiles64(std::min(outer, S.p - C0), S.p - C0);
+                kw = std::min(kw, S.p - C0);
+            }
+            const int ks_w = split_for(tw, kw);
+            for (auto& S : sides) {
+                const int p = S.p, C0 = ob * outer;
+                if (C0 >= p) continue;
+                const int ho = p - C0, wb = std::min(outer, ho);
+                const float* Vo = wsf(S.Vb) + S.outer_rows[ob] * outer;
+                const float* Yo = wsf(S.Yb) + S.outer_rows[ob] * outer;
+                float* Qs = wsf(S.Qm) + (int64_t)C0 * p + C0;   // Q[C0:, C0:]
+                float* Wb = wsf(S.W);
+                const int64_t wslab = (int64_t)outer * p;
+                GemmDesc w = gd(Vo, outer, Qs, p, Wb, p, wb, ho, ho);   // W = V^T Q_s
+                const int ns = set_split(w, ks_w);
+                w.dslab = wslab;
+                w1.push_back({w, true, false});
+                GemmDesc q = gd(Yo, outer, Wb, p, Qs, p, ho, ho, wb, -1.f, 1.f, Qs, p);
+                q.bnslab = ns; q.bslab = wslab;
+                w2.push_back({q, false, false});
+            }
+            for (auto* items : {&w1, &w2}) {
+                Seq g = make_gemm(*items, FAM_GEMM_QR, outer == kOuter);
+                qr_join.insert(qr_join.end(), g.begin(), g.end());
             }
         }
     }
