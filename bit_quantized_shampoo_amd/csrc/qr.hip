@@ -46,18 +46,25 @@ namespace {
 constexpr int NSLOT = PANEL_THREADS / 32;   // row slots (half-waves)
 constexpr int NWAVE = PANEL_THREADS / 64;
 constexpr int PW = 32;                       // panel width
-constexpr int PART = PW * NWAVE;             // one partials buffer: [32 columns][NWAVE]
+// one partials buffer: [32 columns][PSTR], NWAVE used; the 12-float column pitch keeps the
+// two 16-byte reads of 8 consecutive lanes' columns on distinct banks
+constexpr int PSTR = 12;
+constexpr int PART = PW * PSTR;
 
 // LDS layout (floats)
-constexpr int OFF_PART = 0;                      // [2][32][NWAVE]
+constexpr int OFF_PART = 0;                      // [2][32][PSTR]
 constexpr int OFF_ROWJ = OFF_PART + 2 * PART;    // [2][32]
 constexpr int OFF_SALL = OFF_ROWJ + 64;          // [32 columns][33] s_j[c] of step j at c * 33 + j
 constexpr int OFF_TAU = OFF_SALL + PW * 33;      // [32]
 constexpr int OFF_T = OFF_TAU + PW;              // [32][33]
 constexpr int OFF_RED = OFF_T + PW * 33;         // [NWAVE]
 constexpr int OFF_RD = OFF_RED + NWAVE;          // [32] R diagonal (written out after the loop)
-constexpr int OFF_COL = ((OFF_RD + PW + 3) / 4) * 4;  // [NSLOT][64] column j+1 of each half-wave's rows
-constexpr int OFF_VS = OFF_COL + NSLOT * 64;     // [hpad][33] V staging (register variant)
+// Column j+1 of each half-wave's rows: the two half-waves of a wave read their slots in
+// the same instruction, so the slot pitch is offset by 4 banks from a multiple of the bank
+// count (64 + 4 floats): the two 16-byte broadcasts hit different banks.
+constexpr int COL_PITCH = 68;
+constexpr int OFF_COL = ((OFF_RD + PW + 3) / 4) * 4;  // [NSLOT][COL_PITCH]
+constexpr int OFF_VS = OFF_COL + NSLOT * COL_PITCH;  // [hpad][33] V staging (register variant)
 constexpr int OFF_VS_T12 = OFF_COL;              // [16][16] scratch of build_T (after the loop)
 static_assert(NWAVE == 8, "partials are read as two 16-byte vectors");
 
@@ -91,7 +98,7 @@ __device__ __forceinline__ float sum_partials(const float* p) {
 
 // Combined partials of step `buf` for column col, and row j's entry in that column.
 __device__ __forceinline__ float read_d(const float* smem, int buf, int col) {
-    return sum_partials(smem + OFF_PART + buf * PART + col * NWAVE);
+    return sum_partials(smem + OFF_PART + buf * PART + col * PSTR);
 }
 __device__ __forceinline__ float read_row(const float* smem, int buf, int col) {
     return smem[OFF_ROWJ + buf * 32 + col];
@@ -102,7 +109,7 @@ __device__ __forceinline__ float read_row(const float* smem, int buf, int col) {
 __device__ __forceinline__ void write_partial(float* smem, int buf, int c, int lane, int wv, float pacc) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(pacc), __float_as_uint(pacc), false, false);
     const float other = __uint_as_float(lane < 32 ? sw[1] : sw[0]);
-    if (lane < 32) smem[OFF_PART + buf * PART + c * NWAVE + wv] = pacc + other;
+    if (lane < 32) smem[OFF_PART + buf * PART + c * PSTR + wv] = pacc + other;
 }
 
 __device__ __forceinline__ float panel_max(float mx, float* smem, int lane, int wv) {
@@ -606,7 +613,7 @@ __device__ __forceinline__ void panel_body(const PanelDesc& d, const PanelExtra&
     __syncthreads();
 
     // column j+1 of this half-wave's rows, published by its lane j+1 (same wave: no barrier)
-    float* colbuf = smem + OFF_COL + slot * 64;
+    float* colbuf = smem + OFF_COL + slot * COL_PITCH;
     for (int j = 0; j < nb; ++j) {
         const int buf = j & 1;
         const int jn = j + 1;
