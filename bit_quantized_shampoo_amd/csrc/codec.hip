@@ -21,10 +21,12 @@
 // Both kernels are HBM-bound streams: the quantizer reads 4 B and writes
 // 0.5 B + 4/64 B per element, the dequantizer the reverse.
 //  * quant: one lane per 4 consecutive elements (a 16-byte load), 16 lanes per
-//    block; the block absmax is a 4-step xor-shuffle reduction inside the
-//    16-lane group; each lane writes its 4 codes as one 16-bit store, lane 0 of
-//    the group writes the scale.  The code comes from one LDS table lookup keyed
-//    by the bits of x_hat instead of a scan over the 15 midpoints.
+//    block; the block absmax is a 4-step DPP reduction inside the 16-lane row;
+//    x_hat comes from one correctly rounded reciprocal per block and two fused
+//    multiply-add corrections per element (bit-identical to the IEEE division);
+//    each lane writes its 4 codes as one 16-bit store, lane 0 of the group
+//    writes the scale.  The code comes from one LDS table lookup keyed by the
+//    bits of x_hat instead of a scan over the 15 midpoints.
 //  * dequant: a lane expands 4 elements at a time (one 16-bit code word, one
 //    16-byte store), several quads per lane in flight, spaced so that every store
 //    instruction of a wave writes 1 KB contiguous; levels from a 16-entry LDS table.
@@ -196,7 +198,7 @@ __device__ __forceinline__ void dequant_item(const CodecDesc& d, int tile) {
         const int64_t e0 = q * 4;
         if (e0 + 4 <= n && aligned) {
             const floatx4 a = {v[0], v[1], v[2], v[3]};
-            stg(reinterpret_cast<floatx4*>(x + e0), a);
+            stg_nt(reinterpret_cast<floatx4*>(x + e0), a);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -217,10 +219,37 @@ __global__ __launch_bounds__(256) void dequant_single_kernel(CodecDesc d) {
     dequant_item<CB>(d, blockIdx.x);
 }
 
-// Quantization: a lane codes 4 consecutive elements (one 16-byte load), 16 lanes
-// cover a quantization block and reduce its absmax with xor shuffles; each lane
-// handles QUANT_QUADS such quads spaced 256 quads apart.
+// Quantization: a lane codes 4 consecutive elements (one 16-byte load), 16 lanes (one
+// DPP row) cover a quantization block; each lane handles QUANT_QUADS such quads spaced
+// 256 quads apart.  The block absmax is taken on the magnitudes' bit patterns (as
+// unsigned integers they order like the floats, and NaN / Inf sort above every finite
+// value, so the same maximum flags non-finite input) and reduced over the row with
+// four DPP rotations.
 constexpr int QUANT_QUADS = QUANT_TILE / (256 * 4);
+
+// Largest value over the 16 lanes of a DPP row: rotations by 8, 4, 2, 1 reach every lane.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t m) {
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x128, 0xf, 0xf, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x124, 0xf, 0xf, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x122, 0xf, 0xf, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x121, 0xf, 0xf, false));
+    return m;
+}
+
+// x / s rounded to nearest from y = RN(1/s), without a division per element.  The first
+// correction q1 = q0 + (x - q0 s) y leaves q1 within one ulp of x / s; the second is
+// Markstein's correction step: when y = RN(1/s) and q is within one ulp of x / s, the
+// remainder x - q s is exact in one fused multiply-add and RN(q + (x - q s) y) = RN(x / s).
+// Its conditions (no underflow of the remainders where the quotient can reach a decision
+// midpoint, |x/s| >= 2^-9) hold for 2^-60 <= s <= 2^60; a quotient below 2^-12 lies below
+// every midpoint however it is rounded.  Other scales take the IEEE division.
+constexpr uint32_t kRecipLo = 0x21800000u;   // 2^-60
+constexpr uint32_t kRecipHi = 0x5d800000u;   // 2^60
+__device__ __forceinline__ float quotient_rn(float x, float s, float y) {
+    const float q0 = x * y;
+    const float q1 = fmaf(fmaf(-q0, s, x), y, q0);
+    return fmaf(fmaf(-q1, s, x), y, q1);
+}
 
 template <class CB>
 __device__ __forceinline__ void quant_item(const CodecDesc& d, int tile, uint32_t* __restrict__ flag) {
@@ -233,45 +262,58 @@ __device__ __forceinline__ void quant_item(const CodecDesc& d, int tile, uint32_
     const int64_t q0 = (int64_t)tile * (QUANT_TILE / 4) + threadIdx.x;
     const float* __restrict__ x = d.x_in;
     const bool aligned = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+    // every element of the tile exists: straight-line streaming loads
+    const bool full = aligned && (int64_t)(tile + 1) * QUANT_TILE <= n;
     float v[QUANT_QUADS][4];
+    if (full) {
 #pragma unroll
-    for (int k = 0; k < QUANT_QUADS; ++k) {
-        const int64_t e0 = (q0 + k * 256) * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[k][e] = 0.f;
-        if (e0 + 4 <= n && aligned) {
-            const floatx4 q = *reinterpret_cast<const floatx4*>(x + e0);
+        for (int k = 0; k < QUANT_QUADS; ++k) {
+            const floatx4 q = ldg_nt(reinterpret_cast<const floatx4*>(x + (q0 + k * 256) * 4));
             v[k][0] = q[0]; v[k][1] = q[1]; v[k][2] = q[2]; v[k][3] = q[3];
-        } else {
+        }
+    } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (e0 + e < n) v[k][e] = x[e0 + e];
+        for (int k = 0; k < QUANT_QUADS; ++k) {
+            const int64_t e0 = (q0 + k * 256) * 4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[k][e] = 0.f;
+            if (e0 + 4 <= n && aligned) {
+                const floatx4 q = ldg_nt(reinterpret_cast<const floatx4*>(x + e0));
+                v[k][0] = q[0]; v[k][1] = q[1]; v[k][2] = q[2]; v[k][3] = q[3];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (e0 + e < n) v[k][e] = ldg(x + e0 + e);
+            }
         }
     }
     __syncthreads();
-    bool finite = true;
+    uint32_t bad = 0;
 #pragma unroll
     for (int k = 0; k < QUANT_QUADS; ++k) {
         const int64_t qd = q0 + k * 256;
-        float amax = 0.f;
+        uint32_t m = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            finite = finite && __builtin_isfinite(v[k][e]);
-            amax = fmaxf(amax, fabsf(v[k][e]));
-        }
-        // absmax over the 16 lanes of this quantization block (lane groups are aligned)
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+        for (int e = 0; e < 4; ++e) m = max(m, __float_as_uint(v[k][e]) & 0x7fffffffu);
+        m = row_max_u32(m);
+        bad |= m >= 0x7f800000u ? 1u : 0u;
+        const float amax = __uint_as_float(m);
         if (qd < nquads) {
             uint32_t packed = 0;
+            if (m >= kRecipLo && m <= kRecipHi) {
+                const float y = __fdiv_rn(1.0f, amax);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) packed |= code_of<CB>(__fdiv_rn(v[k][e], amax), tab) << (4 * e);
-            if (amax == 0.f) packed = 0x7777u;
+                for (int e = 0; e < 4; ++e) packed |= code_of<CB>(quotient_rn(v[k][e], amax, y), tab) << (4 * e);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) packed |= code_of<CB>(__fdiv_rn(v[k][e], amax), tab) << (4 * e);
+                if (m == 0u) packed = 0x7777u;
+            }
             reinterpret_cast<uint16_t*>(d.codes_out)[qd] = (uint16_t)packed;
             if ((qd & 15) == 0) d.scales_out[qd >> 4] = amax;
         }
     }
-    if (!finite && flag) flag[0] = 1u;
+    if (bad && flag) flag[0] = 1u;
 }
 
 template <class CB>

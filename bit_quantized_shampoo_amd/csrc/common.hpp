@@ -45,6 +45,18 @@ __device__ __forceinline__ void stg(T* p, T v) {
     using G = __attribute__((address_space(1))) T;
     *(G*)p = v;
 }
+// Streaming forms for data touched once (the codec's fp32 side): the nontemporal hint
+// keeps single-use lines from displacing reused ones and lets the memory system stream them.
+template <class T>
+__device__ __forceinline__ T ldg_nt(const T* p) {
+    using G = __attribute__((address_space(1))) const T;
+    return __builtin_nontemporal_load((G*)p);
+}
+template <class T>
+__device__ __forceinline__ void stg_nt(T* p, T v) {
+    using G = __attribute__((address_space(1))) T;
+    __builtin_nontemporal_store(v, (G*)p);
+}
 
 // Per-block user pointers of one call, uploaded once per call; descriptors refer
 // to an entry by index so that the static descriptor tables never change.

@@ -24,7 +24,7 @@ hipError_t launch_gemm(int cfg, int mode, bool vec, bool slab, const GemmDesc* d
 bool gemm_vec_ok(const GemmDesc& d);
 
 // Codec: elements per workgroup tile.
-constexpr int DEQ_TILE = 8192;     // 256 threads x 8 quads x 4 elements
+constexpr int DEQ_TILE = 4096;     // 256 threads x 4 quads x 4 elements
 constexpr int QUANT_TILE = 4096;   // 256 threads x 4 quads x 4 elements
 constexpr int COPY_TILE = 8192;    // bytes of codes per workgroup
 // workgroups for n elements (quantization blocks of 64 padded)

@@ -63,6 +63,17 @@ def _cases(cb="ls"):
     z[200] = 7.0
     cases["zeros_subnormals"] = z
     cases["identity_1024"] = np.eye(1024, dtype=np.float32).ravel()
+    # block scales from the subnormal range to 2^120, both sides of the range in which
+    # the quantizer divides through one reciprocal per block (2^-60 .. 2^60), with
+    # values on and next to the decision midpoints times each scale
+    exps = np.concatenate([np.arange(-149, 121, 3), [-61, -60, -59, 59, 60, 61, -126, -127]])
+    sb = np.zeros((exps.size, 64), np.float32)
+    for i, e in enumerate(exps):
+        base = np.concatenate([rng.uniform(-1, 1, 32), m32[rng.integers(0, 15, 31)]])
+        sb[i, 0] = 1.0
+        sb[i, 1:] = base
+        sb[i] = (sb[i].astype(np.float64) * 2.0 ** float(e)).astype(np.float32)
+    cases["scale_range"] = sb.ravel()
     return cases
 
 
