@@ -93,7 +93,7 @@ struct Buckets {
 
 template <class CB>
 struct QTab {
-    uint32_t thr[2 * Buckets<CB>::N];    // the in-bucket midpoint (as magnitude bits), or all ones
+    uint32_t thr[2 * Buckets<CB>::N];    // the in-bucket midpoint (as x_hat bits), or all ones
     uint32_t code[2 * Buckets<CB>::N];   // low nibble: code at or below thr; next nibble: code above
     int max_per_bucket;
     bool mids_in_range;                  // every midpoint magnitude lies in [2^-9, 2)
@@ -126,8 +126,10 @@ constexpr QTab<CB> make_qtab() {
                 if (B::bucket_of(mag) == b) {
                     ++inb;
                     // positive: code rises once x_hat > m; negative: the count of
-                    // midpoints below x_hat drops once |x_hat| >= |m|
-                    thr = s == 0 ? mag : mag - 1u;
+                    // midpoints below x_hat drops once |x_hat| >= |m|.  The threshold is
+                    // compared with x_hat's whole bit pattern, so a negative entry
+                    // carries the sign bit.
+                    thr = s == 0 ? mag : ((mag - 1u) | 0x80000000u);
                 }
             }
             const int lo = s == 0 ? 7 + below : 7 - below;
@@ -158,10 +160,12 @@ template <class CB>
 __device__ __forceinline__ uint32_t code_of(float xh, const uint2* __restrict__ tab) {
     using B = Buckets<CB>;
     const uint32_t u = __float_as_uint(xh);
-    const uint32_t mag = u & 0x7fffffffu;
-    const int b = min(max((int)(mag >> B::SHIFT) - B::E0, 0), B::N - 1) + (int)(u >> 31) * B::N;
-    const uint2 e = tab[b];
-    return mag > e.x ? (e.y >> 4) : (e.y & 15u);
+    // exponent and top MB mantissa bits of |x_hat| (one bit-field extract), clamped to
+    // the bucket range (one med3)
+    const uint32_t key = min(max(__builtin_amdgcn_ubfe(u, B::SHIFT, 31 - B::SHIFT), (uint32_t)B::E0),
+                             (uint32_t)(B::E0 + B::N - 1));
+    const uint2 e = tab[(int)key - B::E0 + (int)(u >> 31) * B::N];
+    return __builtin_amdgcn_ubfe(e.y, u > e.x ? 4u : 0u, 4u);
 }
 
 // Dequantization: each lane expands DEQ_QUADS groups of 4 elements (one 16-bit code
