@@ -617,10 +617,12 @@ __device__ __forceinline__ void panel_body(const PanelDesc& d, const PanelExtra&
     for (int j = 0; j < nb; ++j) {
         const int buf = j & 1;
         const int jn = j + 1;
+        // every lane sums its own column's partials; the pivot column's sum and diagonal
+        // entry come from lane j of the wave (half of the LDS reads after the barrier)
         const float dc = read_d(smem, buf, c);
-        const float dj = read_d(smem, buf, j);
-        const float alpha = read_row(smem, buf, j);
         const float ajc = read_row(smem, buf, c);
+        const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dc), j));
+        const float alpha = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ajc), j));
         const Refl R = reflector(alpha, dj);
         const float sv = (c < nb && c != j) ? R.sc * (dc - R.beta * ajc) : 0.f;
         if (slot == 0) {
@@ -821,10 +823,12 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_global_kernel(const Panel
 
     for (int j = 0; j < nb; ++j) {
         const int buf = j & 1;
+        // every lane sums its own column's partials; the pivot column's sum and diagonal
+        // entry come from lane j of the wave (half of the LDS reads after the barrier)
         const float dc = read_d(smem, buf, c);
-        const float dj = read_d(smem, buf, j);
-        const float alpha = read_row(smem, buf, j);
         const float ajc = read_row(smem, buf, c);
+        const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dc), j));
+        const float alpha = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ajc), j));
         const Refl R = reflector(alpha, dj);
         const float sv = (c < nb && c != j) ? R.sc * (dc - R.beta * ajc) : 0.f;
         if (slot == 0) {
