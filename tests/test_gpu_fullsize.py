@@ -1,0 +1,82 @@
+"""Parity at the workloads' full sizes, in the configuration bench.py times (every block
+of the batch on the GPU, cached root matrices, the automatic QR schedule, the workload's
+Bjorck iterations and root interval).
+
+The oracle is too slow for every block of these batches, so:
+  * sampled blocks (every distinct shape of the CNN batch, the first and last blocks of
+    the transformer batch, one 4096 block of the stress batch) get the full
+    teacher-forced comparison of the step harness (statistic, Q diag(lam) Q^T,
+    eigenvalues, codes, d, preconditioned gradient);
+  * every side gets the checks that hold at any size: the new Q is orthonormal
+    (computed in float64 on the device), finite, and a seeded sample of sides has codes
+    equal, bit for bit, to the oracle codec applied to the GPU's own float32 Q.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codec
+from tests.gpu_util import announce, require_gpu
+from tests.test_gpu_step import _run_teacher_forced
+from workloads import get_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _side_checks(shapes, ncodes, seed):
+    rng = np.random.default_rng(seed)
+    sides = [(b, s) for b in range(len(shapes)) for s in (0, 1)]
+    pick = sorted(rng.choice(len(sides), size=min(ncodes, len(sides)), replace=False).tolist())
+
+    def check(blocks, t):
+        worst = 0.0
+        for b, s in sides:
+            Q = blocks.view(b, s, 18)
+            assert bool(torch.isfinite(Q).all()), (t, b, s, "non-finite Q")
+            Qd = Q.double()
+            e = float((Qd.T @ Qd - torch.eye(Q.shape[0], dtype=torch.float64, device=Q.device)).abs().max())
+            worst = max(worst, e)
+            assert e <= 1e-4, (t, b, s, "Q not orthonormal", e)
+        for i in pick:
+            b, s = sides[i]
+            Q32 = blocks.view(b, s, 18).cpu().numpy()
+            st = blocks.side_state(b, s)
+            c_ref, s_ref = codec.quantize_matrix(Q32, 64)
+            assert np.array_equal(st["codes"], c_ref), (t, b, s, "codes")
+            assert np.array_equal(st["scales"].view(np.uint32), s_ref.view(np.uint32)), (t, b, s, "scales")
+        announce(f"  all {len(sides)} sides orthonormal (worst {worst:.2e}), codes of {len(pick)} sides bit-exact")
+
+    return check
+
+
+def _distinct_shape_blocks(shapes):
+    seen, idx = set(), []
+    for i, sh in enumerate(shapes):
+        if sh not in seen:
+            seen.add(sh)
+            idx.append(i)
+    return idx
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,steps,ncodes", [
+    ("cnn_batch", 2, 64),
+    ("transformer_batch", 2, 24),
+    ("large_4096", 2, 6),
+])
+def test_full_size_sampled(name, steps, ncodes):
+    require_gpu()
+    wl = get_workload(name)
+    shapes = wl.shapes
+    if name == "cnn_batch":
+        sample = sorted(set(_distinct_shape_blocks(shapes) + [len(shapes) - 1]))
+    elif name == "transformer_batch":
+        sample = [0, len(shapes) - 1]
+    else:
+        sample = [len(shapes) // 2]
+    announce(f"full size {name}: {len(shapes)} blocks, oracle on blocks {sample}")
+    _run_teacher_forced(shapes, wl.gradients, steps, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
+                        power_iters=wl.power_iters, root_interval=wl.root_interval, root_cache=True,
+                        label=name, qr="auto", sample=sample,
+                        all_sides=_side_checks(shapes, ncodes, seed=len(shapes)))

@@ -29,15 +29,20 @@ TOL = 1e-3
 
 
 def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power_iters=1,
-                        root_interval=1, root_cache=False, label="", qr="auto", codebook="ls"):
+                        root_interval=1, root_cache=False, label="", qr="auto", codebook="ls",
+                        sample=None, all_sides=None):
+    """`sample`: the blocks checked against the oracle (default: every block).
+    `all_sides(blocks, t)`: an optional extra check after each update_stats."""
     from bit_quantized_shampoo_amd import Shampoo4Blocks, Shampoo4Config
     cfg = Shampoo4Config(beta=beta, eps=eps, bjorck_iters=k, power_iters=power_iters,
                          root_cache=root_cache, qr_schedule=qr, codebook=codebook)
-    announce(f"step parity {label}: init {shapes}")
+    announce(f"step parity {label}: init {len(shapes)} blocks")
     blocks = Shampoo4Blocks(shapes, cfg)
     torch.cuda.synchronize()
+    checked = list(range(len(shapes))) if sample is None else list(sample)
     # initial state equals the oracle's
-    for b, (m, n) in enumerate(shapes):
+    for b in checked:
+        m, n = shapes[b]
         for s, p in ((0, m), (1, n)):
             ref = o.initial_side(p, 64, codebook)
             got = blocks.side_state(b, s)
@@ -49,11 +54,14 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
     for t in range(1, steps + 1):
         Gs = grads_fn(t)
         Gd = [to_dev(G) for G in Gs]
-        before = [[blocks.side_state(b, s) for s in (0, 1)] for b in range(len(shapes))]
+        before = {b: [blocks.side_state(b, s) for s in (0, 1)] for b in checked}
         announce(f"step parity {label}: t={t} update_stats")
         blocks.update_stats(Gd)
         torch.cuda.synchronize()
-        for b, (m, n) in enumerate(shapes):
+        if all_sides is not None:
+            all_sides(blocks, t)
+        for b in checked:
+            m, n = shapes[b]
             for s, p in ((0, m), (1, n)):
                 st = before[b][s]
                 Gs_side = o.side_gradient(Gs[b], s)
@@ -85,7 +93,7 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
             announce(f"step parity {label}: t={t} refresh_root")
             blocks.refresh_root()
             torch.cuda.synchronize()
-            for b, (m, n) in enumerate(shapes):
+            for b in checked:
                 for s in (0, 1):
                     st = blocks.side_state(b, s)
                     assert np.array_equal(st["root_codes"], st["codes"])
@@ -95,7 +103,10 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
         announce(f"step parity {label}: t={t} precondition")
         outs = blocks.precondition(Gd)
         torch.cuda.synchronize()
-        for b, (m, n) in enumerate(shapes):
+        for P in outs:
+            assert bool(torch.isfinite(P).all()), (label, t, "non-finite preconditioned gradient")
+        for b in checked:
+            m, n = shapes[b]
             sl, sr = blocks.side_state(b, 0), blocks.side_state(b, 1)
             VL = o.rectified_eigenvectors(sl["root_codes"], sl["root_scales"], m, k, 64, codebook)
             VR = o.rectified_eigenvectors(sr["root_codes"], sr["root_scales"], n, k, 64, codebook)
@@ -294,7 +305,10 @@ def _run_teacher_forced_fp32(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, 
         announce(f"fp32 state {label}: t={t} precondition")
         outs = blocks.precondition(Gd)
         torch.cuda.synchronize()
-        for b, (m, n) in enumerate(shapes):
+        for P in outs:
+            assert bool(torch.isfinite(P).all()), (label, t, "non-finite preconditioned gradient")
+        for b in checked:
+            m, n = shapes[b]
             sl, sr = blocks.side_state(b, 0), blocks.side_state(b, 1)
             VL = o.bjorck(blocks.eigenvectors(b, 0, root=True).cpu().numpy().astype(np.float64), k)
             VR = o.bjorck(blocks.eigenvectors(b, 1, root=True).cpu().numpy().astype(np.float64), k)
