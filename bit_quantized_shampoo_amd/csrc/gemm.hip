@@ -515,6 +515,7 @@ void gemm_tile_dims(int cfg, int* bm, int* bn) {
     switch (cfg) {
         case GEMM_128x128: *bm = 128; *bn = 128; break;
         case GEMM_64x64: *bm = 64; *bn = 64; break;
+        case GEMM_128x32: *bm = 128; *bn = 32; break;
         default: *bm = 32; *bn = 128; break;
     }
 }
@@ -525,6 +526,7 @@ hipError_t launch_gemm(int cfg, int mode, bool vec, bool slab, const GemmDesc* d
     switch (cfg) {
         case GEMM_128x128: return launch_cfg<2, 2, 2, 2>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
         case GEMM_64x64: return launch_cfg<2, 2, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
+        case GEMM_128x32: return launch_cfg<4, 1, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
         default: return launch_cfg<1, 4, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
     }
 }

@@ -9,7 +9,7 @@
 namespace s4 {
 
 // Tile shapes of the fp32 MFMA GEMM (workgroup of 4 waves).
-enum GemmCfg { GEMM_128x128 = 0, GEMM_64x64 = 1, GEMM_32x128 = 2, GEMM_NCFG = 3 };
+enum GemmCfg { GEMM_128x128 = 0, GEMM_64x64 = 1, GEMM_32x128 = 2, GEMM_128x32 = 3, GEMM_NCFG = 4 };
 constexpr int GEMM_MODE_MIXED = -1;   // descriptors of one launch carry different transposes
 void gemm_tile_dims(int cfg, int* bm, int* bn);
 // mode: GEMM_F_TA | GEMM_F_TB shared by all descriptors, or GEMM_MODE_MIXED.

@@ -37,11 +37,15 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 // Timing families: the matrix products are split by the stage they serve.
 enum Family {
     FAM_GEMM_BJORCK = 0, FAM_GEMM_STATS, FAM_GEMM_POWER, FAM_GEMM_QR, FAM_GEMM_RAYLEIGH,
-    FAM_GEMM_PRECOND, FAM_DEQUANT, FAM_QUANT, FAM_PANEL, FAM_RAYLEIGH, FAM_ELEMENTWISE, FAM_GRAFT, FAM_N
+    FAM_GEMM_PRECOND, FAM_DEQUANT, FAM_QUANT, FAM_PANEL, FAM_RAYLEIGH, FAM_ELEMENTWISE, FAM_GRAFT,
+    FAM_GEMM_QR_TRAIL, FAM_GEMM_QR_Q, FAM_N
 };
+// gemm_qr: the reflector products inside an outer block (and the look-ahead schedule's);
+// gemm_qr_trail: an outer block's reflectors on the trailing columns; gemm_qr_q: the
+// accumulation of Q
 const char* kFamilyNames[FAM_N] = {"gemm_bjorck", "gemm_stats", "gemm_power", "gemm_qr", "gemm_rayleigh",
                                    "gemm_precond", "dequant", "quant", "qr_panel", "rayleigh",
-                                   "elementwise", "graft"};
+                                   "elementwise", "graft", "gemm_qr_trail", "gemm_qr_q"};
 
 enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT,
             K_RECORD, K_WAIT, K_GRAFT_NORMS, K_GRAFT_APPLY, K_COPYF, K_NEWTON_NORM, K_NEWTON_SCALE,
@@ -172,11 +176,46 @@ struct shampoo4_ctx_s {
         bool ta, tb;
     };
 
-    // One launch for a batch of products (mixed transposes allowed).
+    // Tile shape that wastes least of its tile on a product: skinny products (one side
+    // up to 32, the panel-wide reflector products) take the 32-wide tiles, products with a
+    // side up to 64 the 64 x 64 tile; -1: square enough for either of the large shapes.
+    static int shape_class(const GemmDesc& d) {
+        if (d.M <= 32) return GEMM_32x128;
+        if (d.N <= 32) return GEMM_128x32;
+        if (d.M <= 64 || d.N <= 64) return GEMM_64x64;
+        return -1;
+    }
+    // Multiply-adds a tile shape computes for a product, padding included.
+    static double padded_work(const GemmDesc& d, int cfg) {
+        int bm, bn;
+        gemm_tile_dims(cfg, &bm, &bn);
+        return (double)((d.M + bm - 1) / bm * bm) * ((d.N + bn - 1) / bn * bn) * d.K;
+    }
+    // The large-shape choice for a set of products: 128 x 128 when its tiles fill the
+    // GPU's workgroup slots (two per CU), else 64 x 64; products of at most 32 rows
+    // always take the 32 x 128 tile.
+    static int default_cfg(const std::vector<GemmItem>& items) {
+        int maxM = 0;
+        long tiles128 = 0;
+        for (auto& it : items) {
+            const GemmDesc& d = it.d;
+            if (d.M <= 0 || d.N <= 0) continue;
+            maxM = std::max(maxM, d.M);
+            const long t = (d.M + 127) / 128;
+            const bool sym = (d.flags & GEMM_F_SYM) && d.M == d.N;
+            tiles128 += sym ? t * (t + 1) / 2 : t * ((d.N + 127) / 128);
+        }
+        return maxM <= 32 ? GEMM_32x128 : (tiles128 >= 512 ? GEMM_128x128 : GEMM_64x64);
+    }
+
+    // Launches for a batch of products (mixed transposes allowed).
     // With split_modes, products of different transpose modes go to separate launches
     // of the specialized kernels (fewer registers than the mixed kernel, which spills a
-    // little at the 128 x 128 tile); otherwise one launch covers them all.
-    Seq make_gemm(std::vector<GemmItem> items, int fam, bool split_modes = false) {
+    // little at the 128 x 128 tile).  With by_shape, products are grouped by tile shape
+    // class (one launch each) when the padding this saves outweighs the extra launches;
+    // otherwise one launch covers them all.  Products with a column-dot epilogue stay in
+    // one launch (their partial rows follow one tile height).
+    Seq make_gemm(std::vector<GemmItem> items, int fam, bool split_modes = false, bool by_shape = true) {
         if (split_modes) {
             Seq out;
             for (int mode = 0; mode < 4; ++mode) {
@@ -184,11 +223,57 @@ struct shampoo4_ctx_s {
                 for (auto& it : items)
                     if (((it.ta ? GEMM_F_TA : 0) | (it.tb ? GEMM_F_TB : 0)) == mode) part.push_back(it);
                 if (part.empty()) continue;
-                Seq g = make_gemm(part, fam, false);
+                Seq g = make_gemm(part, fam, false, by_shape);
                 out.insert(out.end(), g.begin(), g.end());
             }
             return out;
         }
+        bool coldot = false;
+        for (auto& it : items) coldot = coldot || (it.d.flags & GEMM_F_COLDOT);
+        if (by_shape && !coldot) {
+            std::vector<GemmItem> part[GEMM_NCFG + 1];   // by class; the last: square
+            for (auto& it : items) {
+                if (it.d.M <= 0 || it.d.N <= 0) continue;
+                const int c = shape_class(it.d);
+                part[c < 0 ? GEMM_NCFG : c].push_back(it);
+            }
+            int nclass = 0;
+            for (auto& pt : part) nclass += !pt.empty();
+            if (nclass > 1) {
+                // one launch: every product on the batch's default shape; grouped: each
+                // class on its own shape.  A launch is worth about 5 us of padded work at
+                // 80 TFLOP/s.
+                const double launch_work = 5e-6 * 80e12 / 2;
+                const int c1 = default_cfg(items);
+                double one = launch_work, grouped = 0;
+                for (int c = 0; c <= GEMM_NCFG; ++c) {
+                    if (part[c].empty()) continue;
+                    const int cc = c < GEMM_NCFG ? c : default_cfg(part[c]);
+                    grouped += launch_work;
+                    for (auto& it : part[c]) {
+                        one += padded_work(it.d, c1);
+                        grouped += padded_work(it.d, cc);
+                    }
+                }
+                if (grouped < one) {
+                    Seq out;
+                    for (int c = 0; c <= GEMM_NCFG; ++c) {
+                        if (part[c].empty()) continue;
+                        Seq g = gemm_launch(part[c], fam, c < GEMM_NCFG ? c : default_cfg(part[c]));
+                        out.insert(out.end(), g.begin(), g.end());
+                    }
+                    return out;
+                }
+            } else if (nclass == 1) {
+                for (int c = 0; c < GEMM_NCFG; ++c)
+                    if (!part[c].empty()) return gemm_launch(part[c], fam, c);
+            }
+        }
+        return gemm_launch(items, fam, default_cfg(items));
+    }
+
+    // One launch of `items` on tile shape cfgsel.
+    Seq gemm_launch(const std::vector<GemmItem>& items, int fam, int cfgsel) {
         std::vector<GemmDesc> ds;
         int modes = 0, first_mode = -2;
         for (auto& it : items) {
@@ -201,15 +286,6 @@ struct shampoo4_ctx_s {
             ds.push_back(d);
         }
         if (ds.empty()) return {};
-        int maxM = 0;
-        long tiles128 = 0;
-        for (auto& d : ds) {
-            maxM = std::max(maxM, d.M);
-            const long t = (d.M + 127) / 128;
-            const bool sym = (d.flags & GEMM_F_SYM) && d.M == d.N;
-            tiles128 += sym ? t * (t + 1) / 2 : t * ((d.N + 127) / 128);
-        }
-        const int cfgsel = maxM <= 32 ? GEMM_32x128 : (tiles128 >= 512 ? GEMM_128x128 : GEMM_64x64);
         int bm, bn;
         gemm_tile_dims(cfgsel, &bm, &bn);
         // a symmetric product computes the tiles on and above the diagonal (square tiles,
@@ -603,7 +679,8 @@ struct shampoo4_ctx_s {
             Seq& st = qr_steps[sidx];
             panel_launches(st, byc, maxh);
             for (auto* items : {&in1, &in2, &out1, &out2}) {
-                Seq g = make_gemm(*items, FAM_GEMM_QR, outer == kOuter);
+                const int fam = (items == &out1 || items == &out2) ? FAM_GEMM_QR_TRAIL : FAM_GEMM_QR;
+                Seq g = make_gemm(*items, fam, outer == kOuter);
                 st.insert(st.end(), g.begin(), g.end());
             }
         }
@@ -639,7 +716,7 @@ struct shampoo4_ctx_s {
                 w2.push_back({q, false, false});
             }
             for (auto* items : {&w1, &w2}) {
-                Seq g = make_gemm(*items, FAM_GEMM_QR, outer == kOuter);
+                Seq g = make_gemm(*items, FAM_GEMM_QR_Q, outer == kOuter);
                 qr_join.insert(qr_join.end(), g.begin(), g.end());
             }
         }
@@ -1618,7 +1695,13 @@ shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t tra
                             beta != 0.f ? C[i] : nullptr, beta != 0.f ? ldc[i] : 0);
         items.push_back({d, transA != 0, transB != 0});
     }
+    // one launch: the workspace holds one descriptor table and one tile prefix (the tile
+    // shape follows the products' class when they all share one)
     Seq seq = tmp.make_gemm(items, FAM_GEMM_PRECOND);
+    if (seq.size() > 1) {
+        tmp.blob.clear();
+        seq = tmp.make_gemm(items, FAM_GEMM_PRECOND, false, false);
+    }
     if (seq.empty()) return SHAMPOO4_OK;
     const Launch& L = seq[0];
     hipStream_t s = as_stream(stream);

@@ -307,8 +307,10 @@ SHAMPOO4_API shampoo4_status shampoo4_inverse_root(int32_t count, const int32_t*
  * enable != 0 starts recording (clears previous records); the report waits for the
  * device and returns, per kernel family, the number of launches, total milliseconds,
  * and algorithmic flops and bytes.  names: "gemm_bjorck", "gemm_stats", "gemm_power",
- * "gemm_qr", "gemm_rayleigh", "gemm_precond" (the matrix products by the stage they
- * serve), "dequant", "quant", "qr_panel", "rayleigh", "elementwise", "graft".  Host arrays of
+ * "gemm_qr", "gemm_qr_trail", "gemm_qr_q", "gemm_rayleigh", "gemm_precond" (the matrix
+ * products by the stage they serve; the QR's are split into the products inside an outer
+ * reflector block, the block's products on the trailing columns and the accumulation of
+ * Q), "dequant", "quant", "qr_panel", "rayleigh", "elementwise", "graft".  Host arrays of
  * length *count (in: capacity, out: used). */
 SHAMPOO4_API shampoo4_status shampoo4_timing(shampoo4_ctx ctx, int32_t enable);
 SHAMPOO4_API shampoo4_status shampoo4_timing_report(shampoo4_ctx ctx, int32_t* count, const char** names,

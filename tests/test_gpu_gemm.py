@@ -43,6 +43,10 @@ def _check(As, Bs, Ds, ta, tb, alpha, beta, Cs):
     [(1024, 1024, 1024)] * 2,             # two large products
     [(1000, 600, 77)] * 6,                # ragged edges on both sides
     [(32, 1000, 700)] * 2,                # skinny M
+    [(1000, 32, 700)] * 2,                # skinny N (128 x 32 tiles)
+    [(96, 20, 1024)] * 4,                 # skinny N, short M, long K
+    [(700, 17, 33)] * 3,                  # skinny N with unaligned rows
+    [(48, 60, 300)] * 3,                  # sides under 64 (64 x 64 tiles)
 ])
 def test_gemm_modes(ta, tb, shapes):
     require_gpu()
