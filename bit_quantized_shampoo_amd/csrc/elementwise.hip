@@ -5,7 +5,9 @@
 //                   partial sums the column-dot GEMM epilogue leaves (fixed order);
 //  * identity fill / sign flip: Q starts as I for the forward accumulation of
 //                   the reflectors and its column j is finally multiplied by
-//                   sign(R_jj) (0 -> +), so that diag(R) >= 0;
+//                   sign(R_jj) (0 -> +), so that diag(R) >= 0; the backward
+//                   accumulation (Q <- H_b Q, last block first) starts instead from
+//                   diag(sign(R_jj)), which gives the flipped Q with no second pass;
 //  * identity state: U = I coded exactly (code 15 on the diagonal, 7 elsewhere,
 //                   scale 1 for blocks holding a diagonal element, else 0), lam = 0,
 //                   root = (I, d = 1).
@@ -40,7 +42,9 @@ __global__ __launch_bounds__(256) void rayleigh_reduce_kernel(const VecDesc* __r
     d.out[j] = t > 0.f ? t : 0.f;
 }
 
-// out = I (p x p, leading dimension ld); a workgroup covers fill_rows(p) whole rows
+// out = I, or with SIGNED diag(sign(aux)) (0 -> +) (p x p, leading dimension ld); a
+// workgroup covers fill_rows(p) whole rows
+template <bool SIGNED>
 __global__ __launch_bounds__(256) void identity_fill_kernel(const VecDesc* __restrict__ descs,
                                                             const int* __restrict__ prefix, int ndesc) {
     const int item = find_item(prefix, ndesc, blockIdx.x);
@@ -51,7 +55,8 @@ __global__ __launch_bounds__(256) void identity_fill_kernel(const VecDesc* __res
     const int r1 = min(r0 + rows, p);
     for (int i = r0; i < r1; ++i) {
         float* __restrict__ row = d.out + (int64_t)i * d.ld;
-        for (int j = threadIdx.x; j < p; j += 256) row[j] = (i == j) ? 1.f : 0.f;
+        const float one = (SIGNED && d.aux[i] < 0.f) ? -1.f : 1.f;
+        for (int j = threadIdx.x; j < p; j += 256) row[j] = (i == j) ? one : 0.f;
     }
 }
 
@@ -180,10 +185,13 @@ hipError_t launch_rayleigh_reduce(const VecDesc* descs, const int* prefix, int n
     return hipGetLastError();
 }
 
-hipError_t launch_identity_fill(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+hipError_t launch_identity_fill(const VecDesc* descs, const int* prefix, int ndesc, int ntiles, bool with_signs,
                                 hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
-    S4_LAUNCH(identity_fill_kernel, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    if (with_signs)
+        S4_LAUNCH(identity_fill_kernel<true>, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
+    else
+        S4_LAUNCH(identity_fill_kernel<false>, dim3(ntiles), dim3(256), 0, stream, descs, prefix, ndesc);
     return hipGetLastError();
 }
 

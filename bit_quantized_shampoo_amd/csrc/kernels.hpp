@@ -69,7 +69,8 @@ constexpr int fill_tiles(int p) { return (p + fill_rows(p) - 1) / fill_rows(p); 
 // column-dot GEMM epilogue
 hipError_t launch_rayleigh_reduce(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
                                   uint32_t* flag, hipStream_t stream);
-hipError_t launch_identity_fill(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
+// with_signs: diag(sign(aux)) (0 -> +) instead of I
+hipError_t launch_identity_fill(const VecDesc* descs, const int* prefix, int ndesc, int ntiles, bool with_signs,
                                 hipStream_t stream);
 hipError_t launch_sign_flip(const VecDesc* descs, const int* prefix, int ndesc, int ntiles,
                             hipStream_t stream);

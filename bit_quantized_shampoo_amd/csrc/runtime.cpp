@@ -54,7 +54,8 @@ enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_I
 struct Launch {
     Kind kind = K_GEMM;
     int cfg = 0;
-    int mode = 0;        // GEMM: shared transpose flags or GEMM_MODE_MIXED; panel, QR step: rows class
+    int mode = 0;        // GEMM: shared transpose flags or GEMM_MODE_MIXED; panel, QR step: rows class;
+                         // identity fill: 1 = diag(sign(R_jj))
     int fam = FAM_ELEMENTWISE;
     size_t desc_off = 0, prefix_off = 0;   // offsets inside the descriptor region (QR step: the
                                            // panel table and the slab table)
@@ -121,6 +122,7 @@ struct shampoo4_ctx_s {
     hipStream_t cap = nullptr;
     hipGraphExec_t stats_graph[2] = {};
     Seq qinit, sign, ray_gemm, rayleigh, quant, root_d, root_copy;
+    Seq qinit_signed;                     // backward accumulation: Q starts as diag(sign(R_jj))
     Seq pre[4];
     Seq root_mat, pre_cached[2];        // ROOT_CACHE: root matrices, then two products per block
     Seq graft_seq[2];                    // per graft mode (bytes differ): norms, apply
@@ -1009,6 +1011,8 @@ struct shampoo4_ctx_s {
                 tin.push_back((int)((std::max<int64_t>(S.nqb, p) + 255) / 256));
             }
             qinit = {make_items(K_IDENTITY, qi, tqi)};
+            qinit_signed = {make_items(K_IDENTITY, qi, tqi)};
+            qinit_signed[0].mode = 1;
             sign = {make_items(K_SIGN, qi, tqi)};
             ray_gemm = make_gemm(yg, FAM_GEMM_RAYLEIGH);
             int bm = 32, bn = 128;
@@ -1183,7 +1187,7 @@ struct shampoo4_ctx_s {
                 break;
             case K_IDENTITY:
                 e = launch_identity_fill(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix,
-                                         L.ndesc, L.ntiles, s);
+                                         L.ndesc, L.ntiles, L.mode == 1, s);
                 break;
             case K_SIGN:
                 e = launch_sign_flip(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix, L.ndesc,
@@ -1288,10 +1292,14 @@ struct shampoo4_ctx_s {
         if (e == hipSuccess) e = run(stats_g, s);
         for (int it = 0; it < cfg.power_iters && e == hipSuccess; ++it) {
             e = run(it == 0 ? power_first[var] : power_next, s);
-            if (e == hipSuccess) e = run(qinit, s);
+            // forward accumulation (fused and look-ahead schedules): Q = I, reflectors, then
+            // the column signs; backward (blocked): the factorization, then Q from the signs
+            const bool backward_q = !fused && !lookahead;
+            if (e == hipSuccess && !backward_q) e = run(qinit, s);
             for (size_t p = 0; p < qr_steps.size() && e == hipSuccess; ++p) e = run(qr_steps[p], s);
+            if (e == hipSuccess && backward_q) e = run(qinit_signed, s);
             if (e == hipSuccess) e = run(qr_join, s);
-            if (e == hipSuccess) e = run(sign, s);
+            if (e == hipSuccess && !backward_q) e = run(sign, s);
         }
         if (e == hipSuccess) e = run(ray_gemm, s);
         if (e == hipSuccess) e = run(rayleigh, s);
