@@ -808,13 +808,28 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_global_kernel(const Panel
         }
         __syncthreads();
     }
+    // Rows are visited GU at a time with every load of a batch issued before any use:
+    // the panel lives in L2, and a row-at-a-time loop waits one L2 round trip per row.
+    // Addresses are clamped into the panel and out-of-range values masked.
+    constexpr int GU = 16;
+    const int cc = c < nb ? c : nb - 1;
     {
         float pacc = 0.f, rj = 0.f;
-        for (int r = slot; r < h; r += NSLOT) {
-            const float xv = (c < nb) ? Ap[r * ld + c] : 0.f;
-            const float x0 = Ap[r * ld];
-            pacc += x0 * xv;
-            if (r == 0) rj = xv;
+        for (int rb = slot; rb < h; rb += NSLOT * GU) {
+            float xv[GU], x0[GU];
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                const int r = min(rb + NSLOT * u, h - 1);
+                xv[u] = Ap[(int64_t)r * ld + cc];
+                x0[u] = Ap[(int64_t)r * ld];
+            }
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                const int r = rb + NSLOT * u;
+                const float x = (c < nb && r < h) ? xv[u] : 0.f;
+                pacc = fmaf(x0[u], x, pacc);
+                if (r == 0) rj = x;
+            }
         }
         write_partial(smem, 0, c, lane, wv, pacc);
         if (slot == 0) smem[OFF_ROWJ + c] = rj;
@@ -842,20 +857,31 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_global_kernel(const Panel
         const int jn = j + 1;
         float pacc = 0.f, rj = 0.f;
         const int r0 = j + ((slot - (j & (NSLOT - 1)) + NSLOT) & (NSLOT - 1));
-        for (int r = r0; r < h; r += NSLOT) {
-            float xv = (c < nb) ? Ap[r * ld + c] : 0.f;
-            const float xj = Ap[r * ld + j];
-            const float vr = (r == j) ? 1.f : R.sc * xj;
-            if (c == j) {
-                xv = (r == j) ? R.beta : vr;
-                Ap[r * ld + c] = xv;
-            } else if (c > j && c < nb) {
-                xv -= f * vr;
-                Ap[r * ld + c] = xv;
+        for (int rb = r0; rb < h; rb += NSLOT * GU) {
+            float xv[GU], xj[GU];
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                const int r = min(rb + NSLOT * u, h - 1);
+                xv[u] = Ap[(int64_t)r * ld + cc];
+                xj[u] = Ap[(int64_t)r * ld + j];
             }
-            const float xn = __shfl(xv, jn, 32);
-            if (r >= jn) pacc += xn * xv;
-            if (r == jn) rj = xv;
+#pragma unroll
+            for (int u = 0; u < GU; ++u) {
+                const int r = rb + NSLOT * u;
+                const bool in = r < h;
+                float x = c < nb ? xv[u] : 0.f;
+                const float vr = (r == j) ? 1.f : R.sc * xj[u];
+                if (in && c == j) {
+                    x = (r == j) ? R.beta : vr;
+                    Ap[(int64_t)r * ld + c] = x;
+                } else if (in && c > j && c < nb) {
+                    x -= f * vr;
+                    Ap[(int64_t)r * ld + c] = x;
+                }
+                const float xn = __shfl(x, jn, 32);
+                if (in && r >= jn) pacc += xn * x;
+                if (in && r == jn) rj = x;
+            }
         }
         write_partial(smem, buf ^ 1, c, lane, wv, pacc);
         if (slot == (jn & (NSLOT - 1))) smem[OFF_ROWJ + (buf ^ 1) * 32 + c] = rj;
