@@ -63,8 +63,14 @@ constexpr int OFF_RD = OFF_RED + NWAVE;          // [32] R diagonal (written out
 // the same instruction, so the slot pitch is offset by 4 banks from a multiple of the bank
 // count (64 + 4 floats): the two 16-byte broadcasts hit different banks.
 constexpr int COL_PITCH = 68;
-constexpr int OFF_COL = ((OFF_RD + PW + 3) / 4) * 4;  // [NSLOT][COL_PITCH]
-constexpr int OFF_VS = OFF_COL + NSLOT * COL_PITCH;  // [hpad][33] V staging (register variant)
+// Two-column layout (panels of more than 192 rows): row group G's slice of the pivot column
+// at G * COL2_PITCH; the four row groups of a wave read theirs in one instruction, so the
+// pitch sits 4 banks off a multiple of the bank count.
+constexpr int NGRP = PANEL_THREADS / 16;     // row groups of 16 lanes
+constexpr int COL2_PITCH = 36;
+constexpr int COL_AREA = NSLOT * COL_PITCH > NGRP * COL2_PITCH ? NSLOT * COL_PITCH : NGRP * COL2_PITCH;
+constexpr int OFF_COL = ((OFF_RD + PW + 3) / 4) * 4;  // [NSLOT][COL_PITCH] or [NGRP][COL2_PITCH]
+constexpr int OFF_VS = OFF_COL + COL_AREA;  // [rows][33] V staging / layout transpose (register variant)
 constexpr int OFF_VS_T12 = OFF_COL;              // [16][16] scratch of build_T (after the loop)
 static_assert(NWAVE == 8, "partials are read as two 16-byte vectors");
 
@@ -469,6 +475,236 @@ struct PanelExtra {
 // MODE 1: a panel of a fused QR step: writes V and T (the consumers apply T themselves).
 // MODE 2: as 1, after first applying the previous panel's block I - Vp Tp Vp^T (transposed,
 //         from the left) to the panel's columns, in registers.
+// Value of the lane in the partner 16-lane row (rows 0-1 and 2-3 pair up), and in the other
+// 32-lane half (v_permlane16_swap / v_permlane32_swap of a value with itself).
+__device__ __forceinline__ float other_row16(float v, int lane) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 16) ? sw[0] : sw[1]);
+}
+__device__ __forceinline__ float other_half32(float v, int lane) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((lane & 32) ? sw[0] : sw[1]);
+}
+// Sum over the four 16-lane rows of a wave, the same value in every lane.
+__device__ __forceinline__ float rows4_sum(float v, int lane) {
+    const float a = v + other_row16(v, lane);
+    return a + other_half32(a, lane);
+}
+
+// The reflector loop and the outputs of panels with more than 192 rows (16 or more rows per
+// lane in the one-column layout), two columns per lane.
+// With one column per lane, step j's pivot column lives in one lane of each half-wave,
+// which stores NR values for its half-wave to read back: NR/4 16-byte LDS stores per wave
+// and step with two active lanes each, and those stores (not the reads, which are
+// same-address broadcasts) are what a step of a tall panel waits on.  Here lane bits 0..3
+// pick the column pair (c16, c16 + 16) and bits 4..5 the row group: row group
+// G = 4 wv + g owns rows G + 32 i, so the pivot column of a row group still sits in one
+// lane, but the four row groups of a wave store their NR/2 values in the same instructions
+// (half the stores).  The panel is handed over from the one-column layout of the load and
+// the previous block's application through LDS (rows x 33 floats).
+template <int NR, int MODE>
+__device__ __forceinline__ void panel_two_cols(const PanelDesc& d, const PanelExtra& ex, float* smem,
+                                               const float (&x)[NR]) {
+    static_assert(NR % 2 == 0, "two rows of the one-column layout per row of the two-column one");
+    constexpr int NR2 = NR / 2;
+    const int h = d.h, nb = d.nb;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    const int c = lane & 31;
+    const int slot = wv * 2 + (lane >> 5);
+    const int c16 = lane & 15;
+    const int g = lane >> 4;
+    const int G = 4 * wv + g;
+    // hand-over: rows slot + 16 i of column c -> LDS -> rows G + 32 i of columns c16, c16 + 16
+    float* tr = smem + OFF_VS;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) tr[(slot + NSLOT * i) * 33 + c] = x[i];
+    __syncthreads();
+    float y[2][NR2], yc[NR2];
+#pragma unroll
+    for (int i = 0; i < NR2; ++i) {
+        const float* row = tr + (G + NGRP * i) * 33;
+        y[0][i] = row[c16];
+        y[1][i] = row[c16 + 16];
+        yc[i] = row[0];
+    }
+    {   // dots with column 0, row 0 of every column
+        float pacc[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NR2; ++i)
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) pacc[sl] = fmaf(yc[i], y[sl][i], pacc[sl]);
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const float t = rows4_sum(pacc[sl], lane);
+            if (g == 0) smem[OFF_PART + (c16 + 16 * sl) * PSTR + wv] = t;
+        }
+        if (G == 0) {
+            smem[OFF_ROWJ + c16] = y[0][0];
+            smem[OFF_ROWJ + c16 + 16] = y[1][0];
+        }
+    }
+    __syncthreads();
+
+    float* colb = smem + OFF_COL + G * COL2_PITCH;
+    for (int j = 0; j < nb; ++j) {
+        const int buf = j & 1;
+        const int jn = j + 1;
+        // even row groups sum column c16's partials, odd ones column c16 + 16's; lane j
+        // (row group j >> 4, c16 = j & 15) holds the pivot column's
+        const int sr = g & 1;
+        const float dm = read_d(smem, buf, c16 + 16 * sr);
+        const float am = read_row(smem, buf, c16 + 16 * sr);
+        const float dmo = other_row16(dm, lane);
+        const float amo = other_row16(am, lane);
+        const float dcs[2] = {sr ? dmo : dm, sr ? dm : dmo};
+        const float acs[2] = {sr ? amo : am, sr ? am : amo};
+        const float dj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dm), j));
+        const float alpha = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(am), j));
+        const Refl R = reflector(alpha, dj);
+        float sv[2], coef[2], dval[2], dkeep[2], dsub[2];
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int cs = c16 + 16 * sl;
+            sv[sl] = (cs < nb && cs != j) ? R.sc * (dcs[sl] - R.beta * acs[sl]) : 0.f;
+            const float f = R.tau * sv[sl];
+            coef[sl] = (cs == j) ? R.sc - 1.f : ((cs > j) ? -f * R.sc : 0.f);
+            dval[sl] = (cs == j) ? R.beta : 0.f;
+            dkeep[sl] = (cs == j) ? 0.f : 1.f;
+            dsub[sl] = (cs > j) ? f : 0.f;
+        }
+        if (G == 0) {
+            smem[OFF_SALL + c16 * 33 + j] = sv[0];
+            smem[OFF_SALL + (c16 + 16) * 33 + j] = sv[1];
+            if (c16 == 0) {
+                smem[OFF_TAU + j] = R.tau;
+                smem[OFF_RD + j] = R.beta;
+            }
+        }
+        // update (rows below j: y + coef yc; row j: the pivot lane stores beta, later columns
+        // subtract f); columns 0..15 are all final once j > 15
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            if (sl == 0 && j > 15) continue;
+#pragma unroll
+            for (int i = 0; i < NR2; ++i) {
+                const float xv = y[sl][i];
+                float nx = fmaf(coef[sl], yc[i], xv);
+                if (i == 0) {
+                    const float dgv = fmaf(dkeep[sl], xv, dval[sl]) - dsub[sl];
+                    nx = (G < j) ? xv : ((G == j) ? dgv : nx);
+                }
+                y[sl][i] = nx;
+            }
+        }
+        // column jn of this row group's rows, from its lane (c16 = jn & 15)
+        if (jn < nb && c16 == (jn & 15)) {
+            const int sn = jn >> 4;
+            float vn[NR2];
+#pragma unroll
+            for (int i = 0; i < NR2; ++i) vn[i] = sn ? y[1][i] : y[0][i];
+            if constexpr (NR2 % 4 == 0) {
+#pragma unroll
+                for (int q = 0; q < NR2 / 4; ++q) {
+                    const floatx4 v = {vn[4 * q], vn[4 * q + 1], vn[4 * q + 2], vn[4 * q + 3]};
+                    *reinterpret_cast<floatx4*>(colb + 4 * q) = v;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NR2; ++i) colb[i] = vn[i];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float xn[NR2];
+        if constexpr (NR2 % 4 == 0) {
+#pragma unroll
+            for (int q = 0; q < NR2 / 4; ++q) {
+                const floatx4 v = *reinterpret_cast<const floatx4*>(colb + 4 * q);
+                xn[4 * q] = v[0]; xn[4 * q + 1] = v[1]; xn[4 * q + 2] = v[2]; xn[4 * q + 3] = v[3];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NR2; ++i) xn[i] = colb[i];
+        }
+        float pacc[2] = {0.f, 0.f}, rj[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NR2; ++i) {
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                if (i == 0) {   // rows 0..31: only rows >= jn count
+                    pacc[sl] += (G >= jn) ? xn[0] * y[sl][0] : 0.f;
+                    rj[sl] = (G == jn) ? y[sl][0] : rj[sl];
+                } else {
+                    pacc[sl] = fmaf(xn[i], y[sl][i], pacc[sl]);
+                }
+            }
+            yc[i] = xn[i];
+        }
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const float t = rows4_sum(pacc[sl], lane);
+            if (g == 0) smem[OFF_PART + (buf ^ 1) * PART + (c16 + 16 * sl) * PSTR + wv] = t;
+        }
+        if (G == jn) {
+            smem[OFF_ROWJ + (buf ^ 1) * 32 + c16] = rj[0];
+            smem[OFF_ROWJ + (buf ^ 1) * 32 + c16 + 16] = rj[1];
+        }
+        __syncthreads();
+    }
+
+    if (tid < nb) d.rdiag[d.c0 + tid] = smem[OFF_RD + tid];
+    float* Vt = d.V + (int64_t)d.zrows * d.vld;
+    auto vval = [&](int sl, int i) {
+        const int r = G + NGRP * i, cs = c16 + 16 * sl;
+        float v = 0.f;
+        if (r < h && cs < nb) v = (r > cs) ? y[sl][i] : (r == cs ? 1.f : 0.f);
+        return v;
+    };
+    if constexpr (MODE == 0) {
+        // explicit V to global and to LDS (rows padded to 32 with zeros), then Y = V T
+        float* Vs = smem + OFF_VS;
+        float* Yt = d.Y + (int64_t)d.zrows * d.vld;
+        const int hpad = (h + 31) & ~31;
+#pragma unroll
+        for (int i = 0; i < NR2; ++i) {
+            const int r = G + NGRP * i;
+            if (r < hpad) {
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) {
+                    const float v = vval(sl, i);
+                    Vs[r * 33 + c16 + 16 * sl] = v;
+                    if (r < h) Vt[(int64_t)r * d.vld + c16 + 16 * sl] = v;
+                }
+            }
+        }
+        build_T(smem, nb, tid);
+        zero_above(d, tid);
+        __syncthreads();
+        form_Y(Vs, 33, smem, Yt, d.vld, h, tid);
+    } else {
+        auto write_v = [&]() {
+#pragma unroll
+            for (int i = 0; i < NR2; ++i) {
+                const int r = G + NGRP * i;
+                if (r < h) {
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl) stg(Vt + (int64_t)r * d.vld + c16 + 16 * sl, vval(sl, i));
+                }
+            }
+        };
+        if (wv != 0) write_v();
+        build_T_diag(smem, nb, tid);
+        if (wv == 0) write_v();
+        __syncthreads();
+        build_T_offdiag(smem, nb, tid);
+        __syncthreads();
+        for (int e = tid; e < PW * PW; e += PANEL_THREADS) stg(ex.T + e, smem[OFF_T + (e >> 5) * 33 + (e & 31)]);
+    }
+}
+
 template <int NR, int MODE>
 __device__ __forceinline__ void panel_body(const PanelDesc& d, const PanelExtra& ex, float* smem) {
     const int h = d.h, nb = d.nb;
@@ -599,6 +835,10 @@ __device__ __forceinline__ void panel_body(const PanelDesc& d, const PanelExtra&
 #pragma unroll
             for (int i = 0; i < NR; ++i) x[i] = ldexpf(x[i], -e);
         }
+    }
+    if constexpr (NR >= 16) {
+        panel_two_cols<NR, MODE>(d, ex, smem, x);
+        return;
     }
     {   // dots for column 0
         float pacc = 0.f;
@@ -928,10 +1168,19 @@ hipError_t launch_step(const StepPanelDesc* panels, int npanel, const SlabDesc* 
 
 }  // namespace
 
-size_t qr_step_lds_bytes(int) {
+// rows of the layout hand-over buffer of a panel of up to max_h rows (two-column path,
+// 16 or more rows per lane)
+static int handover_rows(int max_h) {
+    const int nr = panel_rows_class(max_h < 1 ? 1 : max_h);
+    return nr >= 16 ? NSLOT * nr : 0;
+}
+
+size_t qr_step_lds_bytes(int max_h) {
     // the fused panel keeps V in registers and writes it to global directly; LDS holds the
-    // fixed panel area and the partial products of the block applications
-    return (size_t)(OFF_VS + WY_PART) * sizeof(float);
+    // fixed panel area and the partial products of the block applications or the layout
+    // hand-over of a tall panel
+    const int tail = handover_rows(max_h) * 33 > WY_PART ? handover_rows(max_h) * 33 : WY_PART;
+    return (size_t)(OFF_VS + tail) * sizeof(float);
 }
 
 hipError_t launch_qr_step(int rows_class, const StepPanelDesc* panels, int npanel, const SlabDesc* slabs,
@@ -954,8 +1203,9 @@ int panel_rows_class(int h) {
 
 size_t panel_lds_bytes(bool in_regs, int max_h) {
     const size_t fixed = (size_t)OFF_VS * sizeof(float);
-    const size_t hpad = (size_t)((max_h + 31) & ~31);
-    return fixed + (in_regs ? hpad * 33 * sizeof(float) : 0);
+    const int hpad = (max_h + 31) & ~31;
+    const int rows = handover_rows(max_h) > hpad ? handover_rows(max_h) : hpad;
+    return fixed + (in_regs ? (size_t)rows * 33 * sizeof(float) : 0);
 }
 
 hipError_t launch_panel(int rows_class, const PanelDesc* descs, int ndesc, int max_h,
