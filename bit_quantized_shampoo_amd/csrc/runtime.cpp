@@ -105,6 +105,10 @@ struct shampoo4_ctx_s {
     Seq deq_stats, deq_root, init_seq;
     std::vector<Seq> bj_stats, bj_root;
     Seq stats_x[2], stats_g, power_first[2], power_next;
+    // statistics with (1 - beta) G G^T folded into the first Bjorck Gram launch (which
+    // does not fill the GPU by itself) and beta V diag(lam) V^T added onto it
+    std::vector<Seq> bj_stats_fold;
+    Seq stats_x_fold;
     std::vector<Seq> qr_steps;            // per panel index: panel, block and trailing products
     Seq qr_join;                          // second stream's work joined back (look-ahead plans)
     int outer = kOuter;                   // columns whose reflectors update the trailing matrix together
@@ -460,7 +464,9 @@ struct shampoo4_ctx_s {
     }
     static int copyf_tiles(int64_t n) { return (int)((n + COPYF_TILE - 1) / COPYF_TILE); }
 
-    void build_bjorck(bool root, Seq& deq, std::vector<Seq>& iters) {
+    // gram0_extra: products that ride in the first iteration's Gram launch
+    void build_bjorck(bool root, Seq& deq, std::vector<Seq>& iters,
+                      const std::vector<GemmItem>* gram0_extra = nullptr) {
         const int k = cfg.bjorck_iters;
         std::vector<CodecDesc> cds;
         std::vector<int> tiles;
@@ -510,6 +516,7 @@ struct shampoo4_ctx_s {
                 upd.push_back({gd(wsf(in), p, wsf(S.Wg), p, wsf(out), p, p, p, p, -0.5f, 1.5f, wsf(in), p),
                                false, false});
             }
+            if (i == 0 && gram0_extra) gram.insert(gram.end(), gram0_extra->begin(), gram0_extra->end());
             Seq s = make_gemm(gram, FAM_GEMM_BJORCK);
             Seq u = make_gemm(upd, FAM_GEMM_BJORCK);
             s.insert(s.end(), u.begin(), u.end());
@@ -953,6 +960,34 @@ struct shampoo4_ctx_s {
             }
             stats_g = make_gemm(gs, FAM_GEMM_STATS);
             power_next = make_gemm(pn, FAM_GEMM_POWER);
+            // folded form: Lt = (1 - beta) G G^T in the Gram launch, then += beta V diag(lam) V^T
+            // (taken when the Gram launch leaves the GPU's workgroup slots idle; a full
+            // one would gain only a launch and lose the single-transpose kernel)
+            bj_stats_fold.clear();
+            stats_x_fold.clear();
+            long gram_tiles = 0;   // 128 x 128 tiles of the Gram products
+            for (auto& S : sides) {
+                const long t = (S.p + 127) / 128;
+                gram_tiles += t * (t + 1) / 2;
+            }
+            if (cfg.bjorck_iters > 0 && gram_tiles < 512) {
+                for (auto& it : gs) {
+                    it.d.beta = 0.f;
+                    it.d.C = nullptr;
+                }
+                Seq unused;
+                build_bjorck(false, unused, bj_stats_fold, &gs);
+                std::vector<GemmItem> xs;
+                for (auto& S : sides) {
+                    const int p = S.p;
+                    const float* V = wsf(S.Vs);
+                    GemmDesc d = gd(V, p, V, p, wsf(S.Lt), p, p, p, p, beta, 1.f, wsf(S.Lt), p);
+                    d.kscale = stf(S.lam);
+                    d.flags |= GEMM_F_SYM;
+                    xs.push_back({d, false, true});
+                }
+                stats_x_fold = make_gemm(xs, FAM_GEMM_STATS);
+            }
         }
 
         {   // panel-wide blocks on one stream run as fused QR steps when every panel fits
@@ -1283,13 +1318,18 @@ struct shampoo4_ctx_s {
     hipError_t stats_body(bool reuse, hipStream_t s) {
         const int var = reuse ? 1 : 0;
         hipError_t e = hipSuccess;
+        const bool fold = !reuse && !bj_stats_fold.empty();
         if (!reuse) {
             e = run(deq_stats, s);
-            for (auto& it : bj_stats)
+            for (auto& it : (fold ? bj_stats_fold : bj_stats))
                 if (e == hipSuccess) e = run(it, s);
         }
-        if (e == hipSuccess) e = run(stats_x[var], s);
-        if (e == hipSuccess) e = run(stats_g, s);
+        if (fold) {
+            if (e == hipSuccess) e = run(stats_x_fold, s);
+        } else {
+            if (e == hipSuccess) e = run(stats_x[var], s);
+            if (e == hipSuccess) e = run(stats_g, s);
+        }
         for (int it = 0; it < cfg.power_iters && e == hipSuccess; ++it) {
             e = run(it == 0 ? power_first[var] : power_next, s);
             // forward accumulation (fused and look-ahead schedules): Q = I, reflectors, then
