@@ -98,6 +98,7 @@ struct shampoo4_ctx_s {
     std::vector<Side> sides;             // 2 per block: L then R
     std::vector<size_t> X1, X2;          // per block precondition temporaries
     size_t io_off = 0, gio_off = 0, flag_off = 0, parts_off = 0, desc_base = 0;
+    std::vector<uint8_t> last_io, last_gio;   // host copies of the tables last uploaded
     std::vector<uint8_t> blob;           // descriptor region contents
     size_t lds_limit = 0;                // bytes of LDS one workgroup may use
     int max_panels = 0;
@@ -1298,8 +1299,13 @@ struct shampoo4_ctx_s {
     }
 
     // One per-call table (nb entries of 32 bytes) through a pinned staging slot.
+    // A table equal to the one last uploaded to the same slot is not sent again (calls
+    // on a context are ordered on one stream, so the device copy is already current).
     hipError_t upload_table(const void* table, size_t dev_off, hipStream_t s) {
         const size_t bytes = (size_t)nb * sizeof(IoEntry);
+        std::vector<uint8_t>& last = dev_off == io_off ? last_io : last_gio;
+        const uint8_t* src = static_cast<const uint8_t*>(table);
+        if (last.size() == bytes && std::memcmp(last.data(), src, bytes) == 0) return hipSuccess;
         const int slot = ring_next;
         ring_next = (ring_next + 1) % kRing;
         if (ring_used[slot]) {
@@ -1311,7 +1317,9 @@ struct shampoo4_ctx_s {
         hipError_t e = hipMemcpyAsync(ws + dev_off, dst, bytes, hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return e;
         ring_used[slot] = true;
-        return hipEventRecord(ring_ev[slot], s);
+        e = hipEventRecord(ring_ev[slot], s);
+        if (e == hipSuccess) last.assign(src, src + bytes);
+        return e;
     }
 
     // The kernels of one statistics update (everything after the io upload).
