@@ -27,7 +27,7 @@ BUF_V, BUF_STAT, BUF_Q, BUF_ROOT_V = 16, 17, 18, 19
 
 EXPORTED = [
     "shampoo4_abi_version", "shampoo4_strerror", "shampoo4_plan", "shampoo4_init",
-    "shampoo4_update_stats", "shampoo4_refresh_root", "shampoo4_precondition",
+    "shampoo4_update_stats", "shampoo4_refresh_root", "shampoo4_precondition", "shampoo4_step",
     "shampoo4_check", "shampoo4_destroy", "shampoo4_layout", "shampoo4_quantize",
     "shampoo4_dequantize", "shampoo4_codebook", "shampoo4_quantize_ex", "shampoo4_dequantize_ex",
     "shampoo4_codebook_ex", "shampoo4_gemm_workspace_bytes",
@@ -93,6 +93,7 @@ def lib() -> ctypes.CDLL:
         "shampoo4_update_stats": (st, [vp, ctypes.POINTER(Io), vp]),
         "shampoo4_refresh_root": (st, [vp, vp]),
         "shampoo4_precondition": (st, [vp, ctypes.POINTER(Io), vp]),
+        "shampoo4_step": (st, [vp, ctypes.POINTER(Io), i32, vp]),
         "shampoo4_check": (st, [vp, vp, ctypes.POINTER(u32)]),
         "shampoo4_destroy": (st, [vp]),
         "shampoo4_layout": (st, [vp, i32, i32, ctypes.c_int, ctypes.POINTER(sz), ctypes.POINTER(sz)]),

@@ -119,6 +119,10 @@ struct shampoo4_ctx_s {
     int codebook = SHAMPOO4_CODEBOOK_LINEAR_SQUARE;   // 4-bit codebook of U and the root
     int n_sync = 0;                       // synchronization events the plan uses
     hipStream_t aux = nullptr;
+    // precondition overlapped with the statistics update (shampoo4_step): its stream and
+    // the fork / join events, created on first use
+    hipStream_t pre_strm = nullptr;
+    hipEvent_t pre_fork = nullptr, pre_join = nullptr;
     std::vector<hipEvent_t> sync_ev;
     // update_stats replayed from a HIP graph (captured on `cap` at the first call of each
     // variant: with or without the cached rectified eigenvectors)
@@ -159,6 +163,9 @@ struct shampoo4_ctx_s {
         for (auto& g : stats_graph)
             if (g) (void)hipGraphExecDestroy(g);
         if (aux) (void)hipStreamDestroy(aux);
+        if (pre_strm) (void)hipStreamDestroy(pre_strm);
+        if (pre_fork) (void)hipEventDestroy(pre_fork);
+        if (pre_join) (void)hipEventDestroy(pre_join);
         if (cap) (void)hipStreamDestroy(cap);
         if (pinned) (void)hipHostFree(pinned);
     }
@@ -1323,7 +1330,9 @@ struct shampoo4_ctx_s {
     }
 
     // The kernels of one statistics update (everything after the io upload).
-    hipError_t stats_body(bool reuse, hipStream_t s) {
+    // fork: recorded on s where the QR of the first power step begins (work forked from
+    // there shares the GPU with the latency-bound panel chain rather than the products)
+    hipError_t stats_body(bool reuse, hipStream_t s, hipEvent_t fork = nullptr) {
         const int var = reuse ? 1 : 0;
         hipError_t e = hipSuccess;
         const bool fold = !reuse && !bj_stats_fold.empty();
@@ -1340,6 +1349,7 @@ struct shampoo4_ctx_s {
         }
         for (int it = 0; it < cfg.power_iters && e == hipSuccess; ++it) {
             e = run(it == 0 ? power_first[var] : power_next, s);
+            if (e == hipSuccess && it == 0 && fork) e = hipEventRecord(fork, s);
             // forward accumulation (fused and look-ahead schedules): Q = I, reflectors, then
             // the column signs; backward (blocked): the factorization, then Q from the signs
             const bool backward_q = !fused && !lookahead;
@@ -1352,6 +1362,37 @@ struct shampoo4_ctx_s {
         if (e == hipSuccess) e = run(ray_gemm, s);
         if (e == hipSuccess) e = run(rayleigh, s);
         if (e == hipSuccess) e = run(quant, s);
+        return e;
+    }
+
+    // The statistics update after its io upload: graph replay or eager launches.
+    // fork (optional): an event recorded where the QR begins (before the whole update
+    // when it is replayed from a graph, or when no power step runs)
+    hipError_t submit_stats(hipStream_t s, hipEvent_t fork = nullptr) {
+        const bool reuse = (cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) && root_v_valid && root_v_is_stats;
+        const int var = reuse ? 1 : 0;
+        hipError_t e = hipSuccess;
+        if (use_graphs && graph_ok && !timing) {
+            if (!stats_graph[var]) capture_stats(reuse);
+            if (stats_graph[var]) {
+                if (fork) e = hipEventRecord(fork, s);
+                if (e == hipSuccess) e = hipGraphLaunch(stats_graph[var], s);
+            } else {
+                e = stats_body(reuse, s, fork);
+            }
+        } else {
+            e = stats_body(reuse, s, fork);
+        }
+        if (e == hipSuccess && fork && cfg.power_iters < 1) e = hipEventRecord(fork, s);
+        root_v_is_stats = false;
+        return e;
+    }
+
+    hipError_t ensure_pre_stream() {
+        if (pre_strm) return hipSuccess;
+        hipError_t e = hipEventCreateWithFlags(&pre_fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&pre_join, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipStreamCreateWithFlags(&pre_strm, hipStreamNonBlocking);
         return e;
     }
 
@@ -1538,16 +1579,7 @@ shampoo4_status shampoo4_update_stats(shampoo4_ctx c, const shampoo4_io* io, voi
     if (st != SHAMPOO4_OK) return st;
     hipStream_t s = as_stream(stream);
     if (c->upload_io(io, s) != hipSuccess) return SHAMPOO4_EHIP;
-    const bool reuse = (c->cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) && c->root_v_valid && c->root_v_is_stats;
-    hipError_t e = hipSuccess;
-    if (c->use_graphs && c->graph_ok && !c->timing) {
-        if (!c->stats_graph[reuse ? 1 : 0]) c->capture_stats(reuse);
-        e = c->stats_graph[reuse ? 1 : 0] ? hipGraphLaunch(c->stats_graph[reuse ? 1 : 0], s) : c->stats_body(reuse, s);
-    } else {
-        e = c->stats_body(reuse, s);
-    }
-    c->root_v_is_stats = false;
-    return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+    return c->submit_stats(s) == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
 
 shampoo4_status shampoo4_refresh_root(shampoo4_ctx c, void* stream) {
@@ -1581,6 +1613,35 @@ shampoo4_status shampoo4_precondition(shampoo4_ctx c, const shampoo4_io* io, voi
     } else {
         for (int i = 0; i < 4 && e == hipSuccess; ++i) e = c->run(c->pre[i], s);
     }
+    return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+}
+
+shampoo4_status shampoo4_step(shampoo4_ctx c, const shampoo4_io* io, int32_t refresh, void* stream) {
+    if (!c) return SHAMPOO4_EINVAL;
+    shampoo4_status st = validate_io(c, io, true);
+    if (st != SHAMPOO4_OK) return st;
+    // (batches large enough for the blocked QR keep the GPU busy by themselves: there
+    // the three parts run in order)
+    const bool overlap = !refresh && (c->cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) && c->root_v_valid &&
+                         c->outer == kPanel;
+    if (!overlap) {
+        st = shampoo4_update_stats(c, io, stream);
+        if (st == SHAMPOO4_OK && refresh) st = shampoo4_refresh_root(c, stream);
+        if (st == SHAMPOO4_OK) st = shampoo4_precondition(c, io, stream);
+        return st;
+    }
+    // P = Rt_L G Rt_R reads only the cached root matrices, G and its own temporaries,
+    // none of which the statistics update touches: it runs on a second stream (default
+    // priority) beside the statistics chain, from where that chain's QR begins (its
+    // panels leave most CUs idle).
+    hipStream_t s = as_stream(stream);
+    if (c->ensure_pre_stream() != hipSuccess) return SHAMPOO4_EHIP;
+    if (c->upload_io(io, s) != hipSuccess) return SHAMPOO4_EHIP;
+    hipError_t e = c->submit_stats(s, c->pre_fork);
+    if (e == hipSuccess) e = hipStreamWaitEvent(c->pre_strm, c->pre_fork, 0);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = c->run(c->pre_cached[i], c->pre_strm);
+    if (e == hipSuccess) e = hipEventRecord(c->pre_join, c->pre_strm);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, c->pre_join, 0);
     return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
 

@@ -143,11 +143,15 @@ class Shampoo4Blocks:
         return outs
 
     def step(self, grads, t: int, root_interval: int = 1, outs=None, stream=None):
-        """update_stats, refresh_root when t % root_interval == 0, precondition."""
-        self.update_stats(grads, stream)
-        if t % root_interval == 0:
-            self.refresh_root(stream)
-        return self.precondition(grads, outs, stream)
+        """update_stats, refresh_root when t % root_interval == 0, precondition, as one
+        call (shampoo4_step: without a refresh, the precondition runs beside the
+        statistics update on a second stream)."""
+        if outs is None:
+            outs = [torch.empty((m, n), dtype=torch.float32, device=self.device) for (m, n) in self.shapes]
+        io = self._io(grads, outs)
+        refresh = int(t % root_interval == 0)
+        L.check(L.lib().shampoo4_step(self._ctx, io, refresh, _stream_ptr(stream)), "shampoo4_step")
+        return outs
 
     def graft(self, grads, directions, weights, moments=None, *, mode: str = "sgd", lr: float = 1.0,
               eps_graft: float = 1e-8, step: int = 1, beta1: float = 0.9, beta2: float = 0.999,

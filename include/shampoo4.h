@@ -192,6 +192,17 @@ SHAMPOO4_API shampoo4_status shampoo4_refresh_root(shampoo4_ctx ctx, void* strea
 /* Preconditioned direction of every block into io[b].P. */
 SHAMPOO4_API shampoo4_status shampoo4_precondition(shampoo4_ctx ctx, const shampoo4_io* io, void* stream);
 
+/* One optimizer step of every block, the order of the blog's "Algorithm" section:
+ * the statistics update, the root refresh when `refresh` is nonzero, then the
+ * preconditioned direction into io[b].P (io as for shampoo4_precondition).  Results
+ * equal, bit for bit, those of the three calls above in that order.  Without a refresh
+ * and with SHAMPOO4_FLAG_ROOT_CACHE and valid cached roots, the preconditioned direction
+ * only reads the cached root matrices and G, so it runs on a second stream of the
+ * context (default priority) beside the statistics update; the call makes `stream`
+ * wait for it before returning, so later work on `stream` sees P.  Errors as for the
+ * three calls; a failed validation enqueues nothing. */
+SHAMPOO4_API shampoo4_status shampoo4_step(shampoo4_ctx ctx, const shampoo4_io* io, int32_t refresh, void* stream);
+
 /* Grafting and the weight update ("Shampoo -- Second-Order Optimizer", section
  * "Grafting: borrow a step size that already works"): per block,
  *     W <- W - lr * ||d_graft||_F / (||P||_F + eps_graft) * P

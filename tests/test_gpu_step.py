@@ -390,3 +390,35 @@ def test_graph_replays_match_eager(qr):
             assert torch.equal(a, b), (qr, t, "P")
     eager.close()
     graph.close()
+
+
+@pytest.mark.parametrize("qr", ["auto", "blocked"])
+def test_step_call_matches_separate_calls(qr):
+    """shampoo4_step (precondition beside the statistics update on a second stream when
+    no refresh is due) leaves the state and P bit-identical to update_stats,
+    refresh_root and precondition called one after another on one stream, over steps
+    with and without a refresh, with and without cached roots."""
+    require_gpu()
+    from bit_quantized_shampoo_amd import Shampoo4Blocks, Shampoo4Config
+    shapes = [(96, 64), (130, 200), (512, 384)]
+    rng = np.random.default_rng(21)
+    Gs = [[to_dev(rng.standard_normal(s).astype(np.float32)) for s in shapes] for _ in range(7)]
+    for cache in (True, False):
+        announce(f"step call vs separate calls qr={qr} root_cache={cache}")
+        one = Shampoo4Blocks(shapes, Shampoo4Config(root_cache=cache, qr_schedule=qr))
+        sep = Shampoo4Blocks(shapes, Shampoo4Config(root_cache=cache, qr_schedule=qr))
+        for t in range(1, 8):
+            P1 = one.step(Gs[t - 1], t, root_interval=3)
+            sep.update_stats(Gs[t - 1])
+            if t % 3 == 0:
+                sep.refresh_root()
+            P2 = sep.precondition(Gs[t - 1])
+            torch.cuda.synchronize()
+            for b in range(len(shapes)):
+                assert torch.equal(P1[b], P2[b]), (qr, cache, t, b, "P")
+                for s_ in (0, 1):
+                    s1, s2 = one.side_state(b, s_), sep.side_state(b, s_)
+                    for k in s1:
+                        assert np.array_equal(s1[k], s2[k]), (qr, cache, t, b, s_, k)
+        one.close()
+        sep.close()
