@@ -63,7 +63,10 @@ constexpr int OFF_RD = OFF_RED + NWAVE;          // [32] R diagonal (written out
 // the same instruction, so the slot pitch is offset by 4 banks from a multiple of the bank
 // count (64 + 4 floats): the two 16-byte broadcasts hit different banks.
 constexpr int COL_PITCH = 68;
-// Two-column layout (panels of more than 192 rows): row group G's slice of the pivot column
+// Rows per lane (one-column count) from which panels take the two-column layout: below
+// it the one-column loop is faster (measured per register class on 1024-sized blocks).
+constexpr int kTwoColMinNR = 24;
+// Two-column layout (panels of more than 320 rows): row group G's slice of the pivot column
 // at G * COL2_PITCH; the four row groups of a wave read theirs in one instruction, so the
 // pitch sits 4 banks off a multiple of the bank count.
 constexpr int NGRP = PANEL_THREADS / 16;     // row groups of 16 lanes
@@ -491,7 +494,7 @@ __device__ __forceinline__ float rows4_sum(float v, int lane) {
     return a + other_half32(a, lane);
 }
 
-// The reflector loop and the outputs of panels with more than 192 rows (16 or more rows per
+// The reflector loop and the outputs of panels with more than 320 rows (24 or more rows per
 // lane in the one-column layout), two columns per lane.
 // With one column per lane, step j's pivot column lives in one lane of each half-wave,
 // which stores NR values for its half-wave to read back: NR/4 16-byte LDS stores per wave
@@ -836,7 +839,7 @@ __device__ __forceinline__ void panel_body(const PanelDesc& d, const PanelExtra&
             for (int i = 0; i < NR; ++i) x[i] = ldexpf(x[i], -e);
         }
     }
-    if constexpr (NR >= 16) {
+    if constexpr (NR >= kTwoColMinNR) {
         panel_two_cols<NR, MODE>(d, ex, smem, x);
         return;
     }
@@ -1168,11 +1171,10 @@ hipError_t launch_step(const StepPanelDesc* panels, int npanel, const SlabDesc* 
 
 }  // namespace
 
-// rows of the layout hand-over buffer of a panel of up to max_h rows (two-column path,
-// 16 or more rows per lane)
+// rows of the layout hand-over buffer of a panel of up to max_h rows (two-column path)
 static int handover_rows(int max_h) {
     const int nr = panel_rows_class(max_h < 1 ? 1 : max_h);
-    return nr >= 16 ? NSLOT * nr : 0;
+    return nr >= kTwoColMinNR ? NSLOT * nr : 0;
 }
 
 size_t qr_step_lds_bytes(int max_h) {

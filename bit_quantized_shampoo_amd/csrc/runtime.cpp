@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <memory>
 #include <vector>
 
@@ -1330,9 +1331,9 @@ struct shampoo4_ctx_s {
     }
 
     // The kernels of one statistics update (everything after the io upload).
-    // fork: recorded on s where the QR of the first power step begins (work forked from
-    // there shares the GPU with the latency-bound panel chain rather than the products)
-    hipError_t stats_body(bool reuse, hipStream_t s, hipEvent_t fork = nullptr) {
+    // at_qr: called where the QR of the first power step begins (work forked from there
+    // shares the GPU with the latency-bound panel chain rather than the products)
+    hipError_t stats_body(bool reuse, hipStream_t s, const std::function<hipError_t()>* at_qr = nullptr) {
         const int var = reuse ? 1 : 0;
         hipError_t e = hipSuccess;
         const bool fold = !reuse && !bj_stats_fold.empty();
@@ -1349,7 +1350,7 @@ struct shampoo4_ctx_s {
         }
         for (int it = 0; it < cfg.power_iters && e == hipSuccess; ++it) {
             e = run(it == 0 ? power_first[var] : power_next, s);
-            if (e == hipSuccess && it == 0 && fork) e = hipEventRecord(fork, s);
+            if (e == hipSuccess && it == 0 && at_qr) e = (*at_qr)();
             // forward accumulation (fused and look-ahead schedules): Q = I, reflectors, then
             // the column signs; backward (blocked): the factorization, then Q from the signs
             const bool backward_q = !fused && !lookahead;
@@ -1366,24 +1367,24 @@ struct shampoo4_ctx_s {
     }
 
     // The statistics update after its io upload: graph replay or eager launches.
-    // fork (optional): an event recorded where the QR begins (before the whole update
-    // when it is replayed from a graph, or when no power step runs)
-    hipError_t submit_stats(hipStream_t s, hipEvent_t fork = nullptr) {
+    // at_qr (optional): called where the QR begins (before the whole update when it is
+    // replayed from a graph, after it when no power step runs)
+    hipError_t submit_stats(hipStream_t s, const std::function<hipError_t()>* at_qr = nullptr) {
         const bool reuse = (cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) && root_v_valid && root_v_is_stats;
         const int var = reuse ? 1 : 0;
         hipError_t e = hipSuccess;
         if (use_graphs && graph_ok && !timing) {
             if (!stats_graph[var]) capture_stats(reuse);
             if (stats_graph[var]) {
-                if (fork) e = hipEventRecord(fork, s);
+                if (at_qr) e = (*at_qr)();
                 if (e == hipSuccess) e = hipGraphLaunch(stats_graph[var], s);
             } else {
-                e = stats_body(reuse, s, fork);
+                e = stats_body(reuse, s, at_qr);
             }
         } else {
-            e = stats_body(reuse, s, fork);
+            e = stats_body(reuse, s, at_qr);
         }
-        if (e == hipSuccess && fork && cfg.power_iters < 1) e = hipEventRecord(fork, s);
+        if (e == hipSuccess && at_qr && cfg.power_iters < 1) e = (*at_qr)();
         root_v_is_stats = false;
         return e;
     }
@@ -1637,10 +1638,16 @@ shampoo4_status shampoo4_step(shampoo4_ctx c, const shampoo4_io* io, int32_t ref
     hipStream_t s = as_stream(stream);
     if (c->ensure_pre_stream() != hipSuccess) return SHAMPOO4_EHIP;
     if (c->upload_io(io, s) != hipSuccess) return SHAMPOO4_EHIP;
-    hipError_t e = c->submit_stats(s, c->pre_fork);
-    if (e == hipSuccess) e = hipStreamWaitEvent(c->pre_strm, c->pre_fork, 0);
-    for (int i = 0; i < 2 && e == hipSuccess; ++i) e = c->run(c->pre_cached[i], c->pre_strm);
-    if (e == hipSuccess) e = hipEventRecord(c->pre_join, c->pre_strm);
+    // the precondition is enqueued at the fork point itself (host order), so its launches
+    // reach the GPU as the QR starts rather than after the host has queued the whole chain
+    const std::function<hipError_t()> fork = [c, s]() {
+        hipError_t e = hipEventRecord(c->pre_fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(c->pre_strm, c->pre_fork, 0);
+        for (int i = 0; i < 2 && e == hipSuccess; ++i) e = c->run(c->pre_cached[i], c->pre_strm);
+        if (e == hipSuccess) e = hipEventRecord(c->pre_join, c->pre_strm);
+        return e;
+    };
+    hipError_t e = c->submit_stats(s, &fork);
     if (e == hipSuccess) e = hipStreamWaitEvent(s, c->pre_join, 0);
     return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
