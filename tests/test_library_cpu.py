@@ -118,6 +118,8 @@ def test_null_arguments_rejected_on_host():
     assert lib.shampoo4_update_stats(None, None, None) == L.EINVAL
     assert lib.shampoo4_refresh_root(None, None) == L.EINVAL
     assert lib.shampoo4_precondition(None, None, None) == L.EINVAL
+    assert lib.shampoo4_step(None, None, 0, None) == L.EINVAL
+    assert lib.shampoo4_step(None, None, 1, None) == L.EINVAL
     assert lib.shampoo4_destroy(None) == L.EINVAL
     assert lib.shampoo4_quantize(None, 5, 64, None, None, None) == L.EINVAL
     assert lib.shampoo4_quantize(None, 5, 32, None, None, None) == L.EINVAL
