@@ -175,8 +175,10 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
             for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
 
     // raw operand loads of the slice in flight, and the raw K-scale values of B's rows
-    floatx4 ra[RA][kSlabs<SLAB>], rb[RB][kSlabs<SLAB>];
-    float kraw[RB][TB ? 4 : 1];
+    struct Raw {
+        floatx4 a[RA][kSlabs<SLAB>], b[RB][kSlabs<SLAB>];
+        float k[RB][TB ? 4 : 1];
+    };
 
     // The K scale (statistics: V diag(lam) V^T) is applied branch-free: without one, the
     // scale is read from B itself and replaced by 1 with a bit mask.
@@ -196,30 +198,30 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
 
     // Every thread issues all its loads of a slice unconditionally (threads past the
     // slice's last quad reload it and do not store it), so no load sits behind a branch.
-    auto load_slice = [&](int k0) {
+    auto load_slice = [&](Raw& R, int k0) {
 #pragma unroll
         for (int r = 0; r < RA; ++r) {
             int row, col;
             a_coord(min(tid + r * 256, NQA - 1), k0, row, col);
-            raw_quads<VEC, SLAB>(ra[r], A, aslab, anslab, lda, row, col, TA ? K : M, TA ? M : K);
+            raw_quads<VEC, SLAB>(R.a[r], A, aslab, anslab, lda, row, col, TA ? K : M, TA ? M : K);
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             int row, col;
             b_coord(min(tid + r * 256, NQB - 1), k0, row, col);
-            raw_quads<VEC, SLAB>(rb[r], B, bslab, bnslab, ldb, row, col, TB ? N : K, TB ? K : N);
+            raw_quads<VEC, SLAB>(R.b[r], B, bslab, bnslab, ldb, row, col, TB ? N : K, TB ? K : N);
             if constexpr (TB) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) kraw[r][e] = ldg(ksp + min(col + e, K - 1));
+                for (int e = 0; e < 4; ++e) R.k[r][e] = ldg(ksp + min(col + e, K - 1));
             } else {
-                kraw[r][0] = ldg(ksp + min(row, K - 1));
+                R.k[r][0] = ldg(ksp + min(row, K - 1));
             }
         }
     };
 
     // masks, slab sums and the K scale are applied here, after the previous slice's
     // matrix-core work, then the slice goes to LDS
-    auto store_slice = [&](int buf, int k0) {
+    auto store_slice = [&](const Raw& R, int buf, int k0) {
         float* as = As + buf * A_SZ;
         float* bs = Bs + buf * B_SZ;
 #pragma unroll
@@ -227,7 +229,7 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
             const int q = tid + r * 256;
             int row, col;
             a_coord(min(q, NQA - 1), k0, row, col);
-            const floatx4 v = finish_quads<VEC, SLAB>(ra[r], anslab, row, col, TA ? K : M, TA ? M : K);
+            const floatx4 v = finish_quads<VEC, SLAB>(R.a[r], anslab, row, col, TA ? K : M, TA ? M : K);
             if (NQA % 256 == 0 || q < NQA) {
                 if constexpr (!TA) {
                     const int i = q / (BK / 4), kq = (q % (BK / 4)) * 4;
@@ -243,12 +245,12 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
             const int q = tid + r * 256;
             int row, col;
             b_coord(min(q, NQB - 1), k0, row, col);
-            floatx4 v = finish_quads<VEC, SLAB>(rb[r], bnslab, row, col, TB ? N : K, TB ? K : N);
+            floatx4 v = finish_quads<VEC, SLAB>(R.b[r], bnslab, row, col, TB ? N : K, TB ? K : N);
             if constexpr (TB) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] *= kfac(kraw[r][e]);   // past K: already zero
+                for (int e = 0; e < 4; ++e) v[e] *= kfac(R.k[r][e]);   // past K: already zero
             } else {
-                const float f = kfac(kraw[r][0]);
+                const float f = kfac(R.k[r][0]);
                 v[0] *= f; v[1] *= f; v[2] *= f; v[3] *= f;
             }
             if (NQB % 256 == 0 || q < NQB) {
@@ -263,20 +265,9 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
         }
     };
 
-    const int nk = (K - kbeg + BK - 1) / BK;
-    if (nk > 0) {
-        load_slice(kbeg);
-        store_slice(0, kbeg);
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) load_slice(kbeg + (kt + 1) * BK);
+    auto compute = [&](int cur) {
         const float* as = As + cur * A_SZ;
         const float* bs = Bs + cur * B_SZ;
-
 #pragma unroll
         for (int kc = 0; kc < BK / 8; ++kc) {
             const int kb = kc * 8 + h * 4;
@@ -311,8 +302,42 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
                                                                          acc[m][n], 0, 0, 0);
         }
 
-        if (more) store_slice(cur ^ 1, kbeg + (kt + 1) * BK);
+    };
+
+    const int nk = (K - kbeg + BK - 1) / BK;
+    Raw r0, r1;
+    if (nk > 0) {
+        load_slice(r0, kbeg);
+        store_slice(r0, 0, kbeg);
+    }
+    if constexpr (TM * TN == 1 && !SLAB) {
+        // Inside the loop the loads are issued unconditionally (past K they reload
+        // clamped addresses and are never stored): a load behind a branch makes the wait
+        // before the older set's store cover the newer set too.  With K = 0 nothing is
+        // loaded (the clamps need at least one element along K).
+        if (nk > 0) load_slice(r1, kbeg + BK);
         __syncthreads();
+        for (int kt = 0; kt < nk; kt += 2) {
+            load_slice(r0, kbeg + (kt + 2) * BK);
+            compute(0);
+            if (kt + 1 < nk) store_slice(r1, 1, kbeg + (kt + 1) * BK);
+            __syncthreads();
+            if (kt + 1 >= nk) break;
+            load_slice(r1, kbeg + (kt + 3) * BK);
+            compute(1);
+            if (kt + 2 < nk) store_slice(r0, 0, kbeg + (kt + 2) * BK);
+            __syncthreads();
+        }
+    } else {
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            const bool more = kt + 1 < nk;
+            if (more) load_slice(r0, kbeg + (kt + 1) * BK);
+            compute(cur);
+            if (more) store_slice(r0, cur ^ 1, kbeg + (kt + 1) * BK);
+            __syncthreads();
+        }
     }
 
     // Epilogue.  Accumulator register r of lane (h, l32) holds
