@@ -110,9 +110,13 @@ __device__ __forceinline__ floatx4 finish_quads(const floatx4 (&w)[kSlabs<SLAB>]
     return finish_quad<VEC>(v, row, col, rows, cols);
 }
 
-template <int WM, int WN, int TM, int TN, bool TA, bool TB, bool VEC, bool SLAB>
+// KW = 2: two groups of four waves split the K slices of one tile (group g takes slices
+// g, g + 2, ...; the same trip count for both, a slice past K loads as zeros) and add
+// their accumulators through LDS at the end: two waves per SIMD for a tile that would
+// otherwise have one.  Not for the column-dot epilogue (its barrier runs on one group).
+template <int WM, int WN, int TM, int TN, bool TA, bool TB, bool VEC, bool SLAB, int KW = 1>
 __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEntry* __restrict__ io,
-                                          float* __restrict__ As, float* __restrict__ Bs) {
+                                          float* __restrict__ As0, float* __restrict__ Bs0) {
     using T = Tile<WM, WN, TM, TN>;
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK, KCP = T::KCP, AMCP = T::AMCP, BMCP = T::BMCP;
     constexpr int A_SZ = TA ? T::A_MC : T::A_KC;
@@ -158,7 +162,10 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
     const int64_t aslab = dsc.aslab, bslab = dsc.bslab;
     const float* __restrict__ kscale = dsc.kscale;
 
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & 255;
+    const int kg = KW > 1 ? (int)(threadIdx.x >> 8) : 0;    // K group
+    float* __restrict__ As = As0 + kg * 2 * A_SZ;
+    float* __restrict__ Bs = Bs0 + kg * 2 * B_SZ;
     const int lane = tid & 63;
     const int wv = tid >> 6;
     const int wave_m = wv % WM;
@@ -304,28 +311,29 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
 
     };
 
-    const int nk = (K - kbeg + BK - 1) / BK;
+    const int nk = ((K - kbeg + BK - 1) / BK + KW - 1) / KW;   // slices per K group
+    auto kof = [&](int s) { return kbeg + (KW * s + kg) * BK; };
     Raw r0, r1;
     if (nk > 0) {
-        load_slice(r0, kbeg);
-        store_slice(r0, 0, kbeg);
+        load_slice(r0, kof(0));
+        store_slice(r0, 0, kof(0));
     }
     if constexpr (TM * TN == 1 && !SLAB) {
         // Inside the loop the loads are issued unconditionally (past K they reload
         // clamped addresses and are never stored): a load behind a branch makes the wait
         // before the older set's store cover the newer set too.  With K = 0 nothing is
         // loaded (the clamps need at least one element along K).
-        if (nk > 0) load_slice(r1, kbeg + BK);
+        if (nk > 0) load_slice(r1, kof(1));
         __syncthreads();
         for (int kt = 0; kt < nk; kt += 2) {
-            load_slice(r0, kbeg + (kt + 2) * BK);
+            load_slice(r0, kof(kt + 2));
             compute(0);
-            if (kt + 1 < nk) store_slice(r1, 1, kbeg + (kt + 1) * BK);
+            if (kt + 1 < nk) store_slice(r1, 1, kof(kt + 1));
             __syncthreads();
             if (kt + 1 >= nk) break;
-            load_slice(r1, kbeg + (kt + 3) * BK);
+            load_slice(r1, kof(kt + 3));
             compute(1);
-            if (kt + 2 < nk) store_slice(r0, 0, kbeg + (kt + 2) * BK);
+            if (kt + 2 < nk) store_slice(r0, 0, kof(kt + 2));
             __syncthreads();
         }
     } else {
@@ -333,11 +341,38 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
             const bool more = kt + 1 < nk;
-            if (more) load_slice(r0, kbeg + (kt + 1) * BK);
+            if (more) load_slice(r0, kof(kt + 1));
             compute(cur);
-            if (more) store_slice(r0, cur ^ 1, kbeg + (kt + 1) * BK);
+            if (more) store_slice(r0, cur ^ 1, kof(kt + 1));
             __syncthreads();
         }
+    }
+
+    if constexpr (KW > 1) {
+        // group 1's accumulators through LDS (free after the loop's last barrier) into
+        // group 0's, which then runs the epilogue alone (it has no workgroup barrier)
+        static_assert(KW == 2, "two K groups");
+        constexpr int NACC = TM * TN * 16;
+        if (kg == 1) {
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int n = 0; n < TN; ++n)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) As0[((m * TN + n) * 16 + r) * 256 + tid] = acc[m][n][r];
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int m = 0; m < TM; ++m)
+#pragma unroll
+                for (int n = 0; n < TN; ++n)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[m][n][r] += As0[((m * TN + n) * 16 + r) * 256 + tid];
+        }
+        __syncthreads();   // the epilogue reuses the LDS
+        if (kg == 1) return;
+        (void)NACC;
     }
 
     // Epilogue.  Accumulator register r of lane (h, l32) holds
@@ -456,67 +491,83 @@ static_assert(2 * Tile<2, 2, 2, 2>::A_MC >= 2 * 32 * 33 && 2 * Tile<2, 2, 2, 2>:
               "LDS of the 128 x 128 tile too small for the mirrored stores");
 
 // One transpose mode for the whole launch, 16-byte loads, no split-K slabs.
-template <int WM, int WN, int TM, int TN, bool TA, bool TB>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmDesc* __restrict__ descs,
-                                                   const int* __restrict__ prefix, int ndesc,
-                                                   const IoEntry* __restrict__ io) {
+template <int WM, int WN, int TM, int TN, bool TA, bool TB, int KW>
+__global__ __launch_bounds__(256 * KW, 2) void gemm_kernel(const GemmDesc* __restrict__ descs,
+                                                        const int* __restrict__ prefix, int ndesc,
+                                                        const IoEntry* __restrict__ io) {
     using T = Tile<WM, WN, TM, TN>;
     constexpr int A_SZ = TA ? T::A_MC : T::A_KC;
     constexpr int B_SZ = TB ? T::B_KC : T::B_MC;
-    constexpr int A_ALL = (2 * A_SZ > T::RED) ? 2 * A_SZ : T::RED;
+    constexpr int A_NEED = (KW > 1 && TM * TN * 16 * 256 > T::RED) ? TM * TN * 16 * 256 : T::RED;
+    constexpr int A_ALL = (2 * KW * A_SZ > A_NEED) ? 2 * KW * A_SZ : A_NEED;
     __shared__ __attribute__((aligned(16))) float As[A_ALL];
-    __shared__ __attribute__((aligned(16))) float Bs[2 * B_SZ];
+    __shared__ __attribute__((aligned(16))) float Bs[2 * KW * B_SZ];
     const int item = find_item(prefix, ndesc, blockIdx.x);
-    gemm_body<WM, WN, TM, TN, TA, TB, true, false>(descs[item], blockIdx.x - prefix[item], io, As, Bs);
+    gemm_body<WM, WN, TM, TN, TA, TB, true, false, KW>(descs[item], blockIdx.x - prefix[item], io, As, Bs);
 }
 
 // Transpose mode per descriptor (uniform per workgroup); VEC and SLAB per launch.
-template <int WM, int WN, int TM, int TN, bool VEC, bool SLAB>
-__global__ __launch_bounds__(256, 2) void gemm_kernel_mixed(const GemmDesc* __restrict__ descs,
-                                                         const int* __restrict__ prefix, int ndesc,
-                                                         const IoEntry* __restrict__ io) {
+template <int WM, int WN, int TM, int TN, bool VEC, bool SLAB, int KW>
+__global__ __launch_bounds__(256 * KW, 2) void gemm_kernel_mixed(const GemmDesc* __restrict__ descs,
+                                                              const int* __restrict__ prefix, int ndesc,
+                                                              const IoEntry* __restrict__ io) {
     using T = Tile<WM, WN, TM, TN>;
-    constexpr int A_ALL = (2 * T::A_MAX > T::RED) ? 2 * T::A_MAX : T::RED;
+    constexpr int A_NEED = (KW > 1 && TM * TN * 16 * 256 > T::RED) ? TM * TN * 16 * 256 : T::RED;
+    constexpr int A_ALL = (2 * KW * T::A_MAX > A_NEED) ? 2 * KW * T::A_MAX : A_NEED;
     __shared__ __attribute__((aligned(16))) float As[A_ALL];
-    __shared__ __attribute__((aligned(16))) float Bs[2 * T::B_MAX];
+    __shared__ __attribute__((aligned(16))) float Bs[2 * KW * T::B_MAX];
     const int item = find_item(prefix, ndesc, blockIdx.x);
     const GemmDesc& d = descs[item];
     const int t = blockIdx.x - prefix[item];
     switch (d.flags & (GEMM_F_TA | GEMM_F_TB)) {
-        case 0: gemm_body<WM, WN, TM, TN, false, false, VEC, SLAB>(d, t, io, As, Bs); break;
-        case GEMM_F_TB: gemm_body<WM, WN, TM, TN, false, true, VEC, SLAB>(d, t, io, As, Bs); break;
-        case GEMM_F_TA: gemm_body<WM, WN, TM, TN, true, false, VEC, SLAB>(d, t, io, As, Bs); break;
-        default: gemm_body<WM, WN, TM, TN, true, true, VEC, SLAB>(d, t, io, As, Bs); break;
+        case 0: gemm_body<WM, WN, TM, TN, false, false, VEC, SLAB, KW>(d, t, io, As, Bs); break;
+        case GEMM_F_TB: gemm_body<WM, WN, TM, TN, false, true, VEC, SLAB, KW>(d, t, io, As, Bs); break;
+        case GEMM_F_TA: gemm_body<WM, WN, TM, TN, true, false, VEC, SLAB, KW>(d, t, io, As, Bs); break;
+        default: gemm_body<WM, WN, TM, TN, true, true, VEC, SLAB, KW>(d, t, io, As, Bs); break;
     }
 }
 
-template <int WM, int WN, int TM, int TN>
+template <int WM, int WN, int TM, int TN, int KW = 1>
 hipError_t launch_cfg(int mode, bool vec, bool slab, const GemmDesc* descs, const int* prefix, int ndesc,
                       int ntiles, const IoEntry* io, hipStream_t stream) {
-    dim3 grid(ntiles), block(256);
+    dim3 grid(ntiles), block(256 * KW);
+    if constexpr (KW > 1) {   // K groups: 16-byte loads without split-K slabs only
+        if (!vec || slab) return hipErrorInvalidValue;
+        if (mode == GEMM_MODE_MIXED)
+            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, true, false, KW>), grid, block, 0, stream, descs, prefix, ndesc, io);
+        else if (mode == 0)
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, false, KW>), grid, block, 0, stream, descs, prefix, ndesc, io);
+        else if (mode == GEMM_F_TB)
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, true, KW>), grid, block, 0, stream, descs, prefix, ndesc, io);
+        else if (mode == GEMM_F_TA)
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, false, KW>), grid, block, 0, stream, descs, prefix, ndesc, io);
+        else
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, true, KW>), grid, block, 0, stream, descs, prefix, ndesc, io);
+        return hipGetLastError();
+    }
     if (!vec || slab || mode == GEMM_MODE_MIXED) {
         if (vec && slab)
-            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, true, true>), grid, block, 0, stream, descs, prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, true, true, 1>), grid, block, 0, stream, descs, prefix, ndesc, io);
         else if (vec)
-            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, true, false>), grid, block, 0, stream, descs, prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, true, false, 1>), grid, block, 0, stream, descs, prefix, ndesc, io);
         else if (slab)
-            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, false, true>), grid, block, 0, stream, descs, prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, false, true, 1>), grid, block, 0, stream, descs, prefix, ndesc, io);
         else
-            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, false, false>), grid, block, 0, stream, descs, prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel_mixed<WM, WN, TM, TN, false, false, 1>), grid, block, 0, stream, descs, prefix, ndesc, io);
         return hipGetLastError();
     }
     switch (mode) {
         case 0:
-            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, false>), grid, block, 0, stream, descs, prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, false, 1>), grid, block, 0, stream, descs, prefix, ndesc, io);
             break;
         case GEMM_F_TB:
-            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, true>), grid, block, 0, stream, descs, prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, false, true, 1>), grid, block, 0, stream, descs, prefix, ndesc, io);
             break;
         case GEMM_F_TA:
-            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, false>), grid, block, 0, stream, descs, prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, false, 1>), grid, block, 0, stream, descs, prefix, ndesc, io);
             break;
         default:
-            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, true>), grid, block, 0, stream, descs, prefix, ndesc, io);
+            S4_LAUNCH((gemm_kernel<WM, WN, TM, TN, true, true, 1>), grid, block, 0, stream, descs, prefix, ndesc, io);
             break;
     }
     return hipGetLastError();
@@ -539,7 +590,8 @@ bool gemm_vec_ok(const GemmDesc& d) {
 void gemm_tile_dims(int cfg, int* bm, int* bn) {
     switch (cfg) {
         case GEMM_128x128: *bm = 128; *bn = 128; break;
-        case GEMM_64x64: *bm = 64; *bn = 64; break;
+        case GEMM_64x64:
+        case GEMM_64x64_K2: *bm = 64; *bn = 64; break;
         case GEMM_128x32: *bm = 128; *bn = 32; break;
         default: *bm = 32; *bn = 128; break;
     }
@@ -551,6 +603,9 @@ hipError_t launch_gemm(int cfg, int mode, bool vec, bool slab, const GemmDesc* d
     switch (cfg) {
         case GEMM_128x128: return launch_cfg<2, 2, 2, 2>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
         case GEMM_64x64: return launch_cfg<2, 2, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
+        case GEMM_64x64_K2:   // (the K groups need 16-byte loads: a per-call caller operand may deny them)
+            if (!vec || slab) return launch_cfg<2, 2, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
+            return launch_cfg<2, 2, 1, 1, 2>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
         case GEMM_128x32: return launch_cfg<4, 1, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
         default: return launch_cfg<1, 4, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
     }

@@ -9,7 +9,10 @@
 namespace s4 {
 
 // Tile shapes of the fp32 MFMA GEMM (workgroup of 4 waves).
-enum GemmCfg { GEMM_128x128 = 0, GEMM_64x64 = 1, GEMM_32x128 = 2, GEMM_128x32 = 3, GEMM_NCFG = 4 };
+// tile shapes (the first GEMM_NCFG are the shape classes); GEMM_64x64_K2: the 64 x 64
+// tile with two groups of four waves splitting K (16-byte loads, no slabs, no column dots)
+enum GemmCfg { GEMM_128x128 = 0, GEMM_64x64 = 1, GEMM_32x128 = 2, GEMM_128x32 = 3, GEMM_NCFG = 4,
+               GEMM_64x64_K2 = 5 };
 constexpr int GEMM_MODE_MIXED = -1;   // descriptors of one launch carry different transposes
 void gemm_tile_dims(int cfg, int* bm, int* bn);
 // mode: GEMM_F_TA | GEMM_F_TB shared by all descriptors, or GEMM_MODE_MIXED.
