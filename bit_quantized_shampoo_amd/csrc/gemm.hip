@@ -113,7 +113,7 @@ __device__ __forceinline__ floatx4 finish_quads(const floatx4 (&w)[kSlabs<SLAB>]
 // KW = 2: two groups of four waves split the K slices of one tile (group g takes slices
 // g, g + 2, ...; the same trip count for both, a slice past K loads as zeros) and add
 // their accumulators through LDS at the end: two waves per SIMD for a tile that would
-// otherwise have one.  Not for the column-dot epilogue (its barrier runs on one group).
+// otherwise have one.  Group 0 then runs the epilogue.
 template <int WM, int WN, int TM, int TN, bool TA, bool TB, bool VEC, bool SLAB, int KW = 1>
 __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEntry* __restrict__ io,
                                           float* __restrict__ As0, float* __restrict__ Bs0) {
@@ -371,7 +371,12 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
                     for (int r = 0; r < 16; ++r) acc[m][n][r] += As0[((m * TN + n) * 16 + r) * 256 + tid];
         }
         __syncthreads();   // the epilogue reuses the LDS
-        if (kg == 1) return;
+        if (kg == 1) {
+            // group 0's epilogue: the column-dot form has one workgroup barrier, which
+            // this group meets before leaving; the others have none
+            if (dsc.flags & GEMM_F_COLDOT) __syncthreads();
+            return;
+        }
         (void)NACC;
     }
 

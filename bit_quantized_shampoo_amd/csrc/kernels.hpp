@@ -10,7 +10,7 @@ namespace s4 {
 
 // Tile shapes of the fp32 MFMA GEMM (workgroup of 4 waves).
 // tile shapes (the first GEMM_NCFG are the shape classes); GEMM_64x64_K2: the 64 x 64
-// tile with two groups of four waves splitting K (16-byte loads, no slabs, no column dots)
+// tile with two groups of four waves splitting K (16-byte loads, no split-K slabs)
 enum GemmCfg { GEMM_128x128 = 0, GEMM_64x64 = 1, GEMM_32x128 = 2, GEMM_128x32 = 3, GEMM_NCFG = 4,
                GEMM_64x64_K2 = 5 };
 constexpr int GEMM_MODE_MIXED = -1;   // descriptors of one launch carry different transposes

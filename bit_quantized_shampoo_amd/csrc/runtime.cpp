@@ -344,9 +344,7 @@ struct shampoo4_ctx_s {
         L.cfg = cfgsel;
         // a 64 x 64 launch of at most four tiles per CU runs its tiles with two K groups
         // of waves (two waves per SIMD where one tile per CU would give one)
-        bool coldot_any = false;
-        for (auto& d : ds) coldot_any = coldot_any || (d.flags & GEMM_F_COLDOT);
-        if (cfgsel == GEMM_64x64 && L.vec && !L.slab && !coldot_any && total <= 1024) L.cfg = GEMM_64x64_K2;
+        if (cfgsel == GEMM_64x64 && L.vec && !L.slab && total <= 1024) L.cfg = GEMM_64x64_K2;
         L.mode = modes ? GEMM_MODE_MIXED : first_mode;
         L.ndesc = (int)ds.size();
         L.ntiles = total;
