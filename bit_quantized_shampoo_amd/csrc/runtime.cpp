@@ -1392,11 +1392,12 @@ struct shampoo4_ctx_s {
         return e;
     }
 
+    // (each object is created once; a failed creation is retried on the next call)
     hipError_t ensure_pre_stream() {
-        if (pre_strm) return hipSuccess;
-        hipError_t e = hipEventCreateWithFlags(&pre_fork, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipEventCreateWithFlags(&pre_join, hipEventDisableTiming);
-        if (e == hipSuccess) e = hipStreamCreateWithFlags(&pre_strm, hipStreamNonBlocking);
+        hipError_t e = hipSuccess;
+        if (!pre_fork) e = hipEventCreateWithFlags(&pre_fork, hipEventDisableTiming);
+        if (e == hipSuccess && !pre_join) e = hipEventCreateWithFlags(&pre_join, hipEventDisableTiming);
+        if (e == hipSuccess && !pre_strm) e = hipStreamCreateWithFlags(&pre_strm, hipStreamNonBlocking);
         return e;
     }
 
