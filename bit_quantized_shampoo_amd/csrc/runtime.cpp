@@ -135,6 +135,9 @@ struct shampoo4_ctx_s {
     Seq qinit_signed;                     // backward accumulation: Q starts as diag(sign(R_jj))
     Seq pre[4];
     Seq root_mat, pre_cached[2];        // ROOT_CACHE: root matrices, then two products per block
+    // the same two products on 128 x 128 tiles, for the copy beside the QR chain: fewer,
+    // longer workgroups leave most CUs to the panel launches
+    Seq pre_side[2];
     Seq graft_seq[2];                    // per graft mode (bytes differ): norms, apply
     GraftParams graft_prm{};
     float newton_eps = 0.f;              // damping of the coupled Newton inverse root (standalone call)
@@ -1145,6 +1148,13 @@ struct shampoo4_ctx_s {
             root_mat = make_gemm(rm, FAM_GEMM_PRECOND);
             pre_cached[0] = make_gemm(q1, FAM_GEMM_PRECOND);
             pre_cached[1] = make_gemm(q2, FAM_GEMM_PRECOND);
+            pre_side[0] = gemm_launch(q1, FAM_GEMM_PRECOND, GEMM_128x128);
+            pre_side[1] = gemm_launch(q2, FAM_GEMM_PRECOND, GEMM_128x128);
+            // both forms sum each output over K in the same order (one group of waves
+            // per tile, whatever its shape), so P is bit-identical whichever runs
+            for (auto& sq : pre_cached)
+                for (auto& L : sq)
+                    if (L.cfg == GEMM_64x64_K2) L.cfg = GEMM_64x64;
         }
     }
 
@@ -1647,7 +1657,7 @@ shampoo4_status shampoo4_step(shampoo4_ctx c, const shampoo4_io* io, int32_t ref
     const std::function<hipError_t()> fork = [c, s]() {
         hipError_t e = hipEventRecord(c->pre_fork, s);
         if (e == hipSuccess) e = hipStreamWaitEvent(c->pre_strm, c->pre_fork, 0);
-        for (int i = 0; i < 2 && e == hipSuccess; ++i) e = c->run(c->pre_cached[i], c->pre_strm);
+        for (int i = 0; i < 2 && e == hipSuccess; ++i) e = c->run(c->pre_side[i], c->pre_strm);
         if (e == hipSuccess) e = hipEventRecord(c->pre_join, c->pre_strm);
         return e;
     };
