@@ -149,6 +149,8 @@ static_assert(sizeof(StepPanelDesc) == 96, "StepPanelDesc layout");
 // `count` <= 32 columns of P (role 0; M points at row r0 of the first column, h rows) or as
 // M <- M - ((M V) T) V^T to `count` <= 32 rows of Q (role 1; M points at column r0 of the
 // first row, h columns).
+// Role 1 with ident = 1: M holds the identity on input (Q's first block application):
+// M[m][k] is read as 1 where m + diag == k, else 0, and M's memory is only written.
 struct SlabDesc {
     float* M;
     const float* V;
@@ -156,8 +158,8 @@ struct SlabDesc {
     int64_t ld;               // of M
     int64_t vld;
     int32_t role, h;
-    int32_t count, pad0;
-    int64_t pad1;
+    int32_t count, ident;
+    int64_t diag;
 };
 static_assert(sizeof(SlabDesc) == 64, "SlabDesc layout");
 

@@ -376,11 +376,16 @@ __device__ __forceinline__ void wy_update_rows(const float* __restrict__ V, int6
 // Z[m][i] = sum_{k < h} M[m][k] Y[k][i] for rows m < nrows of M (Z row-major 32 x 32 in LDS);
 // Y is a 32-column block (V in the fused step).
 // Wave w takes the 32-column chunks w, w + 8, ...
+// ident: M is the identity shifted by diag (M[m][k] = [m + diag == k]), not read.
 __device__ __forceinline__ void wy_right_product(const float* __restrict__ M, int64_t ld, int nrows, const float* __restrict__ Y,
-                                 int64_t vld, int h, float* part, float* Z, int tid) {
+                                 int64_t vld, int h, float* part, float* Z, int tid, bool ident = false,
+                                 int64_t diag = 0) {
     const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, hh = lane >> 5;
     const int mr = l32 < nrows ? l32 : nrows - 1;
     const uint32_t rmask = l32 < nrows ? 0xffffffffu : 0u;
+    // the identity is merged in with a bit mask after an unconditional load (a select
+    // on a loaded value would become a branch around the load)
+    const uint32_t keep = ident ? 0u : 0xffffffffu;
     floatx16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -389,7 +394,9 @@ __device__ __forceinline__ void wy_right_product(const float* __restrict__ M, in
 #pragma unroll
         for (int ks = 0; ks < 16; ++ks) {
             const int k = kb + ks < h ? kb + ks : h - 1;
-            B.a[ks] = ldg(M + (int64_t)mr * ld + k);    // A operand: M[l32][k]
+            const float mv = ldg(M + (int64_t)mr * ld + k);    // A operand: M[l32][k]
+            const uint32_t iv = (mr + diag == k) ? 0x3f800000u : 0u;
+            B.a[ks] = __uint_as_float((__float_as_uint(mv) & keep) | (iv & ~keep));
             B.b[ks] = ldg(Y + (int64_t)k * vld + l32);  // B operand: Y[k][l32]
         }
     };
@@ -407,17 +414,21 @@ __device__ __forceinline__ void wy_right_product(const float* __restrict__ M, in
 
 // M[m][c] -= sum_i Z[m][i] V[c][i] for rows m < nrows and columns c < h.
 __device__ __forceinline__ void wy_update_cols(float* M, int64_t ld, int nrows, const float* __restrict__ V, int64_t vld, int h,
-                               const float* Z, int tid) {
+                               const float* Z, int tid, bool ident = false, int64_t diag = 0) {
     const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, hh = lane >> 5;
     float za[16];                                     // A operand: -Z[l32][ks + 16 hh]
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) za[ks] = -Z[l32 * 32 + 16 * hh + ks];
+    const uint32_t keep = ident ? 0u : 0xffffffffu;   // identity merged in after the load
     auto load = [&](int t, WyBuf& B) {               // a: the block of M (C operand), b: V row
         const int col = 32 * t + l32 < h ? 32 * t + l32 : h - 1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = acc_row(r, hh);
-            B.a[r] = ldg(M + (int64_t)(row < nrows ? row : nrows - 1) * ld + col);
+            const int rr = row < nrows ? row : nrows - 1;
+            const float mv = ldg(M + (int64_t)rr * ld + col);
+            const uint32_t iv = (rr + diag == col) ? 0x3f800000u : 0u;
+            B.a[r] = __uint_as_float((__float_as_uint(mv) & keep) | (iv & ~keep));
         }
         load_vrow16(V + (int64_t)col * vld + 16 * hh, B.b);  // B operand: V[32 t + l32][ks + 16 hh]
     };
@@ -1020,9 +1031,10 @@ __global__ __launch_bounds__(PANEL_THREADS) void qr_step_kernel(const StepPanelD
         wy_apply_t<true>(smem + OFF_T, smem + OFF_SALL, tid);
         wy_update_rows(s.V, s.vld, s.M, s.ld, s.h, s.count, smem + OFF_SALL, tid);
     } else {
-        wy_right_product(s.M, s.ld, s.count, s.V, s.vld, s.h, smem + OFF_VS, smem + OFF_SALL, tid);
+        const bool ident = s.ident != 0;
+        wy_right_product(s.M, s.ld, s.count, s.V, s.vld, s.h, smem + OFF_VS, smem + OFF_SALL, tid, ident, s.diag);
         wy_apply_t<false>(smem + OFF_T, smem + OFF_SALL, tid);
-        wy_update_cols(s.M, s.ld, s.count, s.V, s.vld, s.h, smem + OFF_SALL, tid);
+        wy_update_cols(s.M, s.ld, s.count, s.V, s.vld, s.h, smem + OFF_SALL, tid, ident, s.diag);
     }
 }
 

@@ -816,6 +816,10 @@ struct shampoo4_ctx_s {
                         sd.M = Qm + (int64_t)q0 * p + r0;
                         sd.V = V; sd.T = T; sd.ld = p; sd.vld = kPanel;
                         sd.role = 1; sd.h = h; sd.count = std::min(kPanel, p - q0);
+                        // Q = I before the first block: the slabs take it as such and
+                        // write all of Q (block 0 spans every column), so no fill runs
+                        sd.ident = k == 1 ? 1 : 0;
+                        sd.diag = q0 - r0;
                         sds.push_back(sd);
                         flops += 4.0 * h * nbk * sd.count;
                         bytes += 4.0 * h * (2.0 * kPanel + 2.0 * sd.count);
@@ -1364,10 +1368,11 @@ struct shampoo4_ctx_s {
         for (int it = 0; it < cfg.power_iters && e == hipSuccess; ++it) {
             e = run(it == 0 ? power_first[var] : power_next, s);
             if (e == hipSuccess && it == 0 && at_qr) e = (*at_qr)();
-            // forward accumulation (fused and look-ahead schedules): Q = I, reflectors, then
-            // the column signs; backward (blocked): the factorization, then Q from the signs
+            // forward accumulation (fused and look-ahead schedules): Q = I (in the fused
+            // steps the first Q slabs take it as given), reflectors, then the column signs;
+            // backward (blocked): the factorization, then Q from the signs
             const bool backward_q = !fused && !lookahead;
-            if (e == hipSuccess && !backward_q) e = run(qinit, s);
+            if (e == hipSuccess && !backward_q && !fused) e = run(qinit, s);
             for (size_t p = 0; p < qr_steps.size() && e == hipSuccess; ++p) e = run(qr_steps[p], s);
             if (e == hipSuccess && backward_q) e = run(qinit_signed, s);
             if (e == hipSuccess) e = run(qr_join, s);
