@@ -60,21 +60,39 @@ __global__ __launch_bounds__(256) void identity_fill_kernel(const VecDesc* __res
     }
 }
 
-// column j of out times sign(aux[j]) (0 counts as +), same row tiling
+// column j of out times sign(aux[j]) (0 counts as +), same row tiling.  A thread's
+// elements of a chunk (FILL_TILE / 256 of them, strided by 256) are all loaded, at clamped
+// addresses, before any is stored: a load-negate-store chain per element waited one
+// memory round trip each.
 __global__ __launch_bounds__(256) void sign_flip_kernel(const VecDesc* __restrict__ descs,
                                                         const int* __restrict__ prefix, int ndesc) {
+    constexpr int PER = FILL_TILE / 256;
     const int item = find_item(prefix, ndesc, blockIdx.x);
     const VecDesc& d = descs[item];
     const int p = d.p;
     const int rows = fill_rows(p);
     const int r0 = (blockIdx.x - prefix[item]) * rows;
-    const int r1 = min(r0 + rows, p);
-    for (int j = threadIdx.x; j < p; j += 256) {
-        if (!(d.aux[j] < 0.f)) continue;
-        for (int i = r0; i < r1; ++i) {
-            float* __restrict__ e = d.out + (int64_t)i * d.ld + j;
-            *e = -*e;
+    const int n = (min(r0 + rows, p) - r0) * p;       // elements of this row tile
+    const int qs = 256 / p, rs = 256 % p;             // a stride of 256 elements in (row, col)
+    for (int base = 0; base < n; base += PER * 256) {
+        int i = (base + (int)threadIdx.x) / p, jj = (base + (int)threadIdx.x) % p;
+        float v[PER], sg[PER];
+        int64_t off[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const bool in = base + k * 256 + (int)threadIdx.x < n;
+            const int ic = in ? r0 + i : r0, jc = in ? jj : 0;
+            off[k] = (int64_t)ic * d.ld + jc;
+            v[k] = ldg(d.out + off[k]);
+            // out of range: +0 (no store), by a mask rather than a select on the load
+            sg[k] = __uint_as_float(__float_as_uint(ldg(d.aux + jc)) & (in ? 0xffffffffu : 0u));
+            i += qs;
+            jj += rs;
+            if (jj >= p) { jj -= p; ++i; }
         }
+#pragma unroll
+        for (int k = 0; k < PER; ++k)
+            if (sg[k] < 0.f) stg(d.out + off[k], -v[k]);
     }
 }
 
