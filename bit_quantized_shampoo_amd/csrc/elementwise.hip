@@ -36,8 +36,17 @@ __global__ __launch_bounds__(256) void rayleigh_reduce_kernel(const VecDesc* __r
     const VecDesc& d = descs[item];
     const int j = (blockIdx.x - prefix[item]) * 256 + threadIdx.x;
     if (j >= d.p) return;
+    // partial rows 16 at a time, all loads (clamped rows) issued before the sum, which
+    // adds them in row order
     float t = 0.f;
-    for (int r = 0; r < d.rows; ++r) t += d.a[(int64_t)r * d.ld + j];
+    for (int r0 = 0; r0 < d.rows; r0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) v[k] = ldg(d.a + (int64_t)min(r0 + k, d.rows - 1) * d.ld + j);
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            if (r0 + k < d.rows) t += v[k];
+    }
     if (!__builtin_isfinite(t)) flag[0] = 1u;
     d.out[j] = t > 0.f ? t : 0.f;
 }
