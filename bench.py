@@ -27,8 +27,14 @@ if ROOT not in sys.path:
 METRIC = "preconditioned block-steps/sec + GEMM TFLOP/s (% MFMA peak), quant GB/s (% HBM)"
 PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBPS = 8000.0
-PEAK_FP32_VALU_TFLOPS = 157.3   # 256 CUs x 2.4 GHz x 256 fp32 flops per CU per clock
-DEFAULT_CONFIG = "single_1024"
+# fp32 vector peak of the code as built: packed fp32 instructions are disabled, so a CU
+# retires 64 fp32 FMAs (128 flops) per clock: 256 CUs x 2.4 GHz x 128 = 78.6 TFLOP/s
+PEAK_FP32_VALU_TFLOPS = 78.6
+CLOCK_GHZ = 2.4
+SIMDS = 256 * 4
+# the largest workload that fits one GPU: 64 blocks of 4096 x 4096, 5 Bjorck iterations,
+# both roots refreshed every step
+DEFAULT_CONFIG = "large_4096"
 
 
 def log(msg: str):
@@ -114,6 +120,131 @@ def summarize_traffic(workload: str, outdir: str):
     print(traffic_path(workload))
 
 
+def _find_csv(outdir: str, suffix: str) -> str:
+    import glob
+    hits = sorted(glob.glob(os.path.join(outdir, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {outdir}")
+    return hits[0]
+
+
+def _family_of(name: str):
+    for fam, (test, _) in FAMILIES.items():
+        if test(name):
+            return fam
+    return None
+
+
+def _bench_line(path: str):
+    with open(path) as f:
+        for line in reversed(f.read().strip().splitlines()):
+            if line.startswith("{"):
+                return json.loads(line)
+    raise ValueError(f"no JSON line in {path}")
+
+
+def summarize_kernels(workload: str, outdir: str):
+    """profiles/kernels_<workload>.md from a rocprofv3 --kernel-trace --stats run of the
+    bench, with the per-family averages set beside the bench's live HIP-event figures."""
+    import csv
+    run = os.path.join(outdir, f"prof_{workload}")
+    with open(_find_csv(run, "kernel_stats.csv")) as f:
+        rows = list(csv.DictReader(f))
+    line = _bench_line(os.path.join(outdir, f"prof_{workload}.json"))
+    total_ns = sum(float(r["TotalDurationNs"]) for r in rows)
+    fam = {}
+    for r in rows:
+        k = _family_of(r["Name"])
+        if k:
+            a = fam.setdefault(k, [0, 0.0])
+            a[0] += int(r["Calls"])
+            a[1] += float(r["TotalDurationNs"])
+    dom = line["roofline"]["family"]
+    steps, warm = line["steps"], line["warmup"]
+    isteps = line.get("instrumented_steps", steps)
+    out = [f"# Kernel time summary — `{workload}` bench", "",
+           "Command (from the repository root, on one MI355X):", "", "```",
+           "cd /tmp && export TMPDIR=/tmp",
+           f"rocprofv3 --kernel-trace --stats --output-format csv -d <repo>/gpurun_out/prof_{workload} -o run "
+           f"-- python3 <repo>/bench.py --config {workload} --steps {steps} --warmup {warm} --no-cpu "
+           f"> <repo>/gpurun_out/prof_{workload}.json",
+           f"python3 <repo>/bench.py --summarize-kernels <repo>/gpurun_out --config {workload}", "```", "",
+           f"The trace covers context set-up, input generation, {warm} warmup, {steps} timed and {isteps} "
+           f"event-instrumented steps.  Bench line of that run (under the profiler): {line['value']} "
+           f"block-steps/s, {line['ms_per_step']} ms/step.", "",
+           "Per kernel family (all launches in the trace; the bench's live figure is the average launch "
+           "of its instrumented pass, in-dispatch HIP events on the library's stream):", "",
+           "| Family | Calls | Total ms | Average µs (profiler) | Average µs (bench, live) |",
+           "|---|---|---|---|---|"]
+    for k, (calls, ns) in sorted(fam.items(), key=lambda kv: -kv[1][1]):
+        live = line.get("rooflines", {}).get(k, {}).get("avg_launch_us")
+        out.append(f"| `{k}`{' (dominant)' if k == dom else ''} | {calls} | {ns / 1e6:.2f} | "
+                   f"{ns / calls / 1e3:.2f} | {live if live is not None else '—'} |")
+    out += ["", "Kernels (top 30 by time):", "", "| Kernel | Calls | Total ms | Average µs | % |", "|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:30]:
+        nm = r["Name"].replace("|", "\\|")
+        out.append(f"| `{nm[:90]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                   f"{float(r['AverageNs']) / 1e3:.2f} | {100.0 * float(r['TotalDurationNs']) / total_ns:.1f} |")
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(path)
+
+
+def summarize_mfma(workload: str, outdir: str):
+    """profiles/mfma_<workload>.md: matrix-core use of the GEMM kernels from one rocprofv3
+    --pmc run (SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES) with its kernel trace: per dispatch
+    the MFMA instructions (4096 flops each: v_mfma_f32_32x32x2_f32, 32 x 32 x 2 per wave)
+    over the dispatch time, and the busy cycles over SIMDs x dispatch cycles at 2.4 GHz."""
+    import csv
+    from collections import defaultdict
+    run = os.path.join(outdir, f"pmc_mfma_{workload}")
+    with open(_find_csv(run, "counter_collection.csv")) as f:
+        crow = list(csv.DictReader(f))
+    with open(_find_csv(run, "kernel_trace.csv")) as f:
+        trow = list(csv.DictReader(f))
+    dur = {r["Dispatch_Id"]: float(r["End_Timestamp"]) - float(r["Start_Timestamp"]) for r in trow}
+    per = defaultdict(dict)
+    names = {}
+    for r in crow:
+        per[r["Dispatch_Id"]][r["Counter_Name"]] = per[r["Dispatch_Id"]].get(r["Counter_Name"], 0.0) + \
+            float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    agg = defaultdict(lambda: [0, 0.0, 0.0, 0.0])   # dispatches, ns, instructions, busy cycles
+    for d, c in per.items():
+        if _family_of(names[d]) != "gemm" or d not in dur:
+            continue
+        key = names[d].split("(")[0]
+        for k in (key, "all gemm"):
+            a = agg[k]
+            a[0] += 1
+            a[1] += dur[d]
+            a[2] += c.get("SQ_INSTS_MFMA", 0.0)
+            a[3] += c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+    out = [f"# Matrix-core use of the GEMM kernels — `{workload}` bench", "",
+           "Commands (from the repository root, on one MI355X):", "", "```",
+           "cd /tmp && export TMPDIR=/tmp",
+           f"rocprofv3 --pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES --kernel-trace --output-format csv "
+           f"-d <repo>/gpurun_out/pmc_mfma_{workload} -o run -- python3 <repo>/bench.py --config {workload} "
+           f"--steps 1 --warmup 0 --no-cpu",
+           f"python3 <repo>/bench.py --summarize-mfma <repo>/gpurun_out --config {workload}", "```", "",
+           "Per dispatch: MFMA rate = SQ_INSTS_MFMA x 4096 flops / dispatch time (every product runs on "
+           "v_mfma_f32_32x32x2_f32, 4096 flops per wave instruction); busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+           f"({SIMDS} SIMDs x dispatch time x {CLOCK_GHZ} GHz).  Counters serialize the dispatches, so times "
+           "are those of kernels running alone.", "",
+           "| Kernel | Dispatches | Time ms | MFMA TFLOP/s (% of 157.3) | MFMA busy | busy cycles per instruction |",
+           "|---|---|---|---|---|---|"]
+    for k, (n, ns, ins, busy) in sorted(agg.items(), key=lambda kv: (kv[0] != "all gemm", -kv[1][1])):
+        tf = ins * 4096 / ns / 1e3 if ns else 0.0
+        frac = busy / (SIMDS * ns * CLOCK_GHZ) if ns else 0.0
+        out.append(f"| `{k[:80]}` | {n} | {ns / 1e6:.2f} | {tf:.1f} ({100 * tf / PEAK_FP32_MFMA_TFLOPS:.1f}%) | "
+                   f"{100 * frac:.1f}% | {busy / ins if ins else 0:.1f} |")
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(path)
+
+
 def recorded_traffic(workload: str) -> dict:
     """family -> scaled HBM bytes per launch, for kernels unchanged since the counters."""
     out = {}
@@ -140,7 +271,7 @@ def make_gradients(wl, steps: int, device):
     import numpy as np
     import torch
     total_bytes = sum(m * n * 4 for m, n in wl.shapes)
-    distinct = steps if total_bytes * steps <= (2 << 30) else max(1, min(steps, (8 << 30) // total_bytes))
+    distinct = steps if total_bytes * steps <= (2 << 30) else max(1, min(steps, (24 << 30) // total_bytes))
     if total_bytes * distinct <= (512 << 20):
         out = []
         for t in range(1, distinct + 1):
@@ -214,9 +345,22 @@ def cpu_baseline(wl, budget_s: float = 15.0, codebook: str = "ls"):
         "unit": "block-steps/s",
         "cores": threads,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"{steps} step(s) x {len(sel)} of {len(wl.blocks)} blocks of {wl.name} "
                   f"(float64 NumPy, {elapsed:.1f} s, {os.cpu_count()} host cpus visible)",
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def main():
@@ -242,6 +386,13 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--summarize-traffic", metavar="OUTDIR", default=None,
                     help="write profiles/traffic_<config>.md from the rocprofv3 --pmc runs under OUTDIR")
+    ap.add_argument("--summarize-kernels", metavar="OUTDIR", default=None,
+                    help="write profiles/kernels_<config>.md from a rocprofv3 --kernel-trace --stats run "
+                         "under OUTDIR/prof_<config> (with the bench line that run printed in OUTDIR/"
+                         "prof_<config>.json)")
+    ap.add_argument("--summarize-mfma", metavar="OUTDIR", default=None,
+                    help="write profiles/mfma_<config>.md from a rocprofv3 --pmc SQ_INSTS_MFMA "
+                         "SQ_VALU_MFMA_BUSY_CYCLES --kernel-trace run under OUTDIR/pmc_mfma_<config>")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -254,6 +405,12 @@ def main():
 
     if args.summarize_traffic:
         summarize_traffic(args.config, args.summarize_traffic)
+        return
+    if args.summarize_kernels:
+        summarize_kernels(args.config, args.summarize_kernels)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.config, args.summarize_mfma)
         return
 
     import torch
@@ -273,7 +430,7 @@ def main():
     from workloads import cost, get_workload
 
     wl = get_workload(args.config)
-    steps = args.steps if args.steps is not None else (100 if len(wl.blocks) <= 4 else 5)
+    steps = args.steps if args.steps is not None else (100 if len(wl.blocks) <= 4 else 10)
     warmup = args.warmup if args.warmup is not None else (10 if len(wl.blocks) <= 4 else 2)
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
@@ -320,10 +477,12 @@ def main():
     value = len(wl.blocks) * steps / (ms / 1e3)
     log(f"[bench] timed {steps} steps: {ms_per_step:.3f} ms/step, {value:.1f} block-steps/s")
 
-    # second pass, every launch bracketed by HIP events on the library's stream
+    # second pass, every launch bracketed by HIP events on the library's stream (at most
+    # a few seconds of steps: the events serialize nothing, but the pass repeats work)
+    isteps = steps if ms_per_step * steps <= 10000 else max(1, min(steps, int(10000 // ms_per_step)))
     blocks.timing(True)
     t = t_start
-    for _ in range(steps):
+    for _ in range(isteps):
         t += 1
         run(t)
     rep = blocks.timing_report()
@@ -331,7 +490,7 @@ def main():
     torch.cuda.synchronize()
     for name, r in rep.items():
         if r["launches"]:
-            log(f"[bench] {name:12s} launches {r['launches']:6d}  {r['ms'] / steps:9.3f} ms/step  "
+            log(f"[bench] {name:12s} launches {r['launches']:6d}  {r['ms'] / isteps:9.3f} ms/step  "
                 f"{r['flops'] / max(r['ms'], 1e-9) / 1e9:8.2f} TFLOP/s  "
                 f"{r['bytes'] / max(r['ms'], 1e-9) / 1e6:8.1f} GB/s")
     fam = {"gemm": {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0}}
@@ -352,11 +511,17 @@ def main():
     traffic = recorded_traffic(wl.name)
     kernels = {
         "gemm": ("mfma", "gemm_kernel (fp32 v_mfma_f32_32x32x2_f32): every matrix product of the step; "
-                 "algorithmic flops = 2 M N K of the products each launch is given"),
+                 "algorithmic flops = 2 M N K of each product a launch is given, a symmetric product "
+                 "(V^T V, V diag(lam) V^T, G G^T, V diag(d) V^T) counted by its M (M + 1) / 2 distinct "
+                 "entries, K M (M + 1)"),
         "qr_panel": ("alu", "panel_*_kernel / qr_step_kernel: Householder factorization of one 32-column "
                      "panel per workgroup (one workgroup per side: a dependent chain of reflector steps, "
-                     "latency-bound); in the fused QR step of small batches the same launch carries the "
-                     "previous panel's compact-WY products on other workgroups (their flops included)"),
+                     "latency-bound); in the fused QR step of small batches the same launch applies the "
+                     "previous panel's reflectors to the trailing columns and to Q on other workgroups. "
+                     "Algorithmic flops: the standard Householder counts, 2 h nb^2 - 2 nb^3 / 3 per h x nb "
+                     "panel and 4 h nb c - 2 nb^2 c per nb reflectors of length h on c columns, with Q "
+                     "counted as formed backward (its h x h part per panel): (8/3) p^3 per side in all; "
+                     "peak: the fp32 vector rate without packed instructions"),
         "quant": ("hbm", "quant_kernel: 4.5625 B per element (fp32 in, nibble + 1/16 scale out)"),
         "dequant": ("hbm", "dequant_kernel: 4.5625 B per element (nibble + scale in, fp32 out)"),
         "graft": ("hbm", "graft_norms_kernel + graft_apply_kernel: per element G and P read (Adam: moments "
@@ -368,6 +533,7 @@ def main():
         if not r or not r["launches"] or r["ms"] <= 0:
             continue
         per_launch_s = r["ms"] * 1e-3 / r["launches"]
+        lps = r["launches"] / isteps
         if bound == "hbm":
             achieved, peak, unit = r["bytes"] / r["launches"] / per_launch_s / 1e9, PEAK_HBM_GBPS, "GB/s"
         else:
@@ -378,8 +544,8 @@ def main():
             "frac": round(achieved / peak, 6),
             "traffic": round(traffic[name]) if name in traffic else None,
             "algorithmic_bytes_per_launch": round(r["bytes"] / r["launches"]),
-            "launches_per_step": r["launches"] / steps, "avg_launch_us": round(per_launch_s * 1e6, 3),
-            "ms_per_step": round(r["ms"] / steps, 4),
+            "launches_per_step": lps, "avg_launch_us": round(per_launch_s * 1e6, 3),
+            "ms_per_step": round(r["ms"] / isteps, 4),
         }
     dominant = max(rooflines, key=lambda k: rooflines[k]["ms_per_step"])
     roofline = dict(rooflines[dominant], family=dominant)
@@ -413,7 +579,8 @@ def main():
         "algorithmic_tflops_per_step": round(step_flops / (ms_per_step * 1e-3) / 1e12, 3),
         "roofline": roofline,
         "rooflines": rooflines,
-        "kernel_ms_per_step": {k: round(v["ms"] / steps, 4) for k, v in rep.items() if v["launches"]},
+        "kernel_ms_per_step": {k: round(v["ms"] / isteps, 4) for k, v in rep.items() if v["launches"]},
+        "instrumented_steps": isteps,
         "cpu_baseline": None,
     }
     if args.newton > 0:

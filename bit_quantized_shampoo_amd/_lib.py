@@ -23,7 +23,7 @@ CODEBOOK_LINEAR_SQUARE = 0
 CODEBOOK_DYNAMIC_TREE = 1
 
 BUF_CODES, BUF_SCALES, BUF_EIG, BUF_ROOT_CODES, BUF_ROOT_SCALES, BUF_ROOT_D = range(6)
-BUF_V, BUF_STAT, BUF_Q, BUF_ROOT_V = 16, 17, 18, 19
+BUF_V, BUF_STAT, BUF_Q, BUF_ROOT_V, BUF_ROOT_MAT = 16, 17, 18, 19, 20
 
 EXPORTED = [
     "shampoo4_abi_version", "shampoo4_strerror", "shampoo4_plan", "shampoo4_init",

@@ -126,11 +126,12 @@ struct shampoo4_ctx_s {
     hipEvent_t pre_fork = nullptr, pre_join = nullptr;
     std::vector<hipEvent_t> sync_ev;
     // update_stats replayed from a HIP graph (captured on `cap` at the first call of each
-    // variant: with or without the cached rectified eigenvectors)
+    // variant: with or without the cached rectified eigenvectors, and with or without
+    // 16-byte loads of the gradients, which the captured kernels bake in)
     bool use_graphs = false;
     bool graph_ok = true;
     hipStream_t cap = nullptr;
-    hipGraphExec_t stats_graph[2] = {};
+    hipGraphExec_t stats_graph[2][2] = {};
     Seq qinit, sign, ray_gemm, rayleigh, quant, root_d, root_copy;
     Seq qinit_signed;                     // backward accumulation: Q starts as diag(sign(R_jj))
     Seq pre[4];
@@ -164,8 +165,9 @@ struct shampoo4_ctx_s {
         for (auto& e : ev_pool) (void)hipEventDestroy(e);
         for (auto& e : sync_ev)
             if (e) (void)hipEventDestroy(e);
-        for (auto& g : stats_graph)
-            if (g) (void)hipGraphExecDestroy(g);
+        for (auto& gv : stats_graph)
+            for (auto& g : gv)
+                if (g) (void)hipGraphExecDestroy(g);
         if (aux) (void)hipStreamDestroy(aux);
         if (pre_strm) (void)hipStreamDestroy(pre_strm);
         if (pre_fork) (void)hipEventDestroy(pre_fork);
@@ -320,13 +322,8 @@ struct shampoo4_ctx_s {
             if (d.flags & GEMM_F_SYM) {
                 const int t = d.tiles_m;
                 total += t * (t + 1) / 2 * std::max(1, d.ksplit);
-                // algorithmic work of the tiles computed: rows x columns of each tile on or
-                // above the diagonal
-                double elems = 0;
-                for (int tn = 0; tn < t; ++tn)
-                    for (int tm = 0; tm <= tn; ++tm)
-                        elems += (double)std::min(bm, d.M - tm * bm) * std::min(bn, d.N - tn * bn);
-                L.flops += 2.0 * elems * d.K;
+                // algorithmic work of a symmetric product: its M (M + 1) / 2 distinct entries
+                L.flops += (double)d.M * (d.M + 1) * d.K;
             } else {
                 total += d.tiles_m * ((d.N + bn - 1) / bn) * std::max(1, d.ksplit);
                 L.flops += 2.0 * d.M * d.N * d.K;
@@ -574,19 +571,24 @@ struct shampoo4_ctx_s {
             L.max_h = maxh[b];
             L.ntiles = (int)byc[b].size();
             for (const auto& pd : byc[b]) {
-                L.flops += panel_flops(pd.h, pd.nb);
+                L.flops += householder_flops(pd.h, pd.nb);
                 L.bytes += 4.0 * (double)pd.h * pd.nb * 3;   // read the panel, write V and Y
             }
             st.push_back(L);
         }
     }
-    // Algorithmic flops of one h x nb panel: for reflector j the column dots over rows
-    // j.. of columns j.. (2 (h-j)(nb-j)) and the update of columns j+1.. (2 (h-j)(nb-j-1)),
-    // the triangular factor T (nb^3 / 3) and Y = V T with triangular T (h nb^2).
-    static double panel_flops(int h, int nb) {
-        double f = (double)nb * nb * nb / 3.0 + (double)h * nb * nb;
-        for (int j = 0; j < nb; ++j) f += 2.0 * (h - j) * (2.0 * (nb - j) - 1.0);
-        return f;
+    // Algorithmic flops (the standard Householder counts; what the kernels add on top, the
+    // triangular factor T and its products, is not counted):
+    //   factorization of an h x nb panel                      2 h nb^2 - 2 nb^3 / 3
+    //   nb reflectors of length h applied to c columns         4 h nb c - 2 nb^2 c
+    // Summed over the panels of a p x p matrix: (4/3) p^3 for the factorization and, with Q
+    // formed by applying each panel to the h x h part of Q it reaches (c = h), another
+    // (4/3) p^3 for Q.
+    static double householder_flops(int h, int nb) {
+        return 2.0 * h * nb * nb - 2.0 * nb * nb * nb / 3.0;
+    }
+    static double reflector_apply_flops(int h, int nb, int c) {
+        return 4.0 * h * nb * c - 2.0 * (double)nb * nb * c;
     }
     static Launch sync_op(Kind k, int strm, int ev) {
         Launch L;
@@ -787,12 +789,12 @@ struct shampoo4_ctx_s {
                         sp.Tp = tblock(k - 1);
                         sp.nbp = kPanel;
                         sp.hp = pd.h + kPanel;
-                        flops += 4.0 * sp.hp * kPanel * pd.nb + 4.0 * kPanel * kPanel * pd.nb;
+                        flops += reflector_apply_flops(sp.hp, kPanel, pd.nb);
                         bytes += 4.0 * (2.0 * sp.hp * kPanel + (double)kPanel * pd.nb + kPanel * kPanel);
                     }
                     pds.push_back(sp);
                     max_h = std::max(max_h, pd.h);
-                    flops += panel_flops(pd.h, pd.nb);
+                    flops += householder_flops(pd.h, pd.nb);
                     bytes += 4.0 * (double)pd.h * pd.nb * 3;
                 }
                 const int r0 = (k - 1) * kPanel;
@@ -807,7 +809,7 @@ struct shampoo4_ctx_s {
                         sd.V = V; sd.T = T; sd.ld = p; sd.vld = kPanel;
                         sd.role = 0; sd.h = h; sd.count = std::min(kPanel, p - cs);
                         sds.push_back(sd);
-                        flops += 4.0 * h * nbk * sd.count;
+                        flops += reflector_apply_flops(h, nbk, sd.count);
                         bytes += 4.0 * h * (2.0 * kPanel + 2.0 * sd.count);
                     }
                     for (int q0 = 0; q0 < p; q0 += kPanel) {
@@ -821,7 +823,10 @@ struct shampoo4_ctx_s {
                         sd.ident = k == 1 ? 1 : 0;
                         sd.diag = q0 - r0;
                         sds.push_back(sd);
-                        flops += 4.0 * h * nbk * sd.count;
+                        // Q is accumulated forward over all its rows here; the algorithmic
+                        // count is that of applying the panel to the h x h part of Q it
+                        // reaches (its share of the (4/3) p^3 of forming Q)
+                        if (q0 == 0) flops += reflector_apply_flops(h, nbk, h);
                         bytes += 4.0 * h * (2.0 * kPanel + 2.0 * sd.count);
                     }
                 }
@@ -1389,13 +1394,13 @@ struct shampoo4_ctx_s {
     // replayed from a graph, after it when no power step runs)
     hipError_t submit_stats(hipStream_t s, const std::function<hipError_t()>* at_qr = nullptr) {
         const bool reuse = (cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) && root_v_valid && root_v_is_stats;
-        const int var = reuse ? 1 : 0;
+        const int var = reuse ? 1 : 0, vi = io_vec ? 1 : 0;
         hipError_t e = hipSuccess;
         if (use_graphs && graph_ok && !timing) {
-            if (!stats_graph[var]) capture_stats(reuse);
-            if (stats_graph[var]) {
+            if (!stats_graph[var][vi]) capture_stats(reuse);
+            if (stats_graph[var][vi]) {
                 if (at_qr) e = (*at_qr)();
-                if (e == hipSuccess) e = hipGraphLaunch(stats_graph[var], s);
+                if (e == hipSuccess) e = hipGraphLaunch(stats_graph[var][vi], s);
             } else {
                 e = stats_body(reuse, s, at_qr);
             }
@@ -1416,10 +1421,11 @@ struct shampoo4_ctx_s {
         return e;
     }
 
-    // Capture the statistics update once per variant on the private stream; a failed
-    // capture turns graphs off for the context (the calls then launch eagerly).
+    // Capture the statistics update once per variant (and gradient load width, io_vec
+    // as set by the current call's upload) on the private stream; a failed capture turns
+    // graphs off for the context (the calls then launch eagerly).
     void capture_stats(bool reuse) {
-        const int var = reuse ? 1 : 0;
+        const int var = reuse ? 1 : 0, vi = io_vec ? 1 : 0;
         if (!cap && hipStreamCreateWithFlags(&cap, hipStreamNonBlocking) != hipSuccess) {
             graph_ok = false;
             return;
@@ -1432,8 +1438,8 @@ struct shampoo4_ctx_s {
         hipGraph_t g = nullptr;
         const hipError_t e2 = hipStreamEndCapture(cap, &g);
         if (e != hipSuccess || e2 != hipSuccess || !g ||
-            hipGraphInstantiate(&stats_graph[var], g, nullptr, nullptr, 0) != hipSuccess) {
-            stats_graph[var] = nullptr;
+            hipGraphInstantiate(&stats_graph[var][vi], g, nullptr, nullptr, 0) != hipSuccess) {
+            stats_graph[var][vi] = nullptr;
             graph_ok = false;
         }
         if (g) (void)hipGraphDestroy(g);
@@ -1749,6 +1755,7 @@ shampoo4_status shampoo4_layout(shampoo4_ctx c, int32_t block, int32_t side, sha
         case SHAMPOO4_BUF_STAT: *offset = S.Lt; *bytes = mat; break;
         case SHAMPOO4_BUF_Q: *offset = S.Qm; *bytes = mat; break;
         case SHAMPOO4_BUF_ROOT_V: *offset = S.Vr; *bytes = mat; break;
+        case SHAMPOO4_BUF_ROOT_MAT: *offset = S.Rt; *bytes = mat; break;
         default: return SHAMPOO4_EINVAL;
     }
     return SHAMPOO4_OK;

@@ -97,7 +97,9 @@ typedef enum {
    empty) and every stage runs the same kernels with the codec replaced by copies. */
 #define SHAMPOO4_FLAG_FP32_STATE 16u
 /* Replay shampoo4_update_stats from a HIP graph captured at the first call (one graph
-   per variant: with or without the cached rectified eigenvectors): the kernels, and the
+   per variant: with or without the cached rectified eigenvectors, and with or without
+   16-byte loads of the gradients, which need every G 16-byte aligned with ldg a
+   multiple of 4): the kernels, and the
    second stream of QR_LOOKAHEAD with its event dependencies, are submitted as one graph
    launch instead of one host call each.  The io upload stays a separate copy before the
    launch.  While kernel timing is on, and if a capture fails, calls launch eagerly. */
@@ -153,8 +155,10 @@ typedef enum {
                                      last update_stats */
     SHAMPOO4_BUF_STAT = 17,       /* workspace: fp32 [p,p] statistic L~ of the last update */
     SHAMPOO4_BUF_Q = 18,          /* workspace: fp32 [p,p] refreshed eigenvectors Q */
-    SHAMPOO4_BUF_ROOT_V = 19      /* workspace: fp32 [p,p] rectified root eigenvectors of
+    SHAMPOO4_BUF_ROOT_V = 19,     /* workspace: fp32 [p,p] rectified root eigenvectors of
                                      the last refresh_root (ROOT_CACHE) or precondition */
+    SHAMPOO4_BUF_ROOT_MAT = 20    /* workspace: fp32 [p,p] root matrix V^r diag(d) V^r^T
+                                     (ROOT_CACHE: formed at init and at every refresh_root) */
 } shampoo4_buffer;
 
 /* ABI version of the loaded library (SHAMPOO4_ABI_VERSION). */
@@ -173,9 +177,11 @@ SHAMPOO4_API shampoo4_status shampoo4_plan(const shampoo4_config* cfg, int32_t n
 
 /* Create a context over caller-owned device buffers (both 256-byte aligned and at
  * least as large as shampoo4_plan reports) and, unless SHAMPOO4_FLAG_KEEP_STATE is
- * set, enqueue the initial state: U = I, lam = 0, root = (I, d = 1).  Enqueues the
- * descriptor tables into the workspace and waits for that copy (the only call that
- * synchronizes with the stream).  The buffers must outlive the context. */
+ * set, enqueue the initial state: U = I, lam = 0, root = (I, d = 1) (the pages fix no
+ * initial state; the identity root leaves G unchanged until the first refresh).
+ * Enqueues the descriptor tables into the workspace and waits for `stream` before
+ * returning (init and shampoo4_check are the only calls that synchronize: the host
+ * copy of the tables is freed afterwards).  The buffers must outlive the context. */
 SHAMPOO4_API shampoo4_status shampoo4_init(const shampoo4_config* cfg, int32_t nblocks,
                               const shampoo4_shape* shapes,
                               void* state, size_t state_bytes,
@@ -183,18 +189,36 @@ SHAMPOO4_API shampoo4_status shampoo4_init(const shampoo4_config* cfg, int32_t n
                               void* stream, shampoo4_ctx* out);
 
 /* One statistics update of every block: io is a host array of nblocks entries
- * (only G/ldg are read). */
+ * (only G/ldg are read).  Per side: the stored eigenvectors are dequantized and
+ * rectified ("4-bit Shampoo ..." abstract: the quantized eigenvector matrix is kept and
+ * its orthogonality rectified), the factor is rebuilt from them and its eigenvalues and
+ * updated with G G^T (side R: G^T G) as an exponential moving average ("Shampoo --
+ * Second-Order Optimizer", "Kronecker factorization" for the products, "Pitfalls, and
+ * the small-model view" for the EMA), and its eigenpairs are refreshed warm-started
+ * from the rectified eigenvectors, L = U Lambda U^T ("Rotation, not just rescaling"),
+ * then re-quantized.  The root snapshot is not touched. */
 SHAMPOO4_API shampoo4_status shampoo4_update_stats(shampoo4_ctx ctx, const shampoo4_io* io, void* stream);
 
-/* Root refresh of every block: d = (lam + eps)^(-1/4), root codes <- codes. */
+/* Root refresh of every block: d = (lam + eps)^(-1/4), root codes <- codes.  The
+ * damped eigen form of the inverse fourth root, U (Lambda + eps I)^(-1/4) U^T ("Shampoo
+ * -- Second-Order Optimizer", "Computing the inverse fourth root"), taken only every
+ * T steps while the statistics are updated every step ("The cost dial: update
+ * frequency, memory, blocking"); the caller decides when. */
 SHAMPOO4_API shampoo4_status shampoo4_refresh_root(shampoo4_ctx ctx, void* stream);
 
-/* Preconditioned direction of every block into io[b].P. */
+/* Preconditioned direction of every block into io[b].P: L^(-1/4) G R^(-1/4) ("Shampoo
+ * -- Second-Order Optimizer", "Where the fourth root comes from") in the eigen form of
+ * "Rotation, not just rescaling", with the root eigenvectors dequantized and rectified
+ * first ("4-bit Shampoo ..." abstract: rectification also serves the inverse 4-th
+ * root).  io[b].G and io[b].P are read / written; G is not modified. */
 SHAMPOO4_API shampoo4_status shampoo4_precondition(shampoo4_ctx ctx, const shampoo4_io* io, void* stream);
 
-/* One optimizer step of every block, the order of the blog's "Algorithm" section:
- * the statistics update, the root refresh when `refresh` is nonzero, then the
- * preconditioned direction into io[b].P (io as for shampoo4_precondition).  Results
+/* One optimizer step of every block, in the order "Shampoo -- Second-Order Optimizer"
+ * gives it: the statistics update every step ("Kronecker factorization"), the inverse
+ * roots only when `refresh` is nonzero ("Computing the inverse fourth root"; every T
+ * steps, "The cost dial: update frequency, memory, blocking"), then the preconditioned
+ * direction into io[b].P ("Where the fourth root comes from"; io as for
+ * shampoo4_precondition).  Results
  * equal, bit for bit, those of the three calls above in that order.  Without a refresh
  * and with SHAMPOO4_FLAG_ROOT_CACHE and valid cached roots, the preconditioned direction
  * only reads the cached root matrices and G, so it runs on a second stream of the

@@ -3,10 +3,13 @@ of the batch on the GPU, cached root matrices, the automatic QR schedule, the wo
 Bjorck iterations and root interval).
 
 The oracle is too slow for every block of these batches, so:
-  * sampled blocks (every distinct shape of the CNN batch, the first and last blocks of
-    the transformer batch, one 4096 block of the stress batch) get the full
-    teacher-forced comparison of the step harness (statistic, Q diag(lam) Q^T,
-    eigenvalues, codes, d, preconditioned gradient);
+  * sampled blocks (every distinct shape of the CNN batch and its last block, a block
+    of each layer kind of the transformer batch's first layer and its last block, the
+    first and last 4096 blocks of the stress batch) get the full teacher-forced
+    comparison of the step harness (statistic, Q diag(lam) Q^T, eigenvalues, codes, d,
+    root matrices, preconditioned gradient) over the workload's whole schedule (10, 10
+    and 3 steps, checked in windows, one test each; the 4096 batch's last step also on
+    its last block), every step run as one shampoo4_step call like the benchmark;
   * every side gets the checks that hold at any size: the new Q is orthonormal
     (computed in float64 on the device), finite, and a seeded sample of sides has codes
     equal, bit for bit, to the oracle codec applied to the GPU's own float32 Q.
@@ -60,23 +63,28 @@ def _distinct_shape_blocks(shapes):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,steps,ncodes", [
-    ("cnn_batch", 2, 64),
-    ("transformer_batch", 2, 24),
-    ("large_4096", 2, 6),
+@pytest.mark.parametrize("name,first,last,blocks,ncodes", [
+    ("cnn_batch", 1, 5, "sample", 64),
+    ("cnn_batch", 6, 10, "sample", 64),
+    ("transformer_batch", 1, 5, "sample", 24),
+    ("transformer_batch", 6, 10, "sample", 24),
+    ("large_4096", 1, 2, "first", 6),
+    ("large_4096", 3, 3, "first", 6),
+    ("large_4096", 3, 3, "last", 6),
 ])
-def test_full_size_sampled(name, steps, ncodes):
+def test_full_size_sampled(name, first, last, blocks, ncodes):
     require_gpu()
     wl = get_workload(name)
     shapes = wl.shapes
     if name == "cnn_batch":
         sample = sorted(set(_distinct_shape_blocks(shapes) + [len(shapes) - 1]))
     elif name == "transformer_batch":
-        sample = [0, len(shapes) - 1]
+        # one block of each of the four layer kinds in the first layer, and the last block
+        sample = [0, 3, 4, 8, len(shapes) - 1]
     else:
-        sample = [len(shapes) // 2]
-    announce(f"full size {name}: {len(shapes)} blocks, oracle on blocks {sample}")
-    _run_teacher_forced(shapes, wl.gradients, steps, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
+        sample = [0] if blocks == "first" else [len(shapes) - 1]
+    announce(f"full size {name}: {len(shapes)} blocks, oracle on blocks {sample}, steps {first}-{last}")
+    _run_teacher_forced(shapes, wl.gradients, last, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
                         power_iters=wl.power_iters, root_interval=wl.root_interval, root_cache=True,
-                        label=name, qr="auto", sample=sample,
-                        all_sides=_side_checks(shapes, ncodes, seed=len(shapes)))
+                        label=f"{name} {first}-{last}", qr="auto", sample=sample, use_step=True,
+                        check_from=first, all_sides=_side_checks(shapes, ncodes, seed=len(shapes)))

@@ -457,3 +457,85 @@ def test_initial_root_is_identity():
     orc = o.Shampoo4Oracle([(5, 3)])
     G = rng.standard_normal((5, 3)).astype(np.float32)
     assert np.array_equal(orc.precondition([G])[0], G)
+
+
+# ---------------------------------------------------------------------------
+# Root refresh every T > 1 steps ("The cost dial": accumulate every step,
+# recompute the roots only every T steps)
+# ---------------------------------------------------------------------------
+
+def test_diagonal_gradients_with_stale_root_between_refreshes():
+    """Square diagonal gradients with the root refreshed every T = 3 steps: the
+    eigenvalues follow the RMSprop accumulator at every step, but the direction uses
+    the accumulator as it was at the last refresh, g_t / sqrt(v_tau + eps) with
+    tau = 3 * floor(t / 3), and the identity root (P = G) before the first refresh.
+    A schedule that refreshed every step, or that paired the current eigenvalues with
+    the stale root, fails."""
+    rng = _rng(17)
+    p, T = 12, 3
+    beta, eps = 0.9, 1e-6
+    orc = o.Shampoo4Oracle([(p, p)], beta=beta, eps=eps)
+    v = np.zeros(p, np.float32)
+    v_root = None
+    b32 = np.float32(beta)
+    for t in range(1, 11):
+        g = rng.standard_normal(p).astype(np.float32) * np.float32(10.0) ** rng.uniform(-1, 1, p).astype(np.float32)
+        P = orc.step([np.diag(g)], t, root_interval=T)[0]
+        v = (np.float64(b32) * v + (1.0 - np.float64(b32)) * g.astype(np.float64) ** 2).astype(np.float32)
+        for s in (0, 1):
+            assert np.allclose(orc.sides[0][s].lam, v, rtol=1e-6, atol=1e-30)
+        if t % T == 0:
+            v_root = v.copy()
+        if v_root is None:
+            assert np.array_equal(P, np.diag(g))
+        else:
+            upd = g / np.sqrt(v_root.astype(np.float64) + float(np.float32(eps)))
+            assert np.allclose(np.diag(P), upd, rtol=1e-6, atol=1e-30), t
+            if t % T != 0:
+                # the current accumulator differs from the one the root was taken from
+                assert not np.allclose(np.diag(P), g / np.sqrt(v.astype(np.float64) + eps), rtol=1e-4)
+        assert np.count_nonzero(P - np.diag(np.diag(P))) == 0
+
+
+def test_root_snapshot_is_the_state_at_the_last_refresh():
+    """Between refreshes the root codes and d stay those taken at the last refresh while
+    the statistics state moves on every step (general, non-diagonal gradients)."""
+    rng = _rng(18)
+    m, n, T = 9, 6, 4
+    orc = o.Shampoo4Oracle([(m, n)], beta=0.9, eps=1e-6)
+    snap = None
+    for t in range(1, 10):
+        G = rng.standard_normal((m, n)).astype(np.float32)
+        orc.step([G], t, root_interval=T)
+        sides = orc.sides[0]
+        if t % T == 0:
+            snap = [(s.codes.copy(), s.scales.copy(), o.root_scaling(s.lam, 1e-6)) for s in sides]
+        for s_, st in enumerate(sides):
+            if snap is None:
+                ref = o.initial_side(st.p)
+                assert np.array_equal(st.root_codes, ref.codes) and np.all(st.d == 1)
+            else:
+                c, sc, d = snap[s_]
+                assert np.array_equal(st.root_codes, c) and np.array_equal(st.root_scales, sc)
+                assert np.array_equal(st.d, d)
+
+
+def test_degree_zero_homogeneity_with_root_interval():
+    """Homogeneity holds for the whole schedule at T = 3 too: codes bit-identical under
+    G -> 2G and directions equal at eps = 0 (from step 1 the identity root gives P = G,
+    which scales; from the first refresh on the step is invariant)."""
+    rng = _rng(19)
+    m, n, T = 6, 6, 3
+    Gs = [rng.standard_normal((m, n)).astype(np.float32) for _ in range(7)]
+    a = o.Shampoo4Oracle([(m, n)], beta=0.9, eps=0.0)
+    b = o.Shampoo4Oracle([(m, n)], beta=0.9, eps=0.0)
+    for t, G in enumerate(Gs, start=1):
+        Pa = a.step([G], t, root_interval=T)[0]
+        Pb = b.step([np.float32(2) * G], t, root_interval=T)[0]
+        for s in (0, 1):
+            assert np.array_equal(a.sides[0][s].codes, b.sides[0][s].codes)
+            assert np.array_equal(a.sides[0][s].root_codes, b.sides[0][s].root_codes)
+        if t < T:
+            assert np.array_equal(Pb, np.float32(2) * Pa)
+        else:
+            assert np.linalg.norm(Pa - Pb) <= 1e-6 * np.linalg.norm(Pa), t
