@@ -143,6 +143,12 @@ def _bench_line(path: str):
     raise ValueError(f"no JSON line in {path}")
 
 
+def _short_kernel_name(name: str) -> str:
+    """Kernel name without return type, namespaces and parameter list."""
+    n = name.replace("void ", "").replace("(anonymous namespace)::", "").replace("s4::", "")
+    return n.split("(")[0]
+
+
 def summarize_kernels(workload: str, outdir: str):
     """profiles/kernels_<workload>.md from a rocprofv3 --kernel-trace --stats run of the
     bench, with the per-family averages set beside the bench's live HIP-event figures."""
@@ -162,6 +168,21 @@ def summarize_kernels(workload: str, outdir: str):
     dom = line["roofline"]["family"]
     steps, warm = line["steps"], line["warmup"]
     isteps = line.get("instrumented_steps", steps)
+    # the launches of the timed and instrumented steps (the trace's last ones), without
+    # the context set-up and warmup
+    steady = {}
+    try:
+        with open(_find_csv(run, "kernel_trace.csv")) as f:
+            trace = list(csv.DictReader(f))
+        trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+        for k, rl in line.get("rooflines", {}).items():
+            n = int(round(rl["launches_per_step"] * (steps + isteps)))
+            d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
+                 if _family_of(r["Kernel_Name"]) == k][-n:]
+            if d:
+                steady[k] = sum(d) / len(d) / 1e3
+    except FileNotFoundError:
+        pass
     out = [f"# Kernel time summary — `{workload}` bench", "",
            "Command (from the repository root, on one MI355X):", "", "```",
            "cd /tmp && export TMPDIR=/tmp",
@@ -174,15 +195,17 @@ def summarize_kernels(workload: str, outdir: str):
            f"block-steps/s, {line['ms_per_step']} ms/step.", "",
            "Per kernel family (all launches in the trace; the bench's live figure is the average launch "
            "of its instrumented pass, in-dispatch HIP events on the library's stream):", "",
-           "| Family | Calls | Total ms | Average µs (profiler) | Average µs (bench, live) |",
-           "|---|---|---|---|---|"]
+           "| Family | Calls | Total ms | Average µs, all launches | Average µs, launches of the "
+           "timed and instrumented steps (profiler) | Average µs (bench, live) |",
+           "|---|---|---|---|---|---|"]
     for k, (calls, ns) in sorted(fam.items(), key=lambda kv: -kv[1][1]):
         live = line.get("rooflines", {}).get(k, {}).get("avg_launch_us")
+        st = f"{steady[k]:.2f}" if k in steady else "—"
         out.append(f"| `{k}`{' (dominant)' if k == dom else ''} | {calls} | {ns / 1e6:.2f} | "
-                   f"{ns / calls / 1e3:.2f} | {live if live is not None else '—'} |")
+                   f"{ns / calls / 1e3:.2f} | {st} | {live if live is not None else '—'} |")
     out += ["", "Kernels (top 30 by time):", "", "| Kernel | Calls | Total ms | Average µs | % |", "|---|---|---|---|---|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[:30]:
-        nm = r["Name"].replace("|", "\\|")
+        nm = _short_kernel_name(r["Name"]).replace("|", "\\|")
         out.append(f"| `{nm[:90]}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
                    f"{float(r['AverageNs']) / 1e3:.2f} | {100.0 * float(r['TotalDurationNs']) / total_ns:.1f} |")
     path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
@@ -214,7 +237,7 @@ def summarize_mfma(workload: str, outdir: str):
     for d, c in per.items():
         if _family_of(names[d]) != "gemm" or d not in dur:
             continue
-        key = names[d].split("(")[0]
+        key = _short_kernel_name(names[d])
         for k in (key, "all gemm"):
             a = agg[k]
             a[0] += 1
