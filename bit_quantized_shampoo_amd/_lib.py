@@ -19,6 +19,8 @@ FLAG_QR_LOOKAHEAD = 8
 FLAG_FP32_STATE = 16
 FLAG_GRAPHS = 32
 FLAG_DT_CODEBOOK = 64
+DIAG_L = 1
+DIAG_R = 2
 CODEBOOK_LINEAR_SQUARE = 0
 CODEBOOK_DYNAMIC_TREE = 1
 
@@ -32,7 +34,7 @@ EXPORTED = [
     "shampoo4_dequantize", "shampoo4_codebook", "shampoo4_quantize_ex", "shampoo4_dequantize_ex",
     "shampoo4_codebook_ex", "shampoo4_gemm_workspace_bytes",
     "shampoo4_gemm_batched", "shampoo4_timing", "shampoo4_timing_report", "shampoo4_graft",
-    "shampoo4_inverse_root_workspace_bytes", "shampoo4_inverse_root",
+    "shampoo4_inverse_root_workspace_bytes", "shampoo4_inverse_root", "shampoo4_plan_ex", "shampoo4_init_ex",
 ]
 
 GRAFT_SGD, GRAFT_ADAM = 0, 1
@@ -90,6 +92,10 @@ def lib() -> ctypes.CDLL:
                                ctypes.POINTER(sz), ctypes.POINTER(sz)]),
         "shampoo4_init": (st, [ctypes.POINTER(Config), i32, ctypes.POINTER(Shape), vp, sz, vp, sz, vp,
                                ctypes.POINTER(vp)]),
+        "shampoo4_plan_ex": (st, [ctypes.POINTER(Config), i32, ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_uint8),
+                                  ctypes.POINTER(sz), ctypes.POINTER(sz)]),
+        "shampoo4_init_ex": (st, [ctypes.POINTER(Config), i32, ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_uint8),
+                                  vp, sz, vp, sz, vp, ctypes.POINTER(vp)]),
         "shampoo4_update_stats": (st, [vp, ctypes.POINTER(Io), vp]),
         "shampoo4_refresh_root": (st, [vp, vp]),
         "shampoo4_precondition": (st, [vp, ctypes.POINTER(Io), vp]),

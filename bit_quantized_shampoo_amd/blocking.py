@@ -3,14 +3,15 @@
 Follows "Shampoo -- Second-Order Optimizer", section "Blocked and distributed variants":
 every matrix parameter is cut into tiles of at most ``block`` x ``block`` that are
 preconditioned independently (capping both the factor memory and the cubic cost), and
-the page's two fallbacks route parameters without a usable matrix structure to a
-diagonal method:
+the page's two fallbacks:
 
-* 1-D (and 0-D) parameters such as biases and normalization gains;
-* parameters with a dimension above ``max_dim`` when blocking is off (``block=None``):
-  the page drops that side's factor and keeps a diagonal method along it; this library
-  preconditions both sides of every block, so such a parameter goes to the diagonal
-  method as a whole.
+* a tile dimension above the threshold ``max_dim`` (blocking off, ``block=None``, or
+  tiles larger than the threshold): that side's factor is dropped and the tile keeps
+  diagonal AdaGrad along it, the library's diagonal side (``Shampoo4Blocks(...,
+  diagonal=block_diagonal_sides(plans))``), up to the library's limit ``max_diag_dim``
+  for such a side; a parameter beyond that goes to the caller's diagonal method whole;
+* 1-D (and 0-D) parameters such as biases and normalization gains stay on the caller's
+  diagonal method (kind "diagonal").
 
 Matrix parameters of higher rank (convolution kernels [out, in, kh, kw]) are viewed as
 [out, in * kh * kw].  Tiles are row-major with a remainder tile at the end of each row
@@ -31,6 +32,7 @@ class ParamPlan:
     kind: str                       # "blocks" or "diagonal"
     matrix: tuple | None = None     # (m, n) 2-D view for "blocks"
     tiles: list = field(default_factory=list)   # (r0, c0, rows, cols)
+    tile_diagonal: list = field(default_factory=list)   # per tile (side L diagonal, side R diagonal)
 
 
 def matrix_view_shape(shape) -> tuple | None:
@@ -48,10 +50,14 @@ def tile(m: int, n: int, block: int) -> list:
             for r0 in range(0, m, block) for c0 in range(0, n, block)]
 
 
-def plan_blocks(shapes, block: int | None = 1024, max_dim: int = 8192) -> list:
-    """One ParamPlan per parameter shape."""
+def plan_blocks(shapes, block: int | None = 1024, max_dim: int = 8192, max_diag_dim: int = 65536) -> list:
+    """One ParamPlan per parameter shape.  A tile side longer than ``max_dim`` is
+    diagonal; a parameter whose diagonal side would exceed ``max_diag_dim`` goes to the
+    caller's diagonal method whole."""
     if block is not None and block < 1:
         raise ValueError("block must be positive")
+    if not 1 <= max_dim <= max_diag_dim:
+        raise ValueError("need 1 <= max_dim <= max_diag_dim")
     out = []
     for i, shape in enumerate(shapes):
         shape = tuple(int(d) for d in shape)
@@ -60,19 +66,23 @@ def plan_blocks(shapes, block: int | None = 1024, max_dim: int = 8192) -> list:
             out.append(ParamPlan(i, shape, "diagonal"))
             continue
         m, n = mv
-        if block is None:
-            if m > max_dim or n > max_dim:
-                out.append(ParamPlan(i, shape, "diagonal"))
-            else:
-                out.append(ParamPlan(i, shape, "blocks", mv, [(0, 0, m, n)]))
+        tiles = [(0, 0, m, n)] if block is None else tile(m, n, block)
+        if any(t[2] > max_diag_dim or t[3] > max_diag_dim for t in tiles):
+            out.append(ParamPlan(i, shape, "diagonal"))
             continue
-        out.append(ParamPlan(i, shape, "blocks", mv, tile(m, n, block)))
+        diag = [(t[2] > max_dim, t[3] > max_dim) for t in tiles]
+        out.append(ParamPlan(i, shape, "blocks", mv, tiles, diag))
     return out
 
 
 def block_shapes(plans) -> list:
     """(rows, cols) of every tile, in plan order (the shapes a context is built for)."""
     return [(t[2], t[3]) for p in plans if p.kind == "blocks" for t in p.tiles]
+
+
+def block_diagonal_sides(plans) -> list:
+    """(side L diagonal, side R diagonal) of every tile, in block_shapes order."""
+    return [d for p in plans if p.kind == "blocks" for d in p.tile_diagonal]
 
 
 def block_views(tensors, plans) -> list:

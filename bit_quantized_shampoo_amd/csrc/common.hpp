@@ -212,6 +212,11 @@ struct VecDesc {
 static_assert(sizeof(VecDesc) == 64, "VecDesc layout");
 
 // Initial state of one side: U = I (codes and scales), lam = 0, root = (I, d = 1).
+enum : int32_t {
+    INIT_4BIT = 0,            // U as 4-bit codes and scales
+    INIT_FP32 = 1,            // U kept in float32: codes/rcodes hold p x p floats, no scales
+    INIT_DIAG = 2,            // diagonal side: only lam = 0 and d = 1
+};
 struct InitDesc {
     uint8_t* codes;
     float* scales;
@@ -220,9 +225,23 @@ struct InitDesc {
     float* rscales;
     float* d;
     int32_t p;
-    int32_t fp32;             // U kept in float32: codes/rcodes hold p x p floats, no scales
+    int32_t kind;             // INIT_*
 };
 static_assert(sizeof(InitDesc) == 56, "InitDesc layout");
+
+// One block with a diagonal side (the fallback for a side over the size threshold):
+// G (and P) through io entry `blk`; rowpart [tiles_n][m] receives partial row sums of G^2
+// (side L diagonal), colpart [tiles_m][n] partial column sums (side R diagonal); d_l and
+// d_r are the root scalings of a block whose two sides are diagonal (P = diag(d_l) G
+// diag(d_r)).
+struct DiagDesc {
+    float* rowpart;
+    float* colpart;
+    const float* d_l;
+    const float* d_r;
+    int32_t m, n, blk, tiles_n;
+};
+static_assert(sizeof(DiagDesc) == 48, "DiagDesc layout");
 
 // Find the work item owning `tile` from an inclusive-exclusive prefix of tile counts.
 __device__ __forceinline__ int find_item(const int* __restrict__ prefix, int n, int tile) {

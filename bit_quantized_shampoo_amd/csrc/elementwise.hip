@@ -113,7 +113,9 @@ __global__ __launch_bounds__(256) void identity_state_kernel(const InitDesc* __r
     const int64_t n = p * p;
     const int64_t nqb = (n + 63) / 64;
     const int64_t i = (int64_t)(blockIdx.x - prefix[item]) * 256 + threadIdx.x;
-    if (i < nqb && d.fp32) {   // float32 U = I: 64 elements per thread
+    if (d.kind == INIT_DIAG) {
+        // diagonal side: no eigenvectors
+    } else if (i < nqb && d.kind == INIT_FP32) {   // float32 U = I: 64 elements per thread
         float* u = reinterpret_cast<float*>(d.codes);
         float* ru = reinterpret_cast<float*>(d.rcodes);
         for (int e = 0; e < 64; ++e) {

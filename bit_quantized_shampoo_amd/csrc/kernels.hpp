@@ -94,6 +94,19 @@ hipError_t launch_newton_scale(const NewtonDesc* descs, int ndesc, hipStream_t s
 hipError_t launch_newton_elem(const NewtonDesc* descs, const int* prefix, int ndesc, int ntiles, int mode,
                               float eps, hipStream_t stream);
 
+// Diagonal fallback: partial sums of G^2 over tiles of DIAG_TR rows x DIAG_TC columns,
+// their EMA into the diagonal statistic, and P = diag(d_L) G diag(d_R).
+constexpr int DIAG_TR = 32;
+constexpr int DIAG_TC = 256;
+constexpr int diag_scale_rows(int n) { return n >= 4096 ? 1 : 4096 / n; }
+hipError_t launch_diag_partials(const DiagDesc* descs, const int* prefix, int ndesc, int ntiles,
+                                const IoEntry* io, hipStream_t stream);
+// out_j = beta out_j + (1 - beta) sum_{t < rows} a[t * ld + j] (VecDesc: a, out, ld, p, rows)
+hipError_t launch_diag_ema(const VecDesc* descs, const int* prefix, int ndesc, int ntiles, float beta,
+                           uint32_t* flag, hipStream_t stream);
+hipError_t launch_diag_scale(const DiagDesc* descs, const int* prefix, int ndesc, int ntiles,
+                             const IoEntry* io, hipStream_t stream);
+
 // Grafting epilogue: two launches over the same row tiles of every block.
 constexpr int GRAFT_TILE = 4096;             // elements per workgroup (at least one row)
 constexpr int graft_rows(int n) { return n >= GRAFT_TILE ? 1 : GRAFT_TILE / n; }

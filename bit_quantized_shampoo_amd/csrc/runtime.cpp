@@ -31,7 +31,8 @@ static_assert(sizeof(IoEntry) == sizeof(shampoo4_io) && sizeof(GraftIo) == sizeo
 constexpr int kPanel = 32;          // Householder panel width
 constexpr int kOuter = 128;         // columns whose reflectors update the trailing matrix together
 constexpr int kMaxSplit = GEMM_MAX_SLABS;   // split-K chunks of the skinny QR products
-constexpr int kMaxDim = 8192;
+constexpr int kMaxDim = 8192;       // order of a side that keeps eigenvectors
+constexpr int kMaxDiagDim = 65536;  // order of a diagonal side
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -39,18 +40,18 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 enum Family {
     FAM_GEMM_BJORCK = 0, FAM_GEMM_STATS, FAM_GEMM_POWER, FAM_GEMM_QR, FAM_GEMM_RAYLEIGH,
     FAM_GEMM_PRECOND, FAM_DEQUANT, FAM_QUANT, FAM_PANEL, FAM_RAYLEIGH, FAM_ELEMENTWISE, FAM_GRAFT,
-    FAM_GEMM_QR_TRAIL, FAM_GEMM_QR_Q, FAM_N
+    FAM_GEMM_QR_TRAIL, FAM_GEMM_QR_Q, FAM_DIAG, FAM_N
 };
 // gemm_qr: the reflector products inside an outer block (and the look-ahead schedule's);
 // gemm_qr_trail: an outer block's reflectors on the trailing columns; gemm_qr_q: the
 // accumulation of Q
 const char* kFamilyNames[FAM_N] = {"gemm_bjorck", "gemm_stats", "gemm_power", "gemm_qr", "gemm_rayleigh",
                                    "gemm_precond", "dequant", "quant", "qr_panel", "rayleigh",
-                                   "elementwise", "graft", "gemm_qr_trail", "gemm_qr_q"};
+                                   "elementwise", "graft", "gemm_qr_trail", "gemm_qr_q", "diag"};
 
 enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT,
             K_RECORD, K_WAIT, K_GRAFT_NORMS, K_GRAFT_APPLY, K_COPYF, K_NEWTON_NORM, K_NEWTON_SCALE,
-            K_NEWTON_ELEM, K_QRSTEP };
+            K_NEWTON_ELEM, K_QRSTEP, K_DIAG_PARTIALS, K_DIAG_EMA, K_DIAG_SCALE };
 
 struct Launch {
     Kind kind = K_GEMM;
@@ -72,6 +73,7 @@ using Seq = std::vector<Launch>;
 
 struct Side {
     int p = 0, q = 0;
+    bool diag = false;   // diagonal fallback: only the diagonal statistic (lam) and d
     int64_t nqb = 0;
     // state offsets
     size_t codes = 0, scales = 0, lam = 0, rcodes = 0, rscales = 0, d = 0;
@@ -97,7 +99,10 @@ struct shampoo4_ctx_s {
     uint8_t* ws = nullptr;
     size_t st_bytes = 0, ws_bytes = 0;
     std::vector<Side> sides;             // 2 per block: L then R
+    std::vector<std::reference_wrapper<Side>> full;   // the sides that keep eigenvectors
+    std::vector<uint8_t> diag_bits;      // per block: SHAMPOO4_DIAG_L | SHAMPOO4_DIAG_R
     std::vector<size_t> X1, X2;          // per block precondition temporaries
+    std::vector<size_t> RP, CP;          // per block partial row / column sums of G^2 (diagonal sides)
     size_t io_off = 0, gio_off = 0, flag_off = 0, parts_off = 0, desc_base = 0;
     std::vector<uint8_t> last_io, last_gio;   // host copies of the tables last uploaded
     std::vector<uint8_t> blob;           // descriptor region contents
@@ -140,6 +145,7 @@ struct shampoo4_ctx_s {
     // longer workgroups leave most CUs to the panel launches
     Seq pre_side[2];
     Seq graft_seq[2];                    // per graft mode (bytes differ): norms, apply
+    Seq diag_stats, diag_pre;            // diagonal sides: statistic; P of blocks with both sides diagonal
     GraftParams graft_prm{};
     float newton_eps = 0.f;              // damping of the coupled Newton inverse root (standalone call)
 
@@ -359,7 +365,9 @@ struct shampoo4_ctx_s {
         L.kind = kind;
         L.fam = kind == K_DEQUANT ? FAM_DEQUANT : kind == K_QUANT ? FAM_QUANT : kind == K_PANEL ? FAM_PANEL
               : kind == K_RAYLEIGH ? FAM_RAYLEIGH
-              : (kind == K_GRAFT_NORMS || kind == K_GRAFT_APPLY) ? FAM_GRAFT : FAM_ELEMENTWISE;
+              : (kind == K_GRAFT_NORMS || kind == K_GRAFT_APPLY) ? FAM_GRAFT
+              : (kind == K_DIAG_PARTIALS || kind == K_DIAG_EMA || kind == K_DIAG_SCALE) ? FAM_DIAG
+              : FAM_ELEMENTWISE;
         std::vector<int> prefix;
         int total = 0;
         for (int t : tiles) {
@@ -385,7 +393,11 @@ struct shampoo4_ctx_s {
         // latency: panel-wide updates on the caller's stream (or, on request, with the
         // trailing and Q updates overlapped on a second stream).
         double work = 0;
-        for (auto& sh : shapes) work += (double)sh.m * sh.m * sh.m + (double)sh.n * sh.n * sh.n;
+        for (int b = 0; b < nb; ++b) {
+            const double m = shapes[b].m, n = shapes[b].n;
+            if (!(diag_bits[b] & SHAMPOO4_DIAG_L)) work += m * m * m;
+            if (!(diag_bits[b] & SHAMPOO4_DIAG_R)) work += n * n * n;
+        }
         lookahead = (cfg.flags & SHAMPOO4_FLAG_QR_LOOKAHEAD) != 0;
         const bool blocked = (cfg.flags & SHAMPOO4_FLAG_QR_BLOCKED) ||
                              (!lookahead && work >= 16.0 * 1073741824.0);
@@ -404,12 +416,25 @@ struct shampoo4_ctx_s {
         }
         X1.resize(nb);
         X2.resize(nb);
+        RP.assign(nb, 0);
+        CP.assign(nb, 0);
         for (int b = 0; b < nb; ++b) {
             for (int s = 0; s < 2; ++s) {
                 Side& S = sides[2 * b + s];
                 S.p = s == 0 ? shapes[b].m : shapes[b].n;
                 S.q = s == 0 ? shapes[b].n : shapes[b].m;
+                S.diag = (diag_bits[b] & (s == 0 ? SHAMPOO4_DIAG_L : SHAMPOO4_DIAG_R)) != 0;
                 const int64_t p = S.p;
+                if (S.diag) {   // the diagonal statistic and d only
+                    S.nqb = 0;
+                    S.codes = st_take(0);
+                    S.scales = st_take(0);
+                    S.lam = st_take(p * 4);
+                    S.rcodes = st_take(0);
+                    S.rscales = st_take(0);
+                    S.d = st_take(p * 4);
+                    continue;
+                }
                 S.nqb = (p * p + 63) / 64;
                 const size_t ubytes = fp32_state ? (size_t)p * p * 4 : (size_t)S.nqb * 32;
                 const size_t sbytes = fp32_state ? 0 : (size_t)S.nqb * 4;
@@ -445,11 +470,19 @@ struct shampoo4_ctx_s {
             }
             X1[b] = ws_take((size_t)shapes[b].m * shapes[b].n * 4);
             X2[b] = ws_take((size_t)shapes[b].m * shapes[b].n * 4);
+            const int64_t m = shapes[b].m, n = shapes[b].n;
+            if (diag_bits[b] & SHAMPOO4_DIAG_L) RP[b] = ws_take((size_t)((n + DIAG_TC - 1) / DIAG_TC) * m * 4);
+            if (diag_bits[b] & SHAMPOO4_DIAG_R) CP[b] = ws_take((size_t)((m + DIAG_TR - 1) / DIAG_TR) * n * 4);
         }
         st_bytes = so;
         desc_base = wo;
         max_panels = 0;
-        for (auto& S : sides) max_panels = std::max(max_panels, (S.p + kPanel - 1) / kPanel);
+        full.clear();
+        for (auto& S : sides)
+            if (!S.diag) {
+                full.push_back(S);
+                max_panels = std::max(max_panels, (S.p + kPanel - 1) / kPanel);
+            }
     }
 
     GemmDesc gd(const float* A, int64_t lda, const float* B, int64_t ldb, float* D, int64_t ldd,
@@ -482,7 +515,7 @@ struct shampoo4_ctx_s {
         const int k = cfg.bjorck_iters;
         std::vector<CodecDesc> cds;
         std::vector<int> tiles;
-        for (auto& S : sides) {
+        for (Side& S : full) {
             const size_t fin = root ? S.Vr : S.Vs;
             const size_t start = (k % 2 == 1) ? S.Tmp : fin;
             CodecDesc c;
@@ -497,7 +530,7 @@ struct shampoo4_ctx_s {
         if (fp32_state) {   // 32-bit state: U is copied into the Bjorck chain's first buffer
             std::vector<VecDesc> vd;
             std::vector<int> vt;
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 const size_t fin = root ? S.Vr : S.Vs;
                 vd.push_back(copyf_desc(stf(root ? S.rcodes : S.codes), wsf((k % 2 == 1) ? S.Tmp : fin),
                                         (int64_t)S.p * S.p));
@@ -505,17 +538,17 @@ struct shampoo4_ctx_s {
             }
             Launch L = make_items(K_COPYF, vd, vt);
             L.fam = FAM_DEQUANT;
-            for (auto& S : sides) L.bytes += (double)S.p * S.p * 8.0;
+            for (Side& S : full) L.bytes += (double)S.p * S.p * 8.0;
             deq = {L};
         } else {
             Launch L = make_items(K_DEQUANT, cds, tiles);
-            for (auto& S : sides) L.bytes += (double)S.p * S.p * (4.0 + 0.5 + 4.0 / 64);
+            for (Side& S : full) L.bytes += (double)S.p * S.p * (4.0 + 0.5 + 4.0 / 64);
             deq = {L};
         }
         iters.clear();
         for (int i = 0; i < k; ++i) {
             std::vector<GemmItem> gram, upd;
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 const size_t fin = root ? S.Vr : S.Vs;
                 const size_t start = (k % 2 == 1) ? S.Tmp : fin;
                 const size_t other = (start == S.Tmp) ? fin : S.Tmp;
@@ -623,7 +656,7 @@ struct shampoo4_ctx_s {
             // GPU still spreads its long-K (K = panel height) products
             long tin = 0, tout = 0;
             int kin = 1 << 30, kout = 1 << 30;
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 const int p = S.p, c0 = sidx * kPanel;
                 if (c0 >= p) continue;
                 const int C0 = c0 / outer * outer, wb = std::min(outer, p - C0);
@@ -637,7 +670,7 @@ struct shampoo4_ctx_s {
                 }
             }
             const int ks_in = split_for(tin, kin), ks_out = split_for(tout, kout);
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 const int p = S.p;
                 const int c0 = sidx * kPanel;
                 if (c0 >= p) continue;
@@ -712,19 +745,19 @@ struct shampoo4_ctx_s {
         }
         // backward accumulation of Q (Q holds I): block b, last to first
         int max_outer = 0;
-        for (auto& S : sides) max_outer = std::max(max_outer, (S.p + outer - 1) / outer);
+        for (Side& S : full) max_outer = std::max(max_outer, (S.p + outer - 1) / outer);
         for (int ob = max_outer - 1; ob >= 0; --ob) {
             std::vector<GemmItem> w1, w2;
             long tw = 0;
             int kw = 1 << 30;
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 const int C0 = ob * outer;
                 if (C0 >= S.p) continue;
                 tw += tiles64(std::min(outer, S.p - C0), S.p - C0);
                 kw = std::min(kw, S.p - C0);
             }
             const int ks_w = split_for(tw, kw);
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 const int p = S.p, C0 = ob * outer;
                 if (C0 >= p) continue;
                 const int ho = p - C0, wb = std::min(outer, ho);
@@ -762,7 +795,7 @@ struct shampoo4_ctx_s {
             std::vector<SlabDesc> sds;
             int max_h = 0;
             double flops = 0, bytes = 0;
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 const int p = S.p;
                 float* Pm = wsf(S.Pm);
                 float* Qm = wsf(S.Qm);
@@ -863,7 +896,7 @@ struct shampoo4_ctx_s {
             std::vector<GemmItem> la1, la2, r1, r2, q1, q2;
             long tla = 0, trest = 0;
             int kmin = 1 << 30;
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 const int p = S.p, c0 = sidx * kPanel;
                 if (c0 >= p) continue;
                 const int nbw = std::min(kPanel, p - c0);
@@ -873,7 +906,7 @@ struct shampoo4_ctx_s {
                 kmin = std::min(kmin, p - c0);
             }
             const int ks_la = split_for(tla, kmin), ks_rest = split_for(trest, kmin);
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 const int p = S.p;
                 const int c0 = sidx * kPanel;
                 if (c0 >= p) continue;
@@ -956,7 +989,7 @@ struct shampoo4_ctx_s {
         // statistics: Lt = beta V diag(lam) V^T, then Lt += (1 - beta) G G^T (side R: G^T G)
         for (int var = 0; var < 2; ++var) {
             std::vector<GemmItem> xs, pw;
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 const int p = S.p;
                 const float* V = wsf(var == 0 ? S.Vs : S.Vr);
                 GemmDesc d = gd(V, p, V, p, wsf(S.Lt), p, p, p, p, beta);
@@ -973,6 +1006,7 @@ struct shampoo4_ctx_s {
             for (int b = 0; b < nb; ++b) {
                 for (int s = 0; s < 2; ++s) {
                     Side& S = sides[2 * b + s];
+                    if (S.diag) continue;
                     const int p = S.p, q = S.q;
                     GemmDesc d = gd(nullptr, 0, nullptr, 0, wsf(S.Lt), p, p, p, q, 1.f - beta, 1.f,
                                     wsf(S.Lt), p);
@@ -990,7 +1024,7 @@ struct shampoo4_ctx_s {
             bj_stats_fold.clear();
             stats_x_fold.clear();
             long gram_tiles = 0;   // 128 x 128 tiles of the Gram products
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 const long t = (S.p + 127) / 128;
                 gram_tiles += t * (t + 1) / 2;
             }
@@ -1002,7 +1036,7 @@ struct shampoo4_ctx_s {
                 Seq unused;
                 build_bjorck(false, unused, bj_stats_fold, &gs);
                 std::vector<GemmItem> xs;
-                for (auto& S : sides) {
+                for (Side& S : full) {
                     const int p = S.p;
                     const float* V = wsf(S.Vs);
                     GemmDesc d = gd(V, p, V, p, wsf(S.Lt), p, p, p, p, beta, 1.f, wsf(S.Lt), p);
@@ -1017,7 +1051,7 @@ struct shampoo4_ctx_s {
         {   // panel-wide blocks on one stream run as fused QR steps when every panel fits
             // the register-resident kernel (and the device's LDS)
             int pmax = 0;
-            for (auto& sh : shapes) pmax = std::max(pmax, std::max(sh.m, sh.n));
+            for (Side& S : full) pmax = std::max(pmax, S.p);
             fused = outer == kPanel && !lookahead && pmax <= PANEL_LDS_MAX_ROWS &&
                     qr_step_lds_bytes(pmax) <= lds_limit;
         }
@@ -1036,6 +1070,18 @@ struct shampoo4_ctx_s {
             for (auto& S : sides) {
                 const int p = S.p;
                 VecDesc v;
+                if (S.diag) {   // the diagonal statistic: its root scaling and initial state only
+                    std::memset(&v, 0, sizeof(v));
+                    v.a = stf(S.lam); v.out = stf(S.d); v.p = p;
+                    rt.push_back(v);
+                    trt.push_back((p + 255) / 256);
+                    InitDesc id;
+                    std::memset(&id, 0, sizeof(id));
+                    id.lam = stf(S.lam); id.d = stf(S.d); id.p = p; id.kind = INIT_DIAG;
+                    in.push_back(id);
+                    tin.push_back((p + 255) / 256);
+                    continue;
+                }
                 std::memset(&v, 0, sizeof(v));
                 v.out = wsf(S.Qm); v.aux = wsf(S.rdiag); v.ld = p; v.p = p;
                 qi.push_back(v);
@@ -1076,7 +1122,7 @@ struct shampoo4_ctx_s {
             ray_gemm = make_gemm(yg, FAM_GEMM_RAYLEIGH);
             int bm = 32, bn = 128;
             gemm_tile_dims(ray_gemm.empty() ? GEMM_32x128 : ray_gemm[0].cfg, &bm, &bn);
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 VecDesc v;
                 std::memset(&v, 0, sizeof(v));
                 v.a = wsf(S.Wg); v.out = stf(S.lam); v.ld = S.p; v.p = S.p; v.rows = (S.p + bm - 1) / bm;
@@ -1088,7 +1134,7 @@ struct shampoo4_ctx_s {
             if (fp32_state) {
                 std::vector<VecDesc> qv, rv;
                 std::vector<int> qt;
-                for (auto& S : sides) {
+                for (Side& S : full) {
                     const int64_t n = (int64_t)S.p * S.p;
                     qv.push_back(copyf_desc(wsf(S.Qm), stf(S.codes), n));
                     rv.push_back(copyf_desc(stf(S.codes), stf(S.rcodes), n));
@@ -1097,10 +1143,11 @@ struct shampoo4_ctx_s {
                 Launch Lq = make_items(K_COPYF, qv, qt);
                 Lq.fam = FAM_QUANT;
                 Lq.mode = 1;   // check finiteness
-                for (auto& S : sides) Lq.bytes += (double)S.p * S.p * 8.0;
+                for (Side& S : full) Lq.bytes += (double)S.p * S.p * 8.0;
                 quant = {Lq};
                 root_copy = {make_items(K_COPYF, rv, qt)};
-                for (auto& d : in) d.fp32 = 1;
+                for (auto& d : in)
+                    if (d.kind == INIT_4BIT) d.kind = INIT_FP32;
             } else {
                 Launch Lq = make_items(K_QUANT, qd, tq);
                 Lq.bytes = qbytes;
@@ -1116,6 +1163,29 @@ struct shampoo4_ctx_s {
                 const Side& L = sides[2 * b];
                 const Side& R = sides[2 * b + 1];
                 const int m = shapes[b].m, n = shapes[b].n;
+                if (L.diag && R.diag) continue;       // diag(d_L) G diag(d_R): diag_pre
+                if (R.diag) {                         // X1 = diag(d_L) V_L^T G; P = V_L X1 diag(d_R)
+                    GemmDesc d1 = gd(wsf(L.Vr), m, nullptr, 0, wsf(X1[b]), n, m, n, m);
+                    d1.b_io = b;
+                    d1.rscale = stf(L.d);
+                    p1.push_back({d1, true, false});
+                    GemmDesc d2 = gd(wsf(L.Vr), m, wsf(X1[b]), n, nullptr, 0, m, n, m);
+                    d2.d_io = b;
+                    d2.cscale = stf(R.d);
+                    p2.push_back({d2, false, false});
+                    continue;
+                }
+                if (L.diag) {                         // X1 = G V_R diag(d_R); P = diag(d_L) X1 V_R^T
+                    GemmDesc d1 = gd(nullptr, 0, wsf(R.Vr), n, wsf(X1[b]), n, m, n, n);
+                    d1.a_io = b;
+                    d1.cscale = stf(R.d);
+                    p1.push_back({d1, false, false});
+                    GemmDesc d2 = gd(wsf(X1[b]), n, wsf(R.Vr), n, nullptr, 0, m, n, n);
+                    d2.d_io = b;
+                    d2.rscale = stf(L.d);
+                    p2.push_back({d2, false, true});
+                    continue;
+                }
                 GemmDesc d1 = gd(wsf(L.Vr), m, nullptr, 0, wsf(X1[b]), n, m, n, m);
                 d1.b_io = b;
                 d1.rscale = stf(L.d);
@@ -1137,7 +1207,7 @@ struct shampoo4_ctx_s {
         // and precondition is X1 = Rt_L G, P = X1 Rt_R (same product, other association)
         {
             std::vector<GemmItem> rm, q1, q2;
-            for (auto& S : sides) {
+            for (Side& S : full) {
                 GemmDesc d = gd(wsf(S.Vr), S.p, wsf(S.Vr), S.p, wsf(S.Rt), S.p, S.p, S.p, S.p);
                 d.kscale = stf(S.d);
                 d.flags |= GEMM_F_SYM;                   // V diag(d) V^T
@@ -1147,6 +1217,23 @@ struct shampoo4_ctx_s {
                 const Side& L = sides[2 * b];
                 const Side& R = sides[2 * b + 1];
                 const int m = shapes[b].m, n = shapes[b].n;
+                if (L.diag && R.diag) continue;       // diag_pre
+                if (R.diag) {                         // P = Rt_L G diag(d_R)
+                    GemmDesc d1 = gd(wsf(L.Rt), m, nullptr, 0, nullptr, 0, m, n, m);
+                    d1.b_io = b;
+                    d1.d_io = b;
+                    d1.cscale = stf(R.d);
+                    q1.push_back({d1, false, false});
+                    continue;
+                }
+                if (L.diag) {                         // P = diag(d_L) G Rt_R
+                    GemmDesc d1 = gd(nullptr, 0, wsf(R.Rt), n, nullptr, 0, m, n, n);
+                    d1.a_io = b;
+                    d1.d_io = b;
+                    d1.rscale = stf(L.d);
+                    q1.push_back({d1, false, false});
+                    continue;
+                }
                 GemmDesc d1 = gd(wsf(L.Rt), m, nullptr, 0, wsf(X1[b]), n, m, n, m);
                 d1.b_io = b;
                 q1.push_back({d1, false, false});
@@ -1164,6 +1251,69 @@ struct shampoo4_ctx_s {
             for (auto& sq : pre_cached)
                 for (auto& L : sq)
                     if (L.cfg == GEMM_64x64_K2) L.cfg = GEMM_64x64;
+        }
+        build_diag();
+    }
+
+    // Diagonal sides: the partial sums of G^2 and their EMA into the statistic (update),
+    // and P = diag(d_L) G diag(d_R) for blocks whose two sides are diagonal (precondition).
+    void build_diag() {
+        diag_stats.clear();
+        diag_pre.clear();
+        std::vector<DiagDesc> parts, scale;
+        std::vector<int> tparts, tscale;
+        std::vector<VecDesc> ema;
+        std::vector<int> tema;
+        double pbytes = 0, ebytes = 0, sbytes = 0;
+        for (int b = 0; b < nb; ++b) {
+            const Side& L = sides[2 * b];
+            const Side& R = sides[2 * b + 1];
+            if (!L.diag && !R.diag) continue;
+            const int m = shapes[b].m, n = shapes[b].n;
+            const int tm = (m + DIAG_TR - 1) / DIAG_TR, tn = (n + DIAG_TC - 1) / DIAG_TC;
+            DiagDesc d;
+            std::memset(&d, 0, sizeof(d));
+            d.rowpart = L.diag ? wsf(RP[b]) : nullptr;
+            d.colpart = R.diag ? wsf(CP[b]) : nullptr;
+            d.d_l = stf(L.d);
+            d.d_r = stf(R.d);
+            d.m = m; d.n = n; d.blk = b; d.tiles_n = tn;
+            parts.push_back(d);
+            tparts.push_back(tm * tn);
+            pbytes += 4.0 * m * n + (L.diag ? 4.0 * tn * m : 0) + (R.diag ? 4.0 * tm * n : 0);
+            for (int s = 0; s < 2; ++s) {
+                const Side& S = sides[2 * b + s];
+                if (!S.diag) continue;
+                VecDesc v;
+                std::memset(&v, 0, sizeof(v));
+                v.a = wsf(s == 0 ? RP[b] : CP[b]);
+                v.out = stf(S.lam);
+                v.ld = S.p;
+                v.p = S.p;
+                v.rows = s == 0 ? tn : tm;
+                ema.push_back(v);
+                tema.push_back((S.p + 255) / 256);
+                ebytes += 4.0 * S.p * (v.rows + 2);
+            }
+            if (L.diag && R.diag) {
+                scale.push_back(d);
+                tscale.push_back((m + diag_scale_rows(n) - 1) / diag_scale_rows(n));
+                sbytes += 8.0 * m * n + 4.0 * (m + n);
+            }
+        }
+        if (!parts.empty()) {
+            Launch a = make_items(K_DIAG_PARTIALS, parts, tparts);
+            a.bytes = pbytes;
+            a.uses_io = true;
+            Launch e = make_items(K_DIAG_EMA, ema, tema);
+            e.bytes = ebytes;
+            diag_stats = {a, e};
+        }
+        if (!scale.empty()) {
+            Launch c = make_items(K_DIAG_SCALE, scale, tscale);
+            c.bytes = sbytes;
+            c.uses_io = true;
+            diag_pre = {c};
         }
     }
 
@@ -1286,6 +1436,18 @@ struct shampoo4_ctx_s {
                 e = launch_graft_apply(reinterpret_cast<const GraftDesc*>(base + L.desc_off), prefix, L.ndesc,
                                        L.ntiles, io, wsp<GraftIo>(gio_off), graft_prm, s);
                 break;
+            case K_DIAG_PARTIALS:
+                e = launch_diag_partials(reinterpret_cast<const DiagDesc*>(base + L.desc_off), prefix, L.ndesc,
+                                         L.ntiles, io, s);
+                break;
+            case K_DIAG_EMA:
+                e = launch_diag_ema(reinterpret_cast<const VecDesc*>(base + L.desc_off), prefix, L.ndesc,
+                                    L.ntiles, cfg.beta, flag, s);
+                break;
+            case K_DIAG_SCALE:
+                e = launch_diag_scale(reinterpret_cast<const DiagDesc*>(base + L.desc_off), prefix, L.ndesc,
+                                      L.ntiles, io, s);
+                break;
             case K_RECORD:
             case K_WAIT:
                 break;
@@ -1357,9 +1519,9 @@ struct shampoo4_ctx_s {
     // shares the GPU with the latency-bound panel chain rather than the products)
     hipError_t stats_body(bool reuse, hipStream_t s, const std::function<hipError_t()>* at_qr = nullptr) {
         const int var = reuse ? 1 : 0;
-        hipError_t e = hipSuccess;
+        hipError_t e = run(diag_stats, s);
         const bool fold = !reuse && !bj_stats_fold.empty();
-        if (!reuse) {
+        if (!reuse && e == hipSuccess) {
             e = run(deq_stats, s);
             for (auto& it : (fold ? bj_stats_fold : bj_stats))
                 if (e == hipSuccess) e = run(it, s);
@@ -1476,11 +1638,16 @@ shampoo4_status validate_cfg(const shampoo4_config* cfg) {
     return SHAMPOO4_OK;
 }
 
-shampoo4_status validate_shapes(int32_t nblocks, const shampoo4_shape* shapes) {
+shampoo4_status validate_shapes(int32_t nblocks, const shampoo4_shape* shapes, const uint8_t* diag_sides) {
     if (nblocks < 1 || nblocks > (1 << 20) || !shapes) return SHAMPOO4_EINVAL;
-    for (int b = 0; b < nblocks; ++b)
-        if (shapes[b].m < 1 || shapes[b].n < 1 || shapes[b].m > kMaxDim || shapes[b].n > kMaxDim)
+    for (int b = 0; b < nblocks; ++b) {
+        const uint8_t dg = diag_sides ? diag_sides[b] : 0;
+        if (dg & ~(SHAMPOO4_DIAG_L | SHAMPOO4_DIAG_R)) return SHAMPOO4_EINVAL;
+        const int lim_m = (dg & SHAMPOO4_DIAG_L) ? kMaxDiagDim : kMaxDim;
+        const int lim_n = (dg & SHAMPOO4_DIAG_R) ? kMaxDiagDim : kMaxDim;
+        if (shapes[b].m < 1 || shapes[b].n < 1 || shapes[b].m > lim_m || shapes[b].n > lim_n)
             return SHAMPOO4_ESHAPE;
+    }
     return SHAMPOO4_OK;
 }
 
@@ -1500,11 +1667,13 @@ shampoo4_status validate_io(const shampoo4_ctx_s* c, const shampoo4_io* io, bool
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 std::unique_ptr<shampoo4_ctx_s> make_plan(const shampoo4_config* cfg, int32_t nblocks,
-                                          const shampoo4_shape* shapes) {
+                                          const shampoo4_shape* shapes, const uint8_t* diag_sides) {
     auto c = std::make_unique<shampoo4_ctx_s>();
     c->cfg = *cfg;
     c->nb = nblocks;
     c->shapes.assign(shapes, shapes + nblocks);
+    c->diag_bits.assign(nblocks, 0);
+    if (diag_sides) c->diag_bits.assign(diag_sides, diag_sides + nblocks);
     c->lds_limit = 160 * 1024;
     c->layout();
     return c;
@@ -1531,11 +1700,16 @@ const char* shampoo4_strerror(shampoo4_status s) {
 
 shampoo4_status shampoo4_plan(const shampoo4_config* cfg, int32_t nblocks, const shampoo4_shape* shapes,
                               size_t* state_bytes, size_t* workspace_bytes) {
+    return shampoo4_plan_ex(cfg, nblocks, shapes, nullptr, state_bytes, workspace_bytes);
+}
+
+shampoo4_status shampoo4_plan_ex(const shampoo4_config* cfg, int32_t nblocks, const shampoo4_shape* shapes,
+                                 const uint8_t* diag_sides, size_t* state_bytes, size_t* workspace_bytes) {
     shampoo4_status st = validate_cfg(cfg);
     if (st != SHAMPOO4_OK) return st;
-    if ((st = validate_shapes(nblocks, shapes)) != SHAMPOO4_OK) return st;
+    if ((st = validate_shapes(nblocks, shapes, diag_sides)) != SHAMPOO4_OK) return st;
     if (!state_bytes || !workspace_bytes) return SHAMPOO4_EINVAL;
-    auto c = make_plan(cfg, nblocks, shapes);
+    auto c = make_plan(cfg, nblocks, shapes, diag_sides);
     c->build();   // null bases: only the sizes matter
     c->build_graft();
     *state_bytes = c->st_bytes;
@@ -1547,13 +1721,20 @@ shampoo4_status shampoo4_plan(const shampoo4_config* cfg, int32_t nblocks, const
 shampoo4_status shampoo4_init(const shampoo4_config* cfg, int32_t nblocks, const shampoo4_shape* shapes,
                               void* state, size_t state_bytes, void* workspace, size_t workspace_bytes,
                               void* stream, shampoo4_ctx* out) {
+    return shampoo4_init_ex(cfg, nblocks, shapes, nullptr, state, state_bytes, workspace, workspace_bytes, stream,
+                            out);
+}
+
+shampoo4_status shampoo4_init_ex(const shampoo4_config* cfg, int32_t nblocks, const shampoo4_shape* shapes,
+                                 const uint8_t* diag_sides, void* state, size_t state_bytes, void* workspace,
+                                 size_t workspace_bytes, void* stream, shampoo4_ctx* out) {
     shampoo4_status st = validate_cfg(cfg);
     if (st != SHAMPOO4_OK) return st;
-    if ((st = validate_shapes(nblocks, shapes)) != SHAMPOO4_OK) return st;
+    if ((st = validate_shapes(nblocks, shapes, diag_sides)) != SHAMPOO4_OK) return st;
     if (!state || !workspace || !out) return SHAMPOO4_EINVAL;
     if ((reinterpret_cast<uintptr_t>(state) % kAlign) || (reinterpret_cast<uintptr_t>(workspace) % kAlign))
         return SHAMPOO4_EALIGN;
-    auto c = make_plan(cfg, nblocks, shapes);
+    auto c = make_plan(cfg, nblocks, shapes, diag_sides);
     {   // panel register classes are limited by what one workgroup may allocate in LDS
         int dev = 0, lds = 0;
         if (hipGetDevice(&dev) != hipSuccess) return SHAMPOO4_EHIP;
@@ -1639,6 +1820,7 @@ shampoo4_status shampoo4_precondition(shampoo4_ctx c, const shampoo4_io* io, voi
     } else {
         for (int i = 0; i < 4 && e == hipSuccess; ++i) e = c->run(c->pre[i], s);
     }
+    if (e == hipSuccess) e = c->run(c->diag_pre, s);
     return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
 
@@ -1669,6 +1851,7 @@ shampoo4_status shampoo4_step(shampoo4_ctx c, const shampoo4_io* io, int32_t ref
         hipError_t e = hipEventRecord(c->pre_fork, s);
         if (e == hipSuccess) e = hipStreamWaitEvent(c->pre_strm, c->pre_fork, 0);
         for (int i = 0; i < 2 && e == hipSuccess; ++i) e = c->run(c->pre_side[i], c->pre_strm);
+        if (e == hipSuccess) e = c->run(c->diag_pre, c->pre_strm);
         if (e == hipSuccess) e = hipEventRecord(c->pre_join, c->pre_strm);
         return e;
     };
@@ -1744,6 +1927,7 @@ shampoo4_status shampoo4_layout(shampoo4_ctx c, int32_t block, int32_t side, sha
     const Side& S = c->sides[2 * block + side];
     const size_t p = S.p;
     const size_t mat = p * p * 4;
+    if (S.diag && which >= SHAMPOO4_BUF_V) return SHAMPOO4_EINVAL;   // a diagonal side has no matrices
     switch (which) {
         case SHAMPOO4_BUF_CODES: *offset = S.codes; *bytes = c->fp32_state ? (size_t)p * p * 4 : S.nqb * 32; break;
         case SHAMPOO4_BUF_SCALES: *offset = S.scales; *bytes = c->fp32_state ? 0 : S.nqb * 4; break;

@@ -73,26 +73,41 @@ class Shampoo4Config:
         return L.Config(self.beta, self.eps, self.qblock, self.bjorck_iters, self.power_iters, flags)
 
 
-def plan(shapes, config: Shampoo4Config):
+def _diag_bits(diagonal, nblocks: int):
+    """Per-block bytes of diagonal sides from pairs (side L diagonal, side R diagonal)."""
+    if diagonal is None:
+        return None
+    if len(diagonal) != nblocks:
+        raise ValueError(f"diagonal needs one (L, R) pair per block ({nblocks})")
+    bits = [(L.DIAG_L if dl else 0) | (L.DIAG_R if dr else 0) for dl, dr in diagonal]
+    return (ctypes.c_uint8 * nblocks)(*bits)
+
+
+def plan(shapes, config: Shampoo4Config, diagonal=None):
     shapes = [(int(m), int(n)) for (m, n) in shapes]
     arr = (L.Shape * len(shapes))(*[L.Shape(m, n) for (m, n) in shapes])
     sb, wb = ctypes.c_size_t(0), ctypes.c_size_t(0)
     cfg = config.c()
-    L.check(L.lib().shampoo4_plan(ctypes.byref(cfg), len(shapes), arr, ctypes.byref(sb), ctypes.byref(wb)),
-            "shampoo4_plan")
+    L.check(L.lib().shampoo4_plan_ex(ctypes.byref(cfg), len(shapes), arr, _diag_bits(diagonal, len(shapes)),
+                                     ctypes.byref(sb), ctypes.byref(wb)), "shampoo4_plan_ex")
     return sb.value, wb.value
 
 
 class Shampoo4Blocks:
-    """4-bit Shampoo state for a list of blocks G_b:[m_b, n_b] on one GPU."""
+    """4-bit Shampoo state for a list of blocks G_b:[m_b, n_b] on one GPU.
+
+    `diagonal`: optional per-block pairs (side L diagonal, side R diagonal) for the
+    one-sided fallback of a side over the size threshold (see blocking.plan_blocks)."""
 
     def __init__(self, shapes, config: Shampoo4Config | None = None, device="cuda",
-                 state: torch.Tensor | None = None):
+                 state: torch.Tensor | None = None, diagonal=None):
         self.config = config or Shampoo4Config()
         self.shapes = [(int(m), int(n)) for (m, n) in shapes]
         self.nblocks = len(self.shapes)
         self.device = torch.device(device)
-        sb, wb = plan(self.shapes, self.config)
+        self.diagonal = [(bool(a), bool(b)) for a, b in diagonal] if diagonal is not None else None
+        self._diag_arr = _diag_bits(self.diagonal, self.nblocks)
+        sb, wb = plan(self.shapes, self.config, self.diagonal)
         keep = state is not None
         if keep:
             _require_gpu_tensor(state, torch.uint8, "state")
@@ -105,9 +120,9 @@ class Shampoo4Blocks:
         self._shape_arr = (L.Shape * self.nblocks)(*[L.Shape(m, n) for (m, n) in self.shapes])
         self._ctx = ctypes.c_void_p(0)
         cfg = self.config.c(keep_state=keep)
-        L.check(L.lib().shampoo4_init(ctypes.byref(cfg), self.nblocks, self._shape_arr,
-                                      _ptr(self.state), sb, _ptr(self.workspace), wb,
-                                      _stream_ptr(), ctypes.byref(self._ctx)), "shampoo4_init")
+        L.check(L.lib().shampoo4_init_ex(ctypes.byref(cfg), self.nblocks, self._shape_arr, self._diag_arr,
+                                         _ptr(self.state), sb, _ptr(self.workspace), wb,
+                                         _stream_ptr(), ctypes.byref(self._ctx)), "shampoo4_init_ex")
 
     def close(self):
         if self._ctx and self._ctx.value:
@@ -239,7 +254,7 @@ class Shampoo4Blocks:
         L.check(L.lib().shampoo4_timing(self._ctx, 1 if enable else 0), "shampoo4_timing")
 
     def timing_report(self) -> dict:
-        n = 16
+        n = 32
         cnt = ctypes.c_int32(n)
         names = (ctypes.c_char_p * n)()
         launches = (ctypes.c_int64 * n)()

@@ -61,7 +61,8 @@ typedef struct shampoo4_ctx_s* shampoo4_ctx;
 typedef enum {
     SHAMPOO4_OK = 0,
     SHAMPOO4_EINVAL = 1,      /* null pointer, bad config value, bad index */
-    SHAMPOO4_ESHAPE = 2,      /* a block dimension outside [1, 8192], or ld < cols */
+    SHAMPOO4_ESHAPE = 2,      /* a block dimension outside [1, 8192] (a diagonal side: [1, 65536]),
+                                 or ld < cols */
     SHAMPOO4_EALIGN = 3,      /* a state/workspace buffer not 256-byte aligned */
     SHAMPOO4_ESMALLBUF = 4,   /* buffer smaller than shampoo4_plan reported */
     SHAMPOO4_EHIP = 5,        /* a HIP runtime call or kernel launch failed */
@@ -187,6 +188,33 @@ SHAMPOO4_API shampoo4_status shampoo4_init(const shampoo4_config* cfg, int32_t n
                               void* state, size_t state_bytes,
                               void* workspace, size_t workspace_bytes,
                               void* stream, shampoo4_ctx* out);
+
+/* Diagonal fallback ("Shampoo -- Second-Order Optimizer", "Blocked and distributed
+ * variants": if one dimension of a block exceeds a threshold, that side's factor is
+ * dropped and diagonal AdaGrad is used along it).  A side marked diagonal keeps no
+ * eigenvector matrix: its state is the diagonal of its factor as the same exponential
+ * moving average, lam_i <- beta lam_i + (1 - beta) sum_j Gs[i][j]^2 (Gs = G for side L,
+ * G^T for side R), updated by update_stats, with d = (lam + eps)^(-1/4) at refresh_root
+ * (the same -1/4 exponent as a full side, so the step stays homogeneous of degree 0);
+ * precondition uses diag(d) in place of that side's root matrix.  The caller picks the
+ * sides (the threshold is the caller's: see blocking.py).  A diagonal side may have an
+ * order up to 65536 (a side with eigenvectors: 8192); its state holds no codes and
+ * scales (those buffers have size 0 in shampoo4_layout) and it has no workspace
+ * matrices (shampoo4_layout of BUF_V .. BUF_ROOT_MAT returns EINVAL). */
+#define SHAMPOO4_DIAG_L 1u
+#define SHAMPOO4_DIAG_R 2u
+
+/* shampoo4_plan / shampoo4_init with per-block diagonal sides: diag_sides is a host array
+ * of nblocks bytes, each SHAMPOO4_DIAG_L | SHAMPOO4_DIAG_R or 0 (NULL: no diagonal side,
+ * the plain calls).  EINVAL: other bits; ESHAPE: a dimension above its side's limit. */
+SHAMPOO4_API shampoo4_status shampoo4_plan_ex(const shampoo4_config* cfg, int32_t nblocks,
+                                              const shampoo4_shape* shapes, const uint8_t* diag_sides,
+                                              size_t* state_bytes, size_t* workspace_bytes);
+SHAMPOO4_API shampoo4_status shampoo4_init_ex(const shampoo4_config* cfg, int32_t nblocks,
+                                              const shampoo4_shape* shapes, const uint8_t* diag_sides,
+                                              void* state, size_t state_bytes,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* stream, shampoo4_ctx* out);
 
 /* One statistics update of every block: io is a host array of nblocks entries
  * (only G/ldg are read).  Per side: the stored eigenvectors are dequantized and
@@ -345,7 +373,8 @@ SHAMPOO4_API shampoo4_status shampoo4_inverse_root(int32_t count, const int32_t*
  * "gemm_qr", "gemm_qr_trail", "gemm_qr_q", "gemm_rayleigh", "gemm_precond" (the matrix
  * products by the stage they serve; the QR's are split into the products inside an outer
  * reflector block, the block's products on the trailing columns and the accumulation of
- * Q), "dequant", "quant", "qr_panel", "rayleigh", "elementwise", "graft".  Host arrays of
+ * Q), "dequant", "quant", "qr_panel", "rayleigh", "elementwise", "graft", "diag" (the
+ * diagonal sides' statistic and the both-diagonal precondition).  Host arrays of
  * length *count (in: capacity, out: used). */
 SHAMPOO4_API shampoo4_status shampoo4_timing(shampoo4_ctx ctx, int32_t enable);
 SHAMPOO4_API shampoo4_status shampoo4_timing_report(shampoo4_ctx ctx, int32_t* count, const char** names,

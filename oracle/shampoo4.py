@@ -45,6 +45,17 @@ precondition(G)
 Initial state: U = I (exact in the codebook), lam = 0, root = (I, d = 1), so
 P_out = G until the first root refresh.
 
+Diagonal fallback ("Blocked and distributed variants": if one dimension exceeds a
+threshold, that side's factor is dropped and diagonal AdaGrad is used along it): a side
+marked diagonal keeps no eigenvector matrix, only the diagonal of its factor as the same
+exponential moving average,
+    lam_i <- beta * lam_i + (1 - beta) * sum_j Gs[i, j]^2      (Gs: G for L, G^T for R)
+and at a refresh d_i = (lam_i + eps)^(-1/4) like the eigenvalues of a full side; the
+direction uses diag(d) in place of that side's root matrix.  Reading: the diagonal is
+what diagonal AdaGrad accumulates along that dimension, and keeping the -1/4 exponent
+keeps the step homogeneous of degree 0 and equal to the two-sided step whenever the
+dropped factor is itself diagonal.
+
 Parity status: steps 1-7 are pinned individually by the oracle tests
 (codec round trips, Bjorck fixed points and convergence to the polar factor,
 eigen refresh on exact eigenvectors and convergence to numpy.linalg.eigh,
@@ -137,6 +148,14 @@ def root_scaling(lam32, eps: float) -> np.ndarray:
     return ((lam + e) ** -0.25).astype(np.float32)
 
 
+def diagonal_statistics(lam, Gs, beta: float) -> np.ndarray:
+    """Diagonal fallback statistic: beta * lam + (1 - beta) * (row sums of Gs^2), the
+    diagonal of the EMA factor beta * L + (1 - beta) * Gs Gs^T (float64)."""
+    b = np.float64(np.float32(beta))
+    Gs = np.asarray(Gs, dtype=np.float64)
+    return b * np.asarray(lam, dtype=np.float64) + (1.0 - b) * np.sum(Gs * Gs, axis=1)
+
+
 def root_matrix(V, d) -> np.ndarray:
     """V diag(d) V^T (float64)."""
     V = np.asarray(V, dtype=np.float64)
@@ -161,16 +180,24 @@ class SideState:
     root_codes: np.ndarray
     root_scales: np.ndarray
     d: np.ndarray
+    diagonal: bool = False      # diagonal fallback: no eigenvectors, lam is the diagonal
     # diagnostics of the last update (float64), for teacher-forced checks
     last_Lt: np.ndarray | None = field(default=None, repr=False)
     last_Q: np.ndarray | None = field(default=None, repr=False)
 
     def copy(self) -> "SideState":
         return SideState(self.p, self.codes.copy(), self.scales.copy(), self.lam.copy(),
-                         self.root_codes.copy(), self.root_scales.copy(), self.d.copy())
+                         self.root_codes.copy(), self.root_scales.copy(), self.d.copy(),
+                         self.diagonal)
 
 
-def initial_side(p: int, qblock: int = 64, codebook: str = codec.LINEAR_SQUARE) -> SideState:
+def initial_side(p: int, qblock: int = 64, codebook: str = codec.LINEAR_SQUARE,
+                 diagonal: bool = False) -> SideState:
+    if diagonal:
+        empty_c, empty_s = np.zeros(0, np.uint8), np.zeros(0, np.float32)
+        return SideState(p=p, codes=empty_c, scales=empty_s, lam=np.zeros(p, np.float32),
+                         root_codes=empty_c.copy(), root_scales=empty_s.copy(),
+                         d=np.ones(p, np.float32), diagonal=True)
     codes, scales = codec.quantize_matrix(np.eye(p, dtype=np.float32), qblock, codebook)
     return SideState(p=p, codes=codes, scales=scales,
                      lam=np.zeros(p, np.float32),
@@ -182,6 +209,10 @@ def update_side(st: SideState, Gs, beta: float, bjorck_iters: int,
                 power_iters: int = 1, qblock: int = 64,
                 codebook: str = codec.LINEAR_SQUARE) -> SideState:
     """Steps 1-5 for one side.  Returns the new state (root unchanged)."""
+    if st.diagonal:
+        out = st.copy()
+        out.lam = diagonal_statistics(st.lam, Gs, beta).astype(np.float32)
+        return out
     V = rectified_eigenvectors(st.codes, st.scales, st.p, bjorck_iters, qblock, codebook)
     Lt = statistics(V, st.lam, Gs, beta)
     Q, lam = eigen_refresh(Lt, V, power_iters)
@@ -205,6 +236,9 @@ def refresh_side(st: SideState, eps: float) -> SideState:
 
 def root_eigenvectors(st: SideState, bjorck_iters: int, qblock: int = 64,
                       codebook: str = codec.LINEAR_SQUARE) -> np.ndarray:
+    """Rectified root eigenvectors (the identity for a diagonal side, whose root is diag(d))."""
+    if st.diagonal:
+        return np.eye(st.p)
     return rectified_eigenvectors(st.root_codes, st.root_scales, st.p, bjorck_iters, qblock, codebook)
 
 
@@ -212,7 +246,9 @@ class Shampoo4Oracle:
     """The whole schedule over a list of blocks (one SideState per block and side)."""
 
     def __init__(self, shapes, beta: float = 0.95, eps: float = 1e-6, qblock: int = 64,
-                 bjorck_iters: int = 1, power_iters: int = 1, codebook: str = codec.LINEAR_SQUARE):
+                 bjorck_iters: int = 1, power_iters: int = 1, codebook: str = codec.LINEAR_SQUARE,
+                 diagonal=None):
+        """`diagonal`: per block a pair (side L diagonal, side R diagonal); default none."""
         self.shapes = [tuple(int(v) for v in s) for s in shapes]
         self.beta = beta
         self.eps = eps
@@ -220,8 +256,10 @@ class Shampoo4Oracle:
         self.bjorck_iters = bjorck_iters
         self.power_iters = power_iters
         self.codebook = codebook
-        self.sides = [[initial_side(m, qblock, codebook), initial_side(n, qblock, codebook)]
-                      for (m, n) in self.shapes]
+        diagonal = diagonal or [(False, False)] * len(self.shapes)
+        self.diagonal = [(bool(a), bool(b)) for a, b in diagonal]
+        self.sides = [[initial_side(m, qblock, codebook, dl), initial_side(n, qblock, codebook, dr)]
+                      for (m, n), (dl, dr) in zip(self.shapes, self.diagonal)]
 
     def update_stats(self, Gs):
         for b, G in enumerate(Gs):
@@ -239,9 +277,17 @@ class Shampoo4Oracle:
         out = []
         for b, G in enumerate(Gs):
             sl, sr = self.sides[b]
-            VL = root_eigenvectors(sl, self.bjorck_iters, self.qblock, self.codebook)
-            VR = root_eigenvectors(sr, self.bjorck_iters, self.qblock, self.codebook)
-            out.append(precondition_block(VL, sl.d, VR, sr.d, G).astype(np.float32))
+            X = np.asarray(G, dtype=np.float64)
+            # L^(-1/4) G R^(-1/4); a diagonal side's root is diag(d)
+            if sl.diagonal:
+                X = sl.d.astype(np.float64)[:, None] * X
+            else:
+                X = root_matrix(root_eigenvectors(sl, self.bjorck_iters, self.qblock, self.codebook), sl.d) @ X
+            if sr.diagonal:
+                X = X * sr.d.astype(np.float64)[None, :]
+            else:
+                X = X @ root_matrix(root_eigenvectors(sr, self.bjorck_iters, self.qblock, self.codebook), sr.d)
+            out.append(X.astype(np.float32))
         return out
 
     def step(self, Gs, t: int, root_interval: int = 1):

@@ -42,12 +42,23 @@ def test_conv_kernel_viewed_as_out_by_in_k_k():
 
 
 def test_fallbacks_to_diagonal():
-    plans = bk.plan_blocks([(768,), (), (32768, 4096), (10, 20)], block=None, max_dim=8192)
-    assert [p.kind for p in plans] == ["diagonal", "diagonal", "diagonal", "blocks"]
-    assert bk.diagonal_indices(plans) == [0, 1, 2]
+    plans = bk.plan_blocks([(768,), (), (32768, 4096), (10, 20), (9000, 9000), (100000, 64)],
+                           block=None, max_dim=8192)
+    assert [p.kind for p in plans] == ["diagonal", "diagonal", "blocks", "blocks", "blocks", "diagonal"]
+    # 1-D parameters, and a side beyond the library's diagonal-side limit, stay on the
+    # caller's diagonal method
+    assert bk.diagonal_indices(plans) == [0, 1, 5]
+    # one side over the threshold drops its factor (one-sided), both: diagonal both sides
+    assert bk.block_shapes(plans) == [(32768, 4096), (10, 20), (9000, 9000)]
+    assert bk.block_diagonal_sides(plans) == [(True, False), (False, False), (True, True)]
     # with blocking on, a large dimension is tiled instead
     p = bk.plan_blocks([(32768, 4096)], block=1024)[0]
     assert p.kind == "blocks" and len(p.tiles) == 32 * 4
+    assert set(p.tile_diagonal) == {(False, False)}
+    # tiles larger than the threshold: the remainder tile keeps both factors
+    p = bk.plan_blocks([(20000, 100)], block=16384, max_dim=8192)[0]
+    assert p.tiles == [(0, 0, 16384, 100), (16384, 0, 3616, 100)]
+    assert p.tile_diagonal == [(True, False), (False, False)]
 
 
 def test_views_share_storage():

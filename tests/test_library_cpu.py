@@ -135,3 +135,37 @@ def test_inverse_root_workspace_sizes():
     bad = (i32 * 1)(0)
     assert lib.shampoo4_inverse_root_workspace_bytes(1, bad) == 0
     assert lib.shampoo4_inverse_root(1, bad, None, None, 0.0, 1, None, None, None, 0, None) == L.EINVAL
+
+
+def test_shape_limits_by_side_kind():
+    """A diagonal side may reach 65536, a side with eigenvectors 8192; unknown side bits
+    are rejected (host-only planning)."""
+    _lib()
+    from bit_quantized_shampoo_amd import Shampoo4Config
+    from bit_quantized_shampoo_amd.shampoo4 import plan
+    sb, wb = plan([(16, 65536)], Shampoo4Config(), diagonal=[(False, True)])
+    assert sb > 0 and wb > 0
+    with pytest.raises(L.Shampoo4Error) as e:
+        plan([(16, 65537)], Shampoo4Config(), diagonal=[(False, True)])
+    assert e.value.status == L.ESHAPE
+    with pytest.raises(L.Shampoo4Error) as e:
+        plan([(16, 9000)], Shampoo4Config(), diagonal=[(True, False)])
+    assert e.value.status == L.ESHAPE
+    cfg = L.Config(0.95, 1e-6, 64, 1, 1, 0)
+    arr = (L.Shape * 1)(L.Shape(8, 8))
+    bad = (ctypes.c_uint8 * 1)(4)
+    s0, s1 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert L.lib().shampoo4_plan_ex(ctypes.byref(cfg), 1, arr, bad, ctypes.byref(s0), ctypes.byref(s1)) == L.EINVAL
+
+
+def test_diagonal_sides_hold_no_eigenvectors():
+    """A diagonal side's state is its statistic and d only, and its workspace holds no p x p
+    matrices: the both-diagonal plan of a block is far smaller than the full one."""
+    _lib()
+    from bit_quantized_shampoo_amd import Shampoo4Config
+    from bit_quantized_shampoo_amd.shampoo4 import plan
+    sb_full, wb_full = plan([(512, 512)], Shampoo4Config())
+    sb_diag, wb_diag = plan([(512, 512)], Shampoo4Config(), diagonal=[(True, True)])
+    # per side: four empty 256-byte-aligned pieces (codes, scales, root codes, root scales), lam, d
+    assert sb_diag == 2 * (4 * 256 + 2 * 512 * 4)
+    assert wb_diag < wb_full // 4
