@@ -35,9 +35,11 @@ EXPORTED = [
     "shampoo4_codebook_ex", "shampoo4_gemm_workspace_bytes",
     "shampoo4_gemm_batched", "shampoo4_timing", "shampoo4_timing_report", "shampoo4_graft",
     "shampoo4_inverse_root_workspace_bytes", "shampoo4_inverse_root", "shampoo4_plan_ex", "shampoo4_init_ex",
+    "shampoo4_gemm_batched_static",
 ]
 
 GRAFT_SGD, GRAFT_ADAM = 0, 1
+GEMM_STATIC_MAX = 2048
 
 
 class Config(ctypes.Structure):
@@ -115,6 +117,10 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(vp), ctypes.POINTER(i64), f32, ctypes.POINTER(vp),
                                        ctypes.POINTER(i64), ctypes.POINTER(vp), ctypes.POINTER(i64),
                                        vp, sz, vp]),
+        "shampoo4_gemm_batched_static": (st, [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                              ctypes.POINTER(i32), f32, ctypes.POINTER(vp), ctypes.POINTER(i64),
+                                              ctypes.POINTER(vp), ctypes.POINTER(i64), f32, ctypes.POINTER(vp),
+                                              ctypes.POINTER(i64), ctypes.POINTER(vp), ctypes.POINTER(i64), vp]),
         "shampoo4_timing": (st, [vp, i32]),
         "shampoo4_inverse_root_workspace_bytes": (sz, [i32, ctypes.POINTER(i32)]),
         "shampoo4_inverse_root": (st, [i32, ctypes.POINTER(i32), ctypes.POINTER(vp), ctypes.POINTER(i64), f32, i32,

@@ -22,6 +22,11 @@ void gemm_tile_dims(int cfg, int* bm, int* bn);
 // slab: some descriptor sums split-K slabs while loading (anslab or bnslab > 1).
 hipError_t launch_gemm(int cfg, int mode, bool vec, bool slab, const GemmDesc* descs, const int* prefix,
                        int ndesc, int ntiles, const IoEntry* io, hipStream_t stream);
+// The allocation-free batched GEMM keeps its descriptor table and tile prefix (one 256-byte
+// aligned piece each) in a static device array of this size per GPU.
+constexpr size_t GEMM_STATIC_SCRATCH_BYTES = 384 * 1024;
+// The device address of the current device's array (looked up on its first use).
+hipError_t gemm_static_scratch(void** out);
 // Host check of the 16-byte-load conditions of one descriptor, operands given through
 // the io table excepted (their pointers and pitches are checked per call).
 bool gemm_vec_ok(const GemmDesc& d);

@@ -2000,20 +2000,23 @@ size_t shampoo4_gemm_workspace_bytes(int32_t count) {
     return align_up((size_t)std::max(count, 0) * sizeof(GemmDesc)) + align_up(((size_t)std::max(count, 0) + 1) * 4);
 }
 
-shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t transB, const int32_t* M,
-                                      const int32_t* N, const int32_t* K, float alpha, const float* const* A,
-                                      const int64_t* lda, const float* const* B, const int64_t* ldb, float beta,
-                                      const float* const* C, const int64_t* ldc, float* const* D,
-                                      const int64_t* ldd, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates a batched product and plans its single launch: `tmp.blob` then holds the
+// descriptor table and tile prefix (offsets in `L` relative to the blob's start); `L.ntiles`
+// is 0 when there is nothing to compute.
+shampoo4_status plan_gemm_batched(int32_t count, int32_t transA, int32_t transB, const int32_t* M,
+                                  const int32_t* N, const int32_t* K, float alpha, const float* const* A,
+                                  const int64_t* lda, const float* const* B, const int64_t* ldb, float beta,
+                                  const float* const* C, const int64_t* ldc, float* const* D, const int64_t* ldd,
+                                  shampoo4_ctx_s& tmp, Launch& L) {
+    L = Launch{};
     if (count < 0) return SHAMPOO4_EINVAL;
     if (count == 0) return SHAMPOO4_OK;
-    if (!M || !N || !K || !A || !lda || !B || !ldb || !D || !ldd || !workspace) return SHAMPOO4_EINVAL;
+    if (!M || !N || !K || !A || !lda || !B || !ldb || !D || !ldd) return SHAMPOO4_EINVAL;
     if (beta != 0.f && (!C || !ldc)) return SHAMPOO4_EINVAL;
-    if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return SHAMPOO4_EALIGN;
-    if (workspace_bytes < shampoo4_gemm_workspace_bytes(count)) return SHAMPOO4_ESMALLBUF;
-    shampoo4_ctx_s tmp;
-    tmp.ws = static_cast<uint8_t*>(workspace);
     std::vector<shampoo4_ctx_s::GemmItem> items;
     for (int i = 0; i < count; ++i) {
         if (M[i] < 0 || N[i] < 0 || K[i] < 0) return SHAMPOO4_ESHAPE;
@@ -2029,24 +2032,67 @@ shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t tra
                             beta != 0.f ? C[i] : nullptr, beta != 0.f ? ldc[i] : 0);
         items.push_back({d, transA != 0, transB != 0});
     }
-    // one launch: the workspace holds one descriptor table and one tile prefix (the tile
-    // shape follows the products' class when they all share one)
+    // one launch: one descriptor table and one tile prefix (the tile shape follows the
+    // products' class when they all share one)
     Seq seq = tmp.make_gemm(items, FAM_GEMM_PRECOND);
     if (seq.size() > 1) {
         tmp.blob.clear();
         seq = tmp.make_gemm(items, FAM_GEMM_PRECOND, false, false);
     }
-    if (seq.empty()) return SHAMPOO4_OK;
-    const Launch& L = seq[0];
-    hipStream_t s = as_stream(stream);
+    if (!seq.empty()) L = seq[0];
+    return SHAMPOO4_OK;
+}
+
+// Copies the planned table to `dev` (device memory) and launches the product on it.
+shampoo4_status run_gemm_batched(const shampoo4_ctx_s& tmp, const Launch& L, uint8_t* dev, hipStream_t s) {
+    if (hipMemcpyAsync(dev, tmp.blob.data(), tmp.blob.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+        return SHAMPOO4_EHIP;
+    hipError_t e = launch_gemm(L.cfg, L.mode, L.vec, L.slab, reinterpret_cast<const GemmDesc*>(dev + L.desc_off),
+                               reinterpret_cast<const int*>(dev + L.prefix_off), L.ndesc, L.ntiles, nullptr, s);
+    return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t transB, const int32_t* M,
+                                      const int32_t* N, const int32_t* K, float alpha, const float* const* A,
+                                      const int64_t* lda, const float* const* B, const int64_t* ldb, float beta,
+                                      const float* const* C, const int64_t* ldc, float* const* D,
+                                      const int64_t* ldd, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+    if (count > 0) {
+        if (!workspace) return SHAMPOO4_EINVAL;
+        if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return SHAMPOO4_EALIGN;
+        if (workspace_bytes < shampoo4_gemm_workspace_bytes(count)) return SHAMPOO4_ESMALLBUF;
+    }
+    shampoo4_ctx_s tmp;
+    Launch L;
+    shampoo4_status st = plan_gemm_batched(count, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                           D, ldd, tmp, L);
+    if (st != SHAMPOO4_OK || L.ntiles <= 0) return st;
     // the descriptors and their tile prefix sit at the start of the caller's workspace
     if (tmp.blob.size() > workspace_bytes) return SHAMPOO4_ESMALLBUF;
-    if (hipMemcpyAsync(workspace, tmp.blob.data(), tmp.blob.size(), hipMemcpyHostToDevice, s) != hipSuccess)
-        return SHAMPOO4_EHIP;
-    const uint8_t* base = static_cast<const uint8_t*>(workspace);
-    hipError_t e = launch_gemm(L.cfg, L.mode, L.vec, L.slab, reinterpret_cast<const GemmDesc*>(base + L.desc_off),
-                               reinterpret_cast<const int*>(base + L.prefix_off), L.ndesc, L.ntiles, nullptr, s);
-    return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
+    return run_gemm_batched(tmp, L, static_cast<uint8_t*>(workspace), as_stream(stream));
+}
+
+shampoo4_status shampoo4_gemm_batched_static(int32_t count, int32_t transA, int32_t transB, const int32_t* M,
+                                             const int32_t* N, const int32_t* K, float alpha,
+                                             const float* const* A, const int64_t* lda, const float* const* B,
+                                             const int64_t* ldb, float beta, const float* const* C,
+                                             const int64_t* ldc, float* const* D, const int64_t* ldd,
+                                             void* stream) {
+    if (count > SHAMPOO4_GEMM_STATIC_MAX) return SHAMPOO4_ESMALLBUF;
+    shampoo4_ctx_s tmp;
+    Launch L;
+    shampoo4_status st = plan_gemm_batched(count, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                           D, ldd, tmp, L);
+    if (st != SHAMPOO4_OK || L.ntiles <= 0) return st;
+    if (tmp.blob.size() > GEMM_STATIC_SCRATCH_BYTES) return SHAMPOO4_ESMALLBUF;
+    void* scr = nullptr;   // this device's array (its address looked up at the first call)
+    if (gemm_static_scratch(&scr) != hipSuccess) return SHAMPOO4_EHIP;
+    return run_gemm_batched(tmp, L, static_cast<uint8_t*>(scr), as_stream(stream));
 }
 
 namespace {

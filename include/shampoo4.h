@@ -346,6 +346,26 @@ SHAMPOO4_API shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA
                                       float* const* D, const int64_t* ldd,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Allocation-free form of shampoo4_gemm_batched, for callers that cannot allocate device
+ * memory or provide a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, results (bit for bit) and errors as for
+ * shampoo4_gemm_batched, without the workspace: the descriptor table goes to a static
+ * device array of the library (384 KiB per GPU, held until the process ends; its address
+ * is looked up on the first call on each device).  The call allocates no device memory.
+ * At most SHAMPOO4_GEMM_STATIC_MAX products per call (more: SHAMPOO4_ESMALLBUF, nothing
+ * enqueued).  Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (concurrent streams or host threads) race on it, so order them (one stream, or
+ * an event between them).  Nothing in the array needs to start at zero: each call writes
+ * the whole table it uses (one copy from pageable host memory, enqueued before the
+ * kernel). */
+#define SHAMPOO4_GEMM_STATIC_MAX 2048
+SHAMPOO4_API shampoo4_status shampoo4_gemm_batched_static(int32_t count, int32_t transA, int32_t transB,
+                                             const int32_t* M, const int32_t* N, const int32_t* K,
+                                             float alpha, const float* const* A, const int64_t* lda,
+                                             const float* const* B, const int64_t* ldb,
+                                             float beta, const float* const* C, const int64_t* ldc,
+                                             float* const* D, const int64_t* ldd, void* stream);
+
 /* Inverse 4th root by the coupled Newton iteration, matrix products only ("Shampoo --
  * Second-Order Optimizer", section "Computing the inverse fourth root", second route),
  * for the unquantized baseline: for each i < count,
