@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "preconditioned block-steps/sec + GEMM TFLOP/s (% MFMA peak), quant GB/s (% HBM)"
 PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_FP64_MFMA_TFLOPS = 78.6
 PEAK_HBM_GBPS = 8000.0
 # fp32 vector peak of the code as built: packed fp32 instructions are disabled, so a CU
 # retires 64 fp32 FMAs (128 flops) per clock: 256 CUs x 2.4 GHz x 128 = 78.6 TFLOP/s
@@ -44,7 +45,9 @@ def log(msg: str):
 # kernel families of the roofline: timing-report families -> (kernel-name test, source file)
 FAMILIES = {
     "gemm": (lambda n: "gemm_kernel" in n, "gemm.hip"),
+    "gemm64": (lambda n: "gemm64_kernel" in n, "gemm64.hip"),
     "qr_panel": (lambda n: ("panel_" in n and "_kernel" in n) or "qr_step_kernel" in n, "qr.hip"),
+    "qr_panel64": (lambda n: "panel64_kernel" in n, "qr64.hip"),
     "quant": (lambda n: "quant_kernel" in n and "dequant" not in n, "codec.hip"),
     "dequant": (lambda n: "dequant_kernel" in n, "codec.hip"),
     "graft": (lambda n: "graft_" in n and "_kernel" in n, "graft.hip"),
@@ -403,6 +406,8 @@ def main():
     ap.add_argument("--graft", default="none", choices=["none", "sgd", "adam"],
                     help="add the grafted weight update after the preconditioner to every step")
     ap.add_argument("--graphs", action="store_true", help="replay update_stats from a captured HIP graph")
+    ap.add_argument("--fp64-refresh", action="store_true",
+                    help="run the statistics update (Bjorck .. Rayleigh quotients) in float64")
     ap.add_argument("--qr", default="auto", choices=["auto", "blocked", "lookahead"],
                     help="Householder QR schedule (default: chosen by the library from the batch size)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -460,7 +465,8 @@ def main():
     dev = torch.device("cuda:0")
     cfg = Shampoo4Config(beta=wl.beta, eps=wl.eps, qblock=wl.qblock, bjorck_iters=wl.bjorck_iters,
                          power_iters=wl.power_iters, root_cache=not args.no_root_cache, qr_schedule=args.qr,
-                         fp32_state=args.state == "fp32", graphs=args.graphs, codebook=args.codebook)
+                         fp32_state=args.state == "fp32", graphs=args.graphs, codebook=args.codebook,
+                         fp64_refresh=args.fp64_refresh)
     log(f"[bench] workload {wl.name}: {len(wl.blocks)} blocks, steps {steps}, warmup {warmup}")
     grads, distinct, gen = make_gradients(wl, steps + warmup, dev)
     blocks = Shampoo4Blocks(wl.shapes, cfg, device=dev)
@@ -518,10 +524,10 @@ def main():
                 f"{r['bytes'] / max(r['ms'], 1e-9) / 1e6:8.1f} GB/s")
     fam = {"gemm": {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0}}
     for name, r in rep.items():
-        if name.startswith("gemm"):
+        if name.startswith("gemm") and name != "gemm64":
             for k in fam["gemm"]:
                 fam["gemm"][k] += r[k]
-        elif name in ("qr_panel", "quant", "dequant", "graft"):
+        elif name in ("qr_panel", "quant", "dequant", "graft", "gemm64", "diag"):
             fam[name] = dict(r)
     g = fam["gemm"]
     gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12 if g["ms"] > 0 else 0.0
@@ -549,6 +555,10 @@ def main():
         "dequant": ("hbm", "dequant_kernel: 4.5625 B per element (nibble + scale in, fp32 out)"),
         "graft": ("hbm", "graft_norms_kernel + graft_apply_kernel: per element G and P read (Adam: moments "
                   "read and written) for the block norms, then P and W read and W written"),
+        "gemm64": ("mfma64", "gemm64_kernel (fp64 v_mfma_f64_16x16x4_f64): every product of the float64 "
+                   "statistics update; algorithmic flops = 2 M N K of each product"),
+        "diag": ("hbm", "diag_partials / diag_ema / diag_scale kernels of the diagonal sides: G read once "
+                 "for the statistic, G read and P written for a both-diagonal block"),
     }
     rooflines = {}
     for name, (bound, desc) in kernels.items():
@@ -561,9 +571,10 @@ def main():
             achieved, peak, unit = r["bytes"] / r["launches"] / per_launch_s / 1e9, PEAK_HBM_GBPS, "GB/s"
         else:
             achieved = r["flops"] / r["launches"] / per_launch_s / 1e12
-            peak, unit = (PEAK_FP32_MFMA_TFLOPS if bound == "mfma" else PEAK_FP32_VALU_TFLOPS), "TFLOP/s"
+            peak = {"mfma": PEAK_FP32_MFMA_TFLOPS, "mfma64": PEAK_FP64_MFMA_TFLOPS}.get(bound, PEAK_FP32_VALU_TFLOPS)
+            unit = "TFLOP/s"
         rooflines[name] = {
-            "bound": bound, "kernel": desc, "achieved": round(achieved, 4), "peak": peak, "unit": unit,
+            "bound": "mfma" if bound == "mfma64" else bound, "kernel": desc, "achieved": round(achieved, 4), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 6),
             "traffic": round(traffic[name]) if name in traffic else None,
             "algorithmic_bytes_per_launch": round(r["bytes"] / r["launches"]),
@@ -583,7 +594,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "fp32+fp64 (statistics update in fp64)" if args.fp64_refresh else "fp32",
         "data": f"synthetic ({gen}, {distinct} distinct gradient batches)",
         "config": {
             "workload": wl.name,
@@ -593,6 +604,7 @@ def main():
             "bjorck_iters": wl.bjorck_iters, "power_iters": wl.power_iters,
             "root_interval": wl.root_interval, "root_cache": cfg.root_cache, "qr_schedule": args.qr,
             "graft": args.graft, "state": args.state, "codebook": args.codebook, "graphs": args.graphs,
+            "fp64_refresh": args.fp64_refresh,
         },
         "gemm_tflops": round(gemm_tflops, 3),
         "gemm_frac_mfma_peak": round(gemm_tflops / PEAK_FP32_MFMA_TFLOPS, 4),

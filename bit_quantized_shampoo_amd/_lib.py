@@ -19,13 +19,14 @@ FLAG_QR_LOOKAHEAD = 8
 FLAG_FP32_STATE = 16
 FLAG_GRAPHS = 32
 FLAG_DT_CODEBOOK = 64
+FLAG_FP64_REFRESH = 128
 DIAG_L = 1
 DIAG_R = 2
 CODEBOOK_LINEAR_SQUARE = 0
 CODEBOOK_DYNAMIC_TREE = 1
 
 BUF_CODES, BUF_SCALES, BUF_EIG, BUF_ROOT_CODES, BUF_ROOT_SCALES, BUF_ROOT_D = range(6)
-BUF_V, BUF_STAT, BUF_Q, BUF_ROOT_V, BUF_ROOT_MAT = 16, 17, 18, 19, 20
+BUF_V, BUF_STAT, BUF_Q, BUF_ROOT_V, BUF_ROOT_MAT, BUF_STAT64, BUF_Q64 = 16, 17, 18, 19, 20, 21, 22
 
 EXPORTED = [
     "shampoo4_abi_version", "shampoo4_strerror", "shampoo4_plan", "shampoo4_init",

@@ -243,6 +243,45 @@ struct DiagDesc {
 };
 static_assert(sizeof(DiagDesc) == 48, "DiagDesc layout");
 
+// One float64 product of the float64 statistics update: D = alpha op(A) op(B) + beta C,
+// op(B)'s row k times kscale[k] when set.  A and B are double, or float for a launch
+// whose operands are the caller's gradients (a_io / b_io: taken from the io table).
+struct Gemm64Desc {
+    const void* A;
+    const void* B;
+    const double* C;
+    double* D;
+    const float* kscale;
+    int64_t lda, ldb, ldc, ldd;
+    double alpha, beta;
+    int32_t M, N, K, tiles_m;
+    int32_t a_io, b_io;
+};
+static_assert(sizeof(Gemm64Desc) == 112, "Gemm64Desc layout");
+
+// One float64 Householder panel: rows c0.., columns c0..c0+nb-1 (nb <= 32) of the p x p
+// matrix A (leading dimension ld); V and Y = V T receive h x 32 (pitch vld; columns past
+// nb zero), rdiag[c0 + j] the diagonal of R.
+struct Panel64Desc {
+    double* A;
+    double* V;
+    double* Y;
+    double* rdiag;
+    int64_t ld, vld;
+    int32_t c0, h, nb, pad;
+};
+static_assert(sizeof(Panel64Desc) == 64, "Panel64Desc layout");
+
+// Float64 per-column / conversion work item on a p x p matrix (leading dimension p).
+struct Vec64Desc {
+    const double* a;          // coldot: Q; ident: R diagonal; cvt (to float32): source
+    const double* b;          // coldot: W = L~ Q
+    double* out;              // ident: Q; cvt (to float64): destination
+    float* f32;               // coldot: eigenvalues; cvt: the float32 side
+    int32_t p, pad;
+};
+static_assert(sizeof(Vec64Desc) == 40, "Vec64Desc layout");
+
 // Find the work item owning `tile` from an inclusive-exclusive prefix of tile counts.
 __device__ __forceinline__ int find_item(const int* __restrict__ prefix, int n, int tile) {
     int lo = 0, hi = n - 1;

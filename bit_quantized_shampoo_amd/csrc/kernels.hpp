@@ -112,6 +112,22 @@ hipError_t launch_diag_ema(const VecDesc* descs, const int* prefix, int ndesc, i
 hipError_t launch_diag_scale(const DiagDesc* descs, const int* prefix, int ndesc, int ntiles,
                              const IoEntry* io, hipStream_t stream);
 
+// Float64 statistics update: the matrix product on the fp64 matrix cores (128 x 128 tiles;
+// mode GEMM_F_TA | GEMM_F_TB shared by the launch; in_float: the operands are float,
+// else double), Householder panels, Rayleigh quotients, the signed identity start of Q
+// and the float32 <-> float64 conversions (CVT_TILE elements per workgroup).
+int gemm64_tiles(int M, int N);
+int gemm64_tiles_m(int M);
+hipError_t launch_gemm64(int mode, bool in_float, const Gemm64Desc* descs, const int* prefix, int ndesc,
+                         int ntiles, const IoEntry* io, hipStream_t stream);
+hipError_t launch_panel64(const Panel64Desc* descs, int ndesc, hipStream_t stream);
+hipError_t launch_coldot64(const Vec64Desc* descs, const int* prefix, int ndesc, int ntiles, uint32_t* flag,
+                           hipStream_t stream);
+hipError_t launch_ident64(const Vec64Desc* descs, const int* prefix, int ndesc, int ntiles, hipStream_t stream);
+constexpr int CVT_TILE = 4096;
+hipError_t launch_cvt(const Vec64Desc* descs, const int* prefix, int ndesc, int ntiles, int dir,
+                      hipStream_t stream);
+
 // Grafting epilogue: two launches over the same row tiles of every block.
 constexpr int GRAFT_TILE = 4096;             // elements per workgroup (at least one row)
 constexpr int graft_rows(int n) { return n >= GRAFT_TILE ? 1 : GRAFT_TILE / n; }

@@ -40,18 +40,19 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 enum Family {
     FAM_GEMM_BJORCK = 0, FAM_GEMM_STATS, FAM_GEMM_POWER, FAM_GEMM_QR, FAM_GEMM_RAYLEIGH,
     FAM_GEMM_PRECOND, FAM_DEQUANT, FAM_QUANT, FAM_PANEL, FAM_RAYLEIGH, FAM_ELEMENTWISE, FAM_GRAFT,
-    FAM_GEMM_QR_TRAIL, FAM_GEMM_QR_Q, FAM_DIAG, FAM_N
+    FAM_GEMM_QR_TRAIL, FAM_GEMM_QR_Q, FAM_DIAG, FAM_GEMM64, FAM_N
 };
 // gemm_qr: the reflector products inside an outer block (and the look-ahead schedule's);
 // gemm_qr_trail: an outer block's reflectors on the trailing columns; gemm_qr_q: the
 // accumulation of Q
 const char* kFamilyNames[FAM_N] = {"gemm_bjorck", "gemm_stats", "gemm_power", "gemm_qr", "gemm_rayleigh",
                                    "gemm_precond", "dequant", "quant", "qr_panel", "rayleigh",
-                                   "elementwise", "graft", "gemm_qr_trail", "gemm_qr_q", "diag"};
+                                   "elementwise", "graft", "gemm_qr_trail", "gemm_qr_q", "diag", "gemm64"};
 
 enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT,
             K_RECORD, K_WAIT, K_GRAFT_NORMS, K_GRAFT_APPLY, K_COPYF, K_NEWTON_NORM, K_NEWTON_SCALE,
-            K_NEWTON_ELEM, K_QRSTEP, K_DIAG_PARTIALS, K_DIAG_EMA, K_DIAG_SCALE };
+            K_NEWTON_ELEM, K_QRSTEP, K_DIAG_PARTIALS, K_DIAG_EMA, K_DIAG_SCALE, K_GEMM64, K_PANEL64,
+            K_COLDOT64, K_IDENT64, K_CVT };
 
 struct Launch {
     Kind kind = K_GEMM;
@@ -66,6 +67,7 @@ struct Launch {
     bool vec = false;    // GEMM: 16-byte operand loads (io operands: also checked per call)
     bool slab = false;   // GEMM: some operand sums split-K slabs
     bool uses_io = false;
+    bool f32in = false;  // fp64 GEMM: float operands (the gradients)
     int ev = -1;         // K_RECORD / K_WAIT: index of the context's synchronization event
     double flops = 0, bytes = 0;
 };
@@ -80,6 +82,10 @@ struct Side {
     // workspace offsets
     size_t Vs = 0, Vr = 0, Tmp = 0, Wg = 0, Lt = 0, Pm = 0, Qm = 0, Vb = 0, Yb = 0, Z = 0, W = 0, Mb = 0,
            Z2 = 0, rdiag = 0, Tb = 0, Rt = 0;
+    // float64 statistics update: Bjorck ping-pong, Gram, statistic, P (factored in place), Q,
+    // the panels' V and Y, the trailing / Q products' intermediates and R's diagonal
+    size_t V64a = 0, V64b = 0, Wg64 = 0, Lt64 = 0, P64 = 0, Q64 = 0, Vb64 = 0, Yb64 = 0, Z64 = 0, W64 = 0,
+           rd64 = 0;
     std::vector<size_t> outer_rows;   // row offset of outer block o inside Vb / Yb (pitch = outer width)
 };
 
@@ -122,6 +128,9 @@ struct shampoo4_ctx_s {
     bool lookahead = false;               // small batches: trailing and Q updates on a second stream
     bool fused = false;                   // small batches: one launch per panel (QR step kernel)
     bool fp32_state = false;              // U kept in float32 (the 32-bit baseline), no codec
+    bool fp64 = false;                    // statistics update in float64 (FP64_REFRESH)
+    Seq s64_pre, s64_stats, s64_power_first, s64_power_next, s64_qinit, s64_post;   // float64 update
+    std::vector<Seq> s64_bjorck, s64_qr, s64_qacc;
     int codebook = SHAMPOO4_CODEBOOK_LINEAR_SQUARE;   // 4-bit codebook of U and the root
     int n_sync = 0;                       // synchronization events the plan uses
     hipStream_t aux = nullptr;
@@ -385,6 +394,7 @@ struct shampoo4_ctx_s {
     // ---- plan ---------------------------------------------------------------------
     void layout() {
         fp32_state = (cfg.flags & SHAMPOO4_FLAG_FP32_STATE) != 0;
+        fp64 = (cfg.flags & SHAMPOO4_FLAG_FP64_REFRESH) != 0;
         codebook = (cfg.flags & SHAMPOO4_FLAG_DT_CODEBOOK) ? SHAMPOO4_CODEBOOK_DYNAMIC_TREE
                                                            : SHAMPOO4_CODEBOOK_LINEAR_SQUARE;
         use_graphs = (cfg.flags & SHAMPOO4_FLAG_GRAPHS) != 0;
@@ -401,7 +411,7 @@ struct shampoo4_ctx_s {
         lookahead = (cfg.flags & SHAMPOO4_FLAG_QR_LOOKAHEAD) != 0;
         const bool blocked = (cfg.flags & SHAMPOO4_FLAG_QR_BLOCKED) ||
                              (!lookahead && work >= 16.0 * 1073741824.0);
-        outer = blocked ? kOuter : kPanel;
+        outer = (blocked && !fp64) ? kOuter : kPanel;   // the float64 QR goes panel by panel
         sides.assign(2 * nb, Side{});
         size_t so = 0, wo = 0;
         auto st_take = [&](size_t b) { size_t o = so; so += align_up(b ? b : 1); return o; };
@@ -445,6 +455,32 @@ struct shampoo4_ctx_s {
                 S.rscales = st_take(sbytes);
                 S.d = st_take(p * 4);
                 const size_t mat = (size_t)p * p * 4;
+                if (fp64) {   // float32: dequantized U, the root and Q for the quantizer only
+                    S.Vr = ws_take(mat);
+                    S.Rt = ws_take(mat);
+                    S.Tmp = ws_take(mat);
+                    S.Wg = ws_take(mat);
+                    S.Qm = ws_take(mat);
+                    const size_t mat64 = (size_t)p * p * 8;
+                    S.V64a = ws_take(mat64);
+                    S.V64b = ws_take(mat64);
+                    S.Wg64 = ws_take(mat64);
+                    S.Lt64 = ws_take(mat64);
+                    S.P64 = ws_take(mat64);
+                    S.Q64 = ws_take(mat64);
+                    S.outer_rows.clear();
+                    size_t rows = 0;
+                    for (int c0 = 0; c0 < p; c0 += kPanel) {
+                        S.outer_rows.push_back(rows);
+                        rows += p - c0;
+                    }
+                    S.Vb64 = ws_take(rows * kPanel * 8);
+                    S.Yb64 = ws_take(rows * kPanel * 8);
+                    S.Z64 = ws_take((size_t)kPanel * p * 8);
+                    S.W64 = ws_take((size_t)kPanel * p * 8);
+                    S.rd64 = ws_take((size_t)p * 8);
+                    continue;
+                }
                 S.Vs = ws_take(mat);
                 S.Vr = ws_take(mat);
                 S.Rt = ws_take(mat);   // root matrix V^r diag(d) V^r^T (ROOT_CACHE)
@@ -983,9 +1019,16 @@ struct shampoo4_ctx_s {
     void build() {
         blob.clear();
         const float beta = cfg.beta;
-        build_bjorck(false, deq_stats, bj_stats);
         build_bjorck(true, deq_root, bj_root);
+        if (fp64) build_fp64();
+        else build_stats_fp32(beta);
+        build_tail();
+    }
 
+    // The float32 statistics update: Bjorck, the statistic, the power step and the QR
+    // schedule the batch calls for.
+    void build_stats_fp32(float beta) {
+        build_bjorck(false, deq_stats, bj_stats);
         // statistics: Lt = beta V diag(lam) V^T, then Lt += (1 - beta) G G^T (side R: G^T G)
         for (int var = 0; var < 2; ++var) {
             std::vector<GemmItem> xs, pw;
@@ -1058,6 +1101,11 @@ struct shampoo4_ctx_s {
         if (lookahead) build_qr_lookahead();
         else if (fused) build_qr_fused();
         else build_qr_blocked();
+    }
+
+    // Everything after the statistics and QR: the Rayleigh step, requantization, root
+    // refresh, initial state, precondition and the diagonal sides.
+    void build_tail() {
         {
             std::vector<VecDesc> qi, rr, rt;
             std::vector<int> tqi, trr, trt;
@@ -1130,6 +1178,9 @@ struct shampoo4_ctx_s {
                 trr.push_back((S.p + 255) / 256);
             }
             rayleigh = {make_items(K_RAYLEIGH, rr, trr)};
+            if (fp64) {   // the float64 update has its own (s64_*): these float32 ones never run
+                qinit.clear(); qinit_signed.clear(); sign.clear(); ray_gemm.clear(); rayleigh.clear();
+            }
             root_d = {make_items(K_ROOT, rt, trt)};
             if (fp32_state) {
                 std::vector<VecDesc> qv, rv;
@@ -1317,6 +1368,225 @@ struct shampoo4_ctx_s {
         }
     }
 
+    // ---- float64 statistics update (FP64_REFRESH) ------------------------------------
+    struct G64Item {
+        Gemm64Desc d;
+        int mode;      // GEMM_F_TA | GEMM_F_TB
+        bool f32in;    // float operands (the gradients, through the io table)
+    };
+    double* wsd(size_t off) const { return wsp<double>(off); }
+    static Gemm64Desc g64(const void* A, int64_t lda, const void* B, int64_t ldb, double* D, int64_t ldd, int M,
+                          int N, int K, double alpha = 1.0, double beta = 0.0, const double* C = nullptr,
+                          int64_t ldc = 0) {
+        Gemm64Desc d;
+        std::memset(&d, 0, sizeof(d));
+        d.A = A; d.B = B; d.C = C; d.D = D;
+        d.lda = lda; d.ldb = ldb; d.ldc = ldc ? ldc : ldd; d.ldd = ldd;
+        d.M = M; d.N = N; d.K = K;
+        d.alpha = alpha; d.beta = beta;
+        d.a_io = d.b_io = -1;
+        return d;
+    }
+    // one launch per (transpose mode, operand type) present among the items
+    Seq gemm64_seq(const std::vector<G64Item>& items, int fam) {
+        Seq out;
+        for (int f = 0; f < 2; ++f)
+            for (int mode = 0; mode < 4; ++mode) {
+                std::vector<Gemm64Desc> ds;
+                std::vector<int> tiles;
+                double flops = 0, bytes = 0;
+                bool io_used = false;
+                for (auto& it : items) {
+                    if (it.mode != mode || (int)it.f32in != f || it.d.M <= 0 || it.d.N <= 0) continue;
+                    Gemm64Desc d = it.d;
+                    d.tiles_m = gemm64_tiles_m(d.M);
+                    ds.push_back(d);
+                    tiles.push_back(gemm64_tiles(d.M, d.N));
+                    flops += 2.0 * d.M * d.N * d.K;
+                    bytes += (f ? 4.0 : 8.0) * ((double)d.M * d.K + (double)d.K * d.N) +
+                             8.0 * d.M * d.N * (d.beta != 0.0 ? 2 : 1);
+                    io_used = io_used || d.a_io >= 0 || d.b_io >= 0;
+                }
+                if (ds.empty()) continue;
+                Launch L = make_items(K_GEMM64, ds, tiles);
+                L.fam = fam;
+                L.mode = mode;
+                L.f32in = f != 0;
+                L.flops = flops;
+                L.bytes = bytes;
+                L.uses_io = io_used;
+                out.push_back(L);
+            }
+        return out;
+    }
+
+    // U (dequantized, exact in float32) widened to float64; Bjorck, the statistic
+    // beta V diag(lam) V^T + (1 - beta) G G^T, the power step, the Householder QR panel by
+    // panel (each panel's reflectors on the columns right of it, then Q accumulated
+    // backward from diag(sign(R_jj))), the Rayleigh quotients, all in float64; Q rounded
+    // to float32 for the quantizer.  The same steps as the float32 update, in float64.
+    void build_fp64() {
+        const int k = cfg.bjorck_iters;
+        const double beta = (double)cfg.beta;
+        {   // U into Tmp (float32), then widened into V64a
+            std::vector<CodecDesc> cds;
+            std::vector<VecDesc> vd;
+            std::vector<int> tiles, vt, ct;
+            std::vector<Vec64Desc> cv;
+            double bytes = 0;
+            for (Side& S : full) {
+                const int64_t n = (int64_t)S.p * S.p;
+                if (fp32_state) {
+                    vd.push_back(copyf_desc(stf(S.codes), wsf(S.Tmp), n));
+                    vt.push_back(copyf_tiles(n));
+                } else {
+                    CodecDesc c;
+                    std::memset(&c, 0, sizeof(c));
+                    c.codes_in = stp<uint8_t>(S.codes);
+                    c.scales_in = stf(S.scales);
+                    c.x_out = wsf(S.Tmp);
+                    c.n = n;
+                    cds.push_back(c);
+                    tiles.push_back((int)dequant_tiles(n));
+                }
+                bytes += (double)n * (fp32_state ? 8.0 : 4.0 + 0.5 + 4.0 / 64);
+                Vec64Desc v;
+                std::memset(&v, 0, sizeof(v));
+                v.f32 = wsf(S.Tmp);
+                v.out = wsd(S.V64a);
+                v.p = S.p;
+                cv.push_back(v);
+                ct.push_back((int)((n + CVT_TILE - 1) / CVT_TILE));
+            }
+            Launch L = fp32_state ? make_items(K_COPYF, vd, vt) : make_items(K_DEQUANT, cds, tiles);
+            L.fam = FAM_DEQUANT;
+            L.bytes = bytes;
+            Launch C = make_items(K_CVT, cv, ct);
+            C.mode = 0;
+            s64_pre = {L, C};
+        }
+        s64_bjorck.clear();
+        for (int i = 0; i < k; ++i) {
+            std::vector<G64Item> gram, upd;
+            for (Side& S : full) {
+                const int p = S.p;
+                double* in = wsd(i % 2 == 0 ? S.V64a : S.V64b);
+                double* out = wsd(i % 2 == 0 ? S.V64b : S.V64a);
+                gram.push_back({g64(in, p, in, p, wsd(S.Wg64), p, p, p, p), GEMM_F_TA, false});
+                upd.push_back({g64(in, p, wsd(S.Wg64), p, out, p, p, p, p, -0.5, 1.5, in, p), 0, false});
+            }
+            Seq sq = gemm64_seq(gram, FAM_GEMM64);
+            Seq su = gemm64_seq(upd, FAM_GEMM64);
+            sq.insert(sq.end(), su.begin(), su.end());
+            s64_bjorck.push_back(sq);
+        }
+        auto vfin = [&](const Side& S) { return wsd(k % 2 == 0 ? S.V64a : S.V64b); };
+        {   // the statistic, then the first and the later power steps
+            std::vector<G64Item> xs, gs, pf, pn;
+            for (Side& S : full) {
+                const int p = S.p;
+                Gemm64Desc d = g64(vfin(S), p, vfin(S), p, wsd(S.Lt64), p, p, p, p, beta);
+                d.kscale = stf(S.lam);                    // V diag(lam) V^T
+                xs.push_back({d, GEMM_F_TB, false});
+                pf.push_back({g64(wsd(S.Lt64), p, vfin(S), p, wsd(S.P64), p, p, p, p), 0, false});
+                pn.push_back({g64(wsd(S.Lt64), p, wsd(S.Q64), p, wsd(S.P64), p, p, p, p), 0, false});
+            }
+            for (int b = 0; b < nb; ++b)
+                for (int s = 0; s < 2; ++s) {
+                    Side& S = sides[2 * b + s];
+                    if (S.diag) continue;
+                    const int p = S.p, q = S.q;
+                    Gemm64Desc d = g64(nullptr, 0, nullptr, 0, wsd(S.Lt64), p, p, p, q, 1.0 - beta, 1.0,
+                                       wsd(S.Lt64), p);
+                    d.a_io = d.b_io = b;   // G G^T (side R: G^T G), float gradients
+                    gs.push_back({d, s == 0 ? GEMM_F_TB : GEMM_F_TA, true});
+                }
+            s64_stats = gemm64_seq(xs, FAM_GEMM64);
+            Seq g = gemm64_seq(gs, FAM_GEMM64);
+            s64_stats.insert(s64_stats.end(), g.begin(), g.end());
+            s64_power_first = gemm64_seq(pf, FAM_GEMM64);
+            s64_power_next = gemm64_seq(pn, FAM_GEMM64);
+        }
+        // QR of P64, panel by panel
+        s64_qr.assign(max_panels, Seq{});
+        s64_qacc.assign(max_panels, Seq{});
+        for (int kp = 0; kp < max_panels; ++kp) {
+            std::vector<Panel64Desc> pds;
+            std::vector<int> ones;
+            std::vector<G64Item> z1, z2, w1, w2;
+            double pflops = 0;
+            for (Side& S : full) {
+                const int p = S.p, c0 = kp * kPanel;
+                if (c0 >= p) continue;
+                const int h = p - c0, nbw = std::min(kPanel, h), ntr = p - c0 - nbw;
+                double* Vp = wsd(S.Vb64) + S.outer_rows[kp] * kPanel;
+                double* Yp = wsd(S.Yb64) + S.outer_rows[kp] * kPanel;
+                Panel64Desc pd;
+                std::memset(&pd, 0, sizeof(pd));
+                pd.A = wsd(S.P64); pd.V = Vp; pd.Y = Yp; pd.rdiag = wsd(S.rd64);
+                pd.ld = p; pd.vld = kPanel; pd.c0 = c0; pd.h = h; pd.nb = nbw;
+                pds.push_back(pd);
+                ones.push_back(1);
+                pflops += householder_flops(h, nbw);
+                if (ntr > 0) {   // the panel's reflectors on the columns right of it: A -= V (Y^T A)
+                    double* At = wsd(S.P64) + (int64_t)c0 * p + c0 + nbw;
+                    z1.push_back({g64(Yp, kPanel, At, p, wsd(S.Z64), p, nbw, ntr, h), GEMM_F_TA, false});
+                    z2.push_back({g64(Vp, kPanel, wsd(S.Z64), p, At, p, h, ntr, nbw, -1.0, 1.0, At, p), 0, false});
+                }
+                // Q accumulated backward: Q[c0:, c0:] -= Y (V^T Q[c0:, c0:])
+                double* Qs = wsd(S.Q64) + (int64_t)c0 * p + c0;
+                w1.push_back({g64(Vp, kPanel, Qs, p, wsd(S.W64), p, nbw, h, h), GEMM_F_TA, false});
+                w2.push_back({g64(Yp, kPanel, wsd(S.W64), p, Qs, p, h, h, nbw, -1.0, 1.0, Qs, p), 0, false});
+            }
+            Launch P = make_items(K_PANEL64, pds, ones);
+            P.fam = FAM_PANEL;
+            P.flops = pflops;
+            for (auto& pd : pds) P.bytes += 8.0 * (double)pd.h * pd.nb * 3;
+            Seq& st = s64_qr[kp];
+            st = {P};
+            for (auto* items : {&z1, &z2}) {
+                Seq g = gemm64_seq(*items, FAM_GEMM64);
+                st.insert(st.end(), g.begin(), g.end());
+            }
+            Seq& qa = s64_qacc[max_panels - 1 - kp];   // run last panel first
+            for (auto* items : {&w1, &w2}) {
+                Seq g = gemm64_seq(*items, FAM_GEMM64);
+                qa.insert(qa.end(), g.begin(), g.end());
+            }
+        }
+        {   // Q = diag(sign(R_jj)) before the backward accumulation; Rayleigh; Q to float32
+            std::vector<Vec64Desc> qi, cd, cq;
+            std::vector<int> tqi, tcd, tcq;
+            std::vector<G64Item> ray;
+            for (Side& S : full) {
+                const int p = S.p;
+                Vec64Desc v;
+                std::memset(&v, 0, sizeof(v));
+                v.a = wsd(S.rd64); v.out = wsd(S.Q64); v.p = p;
+                qi.push_back(v);
+                tqi.push_back(p);
+                ray.push_back({g64(wsd(S.Lt64), p, wsd(S.Q64), p, wsd(S.Wg64), p, p, p, p), 0, false});
+                std::memset(&v, 0, sizeof(v));
+                v.a = wsd(S.Q64); v.b = wsd(S.Wg64); v.f32 = stf(S.lam); v.p = p;
+                cd.push_back(v);
+                tcd.push_back((p + 255) / 256);
+                std::memset(&v, 0, sizeof(v));
+                v.a = wsd(S.Q64); v.f32 = wsf(S.Qm); v.p = p;
+                cq.push_back(v);
+                tcq.push_back((int)(((int64_t)p * p + CVT_TILE - 1) / CVT_TILE));
+            }
+            Launch I = make_items(K_IDENT64, qi, tqi);
+            s64_qinit = {I};
+            s64_post = gemm64_seq(ray, FAM_GEMM64);
+            Launch D = make_items(K_COLDOT64, cd, tcd);
+            D.fam = FAM_RAYLEIGH;
+            Launch C = make_items(K_CVT, cq, tcq);
+            C.mode = 1;
+            s64_post.push_back(D);
+            s64_post.push_back(C);
+        }
+    }
+
     // grafting epilogue: the same row tiles for both passes; bytes per element depend on
     // the mode (SGD: G, P read; Adam: also both moments read and written)
     void build_graft() {
@@ -1436,6 +1706,24 @@ struct shampoo4_ctx_s {
                 e = launch_graft_apply(reinterpret_cast<const GraftDesc*>(base + L.desc_off), prefix, L.ndesc,
                                        L.ntiles, io, wsp<GraftIo>(gio_off), graft_prm, s);
                 break;
+            case K_GEMM64:
+                e = launch_gemm64(L.mode, L.f32in, reinterpret_cast<const Gemm64Desc*>(base + L.desc_off), prefix,
+                                  L.ndesc, L.ntiles, io, s);
+                break;
+            case K_PANEL64:
+                e = launch_panel64(reinterpret_cast<const Panel64Desc*>(base + L.desc_off), L.ndesc, s);
+                break;
+            case K_COLDOT64:
+                e = launch_coldot64(reinterpret_cast<const Vec64Desc*>(base + L.desc_off), prefix, L.ndesc, L.ntiles,
+                                    flag, s);
+                break;
+            case K_IDENT64:
+                e = launch_ident64(reinterpret_cast<const Vec64Desc*>(base + L.desc_off), prefix, L.ndesc, L.ntiles, s);
+                break;
+            case K_CVT:
+                e = launch_cvt(reinterpret_cast<const Vec64Desc*>(base + L.desc_off), prefix, L.ndesc, L.ntiles,
+                               L.mode, s);
+                break;
             case K_DIAG_PARTIALS:
                 e = launch_diag_partials(reinterpret_cast<const DiagDesc*>(base + L.desc_off), prefix, L.ndesc,
                                          L.ntiles, io, s);
@@ -1520,6 +1808,7 @@ struct shampoo4_ctx_s {
     hipError_t stats_body(bool reuse, hipStream_t s, const std::function<hipError_t()>* at_qr = nullptr) {
         const int var = reuse ? 1 : 0;
         hipError_t e = run(diag_stats, s);
+        if (fp64) return stats_body_fp64(s, at_qr, e);
         const bool fold = !reuse && !bj_stats_fold.empty();
         if (!reuse && e == hipSuccess) {
             e = run(deq_stats, s);
@@ -1551,11 +1840,29 @@ struct shampoo4_ctx_s {
         return e;
     }
 
+    hipError_t stats_body_fp64(hipStream_t s, const std::function<hipError_t()>* at_qr, hipError_t e) {
+        if (e == hipSuccess) e = run(s64_pre, s);
+        for (auto& it : s64_bjorck)
+            if (e == hipSuccess) e = run(it, s);
+        if (e == hipSuccess) e = run(s64_stats, s);
+        for (int it = 0; it < cfg.power_iters && e == hipSuccess; ++it) {
+            e = run(it == 0 ? s64_power_first : s64_power_next, s);
+            if (e == hipSuccess && it == 0 && at_qr) e = (*at_qr)();
+            for (size_t p = 0; p < s64_qr.size() && e == hipSuccess; ++p) e = run(s64_qr[p], s);
+            if (e == hipSuccess) e = run(s64_qinit, s);
+            for (size_t p = 0; p < s64_qacc.size() && e == hipSuccess; ++p) e = run(s64_qacc[p], s);
+        }
+        if (e == hipSuccess) e = run(s64_post, s);
+        if (e == hipSuccess) e = run(quant, s);
+        return e;
+    }
+
     // The statistics update after its io upload: graph replay or eager launches.
     // at_qr (optional): called where the QR begins (before the whole update when it is
     // replayed from a graph, after it when no power step runs)
     hipError_t submit_stats(hipStream_t s, const std::function<hipError_t()>* at_qr = nullptr) {
-        const bool reuse = (cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) && root_v_valid && root_v_is_stats;
+        // (the float64 update starts from the codes: the cached float32 root is not its V)
+        const bool reuse = (cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) && root_v_valid && root_v_is_stats && !fp64;
         const int var = reuse ? 1 : 0, vi = io_vec ? 1 : 0;
         hipError_t e = hipSuccess;
         if (use_graphs && graph_ok && !timing) {
@@ -1629,11 +1936,14 @@ shampoo4_status validate_cfg(const shampoo4_config* cfg) {
     if (cfg->power_iters < 1 || cfg->power_iters > 8) return SHAMPOO4_EINVAL;
     if (cfg->flags & ~(SHAMPOO4_FLAG_ROOT_CACHE | SHAMPOO4_FLAG_KEEP_STATE | SHAMPOO4_FLAG_QR_BLOCKED |
                        SHAMPOO4_FLAG_QR_LOOKAHEAD | SHAMPOO4_FLAG_FP32_STATE | SHAMPOO4_FLAG_GRAPHS |
-                       SHAMPOO4_FLAG_DT_CODEBOOK))
+                       SHAMPOO4_FLAG_DT_CODEBOOK | SHAMPOO4_FLAG_FP64_REFRESH))
         return SHAMPOO4_EINVAL;
     if ((cfg->flags & SHAMPOO4_FLAG_DT_CODEBOOK) && (cfg->flags & SHAMPOO4_FLAG_FP32_STATE))
         return SHAMPOO4_EINVAL;
     if ((cfg->flags & SHAMPOO4_FLAG_QR_BLOCKED) && (cfg->flags & SHAMPOO4_FLAG_QR_LOOKAHEAD))
+        return SHAMPOO4_EINVAL;
+    if ((cfg->flags & SHAMPOO4_FLAG_FP64_REFRESH) &&
+        (cfg->flags & (SHAMPOO4_FLAG_QR_LOOKAHEAD | SHAMPOO4_FLAG_FP32_STATE)))
         return SHAMPOO4_EINVAL;
     return SHAMPOO4_OK;
 }
@@ -1928,6 +2238,9 @@ shampoo4_status shampoo4_layout(shampoo4_ctx c, int32_t block, int32_t side, sha
     const size_t p = S.p;
     const size_t mat = p * p * 4;
     if (S.diag && which >= SHAMPOO4_BUF_V) return SHAMPOO4_EINVAL;   // a diagonal side has no matrices
+    // the float64 update keeps its statistic and eigenvectors in float64 (and no float32 V)
+    if (c->fp64 && (which == SHAMPOO4_BUF_V || which == SHAMPOO4_BUF_STAT)) return SHAMPOO4_EINVAL;
+    if (!c->fp64 && (which == SHAMPOO4_BUF_STAT64 || which == SHAMPOO4_BUF_Q64)) return SHAMPOO4_EINVAL;
     switch (which) {
         case SHAMPOO4_BUF_CODES: *offset = S.codes; *bytes = c->fp32_state ? (size_t)p * p * 4 : S.nqb * 32; break;
         case SHAMPOO4_BUF_SCALES: *offset = S.scales; *bytes = c->fp32_state ? 0 : S.nqb * 4; break;
@@ -1940,6 +2253,8 @@ shampoo4_status shampoo4_layout(shampoo4_ctx c, int32_t block, int32_t side, sha
         case SHAMPOO4_BUF_Q: *offset = S.Qm; *bytes = mat; break;
         case SHAMPOO4_BUF_ROOT_V: *offset = S.Vr; *bytes = mat; break;
         case SHAMPOO4_BUF_ROOT_MAT: *offset = S.Rt; *bytes = mat; break;
+        case SHAMPOO4_BUF_STAT64: *offset = S.Lt64; *bytes = 2 * mat; break;
+        case SHAMPOO4_BUF_Q64: *offset = S.Q64; *bytes = 2 * mat; break;
         default: return SHAMPOO4_EINVAL;
     }
     return SHAMPOO4_OK;

@@ -59,6 +59,7 @@ class Shampoo4Config:
     fp32_state: bool = False        # keep U in float32 (the 32-bit baseline) instead of 4-bit codes
     graphs: bool = False            # replay update_stats from a captured HIP graph
     codebook: str = "ls"            # 4-bit codebook of U: "ls" linear-square, "dt" dynamic tree
+    fp64_refresh: bool = False      # statistics update (Bjorck .. Rayleigh quotients) in float64
 
     def c(self, keep_state: bool = False) -> L.Config:
         flags = (L.FLAG_ROOT_CACHE if self.root_cache else 0) | (L.FLAG_KEEP_STATE if keep_state else 0)
@@ -70,6 +71,8 @@ class Shampoo4Config:
         if self.graphs:
             flags |= L.FLAG_GRAPHS
         flags |= {"ls": 0, "dt": L.FLAG_DT_CODEBOOK}[self.codebook]
+        if self.fp64_refresh:
+            flags |= L.FLAG_FP64_REFRESH
         return L.Config(self.beta, self.eps, self.qblock, self.bjorck_iters, self.power_iters, flags)
 
 
@@ -222,6 +225,9 @@ class Shampoo4Blocks:
         raw = base[off:off + nbytes]
         if which in (L.BUF_CODES, L.BUF_ROOT_CODES):
             return raw
+        if which in (L.BUF_STAT64, L.BUF_Q64):
+            p = self.shapes[block][side]
+            return raw.view(torch.float64).view(p, p)
         t = raw.view(torch.float32)
         if which >= 16:
             p = self.shapes[block][side]

@@ -110,6 +110,17 @@ typedef enum {
    compares linear-square with (it reports linear-square slightly ahead).  Every stage is
    unchanged but the codec's level table.  EINVAL together with FP32_STATE. */
 #define SHAMPOO4_FLAG_DT_CODEBOOK 64u
+/* Run the statistics update in float64 ("Shampoo -- Second-Order Optimizer", "Computing the
+   inverse fourth root": do the root in float64, since float32 eigensolvers lose the small
+   eigenvalues of a near-singular accumulator; "Pitfalls": root in float64, store in fp32):
+   from the dequantized eigenvectors (exact in float32) on, Bjorck, the statistic, the
+   power step, the Householder QR and the Rayleigh quotients are computed in float64 on the
+   fp64 matrix cores, and Q is rounded to float32 for the quantizer; the stored state, the
+   root and the preconditioned direction stay float32.  Eigenvalues are then resolved down
+   to about p 2^-53 lam_max instead of p 2^-24 lam_max.  The QR runs panel by panel (32
+   columns); EINVAL together with QR_LOOKAHEAD or FP32_STATE.  The workspace holds the float64 matrices
+   instead of most float32 ones (about 84 p^2 bytes per side against 48 p^2). */
+#define SHAMPOO4_FLAG_FP64_REFRESH 128u
 
 /* 4-bit codebooks (16 levels, ascending, code = index; the zero level is code 7).
    LINEAR_SQUARE: sign(t) t^2 on t = -1 + 2j/15 with the j = 7 level exactly 0; times 225:
@@ -158,8 +169,12 @@ typedef enum {
     SHAMPOO4_BUF_Q = 18,          /* workspace: fp32 [p,p] refreshed eigenvectors Q */
     SHAMPOO4_BUF_ROOT_V = 19,     /* workspace: fp32 [p,p] rectified root eigenvectors of
                                      the last refresh_root (ROOT_CACHE) or precondition */
-    SHAMPOO4_BUF_ROOT_MAT = 20    /* workspace: fp32 [p,p] root matrix V^r diag(d) V^r^T
+    SHAMPOO4_BUF_ROOT_MAT = 20,   /* workspace: fp32 [p,p] root matrix V^r diag(d) V^r^T
                                      (ROOT_CACHE: formed at init and at every refresh_root) */
+    SHAMPOO4_BUF_STAT64 = 21,     /* workspace, FP64_REFRESH only: fp64 [p,p] statistic L~ */
+    SHAMPOO4_BUF_Q64 = 22         /* workspace, FP64_REFRESH only: fp64 [p,p] refreshed Q
+                                     (BUF_Q holds it rounded to fp32; with FP64_REFRESH, BUF_V
+                                     and BUF_STAT are EINVAL) */
 } shampoo4_buffer;
 
 /* ABI version of the loaded library (SHAMPOO4_ABI_VERSION). */
@@ -394,7 +409,8 @@ SHAMPOO4_API shampoo4_status shampoo4_inverse_root(int32_t count, const int32_t*
  * products by the stage they serve; the QR's are split into the products inside an outer
  * reflector block, the block's products on the trailing columns and the accumulation of
  * Q), "dequant", "quant", "qr_panel", "rayleigh", "elementwise", "graft", "diag" (the
- * diagonal sides' statistic and the both-diagonal precondition).  Host arrays of
+ * diagonal sides' statistic and the both-diagonal precondition), "gemm64" (every float64
+ * product of FP64_REFRESH).  Host arrays of
  * length *count (in: capacity, out: used). */
 SHAMPOO4_API shampoo4_status shampoo4_timing(shampoo4_ctx ctx, int32_t enable);
 SHAMPOO4_API shampoo4_status shampoo4_timing_report(shampoo4_ctx ctx, int32_t* count, const char** names,

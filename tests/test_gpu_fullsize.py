@@ -88,3 +88,21 @@ def test_full_size_sampled(name, first, last, blocks, ncodes):
                         power_iters=wl.power_iters, root_interval=wl.root_interval, root_cache=True,
                         label=f"{name} {first}-{last}", qr="auto", sample=sample, use_step=True,
                         check_from=first, all_sides=_side_checks(shapes, ncodes, seed=len(shapes)))
+
+
+@pytest.mark.timeout(600)
+def test_fp64_refresh_large_4096():
+    """The 4096 stress batch with the float64 statistics update: its rank-32 signal sits on
+    a noise floor near 1e-6 lam_max that float32 does not resolve (the float32 run compares
+    P from the GPU's own root there); in float64 the whole step is compared from the
+    pre-step state where the codes agree.  Every side orthonormal, codes of a sample
+    bit-exact; the first block against the oracle over the first two steps."""
+    require_gpu()
+    wl = get_workload("large_4096")
+    shapes = wl.shapes
+    announce("full size large_4096 fp64: oracle on block 0, steps 1-2")
+    w = _run_teacher_forced(shapes, wl.gradients, 2, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
+                            power_iters=wl.power_iters, root_interval=wl.root_interval, root_cache=True,
+                            label="large_4096 fp64", qr="auto", sample=[0], use_step=True, fp64=True,
+                            all_sides=_side_checks(shapes, 4, seed=len(shapes)))
+    assert w["stat"] <= 1e-12, w

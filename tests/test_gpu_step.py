@@ -42,29 +42,31 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-3
 BUF_ROOT_MAT = 20
 U32 = 2.0 ** -24     # float32 unit roundoff
+U64 = 2.0 ** -53     # float64 unit roundoff
 
 
-def resolved(lam, p):
+def resolved(lam, p, u=U32):
     """Eigenvalues float32 arithmetic determines: a Rayleigh quotient of an order-p
     statistic computed in float32 (and the statistic itself) carries an absolute error
     of up to about p u |L|, so eigenvalues below p u lam_max are not fixed by the
     float32 path: any value in [0, ~2 p u lam_max] is a correct result there, and
     d = (lam + eps)^(-1/4) with it.  Returns (mask of resolved eigenvalues, threshold)."""
     lam = np.asarray(lam, np.float64)
-    thr = p * U32 * float(lam.max()) if lam.size else 0.0
+    thr = p * u * float(lam.max()) if lam.size else 0.0
     return lam > thr, thr
 
 
 def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power_iters=1,
                         root_interval=1, root_cache=False, label="", qr="auto", codebook="ls",
-                        sample=None, all_sides=None, use_step=False, check_from=1):
+                        sample=None, all_sides=None, use_step=False, check_from=1, fp64=False):
     """`sample`: the blocks checked against the oracle (default: every block).
     `all_sides(blocks, t)`: an optional extra check after each statistics update.
     `check_from`: the first step checked; earlier steps run on the GPU only (a long
     schedule is checked in windows, one test each)."""
     from bit_quantized_shampoo_amd import Shampoo4Blocks, Shampoo4Config
     cfg = Shampoo4Config(beta=beta, eps=eps, bjorck_iters=k, power_iters=power_iters,
-                         root_cache=root_cache, qr_schedule=qr, codebook=codebook)
+                         root_cache=root_cache, qr_schedule=qr, codebook=codebook, fp64_refresh=fp64)
+    unit = U64 if fp64 else U32
     announce(f"step parity {label}: init {len(shapes)} blocks")
     blocks = Shampoo4Blocks(shapes, cfg)
     torch.cuda.synchronize()
@@ -112,7 +114,7 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
                 Gs_side = o.side_gradient(Gs[b], s)
                 V = o.rectified_eigenvectors(st["codes"], st["scales"], p, k, 64, codebook)
                 Lt_ref = o.statistics(V, st["lam"], Gs_side, beta)
-                Lt_gpu = blocks.view(b, s, 17).cpu().numpy().astype(np.float64)
+                Lt_gpu = blocks.view(b, s, 21 if fp64 else 17).cpu().numpy().astype(np.float64)
                 # symmetric up to the float32 rounding of the K-scaled products (off-diagonal
                 # tiles are stored mirrored)
                 assert rel_fro(Lt_gpu, Lt_gpu.T) <= 1e-6, (label, t, b, s, "statistic not symmetric")
@@ -122,7 +124,7 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
                 Q_gpu32 = blocks.view(b, s, 18).cpu().numpy()
                 after = blocks.side_state(b, s)
                 lam_gpu = after["lam"].astype(np.float64)
-                Q_gpu = Q_gpu32.astype(np.float64)
+                Q_gpu = blocks.view(b, s, 22).cpu().numpy() if fp64 else Q_gpu32.astype(np.float64)
                 e_rec = rel_fro((Q_gpu * lam_gpu) @ Q_gpu.T, (Q_ref * lam_ref) @ Q_ref.T)
                 e_lam = rel_fro(lam_gpu, lam_ref)
                 assert e_rec <= TOL, (label, t, b, s, "Q diag(lam) Q^T", e_rec)
@@ -137,7 +139,7 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
                 flips[1] += 2 * c_own.size
                 if refresh:
                     d_own = o.root_scaling(lam_ref.astype(np.float32), eps)
-                    mask, thr = resolved(lam_ref, p)
+                    mask, thr = resolved(lam_ref, p, unit)
                     same = bool(np.array_equal(c_own, after["codes"]) and
                                 np.array_equal(s_own.view(np.uint32), after["scales"].view(np.uint32)))
                     new_root[(b, s)] = (c_own, s_own, d_own, mask, thr, same)
@@ -444,7 +446,7 @@ def _run_teacher_forced_fp32(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, 
                 U0, lam0 = before[b][s]
                 V = o.bjorck(U0.astype(np.float64), k)
                 Lt_ref = o.statistics(V, lam0, o.side_gradient(Gs[b], s), beta)
-                Lt_gpu = blocks.view(b, s, 17).cpu().numpy().astype(np.float64)
+                Lt_gpu = blocks.view(b, s, 21 if fp64 else 17).cpu().numpy().astype(np.float64)
                 assert rel_fro(Lt_gpu, Lt_ref) <= TOL, (label, t, b, s, "statistic")
                 Q_ref, lam_ref = o.eigen_refresh(Lt_gpu, V, 1)
                 Q32 = blocks.view(b, s, 18).cpu().numpy()
@@ -637,3 +639,51 @@ def test_step_call_matches_separate_calls(qr):
                         assert np.array_equal(s1[k], s2[k]), (qr, cache, t, b, s_, k)
         one.close()
         sep.close()
+
+
+# ---------------------------------------------------------------------------
+# The float64 statistics update (SHAMPOO4_FLAG_FP64_REFRESH)
+# ---------------------------------------------------------------------------
+
+def test_fp64_refresh_single_64x32_all_steps():
+    """The 64 x 32 workload (rank-deficient on its 64 side for the first step) over its 20
+    steps with the float64 update, as the benchmark runs it; float64 resolves eigenvalues
+    down to about p 2^-53 lam_max, so the whole step is compared from the pre-step state
+    wherever the codes agree."""
+    require_gpu()
+    wl = get_workload("single_64x32")
+    w = _run_teacher_forced(wl.shapes, wl.gradients, wl.steps, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
+                            root_interval=wl.root_interval, root_cache=True, use_step=True, fp64=True,
+                            label="single_64x32 fp64")
+    # the statistic to float64 rounding; d from the pre-step state to about float32's
+    # storage of the eigenvalues (float32 refreshes: within 1e-3 plus the floor's bound)
+    assert w["stat"] <= 1e-12 and w["d"] <= 1e-5, w
+
+
+@pytest.mark.parametrize("shapes,k,T", [
+    ([(1, 1), (2, 3), (5, 1)], 1, 1),
+    ([(40, 72), (33, 33), (100, 7)], 2, 2),
+    ([(1100, 40)], 1, 1),
+    ([(300, 257), (129, 128)], 0, 1),
+])
+def test_fp64_refresh_ragged(shapes, k, T):
+    require_gpu()
+    rng = np.random.default_rng(sum(m * 13 + n for m, n in shapes))
+    scales = [(10.0 ** rng.uniform(-1, 1, (m, 1))) * (10.0 ** rng.uniform(-1, 1, (1, n))) for m, n in shapes]
+
+    def grads(t):
+        r = np.random.default_rng([t, 64, len(shapes)])
+        return [(r.standard_normal((m, n)) * sc).astype(np.float32) for (m, n), sc in zip(shapes, scales)]
+
+    w = _run_teacher_forced(shapes, grads, 4, k=k, root_interval=T, root_cache=True, use_step=True, fp64=True,
+                            label=f"fp64 ragged {shapes}")
+    assert w["stat"] <= 1e-12, w
+
+
+def test_fp64_refresh_single_1024():
+    require_gpu()
+    wl = get_workload("single_1024")
+    w = _run_teacher_forced(wl.shapes, wl.gradients, 11, beta=wl.beta, eps=wl.eps, k=wl.bjorck_iters,
+                            root_interval=wl.root_interval, root_cache=True, use_step=True, fp64=True,
+                            label="single_1024 fp64")
+    assert w["stat"] <= 1e-12, w

@@ -90,7 +90,11 @@ def test_plan_sizes():
     ([(4, 4)], {"k": -1}, L.EINVAL),
     ([(4, 4)], {"k": 17}, L.EINVAL),
     ([(4, 4)], {"pi": 0}, L.EINVAL),
-    ([(4, 4)], {"flags": 128}, L.EINVAL),
+    ([(4, 4)], {"flags": 256}, L.EINVAL),
+    ([(4, 4)], {"flags": L.FLAG_FP64_REFRESH}, L.OK),
+    ([(4, 4)], {"flags": L.FLAG_FP64_REFRESH | L.FLAG_QR_LOOKAHEAD}, L.EINVAL),
+    ([(4, 4)], {"flags": L.FLAG_FP64_REFRESH | L.FLAG_FP32_STATE}, L.EINVAL),
+    ([(4, 4)], {"flags": L.FLAG_FP64_REFRESH | L.FLAG_QR_BLOCKED | L.FLAG_DT_CODEBOOK}, L.OK),
     ([(4, 4)], {"flags": L.FLAG_DT_CODEBOOK}, L.OK),
     ([(4, 4)], {"flags": L.FLAG_DT_CODEBOOK | L.FLAG_FP32_STATE}, L.EINVAL),
     ([(4, 4)], {"flags": L.FLAG_GRAPHS}, L.OK),
