@@ -20,6 +20,7 @@ FLAG_FP32_STATE = 16
 FLAG_GRAPHS = 32
 FLAG_DT_CODEBOOK = 64
 FLAG_FP64_REFRESH = 128
+FLAG_FP32_MFMA = 256
 DIAG_L = 1
 DIAG_R = 2
 CODEBOOK_LINEAR_SQUARE = 0
@@ -36,10 +37,11 @@ EXPORTED = [
     "shampoo4_codebook_ex", "shampoo4_gemm_workspace_bytes",
     "shampoo4_gemm_batched", "shampoo4_timing", "shampoo4_timing_report", "shampoo4_graft",
     "shampoo4_inverse_root_workspace_bytes", "shampoo4_inverse_root", "shampoo4_plan_ex", "shampoo4_init_ex",
-    "shampoo4_gemm_batched_static",
+    "shampoo4_gemm_batched_static", "shampoo4_gemm_batched_ex",
 ]
 
 GRAFT_SGD, GRAFT_ADAM = 0, 1
+GEMM_AUTO, GEMM_FP32, GEMM_X3 = 0, 1, 2
 GEMM_STATIC_MAX = 2048
 
 
@@ -118,6 +120,11 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(vp), ctypes.POINTER(i64), f32, ctypes.POINTER(vp),
                                        ctypes.POINTER(i64), ctypes.POINTER(vp), ctypes.POINTER(i64),
                                        vp, sz, vp]),
+        "shampoo4_gemm_batched_ex": (st, [i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                          ctypes.POINTER(i32), f32, ctypes.POINTER(vp), ctypes.POINTER(i64),
+                                          ctypes.POINTER(vp), ctypes.POINTER(i64), f32, ctypes.POINTER(vp),
+                                          ctypes.POINTER(i64), ctypes.POINTER(vp), ctypes.POINTER(i64),
+                                          vp, sz, vp]),
         "shampoo4_gemm_batched_static": (st, [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                               ctypes.POINTER(i32), f32, ctypes.POINTER(vp), ctypes.POINTER(i64),
                                               ctypes.POINTER(vp), ctypes.POINTER(i64), f32, ctypes.POINTER(vp),

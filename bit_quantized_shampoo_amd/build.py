@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libshampoo4.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["gemm.hip", "codec.hip", "qr.hip", "elementwise.hip", "graft.hip", "newton.hip", "diag.hip",
+SOURCES = ["gemm.hip", "gemm_x3.hip", "codec.hip", "qr.hip", "elementwise.hip", "graft.hip", "newton.hip", "diag.hip",
            "scratch.hip", "gemm64.hip", "qr64.hip", "runtime.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -29,7 +29,7 @@
 //  * split K for long-K, few-tile products: chunk s of the K range writes its own
 //    partial slab and the consuming product sums the slabs while loading its
 //    operand tiles (a fixed order, so results are deterministic).
-#include "kernels.hpp"
+#include "gemm_common.hpp"
 
 namespace s4 {
 
@@ -49,14 +49,6 @@ struct Tile {
     static constexpr int B_MAX = B_KC > B_MC ? B_KC : B_MC;
     static constexpr int RED = WM * BN;        // COLDOT cross-wave partials
 };
-
-// Operand loads are branch-free: every address is clamped into the operand and
-// out-of-range elements are zeroed with an AND on the loaded bits.  (A select on a
-// loaded value is turned into a branch around the load with a wait for it inside,
-// which serializes the loads of a tile.)
-__device__ __forceinline__ float keep_if(float v, bool keep) {
-    return __uint_as_float(__float_as_uint(v) & (keep ? 0xffffffffu : 0u));
-}
 
 // Elements (row, col..col+3) of a rows x cols operand (rows, cols >= 1) are loaded in
 // two phases so that a slice's loads stay in flight across the matrix-core work of the
@@ -126,22 +118,9 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
     constexpr int RA = (NQA + 255) / 256;
     constexpr int RB = (NQB + 255) / 256;
 
-    const int tiles_m = dsc.tiles_m;
+    int ks, tile_m, tile_n;
+    decode_tile<BM, BN>(dsc, t, ks, tile_m, tile_n);
     const bool sym = (dsc.flags & GEMM_F_SYM) != 0;
-    const int tiles_mn = sym ? tiles_m * (tiles_m + 1) / 2 : tiles_m * ((dsc.N + BN - 1) / BN);
-    const int ks = t / tiles_mn;                 // split-K chunk (0 without split)
-    const int tmn = t - ks * tiles_mn;
-    int tile_m, tile_n;
-    if (sym) {   // upper triangle, column by column: tmn = tn (tn + 1) / 2 + tm with tm <= tn
-        int tn = (int)((sqrtf(8.f * (float)tmn + 1.f) - 1.f) * 0.5f);
-        while ((tn + 1) * (tn + 2) / 2 <= tmn) ++tn;
-        while (tn * (tn + 1) / 2 > tmn) --tn;
-        tile_n = tn;
-        tile_m = tmn - tn * (tn + 1) / 2;
-    } else {
-        tile_m = tmn % tiles_m;
-        tile_n = tmn / tiles_m;
-    }
     const bool mirror = (BM == BN) && sym && tile_m != tile_n;   // square tiles only
     const int row0 = tile_m * BM;
     const int col0 = tile_n * BN;
@@ -380,113 +359,7 @@ __device__ __forceinline__ void gemm_body(const GemmDesc& dsc, int t, const IoEn
         (void)NACC;
     }
 
-    // Epilogue.  Accumulator register r of lane (h, l32) holds
-    // row 8*(r/4) + 4*h + (r%4), column l32 of its 32x32 block.
-    const float alpha = dsc.alpha, beta = dsc.beta;
-    const float* __restrict__ C = dsc.C;
-    const int64_t ldc = dsc.ldc;
-
-    if (dsc.flags & GEMM_F_COLDOT) {
-        // LDS is free after the final barrier of the K loop: reuse As for partials
-        float* red = As;
-#pragma unroll
-        for (int n = 0; n < TN; ++n) {
-            const int lcol = wave_n * TN * 32 + n * 32 + l32;
-            const int col = col0 + lcol;
-            float s = 0.f;
-            const int colc = min(col, N - 1);
-#pragma unroll
-            for (int m = 0; m < TM; ++m) {
-                float cv[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                    cv[r] = ldg(C + (int64_t)min(row, M - 1) * ldc + colc);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                    s += acc[m][n][r] * keep_if(cv[r], row < M && col < N);
-                }
-                __builtin_amdgcn_sched_barrier(0);   // one 32 x 32 block's C values live at a time
-            }
-            s += __shfl_xor(s, 32);
-            if (h == 0) red[wave_m * BN + lcol] = s;
-        }
-        __syncthreads();
-        if (wave_m == 0 && h == 0) {
-#pragma unroll
-            for (int n = 0; n < TN; ++n) {
-                const int lcol = wave_n * TN * 32 + n * 32 + l32;
-                const int col = col0 + lcol;
-                float s = 0.f;
-#pragma unroll
-                for (int w = 0; w < WM; ++w) s += red[w * BN + lcol];
-                if (col < N) stg(D + (int64_t)tile_m * ldd + col, alpha * s);
-            }
-        }
-        return;
-    }
-
-    const float* __restrict__ rs = dsc.rscale;
-    const float* __restrict__ cs = dsc.cscale;
-    // the C, row-scale and column-scale values of a 32 x 32 block are loaded (clamped
-    // addresses) before any is used, absent ones from D in their place and replaced by
-    // bit masks; stores are predicated on the bounds
-    const float* __restrict__ cp = (beta != 0.f) ? C : D;
-    const int64_t ldcp = (beta != 0.f) ? ldc : ldd;
-    const float* __restrict__ rsp = rs ? rs : D;
-    const uint32_t rsm = rs ? 0xffffffffu : 0u;
-    const float* __restrict__ csp = cs ? cs : D;
-    const uint32_t csm = cs ? 0xffffffffu : 0u;
-#pragma unroll
-    for (int n = 0; n < TN; ++n) {
-        const int col = col0 + wave_n * TN * 32 + n * 32 + l32;
-        const int colc = min(col, N - 1);
-        const float csv = __uint_as_float((__float_as_uint(ldg(csp + colc)) & csm) | (0x3f800000u & ~csm));
-#pragma unroll
-        for (int m = 0; m < TM; ++m) {
-            float cv[16], rv[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                const int rowc = min(row, M - 1);
-                cv[r] = keep_if(ldg(cp + (int64_t)rowc * ldcp + colc), beta != 0.f);
-                rv[r] = __uint_as_float((__float_as_uint(ldg(rsp + rowc)) & rsm) | (0x3f800000u & ~rsm));
-            }
-            float v[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = row0 + wave_m * TM * 32 + m * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-                v[r] = fmaf(beta, cv[r], alpha * acc[m][n][r] * rv[r] * csv);
-                if (row < M && col < N) stg(D + (int64_t)row * ldd + col, v[r]);
-            }
-            if (mirror) {
-                // the transposed block through a per-wave LDS tile (both operand buffers are
-                // free after the K loop's last barrier), stored with one row per half-wave
-                float* tl = (wv < 2 ? As : Bs) + (wv & 1) * (32 * 33);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) tl[((r >> 2) * 8 + h * 4 + (r & 3)) * 33 + l32] = v[r];
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                const int r0b = row0 + wave_m * TM * 32 + m * 32;
-                const int c0b = col0 + wave_n * TN * 32 + n * 32;
-#pragma unroll
-                for (int s = 0; s < 16; ++s) {
-                    const int g = 2 * s + h;                    // column of the block -> row of D
-                    const float tv = tl[l32 * 33 + g];
-                    if (c0b + g < M && r0b + l32 < N) stg(D + (int64_t)(c0b + g) * ldd + r0b + l32, tv);
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            }
-            // one 32 x 32 block at a time: keeps the next block's loads from being
-            // hoisted here (their registers would cap the kernel's occupancy)
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
+    gemm_epilogue<WM, WN, TM, TN>(acc, dsc, D, ldd, tile_m, row0, col0, mirror, As, Bs, tid);
 }
 
 // The mirrored-store tiles of GEMM_F_SYM: two 32 x 33 tiles in each operand buffer.
@@ -582,19 +455,23 @@ hipError_t launch_cfg(int mode, bool vec, bool slab, const GemmDesc* descs, cons
 
 bool gemm_vec_ok(const GemmDesc& d) {
     const bool ta = d.flags & GEMM_F_TA, tb = d.flags & GEMM_F_TB;
-    auto ok = [](const void* p, int64_t ld, int64_t extent, int nslab, int64_t slab) {
+    // (the bf16 split kernel also needs each operand to span less than 2 GiB: its buffer
+    // loads take 32-bit offsets)
+    auto ok = [](const void* p, int64_t ld, int64_t rows, int64_t extent, int nslab, int64_t slab) {
         return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && (ld & 3) == 0 && (extent & 3) == 0 &&
-               (nslab <= 1 || (slab & 3) == 0);
+               (nslab <= 1 || (slab & 3) == 0) && (rows - 1) * ld + extent < (int64_t(1) << 29);
     };
     const int64_t ea = ta ? d.M : d.K, eb = tb ? d.K : d.N;
-    const bool a = d.a_io >= 0 ? (ea & 3) == 0 : ok(d.A, d.lda, ea, d.anslab, d.aslab);
-    const bool b = d.b_io >= 0 ? (eb & 3) == 0 : ok(d.B, d.ldb, eb, d.bnslab, d.bslab);
+    const int64_t ra = ta ? d.K : d.M, rb = tb ? d.N : d.K;
+    const bool a = d.a_io >= 0 ? (ea & 3) == 0 : ok(d.A, d.lda, ra, ea, d.anslab, d.aslab);
+    const bool b = d.b_io >= 0 ? (eb & 3) == 0 : ok(d.B, d.ldb, rb, eb, d.bnslab, d.bslab);
     return a && b;
 }
 
 void gemm_tile_dims(int cfg, int* bm, int* bn) {
     switch (cfg) {
         case GEMM_128x128: *bm = 128; *bn = 128; break;
+        case GEMM_X3: *bm = GEMM_X3_BM; *bn = GEMM_X3_BN; break;
         case GEMM_64x64:
         case GEMM_64x64_K2: *bm = 64; *bn = 64; break;
         case GEMM_128x32: *bm = 128; *bn = 32; break;
@@ -602,11 +479,14 @@ void gemm_tile_dims(int cfg, int* bm, int* bn) {
     }
 }
 
-hipError_t launch_gemm(int cfg, int mode, bool vec, bool slab, const GemmDesc* descs, const int* prefix,
-                       int ndesc, int ntiles, const IoEntry* io, hipStream_t stream) {
+hipError_t launch_gemm(int cfg, int mode, bool vec, bool slab, bool kscale, const GemmDesc* descs,
+                       const int* prefix, int ndesc, int ntiles, const IoEntry* io, hipStream_t stream) {
     if (ntiles <= 0) return hipSuccess;
     switch (cfg) {
         case GEMM_128x128: return launch_cfg<2, 2, 2, 2>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
+        case GEMM_X3:
+            if (slab) return hipErrorInvalidValue;
+            return launch_gemm_x3(mode, vec, kscale, descs, prefix, ndesc, ntiles, io, stream);
         case GEMM_64x64: return launch_cfg<2, 2, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
         case GEMM_64x64_K2:   // (the K groups need 16-byte loads: a per-call caller operand may deny them)
             if (!vec || slab) return launch_cfg<2, 2, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);

@@ -66,6 +66,7 @@ struct Launch {
     int strm = 0;        // 0: the caller's stream, 1: the context's second stream
     bool vec = false;    // GEMM: 16-byte operand loads (io operands: also checked per call)
     bool slab = false;   // GEMM: some operand sums split-K slabs
+    bool kscale = false; // GEMM: some product scales op(B)'s rows
     bool uses_io = false;
     bool f32in = false;  // fp64 GEMM: float operands (the gradients)
     int ev = -1;         // K_RECORD / K_WAIT: index of the context's synchronization event
@@ -143,6 +144,7 @@ struct shampoo4_ctx_s {
     // variant: with or without the cached rectified eigenvectors, and with or without
     // 16-byte loads of the gradients, which the captured kernels bake in)
     bool use_graphs = false;
+    bool x3 = true;                       // 128 x 128 products on the three-piece bf16 kernel
     bool graph_ok = true;
     hipStream_t cap = nullptr;
     hipGraphExec_t stats_graph[2][2] = {};
@@ -307,8 +309,9 @@ struct shampoo4_ctx_s {
         return gemm_launch(items, fam, default_cfg(items));
     }
 
-    // One launch of `items` on tile shape cfgsel.
-    Seq gemm_launch(const std::vector<GemmItem>& items, int fam, int cfgsel) {
+    // One launch of `items` on tile shape cfgsel (128 x 128: on the three-piece bf16 kernel
+    // unless allow_x3 is false or the context keeps the fp32 matrix cores).
+    Seq gemm_launch(const std::vector<GemmItem>& items, int fam, int cfgsel, bool allow_x3 = true) {
         std::vector<GemmDesc> ds;
         int modes = 0, first_mode = -2;
         for (auto& it : items) {
@@ -321,6 +324,10 @@ struct shampoo4_ctx_s {
             ds.push_back(d);
         }
         if (ds.empty()) return {};
+        // the three-piece bf16 kernel takes the 128 x 128 launches without split-K slab sums
+        bool slab = false;
+        for (auto& d : ds) slab = slab || d.anslab > 1 || d.bnslab > 1;
+        if (cfgsel == GEMM_128x128 && x3 && allow_x3 && !slab) cfgsel = GEMM_X3;
         int bm, bn;
         gemm_tile_dims(cfgsel, &bm, &bn);
         // a symmetric product computes the tiles on and above the diagonal (square tiles,
@@ -352,6 +359,7 @@ struct shampoo4_ctx_s {
         for (auto& d : ds) {
             L.vec = L.vec && gemm_vec_ok(d);
             L.slab = L.slab || d.anslab > 1 || d.bnslab > 1;
+            L.kscale = L.kscale || d.kscale != nullptr;
             L.uses_io = L.uses_io || d.a_io >= 0 || d.b_io >= 0;
         }
         L.kind = K_GEMM;
@@ -398,6 +406,7 @@ struct shampoo4_ctx_s {
         codebook = (cfg.flags & SHAMPOO4_FLAG_DT_CODEBOOK) ? SHAMPOO4_CODEBOOK_DYNAMIC_TREE
                                                            : SHAMPOO4_CODEBOOK_LINEAR_SQUARE;
         use_graphs = (cfg.flags & SHAMPOO4_FLAG_GRAPHS) != 0;
+        x3 = (cfg.flags & SHAMPOO4_FLAG_FP32_MFMA) == 0;
         // Large batches are throughput-bound: reflectors go to the trailing matrix 128
         // columns at a time.  Small ones are bound by the chain of panels and by launch
         // latency: panel-wide updates on the caller's stream (or, on request, with the
@@ -1295,10 +1304,16 @@ struct shampoo4_ctx_s {
             root_mat = make_gemm(rm, FAM_GEMM_PRECOND);
             pre_cached[0] = make_gemm(q1, FAM_GEMM_PRECOND);
             pre_cached[1] = make_gemm(q2, FAM_GEMM_PRECOND);
-            pre_side[0] = gemm_launch(q1, FAM_GEMM_PRECOND, GEMM_128x128);
-            pre_side[1] = gemm_launch(q2, FAM_GEMM_PRECOND, GEMM_128x128);
             // both forms sum each output over K in the same order (one group of waves
-            // per tile, whatever its shape), so P is bit-identical whichever runs
+            // per tile, whatever its shape, on the same kind of matrix core), so P is
+            // bit-identical whichever runs
+            auto all_x3 = [](const Seq& sq) {
+                bool all = !sq.empty();
+                for (auto& L : sq) all = all && L.cfg == GEMM_X3;
+                return all;
+            };
+            pre_side[0] = gemm_launch(q1, FAM_GEMM_PRECOND, GEMM_128x128, all_x3(pre_cached[0]));
+            pre_side[1] = gemm_launch(q2, FAM_GEMM_PRECOND, GEMM_128x128, all_x3(pre_cached[1]));
             for (auto& sq : pre_cached)
                 for (auto& L : sq)
                     if (L.cfg == GEMM_64x64_K2) L.cfg = GEMM_64x64;
@@ -1638,7 +1653,7 @@ struct shampoo4_ctx_s {
         const int fam = L.fam;
         switch (L.kind) {
             case K_GEMM:
-                e = launch_gemm(L.cfg, L.mode, L.vec && (!L.uses_io || io_vec), L.slab,
+                e = launch_gemm(L.cfg, L.mode, L.vec && (!L.uses_io || io_vec), L.slab, L.kscale,
                                 reinterpret_cast<const GemmDesc*>(base + L.desc_off), prefix, L.ndesc, L.ntiles,
                                 io, s);
                 break;
@@ -1774,7 +1789,8 @@ struct shampoo4_ctx_s {
     hipError_t upload_io(const shampoo4_io* io, hipStream_t s) {
         io_vec = true;
         for (int b = 0; b < nb; ++b)
-            io_vec = io_vec && (reinterpret_cast<uintptr_t>(io[b].G) & 15) == 0 && (io[b].ldg & 3) == 0;
+            io_vec = io_vec && (reinterpret_cast<uintptr_t>(io[b].G) & 15) == 0 && (io[b].ldg & 3) == 0 &&
+                     (int64_t)(shapes[b].m - 1) * io[b].ldg + shapes[b].n < (int64_t(1) << 29);
         return upload_table(io, io_off, s);
     }
 
@@ -1936,7 +1952,7 @@ shampoo4_status validate_cfg(const shampoo4_config* cfg) {
     if (cfg->power_iters < 1 || cfg->power_iters > 8) return SHAMPOO4_EINVAL;
     if (cfg->flags & ~(SHAMPOO4_FLAG_ROOT_CACHE | SHAMPOO4_FLAG_KEEP_STATE | SHAMPOO4_FLAG_QR_BLOCKED |
                        SHAMPOO4_FLAG_QR_LOOKAHEAD | SHAMPOO4_FLAG_FP32_STATE | SHAMPOO4_FLAG_GRAPHS |
-                       SHAMPOO4_FLAG_DT_CODEBOOK | SHAMPOO4_FLAG_FP64_REFRESH))
+                       SHAMPOO4_FLAG_DT_CODEBOOK | SHAMPOO4_FLAG_FP64_REFRESH | SHAMPOO4_FLAG_FP32_MFMA))
         return SHAMPOO4_EINVAL;
     if ((cfg->flags & SHAMPOO4_FLAG_DT_CODEBOOK) && (cfg->flags & SHAMPOO4_FLAG_FP32_STATE))
         return SHAMPOO4_EINVAL;
@@ -2322,12 +2338,15 @@ namespace {
 // Validates a batched product and plans its single launch: `tmp.blob` then holds the
 // descriptor table and tile prefix (offsets in `L` relative to the blob's start); `L.ntiles`
 // is 0 when there is nothing to compute.
-shampoo4_status plan_gemm_batched(int32_t count, int32_t transA, int32_t transB, const int32_t* M,
+shampoo4_status plan_gemm_batched(int32_t kernel, int32_t count, int32_t transA, int32_t transB, const int32_t* M,
                                   const int32_t* N, const int32_t* K, float alpha, const float* const* A,
                                   const int64_t* lda, const float* const* B, const int64_t* ldb, float beta,
                                   const float* const* C, const int64_t* ldc, float* const* D, const int64_t* ldd,
                                   shampoo4_ctx_s& tmp, Launch& L) {
     L = Launch{};
+    if (kernel != SHAMPOO4_GEMM_AUTO && kernel != SHAMPOO4_GEMM_FP32 && kernel != SHAMPOO4_GEMM_X3)
+        return SHAMPOO4_EINVAL;
+    tmp.x3 = kernel != SHAMPOO4_GEMM_FP32;
     if (count < 0) return SHAMPOO4_EINVAL;
     if (count == 0) return SHAMPOO4_OK;
     if (!M || !N || !K || !A || !lda || !B || !ldb || !D || !ldd) return SHAMPOO4_EINVAL;
@@ -2349,7 +2368,8 @@ shampoo4_status plan_gemm_batched(int32_t count, int32_t transA, int32_t transB,
     }
     // one launch: one descriptor table and one tile prefix (the tile shape follows the
     // products' class when they all share one)
-    Seq seq = tmp.make_gemm(items, FAM_GEMM_PRECOND);
+    Seq seq = kernel == SHAMPOO4_GEMM_X3 ? tmp.gemm_launch(items, FAM_GEMM_PRECOND, GEMM_128x128)
+                                         : tmp.make_gemm(items, FAM_GEMM_PRECOND);
     if (seq.size() > 1) {
         tmp.blob.clear();
         seq = tmp.make_gemm(items, FAM_GEMM_PRECOND, false, false);
@@ -2362,7 +2382,7 @@ shampoo4_status plan_gemm_batched(int32_t count, int32_t transA, int32_t transB,
 shampoo4_status run_gemm_batched(const shampoo4_ctx_s& tmp, const Launch& L, uint8_t* dev, hipStream_t s) {
     if (hipMemcpyAsync(dev, tmp.blob.data(), tmp.blob.size(), hipMemcpyHostToDevice, s) != hipSuccess)
         return SHAMPOO4_EHIP;
-    hipError_t e = launch_gemm(L.cfg, L.mode, L.vec, L.slab, reinterpret_cast<const GemmDesc*>(dev + L.desc_off),
+    hipError_t e = launch_gemm(L.cfg, L.mode, L.vec, L.slab, L.kscale, reinterpret_cast<const GemmDesc*>(dev + L.desc_off),
                                reinterpret_cast<const int*>(dev + L.prefix_off), L.ndesc, L.ntiles, nullptr, s);
     return e == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
@@ -2377,6 +2397,16 @@ shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t tra
                                       const float* const* C, const int64_t* ldc, float* const* D,
                                       const int64_t* ldd, void* workspace, size_t workspace_bytes,
                                       void* stream) {
+    return shampoo4_gemm_batched_ex(SHAMPOO4_GEMM_AUTO, count, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta,
+                                    C, ldc, D, ldd, workspace, workspace_bytes, stream);
+}
+
+shampoo4_status shampoo4_gemm_batched_ex(int32_t kernel, int32_t count, int32_t transA, int32_t transB,
+                                         const int32_t* M, const int32_t* N, const int32_t* K, float alpha,
+                                         const float* const* A, const int64_t* lda, const float* const* B,
+                                         const int64_t* ldb, float beta, const float* const* C, const int64_t* ldc,
+                                         float* const* D, const int64_t* ldd, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
     if (count > 0) {
         if (!workspace) return SHAMPOO4_EINVAL;
         if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return SHAMPOO4_EALIGN;
@@ -2384,8 +2414,8 @@ shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA, int32_t tra
     }
     shampoo4_ctx_s tmp;
     Launch L;
-    shampoo4_status st = plan_gemm_batched(count, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-                                           D, ldd, tmp, L);
+    shampoo4_status st = plan_gemm_batched(kernel, count, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                           ldc, D, ldd, tmp, L);
     if (st != SHAMPOO4_OK || L.ntiles <= 0) return st;
     // the descriptors and their tile prefix sit at the start of the caller's workspace
     if (tmp.blob.size() > workspace_bytes) return SHAMPOO4_ESMALLBUF;
@@ -2401,8 +2431,8 @@ shampoo4_status shampoo4_gemm_batched_static(int32_t count, int32_t transA, int3
     if (count > SHAMPOO4_GEMM_STATIC_MAX) return SHAMPOO4_ESMALLBUF;
     shampoo4_ctx_s tmp;
     Launch L;
-    shampoo4_status st = plan_gemm_batched(count, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-                                           D, ldd, tmp, L);
+    shampoo4_status st = plan_gemm_batched(SHAMPOO4_GEMM_AUTO, count, transA, transB, M, N, K, alpha, A, lda, B, ldb,
+                                           beta, C, ldc, D, ldd, tmp, L);
     if (st != SHAMPOO4_OK || L.ntiles <= 0) return st;
     if (tmp.blob.size() > GEMM_STATIC_SCRATCH_BYTES) return SHAMPOO4_ESMALLBUF;
     void* scr = nullptr;   // this device's array (its address looked up at the first call)

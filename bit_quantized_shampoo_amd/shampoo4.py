@@ -60,6 +60,7 @@ class Shampoo4Config:
     graphs: bool = False            # replay update_stats from a captured HIP graph
     codebook: str = "ls"            # 4-bit codebook of U: "ls" linear-square, "dt" dynamic tree
     fp64_refresh: bool = False      # statistics update (Bjorck .. Rayleigh quotients) in float64
+    fp32_mfma: bool = False         # every product on the fp32 matrix cores (no three-piece bf16 split)
 
     def c(self, keep_state: bool = False) -> L.Config:
         flags = (L.FLAG_ROOT_CACHE if self.root_cache else 0) | (L.FLAG_KEEP_STATE if keep_state else 0)
@@ -73,6 +74,8 @@ class Shampoo4Config:
         flags |= {"ls": 0, "dt": L.FLAG_DT_CODEBOOK}[self.codebook]
         if self.fp64_refresh:
             flags |= L.FLAG_FP64_REFRESH
+        if self.fp32_mfma:
+            flags |= L.FLAG_FP32_MFMA
         return L.Config(self.beta, self.eps, self.qblock, self.bjorck_iters, self.power_iters, flags)
 
 
@@ -310,8 +313,14 @@ def codebook(name: str = "ls"):
 
 
 def gemm_batched(As, Bs, Ds=None, transA=False, transB=False, alpha=1.0, beta=0.0, Cs=None,
-                 workspace: torch.Tensor | None = None, stream=None):
-    """D_i = alpha op(A_i) op(B_i) + beta C_i on the MFMA kernel (row-major 2-D tensors)."""
+                 workspace: torch.Tensor | None = None, stream=None, kernel: str = "auto"):
+    """D_i = alpha op(A_i) op(B_i) + beta C_i on the MFMA kernels (row-major 2-D tensors).
+    kernel: "auto" (tile shape by batch; 128 x 128 launches on the three-piece bf16 kernel),
+    "fp32" (fp32 matrix cores only) or "x3" (128 x 128 tiles on the three-piece bf16 kernel
+    whatever the batch)."""
+    kinds = {"auto": L.GEMM_AUTO, "fp32": L.GEMM_FP32, "x3": L.GEMM_X3}
+    if kernel not in kinds:
+        raise ValueError(f"kernel must be one of {sorted(kinds)}")
     count = len(As)
     Ms, Ns, Ks = [], [], []
     for A, B in zip(As, Bs):
@@ -335,12 +344,12 @@ def gemm_batched(As, Bs, Ds=None, transA=False, transB=False, alpha=1.0, beta=0.
         workspace = torch.empty(need, dtype=torch.uint8, device=As[0].device)
     C_ptrs = vp(*[_ptr(c) for c in Cs]) if Cs else None
     C_ld = i64(*[c.stride(0) for c in Cs]) if Cs else None
-    L.check(L.lib().shampoo4_gemm_batched(
-        count, int(transA), int(transB), i32(*Ms), i32(*Ns), i32(*Ks), alpha,
+    L.check(L.lib().shampoo4_gemm_batched_ex(
+        kinds[kernel], count, int(transA), int(transB), i32(*Ms), i32(*Ns), i32(*Ks), alpha,
         vp(*[_ptr(a) for a in As]), i64(*[a.stride(0) for a in As]),
         vp(*[_ptr(b) for b in Bs]), i64(*[b.stride(0) for b in Bs]), beta, C_ptrs, C_ld,
         vp(*[_ptr(d) for d in Ds]), i64(*[d.stride(0) for d in Ds]),
-        _ptr(workspace), workspace.numel(), _stream_ptr(stream)), "shampoo4_gemm_batched")
+        _ptr(workspace), workspace.numel(), _stream_ptr(stream)), "shampoo4_gemm_batched_ex")
     return Ds, workspace
 
 

@@ -1,6 +1,8 @@
-"""The fp32 MFMA GEMM kernel in isolation against float64 NumPy products:
-every transpose mode, every tile shape (chosen by batch size), ragged edges,
-strided operands, alpha/beta."""
+"""The matrix-product kernels in isolation against float64 NumPy products: the fp32
+matrix-core kernel (every tile shape, chosen by batch size) and the three-piece bf16
+kernel (forced onto 128 x 128 tiles whatever the batch), every transpose mode, ragged
+edges, strided and unaligned operands, alpha/beta.  Both must meet the fp32 bound
+4 eps |A||B| sqrt(K + 1) elementwise."""
 
 import numpy as np
 import pytest
@@ -30,6 +32,7 @@ def _check(As, Bs, Ds, ta, tb, alpha, beta, Cs):
         assert np.all(err <= bound), (i, float(np.max(err / bound)))
 
 
+@pytest.mark.parametrize("kernel", ["auto", "fp32", "x3"])
 @pytest.mark.parametrize("ta", [False, True])
 @pytest.mark.parametrize("tb", [False, True])
 @pytest.mark.parametrize("shapes", [
@@ -41,6 +44,7 @@ def _check(As, Bs, Ds, ta, tb, alpha, beta, Cs):
     [(256, 256, 256)] * 3,
     [(1024, 1024, 1024)],                 # single large product
     [(1024, 1024, 1024)] * 2,             # two large products
+    [(1024, 1024, 1024)] * 8,             # 512 tiles of 128 x 128: auto takes the bf16 split
     [(1000, 600, 77)] * 6,                # ragged edges on both sides
     [(32, 1000, 700)] * 2,                # skinny M
     [(1000, 32, 700)] * 2,                # skinny N (128 x 32 tiles)
@@ -48,7 +52,7 @@ def _check(As, Bs, Ds, ta, tb, alpha, beta, Cs):
     [(700, 17, 33)] * 3,                  # skinny N with unaligned rows
     [(48, 60, 300)] * 3,                  # sides under 64 (64 x 64 tiles)
 ])
-def test_gemm_modes(ta, tb, shapes):
+def test_gemm_modes(kernel, ta, tb, shapes):
     require_gpu()
     from bit_quantized_shampoo_amd import gemm_batched
     rng = np.random.default_rng(hash((ta, tb, len(shapes), shapes[0])) % (2 ** 32))
@@ -58,13 +62,14 @@ def test_gemm_modes(ta, tb, shapes):
         B = rng.standard_normal((N, K) if tb else (K, N)).astype(np.float32)
         As.append(to_dev(A))
         Bs.append(to_dev(B))
-    announce(f"gemm ta={ta} tb={tb} shapes={shapes}")
-    Ds, _ = gemm_batched(As, Bs, transA=ta, transB=tb)
+    announce(f"gemm kernel={kernel} ta={ta} tb={tb} shapes={shapes}")
+    Ds, _ = gemm_batched(As, Bs, transA=ta, transB=tb, kernel=kernel)
     torch.cuda.synchronize()
     _check(As, Bs, Ds, ta, tb, 1.0, 0.0, None)
 
 
-def test_gemm_alpha_beta_and_strides():
+@pytest.mark.parametrize("kernel", ["auto", "x3"])
+def test_gemm_alpha_beta_and_strides(kernel):
     require_gpu()
     from bit_quantized_shampoo_amd import gemm_batched
     rng = np.random.default_rng(7)
@@ -73,15 +78,15 @@ def test_gemm_alpha_beta_and_strides():
     B = to_dev(rng.standard_normal((80, 90)).astype(np.float32))
     C = to_dev(rng.standard_normal((100, 90)).astype(np.float32))
     D = torch.empty((100, 90), dtype=torch.float32, device="cuda")
-    announce("gemm alpha/beta strided")
-    gemm_batched([A], [B], [D], alpha=-0.5, beta=1.5, Cs=[C])
+    announce(f"gemm alpha/beta strided kernel={kernel}")
+    gemm_batched([A], [B], [D], alpha=-0.5, beta=1.5, Cs=[C], kernel=kernel)
     torch.cuda.synchronize()
     _check([A], [B], [D], False, False, -0.5, 1.5, [C])
     # K = 0 gives beta * C
     A0 = big[5:105, 3:3]          # [100, 0] view with a valid base pointer
     B0 = B[:0, :]                 # [0, 90]
     D0 = torch.empty((100, 90), dtype=torch.float32, device="cuda")
-    announce("gemm K=0")
-    gemm_batched([A0], [B0], [D0], alpha=1.0, beta=2.0, Cs=[C])
+    announce(f"gemm K=0 kernel={kernel}")
+    gemm_batched([A0], [B0], [D0], alpha=1.0, beta=2.0, Cs=[C], kernel=kernel)
     torch.cuda.synchronize()
     assert torch.equal(D0, 2.0 * C)

@@ -446,7 +446,7 @@ def _run_teacher_forced_fp32(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, 
                 U0, lam0 = before[b][s]
                 V = o.bjorck(U0.astype(np.float64), k)
                 Lt_ref = o.statistics(V, lam0, o.side_gradient(Gs[b], s), beta)
-                Lt_gpu = blocks.view(b, s, 21 if fp64 else 17).cpu().numpy().astype(np.float64)
+                Lt_gpu = blocks.view(b, s, 17).cpu().numpy().astype(np.float64)
                 assert rel_fro(Lt_gpu, Lt_ref) <= TOL, (label, t, b, s, "statistic")
                 Q_ref, lam_ref = o.eigen_refresh(Lt_gpu, V, 1)
                 Q32 = blocks.view(b, s, 18).cpu().numpy()
