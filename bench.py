@@ -26,7 +26,10 @@ if ROOT not in sys.path:
 
 METRIC = "preconditioned block-steps/sec + GEMM TFLOP/s (% MFMA peak), quant GB/s (% HBM)"
 PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_BF16_MFMA_TFLOPS = 2500.0
 PEAK_FP64_MFMA_TFLOPS = 78.6
+# the three-piece bf16 product runs six bf16 matrix-core products per fp32 product
+X3_PRODUCTS = 6
 PEAK_HBM_GBPS = 8000.0
 # fp32 vector peak of the code as built: packed fp32 instructions are disabled, so a CU
 # retires 64 fp32 FMAs (128 flops) per clock: 256 CUs x 2.4 GHz x 128 = 78.6 TFLOP/s
@@ -44,7 +47,8 @@ def log(msg: str):
 
 # kernel families of the roofline: timing-report families -> (kernel-name test, source file)
 FAMILIES = {
-    "gemm": (lambda n: "gemm_kernel" in n, "gemm.hip"),
+    "gemm_fp32": (lambda n: "gemm_kernel" in n, "gemm.hip"),
+    "gemm_x3": (lambda n: "gemm_x3_kernel" in n, "gemm_x3.hip"),
     "gemm64": (lambda n: "gemm64_kernel" in n, "gemm64.hip"),
     "qr_panel": (lambda n: ("panel_" in n and "_kernel" in n) or "qr_step_kernel" in n, "qr.hip"),
     "qr_panel64": (lambda n: "panel64_kernel" in n, "qr64.hip"),
@@ -220,8 +224,9 @@ def summarize_kernels(workload: str, outdir: str):
 def summarize_mfma(workload: str, outdir: str):
     """profiles/mfma_<workload>.md: matrix-core use of the GEMM kernels from one rocprofv3
     --pmc run (SQ_INSTS_MFMA, SQ_VALU_MFMA_BUSY_CYCLES) with its kernel trace: per dispatch
-    the MFMA instructions (4096 flops each: v_mfma_f32_32x32x2_f32, 32 x 32 x 2 per wave)
-    over the dispatch time, and the busy cycles over SIMDs x dispatch cycles at 2.4 GHz."""
+    the MFMA instructions over the dispatch time (4096 flops per v_mfma_f32_32x32x2_f32 of
+    the fp32 kernel, 32768 per v_mfma_f32_32x32x16_bf16 of the three-piece kernel), and the
+    busy cycles over SIMDs x dispatch cycles at 2.4 GHz."""
     import csv
     from collections import defaultdict
     run = os.path.join(outdir, f"pmc_mfma_{workload}")
@@ -236,17 +241,20 @@ def summarize_mfma(workload: str, outdir: str):
         per[r["Dispatch_Id"]][r["Counter_Name"]] = per[r["Dispatch_Id"]].get(r["Counter_Name"], 0.0) + \
             float(r["Counter_Value"])
         names[r["Dispatch_Id"]] = r["Kernel_Name"]
-    agg = defaultdict(lambda: [0, 0.0, 0.0, 0.0])   # dispatches, ns, instructions, busy cycles
+    inst_flops = {"gemm_fp32": 4096.0, "gemm_x3": 32768.0}
+    peaks = {"gemm_fp32": PEAK_FP32_MFMA_TFLOPS, "gemm_x3": PEAK_BF16_MFMA_TFLOPS}
+    agg = defaultdict(lambda: [0, 0.0, 0.0, 0.0, None])   # dispatches, ns, instructions, busy cycles, family
     for d, c in per.items():
-        if _family_of(names[d]) != "gemm" or d not in dur:
+        fam = _family_of(names[d])
+        if fam not in inst_flops or d not in dur:
             continue
-        key = _short_kernel_name(names[d])
-        for k in (key, "all gemm"):
+        for k in (_short_kernel_name(names[d]), f"all {fam}"):
             a = agg[k]
             a[0] += 1
             a[1] += dur[d]
             a[2] += c.get("SQ_INSTS_MFMA", 0.0)
             a[3] += c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+            a[4] = fam
     out = [f"# Matrix-core use of the GEMM kernels — `{workload}` bench", "",
            "Commands (from the repository root, on one MI355X):", "", "```",
            "cd /tmp && export TMPDIR=/tmp",
@@ -254,16 +262,20 @@ def summarize_mfma(workload: str, outdir: str):
            f"-d <repo>/gpurun_out/pmc_mfma_{workload} -o run -- python3 <repo>/bench.py --config {workload} "
            f"--steps 1 --warmup 0 --no-cpu",
            f"python3 <repo>/bench.py --summarize-mfma <repo>/gpurun_out --config {workload}", "```", "",
-           "Per dispatch: MFMA rate = SQ_INSTS_MFMA x 4096 flops / dispatch time (every product runs on "
-           "v_mfma_f32_32x32x2_f32, 4096 flops per wave instruction); busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+           "Per dispatch: matrix-core rate = SQ_INSTS_MFMA x flops per instruction / dispatch time "
+           "(v_mfma_f32_32x32x2_f32: 4096 flops per wave instruction, against the fp32 peak of 157.3 "
+           "TFLOP/s; v_mfma_f32_32x32x16_bf16: 32768, against the bf16 peak of 2500 TFLOP/s, six of them "
+           "per fp32 product, so the fp32-equivalent rate is a sixth); busy = SQ_VALU_MFMA_BUSY_CYCLES / "
            f"({SIMDS} SIMDs x dispatch time x {CLOCK_GHZ} GHz).  Counters serialize the dispatches, so times "
            "are those of kernels running alone.", "",
-           "| Kernel | Dispatches | Time ms | MFMA TFLOP/s (% of 157.3) | MFMA busy | busy cycles per instruction |",
-           "|---|---|---|---|---|---|"]
-    for k, (n, ns, ins, busy) in sorted(agg.items(), key=lambda kv: (kv[0] != "all gemm", -kv[1][1])):
-        tf = ins * 4096 / ns / 1e3 if ns else 0.0
+           "| Kernel | Dispatches | Time ms | Matrix-core TFLOP/s (% of its peak) | fp32-equivalent TFLOP/s | "
+           "MFMA busy | busy cycles per instruction |",
+           "|---|---|---|---|---|---|---|"]
+    for k, (n, ns, ins, busy, fam) in sorted(agg.items(), key=lambda kv: (not kv[0].startswith("all "), -kv[1][1])):
+        tf = ins * inst_flops[fam] / ns / 1e3 if ns else 0.0
+        eq = tf / X3_PRODUCTS if fam == "gemm_x3" else tf
         frac = busy / (SIMDS * ns * CLOCK_GHZ) if ns else 0.0
-        out.append(f"| `{k[:80]}` | {n} | {ns / 1e6:.2f} | {tf:.1f} ({100 * tf / PEAK_FP32_MFMA_TFLOPS:.1f}%) | "
+        out.append(f"| `{k[:80]}` | {n} | {ns / 1e6:.2f} | {tf:.1f} ({100 * tf / peaks[fam]:.1f}%) | {eq:.1f} | "
                    f"{100 * frac:.1f}% | {busy / ins if ins else 0:.1f} |")
     path = os.path.join(ROOT, "profiles", f"mfma_{workload}.md")
     with open(path, "w") as f:
@@ -522,15 +534,27 @@ def main():
             log(f"[bench] {name:12s} launches {r['launches']:6d}  {r['ms'] / isteps:9.3f} ms/step  "
                 f"{r['flops'] / max(r['ms'], 1e-9) / 1e9:8.2f} TFLOP/s  "
                 f"{r['bytes'] / max(r['ms'], 1e-9) / 1e6:8.1f} GB/s")
-    fam = {"gemm": {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0}}
+    # every fp32-operand product (stage families gemm_*), split by kernel: the three-piece
+    # bf16 kernel (the report's gemm_x3 family) and the fp32 matrix-core kernel (the rest)
+    keys = ("launches", "ms", "flops", "bytes")
+    allg = {k: 0.0 for k in keys}
+    fam = {}
     for name, r in rep.items():
-        if name.startswith("gemm") and name != "gemm64":
-            for k in fam["gemm"]:
-                fam["gemm"][k] += r[k]
+        if name.startswith("gemm") and name not in ("gemm64", "gemm_x3"):
+            for k in keys:
+                allg[k] += r[k]
         elif name in ("qr_panel", "quant", "dequant", "graft", "gemm64", "diag"):
             fam[name] = dict(r)
-    g = fam["gemm"]
-    gemm_tflops = g["flops"] / (g["ms"] * 1e-3) / 1e12 if g["ms"] > 0 else 0.0
+    x3 = rep.get("gemm_x3", {k: 0.0 for k in keys})
+    fam["gemm_x3"] = dict(x3)
+    fam["gemm_fp32"] = {k: allg[k] - x3[k] for k in keys}
+    gemm_tflops = allg["flops"] / (allg["ms"] * 1e-3) / 1e12 if allg["ms"] > 0 else 0.0
+    # matrix-core use over all products: matrix-core flops over the time-weighted peak of
+    # the kernels that ran them
+    mc_time = x3["ms"] * 1e-3 * PEAK_BF16_MFMA_TFLOPS * 1e12 + \
+        fam["gemm_fp32"]["ms"] * 1e-3 * PEAK_FP32_MFMA_TFLOPS * 1e12
+    mc_flops = X3_PRODUCTS * x3["flops"] + fam["gemm_fp32"]["flops"]
+    gemm_frac = mc_flops / mc_time if mc_time > 0 else 0.0
     q = rep["quant"]
     quant_gbps = q["bytes"] / (q["ms"] * 1e-3) / 1e9 if q["ms"] > 0 else 0.0
     dq = rep["dequant"]
@@ -538,11 +562,17 @@ def main():
     step_flops = sum(cost.block_step_flops(m, n, wl.bjorck_iters, wl.root_interval, wl.power_iters,
                                            cached_root=cfg.root_cache) for m, n in wl.shapes)
     traffic = recorded_traffic(wl.name)
+    sym_note = ("algorithmic flops = 2 M N K of each product a launch is given, a symmetric product "
+                "(V^T V, V diag(lam) V^T, G G^T, V diag(d) V^T) counted by its M (M + 1) / 2 distinct "
+                "entries, K M (M + 1)")
     kernels = {
-        "gemm": ("mfma", "gemm_kernel (fp32 v_mfma_f32_32x32x2_f32): every matrix product of the step; "
-                 "algorithmic flops = 2 M N K of each product a launch is given, a symmetric product "
-                 "(V^T V, V diag(lam) V^T, G G^T, V diag(d) V^T) counted by its M (M + 1) / 2 distinct "
-                 "entries, K M (M + 1)"),
+        "gemm_x3": ("mfma_bf16", "gemm_x3_kernel (v_mfma_f32_32x32x16_bf16, fp32 operands split into three "
+                    "bf16 pieces, six bf16 products per fp32 product): the matrix products of launches on "
+                    "128 x 128 tiles; achieved = 6 x the algorithmic flops per second (the bf16 matrix-core "
+                    "work; fp32_equivalent_tflops = the algorithmic rate) against the bf16 matrix-core peak; "
+                    + sym_note),
+        "gemm_fp32": ("mfma", "gemm_kernel (fp32 v_mfma_f32_32x32x2_f32): the matrix products of the other "
+                      "launches (64 x 64 and skinny tiles: single blocks, panel-width QR products); " + sym_note),
         "qr_panel": ("alu", "panel_*_kernel / qr_step_kernel: Householder factorization of one 32-column "
                      "panel per workgroup (one workgroup per side: a dependent chain of reflector steps, "
                      "latency-bound); in the fused QR step of small batches the same launch applies the "
@@ -567,14 +597,20 @@ def main():
             continue
         per_launch_s = r["ms"] * 1e-3 / r["launches"]
         lps = r["launches"] / isteps
+        extra = {}
         if bound == "hbm":
             achieved, peak, unit = r["bytes"] / r["launches"] / per_launch_s / 1e9, PEAK_HBM_GBPS, "GB/s"
         else:
             achieved = r["flops"] / r["launches"] / per_launch_s / 1e12
-            peak = {"mfma": PEAK_FP32_MFMA_TFLOPS, "mfma64": PEAK_FP64_MFMA_TFLOPS}.get(bound, PEAK_FP32_VALU_TFLOPS)
+            if bound == "mfma_bf16":
+                extra["fp32_equivalent_tflops"] = round(achieved, 4)
+                achieved *= X3_PRODUCTS
+            peak = {"mfma": PEAK_FP32_MFMA_TFLOPS, "mfma64": PEAK_FP64_MFMA_TFLOPS,
+                    "mfma_bf16": PEAK_BF16_MFMA_TFLOPS}.get(bound, PEAK_FP32_VALU_TFLOPS)
             unit = "TFLOP/s"
         rooflines[name] = {
-            "bound": "mfma" if bound == "mfma64" else bound, "kernel": desc, "achieved": round(achieved, 4), "peak": peak, "unit": unit,
+            "bound": "mfma" if bound in ("mfma64", "mfma_bf16") else bound, "kernel": desc,
+            "achieved": round(achieved, 4), "peak": peak, "unit": unit, **extra,
             "frac": round(achieved / peak, 6),
             "traffic": round(traffic[name]) if name in traffic else None,
             "algorithmic_bytes_per_launch": round(r["bytes"] / r["launches"]),
@@ -607,7 +643,7 @@ def main():
             "fp64_refresh": args.fp64_refresh,
         },
         "gemm_tflops": round(gemm_tflops, 3),
-        "gemm_frac_mfma_peak": round(gemm_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+        "gemm_frac_mfma_peak": round(gemm_frac, 4),
         "quant_gbps": round(quant_gbps, 1),
         "quant_frac_hbm_peak": round(quant_gbps / PEAK_HBM_GBPS, 4),
         "dequant_gbps": round(dequant_gbps, 1),

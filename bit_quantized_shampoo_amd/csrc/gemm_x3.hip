@@ -31,9 +31,13 @@
 //  * the split costs about 5.5 vector instructions per element loaded, against
 //    TM TN 6 / (TM + TN) matrix-core instructions per element pair: large per-wave
 //    tiles keep it small next to the matrix-core work;
-//  * slices are loaded two ahead (two register sets); a slice's global loads are issued
-//    before the previous slice's matrix-core work, and split and stored after it; one
-//    barrier per slice;
+//  * slices are loaded two ahead (two register sets).  An iteration issues the global
+//    loads of slice s + 2 and the LDS fragment reads of slice s, splits and stores slice
+//    s + 1 (loaded one iteration earlier) while the fragments arrive, then runs slice s's
+//    matrix-core products; one barrier per slice;
+//  * every load of the 16-byte path is a buffer load: rows or columns past the operand and
+//    quads past K read zero from the buffer's range check, so nothing is masked (the
+//    vector work per slice is the split itself: 5.5 instructions per element);
 //  * the K scale of op(B)'s rows (V diag(lam) V^T) is applied to the fp32 values before
 //    the split; the epilogue is the fp32 kernel's (gemm_common.hpp).
 // Split-K chunks (ksplit) are supported; operands that sum split-K slabs while loading
@@ -74,10 +78,14 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 __device__ __forceinline__ void split3(const float (&x)[8], u32x4& p1, u32x4& p2, u32x4& p3) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint32_t h = pk_bf16(x[2 * i], x[2 * i + 1]);
+        // (the empty asm keeps the compiler from re-deriving each half with a conversion
+        // of its own: the pair's packed result is unpacked with one shift and one AND)
+        uint32_t h = pk_bf16(x[2 * i], x[2 * i + 1]);
+        asm volatile("" : "+v"(h));
         const float r0 = x[2 * i] - __uint_as_float(h << 16);
         const float r1 = x[2 * i + 1] - __uint_as_float(h & 0xffff0000u);
-        const uint32_t m = pk_bf16(r0, r1);
+        uint32_t m = pk_bf16(r0, r1);
+        asm volatile("" : "+v"(m));
         const float s0 = r0 - __uint_as_float(m << 16);
         const float s1 = r1 - __uint_as_float(m & 0xffff0000u);
         p1[i] = h;
@@ -86,17 +94,23 @@ __device__ __forceinline__ void split3(const float (&x)[8], u32x4& p1, u32x4& p2
     }
 }
 
-// Raw (unmasked) loads of eight consecutive k of row r of a K-contiguous operand of
-// `rows` x `cols` as stored (k runs along the stored row): two 16-byte loads (the caller
-// guarantees 16-byte alignment, ld % 4 == 0 and cols % 4 == 0, so a quad lies entirely
-// inside or outside the operand), addresses clamped into the operand.
-__device__ __forceinline__ void raw8(float (&v)[8], const float* __restrict__ base, int64_t ld, int r, int k,
-                                     int rows, int cols) {
-    const float* p = base + (int64_t)min(r, rows - 1) * ld;
-    const floatx4 a = ldg(reinterpret_cast<const floatx4*>(p + min(k, cols - 4)));
-    const floatx4 b = ldg(reinterpret_cast<const floatx4*>(p + min(k + 4, cols - 4)));
+// Byte offset that lies past every operand's buffer range (operands span less than 2 GiB):
+// a buffer load from it returns zero.
+constexpr uint32_t OUTSIDE = 0x80000000u;
+
+// Eight consecutive k of one row of a K-contiguous operand (k along the stored row): two
+// 16-byte buffer loads from byte offset off (the caller guarantees 16-byte alignment, ld %
+// 4 == 0 and a K extent that is a multiple of 4, so a quad lies entirely inside or outside
+// the operand).  k_ok0 / k_ok1: the quads at k and k + 4 lie before the end of K; a quad
+// past it, and a row past the operand (off at or beyond OUTSIDE), reads zero.
+__device__ __forceinline__ void row8(float (&v)[8], __amdgpu_buffer_rsrc_t r, uint32_t off, bool k_ok0,
+                                     bool k_ok1) {
+    const uint32_t q0 = k_ok0 ? off : OUTSIDE;
+    const uint32_t q1 = k_ok1 ? off + 16 : OUTSIDE;
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)q0, 0, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)q1, 0, 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
+    for (int e = 0; e < 4; ++e) { v[e] = __uint_as_float(a[e]); v[4 + e] = __uint_as_float(b[e]); }
 }
 
 // The same eight values without the 16-byte conditions: one 4-byte load each, every
@@ -112,27 +126,29 @@ __device__ __forceinline__ void scalar8(float (&v)[8], const float* __restrict__
     }
 }
 
-// Zeroes the out-of-range values loaded by raw8 (row r of op(X), k..k+7 along K).
+// Zeroes the out-of-range values loaded by scalar8 (row r of op(X), k..k+7 along K).
 __device__ __forceinline__ void mask8(float (&v)[8], bool row_ok, int k, int K) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = keep_if(v[e], row_ok && k + e < K);
 }
 
 // Buffer resource over the `rows` stored rows of pitch ld of an operand (the last row
-// counted to `cols`): a buffer load past its end returns zero, so loads down a stored
-// column (k along the stored rows) need no clamp.  The operand spans less than 2 GiB
-// (checked on the host with the 16-byte-load conditions).
+// counted to `cols`): a buffer load past its end returns zero, so rows past the operand
+// (and k past the last stored row, down a stored column) need no mask.  The operand spans
+// less than 2 GiB (checked on the host with the 16-byte-load conditions).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const float* base, int64_t ld, int rows, int cols) {
     const int bytes = (int)(((int64_t)(rows - 1) * ld + cols) * 4);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, bytes, 0x00020000);
 }
 
 // Eight consecutive k of column c of an operand stored K x cols (k along the stored
-// rows): one 4-byte buffer load per k, k past the last row reads zero.  off: byte offset
-// of (k, c); step: bytes between stored rows.
-__device__ __forceinline__ void col8(float (&v)[8], __amdgpu_buffer_rsrc_t r, int off, int step) {
+// rows): one 4-byte buffer load per k, k past the last row reads zero, and so does a
+// column past the operand (off at or beyond OUTSIDE).  off: byte offset of (k, c); step:
+// bytes between stored rows.
+__device__ __forceinline__ void col8(float (&v)[8], __amdgpu_buffer_rsrc_t r, uint32_t off, int step) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off + e * step, 0, 0));
+    for (int e = 0; e < 8; ++e)
+        v[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + e * step), 0, 0));
 }
 
 // KS: op(B)'s rows are scaled by kscale[k] (the statistic V diag(lam) V^T).  VEC: every
@@ -174,35 +190,47 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
     const int l32 = lane & 31;
 
     // Row halves (eight k of one row) of the slice that this thread loads: item
-    // j = tid + 256 i of an operand with R rows is (row j / 2, half j % 2) where the
-    // operand is K-contiguous in memory (two threads per row, 32 contiguous bytes) and
-    // (row j % R, half j / R) where it is not (consecutive rows along the wave).
+    // j = tid + 256 i of an operand with R rows is (row (j % 8) + 8 (j / 16), half
+    // (j / 8) % 2) where the operand is K-contiguous in memory (two threads per row, 64
+    // contiguous bytes; eight consecutive lanes store eight rows at one half, so the
+    // 16-byte LDS stores fall in distinct bank groups) and (row j % R, half j / R) where it
+    // is not (consecutive rows along the wave).
     int ar[NIA], ak[NIA], br[NIB], bk[NIB];
 #pragma unroll
     for (int i = 0; i < NIA; ++i) {
         const int j = tid + 256 * i;
-        ar[i] = TA ? (j & (BM - 1)) : (j >> 1);
-        ak[i] = TA ? (j / BM) * 8 : (j & 1) * 8;
+        ar[i] = TA ? (j & (BM - 1)) : ((j & 7) + 8 * (j >> 4));
+        ak[i] = TA ? (j / BM) * 8 : ((j >> 3) & 1) * 8;
     }
 #pragma unroll
     for (int i = 0; i < NIB; ++i) {
         const int j = tid + 256 * i;
-        br[i] = TB ? (j >> 1) : (j & (BN - 1));
-        bk[i] = TB ? (j & 1) * 8 : (j / BN) * 8;
+        br[i] = TB ? ((j & 7) + 8 * (j >> 4)) : (j & (BN - 1));
+        bk[i] = TB ? ((j >> 3) & 1) * 8 : (j / BN) * 8;
     }
 
-    // operands stored with k along their rows: buffer loads from (k, column) (the
-    // resources of K-contiguous operands are not used)
+    // VEC: every load is a buffer load over the operand as stored; a row (K-contiguous
+    // operand) or column (the others) past the operand starts at OUTSIDE and reads zero,
+    // and so does a quad past K, so the loaded values need no mask.  Offsets are bytes
+    // from the operand's base at the thread's first slice.
     const __amdgpu_buffer_rsrc_t ra = operand_rsrc(A, lda, TA ? K : M, TA ? M : K);
     const __amdgpu_buffer_rsrc_t rb = operand_rsrc(B, ldb, TB ? N : K, TB ? K : N);
     const int astep = (int)(lda * 4), bstep = (int)(ldb * 4);
-    int aoff[NIA], boff[NIB];
+    uint32_t aoff[NIA], boff[NIB];
 #pragma unroll
-    for (int i = 0; i < NIA; ++i)
-        aoff[i] = TA ? (int)(((int64_t)(kbeg + ak[i]) * lda + min(row0 + ar[i], M - 1)) * 4) : 0;
+    for (int i = 0; i < NIA; ++i) {
+        const int r = row0 + ar[i];
+        aoff[i] = r >= M ? OUTSIDE
+                : TA ? (uint32_t)(((int64_t)(kbeg + ak[i]) * lda + r) * 4)
+                     : (uint32_t)(((int64_t)r * lda + kbeg + ak[i]) * 4);
+    }
 #pragma unroll
-    for (int i = 0; i < NIB; ++i)
-        boff[i] = TB ? 0 : (int)(((int64_t)(kbeg + bk[i]) * ldb + min(col0 + br[i], N - 1)) * 4);
+    for (int i = 0; i < NIB; ++i) {
+        const int r = col0 + br[i];
+        boff[i] = r >= N ? OUTSIDE
+                : TB ? (uint32_t)(((int64_t)r * ldb + kbeg + bk[i]) * 4)
+                     : (uint32_t)(((int64_t)(kbeg + bk[i]) * ldb + r) * 4);
+    }
 
     floatx16 acc[TM][TN];
 #pragma unroll
@@ -215,20 +243,20 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
     struct Raw {
         float a[NIA][8], b[NIB][8], k[NIB][KS ? 8 : 1];
     };
-    // slice s (k0 = kbeg + s * BK); loads past K are clamped (K-contiguous operands) or
-    // read zero (the others) and are masked to zero when stored
+    // slice s (k0 = kbeg + s * BK): buffer loads read zero past the operand and past K;
+    // without VEC the loads are clamped and the values masked when stored
     auto load = [&](Raw& R, int s) {
         const int k0 = kbeg + s * BK;
 #pragma unroll
         for (int i = 0; i < NIA; ++i) {
             if constexpr (!VEC) scalar8<!TA>(R.a[i], A, lda, row0 + ar[i], k0 + ak[i], TA ? K : M, TA ? M : K);
-            else if constexpr (!TA) raw8(R.a[i], A, lda, row0 + ar[i], k0 + ak[i], M, K);
+            else if constexpr (!TA) row8(R.a[i], ra, aoff[i] + s * BK * 4, k0 + ak[i] < K, k0 + ak[i] + 4 < K);
             else col8(R.a[i], ra, aoff[i] + s * BK * astep, astep);
         }
 #pragma unroll
         for (int i = 0; i < NIB; ++i) {
             if constexpr (!VEC) scalar8<TB>(R.b[i], B, ldb, col0 + br[i], k0 + bk[i], TB ? N : K, TB ? K : N);
-            else if constexpr (TB) raw8(R.b[i], B, ldb, col0 + br[i], k0 + bk[i], N, K);
+            else if constexpr (TB) row8(R.b[i], rb, boff[i] + s * BK * 4, k0 + bk[i] < K, k0 + bk[i] + 4 < K);
             else col8(R.b[i], rb, boff[i] + s * BK * bstep, bstep);
             if constexpr (KS) {
 #pragma unroll
@@ -242,7 +270,7 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
         uint16_t* base = lds + buf * BUF;
 #pragma unroll
         for (int i = 0; i < NIA; ++i) {
-            mask8(R.a[i], row0 + ar[i] < M, k0 + ak[i], K);
+            if constexpr (!VEC) mask8(R.a[i], row0 + ar[i] < M, k0 + ak[i], K);
             u32x4 p1, p2, p3;
             split3(R.a[i], p1, p2, p3);
             uint16_t* pa = base + ar[i] * PITCH + ak[i];
@@ -252,7 +280,7 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
         }
 #pragma unroll
         for (int i = 0; i < NIB; ++i) {
-            mask8(R.b[i], col0 + br[i] < N, k0 + bk[i], K);
+            if constexpr (!VEC) mask8(R.b[i], col0 + br[i] < N, k0 + bk[i], K);
             if constexpr (KS) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) R.b[i][e] *= R.k[i][e];
@@ -266,21 +294,24 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
         }
     };
 
-    auto compute = [&](int buf) {
-        const uint16_t* base = lds + buf * BUF;
+    struct Frags {
         bf16x8 a[3][TM], b[3][TN];
+    };
+    auto read_frags = [&](Frags& F, int buf) {
+        const uint16_t* base = lds + buf * BUF;
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
 #pragma unroll
             for (int m = 0; m < TM; ++m)
-                a[p][m] = *reinterpret_cast<const bf16x8*>(base + p * PLANE_A +
-                                                           (wave_m * TM * 32 + m * 32 + l32) * PITCH + h * 8);
+                F.a[p][m] = *reinterpret_cast<const bf16x8*>(base + p * PLANE_A +
+                                                             (wave_m * TM * 32 + m * 32 + l32) * PITCH + h * 8);
 #pragma unroll
             for (int n = 0; n < TN; ++n)
-                b[p][n] = *reinterpret_cast<const bf16x8*>(base + 3 * PLANE_A + p * PLANE_B +
-                                                           (wave_n * TN * 32 + n * 32 + l32) * PITCH + h * 8);
+                F.b[p][n] = *reinterpret_cast<const bf16x8*>(base + 3 * PLANE_A + p * PLANE_B +
+                                                             (wave_n * TN * 32 + n * 32 + l32) * PITCH + h * 8);
         }
-        // the six partial products of order >= 2^-16, largest first
+    };
+    auto mfmas = [&](const Frags& F) {
         constexpr int PA[6] = {0, 0, 1, 0, 2, 1};
         constexpr int PB[6] = {0, 1, 0, 2, 0, 1};
 #pragma unroll
@@ -289,11 +320,12 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
             for (int m = 0; m < TM; ++m)
 #pragma unroll
                 for (int n = 0; n < TN; ++n)
-                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PA[q]][m], b[PB[q]][n], acc[m][n], 0, 0, 0);
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[PA[q]][m], F.b[PB[q]][n], acc[m][n], 0, 0, 0);
     };
 
     // Two register sets: slice s + 2 is loaded while slice s is multiplied and slice s + 1
-    // (loaded one iteration earlier) is split into LDS.  Loads and stores are
+    // (loaded one iteration earlier) is split into LDS; slice s's fragments are read
+    // before the split, so their LDS latency hides behind it.  Loads and stores are
     // unconditional inside the loop, so the loads stay ahead of the matrix-core work (a
     // store behind a branch pulls its loads in behind the branch); past K they read
     // zeros, and a store past K goes to the buffer read one iteration earlier, which no
@@ -306,19 +338,22 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
         load(r1, 1);
     }
     __syncthreads();
+    Frags F;
     for (int kt = 0; kt < nk; kt += 2) {
         load(r0, kt + 2);
-        __builtin_amdgcn_sched_barrier(0);   // the loads go out before the matrix-core work
-        compute(0);
+        read_frags(F, 0);
         __builtin_amdgcn_sched_barrier(0);
         store(r1, 1, kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(F);
         __syncthreads();
         if (kt + 1 >= nk) break;
         load(r1, kt + 3);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(1);
+        read_frags(F, 1);
         __builtin_amdgcn_sched_barrier(0);
         store(r0, 0, kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(F);
         __syncthreads();
     }
 

@@ -40,14 +40,16 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 enum Family {
     FAM_GEMM_BJORCK = 0, FAM_GEMM_STATS, FAM_GEMM_POWER, FAM_GEMM_QR, FAM_GEMM_RAYLEIGH,
     FAM_GEMM_PRECOND, FAM_DEQUANT, FAM_QUANT, FAM_PANEL, FAM_RAYLEIGH, FAM_ELEMENTWISE, FAM_GRAFT,
-    FAM_GEMM_QR_TRAIL, FAM_GEMM_QR_Q, FAM_DIAG, FAM_GEMM64, FAM_N
+    FAM_GEMM_QR_TRAIL, FAM_GEMM_QR_Q, FAM_DIAG, FAM_GEMM64, FAM_GEMM_X3, FAM_N
 };
 // gemm_qr: the reflector products inside an outer block (and the look-ahead schedule's);
 // gemm_qr_trail: an outer block's reflectors on the trailing columns; gemm_qr_q: the
-// accumulation of Q
+// accumulation of Q; gemm_x3: every product that ran on the three-piece bf16 kernel,
+// whatever its stage (also counted in its stage's family)
 const char* kFamilyNames[FAM_N] = {"gemm_bjorck", "gemm_stats", "gemm_power", "gemm_qr", "gemm_rayleigh",
                                    "gemm_precond", "dequant", "quant", "qr_panel", "rayleigh",
-                                   "elementwise", "graft", "gemm_qr_trail", "gemm_qr_q", "diag", "gemm64"};
+                                   "elementwise", "graft", "gemm_qr_trail", "gemm_qr_q", "diag", "gemm64",
+                                   "gemm_x3"};
 
 enum Kind { K_GEMM, K_DEQUANT, K_QUANT, K_COPY, K_PANEL, K_RAYLEIGH, K_ROOT, K_IDENTITY, K_SIGN, K_INIT,
             K_RECORD, K_WAIT, K_GRAFT_NORMS, K_GRAFT_APPLY, K_COPYF, K_NEWTON_NORM, K_NEWTON_SCALE,
@@ -92,6 +94,7 @@ struct Side {
 
 struct TimingRec {
     int family;
+    bool x3;             // a matrix product on the three-piece bf16 kernel
     hipEvent_t e0, e1;
     double flops, bytes;
 };
@@ -1761,6 +1764,7 @@ struct shampoo4_ctx_s {
             launch_timing().start = launch_timing().stop = nullptr;
             if (launched) {
                 rec.family = fam;
+                rec.x3 = L.kind == K_GEMM && L.cfg == GEMM_X3;
                 rec.flops = L.flops;
                 rec.bytes = L.bytes;
                 recs.push_back(rec);
@@ -2580,6 +2584,12 @@ shampoo4_status shampoo4_timing_report(shampoo4_ctx c, int32_t* count, const cha
         total_ms[r.family] += ms;
         flops[r.family] += r.flops;
         bytes[r.family] += r.bytes;
+        if (r.x3) {
+            launches[FAM_GEMM_X3] += 1;
+            total_ms[FAM_GEMM_X3] += ms;
+            flops[FAM_GEMM_X3] += r.flops;
+            bytes[FAM_GEMM_X3] += r.bytes;
+        }
     }
     *count = FAM_N;
     return SHAMPOO4_OK;

@@ -444,7 +444,8 @@ SHAMPOO4_API shampoo4_status shampoo4_inverse_root(int32_t count, const int32_t*
  * reflector block, the block's products on the trailing columns and the accumulation of
  * Q), "dequant", "quant", "qr_panel", "rayleigh", "elementwise", "graft", "diag" (the
  * diagonal sides' statistic and the both-diagonal precondition), "gemm64" (every float64
- * product of FP64_REFRESH).  Host arrays of
+ * product of FP64_REFRESH), "gemm_x3" (every product that ran on the three-piece bf16
+ * kernel, whatever its stage; these are also counted in their stage's family).  Host arrays of
  * length *count (in: capacity, out: used). */
 SHAMPOO4_API shampoo4_status shampoo4_timing(shampoo4_ctx ctx, int32_t enable);
 SHAMPOO4_API shampoo4_status shampoo4_timing_report(shampoo4_ctx ctx, int32_t* count, const char** names,

@@ -31,7 +31,8 @@ def test_traffic_summary_parses():
     assert "```traffic" in text and "rocprofv3 --pmc FETCH_SIZE" in text and "rocprofv3 --pmc WRITE_SIZE" in text
     block = text.split("```traffic", 1)[1].split("```", 1)[0].strip().splitlines()
     fams = {line.split()[0] for line in block}
-    assert {"gemm", "qr_panel", "quant", "dequant"} <= fams
+    assert {"qr_panel", "quant", "dequant"} <= fams
+    assert fams & {"gemm_fp32", "gemm_x3", "gemm"}
     rec = bench.recorded_traffic("single_1024")
     # every family whose kernel source is unchanged since the counters carries a positive byte count
     for fam, b in rec.items():
