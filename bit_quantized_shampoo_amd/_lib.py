@@ -21,6 +21,7 @@ FLAG_GRAPHS = 32
 FLAG_DT_CODEBOOK = 64
 FLAG_FP64_REFRESH = 128
 FLAG_FP32_MFMA = 256
+FLAG_DEBUG = 512
 DIAG_L = 1
 DIAG_R = 2
 CODEBOOK_LINEAR_SQUARE = 0

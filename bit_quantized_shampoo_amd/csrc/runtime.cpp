@@ -14,12 +14,29 @@
 #include <cstring>
 #include <functional>
 #include <memory>
+#include <type_traits>
 #include <vector>
 
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 using namespace s4;
+
+namespace {
+
+// A roctx range around each call that enqueues device work: a rocprofv3 run with
+// --marker-trace shows the library's calls on the timeline above their kernels (a
+// push/pop pair costs nothing measurable when no profiler is attached).
+struct CallRange {
+    explicit CallRange(const char* name) { roctxRangePushA(name); }
+    ~CallRange() { roctxRangePop(); }
+    CallRange(const CallRange&) = delete;
+    CallRange& operator=(const CallRange&) = delete;
+};
+
+}  // namespace
 
 namespace {
 
@@ -148,6 +165,11 @@ struct shampoo4_ctx_s {
     // 16-byte loads of the gradients, which the captured kernels bake in)
     bool use_graphs = false;
     bool x3 = true;                       // 128 x 128 products on the three-piece bf16 kernel
+    // SHAMPOO4_FLAG_DEBUG: workspace temporaries (offset, bytes), filled with NaN before each
+    // call; a descriptor found reaching outside the state or workspace at init
+    bool debug = false;
+    std::vector<std::pair<size_t, size_t>> temps;
+    bool bad_desc = false;
     bool graph_ok = true;
     hipStream_t cap = nullptr;
     hipGraphExec_t stats_graph[2][2] = {};
@@ -202,6 +224,58 @@ struct shampoo4_ctx_s {
     T* stp(size_t off) const { return reinterpret_cast<T*>(st + off); }
     float* wsf(size_t off) const { return wsp<float>(off); }
     float* stf(size_t off) const { return stp<float>(off); }
+
+    // ---- debug checks (SHAMPOO4_FLAG_DEBUG) -------------------------------------
+    // [p, p + bytes) must lie inside the state or the workspace's data region (below the
+    // descriptor tables); a null pointer or an empty extent passes.
+    void check_range(const void* p, int64_t bytes) {
+        if (!debug || !p || bytes <= 0 || !ws) return;
+        const uint8_t* q = static_cast<const uint8_t*>(p);
+        const bool in_ws = q >= ws && q + bytes <= ws + desc_base;
+        const bool in_st = st && q >= st && q + bytes <= st + st_bytes;
+        if (!in_ws && !in_st) bad_desc = true;
+    }
+    // bytes spanned by a rows x cols float matrix of pitch ld (plus nslab - 1 slabs of
+    // `slab` elements after it)
+    static int64_t span(int64_t rows, int64_t cols, int64_t ld, int64_t nslab = 1, int64_t slab = 0,
+                        int64_t elem = 4) {
+        if (rows <= 0 || cols <= 0) return 0;
+        return ((rows - 1) * ld + cols + std::max<int64_t>(nslab - 1, 0) * slab) * elem;
+    }
+    void check_gemm(const GemmDesc& d, bool ta, bool tb) {
+        if (!debug) return;
+        if (d.a_io < 0) check_range(d.A, span(ta ? d.K : d.M, ta ? d.M : d.K, d.lda, d.anslab, d.aslab));
+        if (d.b_io < 0) check_range(d.B, span(tb ? d.N : d.K, tb ? d.K : d.N, d.ldb, d.bnslab, d.bslab));
+        const bool coldot = d.flags & GEMM_F_COLDOT;
+        if (d.beta != 0.f || coldot) check_range(d.C, span(d.M, d.N, d.ldc));
+        if (d.d_io < 0) {
+            const int64_t rows = coldot ? (d.M + 127) / 128 : d.M;   // column-dot: one row per tile (at most)
+            check_range(d.D, span(rows, d.N, d.ldd, std::max(1, d.ksplit), d.dslab));
+        }
+        check_range(d.kscale, (int64_t)d.K * 4);
+        check_range(d.rscale, (int64_t)d.M * 4);
+        check_range(d.cscale, (int64_t)d.N * 4);
+    }
+    void check_codec(const CodecDesc& d) {
+        if (!debug) return;
+        const int64_t nb = (d.n + 63) / 64;
+        check_range(d.codes_in, nb * 32);
+        check_range(d.scales_in, nb * 4);
+        check_range(d.codes_out, nb * 32);
+        check_range(d.scales_out, nb * 4);
+        check_range(d.x_in, d.n * 4);
+        check_range(d.x_out, d.n * 4);
+    }
+    // NaN into every temporary (a kernel that reads one before writing it then yields NaN)
+    hipError_t debug_fill(hipStream_t s) {
+        if (!debug) return hipSuccess;
+        for (auto& t : temps) {
+            hipError_t e = hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(ws + t.first), 0x7fc00000,
+                                             t.second / 4, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
 
     // ---- descriptor region ---------------------------------------------------
     size_t blob_put(const void* data, size_t bytes) {
@@ -343,6 +417,7 @@ struct shampoo4_ctx_s {
         Launch L;
         for (auto& d : ds) {
             d.tiles_m = (d.M + bm - 1) / bm;
+            check_gemm(d, d.flags & GEMM_F_TA, d.flags & GEMM_F_TB);
             prefix.push_back(total);
             if (d.flags & GEMM_F_SYM) {
                 const int t = d.tiles_m;
@@ -381,6 +456,8 @@ struct shampoo4_ctx_s {
 
     template <class D>
     Launch make_items(Kind kind, const std::vector<D>& ds, const std::vector<int>& tiles) {
+        if constexpr (std::is_same_v<D, CodecDesc>)
+            for (auto& d : ds) check_codec(d);
         Launch L;
         L.kind = kind;
         L.fam = kind == K_DEQUANT ? FAM_DEQUANT : kind == K_QUANT ? FAM_QUANT : kind == K_PANEL ? FAM_PANEL
@@ -410,6 +487,8 @@ struct shampoo4_ctx_s {
                                                            : SHAMPOO4_CODEBOOK_LINEAR_SQUARE;
         use_graphs = (cfg.flags & SHAMPOO4_FLAG_GRAPHS) != 0;
         x3 = (cfg.flags & SHAMPOO4_FLAG_FP32_MFMA) == 0;
+        debug = (cfg.flags & SHAMPOO4_FLAG_DEBUG) != 0;
+        temps.clear();
         // Large batches are throughput-bound: reflectors go to the trailing matrix 128
         // columns at a time.  Small ones are bound by the chain of panels and by launch
         // latency: panel-wide updates on the caller's stream (or, on request, with the
@@ -428,13 +507,19 @@ struct shampoo4_ctx_s {
         size_t so = 0, wo = 0;
         auto st_take = [&](size_t b) { size_t o = so; so += align_up(b ? b : 1); return o; };
         auto ws_take = [&](size_t b) { size_t o = wo; wo += align_up(b ? b : 1); return o; };
+        // a buffer written before it is read within every call (none survives to the next)
+        auto tmp_take = [&](size_t b) {
+            const size_t o = ws_take(b);
+            if (b) temps.emplace_back(o, b);
+            return o;
+        };
         io_off = ws_take((size_t)nb * sizeof(IoEntry));
         gio_off = ws_take((size_t)nb * sizeof(GraftIo));
         flag_off = ws_take(sizeof(uint32_t) * 4);
         {   // grafting partials: two floats per row tile of every block
             size_t tiles = 0;
             for (auto& sh : shapes) tiles += (sh.m + graft_rows(sh.n) - 1) / graft_rows(sh.n);
-            parts_off = ws_take(tiles * 2 * sizeof(float));
+            parts_off = tmp_take(tiles * 2 * sizeof(float));
         }
         X1.resize(nb);
         X2.resize(nb);
@@ -470,57 +555,57 @@ struct shampoo4_ctx_s {
                 if (fp64) {   // float32: dequantized U, the root and Q for the quantizer only
                     S.Vr = ws_take(mat);
                     S.Rt = ws_take(mat);
-                    S.Tmp = ws_take(mat);
-                    S.Wg = ws_take(mat);
-                    S.Qm = ws_take(mat);
+                    S.Tmp = tmp_take(mat);
+                    S.Wg = tmp_take(mat);
+                    S.Qm = tmp_take(mat);
                     const size_t mat64 = (size_t)p * p * 8;
-                    S.V64a = ws_take(mat64);
-                    S.V64b = ws_take(mat64);
-                    S.Wg64 = ws_take(mat64);
-                    S.Lt64 = ws_take(mat64);
-                    S.P64 = ws_take(mat64);
-                    S.Q64 = ws_take(mat64);
+                    S.V64a = tmp_take(mat64);
+                    S.V64b = tmp_take(mat64);
+                    S.Wg64 = tmp_take(mat64);
+                    S.Lt64 = tmp_take(mat64);
+                    S.P64 = tmp_take(mat64);
+                    S.Q64 = tmp_take(mat64);
                     S.outer_rows.clear();
                     size_t rows = 0;
                     for (int c0 = 0; c0 < p; c0 += kPanel) {
                         S.outer_rows.push_back(rows);
                         rows += p - c0;
                     }
-                    S.Vb64 = ws_take(rows * kPanel * 8);
-                    S.Yb64 = ws_take(rows * kPanel * 8);
-                    S.Z64 = ws_take((size_t)kPanel * p * 8);
-                    S.W64 = ws_take((size_t)kPanel * p * 8);
-                    S.rd64 = ws_take((size_t)p * 8);
+                    S.Vb64 = tmp_take(rows * kPanel * 8);
+                    S.Yb64 = tmp_take(rows * kPanel * 8);
+                    S.Z64 = tmp_take((size_t)kPanel * p * 8);
+                    S.W64 = tmp_take((size_t)kPanel * p * 8);
+                    S.rd64 = tmp_take((size_t)p * 8);
                     continue;
                 }
-                S.Vs = ws_take(mat);
-                S.Vr = ws_take(mat);
+                S.Vs = tmp_take(mat);
+                S.Vr = ws_take(mat);   // rectified root eigenvectors (kept between calls)
                 S.Rt = ws_take(mat);   // root matrix V^r diag(d) V^r^T (ROOT_CACHE)
-                S.Tmp = ws_take(mat);
-                S.Wg = ws_take(mat);
-                S.Lt = ws_take(mat);
-                S.Pm = ws_take(mat);
-                S.Qm = ws_take(mat);
+                S.Tmp = tmp_take(mat);
+                S.Wg = tmp_take(mat);
+                S.Lt = tmp_take(mat);
+                S.Pm = tmp_take(mat);
+                S.Qm = tmp_take(mat);
                 S.outer_rows.clear();
                 size_t rows = 0;
                 for (int c0 = 0; c0 < p; c0 += outer) {
                     S.outer_rows.push_back(rows);
                     rows += p - c0;
                 }
-                S.Vb = ws_take(rows * outer * 4);
-                S.Yb = ws_take(rows * outer * 4);
-                S.Z = ws_take((size_t)kMaxSplit * outer * p * 4);        // split-K slabs of Y^T A
-                S.W = ws_take((size_t)kMaxSplit * outer * p * 4);        // split-K slabs of Q Y
-                S.Mb = ws_take((size_t)kMaxSplit * outer * kPanel * 4);  // split-K slabs of V^T Y
-                S.Z2 = ws_take((size_t)kMaxSplit * kPanel * kPanel * 4); // look-ahead Y^T A
-                S.rdiag = ws_take(p * 4);
-                S.Tb = ws_take((size_t)((p + kPanel - 1) / kPanel) * kPanel * kPanel * 4);   // fused QR: T per panel
+                S.Vb = tmp_take(rows * outer * 4);
+                S.Yb = tmp_take(rows * outer * 4);
+                S.Z = tmp_take((size_t)kMaxSplit * outer * p * 4);        // split-K slabs of Y^T A
+                S.W = tmp_take((size_t)kMaxSplit * outer * p * 4);        // split-K slabs of Q Y
+                S.Mb = tmp_take((size_t)kMaxSplit * outer * kPanel * 4);  // split-K slabs of V^T Y
+                S.Z2 = tmp_take((size_t)kMaxSplit * kPanel * kPanel * 4); // look-ahead Y^T A
+                S.rdiag = tmp_take(p * 4);
+                S.Tb = tmp_take((size_t)((p + kPanel - 1) / kPanel) * kPanel * kPanel * 4);   // fused QR: T per panel
             }
-            X1[b] = ws_take((size_t)shapes[b].m * shapes[b].n * 4);
-            X2[b] = ws_take((size_t)shapes[b].m * shapes[b].n * 4);
+            X1[b] = tmp_take((size_t)shapes[b].m * shapes[b].n * 4);
+            X2[b] = tmp_take((size_t)shapes[b].m * shapes[b].n * 4);
             const int64_t m = shapes[b].m, n = shapes[b].n;
-            if (diag_bits[b] & SHAMPOO4_DIAG_L) RP[b] = ws_take((size_t)((n + DIAG_TC - 1) / DIAG_TC) * m * 4);
-            if (diag_bits[b] & SHAMPOO4_DIAG_R) CP[b] = ws_take((size_t)((m + DIAG_TR - 1) / DIAG_TR) * n * 4);
+            if (diag_bits[b] & SHAMPOO4_DIAG_L) RP[b] = tmp_take((size_t)((n + DIAG_TC - 1) / DIAG_TC) * m * 4);
+            if (diag_bits[b] & SHAMPOO4_DIAG_R) CP[b] = tmp_take((size_t)((m + DIAG_TR - 1) / DIAG_TR) * n * 4);
         }
         st_bytes = so;
         desc_base = wo;
@@ -1956,7 +2041,8 @@ shampoo4_status validate_cfg(const shampoo4_config* cfg) {
     if (cfg->power_iters < 1 || cfg->power_iters > 8) return SHAMPOO4_EINVAL;
     if (cfg->flags & ~(SHAMPOO4_FLAG_ROOT_CACHE | SHAMPOO4_FLAG_KEEP_STATE | SHAMPOO4_FLAG_QR_BLOCKED |
                        SHAMPOO4_FLAG_QR_LOOKAHEAD | SHAMPOO4_FLAG_FP32_STATE | SHAMPOO4_FLAG_GRAPHS |
-                       SHAMPOO4_FLAG_DT_CODEBOOK | SHAMPOO4_FLAG_FP64_REFRESH | SHAMPOO4_FLAG_FP32_MFMA))
+                       SHAMPOO4_FLAG_DT_CODEBOOK | SHAMPOO4_FLAG_FP64_REFRESH | SHAMPOO4_FLAG_FP32_MFMA |
+                       SHAMPOO4_FLAG_DEBUG))
         return SHAMPOO4_EINVAL;
     if ((cfg->flags & SHAMPOO4_FLAG_DT_CODEBOOK) && (cfg->flags & SHAMPOO4_FLAG_FP32_STATE))
         return SHAMPOO4_EINVAL;
@@ -2058,6 +2144,7 @@ shampoo4_status shampoo4_init(const shampoo4_config* cfg, int32_t nblocks, const
 shampoo4_status shampoo4_init_ex(const shampoo4_config* cfg, int32_t nblocks, const shampoo4_shape* shapes,
                                  const uint8_t* diag_sides, void* state, size_t state_bytes, void* workspace,
                                  size_t workspace_bytes, void* stream, shampoo4_ctx* out) {
+    CallRange range_("shampoo4_init_ex");
     shampoo4_status st = validate_cfg(cfg);
     if (st != SHAMPOO4_OK) return st;
     if ((st = validate_shapes(nblocks, shapes, diag_sides)) != SHAMPOO4_OK) return st;
@@ -2076,6 +2163,7 @@ shampoo4_status shampoo4_init_ex(const shampoo4_config* cfg, int32_t nblocks, co
     c->ws = static_cast<uint8_t*>(workspace);
     c->build();
     c->build_graft();
+    if (c->bad_desc) return SHAMPOO4_EINVAL;   // debug: a descriptor reaches outside the buffers
     if (c->n_sync > 0) {   // second stream (default priority) and its synchronization events
         if (hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking) != hipSuccess) return SHAMPOO4_EHIP;
         c->sync_ev.assign(c->n_sync, nullptr);
@@ -2111,18 +2199,22 @@ shampoo4_status shampoo4_init_ex(const shampoo4_config* cfg, int32_t nblocks, co
 }
 
 shampoo4_status shampoo4_update_stats(shampoo4_ctx c, const shampoo4_io* io, void* stream) {
+    CallRange range_("shampoo4_update_stats");
     if (!c) return SHAMPOO4_EINVAL;
     shampoo4_status st = validate_io(c, io, false);
     if (st != SHAMPOO4_OK) return st;
     hipStream_t s = as_stream(stream);
+    if (c->debug_fill(s) != hipSuccess) return SHAMPOO4_EHIP;
     if (c->upload_io(io, s) != hipSuccess) return SHAMPOO4_EHIP;
     return c->submit_stats(s) == hipSuccess ? SHAMPOO4_OK : SHAMPOO4_EHIP;
 }
 
 shampoo4_status shampoo4_refresh_root(shampoo4_ctx c, void* stream) {
+    CallRange range_("shampoo4_refresh_root");
     if (!c) return SHAMPOO4_EINVAL;
     hipStream_t s = as_stream(stream);
-    hipError_t e = c->run(c->root_d, s);
+    hipError_t e = c->debug_fill(s);
+    if (e == hipSuccess) e = c->run(c->root_d, s);
     if (e == hipSuccess) e = c->run(c->root_copy, s);
     if (e == hipSuccess && (c->cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE)) {
         e = c->root_eigenvectors(s);
@@ -2135,10 +2227,12 @@ shampoo4_status shampoo4_refresh_root(shampoo4_ctx c, void* stream) {
 }
 
 shampoo4_status shampoo4_precondition(shampoo4_ctx c, const shampoo4_io* io, void* stream) {
+    CallRange range_("shampoo4_precondition");
     if (!c) return SHAMPOO4_EINVAL;
     shampoo4_status st = validate_io(c, io, true);
     if (st != SHAMPOO4_OK) return st;
     hipStream_t s = as_stream(stream);
+    if (c->debug_fill(s) != hipSuccess) return SHAMPOO4_EHIP;
     if (c->upload_io(io, s) != hipSuccess) return SHAMPOO4_EHIP;
     hipError_t e = hipSuccess;
     if (!((c->cfg.flags & SHAMPOO4_FLAG_ROOT_CACHE) && c->root_v_valid)) {
@@ -2155,6 +2249,7 @@ shampoo4_status shampoo4_precondition(shampoo4_ctx c, const shampoo4_io* io, voi
 }
 
 shampoo4_status shampoo4_step(shampoo4_ctx c, const shampoo4_io* io, int32_t refresh, void* stream) {
+    CallRange range_("shampoo4_step");
     if (!c) return SHAMPOO4_EINVAL;
     shampoo4_status st = validate_io(c, io, true);
     if (st != SHAMPOO4_OK) return st;
@@ -2174,6 +2269,7 @@ shampoo4_status shampoo4_step(shampoo4_ctx c, const shampoo4_io* io, int32_t ref
     // panels leave most CUs idle).
     hipStream_t s = as_stream(stream);
     if (c->ensure_pre_stream() != hipSuccess) return SHAMPOO4_EHIP;
+    if (c->debug_fill(s) != hipSuccess) return SHAMPOO4_EHIP;
     if (c->upload_io(io, s) != hipSuccess) return SHAMPOO4_EHIP;
     // the precondition is enqueued at the fork point itself (host order), so its launches
     // reach the GPU as the QR starts rather than after the host has queued the whole chain
@@ -2192,6 +2288,7 @@ shampoo4_status shampoo4_step(shampoo4_ctx c, const shampoo4_io* io, int32_t ref
 
 shampoo4_status shampoo4_graft(shampoo4_ctx c, const shampoo4_io* io, const shampoo4_graft_io* gio,
                                const shampoo4_graft_config* cfg, void* stream) {
+    CallRange range_("shampoo4_graft");
     if (!c || !gio || !cfg) return SHAMPOO4_EINVAL;
     shampoo4_status st = validate_io(c, io, true);
     if (st != SHAMPOO4_OK) return st;
@@ -2219,6 +2316,7 @@ shampoo4_status shampoo4_graft(shampoo4_ctx c, const shampoo4_io* io, const sham
     if (adam && !(prm.c1 > 0.f && prm.c2 > 0.f)) return SHAMPOO4_EINVAL;
     c->graft_prm = prm;
     hipStream_t s = as_stream(stream);
+    if (c->debug_fill(s) != hipSuccess) return SHAMPOO4_EHIP;
     if (c->upload_io(io, s) != hipSuccess) return SHAMPOO4_EHIP;
     if (c->upload_table(gio, c->gio_off, s) != hipSuccess) return SHAMPOO4_EHIP;
     const hipError_t e = c->run(c->graft_seq[prm.mode], s);
@@ -2226,6 +2324,7 @@ shampoo4_status shampoo4_graft(shampoo4_ctx c, const shampoo4_io* io, const sham
 }
 
 shampoo4_status shampoo4_check(shampoo4_ctx c, void* stream, uint32_t* device_flags) {
+    CallRange range_("shampoo4_check");
     if (!c) return SHAMPOO4_EINVAL;
     hipStream_t s = as_stream(stream);
     uint32_t f = 0;
@@ -2305,6 +2404,7 @@ shampoo4_status shampoo4_dequantize(const uint8_t* codes, const float* scales, i
 
 shampoo4_status shampoo4_quantize_ex(const float* x, int64_t n, int32_t qblock, int32_t codebook, uint8_t* codes,
                                      float* scales, void* stream) {
+    CallRange range_("shampoo4_quantize_ex");
     if (qblock != 64 || n < 0 || !valid_codebook(codebook)) return SHAMPOO4_EINVAL;
     if (n == 0) return SHAMPOO4_OK;
     if (!x || !codes || !scales) return SHAMPOO4_EINVAL;
@@ -2319,6 +2419,7 @@ shampoo4_status shampoo4_quantize_ex(const float* x, int64_t n, int32_t qblock, 
 
 shampoo4_status shampoo4_dequantize_ex(const uint8_t* codes, const float* scales, int64_t n, int32_t qblock,
                                        int32_t codebook, float* x, void* stream) {
+    CallRange range_("shampoo4_dequantize_ex");
     if (qblock != 64 || n < 0 || !valid_codebook(codebook)) return SHAMPOO4_EINVAL;
     if (n == 0) return SHAMPOO4_OK;
     if (!x || !codes || !scales) return SHAMPOO4_EINVAL;
@@ -2411,6 +2512,7 @@ shampoo4_status shampoo4_gemm_batched_ex(int32_t kernel, int32_t count, int32_t 
                                          const int64_t* ldb, float beta, const float* const* C, const int64_t* ldc,
                                          float* const* D, const int64_t* ldd, void* workspace,
                                          size_t workspace_bytes, void* stream) {
+    CallRange range_("shampoo4_gemm_batched_ex");
     if (count > 0) {
         if (!workspace) return SHAMPOO4_EINVAL;
         if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return SHAMPOO4_EALIGN;
@@ -2432,6 +2534,7 @@ shampoo4_status shampoo4_gemm_batched_static(int32_t count, int32_t transA, int3
                                              const int64_t* ldb, float beta, const float* const* C,
                                              const int64_t* ldc, float* const* D, const int64_t* ldd,
                                              void* stream) {
+    CallRange range_("shampoo4_gemm_batched_static");
     if (count > SHAMPOO4_GEMM_STATIC_MAX) return SHAMPOO4_ESMALLBUF;
     shampoo4_ctx_s tmp;
     Launch L;
@@ -2534,6 +2637,7 @@ size_t shampoo4_inverse_root_workspace_bytes(int32_t count, const int32_t* p) {
 shampoo4_status shampoo4_inverse_root(int32_t count, const int32_t* p, const float* const* A, const int64_t* lda,
                                       float eps, int32_t iters, float* const* X, const int64_t* ldx,
                                       void* workspace, size_t workspace_bytes, void* stream) {
+    CallRange range_("shampoo4_inverse_root");
     if (count < 0) return SHAMPOO4_EINVAL;
     if (count == 0) return SHAMPOO4_OK;
     if (!p || !A || !lda || !X || !ldx || !workspace) return SHAMPOO4_EINVAL;

@@ -61,6 +61,7 @@ class Shampoo4Config:
     codebook: str = "ls"            # 4-bit codebook of U: "ls" linear-square, "dt" dynamic tree
     fp64_refresh: bool = False      # statistics update (Bjorck .. Rayleigh quotients) in float64
     fp32_mfma: bool = False         # every product on the fp32 matrix cores (no three-piece bf16 split)
+    debug: bool = False             # descriptor range checks at init, NaN-filled temporaries per call
 
     def c(self, keep_state: bool = False) -> L.Config:
         flags = (L.FLAG_ROOT_CACHE if self.root_cache else 0) | (L.FLAG_KEEP_STATE if keep_state else 0)
@@ -76,6 +77,8 @@ class Shampoo4Config:
             flags |= L.FLAG_FP64_REFRESH
         if self.fp32_mfma:
             flags |= L.FLAG_FP32_MFMA
+        if self.debug:
+            flags |= L.FLAG_DEBUG
         return L.Config(self.beta, self.eps, self.qblock, self.bjorck_iters, self.power_iters, flags)
 
 

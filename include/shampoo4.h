@@ -133,6 +133,14 @@ typedef enum {
    for the same work.  Results differ from the fp32 kernel's in rounding order only.
    This flag keeps every product on the fp32 matrix cores (v_mfma_f32_32x32x2_f32). */
 #define SHAMPOO4_FLAG_FP32_MFMA 256u
+/* Debug checks (costly; results are unchanged): shampoo4_init checks that every
+   matrix-product and codec descriptor it builds stays inside the state or the workspace
+   (EINVAL otherwise), and every call that enqueues work first fills the workspace
+   temporaries (all but the io tables, the device flag, the rectified root eigenvectors,
+   the cached root matrices and the descriptor tables) with NaN, so a kernel that reads a
+   temporary before writing it in the same call yields NaN (raised by shampoo4_check).
+   With SHAMPOO4_FLAG_GRAPHS the fill is enqueued outside the captured graph. */
+#define SHAMPOO4_FLAG_DEBUG 512u
 
 /* 4-bit codebooks (16 levels, ascending, code = index; the zero level is code 7).
    LINEAR_SQUARE: sign(t) t^2 on t = -1 + 2j/15 with the j = 7 level exactly 0; times 225:

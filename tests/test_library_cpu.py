@@ -90,7 +90,8 @@ def test_plan_sizes():
     ([(4, 4)], {"k": -1}, L.EINVAL),
     ([(4, 4)], {"k": 17}, L.EINVAL),
     ([(4, 4)], {"pi": 0}, L.EINVAL),
-    ([(4, 4)], {"flags": 512}, L.EINVAL),
+    ([(4, 4)], {"flags": 1024}, L.EINVAL),
+    ([(4, 4)], {"flags": L.FLAG_DEBUG}, L.OK),
     ([(4, 4)], {"flags": L.FLAG_FP32_MFMA}, L.OK),
     ([(4, 4)], {"flags": L.FLAG_FP32_MFMA | L.FLAG_FP64_REFRESH | L.FLAG_ROOT_CACHE}, L.OK),
     ([(4, 4)], {"flags": L.FLAG_FP64_REFRESH}, L.OK),
