@@ -45,14 +45,27 @@ U32 = 2.0 ** -24     # float32 unit roundoff
 U64 = 2.0 ** -53     # float64 unit roundoff
 
 
-def resolved(lam, p, u=U32):
+def resolved(lam, p, u=U32, P=None, Q=None):
     """Eigenvalues float32 arithmetic determines: a Rayleigh quotient of an order-p
     statistic computed in float32 (and the statistic itself) carries an absolute error
     of up to about p u |L|, so eigenvalues below p u lam_max are not fixed by the
     float32 path: any value in [0, ~2 p u lam_max] is a correct result there, and
-    d = (lam + eps)^(-1/4) with it.  Returns (mask of resolved eigenvalues, threshold)."""
+    d = (lam + eps)^(-1/4) with it.
+    The refresh takes its eigenvectors from the QR of P = L V (one warm-started power
+    step, not a converged eigensolver).  Householder QR is backward stable column by
+    column, so column j of Q is fixed only to about u / min_{i <= j} sin(angle between p_i
+    and p_1 .. p_{i-1}); where P's columns are close to dependent (a rank-deficient
+    statistic whose warm start spans more than its range), the Rayleigh quotient of column
+    j moves by that factor more.  With P (the last QR's input) and Q (its orthonormal
+    factor) given, column j's floor is p u lam_max / min_{i <= j} (|R_ii| / |p_i|), R = Q^T P.
+    Returns (mask of resolved eigenvalues, per-eigenvalue threshold)."""
     lam = np.asarray(lam, np.float64)
     thr = p * u * float(lam.max()) if lam.size else 0.0
+    thr = np.full(lam.shape, thr)
+    if P is not None and lam.size:
+        rd = np.abs(np.einsum("ij,ij->j", Q, P))
+        sines = rd / np.maximum(np.linalg.norm(P, axis=0), 1e-300)
+        thr = thr / np.maximum(np.minimum.accumulate(sines), 1e-300)
     return lam > thr, thr
 
 
@@ -139,7 +152,10 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
                 flips[1] += 2 * c_own.size
                 if refresh:
                     d_own = o.root_scaling(lam_ref.astype(np.float32), eps)
-                    mask, thr = resolved(lam_ref, p, unit)
+                    P_last = Lt_ref @ V
+                    for _ in range(power_iters - 1):
+                        P_last = Lt_ref @ o.qr_positive(P_last)
+                    mask, thr = resolved(lam_ref, p, unit, P_last, Q_ref)
                     same = bool(np.array_equal(c_own, after["codes"]) and
                                 np.array_equal(s_own.view(np.uint32), after["scales"].view(np.uint32)))
                     new_root[(b, s)] = (c_own, s_own, d_own, mask, thr, same)
@@ -168,7 +184,8 @@ def _run_teacher_forced(shapes, grads_fn, steps, beta=0.95, eps=1e-6, k=1, power
                     bound = TOL + 0.5 * thr / (np.maximum(lam_own, 0.0) + eps)
                     assert np.all(rel[mask] <= bound[mask]), (label, t, b, s, "d from the pre-step state",
                                                               float((rel - bound)[mask].max()))
-                    assert np.all(st["lam"][~mask] <= 2 * thr), (label, t, b, s, "unresolved eigenvalue range")
+                    assert np.all(st["lam"][~mask] <= lam_own[~mask] + 2 * thr[~mask]), \
+                        (label, t, b, s, "unresolved eigenvalue range")
                     worst["d"] = max(worst["d"], float(rel[mask].max()) if mask.any() else 0.0)
         if not use_step:
             announce(f"step parity {label}: t={t} precondition")
