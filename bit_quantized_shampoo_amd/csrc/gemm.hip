@@ -380,8 +380,9 @@ __global__ __launch_bounds__(256 * KW, 2) void gemm_kernel(const GemmDesc* __res
     constexpr int A_ALL = (2 * KW * A_SZ > A_NEED) ? 2 * KW * A_SZ : A_NEED;
     __shared__ __attribute__((aligned(16))) float As[A_ALL];
     __shared__ __attribute__((aligned(16))) float Bs[2 * KW * B_SZ];
-    const int item = find_item(prefix, ndesc, blockIdx.x);
-    gemm_body<WM, WN, TM, TN, TA, TB, true, false, KW>(descs[item], blockIdx.x - prefix[item], io, As, Bs);
+    const int blk = gemm_block_index();
+    const int item = find_item(prefix, ndesc, blk);
+    gemm_body<WM, WN, TM, TN, TA, TB, true, false, KW>(descs[item], blk - prefix[item], io, As, Bs);
 }
 
 // Transpose mode per descriptor (uniform per workgroup); VEC and SLAB per launch.
@@ -394,9 +395,10 @@ __global__ __launch_bounds__(256 * KW, 2) void gemm_kernel_mixed(const GemmDesc*
     constexpr int A_ALL = (2 * KW * T::A_MAX > A_NEED) ? 2 * KW * T::A_MAX : A_NEED;
     __shared__ __attribute__((aligned(16))) float As[A_ALL];
     __shared__ __attribute__((aligned(16))) float Bs[2 * KW * T::B_MAX];
-    const int item = find_item(prefix, ndesc, blockIdx.x);
+    const int blk = gemm_block_index();
+    const int item = find_item(prefix, ndesc, blk);
     const GemmDesc& d = descs[item];
-    const int t = blockIdx.x - prefix[item];
+    const int t = blk - prefix[item];
     switch (d.flags & (GEMM_F_TA | GEMM_F_TB)) {
         case 0: gemm_body<WM, WN, TM, TN, false, false, VEC, SLAB, KW>(d, t, io, As, Bs); break;
         case GEMM_F_TB: gemm_body<WM, WN, TM, TN, false, true, VEC, SLAB, KW>(d, t, io, As, Bs); break;
@@ -472,6 +474,7 @@ void gemm_tile_dims(int cfg, int* bm, int* bn) {
     switch (cfg) {
         case GEMM_128x128: *bm = 128; *bn = 128; break;
         case GEMM_X3: *bm = GEMM_X3_BM; *bn = GEMM_X3_BN; break;
+        case GEMM_X3_64:
         case GEMM_64x64:
         case GEMM_64x64_K2: *bm = 64; *bn = 64; break;
         case GEMM_128x32: *bm = 128; *bn = 32; break;
@@ -485,8 +488,9 @@ hipError_t launch_gemm(int cfg, int mode, bool vec, bool slab, bool kscale, cons
     switch (cfg) {
         case GEMM_128x128: return launch_cfg<2, 2, 2, 2>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
         case GEMM_X3:
+        case GEMM_X3_64:
             if (slab) return hipErrorInvalidValue;
-            return launch_gemm_x3(mode, vec, kscale, descs, prefix, ndesc, ntiles, io, stream);
+            return launch_gemm_x3(cfg == GEMM_X3_64, mode, vec, kscale, descs, prefix, ndesc, ntiles, io, stream);
         case GEMM_64x64: return launch_cfg<2, 2, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);
         case GEMM_64x64_K2:   // (the K groups need 16-byte loads: a per-call caller operand may deny them)
             if (!vec || slab) return launch_cfg<2, 2, 1, 1>(mode, vec, slab, descs, prefix, ndesc, ntiles, io, stream);

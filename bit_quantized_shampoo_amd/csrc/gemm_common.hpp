@@ -18,9 +18,27 @@ __device__ __forceinline__ float keep_if(float v, bool keep) {
     return __uint_as_float(__float_as_uint(v) & (keep ? 0xffffffffu : 0u));
 }
 
+// Workgroups of a launch that are resident at once (two per CU on the 256 CUs).
+constexpr int GEMM_RESIDENT = 512;
+
+// Logical tile index of this workgroup.  Workgroups go to the eight XCDs round robin
+// (workgroup b to XCD b % 8), and each XCD has its own L2.  A launch that is resident at
+// once gives XCD x the contiguous range [x n / 8, (x + 1) n / 8) of its tiles (the
+// remainder, under eight, keeps its place), so the tiles one L2 serves share operand
+// panels; a larger launch keeps the plain order (its first wave would otherwise stream
+// eight distant regions of the batch at once).
+__device__ __forceinline__ int gemm_block_index() {
+    const int b = blockIdx.x, n = gridDim.x;
+    if (n > GEMM_RESIDENT) return b;
+    const int n8 = n >> 3;
+    return b < 8 * n8 ? (b & 7) * n8 + (b >> 3) : b;
+}
+
 // Output tile of workgroup t of a descriptor: split-K chunk ks, tile (tile_m, tile_n).
 // Symmetric products enumerate the tiles on and above the diagonal column by column:
-// t = tn (tn + 1) / 2 + tm with tm <= tn.
+// t = tn (tn + 1) / 2 + tm with tm <= tn.  Other products take the tiles column by column
+// (tile_m fastest), or, in a launch resident at once, in groups of up to eight tile rows
+// (rows fastest within a group), so a run of 64 consecutive tiles covers 8 x 8 of them.
 template <int BM, int BN>
 __device__ __forceinline__ void decode_tile(const GemmDesc& dsc, int t, int& ks, int& tile_m, int& tile_n) {
     const int tiles_m = dsc.tiles_m;
@@ -34,6 +52,13 @@ __device__ __forceinline__ void decode_tile(const GemmDesc& dsc, int t, int& ks,
         while (tn * (tn + 1) / 2 > tmn) --tn;
         tile_n = tn;
         tile_m = tmn - tn * (tn + 1) / 2;
+    } else if ((int)gridDim.x <= GEMM_RESIDENT) {
+        const int tiles_n = (dsc.N + BN - 1) / BN;
+        const int g = tmn / (8 * tiles_n);
+        const int gh = min(8, tiles_m - 8 * g);
+        const int local = tmn - 8 * g * tiles_n;
+        tile_m = 8 * g + local % gh;
+        tile_n = local / gh;
     } else {
         tile_m = tmn % tiles_m;
         tile_n = tmn / tiles_m;

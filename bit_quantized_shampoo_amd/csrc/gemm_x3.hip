@@ -20,14 +20,18 @@
 //    workgroups, so one's split work runs beside the other's matrix-core work (larger
 //    tiles with one workgroup per CU, and waves specialized into loaders and multipliers,
 //    measured slower);
-//  * BK = 16: one 32 x 32 x 16 step per slice.  Every thread loads runs of eight
+//  * small batches (too few 128 x 128 tiles to fill the GPU) take a 64 x 64 tile: one
+//    accumulator block per wave and slices of 32 k (two matrix-core steps per slice), so
+//    a workgroup still loads one run of eight k of A and one of B per thread and slice;
+//  * BK = 16 (64 x 64: 32): 32 x 32 x 16 steps per slice.  Every thread loads runs of eight
 //    consecutive k of rows of op(A) and op(B) per slice (two 16-byte loads where the
 //    operand is K-contiguous in memory, eight 4-byte buffer loads along k where it is M- or
 //    N-contiguous, each coalesced across the wave), splits them and stores each piece
 //    plane as one 16-byte LDS store, K-contiguous, so every operand fragment of the matrix
 //    cores is one 16-byte LDS read whatever the operand's layout in memory;
-//  * LDS: for each operand and piece a [rows][24] bf16 plane (48-byte pitch: eight
-//    consecutive rows read at distinct 16-byte bank groups), double buffered, 72 KB;
+//  * LDS: for each operand and piece a [rows][BK + 8] bf16 plane (48- or 80-byte pitch:
+//    consecutive rows read at distinct 16-byte bank groups), double buffered, 72 KB
+//    (64 x 64: 60 KB);
 //  * the split costs about 5.5 vector instructions per element loaded, against
 //    TM TN 6 / (TM + TN) matrix-core instructions per element pair: large per-wave
 //    tiles keep it small next to the matrix-core work;
@@ -53,17 +57,23 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Tile geometry: 2 x 2 waves of TM x TN blocks of 32 x 32.
-template <int TM_, int TN_>
+// Tile geometry: 2 x 2 waves of TM x TN blocks of 32 x 32, slices of BK k (BK / 16
+// matrix-core steps; each thread loads runs of eight k).
+template <int TM_, int TN_, int BK_>
 struct X3Tile {
     static constexpr int WM = 2, WN = 2, TM = TM_, TN = TN_;
-    static constexpr int BM = WM * TM * 32, BN = WN * TN * 32, BK = 16;
-    static constexpr int PITCH = 24;                      // bf16 per LDS row
+    static constexpr int BM = WM * TM * 32, BN = WN * TN * 32, BK = BK_;
+    static constexpr int KG = BK / 8;                     // runs of eight k per row and slice
+    static constexpr int KSTEPS = BK / 16;                // 32 x 32 x 16 steps per slice
+    // bf16 per LDS row: a pitch of (BK + 8) bf16 puts eight (BK = 16: 48-byte pitch) or
+    // sixteen (BK = 32: 80-byte pitch) consecutive rows in distinct 16-byte bank groups
+    static constexpr int PITCH = BK + 8;
     static constexpr int PLANE_A = BM * PITCH, PLANE_B = BN * PITCH;
     static constexpr int BUF = 3 * (PLANE_A + PLANE_B);   // bf16 per buffer
-    static constexpr int NIA = BM * 2 / 256, NIB = BN * 2 / 256;   // row halves per thread
+    static constexpr int NIA = BM * KG / 256, NIB = BN * KG / 256;   // runs per thread
     static constexpr int LDS_BYTES = 2 * BUF * 2;
-    static_assert(BM * 2 % 256 == 0 && BN * 2 % 256 == 0, "whole row halves per thread");
+    static_assert(BK == 16 || BK == 32, "slice depth");
+    static_assert(BM * KG % 256 == 0 && BN * KG % 256 == 0, "whole runs per thread");
     static_assert(LDS_BYTES >= 4 * (2 * 32 * 33 + 2 * 32 * 33) && LDS_BYTES >= 4 * WM * BN,
                   "LDS too small for the epilogue");
 };
@@ -159,7 +169,7 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
                                         uint16_t* __restrict__ lds) {
     constexpr int WM = T::WM, TM = T::TM, TN = T::TN, BM = T::BM, BN = T::BN, BK = T::BK;
     constexpr int PITCH = T::PITCH, PLANE_A = T::PLANE_A, PLANE_B = T::PLANE_B, BUF = T::BUF;
-    constexpr int NIA = T::NIA, NIB = T::NIB;
+    constexpr int NIA = T::NIA, NIB = T::NIB, KG = T::KG, KSTEPS = T::KSTEPS;
     int ks, tile_m, tile_n;
     decode_tile<BM, BN>(dsc, t, ks, tile_m, tile_n);
     const bool sym = (dsc.flags & GEMM_F_SYM) != 0;
@@ -189,24 +199,24 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
     const int h = lane >> 5;
     const int l32 = lane & 31;
 
-    // Row halves (eight k of one row) of the slice that this thread loads: item
-    // j = tid + 256 i of an operand with R rows is (row (j % 8) + 8 (j / 16), half
-    // (j / 8) % 2) where the operand is K-contiguous in memory (two threads per row, 64
-    // contiguous bytes; eight consecutive lanes store eight rows at one half, so the
-    // 16-byte LDS stores fall in distinct bank groups) and (row j % R, half j / R) where it
-    // is not (consecutive rows along the wave).
+    // Runs (eight k of one row) of the slice that this thread loads: item j = tid + 256 i
+    // of an operand with R rows is (row (j % 8) + 8 (j / (8 KG)), run (j / 8) % KG) where
+    // the operand is K-contiguous in memory (KG threads per row, 32 KG contiguous bytes;
+    // eight consecutive lanes store eight rows at one run, so the 16-byte LDS stores fall
+    // in distinct bank groups) and (row j % R, run j / R) where it is not (consecutive
+    // rows along the wave).
     int ar[NIA], ak[NIA], br[NIB], bk[NIB];
 #pragma unroll
     for (int i = 0; i < NIA; ++i) {
         const int j = tid + 256 * i;
-        ar[i] = TA ? (j & (BM - 1)) : ((j & 7) + 8 * (j >> 4));
-        ak[i] = TA ? (j / BM) * 8 : ((j >> 3) & 1) * 8;
+        ar[i] = TA ? (j & (BM - 1)) : ((j & 7) + 8 * (j / (8 * KG)));
+        ak[i] = TA ? (j / BM) * 8 : ((j >> 3) % KG) * 8;
     }
 #pragma unroll
     for (int i = 0; i < NIB; ++i) {
         const int j = tid + 256 * i;
-        br[i] = TB ? ((j & 7) + 8 * (j >> 4)) : (j & (BN - 1));
-        bk[i] = TB ? ((j >> 3) & 1) * 8 : (j / BN) * 8;
+        br[i] = TB ? ((j & 7) + 8 * (j / (8 * KG))) : (j & (BN - 1));
+        bk[i] = TB ? ((j >> 3) % KG) * 8 : (j / BN) * 8;
     }
 
     // VEC: every load is a buffer load over the operand as stored; a row (K-contiguous
@@ -295,32 +305,39 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
     };
 
     struct Frags {
-        bf16x8 a[3][TM], b[3][TN];
+        bf16x8 a[KSTEPS][3][TM], b[KSTEPS][3][TN];
     };
     auto read_frags = [&](Frags& F, int buf) {
         const uint16_t* base = lds + buf * BUF;
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
+        for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-            for (int m = 0; m < TM; ++m)
-                F.a[p][m] = *reinterpret_cast<const bf16x8*>(base + p * PLANE_A +
-                                                             (wave_m * TM * 32 + m * 32 + l32) * PITCH + h * 8);
+            for (int p = 0; p < 3; ++p) {
 #pragma unroll
-            for (int n = 0; n < TN; ++n)
-                F.b[p][n] = *reinterpret_cast<const bf16x8*>(base + 3 * PLANE_A + p * PLANE_B +
-                                                             (wave_n * TN * 32 + n * 32 + l32) * PITCH + h * 8);
-        }
+                for (int m = 0; m < TM; ++m)
+                    F.a[s][p][m] = *reinterpret_cast<const bf16x8*>(
+                        base + p * PLANE_A + (wave_m * TM * 32 + m * 32 + l32) * PITCH + s * 16 + h * 8);
+#pragma unroll
+                for (int n = 0; n < TN; ++n)
+                    F.b[s][p][n] = *reinterpret_cast<const bf16x8*>(
+                        base + 3 * PLANE_A + p * PLANE_B + (wave_n * TN * 32 + n * 32 + l32) * PITCH + s * 16 + h * 8);
+            }
     };
+    // per 16-k step the six piece products in one fixed order, so every output sums its
+    // terms in the same sequence whatever the tile and slice depth
     auto mfmas = [&](const Frags& F) {
         constexpr int PA[6] = {0, 0, 1, 0, 2, 1};
         constexpr int PB[6] = {0, 1, 0, 2, 0, 1};
 #pragma unroll
-        for (int q = 0; q < 6; ++q)
+        for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-            for (int m = 0; m < TM; ++m)
+            for (int q = 0; q < 6; ++q)
 #pragma unroll
-                for (int n = 0; n < TN; ++n)
-                    acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[PA[q]][m], F.b[PB[q]][n], acc[m][n], 0, 0, 0);
+                for (int m = 0; m < TM; ++m)
+#pragma unroll
+                    for (int n = 0; n < TN; ++n)
+                        acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[s][PA[q]][m], F.b[s][PB[q]][n],
+                                                                            acc[m][n], 0, 0, 0);
     };
 
     // Two register sets: slice s + 2 is loaded while slice s is multiplied and slice s + 1
@@ -366,8 +383,9 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel(const GemmDesc* __restr
                                                               const int* __restrict__ prefix, int ndesc,
                                                               const IoEntry* __restrict__ io) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::BUF];
-    const int item = find_item(prefix, ndesc, blockIdx.x);
-    x3_body<T, TA, TB, KS, VEC>(descs[item], blockIdx.x - prefix[item], io, lds);
+    const int blk = gemm_block_index();
+    const int item = find_item(prefix, ndesc, blk);
+    x3_body<T, TA, TB, KS, VEC>(descs[item], blk - prefix[item], io, lds);
 }
 
 // Transpose mode and K scale per descriptor (uniform per workgroup).
@@ -376,9 +394,10 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel_mixed(const GemmDesc* _
                                                                     const int* __restrict__ prefix, int ndesc,
                                                                     const IoEntry* __restrict__ io) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::BUF];
-    const int item = find_item(prefix, ndesc, blockIdx.x);
+    const int blk = gemm_block_index();
+    const int item = find_item(prefix, ndesc, blk);
     const GemmDesc& d = descs[item];
-    const int t = blockIdx.x - prefix[item];
+    const int t = blk - prefix[item];
     if (d.kscale) {
         switch (d.flags & (GEMM_F_TA | GEMM_F_TB)) {
             case 0: x3_body<T, false, false, true, VEC>(d, t, io, lds); break;
@@ -396,19 +415,21 @@ __global__ __launch_bounds__(256, 2) void gemm_x3_kernel_mixed(const GemmDesc* _
     }
 }
 
-using X3T = X3Tile<2, 2>;
+// the batched tile (128 x 128, 16-k slices) and the small-batch tile (64 x 64, 32-k
+// slices: the same matrix-core steps per slice and workgroup as the large tile's half)
+using X3T = X3Tile<2, 2, 16>;
+using X3S = X3Tile<1, 1, 32>;
 static_assert(X3T::BM == GEMM_X3_BM && X3T::BN == GEMM_X3_BN, "host and kernel tile");
+static_assert(X3S::BM == 64 && X3S::BN == 64, "host and kernel tile");
 
-}  // namespace
-
-hipError_t launch_gemm_x3(int mode, bool vec, bool kscale, const GemmDesc* descs, const int* prefix, int ndesc,
+template <class Tile>
+hipError_t launch_x3_tile(int mode, bool vec, bool kscale, const GemmDesc* descs, const int* prefix, int ndesc,
                           int ntiles, const IoEntry* io, hipStream_t stream) {
-    if (ntiles <= 0) return hipSuccess;
     const dim3 grid(ntiles), block(256);
 #define S4_X3K(TA, TB, KS)                                                                                  \
     do {                                                                                                    \
-        if (vec) S4_LAUNCH((gemm_x3_kernel<X3T, TA, TB, KS, true>), grid, block, 0, stream, descs, prefix, ndesc, io); \
-        else S4_LAUNCH((gemm_x3_kernel<X3T, TA, TB, KS, false>), grid, block, 0, stream, descs, prefix, ndesc, io);    \
+        if (vec) S4_LAUNCH((gemm_x3_kernel<Tile, TA, TB, KS, true>), grid, block, 0, stream, descs, prefix, ndesc, io); \
+        else S4_LAUNCH((gemm_x3_kernel<Tile, TA, TB, KS, false>), grid, block, 0, stream, descs, prefix, ndesc, io);    \
     } while (0)
 #define S4_X3(TA, TB)                          \
     do {                                       \
@@ -421,13 +442,22 @@ hipError_t launch_gemm_x3(int mode, bool vec, bool kscale, const GemmDesc* descs
         case GEMM_F_TA: S4_X3(true, false); break;
         case GEMM_F_TA | GEMM_F_TB: S4_X3(true, true); break;
         default:
-            if (vec) S4_LAUNCH((gemm_x3_kernel_mixed<X3T, true>), grid, block, 0, stream, descs, prefix, ndesc, io);
-            else S4_LAUNCH((gemm_x3_kernel_mixed<X3T, false>), grid, block, 0, stream, descs, prefix, ndesc, io);
+            if (vec) S4_LAUNCH((gemm_x3_kernel_mixed<Tile, true>), grid, block, 0, stream, descs, prefix, ndesc, io);
+            else S4_LAUNCH((gemm_x3_kernel_mixed<Tile, false>), grid, block, 0, stream, descs, prefix, ndesc, io);
             break;
     }
 #undef S4_X3
 #undef S4_X3K
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_x3(bool small, int mode, bool vec, bool kscale, const GemmDesc* descs, const int* prefix,
+                          int ndesc, int ntiles, const IoEntry* io, hipStream_t stream) {
+    if (ntiles <= 0) return hipSuccess;
+    return small ? launch_x3_tile<X3S>(mode, vec, kscale, descs, prefix, ndesc, ntiles, io, stream)
+                 : launch_x3_tile<X3T>(mode, vec, kscale, descs, prefix, ndesc, ntiles, io, stream);
 }
 
 }  // namespace s4

@@ -11,11 +11,12 @@ namespace s4 {
 // Tile shapes of the fp32 MFMA GEMM (workgroup of 4 waves).
 // tile shapes (the first GEMM_NCFG are the shape classes); GEMM_64x64_K2: the 64 x 64
 // tile with two groups of four waves splitting K (16-byte loads, no split-K slabs)
-// GEMM_X3: the bf16 matrix cores with each fp32 operand split into three bf16 pieces
-// (gemm_x3.hip; tile GEMM_X3_BM x GEMM_X3_BN), for launches that would take 128 x 128
-// tiles and sum no split-K slabs.
+// GEMM_X3 / GEMM_X3_64: the bf16 matrix cores with each fp32 operand split into three
+// bf16 pieces (gemm_x3.hip; tile GEMM_X3_BM x GEMM_X3_BN, or 64 x 64), for launches that
+// would take 128 x 128 (64 x 64) tiles and sum no split-K slabs.
 enum GemmCfg { GEMM_128x128 = 0, GEMM_64x64 = 1, GEMM_32x128 = 2, GEMM_128x32 = 3, GEMM_NCFG = 4,
-               GEMM_64x64_K2 = 5, GEMM_X3 = 6 };
+               GEMM_64x64_K2 = 5, GEMM_X3 = 6, GEMM_X3_64 = 7 };
+inline bool gemm_cfg_x3(int cfg) { return cfg == GEMM_X3 || cfg == GEMM_X3_64; }
 constexpr int GEMM_MODE_MIXED = -1;   // descriptors of one launch carry different transposes
 void gemm_tile_dims(int cfg, int* bm, int* bn);
 // mode: GEMM_F_TA | GEMM_F_TB shared by all descriptors, or GEMM_MODE_MIXED.
@@ -29,8 +30,8 @@ hipError_t launch_gemm(int cfg, int mode, bool vec, bool slab, bool kscale, cons
 // The three-piece bf16 product (no split-K slab sums; vec as for launch_gemm, with every
 // operand under 2 GiB) on 128 x 128 tiles (2 x 2 waves of 2 x 2 blocks of 32 x 32).
 constexpr int GEMM_X3_BM = 128, GEMM_X3_BN = 128;
-hipError_t launch_gemm_x3(int mode, bool vec, bool kscale, const GemmDesc* descs, const int* prefix, int ndesc,
-                          int ntiles, const IoEntry* io, hipStream_t stream);
+hipError_t launch_gemm_x3(bool small, int mode, bool vec, bool kscale, const GemmDesc* descs, const int* prefix,
+                          int ndesc, int ntiles, const IoEntry* io, hipStream_t stream);
 // The allocation-free batched GEMM keeps its descriptor table and tile prefix (one 256-byte
 // aligned piece each) in a static device array of this size per GPU.
 constexpr size_t GEMM_STATIC_SCRATCH_BYTES = 384 * 1024;

@@ -164,7 +164,7 @@ struct shampoo4_ctx_s {
     // variant: with or without the cached rectified eigenvectors, and with or without
     // 16-byte loads of the gradients, which the captured kernels bake in)
     bool use_graphs = false;
-    bool x3 = true;                       // 128 x 128 products on the three-piece bf16 kernel
+    bool x3 = true;                       // 128 x 128 and 64 x 64 products on the three-piece bf16 kernel
     // SHAMPOO4_FLAG_DEBUG: workspace temporaries (offset, bytes), filled with NaN before each
     // call; a descriptor found reaching outside the state or workspace at init
     bool debug = false;
@@ -328,8 +328,15 @@ struct shampoo4_ctx_s {
     // little at the 128 x 128 tile).  With by_shape, products are grouped by tile shape
     // class (one launch each) when the padding this saves outweighs the extra launches;
     // otherwise one launch covers them all.  Products with a column-dot epilogue stay in
-    // one launch (their partial rows follow one tile height).
-    Seq make_gemm(std::vector<GemmItem> items, int fam, bool split_modes = false, bool by_shape = true) {
+    // one launch (their partial rows follow one tile height).  groups (optional): the
+    // products of each launch, in launch order.
+    Seq make_gemm(std::vector<GemmItem> items, int fam, bool split_modes = false, bool by_shape = true,
+                  std::vector<std::vector<GemmItem>>* groups = nullptr) {
+        auto launch_one = [&](const std::vector<GemmItem>& part, int cfgsel) {
+            Seq g = gemm_launch(part, fam, cfgsel);
+            if (groups && !g.empty()) groups->push_back(part);
+            return g;
+        };
         if (split_modes) {
             Seq out;
             for (int mode = 0; mode < 4; ++mode) {
@@ -337,7 +344,7 @@ struct shampoo4_ctx_s {
                 for (auto& it : items)
                     if (((it.ta ? GEMM_F_TA : 0) | (it.tb ? GEMM_F_TB : 0)) == mode) part.push_back(it);
                 if (part.empty()) continue;
-                Seq g = make_gemm(part, fam, false, by_shape);
+                Seq g = make_gemm(part, fam, false, by_shape, groups);
                 out.insert(out.end(), g.begin(), g.end());
             }
             return out;
@@ -373,21 +380,21 @@ struct shampoo4_ctx_s {
                     Seq out;
                     for (int c = 0; c <= GEMM_NCFG; ++c) {
                         if (part[c].empty()) continue;
-                        Seq g = gemm_launch(part[c], fam, c < GEMM_NCFG ? c : default_cfg(part[c]));
+                        Seq g = launch_one(part[c], c < GEMM_NCFG ? c : default_cfg(part[c]));
                         out.insert(out.end(), g.begin(), g.end());
                     }
                     return out;
                 }
             } else if (nclass == 1) {
                 for (int c = 0; c < GEMM_NCFG; ++c)
-                    if (!part[c].empty()) return gemm_launch(part[c], fam, c);
+                    if (!part[c].empty()) return launch_one(part[c], c);
             }
         }
-        return gemm_launch(items, fam, default_cfg(items));
+        return launch_one(items, default_cfg(items));
     }
 
-    // One launch of `items` on tile shape cfgsel (128 x 128: on the three-piece bf16 kernel
-    // unless allow_x3 is false or the context keeps the fp32 matrix cores).
+    // One launch of `items` on tile shape cfgsel (128 x 128 and 64 x 64: on the three-piece
+    // bf16 kernel unless allow_x3 is false or the context keeps the fp32 matrix cores).
     Seq gemm_launch(const std::vector<GemmItem>& items, int fam, int cfgsel, bool allow_x3 = true) {
         std::vector<GemmDesc> ds;
         int modes = 0, first_mode = -2;
@@ -401,10 +408,14 @@ struct shampoo4_ctx_s {
             ds.push_back(d);
         }
         if (ds.empty()) return {};
-        // the three-piece bf16 kernel takes the 128 x 128 launches without split-K slab sums
+        // the three-piece bf16 kernel takes the 128 x 128 and 64 x 64 launches without
+        // split-K slab sums
         bool slab = false;
         for (auto& d : ds) slab = slab || d.anslab > 1 || d.bnslab > 1;
-        if (cfgsel == GEMM_128x128 && x3 && allow_x3 && !slab) cfgsel = GEMM_X3;
+        if (x3 && allow_x3 && !slab) {
+            if (cfgsel == GEMM_128x128) cfgsel = GEMM_X3;
+            else if (cfgsel == GEMM_64x64) cfgsel = GEMM_X3_64;
+        }
         int bm, bn;
         gemm_tile_dims(cfgsel, &bm, &bn);
         // a symmetric product computes the tiles on and above the diagonal (square tiles,
@@ -1390,18 +1401,20 @@ struct shampoo4_ctx_s {
                 q2.push_back({d2, false, false});
             }
             root_mat = make_gemm(rm, FAM_GEMM_PRECOND);
-            pre_cached[0] = make_gemm(q1, FAM_GEMM_PRECOND);
-            pre_cached[1] = make_gemm(q2, FAM_GEMM_PRECOND);
-            // both forms sum each output over K in the same order (one group of waves
-            // per tile, whatever its shape, on the same kind of matrix core), so P is
-            // bit-identical whichever runs
-            auto all_x3 = [](const Seq& sq) {
-                bool all = !sq.empty();
-                for (auto& L : sq) all = all && L.cfg == GEMM_X3;
-                return all;
-            };
-            pre_side[0] = gemm_launch(q1, FAM_GEMM_PRECOND, GEMM_128x128, all_x3(pre_cached[0]));
-            pre_side[1] = gemm_launch(q2, FAM_GEMM_PRECOND, GEMM_128x128, all_x3(pre_cached[1]));
+            // the copy beside the QR chain takes each launch's products on 128 x 128 tiles
+            // on the same kind of matrix core: both forms sum each output over K in the
+            // same order (one group of waves per tile, the same steps per 16 k, whatever
+            // the tile), so P is bit-identical whichever runs
+            const std::vector<GemmItem>* qs[2] = {&q1, &q2};
+            for (int i = 0; i < 2; ++i) {
+                std::vector<std::vector<GemmItem>> groups;
+                pre_cached[i] = make_gemm(*qs[i], FAM_GEMM_PRECOND, false, true, &groups);
+                pre_side[i].clear();
+                for (size_t g = 0; g < groups.size(); ++g) {
+                    Seq sq = gemm_launch(groups[g], FAM_GEMM_PRECOND, GEMM_128x128, gemm_cfg_x3(pre_cached[i][g].cfg));
+                    pre_side[i].insert(pre_side[i].end(), sq.begin(), sq.end());
+                }
+            }
             for (auto& sq : pre_cached)
                 for (auto& L : sq)
                     if (L.cfg == GEMM_64x64_K2) L.cfg = GEMM_64x64;
@@ -1849,7 +1862,7 @@ struct shampoo4_ctx_s {
             launch_timing().start = launch_timing().stop = nullptr;
             if (launched) {
                 rec.family = fam;
-                rec.x3 = L.kind == K_GEMM && L.cfg == GEMM_X3;
+                rec.x3 = L.kind == K_GEMM && gemm_cfg_x3(L.cfg);
                 rec.flops = L.flops;
                 rec.bytes = L.bytes;
                 recs.push_back(rec);

@@ -318,7 +318,7 @@ def codebook(name: str = "ls"):
 def gemm_batched(As, Bs, Ds=None, transA=False, transB=False, alpha=1.0, beta=0.0, Cs=None,
                  workspace: torch.Tensor | None = None, stream=None, kernel: str = "auto"):
     """D_i = alpha op(A_i) op(B_i) + beta C_i on the MFMA kernels (row-major 2-D tensors).
-    kernel: "auto" (tile shape by batch; 128 x 128 launches on the three-piece bf16 kernel),
+    kernel: "auto" (tile shape by batch; 128 x 128 and 64 x 64 launches on the three-piece bf16 kernel),
     "fp32" (fp32 matrix cores only) or "x3" (128 x 128 tiles on the three-piece bf16 kernel
     whatever the batch)."""
     kinds = {"auto": L.GEMM_AUTO, "fp32": L.GEMM_FP32, "x3": L.GEMM_X3}

@@ -121,10 +121,11 @@ typedef enum {
    columns); EINVAL together with QR_LOOKAHEAD or FP32_STATE.  The workspace holds the float64 matrices
    instead of most float32 ones (about 84 p^2 bytes per side against 48 p^2). */
 #define SHAMPOO4_FLAG_FP64_REFRESH 128u
-/* Matrix products of launches on 128 x 128 tiles (the products of large batches: the
-   statistics GG^T / G^TG and V diag(lam) V^T of "Kronecker factorization", Bjorck's
-   V^T V and V (V^T V) of the rectification, the power step, Householder and Rayleigh
-   products and the preconditioner sandwich) run by default on the bf16 matrix cores:
+/* Matrix products of launches on 128 x 128 and 64 x 64 tiles (the statistics GG^T / G^TG
+   and V diag(lam) V^T of "Kronecker factorization", Bjorck's V^T V and V (V^T V) of the
+   rectification, the power step, Householder and Rayleigh products and the
+   preconditioner sandwich; not the skinny panel-width products of the blocked QR nor
+   products whose operands sum split-K slabs) run by default on the bf16 matrix cores:
    every fp32 operand element is split exactly into three bf16 pieces (x = x1 + x2 + x3,
    eight significant bits each) and the six partial products of order >= 2^-16
    (x1y1, x1y2, x2y1, x1y3, x3y1, x2y2) are accumulated in fp32.  The dropped products are
@@ -369,8 +370,9 @@ SHAMPOO4_API size_t shampoo4_gemm_workspace_bytes(int32_t count);
  *   D_i = alpha * op(A_i) op(B_i) + beta * C_i     (op = transpose when trans* != 0)
  * with op(A_i) [M,K], op(B_i) [K,N], C_i and D_i [M,N] row-major.  All pointer arrays
  * are host arrays of device pointers; C may be NULL when beta == 0.  Used to test and
- * time the matrix-product kernels every stage of the step runs on (a 128 x 128 launch on the
- * three-piece bf16 kernel: see SHAMPOO4_FLAG_FP32_MFMA and shampoo4_gemm_batched_ex).  `workspace` is a
+ * time the matrix-product kernels every stage of the step runs on (a 128 x 128 or 64 x 64
+ * launch on the three-piece bf16 kernel: see SHAMPOO4_FLAG_FP32_MFMA and
+ * shampoo4_gemm_batched_ex).  `workspace` is a
  * 256-byte aligned device buffer of at least shampoo4_gemm_workspace_bytes(count)
  * bytes that receives the descriptors (one host-to-device copy from pageable memory
  * is enqueued before the kernel); it must stay untouched until the kernel ran. */
@@ -385,13 +387,15 @@ SHAMPOO4_API shampoo4_status shampoo4_gemm_batched(int32_t count, int32_t transA
 /* shampoo4_gemm_batched with a choice of kernel (arguments, workspace and errors as
  * there; EINVAL for another `kernel` value):
  *   SHAMPOO4_GEMM_AUTO  as shampoo4_gemm_batched: the launch's tile shape follows the batch
- *                       (128 x 128 once the products have 512 such tiles), and a 128 x 128
- *                       launch runs on the three-piece bf16 kernel (SHAMPOO4_FLAG_FP32_MFMA)
- *                       when every operand allows 16-byte loads (16-byte aligned base,
- *                       pitch and contiguous extent multiples of 4);
+ *                       (128 x 128 once the products have 512 such tiles, else 64 x 64;
+ *                       32-wide tiles for products with a side of at most 32), and a
+ *                       128 x 128 or 64 x 64 launch runs on the three-piece bf16 kernel
+ *                       (SHAMPOO4_FLAG_FP32_MFMA), with 16-byte loads where every operand
+ *                       allows them (16-byte aligned base, pitch and contiguous extent
+ *                       multiples of 4), else 4-byte loads;
  *   SHAMPOO4_GEMM_FP32  every product on the fp32 matrix cores;
  *   SHAMPOO4_GEMM_X3    one launch on 128 x 128 tiles whatever the batch, on the three-piece
- *                       bf16 kernel when the operands allow 16-byte loads (else fp32). */
+ *                       bf16 kernel. */
 #define SHAMPOO4_GEMM_AUTO 0
 #define SHAMPOO4_GEMM_FP32 1
 #define SHAMPOO4_GEMM_X3 2

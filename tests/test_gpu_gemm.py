@@ -1,8 +1,10 @@
 """The matrix-product kernels in isolation against float64 NumPy products: the fp32
-matrix-core kernel (every tile shape, chosen by batch size) and the three-piece bf16
-kernel (forced onto 128 x 128 tiles whatever the batch), every transpose mode, ragged
-edges, strided and unaligned operands, alpha/beta.  Both must meet the fp32 bound
-4 eps |A||B| sqrt(K + 1) elementwise."""
+matrix-core kernel (every tile shape, chosen by batch size), the three-piece bf16 kernel
+on its small-batch 64 x 64 tile (auto) and forced onto 128 x 128 tiles whatever the
+batch (x3), every transpose mode, ragged edges, strided and unaligned operands,
+alpha/beta.  All must meet the fp32 bound 4 eps |A||B| sqrt(K + 1) elementwise; the two
+three-piece tiles must agree bit for bit (each output sums the same terms in the same
+order)."""
 
 import numpy as np
 import pytest
@@ -90,3 +92,30 @@ def test_gemm_alpha_beta_and_strides(kernel):
     gemm_batched([A0], [B0], [D0], alpha=1.0, beta=2.0, Cs=[C], kernel=kernel)
     torch.cuda.synchronize()
     assert torch.equal(D0, 2.0 * C)
+
+
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("shapes", [
+    [(1024, 1024, 1024)] * 2,             # the single-block products of a 1024 block
+    [(130, 70, 129), (31, 200, 5)],       # ragged, K not a multiple of 16 or 32
+    [(300, 260, 1000)] * 3,               # K a multiple of 8, not of 32
+])
+def test_x3_tiles_bit_identical(ta, tb, shapes):
+    """64 x 64 tiles (32-k slices) and 128 x 128 tiles (16-k slices) of the three-piece
+    kernel: every output takes the same six piece products per 16 k in the same order, so
+    the results are equal bit for bit (the step's precondition beside the QR chain relies
+    on it)."""
+    require_gpu()
+    from bit_quantized_shampoo_amd import gemm_batched
+    rng = np.random.default_rng(len(shapes) * 7 + 2 * ta + tb)
+    As, Bs = [], []
+    for (M, N, K) in shapes:
+        As.append(to_dev(rng.standard_normal((K, M) if ta else (M, K)).astype(np.float32)))
+        Bs.append(to_dev(rng.standard_normal((N, K) if tb else (K, N)).astype(np.float32)))
+    announce(f"x3 tiles bit-identical ta={ta} tb={tb} shapes={shapes}")
+    D64, _ = gemm_batched(As, Bs, transA=ta, transB=tb, kernel="auto")
+    D128, _ = gemm_batched(As, Bs, transA=ta, transB=tb, kernel="x3")
+    torch.cuda.synchronize()
+    _check(As, Bs, D64, ta, tb, 1.0, 0.0, None)
+    for a, b in zip(D64, D128):
+        assert torch.equal(a, b)
