@@ -289,6 +289,22 @@ def test_ragged_batches(shapes, k, power_iters, T, cache, qr):
                         root_cache=cache, label=f"ragged {shapes} qr={qr}", qr=qr)
 
 
+def test_blocked_qr_wide_outer_blocks():
+    """Orders from 2048 take 256-column outer blocks in the blocked QR: a 2100-order side
+    (eight full outer blocks and a ragged one of 52 columns) against the oracle."""
+    require_gpu()
+    shapes = [(2100, 300)]
+    rng = np.random.default_rng(2100)
+    scales = [(10.0 ** rng.uniform(-1, 1, (m, 1))) * (10.0 ** rng.uniform(-1, 1, (1, n))) for m, n in shapes]
+
+    def grads(t):
+        r = np.random.default_rng([t, 2100])
+        return [(r.standard_normal((m, n)) * sc).astype(np.float32) for (m, n), sc in zip(shapes, scales)]
+
+    _run_teacher_forced(shapes, grads, 3, k=1, power_iters=1, root_interval=1, root_cache=True,
+                        label="blocked qr 2100", qr="blocked")
+
+
 def test_single_1024_steps():
     """The 1024 x 1024 workload for its first root-refresh period (stats every step,
     root every 10 steps), so precondition runs with the identity root and then with
