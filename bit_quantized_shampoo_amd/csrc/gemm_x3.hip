@@ -227,6 +227,11 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
     // from the operand's base at the thread's first slice.
     const __amdgpu_buffer_rsrc_t ra = operand_rsrc(A, lda, TA ? K : M, TA ? M : K);
     const __amdgpu_buffer_rsrc_t rb = operand_rsrc(B, ldb, TB ? N : K, TB ? K : N);
+    // the K scale as a buffer of K floats: where 16-byte loads are allowed and one operand
+    // is K-contiguous (so K is a multiple of 4), a run's eight scales are two 16-byte loads
+    // (a quad past K reads zero); otherwise eight clamped 4-byte loads
+    constexpr bool KQUAD = VEC && (!TA || TB);
+    [[maybe_unused]] const __amdgpu_buffer_rsrc_t rk = operand_rsrc(KS ? ksc : A, 0, 1, K);
     const int astep = (int)(lda * 4), bstep = (int)(ldb * 4);
     uint32_t aoff[NIA], boff[NIB];
 #pragma unroll
@@ -270,7 +275,14 @@ __device__ __forceinline__ void x3_body(const GemmDesc& dsc, int t, const IoEntr
             if constexpr (!VEC) scalar8<TB>(R.b[i], B, ldb, col0 + br[i], k0 + bk[i], TB ? N : K, TB ? K : N);
             else if constexpr (TB) row8(R.b[i], rb, boff[i] + s * BK * 4, k0 + bk[i] < K, k0 + bk[i] + 4 < K);
             else col8(R.b[i], rb, boff[i] + s * BK * bstep, bstep);
-            if constexpr (KS) {
+            if constexpr (KS && KQUAD) {
+                const int kk = k0 + bk[i];
+                const u32x4 qa = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(kk < K ? (uint32_t)kk * 4 : OUTSIDE), 0, 0);
+                const u32x4 qb =
+                    __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(kk + 4 < K ? (uint32_t)kk * 4 + 16 : OUTSIDE), 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) { R.k[i][e] = __uint_as_float(qa[e]); R.k[i][4 + e] = __uint_as_float(qb[e]); }
+            } else if constexpr (KS) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) R.k[i][e] = ldg(ksc + min(k0 + bk[i] + e, K - 1));
             }
