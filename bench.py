@@ -568,11 +568,13 @@ def main():
     kernels = {
         "gemm_x3": ("mfma_bf16", "gemm_x3_kernel (v_mfma_f32_32x32x16_bf16, fp32 operands split into three "
                     "bf16 pieces, six bf16 products per fp32 product): the matrix products of launches on "
-                    "128 x 128 tiles; achieved = 6 x the algorithmic flops per second (the bf16 matrix-core "
+                    "128 x 128 tiles (batches of 512 or more such tiles) and 64 x 64 tiles (smaller "
+                    "batches); achieved = 6 x the algorithmic flops per second (the bf16 matrix-core "
                     "work; fp32_equivalent_tflops = the algorithmic rate) against the bf16 matrix-core peak; "
                     + sym_note),
         "gemm_fp32": ("mfma", "gemm_kernel (fp32 v_mfma_f32_32x32x2_f32): the matrix products of the other "
-                      "launches (64 x 64 and skinny tiles: single blocks, panel-width QR products); " + sym_note),
+                      "launches (skinny tiles: the panel-width QR products; operands that sum split-K "
+                      "slabs; every product with SHAMPOO4_FLAG_FP32_MFMA); " + sym_note),
         "qr_panel": ("alu", "panel_*_kernel / qr_step_kernel: Householder factorization of one 32-column "
                      "panel per workgroup (one workgroup per side: a dependent chain of reflector steps, "
                      "latency-bound); in the fused QR step of small batches the same launch applies the "
