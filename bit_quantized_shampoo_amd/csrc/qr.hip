@@ -1112,14 +1112,18 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_global_kernel(const Panel
         const int jn = j + 1;
         float pacc = 0.f, rj = 0.f;
         const int r0 = j + ((slot - (j & (NSLOT - 1)) + NSLOT) & (NSLOT - 1));
-        for (int rb = r0; rb < h; rb += NSLOT * GU) {
-            float xv[GU], xj[GU];
+        // two batches in flight: the loads of batch b + 1 are issued before batch b is
+        // updated (rows clamped into the panel, so every load is unconditional; rows past
+        // the panel are masked where they are used)
+        auto load_batch = [&](float (&xv)[GU], float (&xj)[GU], int rb) {
 #pragma unroll
             for (int u = 0; u < GU; ++u) {
                 const int r = min(rb + NSLOT * u, h - 1);
                 xv[u] = Ap[(int64_t)r * ld + cc];
                 xj[u] = Ap[(int64_t)r * ld + j];
             }
+        };
+        auto use_batch = [&](const float (&xv)[GU], const float (&xj)[GU], int rb) {
 #pragma unroll
             for (int u = 0; u < GU; ++u) {
                 const int r = rb + NSLOT * u;
@@ -1136,6 +1140,16 @@ __global__ __launch_bounds__(PANEL_THREADS) void panel_global_kernel(const Panel
                 const float xn = __shfl(x, jn, 32);
                 if (in && r >= jn) pacc += xn * x;
                 if (in && r == jn) rj = x;
+            }
+        };
+        {
+            float xa[GU], ja[GU], xb[GU], jb[GU];
+            load_batch(xa, ja, r0);
+            for (int rb = r0; rb < h; rb += 2 * NSLOT * GU) {
+                load_batch(xb, jb, rb + NSLOT * GU);
+                use_batch(xa, ja, rb);
+                load_batch(xa, ja, rb + 2 * NSLOT * GU);
+                use_batch(xb, jb, rb + NSLOT * GU);
             }
         }
         write_partial(smem, buf ^ 1, c, lane, wv, pacc);
