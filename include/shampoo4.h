@@ -83,9 +83,12 @@ typedef enum {
                                          the state buffer already holds a saved state. */
 /* Schedule of the Householder QR (same results either way up to rounding order).  By
    default the plan picks from the total work W = sum over sides of p^3: reflectors reach
-   the trailing matrix and Q in blocks of 128 columns when W >= 16 * 2^30 (throughput:
-   large batches), else panel by panel (32 columns), all on the caller's stream.
-   QR_BLOCKED   always 128-column blocks;
+   the trailing matrix and Q in blocks of 128 columns (256 for orders from 2048) when
+   W >= 16 * 2^30 (throughput: large batches), else panel by panel (32 columns) on the
+   caller's stream.  In blocks, a batch of two or more blocks of orders below 2048
+   factors alternate blocks on a second stream of the context (default priority), forked
+   from the caller's stream and joined back to it within the call.
+   QR_BLOCKED   always blocks;
    QR_LOOKAHEAD 32-column panels; the caller's stream carries only the chain of panels
                 and each panel's update of the next panel, a second stream of the context
                 (default priority) the trailing and Q updates.
@@ -100,9 +103,9 @@ typedef enum {
 /* Replay shampoo4_update_stats from a HIP graph captured at the first call (one graph
    per variant: with or without the cached rectified eigenvectors, and with or without
    16-byte loads of the gradients, which need every G 16-byte aligned with ldg a
-   multiple of 4): the kernels, and the
-   second stream of QR_LOOKAHEAD with its event dependencies, are submitted as one graph
-   launch instead of one host call each.  The io upload stays a separate copy before the
+   multiple of 4): the kernels, and the second stream of QR_LOOKAHEAD or of the blocked
+   QR with its event dependencies, are submitted as one graph launch instead of one host
+   call each.  The io upload stays a separate copy before the
    launch.  While kernel timing is on, and if a capture fails, calls launch eagerly. */
 #define SHAMPOO4_FLAG_GRAPHS 32u
 /* Code the eigenvector matrices (U and the root snapshot) with the 4-bit dynamic tree
